@@ -1,0 +1,222 @@
+/*
+ * hdq.h -- C ABI of libhdq, the MI355X (gfx950) library for the hot path of
+ * 6Bit-Diffusion's dynamic mixed-precision quantization (DMPQ) of video
+ * diffusion transformer linear layers.
+ *
+ * What the method computes, per linear layer and per denoising step
+ * (sources: "6Bit-Diffusion" summary of arXiv:2603.18742 on vetunion.cn,
+ * sections one, three and four; the gist.science explainer "6Bit-Diffusion:
+ * Inference-Time Mixed-Precision Quantization for Video Diffusion Models",
+ * sections 2 and 4):
+ *   1. choose the activation precision from the relative difference of the
+ *      module's input and output at the previous step (large: INT8, small:
+ *      NVFP4), INT8 when there is no previous step, and full precision when
+ *      the input's outlier ratio max|x| / mean|x| is too large;
+ *   2. rotate the activations with a block Hadamard transform and quantize
+ *      them in the same pass;
+ *   3. run the quantized linear layer against weights prepared the same way.
+ * hdq_select_precision is step 1, hdq_quantize is step 2 (and the offline
+ * weight preparation), hdq_linear is steps 2 + 3.
+ *
+ * Conventions, for every entry point:
+ *  - All tensors are row-major with the reduction dimension K contiguous:
+ *    activations X [M, K], weights W [N, K], outputs Y [M, N] = X W^T.
+ *  - bf16 tensors are raw 16-bit patterns (the upper half of an IEEE float).
+ *  - Every pointer marked "device" is device memory the caller owns and keeps
+ *    alive until the enqueued work has finished.  The library allocates no
+ *    memory, never synchronises, and enqueues all work on `stream` (a
+ *    hipStream_t passed as void*; NULL is the default stream).
+ *  - Arguments are validated before anything is enqueued; on error nothing
+ *    is enqueued and a negative HDQ_ERR_* code is returned.  A kernel fault
+ *    surfaces at the caller's next synchronisation.
+ *  - Calls are thread-safe; calls that share output or workspace buffers on
+ *    overlapping streams race, as any stream work would.
+ *  - Rotation: every aligned block of `had_block` consecutive elements along
+ *    K is multiplied by H_b / sqrt(b), H_b the Sylvester Hadamard matrix, in
+ *    float32 by the fast Walsh-Hadamard butterfly (strides 1, 2, 4, ... in
+ *    that order) and one multiply by fl32(1/sqrt(b)).  Weights and
+ *    activations are rotated alike, so (XQ)(WQ)^T = XW^T.
+ *  - Quantized codes use round-half-to-even.  Non-finite inputs are outside
+ *    the quantizers' contract; hdq_select_precision routes them to BF16.
+ */
+#ifndef HDQ_H
+#define HDQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define HDQ_OK 0
+#define HDQ_ERR_INVALID (-1)     /* NULL pointer, bad enum or bad struct field  */
+#define HDQ_ERR_SHAPE (-2)       /* size <= 0, K not a multiple of had_block or */
+                                 /* of the format's block, had_block not a      */
+                                 /* power of two in [2, 128], shapes disagree   */
+#define HDQ_ERR_UNSUPPORTED (-3) /* precision/format/output-dtype combination   */
+#define HDQ_ERR_HIP (-4)         /* a kernel launch failed                      */
+#define HDQ_ERR_WORKSPACE (-5)   /* ws NULL or ws_bytes below what is required  */
+
+/* ---- quantized formats (hdq_qtensor.fmt) ---- */
+/* INT8, one fp32 scale per row: s = max|y| / 127, q = rne(y * (127 / max|y|)).
+ * codes: int8 [rows, cols]; row_scale: fp32 [rows].  (The "INT8" activation
+ * format of the summary's section one, per token.) */
+#define HDQ_FMT_INT8_ROW 0
+/* INT4, one fp32 scale per row (per output channel of a weight): same as
+ * INT8 with 7 for 127.  codes: uint8 [rows, cols/2], element 2j in the low
+ * nibble of byte j, two's complement; row_scale: fp32 [rows].  (The 4-bit
+ * weights of the summary's W4A6 configuration, section four.) */
+#define HDQ_FMT_INT4_ROW 1
+/* NVFP4: FP4 E2M1 codes with one E4M3 scale per aligned 16 elements and one
+ * fp32 tensor scale s_t = amax / 2688 (amax of the rotated tensor):
+ * value = e2m1(code) * e4m3(blk_scale) * s_t.  codes: uint8 [rows, cols/2]
+ * (even element in the low nibble); blk_scale: uint8 [rows, cols/16];
+ * tensor_scale: fp32 [1].  (The "NVFP4" format of section one; the pages do
+ * not define it, the encodings are those of the OCP MX v1.0 formats.) */
+#define HDQ_FMT_NVFP4 2
+/* NVFP4 bytes restricted so that every aligned pair of 16-blocks shares one
+ * power-of-two scale (s_t = amax / 1536, scale = smallest power of two that
+ * fits the pair): a valid NVFP4 tensor that is also MXFP4-shaped, so the
+ * GEMM runs on gfx950's block-scaled FP4 matrix instructions. */
+#define HDQ_FMT_NVFP4_MX 3
+
+/* ---- precisions (decisions) ---- */
+#define HDQ_PREC_NVFP4 0
+#define HDQ_PREC_INT8 1
+#define HDQ_PREC_BF16 2 /* full precision: unrotated bf16 x bf16 GEMM */
+
+/* ---- output dtypes of hdq_linear ---- */
+#define HDQ_DTYPE_F32 0
+#define HDQ_DTYPE_BF16 1
+#define HDQ_DTYPE_I32 2 /* INT8 path only: the raw int32 accumulators */
+
+/* ---- workspace queries (hdq_workspace_bytes op) ---- */
+#define HDQ_OP_SELECT 0
+#define HDQ_OP_QUANTIZE 1
+#define HDQ_OP_LINEAR 2
+
+/* A quantized tensor.  The caller allocates every buffer (device memory)
+ * and fills the pointers; hdq_quantize fills fmt, had_block, rows, cols. */
+typedef struct hdq_qtensor {
+    int32_t fmt;          /* HDQ_FMT_*                                       */
+    int32_t had_block;    /* Hadamard block the rows were rotated with       */
+    int64_t rows;         /* logical shape of the unquantized tensor         */
+    int64_t cols;
+    void *codes;          /* device, layout per format (see above)           */
+    float *row_scale;     /* device, INT8/INT4 only (may be NULL otherwise)  */
+    uint8_t *blk_scale;   /* device, NVFP4 formats only                      */
+    float *tensor_scale;  /* device fp32[1], NVFP4 formats only              */
+} hdq_qtensor;
+
+/* A linear layer's weights in every form a precision may need.  Members a
+ * call does not use may be NULL / zeroed. */
+typedef struct hdq_weights {
+    int64_t N;            /* output features                                 */
+    int64_t K;            /* input features                                  */
+    const void *w_bf16;   /* device bf16 [N, K], unrotated: HDQ_PREC_BF16    */
+    hdq_qtensor w_int4;   /* HDQ_FMT_INT4_ROW [N, K]: HDQ_PREC_INT8          */
+    hdq_qtensor w_fp4;    /* HDQ_FMT_NVFP4 or _MX [N, K]: HDQ_PREC_NVFP4     */
+} hdq_weights;
+
+/*
+ * hdq_select_precision -- step 1 (summary section one: the previous step's
+ * input/output difference picks INT8 or NVFP4; section three: the outlier
+ * ratio max/mean forces full precision, and INT8 is used when there is no
+ * previous-step difference; explainer sections 2 and 4).
+ *
+ *   prev_in, prev_out : device bf16 [prev_numel] each, the module's input and
+ *                       output at the previous step; both NULL = no history.
+ *   cur_in            : device bf16 [rows, cols], the current input.
+ *   had_block         : 0, or the Hadamard block (power of two in [2, 128],
+ *                       dividing cols) used to also report the rotated amax.
+ *   delta_thresh, ratio_thresh : thresholds (e.g. 0.1 and 50).
+ *   decision_dev      : device int32[1] <- HDQ_PREC_*.
+ *   stats_dev         : device fp32[5] <- {delta, ratio, max|x|, mean|x|,
+ *                       rotated amax (0 when had_block == 0)}.
+ *   ws, ws_bytes      : device scratch, >= hdq_workspace_bytes(HDQ_OP_SELECT,
+ *                       rows, cols, prev_numel, 0) bytes.
+ * delta = sum|prev_out - prev_in| / sum|prev_in| (0 if both sums are 0, +inf
+ * if only the denominator is, NaN without history); ratio = max|x| / mean|x|
+ * over cur_in (0 for all zeros, NaN if cur_in holds a NaN or an infinity).
+ * Decision: ratio not <= ratio_thresh -> BF16; else no history -> INT8; else
+ * delta not < delta_thresh -> INT8; else NVFP4.  Sums are float32 partials
+ * reduced in double in a fixed order, so results are deterministic.
+ */
+int hdq_select_precision(const void *prev_in, const void *prev_out, int64_t prev_numel,
+                         const void *cur_in, int64_t rows, int64_t cols, int32_t had_block,
+                         float delta_thresh, float ratio_thresh, int32_t *decision_dev,
+                         float *stats_dev, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * hdq_quantize -- step 2: block-Hadamard rotation fused with quantization
+ * (summary sections one and four).  Also prepares weights offline.
+ *
+ *   x           : device bf16 [rows, cols].
+ *   had_block   : power of two in [2, 128] dividing cols.
+ *   fmt         : HDQ_FMT_*; cols must be a multiple of 2 (INT4), 16 (NVFP4)
+ *                 or 32 (NVFP4_MX).
+ *   tensor_amax : NVFP4 formats: device fp32[1] holding the amax of the
+ *                 rotated tensor (e.g. stats_dev + 4 from
+ *                 hdq_select_precision), or NULL to compute it in a pre-pass
+ *                 (then ws must hold hdq_workspace_bytes(HDQ_OP_QUANTIZE,
+ *                 rows, cols, 0, fmt) bytes).  Ignored for INT formats.
+ *   out         : host struct with caller-allocated device buffers sized for
+ *                 the format; fmt, had_block, rows, cols are written.
+ * Rows whose max |rotated value| is below 2^-100 get zero codes and a zero
+ * scale; an NVFP4 tensor whose amax is below 2^-100 gets s_t = 0 and zero
+ * codes and scale bytes.
+ */
+int hdq_quantize(const void *x, int64_t rows, int64_t cols, int32_t had_block, int32_t fmt,
+                 const float *tensor_amax, hdq_qtensor *out, void *ws, size_t ws_bytes,
+                 void *stream);
+
+/*
+ * hdq_linear -- steps 2 + 3: Y[M, N] = quantized X[M, K] times the weights'
+ * matching form (summary section one: NVFP4 or INT8 activations against
+ * 4-bit weights; section three: full-precision fallback).
+ *
+ *   precision   : HDQ_PREC_* to run, or -1 to read it from decision_dev on
+ *                 the device (every candidate kernel is enqueued and the ones
+ *                 not selected exit at once; no host synchronisation).
+ *   decision_dev: device int32[1] (only read when precision == -1).
+ *   x           : device bf16 [M, K] (the unrotated activations).
+ *   xq          : NULL, or already-quantized activations to use instead of
+ *                 quantizing x (fixed precision only; its format must match
+ *                 the weights': INT8_ROW for INT8, the w_fp4 format for NVFP4).
+ *   x_amax      : NVFP4 only: device fp32[1] rotated amax of x, or NULL to
+ *                 compute it in a pre-pass.
+ *   w           : weights; w->K == K and had_block of both quantized forms
+ *                 must be equal; the needed forms must be present.
+ *   y, y_dtype  : device output [M, N]: HDQ_DTYPE_F32 or _BF16 (all
+ *                 precisions), _I32 (INT8 only: raw accumulators).
+ *   ws, ws_bytes: device scratch >= hdq_workspace_bytes(HDQ_OP_LINEAR, M, K,
+ *                 N, w_fp4.fmt) (0 when xq is given for INT8).
+ * INT8:  acc = sum_k qx*qw (exact int32); y = fl32(fl32(acc * sx[m]) * sw[n]).
+ * NVFP4: y = s_tx * s_tw * sum over 16-blocks of E_x E_w sum_k e2m1 e2m1,
+ *        float32 accumulation.
+ * BF16:  y = x w^T with the unrotated bf16 operands, float32 accumulation.
+ */
+int hdq_linear(int32_t precision, const int32_t *decision_dev, const void *x,
+               const hdq_qtensor *xq, const float *x_amax, int64_t M, int64_t K,
+               const hdq_weights *w, void *y, int32_t y_dtype, void *ws, size_t ws_bytes,
+               void *stream);
+
+/* Scratch bytes an entry point needs.  op = HDQ_OP_SELECT: (M = rows,
+ * K = cols, N = prev_numel); HDQ_OP_QUANTIZE: (M = rows, K = cols, fmt);
+ * HDQ_OP_LINEAR: (M, K, N, fmt = the weights' FP4 format, or -1 when only
+ * INT8/BF16 will run).  Returns 0 on bad arguments. */
+size_t hdq_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N, int32_t fmt);
+
+/* Static text for a status code. */
+const char *hdq_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int hdq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HDQ_H */

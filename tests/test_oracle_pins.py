@@ -1,0 +1,468 @@
+"""Pins of the CPU oracle against what the pages, the format definitions and
+mathematics fix -- never against the oracle's own formulas.
+
+Each test names the part of the oracle it pins and what pins it:
+closed forms (Hadamard orthogonality, spike/constant special cases), an
+independent library (scipy's Hadamard construction, numpy integer matmul,
+torch's FP8 E4M3 codec), the OCP MX format definition (tests/golden), or
+brute force on tiny inputs.
+"""
+import decimal
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+import torch
+
+import oracle as O
+from bit_quantized_video_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+BLOCKS = [2, 4, 8, 16, 32, 64, 128]
+
+
+def rnd_bf16(shape, seed, std=1.0):
+    rng = np.random.default_rng(seed)
+    return synth.to_bf16_bits(rng.standard_normal(shape).astype(np.float32) * np.float32(std))
+
+
+# ------------------------------------------------------------ P1 rotation
+
+@pytest.mark.parametrize("b", BLOCKS)
+def test_hadamard_is_sylvester_and_orthogonal(b):
+    H = O.hadamard_matrix(b)
+    assert np.array_equal(H, scipy.linalg.hadamard(b))          # independent construction
+    assert np.array_equal(H @ H.T, b * np.eye(b, dtype=np.int64))
+    assert np.array_equal(H, H.T)
+
+
+@pytest.mark.parametrize("b", BLOCKS)
+def test_hadamard_scale_is_correctly_rounded(b):
+    decimal.getcontext().prec = 60
+    exact = decimal.Decimal(1) / decimal.Decimal(b).sqrt()
+    c = O.hadamard_scale(b)
+    lo = np.nextafter(c, np.float32(0))
+    hi = np.nextafter(c, np.float32(1))
+    err = lambda v: abs(decimal.Decimal(float(v)) - exact)
+    assert err(c) <= err(lo) and err(c) <= err(hi)
+    assert abs(float(c) - 1 / math.sqrt(b)) < 1e-7
+
+
+@pytest.mark.parametrize("b", BLOCKS)
+def test_fwht_matches_dense_hadamard_on_integers(b):
+    # integer inputs: every butterfly sum is exact in float32, so the result
+    # must equal fl32(H x (exact int64) * c_b) whatever the evaluation order
+    rng = np.random.default_rng(b)
+    xi = rng.integers(-16, 17, size=(5, 4 * b))
+    x16 = synth.to_bf16_bits(xi.astype(np.float32))
+    y = O.rotate_f32(x16, b)
+    H = scipy.linalg.hadamard(b).astype(np.int64)
+    ref = (xi.reshape(5, 4, b) @ H).reshape(5, 4 * b).astype(np.float32) * O.hadamard_scale(b)
+    assert np.array_equal(y, ref)
+
+
+@pytest.mark.parametrize("b", [16, 64, 128])
+def test_fwht_f32_close_to_definition(b):
+    x16 = rnd_bf16((7, 3 * b), seed=b)
+    xf = synth.bf16_bits_to_f32(x16).astype(np.float64)
+    yd = O.rotate_dense_f64(xf, b)
+    y = O.rotate_f32(x16, b).astype(np.float64)
+    l1 = np.abs(xf).reshape(7, 3, b).sum(-1, keepdims=True).repeat(b, -1).reshape(7, 3 * b)
+    bound = (math.log2(b) + 2) * 2.0 ** -24 * l1 / math.sqrt(b)
+    assert np.all(np.abs(y - yd) <= bound)
+
+
+@pytest.mark.parametrize("b", [8, 64, 128])
+def test_rotation_round_trip_and_parseval(b):
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((4, 2 * b))
+    y = O.rotate_dense_f64(x, b)
+    assert np.allclose(O.rotate_dense_f64(y, b), x, rtol=0, atol=1e-12)
+    for j in range(2):
+        blk = slice(j * b, (j + 1) * b)
+        assert np.allclose(np.linalg.norm(y[:, blk], axis=1), np.linalg.norm(x[:, blk], axis=1),
+                           rtol=1e-13)
+
+
+def test_rotation_blocks_are_independent_and_aligned():
+    b = 32
+    x16 = rnd_bf16((3, 4 * b), seed=11)
+    y = O.rotate_f32(x16, b)
+    for j in range(4):
+        blk = slice(j * b, (j + 1) * b)
+        assert np.array_equal(y[:, blk], O.rotate_f32(np.ascontiguousarray(x16[:, blk]), b))
+
+
+# ------------------------------------------------- P2 special cases
+
+@pytest.mark.parametrize("b", BLOCKS)
+def test_constant_block_goes_to_first_coefficient(b):
+    x16 = synth.to_bf16_bits(np.ones((1, b), np.float32))
+    y = O.rotate_f32(x16, b)
+    assert y[0, 0] == np.float32(b) * O.hadamard_scale(b)
+    assert abs(float(y[0, 0]) - math.sqrt(b)) < 1e-5 * math.sqrt(b)
+    assert np.all(y[0, 1:] == 0)
+
+
+@pytest.mark.parametrize("b", [16, 128])
+def test_spike_is_spread_flat(b):
+    # one outlier of size A becomes b values of magnitude A/sqrt(b): the
+    # outlier redistribution the block Hadamard transform is used for
+    A = 96.0
+    H = scipy.linalg.hadamard(b)
+    for j in (0, 5, b - 1):
+        x = np.zeros((1, b), np.float32)
+        x[0, j] = A
+        y = O.rotate_f32(synth.to_bf16_bits(x), b)
+        assert np.all(np.abs(y) == np.float32(A) * O.hadamard_scale(b))
+        assert np.array_equal(np.sign(y[0]), H[j].astype(np.float32))
+
+
+# ------------------------------------------------------- P3 E2M1 codec
+
+def load_e2m1_golden():
+    rows = []
+    with open(os.path.join(GOLDEN, "e2m1_ocp_mx_v1.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                c, v = line.split()
+                rows.append((int(c, 16), float(v)))
+    return rows
+
+
+def e2m1_from_bits(code):
+    s, e, m = (code >> 3) & 1, (code >> 1) & 3, code & 1
+    mag = 0.5 * m if e == 0 else 2.0 ** (e - 1) * (1 + 0.5 * m)
+    return -mag if s else mag
+
+
+def test_e2m1_decode_matches_spec():
+    gold = load_e2m1_golden()
+    assert len(gold) == 16
+    for code, val in gold:
+        assert O.e2m1_decode(code) == val
+        assert e2m1_from_bits(code) == val
+
+
+def test_e2m1_encode_grid_midpoints_saturation():
+    for code in range(16):
+        v = e2m1_from_bits(code)
+        want = code if not (code == 8) else 8
+        assert O.e2m1_encode(np.float32(v)) == want
+    # midpoints round to the even code (mantissa bit 0)
+    mids = {0.25: 0x0, 0.75: 0x2, 1.25: 0x2, 1.75: 0x4, 2.5: 0x4, 3.5: 0x6, 5.0: 0x6}
+    for v, code in mids.items():
+        assert O.e2m1_encode(np.float32(v)) == code
+        assert O.e2m1_encode(np.float32(-v)) == code | 8
+        # just above / below a midpoint goes to the nearer neighbour
+        up = np.nextafter(np.float32(v), np.float32(10))
+        dn = np.nextafter(np.float32(v), np.float32(0))
+        grid = [abs(e2m1_from_bits(c)) for c in range(8)]
+        assert O.e2m1_encode(up) == min(range(8), key=lambda c: abs(grid[c] - float(up)))
+        assert O.e2m1_encode(dn) == min(range(8), key=lambda c: abs(grid[c] - float(dn)))
+    for v in (6.0, 6.4, 7.0, 1e6, float("inf")):
+        assert O.e2m1_encode(np.float32(v)) == 0x7
+        assert O.e2m1_encode(np.float32(-v)) == 0xF
+    assert O.e2m1_encode(np.float32(-0.1)) == 0x8   # sign of a value that rounds to 0
+    assert O.e2m1_encode(np.float32(0.0)) == 0x0
+
+
+def test_e2m1_encode_is_nearest_on_dense_grid():
+    vals = np.linspace(-7, 7, 5601, dtype=np.float32)
+    codes = O.e2m1_encode(vals)
+    dec = np.array([e2m1_from_bits(int(c)) for c in codes])
+    grid = np.array([e2m1_from_bits(c) for c in range(8)])
+    clip = np.clip(vals, -6, 6).astype(np.float64)
+    best = np.abs(np.abs(clip)[:, None] - grid[None, :]).min(1)
+    assert np.all(np.abs(np.abs(clip) - np.abs(dec)) == best)
+
+
+# ------------------------------------------------------- P4 E4M3 codec
+
+def test_e4m3_decode_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    got = O.e4m3_decode(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert O.e4m3_decode(0x7E) == 448.0 and O.e4m3_decode(0x01) == 2.0 ** -9
+
+
+def e4m3_midpoints():
+    pos = np.array([O.e4m3_decode(c) for c in range(0x7F)], np.float64)
+    mids = (pos[:-1] + pos[1:]) / 2
+    return pos, mids
+
+
+def test_e4m3_encode_matches_torch_rne():
+    pos, mids = e4m3_midpoints()
+    rng = np.random.default_rng(5)
+    t = np.concatenate([
+        pos, mids,
+        np.nextafter(mids.astype(np.float32), np.float32(0)),
+        np.nextafter(mids.astype(np.float32), np.float32(1000)),
+        np.exp(rng.uniform(np.log(2.0 ** -12), np.log(448.0), 20000)),
+    ]).astype(np.float32)
+    t = t[(t >= 0) & (t <= 448)]
+    ref = torch.from_numpy(t).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_encode(t), ref)
+
+
+def test_e4m3_encode_saturates_and_flushes():
+    for v in (448.0, 449.0, 464.0, 465.0, 1e4, float("inf")):
+        assert O.e4m3_encode(np.float32(v)) == 0x7E
+    assert O.e4m3_encode(np.float32(2.0 ** -10)) == 0x00     # tie with 0 -> even (0)
+    assert O.e4m3_encode(np.float32(2.0 ** -10 * 1.0001)) == 0x01
+    assert O.e4m3_encode(np.float32(0.0)) == 0x00
+
+
+# ------------------------------------------- P5 quantize error bounds
+
+@pytest.mark.parametrize("qmax", [127, 7])
+def test_int_quant_error_bound(qmax):
+    x16 = synth.gaussian_outliers(64, 512, 0.02, 25.0, synth.rng_for(9, 0))
+    y = O.rotate_f32(x16, 128).astype(np.float64)
+    q, s = O.quant_int(x16, 128, qmax)
+    assert np.all(np.abs(q.astype(np.int64)) <= qmax)
+    assert np.all(np.abs(q).max(1) == qmax)            # the row max maps to +-qmax
+    err = np.abs(y - q.astype(np.float64) * s[:, None].astype(np.float64))
+    assert np.all(err <= s[:, None] * (0.5 + 1e-5))
+    # scale is the row absmax over qmax
+    assert np.allclose(s, np.abs(y).max(1) / qmax, rtol=1e-6)
+
+
+def test_int_quant_zero_and_tiny_rows():
+    x16 = np.zeros((3, 64), np.uint16)
+    x16[1, 5] = synth.to_bf16_bits(np.array([2.0 ** -110], np.float32))[0]
+    x16[2, :] = synth.to_bf16_bits(np.full(64, 0.5, np.float32))
+    q, s = O.quant_int(x16, 16, 127)
+    assert s[0] == 0 and s[1] == 0 and not q[:2].any()
+    assert s[2] > 0 and np.abs(q[2]).max() == 127
+
+
+def nvfp4_error_bound(v_abs, d):
+    step = np.where(v_abs < 2, 0.25, np.where(v_abs < 4, 0.5, 1.0))
+    return step * d
+
+
+@pytest.mark.parametrize("mx", [False, True])
+def test_nvfp4_error_bound(mx):
+    x16 = synth.lognormal_tokens(48, 1024, synth.rng_for(9, 1))
+    y = O.rotate_f32(x16, 128)
+    amax = np.abs(y).max()
+    codes, sc, st = O.quant_nvfp4(x16, 128, mx=mx)
+    assert O.rotated_amax(x16, 128) == amax
+    assert st == np.float32(amax) / np.float32(1536.0 if mx else 2688.0)
+    deq = O.dequant_nvfp4(codes, sc, st, 1024).astype(np.float64)
+    d = (O.e4m3_decode(sc).astype(np.float64) * float(st)).repeat(16, axis=1)
+    v = np.abs(y.astype(np.float64)) / np.where(d > 0, d, 1)
+    normal = np.repeat(sc >= 0x08, 16, axis=1)     # E4M3 exponent field > 0
+    err = np.abs(y - deq)
+    inrange = v <= 6
+    bound = nvfp4_error_bound(v, d) * (1 + 1e-5) + 1e-30
+    assert np.all(err[inrange & normal] <= bound[inrange & normal])
+    # saturation beyond 6 stays within 0.4 d for normal scales
+    sat = ~inrange & normal
+    assert np.all(err[sat] <= 0.4 * d[sat] * (1 + 1e-5))
+    if mx:
+        # pairs of 16-blocks share one power-of-two scale
+        assert np.array_equal(sc[:, 0::2], sc[:, 1::2])
+        vals = O.e4m3_decode(sc)
+        assert np.all(np.log2(vals) == np.round(np.log2(vals)))
+        assert np.all(v <= 6 * (1 + 1e-6))          # nothing saturates
+
+
+def test_nvfp4_zero_tensor_and_zero_blocks():
+    x16 = np.zeros((2, 64), np.uint16)
+    codes, sc, st = O.quant_nvfp4(x16, 32)
+    assert st == 0 and not codes.any() and not sc.any()
+    x16[0, :32] = synth.to_bf16_bits(np.full(32, 3.0, np.float32))
+    codes, sc, st = O.quant_nvfp4(x16, 32)
+    assert sc[1].sum() == 0 and codes[1].sum() == 0   # zero row -> zero blocks
+
+
+# ------------------------------------------------------ P6 GEMMs
+
+@pytest.mark.parametrize("shape", [(1, 1, 32), (7, 5, 64), (33, 17, 128), (64, 64, 96)])
+def test_int_gemm_brute_force(shape):
+    M, N, K = shape
+    rng = np.random.default_rng(M * 1000 + N)
+    qa = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    qw = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    sa = rng.uniform(0.001, 0.1, M).astype(np.float32)
+    sw = rng.uniform(0.001, 0.1, N).astype(np.float32)
+    y, acc = O.gemm_int(qa, sa, qw, sw)
+    assert np.array_equal(acc, qa.astype(np.int64) @ qw.astype(np.int64).T)
+    ref = (qa.astype(np.float64) * sa[:, None]) @ (qw.astype(np.float64) * sw[:, None]).T
+    assert np.allclose(y, ref, rtol=3e-7, atol=0)
+
+
+def test_int4_pack_round_trip_and_layout():
+    q = np.array([[-7, 7, 0, -1, 3, -8 + 1, 1, 2]], np.int8)
+    p = O.pack_int4(q)
+    assert p.tolist() == [[0x79, 0xF0, 0x93, 0x21]]     # even k in the low nibble
+    rng = np.random.default_rng(1)
+    q = rng.integers(-8, 8, size=(9, 64)).astype(np.int8)
+    assert np.array_equal(O.unpack_int4(O.pack_int4(q), 64), q)
+
+
+@pytest.mark.parametrize("mx", [False, True])
+def test_nvfp4_gemm_matches_dequantized_product(mx):
+    xa = synth.lognormal_tokens(9, 256, synth.rng_for(9, 2))
+    xw = synth.gaussian(11, 256, 0.02, synth.rng_for(9, 3))
+    ac, ae, ast = O.quant_nvfp4(xa, 64, mx=mx)
+    wc, we, wst = O.quant_nvfp4(xw, 64, mx=mx)
+    y = O.gemm_nvfp4(ac, ae, ast, wc, we, wst, 256)
+    da = O.dequant_nvfp4(ac, ae, ast, 256).astype(np.float64)
+    dw = O.dequant_nvfp4(wc, we, wst, 256).astype(np.float64)
+    ref = da @ dw.T
+    # each dequantized element carries one float32 rounding (of E*s_t times
+    # the code): error <= 2 * 2^-24 * sum_k |a_k w_k|
+    bound = 2.0 ** -22 * (np.abs(da) @ np.abs(dw).T)
+    assert np.all(np.abs(y - ref) <= bound)
+
+
+def test_bf16_gemm_matches_numpy():
+    x = synth.gaussian(13, 96, 1.0, synth.rng_for(9, 4))
+    w = synth.gaussian(6, 96, 0.02, synth.rng_for(9, 5))
+    y = O.gemm_bf16(x, w)
+    ref = synth.bf16_bits_to_f32(x).astype(np.float64) @ synth.bf16_bits_to_f32(w).astype(np.float64).T
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-15)
+
+
+# --------------------------------------- P7 rotation cancels in the product
+
+def test_rotated_product_equals_plain_product():
+    b = 64
+    x = synth.bf16_bits_to_f32(synth.gaussian_outliers(8, 256, 0.02, 20.0, synth.rng_for(9, 6))).astype(np.float64)
+    w = synth.bf16_bits_to_f32(synth.gaussian(12, 256, 0.02, synth.rng_for(9, 7))).astype(np.float64)
+    xr, wr = O.rotate_dense_f64(x, b), O.rotate_dense_f64(w, b)
+    assert np.allclose(xr @ wr.T, x @ w.T, rtol=1e-10, atol=1e-13)
+
+
+@pytest.mark.parametrize("path", ["int8", "nvfp4", "nvfp4_mx"])
+def test_quantized_linear_approximates_plain_product(path):
+    # a rotation applied to only one operand, or a lost scale, would give an
+    # O(1) error; quantization error alone is a few percent
+    b, K = 128, 512
+    x16 = synth.gaussian_outliers(32, K, 0.01, 20.0, synth.rng_for(9, 8))
+    w16 = synth.gaussian(24, K, 0.02, synth.rng_for(9, 9))
+    ref = O.gemm_bf16(x16, w16)
+    if path == "int8":
+        qa, sa = O.quant_int(x16, b, 127)
+        qw, sw = O.quant_int(w16, b, 7)
+        y, _ = O.gemm_int(qa, sa, qw, sw)
+        tol = 0.2
+    else:
+        mx = path == "nvfp4_mx"
+        ac, ae, ast = O.quant_nvfp4(x16, b, mx=mx)
+        wc, we, wst = O.quant_nvfp4(w16, b, mx=mx)
+        y = O.gemm_nvfp4(ac, ae, ast, wc, we, wst, K)
+        tol = 0.2
+    rel = np.linalg.norm(y - ref) / np.linalg.norm(ref)
+    assert rel < tol, rel
+
+
+# --------------------------------------------- P8 selection hand cases
+
+def bf16(v):
+    return synth.to_bf16_bits(np.asarray(v, np.float32))
+
+
+def test_delta_hand_cases():
+    n = 256
+    x = bf16(np.linspace(-3, 3, n).reshape(4, 64))
+    st = O.stats(x, x, x, 0)
+    assert st[0] == 0.0 and O.decide(True, st[0], st[1]) == O.NVFP4
+    st = O.stats(x, bf16(2 * synth.bf16_bits_to_f32(x)), x, 0)
+    assert st[0] == 1.0 and O.decide(True, st[0], st[1]) == O.INT8
+    # delta exactly at the threshold goes to INT8
+    a, o = bf16(np.full((4, 64), 8.0)), bf16(np.full((4, 64), 9.0))
+    st = O.stats(a, o, a, 0)
+    assert st[0] == 0.125
+    assert O.decide(True, st[0], st[1], delta_thresh=0.125) == O.INT8
+    assert O.decide(True, st[0], st[1], delta_thresh=0.1250001) == O.NVFP4
+    # both previous tensors zero -> delta 0; only the input zero -> +inf
+    z = np.zeros((4, 64), np.uint16)
+    assert O.stats(z, z, a, 0)[0] == 0.0
+    assert O.stats(z, o, a, 0)[0] == math.inf
+
+
+def ratio_case(spike):
+    x = np.ones((1, 64), np.float32)
+    x[0, 17] = spike
+    return bf16(x)
+
+
+def test_ratio_hand_cases():
+    c = bf16(np.full((2, 64), -2.5))
+    assert O.stats(None, None, c, 0)[1] == 1.0                     # constant -> 1
+    assert O.stats(None, None, ratio_case(225.0), 0)[1] == 50.0    # 64*225/288
+    r49 = O.stats(None, None, ratio_case(224.0), 0)[1]
+    r51 = O.stats(None, None, ratio_case(226.0), 0)[1]
+    assert r49 < 50 < r51
+    assert O.decide(False, math.nan, r49) == O.INT8
+    assert O.decide(False, math.nan, 50.0) == O.INT8                # at threshold: no PDR
+    assert O.decide(False, math.nan, r51) == O.BF16
+    assert O.decide(True, 0.0, r51) == O.BF16                       # PDR overrides DMPQ
+    z = np.zeros((1, 64), np.uint16)
+    st = O.stats(z, z, z, 0)
+    assert st[1] == 0.0 and O.decide(True, st[0], st[1]) == O.NVFP4
+
+
+def test_nonfinite_input_goes_full_precision():
+    x = np.ones((1, 64), np.float32)
+    for bad in (np.nan, np.inf, -np.inf):
+        x[0, 3] = bad
+        st = O.stats(None, None, bf16(x), 16)
+        assert math.isnan(st[1])
+        assert O.decide(True, 0.0, st[1]) == O.BF16
+    assert O.decide(True, math.nan, 1.0) == O.INT8     # NaN delta -> conservative INT8
+
+
+def test_no_history_is_int8_unless_pdr():
+    x = bf16(np.ones((2, 64)))
+    st = O.stats(None, None, x, 64)
+    assert math.isnan(st[0])
+    assert O.decide(False, st[0], st[1]) == O.INT8
+    assert st[4] == np.float32(8.0)      # rotated amax of a constant 64-block: 64/8
+
+
+def test_stats_values_against_numpy():
+    pi = synth.gaussian(16, 128, 1.0, synth.rng_for(9, 10))
+    po = synth.gaussian(16, 128, 1.0, synth.rng_for(9, 11))
+    cur = synth.gaussian_outliers(16, 128, 0.05, 30.0, synth.rng_for(9, 12))
+    st = O.stats(pi, po, cur, 128)
+    a, o, c = (synth.bf16_bits_to_f32(t).astype(np.float64) for t in (pi, po, cur))
+    assert np.isclose(st[0], np.abs(o - a).sum() / np.abs(a).sum(), rtol=1e-13)
+    assert np.isclose(st[1], np.abs(c).max() / np.abs(c).mean(), rtol=1e-13)
+    assert st[2] == np.abs(c).max()
+    assert np.isclose(st[4], np.abs(O.rotate_dense_f64(c, 128)).max(), rtol=1e-6)
+
+
+# ---------------------------------------------------- P9 idempotence
+
+def test_int8_requantize_is_idempotent():
+    x16 = synth.gaussian_outliers(32, 256, 0.02, 20.0, synth.rng_for(9, 13))
+    y = O.rotate_f32(x16, 64)
+    q, s = O.quant_int_rotated(y, 127)
+    q2, _ = O.quant_int_rotated(q.astype(np.float32) * s[:, None], 127)
+    assert np.array_equal(q, q2)
+
+
+def test_nvfp4_requantize_is_idempotent_on_normal_scales():
+    x16 = synth.lognormal_tokens(16, 512, synth.rng_for(9, 14), sigma=0.3)
+    y = O.rotate_f32(x16, 128)
+    amax = np.abs(y).max()
+    c, e, st = O.quant_nvfp4_rotated(y, amax)
+    deq = O.dequant_nvfp4(c, e, st, 512)
+    c2, e2, st2 = O.quant_nvfp4_rotated(deq, amax)
+    normal = e >= 0x08
+    assert normal.mean() > 0.99
+    assert np.array_equal(e[normal], e2[normal])
+    nb = np.repeat(normal, 8, axis=1)        # 8 code bytes per 16-block
+    assert np.array_equal(c[nb], c2[nb])
