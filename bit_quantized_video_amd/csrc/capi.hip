@@ -1,0 +1,273 @@
+// capi.hip -- the C ABI of libhdq (declared in include/hdq.h).
+//
+// Validates every argument before anything is enqueued, carves the caller's
+// workspace, and enqueues the kernels on the caller's stream.  No allocation,
+// no synchronisation, no global state.
+#include "hdq.h"
+#include "hdq_internal.h"
+
+#include <hip/hip_runtime.h>
+
+namespace {
+
+using namespace hdq;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool valid_block(int32_t hb) { return hb >= 2 && hb <= 128 && (hb & (hb - 1)) == 0; }
+
+// Shape rules shared by the quantizers: cols a multiple of 8 (16-byte rows of
+// bf16 chunks) and of the Hadamard block and of the format's scale block.
+int check_quant_shape(int64_t rows, int64_t cols, int32_t hb, int32_t fmt) {
+  if (rows <= 0 || cols <= 0 || rows > 0x7fffffff || !valid_block(hb)) return HDQ_ERR_SHAPE;
+  if (cols % 8 != 0 || cols % hb != 0) return HDQ_ERR_SHAPE;
+  if (fmt == HDQ_FMT_NVFP4 && cols % 16 != 0) return HDQ_ERR_SHAPE;
+  if (fmt == HDQ_FMT_NVFP4_MX && cols % 32 != 0) return HDQ_ERR_SHAPE;
+  return HDQ_OK;
+}
+
+bool valid_fmt(int32_t fmt) { return fmt >= HDQ_FMT_INT8_ROW && fmt <= HDQ_FMT_NVFP4_MX; }
+bool is_fp4(int32_t fmt) { return fmt == HDQ_FMT_NVFP4 || fmt == HDQ_FMT_NVFP4_MX; }
+
+// Bytes of one quantized activation tensor [M, K] in `fmt` (codes and scales).
+size_t qtensor_bytes(int64_t M, int64_t K, int32_t fmt) {
+  if (fmt == HDQ_FMT_INT8_ROW) return align_up((size_t)(M * K)) + align_up((size_t)M * 4);
+  if (is_fp4(fmt)) return align_up((size_t)(M * K / 2)) + align_up((size_t)(M * K / 16)) + kAlign;
+  return 0;
+}
+
+// Scratch of the NVFP4 tensor-amax pre-pass: the stats partials + one float.
+size_t amax_prepass_bytes() { return align_up(kStatsPartialBytes) + kAlign; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? HDQ_OK : HDQ_ERR_HIP; }
+
+// Checks a quantized tensor's descriptor against a [rows, cols] operand.
+int check_qtensor(const hdq_qtensor& q, int32_t fmt, int64_t rows, int64_t cols) {
+  if (q.fmt != fmt) return HDQ_ERR_UNSUPPORTED;
+  if (q.rows != rows || q.cols != cols) return HDQ_ERR_SHAPE;
+  if (!valid_block(q.had_block)) return HDQ_ERR_SHAPE;
+  if (q.codes == nullptr) return HDQ_ERR_INVALID;
+  if ((fmt == HDQ_FMT_INT8_ROW || fmt == HDQ_FMT_INT4_ROW) && q.row_scale == nullptr) return HDQ_ERR_INVALID;
+  if (is_fp4(fmt) && (q.blk_scale == nullptr || q.tensor_scale == nullptr)) return HDQ_ERR_INVALID;
+  return HDQ_OK;
+}
+
+// Enqueues rotation + quantization of x into q (fields already filled).
+// amax: NVFP4 rotated amax (device) or null; scratch holds the pre-pass
+// space when amax is null.
+hipError_t enqueue_quantize(const void* x, const hdq_qtensor& q, const float* amax, uint8_t* scratch,
+                            const int32_t* gate, int32_t want, hipStream_t s) {
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  if (q.fmt == HDQ_FMT_INT8_ROW || q.fmt == HDQ_FMT_INT4_ROW)
+    return launch_quant_int_rows(xb, q.rows, q.cols, q.had_block, q.fmt, q.codes, q.row_scale, gate,
+                                 want, s);
+  if (amax == nullptr) {
+    double* partials = reinterpret_cast<double*>(scratch);
+    float* slot = reinterpret_cast<float*>(scratch + align_up(kStatsPartialBytes));
+    hipError_t e = launch_stats(nullptr, nullptr, 0, xb, q.rows * q.cols, q.had_block, 0.0f, 0.0f,
+                                nullptr, nullptr, slot, partials, gate, want, s);
+    if (e != hipSuccess) return e;
+    amax = slot;
+  }
+  return launch_quant_nvfp4(xb, q.rows, q.cols, q.had_block, q.fmt, amax,
+                            static_cast<uint8_t*>(q.codes), q.blk_scale, q.tensor_scale, gate, want, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hdq_status_string(int status) {
+  switch (status) {
+    case HDQ_OK: return "ok";
+    case HDQ_ERR_INVALID: return "invalid argument (null pointer, bad enum or descriptor field)";
+    case HDQ_ERR_SHAPE: return "bad shape (size, alignment or Hadamard block)";
+    case HDQ_ERR_UNSUPPORTED: return "unsupported precision / format / output dtype combination";
+    case HDQ_ERR_HIP: return "HIP launch error";
+    case HDQ_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+int hdq_version(void) { return 10000; }
+
+size_t hdq_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N, int32_t fmt) {
+  if (M <= 0 || K <= 0) return 0;
+  switch (op) {
+    case HDQ_OP_SELECT:
+      return align_up(kStatsPartialBytes);
+    case HDQ_OP_QUANTIZE:
+      if (!valid_fmt(fmt)) return 0;
+      return is_fp4(fmt) ? amax_prepass_bytes() : 0;
+    case HDQ_OP_LINEAR: {
+      (void)N;
+      size_t b = qtensor_bytes(M, K, HDQ_FMT_INT8_ROW);
+      if (is_fp4(fmt)) b += qtensor_bytes(M, K, fmt) + amax_prepass_bytes();
+      return b;
+    }
+    default:
+      return 0;
+  }
+}
+
+int hdq_select_precision(const void* prev_in, const void* prev_out, int64_t prev_numel,
+                         const void* cur_in, int64_t rows, int64_t cols, int32_t had_block,
+                         float delta_thresh, float ratio_thresh, int32_t* decision_dev,
+                         float* stats_dev, void* ws, size_t ws_bytes, void* stream) {
+  if (cur_in == nullptr || decision_dev == nullptr || stats_dev == nullptr) return HDQ_ERR_INVALID;
+  if ((prev_in == nullptr) != (prev_out == nullptr)) return HDQ_ERR_INVALID;
+  if (rows <= 0 || cols <= 0) return HDQ_ERR_SHAPE;
+  if (prev_in != nullptr && prev_numel <= 0) return HDQ_ERR_SHAPE;
+  if (had_block != 0 && (!valid_block(had_block) || cols % had_block != 0 || cols % 8 != 0))
+    return HDQ_ERR_SHAPE;
+  if (ws == nullptr || ws_bytes < align_up(kStatsPartialBytes)) return HDQ_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(launch_stats(static_cast<const uint16_t*>(prev_in),
+                                 static_cast<const uint16_t*>(prev_out), prev_numel,
+                                 static_cast<const uint16_t*>(cur_in), rows * cols, had_block,
+                                 delta_thresh, ratio_thresh, decision_dev, stats_dev, nullptr,
+                                 static_cast<double*>(ws), nullptr, 0, s));
+}
+
+int hdq_quantize(const void* x, int64_t rows, int64_t cols, int32_t had_block, int32_t fmt,
+                 const float* tensor_amax, hdq_qtensor* out, void* ws, size_t ws_bytes,
+                 void* stream) {
+  if (x == nullptr || out == nullptr || !valid_fmt(fmt)) return HDQ_ERR_INVALID;
+  int st = check_quant_shape(rows, cols, had_block, fmt);
+  if (st != HDQ_OK) return st;
+  hdq_qtensor q = *out;
+  q.fmt = fmt;
+  q.had_block = had_block;
+  q.rows = rows;
+  q.cols = cols;
+  if ((st = check_qtensor(q, fmt, rows, cols)) != HDQ_OK) return st;
+  if (is_fp4(fmt) && tensor_amax == nullptr &&
+      (ws == nullptr || ws_bytes < amax_prepass_bytes()))
+    return HDQ_ERR_WORKSPACE;
+  *out = q;
+  return hip_status(enqueue_quantize(x, q, is_fp4(fmt) ? tensor_amax : nullptr,
+                                     static_cast<uint8_t*>(ws), nullptr, 0,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+int hdq_linear(int32_t precision, const int32_t* decision_dev, const void* x,
+               const hdq_qtensor* xq, const float* x_amax, int64_t M, int64_t K,
+               const hdq_weights* w, void* y, int32_t y_dtype, void* ws, size_t ws_bytes,
+               void* stream) {
+  if (w == nullptr || y == nullptr) return HDQ_ERR_INVALID;
+  if (precision < -1 || precision > HDQ_PREC_BF16) return HDQ_ERR_INVALID;
+  if (y_dtype < HDQ_DTYPE_F32 || y_dtype > HDQ_DTYPE_I32) return HDQ_ERR_INVALID;
+  if (precision == -1 && (decision_dev == nullptr || xq != nullptr)) return HDQ_ERR_INVALID;
+  if (M <= 0 || K <= 0 || w->N <= 0 || M > 0x7fffffff || K > 0x7fffffff || w->N > 0x7fffffff)
+    return HDQ_ERR_SHAPE;
+  if (w->K != K) return HDQ_ERR_SHAPE;
+  const int64_t N = w->N;
+  const bool run_int8 = precision == HDQ_PREC_INT8 || precision == -1;
+  const bool run_fp4 = precision == HDQ_PREC_NVFP4 || precision == -1;
+  const bool run_bf16 = precision == HDQ_PREC_BF16 || precision == -1;
+  if (y_dtype == HDQ_DTYPE_I32 && (run_fp4 || run_bf16)) return HDQ_ERR_UNSUPPORTED;
+  if (xq == nullptr && x == nullptr) return HDQ_ERR_INVALID;
+  int st;
+  // Weights and activation descriptors for every path that may run.
+  if (run_int8) {
+    if ((st = check_qtensor(w->w_int4, HDQ_FMT_INT4_ROW, N, K)) != HDQ_OK) return st;
+    if (K % 32 != 0 || K % w->w_int4.had_block != 0) return HDQ_ERR_SHAPE;
+    if (xq != nullptr) {
+      if ((st = check_qtensor(*xq, HDQ_FMT_INT8_ROW, M, K)) != HDQ_OK) return st;
+      if (xq->had_block != w->w_int4.had_block) return HDQ_ERR_SHAPE;
+    }
+  }
+  if (run_fp4) {
+    const int32_t f = w->w_fp4.fmt;
+    if (!is_fp4(f)) return HDQ_ERR_UNSUPPORTED;
+    if ((st = check_qtensor(w->w_fp4, f, N, K)) != HDQ_OK) return st;
+    if (K % 32 != 0 || K % w->w_fp4.had_block != 0) return HDQ_ERR_SHAPE;
+    if (xq != nullptr) {
+      if ((st = check_qtensor(*xq, f, M, K)) != HDQ_OK) return st;
+      if (xq->had_block != w->w_fp4.had_block) return HDQ_ERR_SHAPE;
+    }
+  }
+  if (run_bf16) {
+    if (w->w_bf16 == nullptr || x == nullptr) return HDQ_ERR_INVALID;
+    if (K % 8 != 0) return HDQ_ERR_SHAPE;
+  }
+  if (run_int8 && run_fp4 && w->w_int4.had_block != w->w_fp4.had_block) return HDQ_ERR_SHAPE;
+  // Workspace.
+  size_t need = 0;
+  if (xq == nullptr) {
+    if (run_int8) need += qtensor_bytes(M, K, HDQ_FMT_INT8_ROW);
+    if (run_fp4) need += qtensor_bytes(M, K, w->w_fp4.fmt) + (x_amax ? 0 : amax_prepass_bytes());
+  }
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return HDQ_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t* gate = precision == -1 ? decision_dev : nullptr;
+  uint8_t* cursor = static_cast<uint8_t*>(ws);
+  hipError_t e;
+  if (run_int8) {
+    hdq_qtensor q;
+    if (xq != nullptr) {
+      q = *xq;
+    } else {
+      q.fmt = HDQ_FMT_INT8_ROW;
+      q.had_block = w->w_int4.had_block;
+      q.rows = M;
+      q.cols = K;
+      q.codes = cursor;
+      q.row_scale = reinterpret_cast<float*>(cursor + align_up((size_t)(M * K)));
+      q.blk_scale = nullptr;
+      q.tensor_scale = nullptr;
+      cursor += qtensor_bytes(M, K, HDQ_FMT_INT8_ROW);
+      if ((st = check_quant_shape(M, K, q.had_block, q.fmt)) != HDQ_OK) return st;
+      if ((e = enqueue_quantize(x, q, nullptr, nullptr, gate, HDQ_PREC_INT8, s)) != hipSuccess)
+        return HDQ_ERR_HIP;
+    }
+    e = launch_gemm_i8i4(static_cast<const int8_t*>(q.codes), q.row_scale,
+                         static_cast<const uint8_t*>(w->w_int4.codes), w->w_int4.row_scale, y,
+                         y_dtype, M, N, K, gate, HDQ_PREC_INT8, s);
+    if (e != hipSuccess) return HDQ_ERR_HIP;
+  }
+  if (run_fp4) {
+    const int32_t f = w->w_fp4.fmt;
+    hdq_qtensor q;
+    if (xq != nullptr) {
+      q = *xq;
+    } else {
+      q.fmt = f;
+      q.had_block = w->w_fp4.had_block;
+      q.rows = M;
+      q.cols = K;
+      q.codes = cursor;
+      q.blk_scale = cursor + align_up((size_t)(M * K / 2));
+      q.tensor_scale = reinterpret_cast<float*>(q.blk_scale + align_up((size_t)(M * K / 16)));
+      q.row_scale = nullptr;
+      cursor += qtensor_bytes(M, K, f);
+      uint8_t* pre = nullptr;
+      if (x_amax == nullptr) {
+        pre = cursor;
+        cursor += amax_prepass_bytes();
+      }
+      if ((st = check_quant_shape(M, K, q.had_block, q.fmt)) != HDQ_OK) return st;
+      if ((e = enqueue_quantize(x, q, x_amax, pre, gate, HDQ_PREC_NVFP4, s)) != hipSuccess)
+        return HDQ_ERR_HIP;
+    }
+    const uint8_t* xc = static_cast<const uint8_t*>(q.codes);
+    const uint8_t* wc = static_cast<const uint8_t*>(w->w_fp4.codes);
+    if (f == HDQ_FMT_NVFP4_MX)
+      e = launch_gemm_nvfp4_mx(xc, q.blk_scale, q.tensor_scale, wc, w->w_fp4.blk_scale,
+                               w->w_fp4.tensor_scale, y, y_dtype, M, N, K, gate, HDQ_PREC_NVFP4, s);
+    else
+      e = launch_gemm_nvfp4_bf16(xc, q.blk_scale, q.tensor_scale, wc, w->w_fp4.blk_scale,
+                                 w->w_fp4.tensor_scale, y, y_dtype, M, N, K, gate, HDQ_PREC_NVFP4, s);
+    if (e != hipSuccess) return HDQ_ERR_HIP;
+  }
+  if (run_bf16) {
+    e = launch_gemm_bf16(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w->w_bf16), y,
+                         y_dtype, M, N, K, gate, HDQ_PREC_BF16, s);
+    if (e != hipSuccess) return HDQ_ERR_HIP;
+  }
+  return HDQ_OK;
+}
+
+}  // extern "C"

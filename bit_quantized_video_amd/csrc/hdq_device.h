@@ -1,0 +1,150 @@
+// hdq_device.h -- device helpers shared by the gfx950 kernels of libhdq.
+//
+// Rotation, codecs and reductions used by the quantize, statistics and GEMM
+// kernels.  Written for CDNA4 wave64; every helper that talks across lanes
+// assumes all 64 lanes of the wave execute it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hdq {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+
+// Rows whose max |rotated value| is below this quantize to zero codes with a
+// zero scale (below it the reciprocal scales overflow float32).
+constexpr float kTiny = 0x1p-100f;
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// ---- bf16 <-> f32 -------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Eight consecutive bf16 (one 16-byte load) to float.
+__device__ __forceinline__ void bf16x8_to_f32(const uint4 w, float (&x)[8]) {
+  x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x);
+  x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+  x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z);
+  x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+}
+
+// float -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  uint16_t a = __builtin_bit_cast(uint16_t, (__bf16)lo);
+  uint16_t b = __builtin_bit_cast(uint16_t, (__bf16)hi);
+  return (uint32_t)a | ((uint32_t)b << 16);
+}
+
+// ---- cross-lane ---------------------------------------------------------
+// Value held by lane (lane ^ G), G < 32: ds_swizzle in bit-mask mode.
+template <int G>
+__device__ __forceinline__ float xor_lane(float v) {
+  static_assert(G > 0 && G < 32, "swizzle xor mask is 5 bits");
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1F | (G << 10)));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, xor_lane<1>(v));
+  v = fmaxf(v, xor_lane<2>(v));
+  v = fmaxf(v, xor_lane<4>(v));
+  v = fmaxf(v, xor_lane<8>(v));
+  v = fmaxf(v, xor_lane<16>(v));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
+// ---- block Hadamard rotation --------------------------------------------
+// Each lane holds 8 consecutive elements of a row; for a block size hb >= 8
+// the hb/8 lanes (lane & ~(hb/8 - 1)) .. hold one aligned block, for hb < 8
+// each lane holds 8/hb whole blocks.  Fast Walsh-Hadamard butterfly with
+// strides h = 1, 2, 4, ... ascending: the pair (i, i + h), i & h == 0,
+// becomes (u + v, u - v).  Strides 1..4 are inside the lane; stride 8g pairs
+// lane l with lane l ^ g: the lower lane keeps u + v, the upper lane forms
+// u - v as partner + (-own), which IEEE rounds exactly like u - v.  The
+// result is unnormalised (times sqrt(hb)).  hb is wave-uniform.
+template <int H>
+__device__ __forceinline__ void fwht_stage_in(float (&x)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if ((i & H) == 0) {
+      const float u = x[i], v = x[i + H];
+      x[i] = u + v;
+      x[i + H] = u - v;
+    }
+  }
+}
+
+template <int G>
+__device__ __forceinline__ void fwht_stage_x(float (&x)[8], int lane) {
+  const uint32_t flip = (lane & G) ? 0x80000000u : 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    x[i] = xor_lane<G>(x[i]) + __uint_as_float(__float_as_uint(x[i]) ^ flip);
+}
+
+__device__ __forceinline__ void fwht8(float (&x)[8], int lane, int hb) {
+  if (hb >= 2) fwht_stage_in<1>(x);
+  if (hb >= 4) fwht_stage_in<2>(x);
+  if (hb >= 8) fwht_stage_in<4>(x);
+  if (hb >= 16) fwht_stage_x<1>(x, lane);
+  if (hb >= 32) fwht_stage_x<2>(x, lane);
+  if (hb >= 64) fwht_stage_x<4>(x, lane);
+  if (hb >= 128) fwht_stage_x<8>(x, lane);
+}
+
+// ---- FP8 E4M3 block scales (unsigned) -------------------------------------
+// Nearest E4M3 value of t >= 0, ties to even, saturating at 448 (0x7e).
+// v_cvt_pk_fp8_f32 rounds to nearest even for t <= 448 but turns values
+// above 464 into the NaN code, hence the clamp.
+__device__ __forceinline__ uint32_t e4m3_encode(float t) {
+  const float c = fminf(t, 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xffu;
+}
+
+// Value of an unsigned E4M3 byte (0x00..0x7e).
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  const uint32_t e = c >> 3, m = c & 7u;
+  return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+}
+
+// Smallest power of two >= t, clamped to [2^-9, 2^8] (t >= 0).
+__device__ __forceinline__ float pow2_ceil_clamped(float t) {
+  if (!(t > 0x1p-9f)) return 0x1p-9f;
+  if (t >= 256.0f) return 256.0f;
+  const uint32_t u = __float_as_uint(t);
+  if ((u & 0x007fffffu) == 0u) return t;
+  return __uint_as_float((u & 0x7f800000u) + 0x00800000u);
+}
+
+// ---- FP4 E2M1 elements -----------------------------------------------------
+// Two E2M1 codes (nearest, ties to even, saturating at 6, sign bit = sign of
+// the input) in the low byte: a in bits 3:0, b in bits 7:4.
+__device__ __forceinline__ uint32_t e2m1x2_encode(float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0) & 0xffu;
+}
+
+// ---- GEMM tiling ------------------------------------------------------------
+// 64-byte LDS rows: 16-byte chunk c of row r lives at chunk c ^ ((r >> 1) & 3),
+// so a 16-byte fragment read of 8 consecutive rows touches distinct banks.
+__device__ __forceinline__ int lds_off64(int r, int c) { return r * 64 + 16 * (c ^ ((r >> 1) & 3)); }
+
+// Logical tile of this workgroup: contiguous tile ranges per XCD.
+__device__ __forceinline__ void xcd_tile(int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int total = tiles_m * tiles_n;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, local = bid >> 3;
+  const int q = total >> 3, r = total & 7;
+  const int logical = xcd * q + (xcd < r ? xcd : r) + local;
+  tm = logical / tiles_n;
+  tn = logical - tm * tiles_n;
+}
+
+}  // namespace hdq

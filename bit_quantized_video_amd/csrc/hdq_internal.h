@@ -1,0 +1,66 @@
+// hdq_internal.h -- host-side launchers of the libhdq kernels (internal).
+//
+// Each launcher enqueues on `stream` and returns hipGetLastError().  Shapes
+// and pointers are validated by the C-ABI layer (capi.hip) before any
+// launcher runs; the launchers only check what a launch geometry needs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hdq {
+
+enum QFmt : int { kInt8Row = 0, kInt4Row = 1, kNvfp4 = 2, kNvfp4Mx = 3 };
+enum Prec : int { kPrecNvfp4 = 0, kPrecInt8 = 1, kPrecBf16 = 2 };
+enum OutDtype : int { kOutF32 = 0, kOutBf16 = 1, kOutI32 = 2 };
+
+// fl32(1/sqrt(hb)): 2^-k/2 exactly for even log2(hb), otherwise the float
+// nearest 1/sqrt(hb).
+float hadamard_scale(int hb);
+
+// ---- quantize (quant.hip) ----
+// INT8 / INT4 per-row: codes int8 [rows, cols] or packed uint8 [rows, cols/2],
+// row_scale fp32 [rows].
+hipError_t launch_quant_int_rows(const uint16_t* x, int64_t rows, int64_t cols, int hb, int fmt,
+                                 void* codes, float* row_scale, const int32_t* decision,
+                                 int32_t want, hipStream_t s);
+// NVFP4 / NVFP4_MX: codes uint8 [rows, cols/2], blk_scale uint8 [rows, cols/16],
+// tensor_scale fp32 [1]; amax = device fp32[1] rotated tensor amax.
+hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t rows, int64_t cols, int hb, int fmt,
+                              const float* amax, uint8_t* codes, uint8_t* blk_scale,
+                              float* tensor_scale, const int32_t* decision, int32_t want,
+                              hipStream_t s);
+
+// ---- statistics (stats.hip) ----
+constexpr int kStatsMaxBlocks = 1024;
+constexpr size_t kStatsPartialBytes = (size_t)kStatsMaxBlocks * 6 * sizeof(double);
+// Partial sums over prev_in/prev_out (may be null) and cur, then a one-block
+// finalize that writes the five statistics, the decision and/or the rotated
+// amax (any output pointer may be null).
+hipError_t launch_stats(const uint16_t* prev_in, const uint16_t* prev_out, int64_t prev_numel,
+                        const uint16_t* cur, int64_t cur_numel, int hb, float delta_thresh,
+                        float ratio_thresh, int32_t* decision, float* stats, float* amax_out,
+                        double* partials, const int32_t* gate, int32_t want, hipStream_t s);
+
+// ---- GEMMs ----
+// INT8 activations [M, K] x INT4 weights packed [N, K/2]: y = (acc*sx)*sw.
+hipError_t launch_gemm_i8i4(const int8_t* x, const float* sx, const uint8_t* w4, const float* sw,
+                            void* y, int out_dtype, int64_t M, int64_t N, int64_t K,
+                            const int32_t* decision, int32_t want, hipStream_t s);
+// NVFP4 x NVFP4 decoded exactly to bf16 on the fly, bf16 MFMA.
+hipError_t launch_gemm_nvfp4_bf16(const uint8_t* xc, const uint8_t* xs, const float* xts,
+                                  const uint8_t* wc, const uint8_t* ws, const float* wts,
+                                  void* y, int out_dtype, int64_t M, int64_t N, int64_t K,
+                                  const int32_t* decision, int32_t want, hipStream_t s);
+// MX-compatible NVFP4 on the block-scaled FP4 MFMA.
+hipError_t launch_gemm_nvfp4_mx(const uint8_t* xc, const uint8_t* xs, const float* xts,
+                                const uint8_t* wc, const uint8_t* ws, const float* wts,
+                                void* y, int out_dtype, int64_t M, int64_t N, int64_t K,
+                                const int32_t* decision, int32_t want, hipStream_t s);
+// bf16 x bf16 (full-precision fallback).
+hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* w, void* y, int out_dtype,
+                            int64_t M, int64_t N, int64_t K, const int32_t* decision,
+                            int32_t want, hipStream_t s);
+
+}  // namespace hdq

@@ -1,0 +1,297 @@
+// quant.hip -- block-Hadamard rotation fused with quantization (gfx950).
+//
+// The summary of 6Bit-Diffusion (vetunion.cn, section one) rotates each
+// linear layer's activations with a block Hadamard transform to spread
+// outliers before quantizing them to INT8 or NVFP4, and (section four) fuses
+// the transform with the quantizer in one kernel.  Here the rotation never
+// touches memory: a row streams HBM -> registers, is rotated with the
+// in-register / cross-lane butterfly of hdq_device.h, scaled, quantized and
+// written as codes.  Both kernels are HBM-bound (2 B read, 1 or 0.5625 B
+// written per element).
+//
+//  * k_quant_int_rows: INT8 per token (or INT4 per output channel for
+//    weights).  The per-row absmax needs the whole rotated row before the
+//    first code, so one workgroup owns one row and keeps it in registers
+//    (CPT 8-element chunks per thread).
+//  * k_quant_nvfp4: NVFP4 needs only the tensor amax (given) and a 16- or
+//    32-element block max, so it is a flat grid-stride kernel with no
+//    workgroup synchronisation; each wave owns 64 consecutive chunks.
+#include "hdq_device.h"
+#include "hdq_internal.h"
+
+#include <math.h>
+
+namespace hdq {
+
+float hadamard_scale(int hb) { return (float)(1.0 / sqrt((double)hb)); }
+
+// ---------------------------------------------------------------- INT8/INT4
+
+// Packs the low byte of four floats' bit patterns.
+__device__ __forceinline__ uint32_t low_bytes4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);
+  const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x04000c0cu);
+  return ab | cd;
+}
+
+template <int BLOCK, int CPT, bool INT4>
+__global__ __launch_bounds__(BLOCK) void k_quant_int_rows(
+    const uint16_t* __restrict__ x, int64_t cols, int hb, float c_b, void* __restrict__ codes,
+    float* __restrict__ row_scale, const int32_t* __restrict__ decision, int32_t want) {
+  if (decision != nullptr && *decision != want) return;
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int64_t nch = cols >> 3;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + row * cols);
+
+  float v[CPT][8];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int64_t idx = (int64_t)c * BLOCK + tid;
+    uint4 w = make_uint4(0u, 0u, 0u, 0u);
+    if (idx < nch) w = xr[idx];
+    bf16x8_to_f32(w, v[c]);
+  }
+  // Rotate: whole Hadamard blocks sit in aligned lane groups (BLOCK is a
+  // multiple of 16 lanes), and a chunk index past the row end only ever
+  // meets zero-filled partners.
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    fwht8(v[c], lane, hb);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[c][i] = v[c][i] * c_b;
+      amax = fmaxf(amax, fabsf(v[c][i]));
+    }
+  }
+  amax = wave_max(amax);
+  if constexpr (BLOCK > 64) {
+    __shared__ float red[BLOCK / 64];
+    if (lane == 0) red[tid >> 6] = amax;
+    __syncthreads();
+    amax = red[0];
+#pragma unroll
+    for (int w = 1; w < BLOCK / 64; ++w) amax = fmaxf(amax, red[w]);
+  }
+  constexpr float QMAX = INT4 ? 7.0f : 127.0f;
+  float inv = 0.0f, s = 0.0f;
+  if (amax >= kTiny) {
+    s = amax / QMAX;
+    inv = QMAX / amax;
+  }
+  if (tid == 0) row_scale[row] = s;
+
+  // q = round_half_even(y * inv): adding 1.5 * 2^23 rounds to an integer
+  // (the add rounds to nearest even) and leaves it, two's complement, in the
+  // low mantissa bits.  |y * inv| <= 127.00001 (7.000001), so no clamp can
+  // trigger.
+  const float kMagic = 12582912.0f;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int64_t idx = (int64_t)c * BLOCK + tid;
+    if (idx < nch) {
+      uint32_t b[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) b[i] = __float_as_uint(v[c][i] * inv + kMagic);
+      if constexpr (INT4) {
+        uint32_t p = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p |= (b[i] & 0xfu) << (4 * i);
+        reinterpret_cast<uint32_t*>(codes)[row * (cols >> 3) + idx] = p;
+      } else {
+        uint2 p;
+        p.x = low_bytes4(b[0], b[1], b[2], b[3]);
+        p.y = low_bytes4(b[4], b[5], b[6], b[7]);
+        reinterpret_cast<uint2*>(codes)[row * (cols >> 3) + idx] = p;
+      }
+    }
+  }
+}
+
+template <int BLOCK, int CPT>
+static hipError_t launch_int_rows_t(const uint16_t* x, int64_t rows, int64_t cols, int hb,
+                                    bool int4, void* codes, float* sc, const int32_t* dec,
+                                    int32_t want, hipStream_t s) {
+  const float c_b = hadamard_scale(hb);
+  if (int4)
+    hipLaunchKernelGGL((k_quant_int_rows<BLOCK, CPT, true>), dim3((unsigned)rows), dim3(BLOCK), 0,
+                       s, x, cols, hb, c_b, codes, sc, dec, want);
+  else
+    hipLaunchKernelGGL((k_quant_int_rows<BLOCK, CPT, false>), dim3((unsigned)rows), dim3(BLOCK), 0,
+                       s, x, cols, hb, c_b, codes, sc, dec, want);
+  return hipGetLastError();
+}
+
+// Two-pass variant for rows too long to keep in registers: pass one finds
+// the rotated absmax, pass two re-reads the row (from L2) and quantizes.
+template <bool INT4>
+__global__ __launch_bounds__(256) void k_quant_int_rows_long(
+    const uint16_t* __restrict__ x, int64_t cols, int hb, float c_b, void* __restrict__ codes,
+    float* __restrict__ row_scale, const int32_t* __restrict__ decision, int32_t want) {
+  if (decision != nullptr && *decision != want) return;
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t nch = cols >> 3;
+  const uint4* xr = reinterpret_cast<const uint4*>(x + row * cols);
+  float amax = 0.0f;
+  for (int64_t base = 0; base < nch; base += 256) {
+    const int64_t idx = base + tid;
+    float v[8];
+    uint4 w = make_uint4(0u, 0u, 0u, 0u);
+    if (idx < nch) w = xr[idx];
+    bf16x8_to_f32(w, v);
+    fwht8(v, lane, hb);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i] * c_b));
+  }
+  amax = wave_max(amax);
+  __shared__ float red[4];
+  if (lane == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  constexpr float QMAX = INT4 ? 7.0f : 127.0f;
+  float inv = 0.0f, s = 0.0f;
+  if (amax >= kTiny) {
+    s = amax / QMAX;
+    inv = QMAX / amax;
+  }
+  if (tid == 0) row_scale[row] = s;
+  const float kMagic = 12582912.0f;
+  for (int64_t base = 0; base < nch; base += 256) {
+    const int64_t idx = base + tid;
+    float v[8];
+    uint4 w = make_uint4(0u, 0u, 0u, 0u);
+    if (idx < nch) w = xr[idx];
+    bf16x8_to_f32(w, v);
+    fwht8(v, lane, hb);
+    if (idx < nch) {
+      uint32_t b[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) b[i] = __float_as_uint((v[i] * c_b) * inv + kMagic);
+      if constexpr (INT4) {
+        uint32_t p = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p |= (b[i] & 0xfu) << (4 * i);
+        reinterpret_cast<uint32_t*>(codes)[row * nch + idx] = p;
+      } else {
+        uint2 p;
+        p.x = low_bytes4(b[0], b[1], b[2], b[3]);
+        p.y = low_bytes4(b[4], b[5], b[6], b[7]);
+        reinterpret_cast<uint2*>(codes)[row * nch + idx] = p;
+      }
+    }
+  }
+}
+
+hipError_t launch_quant_int_rows(const uint16_t* x, int64_t rows, int64_t cols, int hb, int fmt,
+                                 void* codes, float* row_scale, const int32_t* decision,
+                                 int32_t want, hipStream_t s) {
+  const bool int4 = (fmt == kInt4Row);
+  const int64_t nch = cols >> 3;
+  // Workgroup = 64 threads for short rows, 256 otherwise; each thread keeps
+  // CPT chunks of 8 elements of its row in registers.
+  if (nch <= 64) return launch_int_rows_t<64, 1>(x, rows, cols, hb, int4, codes, row_scale, decision, want, s);
+  if (nch <= 128) return launch_int_rows_t<64, 2>(x, rows, cols, hb, int4, codes, row_scale, decision, want, s);
+  if (nch <= 256) return launch_int_rows_t<64, 4>(x, rows, cols, hb, int4, codes, row_scale, decision, want, s);
+  if (nch <= 384) return launch_int_rows_t<128, 3>(x, rows, cols, hb, int4, codes, row_scale, decision, want, s);
+  if (nch <= 512) return launch_int_rows_t<256, 2>(x, rows, cols, hb, int4, codes, row_scale, decision, want, s);
+  if (nch <= 768) return launch_int_rows_t<256, 3>(x, rows, cols, hb, int4, codes, row_scale, decision, want, s);
+  if (nch <= 1024) return launch_int_rows_t<256, 4>(x, rows, cols, hb, int4, codes, row_scale, decision, want, s);
+  if (nch <= 1536) return launch_int_rows_t<256, 6>(x, rows, cols, hb, int4, codes, row_scale, decision, want, s);
+  if (nch <= 2048) return launch_int_rows_t<256, 8>(x, rows, cols, hb, int4, codes, row_scale, decision, want, s);
+  const float c_b = hadamard_scale(hb);
+  if (int4)
+    hipLaunchKernelGGL(k_quant_int_rows_long<true>, dim3((unsigned)rows), dim3(256), 0, s, x, cols,
+                       hb, c_b, codes, row_scale, decision, want);
+  else
+    hipLaunchKernelGGL(k_quant_int_rows_long<false>, dim3((unsigned)rows), dim3(256), 0, s, x,
+                       cols, hb, c_b, codes, row_scale, decision, want);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- NVFP4
+
+// One 8-element chunk per lane per iteration; a wave covers 64 consecutive
+// chunks (512 elements), so every Hadamard block (<= 128) and every 16- or
+// 32-element scale block lies inside aligned lane groups of one wave.
+template <bool MX>
+__global__ __launch_bounds__(256) void k_quant_nvfp4(
+    const uint16_t* __restrict__ x, int64_t nch, int hb, float c_b,
+    const float* __restrict__ amax_ptr, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ blk_scale, float* __restrict__ tensor_scale,
+    const int32_t* __restrict__ decision, int32_t want) {
+  if (decision != nullptr && *decision != want) return;
+  const int lane = threadIdx.x & 63;
+  const float A = *amax_ptr;
+  // s_t = amax / (6 * 448) for NVFP4 (the largest block maps to E4M3's top
+  // value), amax / (6 * 256) for the MX-compatible variant (the largest
+  // power-of-two block scale is 2^8).
+  const float s_t = (A >= kTiny) ? A / (MX ? 1536.0f : 2688.0f) : 0.0f;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = s_t;
+  const float six_st = 6.0f * s_t;
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  uint32_t* cv = reinterpret_cast<uint32_t*>(codes);
+
+  for (int64_t base = wave * 64; base < nch; base += nwaves * 64) {
+    const int64_t idx = base + lane;
+    const bool ok = idx < nch;
+    float v[8];
+    uint4 w = make_uint4(0u, 0u, 0u, 0u);
+    if (ok) w = xv[idx];
+    bf16x8_to_f32(w, v);
+    fwht8(v, lane, hb);
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[i] = v[i] * c_b;
+      a = fmaxf(a, fabsf(v[i]));
+    }
+    a = fmaxf(a, xor_lane<1>(a));        // 16-element block = lane pair
+    if constexpr (MX) a = fmaxf(a, xor_lane<2>(a));   // 32-element group
+    uint32_t e = 0u;
+    float d = 0.0f;
+    if (s_t > 0.0f) {
+      const float t = a / six_st;
+      e = MX ? e4m3_encode(pow2_ceil_clamped(t)) : e4m3_encode(t);
+      d = e4m3_decode(e) * s_t;
+    }
+    uint32_t packed = 0u;
+    if (d != 0.0f) {
+      const float inv = 1.0f / d;
+      packed = e2m1x2_encode(v[0] * inv, v[1] * inv) | (e2m1x2_encode(v[2] * inv, v[3] * inv) << 8) |
+               (e2m1x2_encode(v[4] * inv, v[5] * inv) << 16) |
+               (e2m1x2_encode(v[6] * inv, v[7] * inv) << 24);
+    }
+    if (ok) {
+      cv[idx] = packed;
+      if ((lane & 1) == 0) blk_scale[idx >> 1] = (uint8_t)e;
+    }
+  }
+}
+
+hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t rows, int64_t cols, int hb, int fmt,
+                              const float* amax, uint8_t* codes, uint8_t* blk_scale,
+                              float* tensor_scale, const int32_t* decision, int32_t want,
+                              hipStream_t s) {
+  const int64_t nch = rows * cols / 8;
+  const int64_t waves_needed = (nch + 63) / 64;
+  // 8 waves per CU x 256 CUs of 4-wave workgroups keeps enough loads in
+  // flight; a grid-stride loop covers the rest.
+  int64_t blocks = (waves_needed + 3) / 4;
+  if (blocks > 2048) blocks = 2048;
+  if (blocks < 1) blocks = 1;
+  const float c_b = hadamard_scale(hb);
+  if (fmt == kNvfp4Mx)
+    hipLaunchKernelGGL(k_quant_nvfp4<true>, dim3((unsigned)blocks), dim3(256), 0, s, x, nch, hb, c_b,
+                       amax, codes, blk_scale, tensor_scale, decision, want);
+  else
+    hipLaunchKernelGGL(k_quant_nvfp4<false>, dim3((unsigned)blocks), dim3(256), 0, s, x, nch, hb,
+                       c_b, amax, codes, blk_scale, tensor_scale, decision, want);
+  return hipGetLastError();
+}
+
+}  // namespace hdq

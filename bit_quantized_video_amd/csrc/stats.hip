@@ -1,0 +1,229 @@
+// stats.hip -- selection statistics and the precision decision (gfx950).
+//
+// The summary of 6Bit-Diffusion (vetunion.cn) picks each module's precision
+// per step from the difference between its input and output at the previous
+// step (section one: large -> INT8, small -> NVFP4), falls back to full
+// precision when the input's outlier ratio max/mean is too large (section
+// three, purified delta refresh), and uses INT8 when no previous-step
+// difference exists (section three, last paragraph).  The explainer on
+// gist.science restates both rules (sections 2 and 4).
+//
+// One streaming pass reads prev_in, prev_out and cur (6 bytes per element,
+// HBM-bound) and writes per-workgroup partials; a one-workgroup finalize
+// reduces them in a fixed order in double, so the statistics and the
+// decision are deterministic.  The same pass yields the rotated amax that
+// NVFP4's tensor scale needs, so the quantizer never reads its input twice.
+#include "hdq_device.h"
+#include "hdq_internal.h"
+
+#include <math.h>
+
+namespace hdq {
+
+// Partial slots per workgroup.
+enum { P_DIFF = 0, P_BASE = 1, P_SUMABS = 2, P_MAXBITS = 3, P_ROTMAX = 4, P_COUNT = 6 };
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+
+__global__ __launch_bounds__(256) void k_stats_partial(
+    const uint16_t* __restrict__ prev_in, const uint16_t* __restrict__ prev_out, int64_t n_prev,
+    const uint16_t* __restrict__ cur, int64_t n_cur, int hb, double* __restrict__ part,
+    const int32_t* __restrict__ gate, int32_t want) {
+  if (gate != nullptr && *gate != want) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t gtid = (int64_t)blockIdx.x * 256 + tid;
+  const int64_t gthreads = (int64_t)gridDim.x * 256;
+
+  // --- relative L1 difference of the previous step's input and output.
+  // float32 sums over each 8-element chunk, double across chunks.
+  double diff = 0.0, base = 0.0;
+  if (prev_in != nullptr) {
+    const int64_t nch = n_prev >> 3;
+    const uint4* a4 = reinterpret_cast<const uint4*>(prev_in);
+    const uint4* o4 = reinterpret_cast<const uint4*>(prev_out);
+    for (int64_t j = gtid; j < nch; j += gthreads) {
+      float a[8], o[8];
+      bf16x8_to_f32(a4[j], a);
+      bf16x8_to_f32(o4[j], o);
+      float d8 = 0.0f, b8 = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        d8 += fabsf(o[i] - a[i]);
+        b8 += fabsf(a[i]);
+      }
+      diff += d8;
+      base += b8;
+    }
+    const int64_t tail = n_prev - (nch << 3);
+    if (gtid < tail) {
+      const float a = bf16_lo(prev_in[(nch << 3) + gtid]);
+      const float o = bf16_lo(prev_out[(nch << 3) + gtid]);
+      diff += fabsf(o - a);
+      base += fabsf(a);
+    }
+  }
+
+  // --- current input: max |x| (on the bf16 bit patterns: for finite values
+  // the order of |x| is the order of (bits & 0x7fff), and a pattern >= 0x7f80
+  // flags an infinity or NaN), sum |x|, and max |rotated x| (unnormalised).
+  uint32_t maxbits = 0u;
+  double sumabs = 0.0;
+  float rotmax = 0.0f;
+  {
+    const int64_t nch = n_cur >> 3;
+    const uint4* c4 = reinterpret_cast<const uint4*>(cur);
+    const int64_t wave = gtid >> 6, nwaves = gthreads >> 6;
+    for (int64_t b0 = wave * 64; b0 < nch; b0 += nwaves * 64) {
+      const int64_t j = b0 + lane;
+      uint4 w = make_uint4(0u, 0u, 0u, 0u);
+      if (j < nch) w = c4[j];
+      const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        maxbits = max(maxbits, wd[q] & 0x7fffu);
+        maxbits = max(maxbits, (wd[q] >> 16) & 0x7fffu);
+      }
+      float v[8];
+      bf16x8_to_f32(w, v);
+      float s8 = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s8 += fabsf(v[i]);
+      sumabs += s8;
+      if (hb > 0) {
+        fwht8(v, lane, hb);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) rotmax = fmaxf(rotmax, fabsf(v[i]));
+      }
+    }
+    const int64_t tail = n_cur - (nch << 3);
+    if (gtid < tail) {  // only reachable without rotation (cols % 8 != 0)
+      const uint32_t bits = cur[(nch << 3) + gtid];
+      maxbits = max(maxbits, bits & 0x7fffu);
+      sumabs += fabsf(bf16_lo(bits));
+    }
+  }
+
+  // --- fixed-order workgroup reduction.
+  __shared__ double red[4][5];
+  diff = wave_sum_d(diff);
+  base = wave_sum_d(base);
+  sumabs = wave_sum_d(sumabs);
+  maxbits = wave_max_u(maxbits);
+  const float rm = wave_max(rotmax);
+  if (lane == 0) {
+    red[tid >> 6][0] = diff;
+    red[tid >> 6][1] = base;
+    red[tid >> 6][2] = sumabs;
+    red[tid >> 6][3] = (double)maxbits;
+    red[tid >> 6][4] = (double)rm;
+  }
+  __syncthreads();
+  if (tid < 5) {
+    double r = red[0][tid];
+    for (int w = 1; w < 4; ++w) r = (tid == 3 || tid == 4) ? fmax(r, red[w][tid]) : r + red[w][tid];
+    part[(int64_t)blockIdx.x * P_COUNT + tid] = r;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_stats_final(
+    const double* __restrict__ part, int nparts, int64_t n_cur, int has_history, float c_b,
+    float delta_thresh, float ratio_thresh, int32_t* __restrict__ decision,
+    float* __restrict__ stats, float* __restrict__ amax_out, const int32_t* __restrict__ gate,
+    int32_t want) {
+  if (gate != nullptr && *gate != want) return;
+  const int tid = threadIdx.x;
+  double acc[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
+  for (int p = tid; p < nparts; p += 256) {
+    acc[0] += part[p * P_COUNT + 0];
+    acc[1] += part[p * P_COUNT + 1];
+    acc[2] += part[p * P_COUNT + 2];
+    acc[3] = fmax(acc[3], part[p * P_COUNT + 3]);
+    acc[4] = fmax(acc[4], part[p * P_COUNT + 4]);
+  }
+  __shared__ double red[256][5];
+#pragma unroll
+  for (int q = 0; q < 5; ++q) red[tid][q] = acc[q];
+  __syncthreads();
+  for (int s = 128; s >= 1; s >>= 1) {
+    if (tid < s) {
+      red[tid][0] += red[tid + s][0];
+      red[tid][1] += red[tid + s][1];
+      red[tid][2] += red[tid + s][2];
+      red[tid][3] = fmax(red[tid][3], red[tid + s][3]);
+      red[tid][4] = fmax(red[tid][4], red[tid + s][4]);
+    }
+    __syncthreads();
+  }
+  if (tid != 0) return;
+  const double diff = red[0][0], base = red[0][1], sumabs = red[0][2];
+  const uint32_t maxbits = (uint32_t)red[0][3];
+  const bool nonfinite = maxbits >= 0x7f80u;
+  const double maxabs = (double)bf16_lo(maxbits);
+  double delta;
+  if (!has_history)
+    delta = __builtin_nan("");
+  else if (base == 0.0)
+    delta = (diff == 0.0) ? 0.0 : __builtin_inf();
+  else
+    delta = diff / base;
+  const double mean = sumabs / (double)n_cur;
+  double ratio;
+  if (nonfinite)
+    ratio = __builtin_nan("");
+  else
+    ratio = (sumabs == 0.0) ? 0.0 : maxabs / mean;
+  // max over fl32(|t| * c_b) equals fl32(max |t| * c_b): rounding is monotone.
+  const float rot_amax = nonfinite ? 0.0f : (float)red[0][4] * c_b;
+  if (stats != nullptr) {
+    stats[0] = (float)delta;
+    stats[1] = (float)ratio;
+    stats[2] = (float)maxabs;
+    stats[3] = (float)mean;
+    stats[4] = rot_amax;
+  }
+  if (amax_out != nullptr) *amax_out = rot_amax;
+  if (decision != nullptr) {
+    int32_t d;
+    if (!(ratio <= (double)ratio_thresh))
+      d = kPrecBf16;  // purified delta refresh: outliers -> full precision
+    else if (!has_history)
+      d = kPrecInt8;  // no previous-step difference -> INT8
+    else if (!(delta < (double)delta_thresh))
+      d = kPrecInt8;  // large previous-step difference -> INT8
+    else
+      d = kPrecNvfp4;
+    *decision = d;
+  }
+}
+
+hipError_t launch_stats(const uint16_t* prev_in, const uint16_t* prev_out, int64_t prev_numel,
+                        const uint16_t* cur, int64_t cur_numel, int hb, float delta_thresh,
+                        float ratio_thresh, int32_t* decision, float* stats, float* amax_out,
+                        double* partials, const int32_t* gate, int32_t want, hipStream_t s) {
+  const int64_t work = (prev_numel > cur_numel ? prev_numel : cur_numel) / 8;
+  int64_t blocks = (work + 255) / 256;
+  if (blocks > kStatsMaxBlocks) blocks = kStatsMaxBlocks;
+  if (blocks < 1) blocks = 1;
+  const bool hist = prev_in != nullptr && prev_out != nullptr;
+  hipLaunchKernelGGL(k_stats_partial, dim3((unsigned)blocks), dim3(256), 0, s,
+                     hist ? prev_in : nullptr, hist ? prev_out : nullptr, hist ? prev_numel : 0,
+                     cur, cur_numel, hb, partials, gate, want);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const float c_b = hb > 0 ? hadamard_scale(hb) : 0.0f;
+  hipLaunchKernelGGL(k_stats_final, dim3(1), dim3(256), 0, s, partials, (int)blocks, cur_numel,
+                     hist ? 1 : 0, c_b, delta_thresh, ratio_thresh, decision, stats, amax_out,
+                     gate, want);
+  return hipGetLastError();
+}
+
+}  // namespace hdq

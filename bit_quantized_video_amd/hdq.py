@@ -1,0 +1,216 @@
+"""Thin Python binding of libhdq (C ABI in include/hdq.h).
+
+Argument marshalling only: torch provides device memory and the current
+stream; every step of the path runs in libhdq's HIP kernels.  The names
+follow the C entry points: select_precision, quantize, linear.  Importing
+this module loads libhdq.so and raises if it is missing (build it with
+__graft_entry__.build() or `python bit_quantized_video_amd/build.py`); there
+is no CPU fallback.
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhdq.so")
+
+# status codes
+OK, ERR_INVALID, ERR_SHAPE, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, -1, -2, -3, -4, -5
+# formats
+FMT_INT8_ROW, FMT_INT4_ROW, FMT_NVFP4, FMT_NVFP4_MX = 0, 1, 2, 3
+# precisions
+PREC_NVFP4, PREC_INT8, PREC_BF16 = 0, 1, 2
+# output dtypes
+DTYPE_F32, DTYPE_BF16, DTYPE_I32 = 0, 1, 2
+# workspace ops
+OP_SELECT, OP_QUANTIZE, OP_LINEAR = 0, 1, 2
+
+EXPORTS = ("hdq_select_precision", "hdq_quantize", "hdq_linear", "hdq_workspace_bytes",
+           "hdq_status_string", "hdq_version")
+
+_c = ctypes
+_p = _c.c_void_p
+
+
+class QTensorDesc(_c.Structure):
+    """hdq_qtensor."""
+    _fields_ = [("fmt", _c.c_int32), ("had_block", _c.c_int32), ("rows", _c.c_int64),
+                ("cols", _c.c_int64), ("codes", _p), ("row_scale", _p), ("blk_scale", _p),
+                ("tensor_scale", _p)]
+
+
+class WeightsDesc(_c.Structure):
+    """hdq_weights."""
+    _fields_ = [("N", _c.c_int64), ("K", _c.c_int64), ("w_bf16", _p), ("w_int4", QTensorDesc),
+                ("w_fp4", QTensorDesc)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libhdq.so is not built ({LIB_PATH}); run __graft_entry__.build()")
+    L = _c.CDLL(LIB_PATH)
+    L.hdq_select_precision.restype = _c.c_int
+    L.hdq_select_precision.argtypes = [_p, _p, _c.c_int64, _p, _c.c_int64, _c.c_int64, _c.c_int32,
+                                       _c.c_float, _c.c_float, _p, _p, _p, _c.c_size_t, _p]
+    L.hdq_quantize.restype = _c.c_int
+    L.hdq_quantize.argtypes = [_p, _c.c_int64, _c.c_int64, _c.c_int32, _c.c_int32, _p,
+                               _c.POINTER(QTensorDesc), _p, _c.c_size_t, _p]
+    L.hdq_linear.restype = _c.c_int
+    L.hdq_linear.argtypes = [_c.c_int32, _p, _p, _c.POINTER(QTensorDesc), _p, _c.c_int64,
+                             _c.c_int64, _c.POINTER(WeightsDesc), _p, _c.c_int32, _p,
+                             _c.c_size_t, _p]
+    L.hdq_workspace_bytes.restype = _c.c_size_t
+    L.hdq_workspace_bytes.argtypes = [_c.c_int32, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int32]
+    L.hdq_status_string.restype = _c.c_char_p
+    L.hdq_status_string.argtypes = [_c.c_int]
+    L.hdq_version.restype = _c.c_int
+    L.hdq_version.argtypes = []
+    return L
+
+
+lib = _load()
+
+
+class HdqError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn}: {lib.hdq_status_string(status).decode()} ({status})")
+
+
+def _check(fn, status):
+    if status != OK:
+        raise HdqError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else _p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return _p(s.cuda_stream)
+
+
+def _bf16(t, name):
+    if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous bfloat16 CUDA tensor")
+    return t
+
+
+def workspace_bytes(op, M, K, N=0, fmt=-1):
+    return int(lib.hdq_workspace_bytes(op, M, K, N, fmt))
+
+
+def _workspace(ws, nbytes, device):
+    if nbytes == 0:
+        return ws
+    if ws is None or ws.numel() < nbytes:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws
+
+
+class QuantizedTensor:
+    """A quantized tensor: torch buffers plus the hdq_qtensor descriptor."""
+
+    def __init__(self, fmt, rows, cols, had_block, device):
+        self.fmt, self.rows, self.cols, self.had_block = fmt, rows, cols, had_block
+        self.row_scale = self.blk_scale = self.tensor_scale = None
+        if fmt == FMT_INT8_ROW:
+            self.codes = torch.empty(rows, cols, dtype=torch.int8, device=device)
+        else:
+            self.codes = torch.empty(rows, cols // 2, dtype=torch.uint8, device=device)
+        if fmt in (FMT_INT8_ROW, FMT_INT4_ROW):
+            self.row_scale = torch.empty(rows, dtype=torch.float32, device=device)
+        else:
+            self.blk_scale = torch.empty(rows, cols // 16, dtype=torch.uint8, device=device)
+            self.tensor_scale = torch.empty(1, dtype=torch.float32, device=device)
+
+    def desc(self):
+        return QTensorDesc(self.fmt, self.had_block, self.rows, self.cols, _ptr(self.codes),
+                           _ptr(self.row_scale), _ptr(self.blk_scale), _ptr(self.tensor_scale))
+
+
+def select_precision(prev_in, prev_out, cur_in, had_block=0, delta_thresh=0.1, ratio_thresh=50.0,
+                     decision=None, stats=None, ws=None, stream=None):
+    """hdq_select_precision.  prev_in/prev_out None = no history.  Returns the
+    device tensors (decision int32[1], stats float32[5])."""
+    cur_in = _bf16(cur_in, "cur_in")
+    rows, cols = cur_in.shape
+    dev = cur_in.device
+    if (prev_in is None) != (prev_out is None):
+        raise ValueError("prev_in and prev_out must both be given or both be None")
+    n_prev = 0
+    if prev_in is not None:
+        _bf16(prev_in, "prev_in")
+        _bf16(prev_out, "prev_out")
+        if prev_in.numel() != prev_out.numel():
+            raise ValueError("prev_in and prev_out differ in size")
+        n_prev = prev_in.numel()
+    decision = torch.empty(1, dtype=torch.int32, device=dev) if decision is None else decision
+    stats = torch.empty(5, dtype=torch.float32, device=dev) if stats is None else stats
+    ws = _workspace(ws, workspace_bytes(OP_SELECT, rows, cols, n_prev), dev)
+    st = lib.hdq_select_precision(_ptr(prev_in), _ptr(prev_out), n_prev, _ptr(cur_in), rows, cols,
+                                  had_block, delta_thresh, ratio_thresh, _ptr(decision),
+                                  _ptr(stats), _ptr(ws), ws.numel(), _stream(stream))
+    _check("hdq_select_precision", st)
+    return decision, stats
+
+
+def quantize(x, had_block, fmt, tensor_amax=None, out=None, ws=None, stream=None):
+    """hdq_quantize: rotate + quantize a bf16 [rows, cols] tensor."""
+    x = _bf16(x, "x")
+    rows, cols = x.shape
+    out = QuantizedTensor(fmt, rows, cols, had_block, x.device) if out is None else out
+    d = out.desc()
+    nbytes = workspace_bytes(OP_QUANTIZE, rows, cols, 0, fmt) if tensor_amax is None else 0
+    ws = _workspace(ws, nbytes, x.device)
+    st = lib.hdq_quantize(_ptr(x), rows, cols, had_block, fmt, _ptr(tensor_amax), _c.byref(d),
+                          _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    _check("hdq_quantize", st)
+    return out
+
+
+class LinearWeights:
+    """A linear layer's weights in every form a precision may need:
+    bf16 (unrotated, for the full-precision fallback), INT4 per output
+    channel, and NVFP4 (or its MX-compatible variant)."""
+
+    def __init__(self, w_bf16, had_block, fp4_fmt=FMT_NVFP4, keep_bf16=True, stream=None):
+        w_bf16 = _bf16(w_bf16, "w")
+        self.N, self.K = w_bf16.shape
+        self.had_block = had_block
+        self.w_bf16 = w_bf16 if keep_bf16 else None
+        self.w_int4 = quantize(w_bf16, had_block, FMT_INT4_ROW, stream=stream)
+        self.w_fp4 = quantize(w_bf16, had_block, fp4_fmt, stream=stream) if fp4_fmt is not None else None
+
+    def desc(self):
+        empty = QTensorDesc(-1, 0, 0, 0, None, None, None, None)
+        return WeightsDesc(self.N, self.K, _ptr(self.w_bf16), self.w_int4.desc(),
+                           self.w_fp4.desc() if self.w_fp4 is not None else empty)
+
+
+def linear(precision, x, w, decision=None, xq=None, x_amax=None, y=None, y_dtype=DTYPE_BF16,
+           ws=None, stream=None):
+    """hdq_linear: Y[M, N] = quantized X[M, K] @ W^T.  precision -1 reads the
+    decision tensor on the device."""
+    if x is not None:
+        x = _bf16(x, "x")
+        M, K = x.shape
+        dev = x.device
+    else:
+        M, K = xq.rows, xq.cols
+        dev = xq.codes.device
+    if y is None:
+        dt = {DTYPE_F32: torch.float32, DTYPE_BF16: torch.bfloat16, DTYPE_I32: torch.int32}[y_dtype]
+        y = torch.empty(M, w.N, dtype=dt, device=dev)
+    wd = w.desc()
+    fp4_fmt = w.w_fp4.fmt if w.w_fp4 is not None else -1
+    nbytes = 0 if xq is not None else workspace_bytes(OP_LINEAR, M, K, w.N, fp4_fmt)
+    ws = _workspace(ws, nbytes, dev)
+    xqd = xq.desc() if xq is not None else None
+    st = lib.hdq_linear(precision, _ptr(decision), _ptr(x), _c.byref(xqd) if xqd is not None else None,
+                        _ptr(x_amax), M, K, _c.byref(wd), _ptr(y), y_dtype, _ptr(ws),
+                        0 if ws is None else ws.numel(), _stream(stream))
+    _check("hdq_linear", st)
+    return y

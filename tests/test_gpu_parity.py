@@ -1,0 +1,434 @@
+"""GPU <-> oracle parity through the C ABI (libhdq via its Python binding).
+
+Bars (per the method's numerics):
+  * quantized codes and scales: bit-exact (a +-1 LSB at a rounding tie is
+    tolerated on <= 1e-5 of the elements; none is expected, both sides round
+    the same float32 values);
+  * integer GEMM on identical codes: bit-exact int32;
+  * INT8 linear outputs: bit-exact (same float32 epilogue order), and in any
+    case relative Frobenius error <= 1e-3 against the oracle's output rounded
+    to the output dtype;
+  * NVFP4 / bf16 linear outputs: relative Frobenius <= 1e-3 against the
+    oracle's double result rounded to the output dtype (only the float32
+    accumulation order differs);
+  * decisions equal unless the oracle's statistic is within 1e-5 (relative)
+    of a threshold.
+Sizes span several tiles and ragged tails; full CogVideoX-shaped configs are
+checked on sampled rows/columns the oracle computes one by one.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from bit_quantized_video_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from bit_quantized_video_amd import hdq  # noqa: E402  (loads libhdq.so; fails loudly if missing)
+
+DEV = torch.device("cuda:0")
+REL_TOL = 1e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(x16):
+    return torch.from_numpy(np.ascontiguousarray(x16).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def bf16_to_np(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def f32_from_bf16_np(x16):
+    return synth.bf16_bits_to_f32(x16)
+
+
+def rel_fro(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.linalg.norm(ref)
+    return np.linalg.norm(got - ref) / (den if den > 0 else 1.0)
+
+
+def round_like(ref64, y_dtype):
+    if y_dtype == hdq.DTYPE_BF16:
+        return f32_from_bf16_np(O.f32_to_bf16(ref64.astype(np.float32))).astype(np.float64)
+    return ref64.astype(np.float32).astype(np.float64)
+
+
+def y_np(y):
+    if y.dtype == torch.bfloat16:
+        return f32_from_bf16_np(bf16_to_np(y)).astype(np.float64)
+    return y.cpu().numpy().astype(np.float64)
+
+
+def sample_rows(M, head=64, tail=48):
+    if M <= head + tail:
+        return np.arange(M)
+    return np.concatenate([np.arange(head), np.arange(M - tail, M)])
+
+
+def assert_codes_equal(got, ref, what):
+    got = np.asarray(got)
+    ref = np.asarray(ref)
+    assert got.shape == ref.shape, what
+    diff = got != ref
+    n = int(diff.sum())
+    if n:
+        frac = n / got.size
+        # tolerated: <= 1e-5 of the elements off by one LSB
+        d = np.abs(got.astype(np.int64) - ref.astype(np.int64))[diff]
+        assert frac <= 1e-5 and d.max() <= 1, f"{what}: {n} mismatches ({frac:.2e}), max diff {d.max()}"
+
+
+def nvfp4_codes_equal(got, ref, what):
+    """Packed E2M1 bytes equal, with +0 and -0 codes taken as equal."""
+    g = np.stack([got & 0xF, got >> 4], -1)
+    r = np.stack([ref & 0xF, ref >> 4], -1)
+    g = np.where((g & 7) == 0, 0, g)
+    r = np.where((r & 7) == 0, 0, r)
+    assert_codes_equal(g, r, what)
+
+
+# ------------------------------------------------------------ quantizers
+
+INT_CASES = [(1, 64, 16), (37, 128, 32), (130, 1024, 64), (300, 1920, 128), (9, 3072, 128),
+             (5, 12288, 128), (3, 20480, 128), (17, 64, 2), (17, 64, 4), (17, 64, 8)]
+
+
+@pytest.mark.parametrize("M,K,hb", INT_CASES)
+@pytest.mark.parametrize("fmt", ["int8", "int4"])
+def test_quantize_int_rows_bitexact(M, K, hb, fmt):
+    say(f"quantize {fmt} M={M} K={K} hb={hb}")
+    x16 = synth.gaussian_outliers(M, K, 0.01, 25.0, synth.rng_for(100, M * 7 + K))
+    qmax = 127 if fmt == "int8" else 7
+    f = hdq.FMT_INT8_ROW if fmt == "int8" else hdq.FMT_INT4_ROW
+    q = hdq.quantize(to_dev(x16), hb, f)
+    torch.cuda.synchronize()
+    rq, rs = O.quant_int(x16, hb, qmax)
+    assert np.array_equal(q.row_scale.cpu().numpy(), rs), "row scales"
+    if fmt == "int8":
+        assert_codes_equal(q.codes.cpu().numpy(), rq, "int8 codes")
+    else:
+        assert_codes_equal(q.codes.cpu().numpy(), O.pack_int4(rq), "int4 bytes")
+
+
+def test_quantize_int_zero_and_tiny_rows():
+    x = np.zeros((4, 256), np.float32)
+    x[1, 7] = 2.0 ** -110            # below the zero-row threshold
+    x[2, :] = 3.0
+    x[3, 5] = -1e-20
+    x16 = synth.to_bf16_bits(x)
+    q = hdq.quantize(to_dev(x16), 64, hdq.FMT_INT8_ROW)
+    rq, rs = O.quant_int(x16, 64, 127)
+    assert np.array_equal(q.row_scale.cpu().numpy(), rs)
+    assert np.array_equal(q.codes.cpu().numpy(), rq)
+
+
+NV_CASES = [(1, 64, 16), (37, 128, 32), (130, 1024, 64), (301, 3072, 128), (5, 12288, 128)]
+
+
+@pytest.mark.parametrize("M,K,hb", NV_CASES)
+@pytest.mark.parametrize("mx", [False, True])
+@pytest.mark.parametrize("amax_given", [False, True])
+def test_quantize_nvfp4_bitexact(M, K, hb, mx, amax_given):
+    say(f"quantize nvfp4 mx={mx} M={M} K={K} hb={hb} amax_given={amax_given}")
+    x16 = synth.lognormal_tokens(M, K, synth.rng_for(101, M * 7 + K))
+    amax = O.rotated_amax(x16, hb)
+    fmt = hdq.FMT_NVFP4_MX if mx else hdq.FMT_NVFP4
+    am = torch.tensor([amax], dtype=torch.float32, device=DEV) if amax_given else None
+    q = hdq.quantize(to_dev(x16), hb, fmt, tensor_amax=am)
+    torch.cuda.synchronize()
+    rc, re_, rst = O.quant_nvfp4(x16, hb, mx=mx)
+    assert q.tensor_scale.item() == rst
+    assert_codes_equal(q.blk_scale.cpu().numpy(), re_, "E4M3 scales")
+    nvfp4_codes_equal(q.codes.cpu().numpy(), rc, "E2M1 codes")
+
+
+def test_quantize_nvfp4_zero_tensor():
+    x16 = np.zeros((8, 128), np.uint16)
+    q = hdq.quantize(to_dev(x16), 64, hdq.FMT_NVFP4)
+    assert q.tensor_scale.item() == 0.0
+    assert not q.codes.any().item() and not q.blk_scale.any().item()
+
+
+# -------------------------------------------------------- statistics
+
+def stats_case(prev_in, prev_out, cur, hb):
+    d, s = hdq.select_precision(None if prev_in is None else to_dev(prev_in),
+                                None if prev_out is None else to_dev(prev_out), to_dev(cur), hb)
+    torch.cuda.synchronize()
+    ref = O.stats(prev_in, prev_out, cur, hb)
+    return int(d.item()), s.cpu().numpy().astype(np.float64), ref
+
+
+def decision_ok(got, ref_stats, has_hist, dth=0.1, rth=50.0):
+    want = O.decide(has_hist, ref_stats[0], ref_stats[1], dth, rth)
+    if got == want:
+        return True
+    near = lambda v, t: math.isfinite(v) and abs(v - t) <= 1e-5 * t
+    return near(ref_stats[0], dth) or near(ref_stats[1], rth)
+
+
+@pytest.mark.parametrize("M,K,s", [(64, 1024, 0.05), (333, 3072, 0.2), (17, 12288, 0.1), (1000, 128, 0.0999)])
+def test_stats_match_oracle(M, K, s):
+    say(f"stats M={M} K={K} s={s}")
+    rng = synth.rng_for(102, M)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    cur = synth.to_bf16_bits(x)
+    prev_in = synth.to_bf16_bits(x)
+    prev_out = synth.to_bf16_bits(x + rng.standard_normal((M, K)).astype(np.float32) * np.float32(s))
+    dec, st, ref = stats_case(prev_in, prev_out, cur, 128)
+    assert abs(st[0] - ref[0]) <= 2e-6 * ref[0] + 1e-30
+    assert abs(st[1] - ref[1]) <= 2e-6 * ref[1]
+    assert st[2] == np.float32(ref[2])
+    assert abs(st[3] - ref[3]) <= 2e-6 * ref[3]
+    assert st[4] == np.float32(ref[4])          # rotated amax: exact (same float32 rotation)
+    assert decision_ok(dec, ref, True)
+
+
+def test_stats_hand_cases():
+    ones = np.ones((4, 64), np.float32)
+    b = synth.to_bf16_bits
+    # no history -> INT8
+    dec, st, ref = stats_case(None, None, b(ones), 64)
+    assert dec == hdq.PREC_INT8 and math.isnan(st[0]) and st[1] == 1.0 and st[4] == 8.0
+    # in == out -> NVFP4; out = 2 in -> INT8
+    assert stats_case(b(ones), b(ones), b(ones), 0)[0] == hdq.PREC_NVFP4
+    assert stats_case(b(ones), b(2 * ones), b(ones), 0)[0] == hdq.PREC_INT8
+    # ratio exactly 50 (64 * 225 / 288) stays quantized, 226 goes to BF16
+    x = np.ones((1, 64), np.float32)
+    x[0, 9] = 225.0
+    dec, st, _ = stats_case(b(ones), b(ones), b(x), 0)
+    assert st[1] == 50.0 and dec == hdq.PREC_NVFP4
+    x[0, 9] = 226.0
+    assert stats_case(b(ones), b(ones), b(x), 0)[0] == hdq.PREC_BF16
+    # non-finite input -> BF16; all-zero input -> ratio 0
+    x[0, 9] = np.inf
+    dec, st, _ = stats_case(b(ones), b(ones), b(x), 16)
+    assert dec == hdq.PREC_BF16 and math.isnan(st[1])
+    x[0, 9] = np.nan
+    assert stats_case(None, None, b(x), 0)[0] == hdq.PREC_BF16
+    z = np.zeros((2, 64), np.uint16)
+    dec, st, _ = stats_case(z, z, z, 0)
+    assert st[0] == 0.0 and st[1] == 0.0 and dec == hdq.PREC_NVFP4
+    # a previous-step numel that is not a multiple of 8, and a cur without rotation
+    pi = b(np.full((1, 13), 2.0, np.float32))
+    po = b(np.full((1, 13), 2.5, np.float32))
+    dec, st, ref = stats_case(pi, po, b(np.ones((3, 7), np.float32)), 0)
+    assert st[0] == 0.25 and dec == hdq.PREC_INT8
+
+
+# ------------------------------------------------------------ GEMMs
+
+def int_operands(M, N, K, hb, seed):
+    x16 = synth.gaussian_outliers(M, K, 0.01, 20.0, synth.rng_for(103, seed))
+    w16 = synth.gaussian(N, K, 0.02, synth.rng_for(104, seed))
+    return x16, w16
+
+
+GEMM_CASES = [(1, 1, 32), (37, 19, 64), (300, 200, 96), (257, 129, 1920), (512, 384, 1024), (64, 5760, 128)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_CASES)
+def test_int_gemm_i32_bitexact(M, N, K):
+    say(f"int gemm i32 M={M} N={N} K={K}")
+    hb = 32
+    x16, w16 = int_operands(M, N, K, hb, M * 31 + N)
+    W = hdq.LinearWeights(to_dev(w16), hb, fp4_fmt=None)
+    xq = hdq.quantize(to_dev(x16), hb, hdq.FMT_INT8_ROW)
+    y = hdq.linear(hdq.PREC_INT8, None, W, xq=xq, y_dtype=hdq.DTYPE_I32)
+    torch.cuda.synchronize()
+    qa, sa = O.quant_int(x16, hb, 127)
+    qw, sw = O.quant_int(w16, hb, 7)
+    _, acc = O.gemm_int(qa, sa, qw, sw)
+    assert np.array_equal(y.cpu().numpy().astype(np.int64), acc)
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_CASES[1:])
+@pytest.mark.parametrize("y_dtype", [hdq.DTYPE_F32, hdq.DTYPE_BF16])
+def test_linear_int8_matches_oracle(M, N, K, y_dtype):
+    say(f"linear int8 M={M} N={N} K={K} y={y_dtype}")
+    hb = 64 if K % 64 == 0 else 32
+    x16, w16 = int_operands(M, N, K, hb, M * 17 + N)
+    W = hdq.LinearWeights(to_dev(w16), hb, fp4_fmt=None)
+    y = hdq.linear(hdq.PREC_INT8, to_dev(x16), W, y_dtype=y_dtype)
+    torch.cuda.synchronize()
+    qa, sa = O.quant_int(x16, hb, 127)
+    qw, sw = O.quant_int(w16, hb, 7)
+    ref, _ = O.gemm_int(qa, sa, qw, sw)
+    ref = round_like(ref.astype(np.float64), y_dtype)
+    got = y_np(y)
+    assert rel_fro(got, ref) <= REL_TOL
+    assert np.array_equal(got, ref)      # same float32 epilogue order: exact
+
+
+@pytest.mark.parametrize("M,N,K", [(37, 19, 64), (300, 200, 96), (257, 129, 1024), (64, 640, 3072)])
+@pytest.mark.parametrize("mx", [False, True])
+@pytest.mark.parametrize("y_dtype", [hdq.DTYPE_F32, hdq.DTYPE_BF16])
+def test_linear_nvfp4_matches_oracle(M, N, K, mx, y_dtype):
+    say(f"linear nvfp4 mx={mx} M={M} N={N} K={K} y={y_dtype}")
+    hb = 32
+    x16 = synth.lognormal_tokens(M, K, synth.rng_for(105, M + N))
+    w16 = synth.gaussian(N, K, 0.02, synth.rng_for(106, M + N))
+    fmt = hdq.FMT_NVFP4_MX if mx else hdq.FMT_NVFP4
+    W = hdq.LinearWeights(to_dev(w16), hb, fp4_fmt=fmt)
+    y = hdq.linear(hdq.PREC_NVFP4, to_dev(x16), W, y_dtype=y_dtype)
+    torch.cuda.synchronize()
+    ac, ae, ast = O.quant_nvfp4(x16, hb, mx=mx)
+    wc, we, wst = O.quant_nvfp4(w16, hb, mx=mx)
+    ref = round_like(O.gemm_nvfp4(ac, ae, ast, wc, we, wst, K), y_dtype)
+    assert rel_fro(y_np(y), ref) <= REL_TOL
+
+
+def test_nvfp4_exact_kernel_accepts_mx_bytes():
+    # MX-compatible bytes are valid NVFP4: the exact (bf16-MFMA) kernel on
+    # them must agree with the block-scaled FP4 kernel
+    M, N, K, hb = 200, 160, 512, 64
+    x16 = synth.lognormal_tokens(M, K, synth.rng_for(107, 1))
+    w16 = synth.gaussian(N, K, 0.02, synth.rng_for(107, 2))
+    Wmx = hdq.LinearWeights(to_dev(w16), hb, fp4_fmt=hdq.FMT_NVFP4_MX)
+    xq = hdq.quantize(to_dev(x16), hb, hdq.FMT_NVFP4_MX)
+    y_mx = hdq.linear(hdq.PREC_NVFP4, None, Wmx, xq=xq, y_dtype=hdq.DTYPE_F32)
+    Wmx.w_fp4.fmt = hdq.FMT_NVFP4
+    xq.fmt = hdq.FMT_NVFP4
+    y_v1 = hdq.linear(hdq.PREC_NVFP4, None, Wmx, xq=xq, y_dtype=hdq.DTYPE_F32)
+    torch.cuda.synchronize()
+    assert rel_fro(y_mx.cpu().numpy(), y_v1.cpu().numpy()) <= 1e-5
+
+
+@pytest.mark.parametrize("M,N,K", [(37, 19, 64), (300, 200, 96), (257, 129, 1024), (64, 640, 3072)])
+@pytest.mark.parametrize("y_dtype", [hdq.DTYPE_F32, hdq.DTYPE_BF16])
+def test_linear_bf16_matches_oracle(M, N, K, y_dtype):
+    say(f"linear bf16 M={M} N={N} K={K}")
+    x16 = synth.gaussian_outliers(M, K, 0.01, 20.0, synth.rng_for(108, M))
+    w16 = synth.gaussian(N, K, 0.02, synth.rng_for(109, M))
+    W = hdq.LinearWeights(to_dev(w16), 32, fp4_fmt=None)
+    y = hdq.linear(hdq.PREC_BF16, to_dev(x16), W, y_dtype=y_dtype)
+    torch.cuda.synchronize()
+    ref = round_like(O.gemm_bf16(x16, w16), y_dtype)
+    assert rel_fro(y_np(y), ref) <= REL_TOL
+
+
+# ---------------------------------------- device-predicated dispatch
+
+@pytest.mark.parametrize("case", ["nvfp4", "int8", "bf16", "nohist"])
+def test_device_predicated_linear_matches_fixed(case):
+    say(f"predicated {case}")
+    M, N, K, hb = 300, 256, 512, 128
+    rng = synth.rng_for(110, 0)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    if case == "bf16":
+        x[:, 3] *= 400.0                      # outlier ratio far above 50
+    x16 = synth.to_bf16_bits(x)
+    s = {"nvfp4": 0.02, "int8": 0.2, "bf16": 0.02, "nohist": 0.0}[case]
+    po16 = synth.to_bf16_bits(x + rng.standard_normal((M, K)).astype(np.float32) * np.float32(s))
+    w16 = synth.gaussian(N, K, 0.02, synth.rng_for(110, 1))
+    W = hdq.LinearWeights(to_dev(w16), hb, fp4_fmt=hdq.FMT_NVFP4)
+    xd = to_dev(x16)
+    hist = case != "nohist"
+    dec, st = hdq.select_precision(to_dev(x16) if hist else None, to_dev(po16) if hist else None, xd, hb)
+    y_dyn = hdq.linear(-1, xd, W, decision=dec, x_amax=st[4:5], y_dtype=hdq.DTYPE_BF16)
+    torch.cuda.synchronize()
+    want = {"nvfp4": hdq.PREC_NVFP4, "int8": hdq.PREC_INT8, "bf16": hdq.PREC_BF16, "nohist": hdq.PREC_INT8}[case]
+    assert int(dec.item()) == want
+    y_fix = hdq.linear(want, xd, W, y_dtype=hdq.DTYPE_BF16)
+    torch.cuda.synchronize()
+    assert torch.equal(y_dyn.view(torch.int16), y_fix.view(torch.int16))
+
+
+def test_repeat_runs_are_bitwise_identical():
+    M, N, K, hb = 513, 384, 1024, 128
+    x16 = synth.lognormal_tokens(M, K, synth.rng_for(111, 0))
+    w16 = synth.gaussian(N, K, 0.02, synth.rng_for(111, 1))
+    xd = to_dev(x16)
+    for fmt in (hdq.FMT_NVFP4, hdq.FMT_NVFP4_MX):
+        W = hdq.LinearWeights(to_dev(w16), hb, fp4_fmt=fmt)
+        for prec in (hdq.PREC_INT8, hdq.PREC_NVFP4, hdq.PREC_BF16):
+            a = hdq.linear(prec, xd, W, y_dtype=hdq.DTYPE_F32)
+            b = hdq.linear(prec, xd, W, y_dtype=hdq.DTYPE_F32)
+            torch.cuda.synchronize()
+            assert torch.equal(a, b), (fmt, prec)
+    d1, s1 = hdq.select_precision(xd, xd, xd, hb)
+    d2, s2 = hdq.select_precision(xd, xd, xd, hb)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2) and torch.equal(d1, d2)
+
+
+# ----------------------------- full-size configs, sampled outputs
+
+def run_config(cfg, path, n_cols=384):
+    c = synth.CONFIGS[cfg]
+    M, K, N, hb = c["M"], c["K"], c["N"], c["had_block"]
+    say(f"config {cfg} {path}: generating M={M} K={K} N={N}")
+    x16 = synth.config_activations(cfg)
+    w16 = synth.config_weights(cfg)
+    y_dtype = hdq.DTYPE_F32 if c["out"] == "f32" else hdq.DTYPE_BF16
+    fmt = {"int8": None, "nvfp4": hdq.FMT_NVFP4, "nvfp4_mx": hdq.FMT_NVFP4_MX}[path]
+    W = hdq.LinearWeights(to_dev(w16), hb, fp4_fmt=fmt)
+    xd = to_dev(x16)
+    prec = hdq.PREC_INT8 if path == "int8" else hdq.PREC_NVFP4
+    say(f"config {cfg} {path}: GPU linear")
+    y = hdq.linear(prec, xd, W, y_dtype=y_dtype)
+    torch.cuda.synchronize()
+    rows = sample_rows(M)
+    cols = np.unique(np.concatenate([np.arange(min(n_cols // 2, N)),
+                                     np.linspace(0, N - 1, n_cols // 2).astype(np.int64)]))
+    say(f"config {cfg} {path}: oracle on {len(rows)} rows x {len(cols)} cols")
+    xs = np.ascontiguousarray(x16[rows])
+    ws = np.ascontiguousarray(w16[cols])
+    if path == "int8":
+        qa, sa = O.quant_int(xs, hb, 127)
+        qw, sw = O.quant_int(ws, hb, 7)
+        ref, _ = O.gemm_int(qa, sa, qw, sw)
+        ref = ref.astype(np.float64)
+        # the sampled rows' codes must also equal the GPU's
+        gq = hdq.quantize(xd, hb, hdq.FMT_INT8_ROW)
+        torch.cuda.synchronize()
+        assert np.array_equal(gq.row_scale.cpu().numpy()[rows], sa)
+        assert_codes_equal(gq.codes.cpu().numpy()[rows], qa, "codes")
+    else:
+        mx = path == "nvfp4_mx"
+        amax = O.rotated_amax(x16, hb)          # tensor amax over all rows
+        wamax = O.rotated_amax(w16, hb)
+        ac, ae, ast = O.quant_nvfp4(xs, hb, amax=amax, mx=mx)
+        wc, we, wst = O.quant_nvfp4(ws, hb, amax=wamax, mx=mx)
+        ref = O.gemm_nvfp4(ac, ae, ast, wc, we, wst, K)
+    ref = round_like(ref, y_dtype)
+    got = y_np(y)[np.ix_(rows, cols)]
+    err = rel_fro(got, ref)
+    say(f"config {cfg} {path}: rel fro {err:.3e}")
+    assert err <= REL_TOL
+    if path == "int8":
+        assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("cfg,path", [(1, "int8"), (1, "nvfp4"), (1, "nvfp4_mx"), (2, "int8"),
+                                      (3, "nvfp4"), (3, "nvfp4_mx"), (4, "int8")])
+def test_config_full_size_sampled(cfg, path):
+    run_config(cfg, path)
+
+
+def test_config1_full_oracle():
+    # the 1024^3 case is small enough for the oracle on every output
+    c = synth.CONFIGS[1]
+    x16, w16 = synth.config_activations(1), synth.config_weights(1)
+    hb = c["had_block"]
+    W = hdq.LinearWeights(to_dev(w16), hb, fp4_fmt=hdq.FMT_NVFP4)
+    y = hdq.linear(hdq.PREC_NVFP4, to_dev(x16), W, y_dtype=hdq.DTYPE_F32)
+    torch.cuda.synchronize()
+    ac, ae, ast = O.quant_nvfp4(x16, hb)
+    wc, we, wst = O.quant_nvfp4(w16, hb)
+    ref = O.gemm_nvfp4(ac, ae, ast, wc, we, wst, 1024).astype(np.float32)
+    assert rel_fro(y.cpu().numpy(), ref) <= REL_TOL
