@@ -1,0 +1,406 @@
+#!/usr/bin/env python
+"""Benchmark of the DMPQ hot path on one MI355X.
+
+Workload (one "step"): the dynamic mixed-precision schedule over 42
+CogVideoX-5B-shaped transformer blocks x 4 linear layers (QKV 3072->9216,
+attention out 3072->3072, FFN up 3072->12288, FFN down 12288->3072) x 3
+denoising timesteps, M = 17776 tokens (13 latent frames x 1350 patches + 226
+text tokens).  Per layer and timestep, on the device with no host round trip:
+  1. hdq_select_precision: relative-L1 difference of the previous step's
+     input/output (threshold 0.1: INT8 above, NVFP4 below) and the outlier
+     ratio max|x|/mean|x| of the input (above 50: bf16 fallback);
+  2. hdq_quantize, gated by that decision: block-Hadamard (128) rotation
+     fused with INT8 per-token or NVFP4 quantization;
+  3. hdq_linear, gated: INT8 x INT4, NVFP4 x NVFP4 or bf16 x bf16 GEMM.
+Inputs are synthetic and resident in HBM before timing: X ~ N(0, 1) bf16 per
+(block, layer); the previous step's input is a copy of X and its output is
+X + N(0, s), s ~ U(0.01, 0.3) per (block, layer, timestep); weights ~ N(0,
+0.02) per (block, layer), prepared (rotated + quantized) before timing.
+
+metric: effective TOPS = sum over layer calls of 2 M N K / step time (the
+step time includes selection, quantization and the gated-off launches).
+Per-kernel durations come from HIP events recorded on the stream the
+kernels run on, inside the timed region.
+
+Other modes: --config {1,2,3,4} times one single-layer configuration
+(quantize + GEMM); --profile-copy runs a plain 1 GiB device copy (the
+reference for HBM-counter calibration).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective TOPS of fused Hadamard-quant+linear (CogVideoX-5B shapes); quant GB/s"
+PEAK = {"int8": 5.0e15, "bf16": 2.5e15, "fp4": 10.1e15, "hbm": 8.0e12}
+HB = 128
+DELTA_T, RATIO_T = 0.1, 50.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--blocks", type=int, default=42)
+    ap.add_argument("--timesteps", type=int, default=3)
+    ap.add_argument("--fp4", choices=["nvfp4", "mx"], default="nvfp4",
+                    help="NVFP4 recipe: plain (exact bf16-MFMA GEMM) or MX-compatible (FP4 MFMA)")
+    ap.add_argument("--config", type=int, default=5, help="5: schedule; 1-4: one linear layer")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-copy", action="store_true")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ helpers
+
+class KernelTimes:
+    """Accumulates (duration, algorithmic work) per kernel kind."""
+
+    def __init__(self):
+        self.t = {}
+        self.work = {}
+        self.n = {}
+
+    def add(self, kind, ms, work):
+        self.t[kind] = self.t.get(kind, 0.0) + ms
+        self.work[kind] = self.work.get(kind, 0.0) + work
+        self.n[kind] = self.n.get(kind, 0) + 1
+
+    def summary(self):
+        out = {}
+        for k in sorted(self.t):
+            out[k] = {"launches": self.n[k], "total_ms": round(self.t[k], 3),
+                      "avg_us": round(1e3 * self.t[k] / self.n[k], 2),
+                      "rate": self.work[k] / (self.t[k] * 1e-3) if self.t[k] > 0 else 0.0}
+        return out
+
+
+def quant_bytes(M, K, prec):
+    """Algorithmic HBM bytes of one fused rotate+quantize of X [M, K] bf16."""
+    if prec == "int8":
+        return 2 * M * K + M * K + 4 * M
+    return 2 * M * K + M * K // 2 + M * K // 16 + 4 + 4
+
+
+def stats_bytes(M, K):
+    return 3 * 2 * M * K
+
+
+# ------------------------------------------------------------------ copy
+
+def profile_copy():
+    n = 1 << 28
+    x = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 5}))
+
+
+# ------------------------------------------------------------ schedule (5)
+
+def build_schedule(args, hdq, synth):
+    dev = torch.device("cuda:0")
+    M = synth.M_COGVIDEOX
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    fp4 = hdq.FMT_NVFP4_MX if args.fp4 == "mx" else hdq.FMT_NVFP4
+    s_levels = synth.schedule_noise_levels(args.blocks, args.timesteps)
+    blocks = []
+    t0 = time.time()
+    for b in range(args.blocks):
+        layers = []
+        for li, (name, K, N) in enumerate(synth.SCHEDULE_LAYERS):
+            x = synth.device_gaussian((M, K), 1.0, gen, dev)
+            prev_in = x.clone()
+            prev_out = [synth.device_noisy_copy(x, float(s_levels[b, li, t]), gen)
+                        for t in range(args.timesteps)]
+            w = synth.device_gaussian((N, K), 0.02, gen, dev)
+            W = hdq.LinearWeights(w, HB, fp4_fmt=fp4)
+            layers.append(dict(name=name, K=K, N=N, x=x, prev_in=prev_in, prev_out=prev_out, W=W,
+                               Wd=W.desc()))
+        blocks.append(layers)
+        if b % 6 == 5 or b == args.blocks - 1:
+            torch.cuda.synchronize()
+            log(f"setup: {b + 1}/{args.blocks} blocks, {torch.cuda.memory_allocated() / 2**30:.1f} GiB, "
+                f"{time.time() - t0:.1f} s")
+    # per layer type: quantized-activation buffers, outputs, workspaces
+    shared = []
+    for name, K, N in synth.SCHEDULE_LAYERS:
+        shared.append(dict(
+            xq8=hdq.QuantizedTensor(hdq.FMT_INT8_ROW, M, K, HB, dev),
+            xq4=hdq.QuantizedTensor(fp4, M, K, HB, dev),
+            y=torch.empty(M, N, dtype=torch.bfloat16, device=dev)))
+    ws_sel = torch.empty(hdq.workspace_bytes(hdq.OP_SELECT, M, 12288, M * 12288), dtype=torch.uint8,
+                         device=dev)
+    T, B, L = args.timesteps, args.blocks, len(synth.SCHEDULE_LAYERS)
+    dec = torch.full((T, B, L, 1), -1, dtype=torch.int32, device=dev)
+    sts = torch.zeros((T, B, L, 5), dtype=torch.float32, device=dev)
+    return dict(M=M, fp4=fp4, blocks=blocks, shared=shared, ws_sel=ws_sel, dec=dec, sts=sts,
+                s_levels=s_levels)
+
+
+def run_schedule_step(S, args, hdq, events=None):
+    """One step: every timestep, block and layer.  With `events`, records 7
+    HIP events per layer call (stream order: select | q8 | q4 | g8 | g4 | gbf)."""
+    M = S["M"]
+    k = 0
+    for t in range(args.timesteps):
+        for b, layers in enumerate(S["blocks"]):
+            for li, L in enumerate(layers):
+                sh = S["shared"][li]
+                d = S["dec"][t, b, li]
+                st = S["sts"][t, b, li]
+                ev = events[k] if events is not None else None
+                k += 1
+                if ev: ev[0].record()
+                hdq.select_precision(L["prev_in"], L["prev_out"][t], L["x"], HB, DELTA_T, RATIO_T,
+                                     decision=d, stats=st, ws=S["ws_sel"])
+                if ev: ev[1].record()
+                hdq.quantize(L["x"], HB, hdq.FMT_INT8_ROW, out=sh["xq8"], decision=d)
+                if ev: ev[2].record()
+                hdq.quantize(L["x"], HB, S["fp4"], tensor_amax=st[4:5], out=sh["xq4"], decision=d)
+                if ev: ev[3].record()
+                hdq.linear(hdq.PREC_INT8, None, L["W"], decision=d, xq=sh["xq8"], y=sh["y"])
+                if ev: ev[4].record()
+                hdq.linear(hdq.PREC_NVFP4, None, L["W"], decision=d, xq=sh["xq4"], y=sh["y"])
+                if ev: ev[5].record()
+                hdq.linear(hdq.PREC_BF16, L["x"], L["W"], decision=d, y=sh["y"])
+                if ev: ev[6].record()
+    return k
+
+
+def schedule_kernel_times(S, args, events_per_step, synth):
+    """Per-kernel durations from the recorded events, attributed by the
+    device decision of each layer call."""
+    M = S["M"]
+    decisions = S["dec"].cpu().numpy().reshape(args.timesteps, args.blocks, -1)
+    kt = KernelTimes()
+    for evs in events_per_step:
+        k = 0
+        for t in range(args.timesteps):
+            for b in range(args.blocks):
+                for li, (name, K, N) in enumerate(synth.SCHEDULE_LAYERS):
+                    ev = evs[k]
+                    k += 1
+                    d = int(decisions[t, b, li])
+                    dt = [ev[i].elapsed_time(ev[i + 1]) for i in range(6)]
+                    flops = 2.0 * M * N * K
+                    kt.add("select_stats", dt[0], stats_bytes(M, K))
+                    kt.add("quant_int8" if d == 1 else "quant_int8_gated_off", dt[1],
+                           quant_bytes(M, K, "int8") if d == 1 else 0)
+                    kt.add("quant_nvfp4" if d == 0 else "quant_nvfp4_gated_off", dt[2],
+                           quant_bytes(M, K, "nvfp4") if d == 0 else 0)
+                    kt.add("gemm_int8" if d == 1 else "gemm_int8_gated_off", dt[3], flops if d == 1 else 0)
+                    kt.add("gemm_nvfp4" if d == 0 else "gemm_nvfp4_gated_off", dt[4], flops if d == 0 else 0)
+                    kt.add("gemm_bf16" if d == 2 else "gemm_bf16_gated_off", dt[5], flops if d == 2 else 0)
+    return kt, decisions
+
+
+def cpu_baseline_schedule(S, args, synth):
+    """The oracle on a bounded sample of the same workload: block 0's four
+    layers at timestep 0 -- selection statistics over the full tensors, then
+    quantize + GEMM on the first R rows in the decided precision, scaled to
+    all M rows.  Weight preparation is excluded (as on the GPU)."""
+    import oracle as O
+    M, R = S["M"], 32
+    fp4_mx = args.fp4 == "mx"
+    t_total = 0.0
+    flops_total = 0.0
+    for li, (name, K, N) in enumerate(synth.SCHEDULE_LAYERS):
+        L = S["blocks"][0][li]
+        np16 = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+        pi, po, x, w = np16(L["prev_in"]), np16(L["prev_out"][0]), np16(L["x"]), np16(L["W"].w_bf16)
+        # weights (untimed preparation)
+        qw, sw = O.quant_int(w, HB, 7)
+        wc, we, wst = O.quant_nvfp4(w, HB, mx=fp4_mx)
+        t0 = time.perf_counter()
+        st = O.stats(pi, po, x, HB)
+        d = O.decide(True, st[0], st[1], DELTA_T, RATIO_T)
+        t_stats = time.perf_counter() - t0
+        xs = np.ascontiguousarray(x[:R])
+        t0 = time.perf_counter()
+        if d == O.INT8:
+            qa, sa = O.quant_int(xs, HB, 127)
+            O.gemm_int(qa, sa, qw, sw)
+        elif d == O.NVFP4:
+            ac, ae, ast = O.quant_nvfp4(xs, HB, amax=np.float32(st[4]), mx=fp4_mx)
+            O.gemm_nvfp4(ac, ae, ast, wc, we, wst, K)
+        else:
+            O.gemm_bf16(xs, w)
+        t_rows = time.perf_counter() - t0
+        t_total += t_stats + t_rows * (M / R)
+        flops_total += 2.0 * M * N * K
+        log(f"cpu baseline: {name} decision={d} stats {t_stats:.2f}s, {R} rows {t_rows:.2f}s")
+    return {"value": flops_total / t_total / 1e12, "unit": "TOPS", "cores": O.num_threads(),
+            "kind": "oracle",
+            "sample": (f"block 0 x 4 layers at timestep 0: selection statistics over the full "
+                       f"[17776, K] tensors (1 thread), rotate+quantize and GEMM in the decided "
+                       f"precision on the first {R} of 17776 rows (GEMM loops OpenMP), scaled "
+                       f"linearly to all rows; weight preparation untimed")}
+
+
+def bench_schedule(args, hdq, synth):
+    S = build_schedule(args, hdq, synth)
+    M = S["M"]
+    flops_step = sum(2.0 * M * N * K for _, K, N in synth.SCHEDULE_LAYERS) * args.blocks * args.timesteps
+    log("warmup")
+    for _ in range(args.warmup):
+        run_schedule_step(S, args, hdq)
+    n_calls = args.timesteps * args.blocks * len(synth.SCHEDULE_LAYERS)
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(n_calls)]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        run_schedule_step(S, args, hdq, events[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = 1e3 * elapsed / args.steps
+    kt, decisions = schedule_kernel_times(S, args, events, synth)
+    ks = kt.summary()
+    counts = {p: int((decisions == v).sum()) for p, v in (("nvfp4", 0), ("int8", 1), ("bf16", 2))}
+    # dominant kernel: the selected-path kernel with the most time
+    main_kinds = ["gemm_int8", "gemm_nvfp4", "gemm_bf16", "quant_int8", "quant_nvfp4", "select_stats"]
+    dom = max((k for k in main_kinds if k in ks), key=lambda k: ks[k]["total_ms"])
+    roof = roofline_for(dom, ks[dom], args)
+    q_bytes = sum(kt.work[k] for k in ("quant_int8", "quant_nvfp4") if k in kt.work)
+    q_ms = sum(kt.t[k] for k in ("quant_int8", "quant_nvfp4") if k in kt.t)
+    # effective TOPS of the fused quant + linear alone (selected kernels only)
+    ql_ms = q_ms + sum(kt.t.get(k, 0.0) for k in ("gemm_int8", "gemm_nvfp4", "gemm_bf16"))
+    ql_flops = sum(kt.work.get(k, 0.0) for k in ("gemm_int8", "gemm_nvfp4", "gemm_bf16"))
+    result = {
+        "metric": METRIC,
+        "value": round(flops_step / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TOPS",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8+nvfp4" if args.fp4 == "nvfp4" else "int8+nvfp4_mx",
+        "data": "synthetic",
+        "config": {"workload": (f"DMPQ schedule: {args.blocks} CogVideoX-5B blocks x (QKV 3072->9216, "
+                                f"out 3072->3072, FFN 3072->12288->3072) x {args.timesteps} timesteps, "
+                                f"M=17776 tokens, Hadamard block 128, delta thresh 0.1, ratio thresh 50, "
+                                f"fp4 recipe {args.fp4}"),
+                   "global_batch": M, "layer_calls_per_step": n_calls},
+        "roofline": roof,
+        "quant_gbps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1) if q_ms > 0 else None,
+        "fused_quant_linear_tops": round(ql_flops / (ql_ms * 1e-3) / 1e12, 2) if ql_ms > 0 else None,
+        "decisions": counts,
+        "kernels": {k: {"launches": v["launches"], "total_ms": v["total_ms"], "avg_us": v["avg_us"]}
+                    for k, v in ks.items()},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline_schedule(S, args, synth)
+        result["cpu_baseline"]["value"] = round(result["cpu_baseline"]["value"], 6)
+    return result
+
+
+def roofline_for(kind, k, args):
+    if kind.startswith("gemm"):
+        dt = {"gemm_int8": "int8", "gemm_bf16": "bf16",
+              "gemm_nvfp4": "fp4" if args.fp4 == "mx" else "bf16"}[kind]
+        peak = PEAK[dt]
+        ach = k["rate"]
+        return {"kernel": kind, "bound": "mfma", "dtype": dt, "achieved": round(ach / 1e12, 1),
+                "peak": round(peak / 1e12, 1), "unit": "TFLOP/s" if dt != "int8" else "TOP/s",
+                "frac": round(ach / peak, 4), "traffic": None}
+    ach = k["rate"]
+    return {"kernel": kind, "bound": "hbm", "achieved": round(ach / 1e9, 1), "peak": 8000.0,
+            "unit": "GB/s", "frac": round(ach / PEAK["hbm"], 4), "traffic": None}
+
+
+# ---------------------------------------------------------- single layer
+
+def bench_single(args, hdq, synth):
+    import oracle as O  # noqa: F401  (only for the CPU-baseline leg)
+    cfg = args.config
+    c = synth.CONFIGS[cfg]
+    M, K, N, hb = c["M"], c["K"], c["N"], c["had_block"]
+    dev = torch.device("cuda:0")
+    log(f"config {cfg}: generating")
+    x16 = synth.config_activations(cfg)
+    w16 = synth.config_weights(cfg)
+    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    xd = to_dev(x16)
+    path = c["paths"][0] if args.fp4 == "nvfp4" else ("nvfp4" if "nvfp4" in c["paths"] else "int8")
+    fmt = hdq.FMT_INT8_ROW if path == "int8" else (hdq.FMT_NVFP4_MX if args.fp4 == "mx" else hdq.FMT_NVFP4)
+    W = hdq.LinearWeights(to_dev(w16), hb, fp4_fmt=None if path == "int8" else fmt)
+    prec = hdq.PREC_INT8 if path == "int8" else hdq.PREC_NVFP4
+    y_dtype = hdq.DTYPE_F32 if c["out"] == "f32" else hdq.DTYPE_BF16
+    xq = hdq.QuantizedTensor(fmt, M, K, hb, dev)
+    amax = None
+    if path != "int8":
+        _, st = hdq.select_precision(None, None, xd, hb)
+        amax = st[4:5]
+    y = torch.empty(M, N, dtype=torch.float32 if y_dtype == hdq.DTYPE_F32 else torch.bfloat16, device=dev)
+    for _ in range(args.warmup):
+        hdq.quantize(xd, hb, fmt, tensor_amax=amax, out=xq)
+        hdq.linear(prec, None, W, xq=xq, y=y, y_dtype=y_dtype)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record()
+        hdq.quantize(xd, hb, fmt, tensor_amax=amax, out=xq)
+        e[1].record()
+        hdq.linear(prec, None, W, xq=xq, y=y, y_dtype=y_dtype)
+        e[2].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    tq = np.mean([e[0].elapsed_time(e[1]) for e in evs])
+    tg = np.mean([e[1].elapsed_time(e[2]) for e in evs])
+    flops = 2.0 * M * N * K
+    qb = quant_bytes(M, K, "int8" if path == "int8" else "nvfp4")
+    dt = "int8" if path == "int8" else ("fp4" if args.fp4 == "mx" else "bf16")
+    res = {"metric": METRIC, "value": round(flops / ((tq + tg) * 1e-3) / 1e12, 2), "unit": "TOPS",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(1e3 * elapsed / args.steps, 3), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": dt, "data": "synthetic",
+           "config": {"workload": c["name"], "global_batch": M},
+           "quant_gbps": round(qb / (tq * 1e-3) / 1e9, 1), "quant_ms": round(tq, 4),
+           "gemm_ms": round(tg, 4),
+           "roofline": {"kernel": f"gemm_{path}", "bound": "mfma", "dtype": dt,
+                        "achieved": round(flops / (tg * 1e-3) / 1e12, 1), "peak": PEAK[dt] / 1e12,
+                        "unit": "TFLOP/s" if dt != "int8" else "TOP/s",
+                        "frac": round(flops / (tg * 1e-3) / PEAK[dt], 4), "traffic": None},
+           "quant_roofline": {"bound": "hbm", "achieved": round(qb / (tq * 1e-3) / 1e9, 1), "peak": 8000.0,
+                              "unit": "GB/s", "frac": round(qb / (tq * 1e-3) / PEAK["hbm"], 4)}}
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the work shards by tokens; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    if args.profile_copy:
+        profile_copy()
+        return
+    from bit_quantized_video_amd import hdq, synth
+    if args.config == 5:
+        res = bench_schedule(args, hdq, synth)
+    else:
+        res = bench_single(args, hdq, synth)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

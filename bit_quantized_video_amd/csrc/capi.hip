@@ -131,9 +131,10 @@ int hdq_select_precision(const void* prev_in, const void* prev_out, int64_t prev
 }
 
 int hdq_quantize(const void* x, int64_t rows, int64_t cols, int32_t had_block, int32_t fmt,
-                 const float* tensor_amax, hdq_qtensor* out, void* ws, size_t ws_bytes,
-                 void* stream) {
+                 const float* tensor_amax, const int32_t* decision_dev, hdq_qtensor* out,
+                 void* ws, size_t ws_bytes, void* stream) {
   if (x == nullptr || out == nullptr || !valid_fmt(fmt)) return HDQ_ERR_INVALID;
+  if (decision_dev != nullptr && fmt == HDQ_FMT_INT4_ROW) return HDQ_ERR_UNSUPPORTED;
   int st = check_quant_shape(rows, cols, had_block, fmt);
   if (st != HDQ_OK) return st;
   hdq_qtensor q = *out;
@@ -146,8 +147,9 @@ int hdq_quantize(const void* x, int64_t rows, int64_t cols, int32_t had_block, i
       (ws == nullptr || ws_bytes < amax_prepass_bytes()))
     return HDQ_ERR_WORKSPACE;
   *out = q;
+  const int32_t want = is_fp4(fmt) ? HDQ_PREC_NVFP4 : HDQ_PREC_INT8;
   return hip_status(enqueue_quantize(x, q, is_fp4(fmt) ? tensor_amax : nullptr,
-                                     static_cast<uint8_t*>(ws), nullptr, 0,
+                                     static_cast<uint8_t*>(ws), decision_dev, want,
                                      static_cast<hipStream_t>(stream)));
 }
 
@@ -159,6 +161,7 @@ int hdq_linear(int32_t precision, const int32_t* decision_dev, const void* x,
   if (precision < -1 || precision > HDQ_PREC_BF16) return HDQ_ERR_INVALID;
   if (y_dtype < HDQ_DTYPE_F32 || y_dtype > HDQ_DTYPE_I32) return HDQ_ERR_INVALID;
   if (precision == -1 && (decision_dev == nullptr || xq != nullptr)) return HDQ_ERR_INVALID;
+  if (precision == HDQ_PREC_BF16 && xq != nullptr) return HDQ_ERR_UNSUPPORTED;
   if (M <= 0 || K <= 0 || w->N <= 0 || M > 0x7fffffff || K > 0x7fffffff || w->N > 0x7fffffff)
     return HDQ_ERR_SHAPE;
   if (w->K != K) return HDQ_ERR_SHAPE;
@@ -202,7 +205,7 @@ int hdq_linear(int32_t precision, const int32_t* decision_dev, const void* x,
   if (need > 0 && (ws == nullptr || ws_bytes < need)) return HDQ_ERR_WORKSPACE;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int32_t* gate = precision == -1 ? decision_dev : nullptr;
+  const int32_t* gate = decision_dev;  // -1: selects the path; fixed P: run only if P
   uint8_t* cursor = static_cast<uint8_t*>(ws);
   hipError_t e;
   if (run_int8) {

@@ -54,7 +54,7 @@ def _load():
     L.hdq_select_precision.argtypes = [_p, _p, _c.c_int64, _p, _c.c_int64, _c.c_int64, _c.c_int32,
                                        _c.c_float, _c.c_float, _p, _p, _p, _c.c_size_t, _p]
     L.hdq_quantize.restype = _c.c_int
-    L.hdq_quantize.argtypes = [_p, _c.c_int64, _c.c_int64, _c.c_int32, _c.c_int32, _p,
+    L.hdq_quantize.argtypes = [_p, _c.c_int64, _c.c_int64, _c.c_int32, _c.c_int32, _p, _p,
                                _c.POINTER(QTensorDesc), _p, _c.c_size_t, _p]
     L.hdq_linear.restype = _c.c_int
     L.hdq_linear.argtypes = [_c.c_int32, _p, _p, _c.POINTER(QTensorDesc), _p, _c.c_int64,
@@ -157,15 +157,17 @@ def select_precision(prev_in, prev_out, cur_in, had_block=0, delta_thresh=0.1, r
     return decision, stats
 
 
-def quantize(x, had_block, fmt, tensor_amax=None, out=None, ws=None, stream=None):
-    """hdq_quantize: rotate + quantize a bf16 [rows, cols] tensor."""
+def quantize(x, had_block, fmt, tensor_amax=None, out=None, ws=None, stream=None, decision=None):
+    """hdq_quantize: rotate + quantize a bf16 [rows, cols] tensor (only when
+    the device decision matches the format's precision, if one is given)."""
     x = _bf16(x, "x")
     rows, cols = x.shape
     out = QuantizedTensor(fmt, rows, cols, had_block, x.device) if out is None else out
     d = out.desc()
     nbytes = workspace_bytes(OP_QUANTIZE, rows, cols, 0, fmt) if tensor_amax is None else 0
     ws = _workspace(ws, nbytes, x.device)
-    st = lib.hdq_quantize(_ptr(x), rows, cols, had_block, fmt, _ptr(tensor_amax), _c.byref(d),
+    st = lib.hdq_quantize(_ptr(x), rows, cols, had_block, fmt, _ptr(tensor_amax), _ptr(decision),
+                          _c.byref(d),
                           _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
     _check("hdq_quantize", st)
     return out
@@ -193,7 +195,8 @@ class LinearWeights:
 def linear(precision, x, w, decision=None, xq=None, x_amax=None, y=None, y_dtype=DTYPE_BF16,
            ws=None, stream=None):
     """hdq_linear: Y[M, N] = quantized X[M, K] @ W^T.  precision -1 reads the
-    decision tensor on the device."""
+    decision tensor on the device; a fixed precision with a decision tensor
+    runs only when the device decision equals it."""
     if x is not None:
         x = _bf16(x, "x")
         M, K = x.shape

@@ -162,6 +162,11 @@ int hdq_select_precision(const void *prev_in, const void *prev_out, int64_t prev
  *                 hdq_select_precision), or NULL to compute it in a pre-pass
  *                 (then ws must hold hdq_workspace_bytes(HDQ_OP_QUANTIZE,
  *                 rows, cols, 0, fmt) bytes).  Ignored for INT formats.
+ *   decision_dev: NULL, or device int32[1]: the kernels then do their work
+ *                 only when it holds the precision that consumes `fmt`
+ *                 (HDQ_PREC_INT8 for INT8_ROW, HDQ_PREC_NVFP4 for the NVFP4
+ *                 formats; not allowed with INT4_ROW), so one enqueued call
+ *                 serves a device-side decision without a host round trip.
  *   out         : host struct with caller-allocated device buffers sized for
  *                 the format; fmt, had_block, rows, cols are written.
  * Rows whose max |rotated value| is below 2^-100 get zero codes and a zero
@@ -169,8 +174,8 @@ int hdq_select_precision(const void *prev_in, const void *prev_out, int64_t prev
  * codes and scale bytes.
  */
 int hdq_quantize(const void *x, int64_t rows, int64_t cols, int32_t had_block, int32_t fmt,
-                 const float *tensor_amax, hdq_qtensor *out, void *ws, size_t ws_bytes,
-                 void *stream);
+                 const float *tensor_amax, const int32_t *decision_dev, hdq_qtensor *out,
+                 void *ws, size_t ws_bytes, void *stream);
 
 /*
  * hdq_linear -- steps 2 + 3: Y[M, N] = quantized X[M, K] times the weights'
@@ -180,11 +185,15 @@ int hdq_quantize(const void *x, int64_t rows, int64_t cols, int32_t had_block, i
  *   precision   : HDQ_PREC_* to run, or -1 to read it from decision_dev on
  *                 the device (every candidate kernel is enqueued and the ones
  *                 not selected exit at once; no host synchronisation).
- *   decision_dev: device int32[1] (only read when precision == -1).
+ *   decision_dev: NULL, or device int32[1].  With precision -1 it selects
+ *                 the path; with a fixed precision P the work is done only
+ *                 when it holds P (so a caller can enqueue each path's
+ *                 pieces, e.g. one quantization shared by several GEMMs).
  *   x           : device bf16 [M, K] (the unrotated activations).
  *   xq          : NULL, or already-quantized activations to use instead of
- *                 quantizing x (fixed precision only; its format must match
- *                 the weights': INT8_ROW for INT8, the w_fp4 format for NVFP4).
+ *                 quantizing x (fixed precision INT8 or NVFP4 only; its format
+ *                 must match the weights': INT8_ROW for INT8, the w_fp4
+ *                 format for NVFP4).
  *   x_amax      : NVFP4 only: device fp32[1] rotated amax of x, or NULL to
  *                 compute it in a pre-pass.
  *   w           : weights; w->K == K and had_block of both quantized forms

@@ -71,14 +71,16 @@ def test_validation_happens_before_any_launch(hdq):
     assert L.hdq_select_precision(None, None, 0, fake, 4, 64, 0, 0.1, 50.0, fake, fake, None, 0, None) == hdq.ERR_WORKSPACE
     # quantize: bad fmt, bad shapes, missing buffers, missing workspace for the amax pre-pass
     q = hdq.QTensorDesc(0, 0, 0, 0, fake, fake, fake, fake)
-    assert L.hdq_quantize(fake, 4, 64, 16, 9, None, ctypes.byref(q), None, 0, None) == hdq.ERR_INVALID
-    assert L.hdq_quantize(fake, 4, 64, 12, 0, None, ctypes.byref(q), None, 0, None) == hdq.ERR_SHAPE
-    assert L.hdq_quantize(fake, 4, 64, 256, 0, None, ctypes.byref(q), None, 0, None) == hdq.ERR_SHAPE
-    assert L.hdq_quantize(fake, 4, 72, 16, 0, None, ctypes.byref(q), None, 0, None) == hdq.ERR_SHAPE
-    assert L.hdq_quantize(fake, 4, 48, 16, hdq.FMT_NVFP4_MX, None, ctypes.byref(q), None, 0, None) == hdq.ERR_SHAPE
-    assert L.hdq_quantize(fake, 4, 64, 16, hdq.FMT_NVFP4, None, ctypes.byref(q), None, 0, None) == hdq.ERR_WORKSPACE
+    assert L.hdq_quantize(fake, 4, 64, 16, 9, None, None, ctypes.byref(q), None, 0, None) == hdq.ERR_INVALID
+    assert L.hdq_quantize(fake, 4, 64, 12, 0, None, None, ctypes.byref(q), None, 0, None) == hdq.ERR_SHAPE
+    assert L.hdq_quantize(fake, 4, 64, 256, 0, None, None, ctypes.byref(q), None, 0, None) == hdq.ERR_SHAPE
+    assert L.hdq_quantize(fake, 4, 72, 16, 0, None, None, ctypes.byref(q), None, 0, None) == hdq.ERR_SHAPE
+    assert L.hdq_quantize(fake, 4, 48, 16, hdq.FMT_NVFP4_MX, None, None, ctypes.byref(q), None, 0, None) == hdq.ERR_SHAPE
+    assert L.hdq_quantize(fake, 4, 64, 16, hdq.FMT_NVFP4, None, None, ctypes.byref(q), None, 0, None) == hdq.ERR_WORKSPACE
     q0 = hdq.QTensorDesc(0, 0, 0, 0, None, fake, fake, fake)
-    assert L.hdq_quantize(fake, 4, 64, 16, 0, None, ctypes.byref(q0), None, 0, None) == hdq.ERR_INVALID
+    assert L.hdq_quantize(fake, 4, 64, 16, 0, None, None, ctypes.byref(q0), None, 0, None) == hdq.ERR_INVALID
+    # a decision gate makes no sense for weight (INT4) quantization
+    assert L.hdq_quantize(fake, 4, 64, 16, hdq.FMT_INT4_ROW, None, fake, ctypes.byref(q), None, 0, None) == hdq.ERR_UNSUPPORTED
     # linear: descriptor mismatches
     w4 = hdq.QTensorDesc(hdq.FMT_INT4_ROW, 16, 32, 64, fake, fake, None, None)
     wf = hdq.QTensorDesc(hdq.FMT_NVFP4, 16, 32, 64, fake, None, fake, fake)
@@ -92,6 +94,7 @@ def test_validation_happens_before_any_launch(hdq):
     assert ok(1, dt=2, x=fake) == hdq.ERR_WORKSPACE        # int8 needs room for the codes
     assert ok(0, dt=2) == hdq.ERR_UNSUPPORTED              # int32 output only on the INT8 path
     assert ok(2, x=None) == hdq.ERR_INVALID                # bf16 needs x
+    assert ok(2, xq=ctypes.byref(hdq.QTensorDesc(hdq.FMT_INT8_ROW, 16, 8, 64, fake, fake, None, None))) == hdq.ERR_UNSUPPORTED
     bad4 = hdq.WeightsDesc(32, 64, fake, hdq.QTensorDesc(hdq.FMT_INT8_ROW, 16, 32, 64, fake, fake, None, None), wf)
     assert ok(1, w=bad4) == hdq.ERR_UNSUPPORTED
     badfp = hdq.WeightsDesc(32, 64, fake, w4, hdq.QTensorDesc(hdq.FMT_NVFP4, 16, 31, 64, fake, None, fake, fake))
