@@ -189,11 +189,223 @@ __global__ __launch_bounds__(256) void k_gemm_bf16mfma(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined kernel for K % 64 == 0: 256 x 256 tile, 8 waves as 2 (tokens) x
+// 4 (features), each 128 x 64 (4 x 2 subtiles of 32 x 32), 64 K per stage,
+// two register sets prefetching the next two stages through buffer loads
+// (rows past M or N read as zero), double-buffered LDS, LDS-only barriers
+// -- the structure of the INT8 kernel.  LDS holds bf16: 128-byte rows per
+// stage (swz128), substep s (16 K) giving lane half h the 16-byte chunk
+// 2s + h.  NVFP4 operands are decoded to exact bf16 when their registers are
+// written to LDS, once per workgroup rather than once per wave.
+template <int SRC>
+struct Bf16Stage;
+template <>
+struct Bf16Stage<kSrcBf16> {
+  uint4 x[4], w[4];  // 4 x 16-byte chunks per operand per thread
+};
+template <>
+struct Bf16Stage<kSrcNvfp4> {
+  uint4 x, w;         // 32 codes per operand per thread
+  uint32_t xs, ws;    // their two E4M3 block scales
+};
+
+template <int SRC, int OUT>
+__global__ __launch_bounds__(512) void k_gemm_bf16_pipe(
+    const void* __restrict__ X, const uint8_t* __restrict__ xsc, const float* __restrict__ xts,
+    const void* __restrict__ W, const uint8_t* __restrict__ wsc, const float* __restrict__ wts,
+    void* __restrict__ Y, int M, int N, int K, const int32_t* __restrict__ decision, int32_t want) {
+  if (decision != nullptr && *decision != want) return;
+  constexpr int BM = 256, BN = 256, BK = 64, WM_T = 4, WN_T = 2;
+  constexpr int XB = BM * BK * 2, SB = XB + BN * BK * 2;  // LDS bytes per stage
+  using Stage = Bf16Stage<SRC>;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % 2, wn = wave / 2;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  int tm, tn;
+  xcd_tile(tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  __amdgpu_buffer_rsrc_t xres, wres, xsres, wsres;
+  uint32_t xvoff, wvoff, svoff = 0;
+  int dst;  // LDS byte offset of this thread's first chunk (same for X and W)
+  if constexpr (SRC == kSrcBf16) {
+    const int64_t ld = 2 * (int64_t)K;
+    xres = make_rsrc(reinterpret_cast<const uint8_t*>(X) + m0 * ld, (uint32_t)((M - m0) * ld));
+    wres = make_rsrc(reinterpret_cast<const uint8_t*>(W) + n0 * ld, (uint32_t)((N - n0) * ld));
+    const int r = tid >> 3, c = tid & 7;  // 8 threads per 128-byte row, 64 rows per round
+    xvoff = wvoff = (uint32_t)(r * ld + 16 * c);
+    dst = r * 128 + 16 * (c ^ swz128(r));
+  } else {
+    const int64_t ld = K / 2, lds_ = K / 16;
+    xres = make_rsrc(reinterpret_cast<const uint8_t*>(X) + m0 * ld, (uint32_t)((M - m0) * ld));
+    wres = make_rsrc(reinterpret_cast<const uint8_t*>(W) + n0 * ld, (uint32_t)((N - n0) * ld));
+    xsres = make_rsrc(xsc + m0 * lds_, (uint32_t)((M - m0) * lds_));
+    wsres = make_rsrc(wsc + n0 * lds_, (uint32_t)((N - n0) * lds_));
+    const int r = tid >> 1, c = tid & 1;  // 2 threads per row: 32 elements each
+    xvoff = wvoff = (uint32_t)(r * ld + 16 * c);
+    svoff = (uint32_t)(r * lds_ + 2 * c);
+    dst = r * 128 + 64 * c;  // chunks 4c .. 4c + 3 of the row (swizzled at store)
+  }
+  auto load = [&](Stage& st, int kt) {
+    if constexpr (SRC == kSrcBf16) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        st.x[p] = buf_load16(xres, xvoff, kt * 128 + p * 64 * 2 * K);
+        st.w[p] = buf_load16(wres, wvoff, kt * 128 + p * 64 * 2 * K);
+      }
+    } else {
+      st.x = buf_load16(xres, xvoff, kt * 32);
+      st.w = buf_load16(wres, wvoff, kt * 32);
+      st.xs = __builtin_amdgcn_raw_buffer_load_b16(xsres, (int)svoff, kt * 4, 0);
+      st.ws = __builtin_amdgcn_raw_buffer_load_b16(wsres, (int)svoff, kt * 4, 0);
+    }
+  };
+  auto store = [&](const Stage& st, int buf) {
+    uint8_t* lx = smem + buf * SB;
+    uint8_t* lw = lx + XB;
+    if constexpr (SRC == kSrcBf16) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        *reinterpret_cast<uint4*>(lx + dst + p * 64 * 128) = st.x[p];
+        *reinterpret_cast<uint4*>(lw + dst + p * 64 * 128) = st.w[p];
+      }
+    } else {
+      const int r = tid >> 1, c = tid & 1;
+      uint4 d[4];
+      decode_nvfp4x16(make_uint2(st.x.x, st.x.y), st.xs & 0xffu, d[0], d[1]);
+      decode_nvfp4x16(make_uint2(st.x.z, st.x.w), st.xs >> 8, d[2], d[3]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<uint4*>(lx + r * 128 + 16 * ((4 * c + q) ^ swz128(r))) = d[q];
+      decode_nvfp4x16(make_uint2(st.w.x, st.w.y), st.ws & 0xffu, d[0], d[1]);
+      decode_nvfp4x16(make_uint2(st.w.z, st.w.w), st.ws >> 8, d[2], d[3]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<uint4*>(lw + r * 128 + 16 * ((4 * c + q) ^ swz128(r))) = d[q];
+    }
+  };
+
+  v16f acc[WN_T][WM_T];
+#pragma unroll
+  for (int j = 0; j < WN_T; ++j)
+#pragma unroll
+    for (int i = 0; i < WM_T; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.0f;
+
+  const int h = lane >> 5, r32 = lane & 31;
+  auto compute = [&](int buf) {
+    const uint8_t* lx = smem + buf * SB;
+    const uint8_t* lw = lx + XB;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      v8bf xf[WM_T], wf[WN_T];
+#pragma unroll
+      for (int i = 0; i < WM_T; ++i) {
+        const int r = wm * WM_T * 32 + i * 32 + r32;
+        xf[i] = *reinterpret_cast<const v8bf*>(lx + r * 128 + 16 * ((2 * ks + h) ^ swz128(r)));
+      }
+#pragma unroll
+      for (int j = 0; j < WN_T; ++j) {
+        const int r = wn * WN_T * 32 + j * 32 + r32;
+        wf[j] = *reinterpret_cast<const v8bf*>(lw + r * 128 + 16 * ((2 * ks + h) ^ swz128(r)));
+      }
+#pragma unroll
+      for (int j = 0; j < WN_T; ++j)
+#pragma unroll
+        for (int i = 0; i < WM_T; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], xf[i], acc[j][i], 0, 0, 0);
+    }
+  };
+
+  const int nk = K / BK;
+  Stage ra, rb;
+  load(ra, 0);
+  if (nk > 1) load(rb, 1);
+  store(ra, 0);
+  lds_barrier();
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    if (kt + 2 < nk) load(ra, kt + 2);
+    compute(0);
+    store(rb, 1);
+    lds_barrier();
+    if (kt + 3 < nk) load(rb, kt + 3);
+    compute(1);
+    if (kt + 2 < nk) store(ra, 0);
+    lds_barrier();
+  }
+  if (kt < nk) compute(0);
+
+  const float scale = (SRC == kSrcNvfp4) ? (*xts) * (*wts) : 1.0f;
+  const bool full_n = n0 + BN <= N && (N & 3) == 0;
+#pragma unroll
+  for (int i = 0; i < WM_T; ++i) {
+    const int m = m0 + wm * WM_T * 32 + i * 32 + r32;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < WN_T; ++j) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * WN_T * 32 + j * 32 + 8 * g + 4 * h;
+        const int64_t off = (int64_t)m * N + n;
+        float y[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[r] = acc[j][i][4 * g + r] * scale;
+        if (full_n) {
+          if constexpr (OUT == kOutF32)
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(Y) + off) = make_float4(y[0], y[1], y[2], y[3]);
+          else
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(Y) + off) =
+                make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+        } else {
+          for (int r = 0; r < 4 && n + r < N; ++r) {
+            if constexpr (OUT == kOutF32)
+              reinterpret_cast<float*>(Y)[off + r] = y[r];
+            else
+              reinterpret_cast<uint16_t*>(Y)[off + r] = __builtin_bit_cast(uint16_t, (__bf16)y[r]);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int SRC, int OUT>
+static hipError_t launch_bf16_pipe(const void* x, const uint8_t* xs, const float* xts, const void* w,
+                                   const uint8_t* ws, const float* wts, void* y, int64_t M, int64_t N,
+                                   int64_t K, const int32_t* decision, int32_t want, hipStream_t s) {
+  constexpr size_t lds = 2 * (size_t)(256 * 64 * 2 * 2);
+  auto kern = k_gemm_bf16_pipe<SRC, OUT>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(512), lds, s, x, xs, xts, w, ws, wts, y, (int)M,
+                     (int)N, (int)K, decision, want);
+  return hipGetLastError();
+}
+
+// The pipelined kernel needs K % 64 == 0 and 32-bit buffer offsets.
+template <int SRC>
+static bool pipe_ok(int64_t M, int64_t N, int64_t K) {
+  const int64_t row = SRC == kSrcBf16 ? 2 * K : K / 2;
+  return K % 64 == 0 && M * row < (1ll << 31) && N * row < (1ll << 31);
+}
+
 template <int SRC>
 static hipError_t launch_bf16mfma(const void* x, const uint8_t* xs, const float* xts, const void* w,
                                   const uint8_t* ws, const float* wts, void* y, int out_dtype,
                                   int64_t M, int64_t N, int64_t K, const int32_t* decision,
                                   int32_t want, hipStream_t s) {
+  if (pipe_ok<SRC>(M, N, K)) {
+    if (out_dtype == kOutF32)
+      return launch_bf16_pipe<SRC, kOutF32>(x, xs, xts, w, ws, wts, y, M, N, K, decision, want, s);
+    return launch_bf16_pipe<SRC, kOutBf16>(x, xs, xts, w, ws, wts, y, M, N, K, decision, want, s);
+  }
   constexpr int WM = 4, WN = 2;
   constexpr int BM = 64 * WM, BN = 64 * WN;
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);

@@ -12,9 +12,9 @@
 //     y = s_tx * s_tw * sum_32-blocks 2^(ex + ew) sum_k e2m1_x e2m1_w.
 // Every product and block sum is exact; only the float32 accumulation rounds.
 //
-// Tiling as gemm_i8.hip (256 x 128 per workgroup, 4 waves of 128 x 64,
-// 64-byte LDS rows holding 128 FP4 codes per stage); the per-row E8M0 bytes
-// of a stage (4 per row) sit in LDS next to the codes.
+// Two kernels: a pipelined one (the INT8 kernel's structure, see below) for
+// K % 128 == 0, and a simple double-buffered one for any K % 32 == 0.  In
+// both the per-row E8M0 bytes of a stage sit in LDS next to the codes.
 #include "hdq_device.h"
 #include "hdq_internal.h"
 
@@ -176,10 +176,198 @@ __global__ __launch_bounds__(256) void k_gemm_fp4mx(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined kernel for K % 128 == 0: the INT8 kernel's structure (256 x 256
+// tile, 8 waves as 2 x 4 of 128 x 64, two register sets prefetching the next
+// two stages through buffer loads, double-buffered LDS, LDS-only barriers)
+// with 128 K per stage: 64-byte code rows (swz64; substep s of 64 K gives
+// lane half h chunk 2s + h) and, per row, the stage's four E8M0 bytes (one
+// per 32 K, from the even E4M3 byte of each MX pair).
+struct Fp4PipeStage {
+  uint4 x[2], w[2];  // codes: 2 x 16-byte chunks per operand per thread
+  uint32_t xs, ws;   // 4 E4M3 bytes (2 MX pairs) per operand per thread
+};
+
+__device__ __forceinline__ uint32_t e8m0x2_from_pairs(uint32_t b) {
+  return e4m3_pow2_to_e8m0(b & 0xffu) | (e4m3_pow2_to_e8m0((b >> 16) & 0xffu) << 8);
+}
+
+template <int OUT>
+__global__ __launch_bounds__(512) void k_gemm_fp4mx_pipe(
+    const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xsc, const float* __restrict__ xts,
+    const uint8_t* __restrict__ wc, const uint8_t* __restrict__ wsc, const float* __restrict__ wts,
+    void* __restrict__ Y, int M, int N, int K, const int32_t* __restrict__ decision, int32_t want) {
+  if (decision != nullptr && *decision != want) return;
+  constexpr int BM = 256, BN = 256, BK = 128, WM_T = 4, WN_T = 2;
+  constexpr int XB = BM * BK / 2, WB = BN * BK / 2;  // code bytes per stage
+  constexpr int SB = XB + WB + (BM + BN) * 4;         // + E8M0 bytes
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % 2, wn = wave / 2;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  int tm, tn;
+  xcd_tile(tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int ld = K / 2, lds_ = K / 16;
+
+  const __amdgpu_buffer_rsrc_t xres = make_rsrc(xc + (int64_t)m0 * ld, (uint32_t)((int64_t)(M - m0) * ld));
+  const __amdgpu_buffer_rsrc_t wres = make_rsrc(wc + (int64_t)n0 * ld, (uint32_t)((int64_t)(N - n0) * ld));
+  const __amdgpu_buffer_rsrc_t xsres = make_rsrc(xsc + (int64_t)m0 * lds_, (uint32_t)((int64_t)(M - m0) * lds_));
+  const __amdgpu_buffer_rsrc_t wsres = make_rsrc(wsc + (int64_t)n0 * lds_, (uint32_t)((int64_t)(N - n0) * lds_));
+  const int cr = tid >> 2, cc = tid & 3;  // code chunks: 4 threads per row, 128 rows per round
+  const uint32_t cvoff = (uint32_t)(cr * ld + 16 * cc);
+  const int cdst = cr * 64 + 16 * (cc ^ swz64(cr));
+  const int sr = tid >> 1, sc = tid & 1;  // scales: 2 threads per row, 4 bytes each
+  const uint32_t svoff = (uint32_t)(sr * lds_ + 4 * sc);
+  const int sdst = sr * 4 + 2 * sc;
+
+  auto load = [&](Fp4PipeStage& st, int kt) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      st.x[p] = buf_load16(xres, cvoff, kt * (BK / 2) + p * 128 * ld);
+      st.w[p] = buf_load16(wres, cvoff, kt * (BK / 2) + p * 128 * ld);
+    }
+    st.xs = __builtin_amdgcn_raw_buffer_load_b32(xsres, (int)svoff, kt * (BK / 16), 0);
+    st.ws = __builtin_amdgcn_raw_buffer_load_b32(wsres, (int)svoff, kt * (BK / 16), 0);
+  };
+  auto store = [&](const Fp4PipeStage& st, int buf) {
+    uint8_t* base = smem + buf * SB;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      *reinterpret_cast<uint4*>(base + cdst + p * 128 * 64) = st.x[p];
+      *reinterpret_cast<uint4*>(base + XB + cdst + p * 128 * 64) = st.w[p];
+    }
+    *reinterpret_cast<uint16_t*>(base + XB + WB + sdst) = (uint16_t)e8m0x2_from_pairs(st.xs);
+    *reinterpret_cast<uint16_t*>(base + XB + WB + BM * 4 + sdst) = (uint16_t)e8m0x2_from_pairs(st.ws);
+  };
+
+  v16f acc[WN_T][WM_T];
+#pragma unroll
+  for (int j = 0; j < WN_T; ++j)
+#pragma unroll
+    for (int i = 0; i < WM_T; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.0f;
+
+  const int h = lane >> 5, r32 = lane & 31;
+  auto compute = [&](int buf) {
+    const uint8_t* lx = smem + buf * SB;
+    const uint8_t* lw = lx + XB;
+    const uint8_t* lxs = lx + XB + WB;
+    const uint8_t* lws = lxs + BM * 4;
+    uint32_t xe4[WM_T], we4[WN_T];
+#pragma unroll
+    for (int i = 0; i < WM_T; ++i) xe4[i] = *reinterpret_cast<const uint32_t*>(lxs + (wm * WM_T * 32 + i * 32 + r32) * 4);
+#pragma unroll
+    for (int j = 0; j < WN_T; ++j) we4[j] = *reinterpret_cast<const uint32_t*>(lws + (wn * WN_T * 32 + j * 32 + r32) * 4);
+#pragma unroll 1  // unrolled, the two substeps' fragments overflow 256 VGPRs
+    for (int ks = 0; ks < BK / 64; ++ks) {
+      const int g = 2 * ks + h;  // this lane's 32-K group within the stage
+      v8i xf[WM_T], wf[WN_T];
+      int xe[WM_T], we[WN_T];
+#pragma unroll
+      for (int i = 0; i < WM_T; ++i) {
+        const int r = wm * WM_T * 32 + i * 32 + r32;
+        const v4i v = *reinterpret_cast<const v4i*>(lx + r * 64 + 16 * (g ^ swz64(r)));
+        xf[i] = v8i{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+        xe[i] = (int)((xe4[i] >> (8 * g)) & 0xffu);
+      }
+#pragma unroll
+      for (int j = 0; j < WN_T; ++j) {
+        const int r = wn * WN_T * 32 + j * 32 + r32;
+        const v4i v = *reinterpret_cast<const v4i*>(lw + r * 64 + 16 * (g ^ swz64(r)));
+        wf[j] = v8i{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+        we[j] = (int)((we4[j] >> (8 * g)) & 0xffu);
+      }
+#pragma unroll
+      for (int j = 0; j < WN_T; ++j)
+#pragma unroll
+        for (int i = 0; i < WM_T; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[j], xf[i], acc[j][i], 4, 4, 0,
+                                                                        we[j], 0, xe[i]);
+    }
+  };
+
+  const int nk = K / BK;
+  Fp4PipeStage ra, rb;
+  load(ra, 0);
+  if (nk > 1) load(rb, 1);
+  store(ra, 0);
+  lds_barrier();
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    if (kt + 2 < nk) load(ra, kt + 2);
+    compute(0);
+    store(rb, 1);
+    lds_barrier();
+    if (kt + 3 < nk) load(rb, kt + 3);
+    compute(1);
+    if (kt + 2 < nk) store(ra, 0);
+    lds_barrier();
+  }
+  if (kt < nk) compute(0);
+
+  const float scale = (*xts) * (*wts);
+  const bool full_n = n0 + BN <= N && (N & 3) == 0;
+#pragma unroll
+  for (int i = 0; i < WM_T; ++i) {
+    const int m = m0 + wm * WM_T * 32 + i * 32 + r32;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < WN_T; ++j) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * WN_T * 32 + j * 32 + 8 * g + 4 * h;
+        const int64_t off = (int64_t)m * N + n;
+        float y[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[r] = acc[j][i][4 * g + r] * scale;
+        if (full_n) {
+          if constexpr (OUT == kOutF32)
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(Y) + off) = make_float4(y[0], y[1], y[2], y[3]);
+          else
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(Y) + off) =
+                make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+        } else {
+          for (int r = 0; r < 4 && n + r < N; ++r) {
+            if constexpr (OUT == kOutF32)
+              reinterpret_cast<float*>(Y)[off + r] = y[r];
+            else
+              reinterpret_cast<uint16_t*>(Y)[off + r] = __builtin_bit_cast(uint16_t, (__bf16)y[r]);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int OUT>
+static hipError_t launch_fp4_pipe(const uint8_t* xc, const uint8_t* xs, const float* xts,
+                                  const uint8_t* wc, const uint8_t* ws, const float* wts, void* y,
+                                  int64_t M, int64_t N, int64_t K, const int32_t* decision,
+                                  int32_t want, hipStream_t s) {
+  constexpr size_t lds = 2 * (size_t)(256 * 64 * 2 + 512 * 4);
+  auto kern = k_gemm_fp4mx_pipe<OUT>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(512), lds, s, xc, xs, xts, wc, ws, wts, y, (int)M,
+                     (int)N, (int)K, decision, want);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_nvfp4_mx(const uint8_t* xc, const uint8_t* xs, const float* xts,
                                 const uint8_t* wc, const uint8_t* ws, const float* wts,
                                 void* y, int out_dtype, int64_t M, int64_t N, int64_t K,
                                 const int32_t* decision, int32_t want, hipStream_t s) {
+  // The pipelined kernel needs K % 128 == 0 and 32-bit buffer offsets.
+  if (K % 128 == 0 && M * K / 2 < (1ll << 31) && N * K / 2 < (1ll << 31)) {
+    if (out_dtype == kOutF32)
+      return launch_fp4_pipe<kOutF32>(xc, xs, xts, wc, ws, wts, y, M, N, K, decision, want, s);
+    return launch_fp4_pipe<kOutBf16>(xc, xs, xts, wc, ws, wts, y, M, N, K, decision, want, s);
+  }
   constexpr int WM = 4, WN = 2;
   constexpr int BM = 64 * WM, BN = 64 * WN;
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);

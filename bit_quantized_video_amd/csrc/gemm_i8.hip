@@ -192,9 +192,237 @@ __global__ __launch_bounds__(256) void k_gemm_i8i4(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined kernel for K % 128 == 0 (every CogVideoX shape).
+//  * Workgroup tile BM tokens x BN features; WAVES_M x WAVES_N waves, each
+//    wave WM_T x WN_T subtiles of 32 x 32.  With 8 waves (two per SIMD) one
+//    wave's LDS / global / barrier waits overlap the other wave's MFMAs.
+//  * K advances 128 per stage.  Two register sets hold the global loads of
+//    the next two stages (the loop is unrolled by two so the sets alternate
+//    without copies); LDS is double-buffered.  Loads for stage kt + 2 are
+//    issued before stage kt is computed and written to LDS after stage
+//    kt + 1 is, so two stages of compute cover their latency.  Barriers
+//    order LDS only (lds_barrier), leaving the prefetches in flight.
+//  * Operands arrive through buffer loads (rows past M or N read as zero;
+//    their outputs are not stored).  X rows are 128 bytes in LDS (swz128),
+//    packed INT4 W rows 64 bytes (swz64).  Within a stage, k-substep pair p
+//    (64 K) gives lane half h the K range [64p + 32h, +32): for W one
+//    16-byte read of packed nibbles unpacked to the two substeps' fragments,
+//    for X two 16-byte reads.  (Any assignment of K to lanes works as long as
+//    both operands use the same one.)
+template <int WAVES_M, int WAVES_N, int WM_T, int WN_T>
+struct I8Cfg {
+  static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
+  static constexpr int BM = WAVES_M * WM_T * 32, BN = WAVES_N * WN_T * 32, BK = 128;
+  static constexpr int XB = BM * BK, SB = XB + BN * BK / 2;  // LDS bytes per stage
+  static constexpr int XC = XB / 16 / THREADS;                // 16-byte loads per thread
+  static constexpr int WC = BN * BK / 2 / 16 / THREADS;
+  static constexpr int XROWS = THREADS / 8, WROWS = THREADS / 4;  // rows per load round
+  static_assert(XC >= 1 && WC >= 1, "tile too small for the workgroup");
+};
+
+template <int XC, int WC>
+struct I8Stage {
+  uint4 x[XC], w[WC];
+};
+
+template <int WAVES_M, int WAVES_N, int WM_T, int WN_T, int OUT>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_i8i4_pipe(
+    const int8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ W4,
+    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K,
+    const int32_t* __restrict__ decision, int32_t want) {
+  if (decision != nullptr && *decision != want) return;
+  using C = I8Cfg<WAVES_M, WAVES_N, WM_T, WN_T>;
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, XB = C::XB, SB = C::SB;
+  using Stage = I8Stage<C::XC, C::WC>;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  int tm, tn;
+  xcd_tile(tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int ldw = K >> 1;
+
+  // Buffer resources over this tile's rows; 8 threads per 128-byte X row and
+  // 4 per W row (coalesced).  Load round p is XROWS (WROWS) rows further on,
+  // a multiple of 16, which leaves the swizzle unchanged: LDS destinations
+  // are a base plus an immediate.
+  const __amdgpu_buffer_rsrc_t xres = make_rsrc(X + (int64_t)m0 * K, (uint32_t)((int64_t)(M - m0) * K));
+  const __amdgpu_buffer_rsrc_t wres = make_rsrc(W4 + (int64_t)n0 * ldw, (uint32_t)((int64_t)(N - n0) * ldw));
+  const int xr0 = tid >> 3, xc0 = tid & 7, wr0 = tid >> 2, wc0 = tid & 3;
+  const uint32_t xvoff = (uint32_t)(xr0 * K + 16 * xc0);
+  const uint32_t wvoff = (uint32_t)(wr0 * ldw + 16 * wc0);
+  const int xdst = xr0 * 128 + 16 * (xc0 ^ swz128(xr0));
+  const int wdst = XB + wr0 * 64 + 16 * (wc0 ^ swz64(wr0));
+  auto load = [&](Stage& st, int kt) {
+#pragma unroll
+    for (int p = 0; p < C::XC; ++p) st.x[p] = buf_load16(xres, xvoff, kt * BK + p * C::XROWS * K);
+#pragma unroll
+    for (int p = 0; p < C::WC; ++p) st.w[p] = buf_load16(wres, wvoff, kt * (BK / 2) + p * C::WROWS * ldw);
+  };
+  auto store = [&](const Stage& st, int buf) {
+    uint8_t* base = smem + buf * SB;
+#pragma unroll
+    for (int p = 0; p < C::XC; ++p) *reinterpret_cast<uint4*>(base + xdst + C::XROWS * 128 * p) = st.x[p];
+#pragma unroll
+    for (int p = 0; p < C::WC; ++p) *reinterpret_cast<uint4*>(base + wdst + C::WROWS * 64 * p) = st.w[p];
+  };
+
+  v16i acc[WN_T][WM_T];
+#pragma unroll
+  for (int j = 0; j < WN_T; ++j)
+#pragma unroll
+    for (int i = 0; i < WM_T; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[j][i][e] = 0;
+
+  const int h = lane >> 5, r32 = lane & 31;
+  auto compute = [&](int buf) {
+    const uint8_t* lx = smem + buf * SB;
+    const uint8_t* lw = lx + XB;
+#pragma unroll
+    for (int p = 0; p < BK / 64; ++p) {
+      v4i xf[WM_T][2];
+#pragma unroll
+      for (int i = 0; i < WM_T; ++i) {
+        const int r = wm * WM_T * 32 + i * 32 + r32;
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          xf[i][s] = *reinterpret_cast<const v4i*>(lx + r * 128 + 16 * ((4 * p + 2 * h + s) ^ swz128(r)));
+      }
+#pragma unroll
+      for (int j = 0; j < WN_T; ++j) {
+        const int r = wn * WN_T * 32 + j * 32 + r32;
+        const uint4 packed = *reinterpret_cast<const uint4*>(lw + r * 64 + 16 * ((2 * p + h) ^ swz64(r)));
+        uint4 lo, hi;
+        unpack_int4x32(packed, lo, hi);
+        const v4i w0 = v4i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w};
+        const v4i w1 = v4i{(int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+#pragma unroll
+        for (int i = 0; i < WM_T; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(w0, xf[i][0], acc[j][i], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < WM_T; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(w1, xf[i][1], acc[j][i], 0, 0, 0);
+      }
+    }
+  };
+
+  const int nk = K / BK;
+  Stage ra, rb;
+  load(ra, 0);
+  if (nk > 1) load(rb, 1);
+  store(ra, 0);
+  lds_barrier();
+  // Pairs of stages; one loop exit keeps the accumulators in one register
+  // allocation.  An odd last stage (left in LDS buffer 0) follows the loop.
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    // stage kt in LDS buffer 0, stage kt + 1 in rb
+    if (kt + 2 < nk) load(ra, kt + 2);
+    compute(0);
+    store(rb, 1);
+    lds_barrier();
+    // stage kt + 1 in LDS buffer 1, stage kt + 2 in ra
+    if (kt + 3 < nk) load(rb, kt + 3);
+    compute(1);
+    if (kt + 2 < nk) store(ra, 0);
+    lds_barrier();
+  }
+  if (kt < nk) compute(0);
+
+  // Epilogue: lane holds token m = ... + (lane & 31) and, for g = 0..3,
+  // features n = 8g + 4h + 0..3 of each 32 x 32 subtile.
+  const bool full_n = n0 + BN <= N && (N & 3) == 0;
+#pragma unroll
+  for (int i = 0; i < WM_T; ++i) {
+    const int m = m0 + wm * WM_T * 32 + i * 32 + r32;
+    if (m >= M) continue;
+    const float sxm = sx[m];
+#pragma unroll
+    for (int j = 0; j < WN_T; ++j) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * WN_T * 32 + j * 32 + 8 * g + 4 * h;
+        const int64_t off = (int64_t)m * N + n;
+        int32_t a[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) a[r] = acc[j][i][4 * g + r] >> 4;
+        if (full_n) {
+          if constexpr (OUT == kOutI32) {
+            *reinterpret_cast<int4*>(reinterpret_cast<int32_t*>(Y) + off) = make_int4(a[0], a[1], a[2], a[3]);
+          } else {
+            const float4 swn = *reinterpret_cast<const float4*>(sw + n);
+            const float y0 = ((float)a[0] * sxm) * swn.x, y1 = ((float)a[1] * sxm) * swn.y;
+            const float y2 = ((float)a[2] * sxm) * swn.z, y3 = ((float)a[3] * sxm) * swn.w;
+            if constexpr (OUT == kOutF32)
+              *reinterpret_cast<float4*>(reinterpret_cast<float*>(Y) + off) = make_float4(y0, y1, y2, y3);
+            else
+              *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(Y) + off) =
+                  make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
+          }
+        } else {
+          for (int r = 0; r < 4; ++r) {
+            if (n + r >= N) break;
+            if constexpr (OUT == kOutI32) {
+              reinterpret_cast<int32_t*>(Y)[off + r] = a[r];
+            } else {
+              const float y = ((float)a[r] * sxm) * sw[n + r];
+              if constexpr (OUT == kOutF32)
+                reinterpret_cast<float*>(Y)[off + r] = y;
+              else
+                reinterpret_cast<uint16_t*>(Y)[off + r] = __builtin_bit_cast(uint16_t, (__bf16)y);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int WAVES_M, int WAVES_N, int WM_T, int WN_T, int OUT>
+static hipError_t launch_pipe(const int8_t* x, const float* sx, const uint8_t* w4, const float* sw,
+                              void* y, int64_t M, int64_t N, int64_t K, const int32_t* decision,
+                              int32_t want, hipStream_t s) {
+  using C = I8Cfg<WAVES_M, WAVES_N, WM_T, WN_T>;
+  constexpr size_t lds = 2 * (size_t)C::SB;
+  auto kern = k_gemm_i8i4_pipe<WAVES_M, WAVES_N, WM_T, WN_T, OUT>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int64_t tiles = ((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(C::THREADS), lds, s, x, sx, w4, sw, y, (int)M,
+                     (int)N, (int)K, decision, want);
+  return hipGetLastError();
+}
+
+// 8 waves as 2 (tokens) x 4 (features), each 128 x 64: two waves per SIMD,
+// the fastest of the layouts measured on the CogVideoX shapes.
+#ifndef HDQ_I8_WAVES_M
+#define HDQ_I8_WAVES_M 2
+#define HDQ_I8_WAVES_N 4
+#define HDQ_I8_WM_T 4
+#define HDQ_I8_WN_T 2
+#endif
+
+static hipError_t launch_pipe_out(const int8_t* x, const float* sx, const uint8_t* w4, const float* sw,
+                                  void* y, int out_dtype, int64_t M, int64_t N, int64_t K,
+                                  const int32_t* decision, int32_t want, hipStream_t s) {
+#define HDQ_I8_CFG HDQ_I8_WAVES_M, HDQ_I8_WAVES_N, HDQ_I8_WM_T, HDQ_I8_WN_T
+  if (out_dtype == kOutF32) return launch_pipe<HDQ_I8_CFG, kOutF32>(x, sx, w4, sw, y, M, N, K, decision, want, s);
+  if (out_dtype == kOutBf16) return launch_pipe<HDQ_I8_CFG, kOutBf16>(x, sx, w4, sw, y, M, N, K, decision, want, s);
+  return launch_pipe<HDQ_I8_CFG, kOutI32>(x, sx, w4, sw, y, M, N, K, decision, want, s);
+#undef HDQ_I8_CFG
+}
+
 hipError_t launch_gemm_i8i4(const int8_t* x, const float* sx, const uint8_t* w4, const float* sw,
                             void* y, int out_dtype, int64_t M, int64_t N, int64_t K,
                             const int32_t* decision, int32_t want, hipStream_t s) {
+  // The pipelined kernel addresses each operand with 32-bit buffer offsets.
+  if (K % 128 == 0 && M * K < (1ll << 31) && N * K / 2 < (1ll << 31))
+    return launch_pipe_out(x, sx, w4, sw, y, out_dtype, M, N, K, decision, want, s);
   constexpr int WM = 4, WN = 2;
   constexpr int BM = 64 * WM, BN = 64 * WN;
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);

@@ -147,4 +147,33 @@ __device__ __forceinline__ void xcd_tile(int tiles_m, int tiles_n, int& tm, int&
   tn = logical - tm * tiles_n;
 }
 
+// ---- multi-stage LDS pipelines ------------------------------------------------
+// Conflict-free 16-byte-chunk swizzles for fragment reads in which lane l
+// reads row l % 32 (consecutive lanes, consecutive rows), both under a 32-bank
+// (8 lanes per LDS cycle) and a 64-bank (16 lanes per cycle) model.
+// 64-byte rows (4 chunks) and 128-byte rows (8 chunks):
+__device__ __forceinline__ int swz64(int r) { return ((r >> 2) & 3) ^ (r & 2); }
+__device__ __forceinline__ int swz128(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS accesses
+// (lgkmcnt) but not for its outstanding global loads, so prefetches for later
+// pipeline stages stay in flight across the barrier.  (__syncthreads()'s
+// fence would also wait for every global load.)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// ---- buffer loads ----------------------------------------------------------------
+// Raw buffer resource over [base, base + bytes): loads at offsets >= bytes
+// return zeros, so tile rows past the end of a tensor read as zero.  The
+// scalar offset argument keeps per-stage / per-row-block offsets in SGPRs.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
 }  // namespace hdq
