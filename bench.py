@@ -55,8 +55,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--blocks", type=int, default=42)
     ap.add_argument("--timesteps", type=int, default=3)
-    ap.add_argument("--fp4", choices=["nvfp4", "mx"], default="nvfp4",
-                    help="NVFP4 recipe: plain (exact bf16-MFMA GEMM) or MX-compatible (FP4 MFMA)")
+    ap.add_argument("--fp4", choices=["nvfp4", "mx"], default="mx",
+                    help="NVFP4 recipe of the headline run: MX-compatible (FP4 MFMA, default) or "
+                         "plain (exact, bf16 MFMA); the schedule also times the other one")
     ap.add_argument("--config", type=int, default=5, help="5: schedule; 1-4: one linear layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-copy", action="store_true")
@@ -118,7 +119,7 @@ def build_schedule(args, hdq, synth):
     M = synth.M_COGVIDEOX
     gen = torch.Generator(device=dev)
     gen.manual_seed(0)
-    fp4 = hdq.FMT_NVFP4_MX if args.fp4 == "mx" else hdq.FMT_NVFP4
+    recipes = {"mx": hdq.FMT_NVFP4_MX, "nvfp4": hdq.FMT_NVFP4}
     s_levels = synth.schedule_noise_levels(args.blocks, args.timesteps)
     blocks = []
     t0 = time.time()
@@ -130,9 +131,8 @@ def build_schedule(args, hdq, synth):
             prev_out = [synth.device_noisy_copy(x, float(s_levels[b, li, t]), gen)
                         for t in range(args.timesteps)]
             w = synth.device_gaussian((N, K), 0.02, gen, dev)
-            W = hdq.LinearWeights(w, HB, fp4_fmt=fp4)
-            layers.append(dict(name=name, K=K, N=N, x=x, prev_in=prev_in, prev_out=prev_out, W=W,
-                               Wd=W.desc()))
+            W = {r: hdq.LinearWeights(w, HB, fp4_fmt=f) for r, f in recipes.items()}
+            layers.append(dict(name=name, K=K, N=N, x=x, prev_in=prev_in, prev_out=prev_out, W=W))
         blocks.append(layers)
         if b % 6 == 5 or b == args.blocks - 1:
             torch.cuda.synchronize()
@@ -143,20 +143,21 @@ def build_schedule(args, hdq, synth):
     for name, K, N in synth.SCHEDULE_LAYERS:
         shared.append(dict(
             xq8=hdq.QuantizedTensor(hdq.FMT_INT8_ROW, M, K, HB, dev),
-            xq4=hdq.QuantizedTensor(fp4, M, K, HB, dev),
+            xq4={r: hdq.QuantizedTensor(f, M, K, HB, dev) for r, f in recipes.items()},
             y=torch.empty(M, N, dtype=torch.bfloat16, device=dev)))
     ws_sel = torch.empty(hdq.workspace_bytes(hdq.OP_SELECT, M, 12288, M * 12288), dtype=torch.uint8,
                          device=dev)
     T, B, L = args.timesteps, args.blocks, len(synth.SCHEDULE_LAYERS)
     dec = torch.full((T, B, L, 1), -1, dtype=torch.int32, device=dev)
     sts = torch.zeros((T, B, L, 5), dtype=torch.float32, device=dev)
-    return dict(M=M, fp4=fp4, blocks=blocks, shared=shared, ws_sel=ws_sel, dec=dec, sts=sts,
+    return dict(M=M, recipes=recipes, blocks=blocks, shared=shared, ws_sel=ws_sel, dec=dec, sts=sts,
                 s_levels=s_levels)
 
 
-def run_schedule_step(S, args, hdq, events=None):
-    """One step: every timestep, block and layer.  With `events`, records 7
-    HIP events per layer call (stream order: select | q8 | q4 | g8 | g4 | gbf)."""
+def run_schedule_step(S, args, hdq, recipe, events=None):
+    """One step: every timestep, block and layer, NVFP4 layers in `recipe`.
+    With `events`, records 7 HIP events per layer call (stream order:
+    select | q8 | q4 | g8 | g4 | gbf)."""
     M = S["M"]
     k = 0
     for t in range(args.timesteps):
@@ -173,13 +174,15 @@ def run_schedule_step(S, args, hdq, events=None):
                 if ev: ev[1].record()
                 hdq.quantize(L["x"], HB, hdq.FMT_INT8_ROW, out=sh["xq8"], decision=d)
                 if ev: ev[2].record()
-                hdq.quantize(L["x"], HB, S["fp4"], tensor_amax=st[4:5], out=sh["xq4"], decision=d)
+                hdq.quantize(L["x"], HB, S["recipes"][recipe], tensor_amax=st[4:5], out=sh["xq4"][recipe],
+                             decision=d)
                 if ev: ev[3].record()
-                hdq.linear(hdq.PREC_INT8, None, L["W"], decision=d, xq=sh["xq8"], y=sh["y"])
+                W = L["W"][recipe]
+                hdq.linear(hdq.PREC_INT8, None, W, decision=d, xq=sh["xq8"], y=sh["y"])
                 if ev: ev[4].record()
-                hdq.linear(hdq.PREC_NVFP4, None, L["W"], decision=d, xq=sh["xq4"], y=sh["y"])
+                hdq.linear(hdq.PREC_NVFP4, None, W, decision=d, xq=sh["xq4"][recipe], y=sh["y"])
                 if ev: ev[5].record()
-                hdq.linear(hdq.PREC_BF16, L["x"], L["W"], decision=d, y=sh["y"])
+                hdq.linear(hdq.PREC_BF16, L["x"], W, decision=d, y=sh["y"])
                 if ev: ev[6].record()
     return k
 
@@ -224,7 +227,8 @@ def cpu_baseline_schedule(S, args, synth):
     for li, (name, K, N) in enumerate(synth.SCHEDULE_LAYERS):
         L = S["blocks"][0][li]
         np16 = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
-        pi, po, x, w = np16(L["prev_in"]), np16(L["prev_out"][0]), np16(L["x"]), np16(L["W"].w_bf16)
+        pi, po, x = np16(L["prev_in"]), np16(L["prev_out"][0]), np16(L["x"])
+        w = np16(L["W"][args.fp4].w_bf16)
         # weights (untimed preparation)
         qw, sw = O.quant_int(w, HB, 7)
         wc, we, wst = O.quant_nvfp4(w, HB, mx=fp4_mx)
@@ -254,36 +258,64 @@ def cpu_baseline_schedule(S, args, synth):
                        f"linearly to all rows; weight preparation untimed")}
 
 
-def bench_schedule(args, hdq, synth):
-    S = build_schedule(args, hdq, synth)
-    M = S["M"]
-    flops_step = sum(2.0 * M * N * K for _, K, N in synth.SCHEDULE_LAYERS) * args.blocks * args.timesteps
-    log("warmup")
+def time_schedule(S, args, hdq, synth, recipe):
+    """Warmup, then exactly args.steps timed steps; per-kernel event times."""
+    log(f"warmup ({recipe})")
     for _ in range(args.warmup):
-        run_schedule_step(S, args, hdq)
+        run_schedule_step(S, args, hdq, recipe)
     n_calls = args.timesteps * args.blocks * len(synth.SCHEDULE_LAYERS)
     events = [[[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(n_calls)]
               for _ in range(args.steps)]
     torch.cuda.synchronize()
-    log(f"timing {args.steps} steps")
+    log(f"timing {args.steps} steps ({recipe})")
     t0 = time.perf_counter()
     for s in range(args.steps):
-        run_schedule_step(S, args, hdq, events[s])
+        run_schedule_step(S, args, hdq, recipe, events[s])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms_per_step = 1e3 * elapsed / args.steps
     kt, decisions = schedule_kernel_times(S, args, events, synth)
+    return 1e3 * elapsed / args.steps, kt, decisions
+
+
+def schedule_quality(S, hdq):
+    """Output error of each precision on one NVFP4-sized layer (block 0 FFN
+    up-projection): relative Frobenius distance of the bf16 output from the
+    unquantized bf16 GEMM's."""
+    L = S["blocks"][0][2]
+    x, ref = L["x"], None
+    out = {}
+    for name, prec, W in (("bf16", hdq.PREC_BF16, L["W"]["mx"]), ("int8", hdq.PREC_INT8, L["W"]["mx"]),
+                          ("nvfp4_mx", hdq.PREC_NVFP4, L["W"]["mx"]),
+                          ("nvfp4", hdq.PREC_NVFP4, L["W"]["nvfp4"])):
+        y = hdq.linear(prec, x, W, y_dtype=hdq.DTYPE_F32)
+        if ref is None:
+            ref = y
+            continue
+        out[name] = float(torch.linalg.norm(y - ref) / torch.linalg.norm(ref))
+    return out
+
+
+def bench_schedule(args, hdq, synth):
+    S = build_schedule(args, hdq, synth)
+    M = S["M"]
+    flops_step = sum(2.0 * M * N * K for _, K, N in synth.SCHEDULE_LAYERS) * args.blocks * args.timesteps
+    n_calls = args.timesteps * args.blocks * len(synth.SCHEDULE_LAYERS)
+    other = "nvfp4" if args.fp4 == "mx" else "mx"
+    runs = {r: time_schedule(S, args, hdq, synth, r) for r in (args.fp4, other)}
+    ms_per_step, kt, decisions = runs[args.fp4]
     ks = kt.summary()
     counts = {p: int((decisions == v).sum()) for p, v in (("nvfp4", 0), ("int8", 1), ("bf16", 2))}
     # dominant kernel: the selected-path kernel with the most time
     main_kinds = ["gemm_int8", "gemm_nvfp4", "gemm_bf16", "quant_int8", "quant_nvfp4", "select_stats"]
     dom = max((k for k in main_kinds if k in ks), key=lambda k: ks[k]["total_ms"])
-    roof = roofline_for(dom, ks[dom], args)
+    roof = roofline_for(dom, ks[dom], args.fp4)
     q_bytes = sum(kt.work[k] for k in ("quant_int8", "quant_nvfp4") if k in kt.work)
     q_ms = sum(kt.t[k] for k in ("quant_int8", "quant_nvfp4") if k in kt.t)
     # effective TOPS of the fused quant + linear alone (selected kernels only)
     ql_ms = q_ms + sum(kt.t.get(k, 0.0) for k in ("gemm_int8", "gemm_nvfp4", "gemm_bf16"))
     ql_flops = sum(kt.work.get(k, 0.0) for k in ("gemm_int8", "gemm_nvfp4", "gemm_bf16"))
+    o_ms, o_kt, _ = runs[other]
+    o_ks = o_kt.summary()
     result = {
         "metric": METRIC,
         "value": round(flops_step / (ms_per_step * 1e-3) / 1e12, 2),
@@ -291,19 +323,27 @@ def bench_schedule(args, hdq, synth):
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int8+nvfp4" if args.fp4 == "nvfp4" else "int8+nvfp4_mx",
+        "dtype": "int8+nvfp4_mx" if args.fp4 == "mx" else "int8+nvfp4",
         "data": "synthetic",
         "config": {"workload": (f"DMPQ schedule: {args.blocks} CogVideoX-5B blocks x (QKV 3072->9216, "
                                 f"out 3072->3072, FFN 3072->12288->3072) x {args.timesteps} timesteps, "
                                 f"M=17776 tokens, Hadamard block 128, delta thresh 0.1, ratio thresh 50, "
-                                f"fp4 recipe {args.fp4}"),
+                                f"NVFP4 recipe {'MX-compatible (FP4 MFMA)' if args.fp4 == 'mx' else 'plain (bf16 MFMA)'}"),
                    "global_batch": M, "layer_calls_per_step": n_calls},
         "roofline": roof,
         "quant_gbps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1) if q_ms > 0 else None,
         "fused_quant_linear_tops": round(ql_flops / (ql_ms * 1e-3) / 1e12, 2) if ql_ms > 0 else None,
         "decisions": counts,
-        "kernels": {k: {"launches": v["launches"], "total_ms": v["total_ms"], "avg_us": v["avg_us"]}
+        "kernels": {k: {"launches": v["launches"], "total_ms": v["total_ms"], "avg_us": v["avg_us"],
+                        "rate": round(v["rate"] / 1e12, 3)}
                     for k, v in ks.items()},
+        "other_recipe": {"recipe": other,
+                         "value": round(flops_step / (o_ms * 1e-3) / 1e12, 2),
+                         "ms_per_step": round(o_ms, 3),
+                         "gemm_nvfp4": {k: o_ks["gemm_nvfp4"][k] for k in ("launches", "total_ms", "avg_us")}
+                         | {"rate_tflops": round(o_ks["gemm_nvfp4"]["rate"] / 1e12, 1)}
+                         if "gemm_nvfp4" in o_ks else None},
+        "quality_rel_err_vs_bf16": schedule_quality(S, hdq),
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
@@ -312,10 +352,10 @@ def bench_schedule(args, hdq, synth):
     return result
 
 
-def roofline_for(kind, k, args):
+def roofline_for(kind, k, recipe):
     if kind.startswith("gemm"):
         dt = {"gemm_int8": "int8", "gemm_bf16": "bf16",
-              "gemm_nvfp4": "fp4" if args.fp4 == "mx" else "bf16"}[kind]
+              "gemm_nvfp4": "fp4" if recipe == "mx" else "bf16"}[kind]
         peak = PEAK[dt]
         ach = k["rate"]
         return {"kernel": kind, "bound": "mfma", "dtype": dt, "achieved": round(ach / 1e12, 1),

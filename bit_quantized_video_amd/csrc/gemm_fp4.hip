@@ -177,19 +177,20 @@ __global__ __launch_bounds__(256) void k_gemm_fp4mx(
 }
 
 // ---------------------------------------------------------------------------
-// Pipelined kernel for K % 128 == 0: the INT8 kernel's structure (256 x 256
+// Pipelined kernel for K % 256 == 0: the INT8 kernel's structure (256 x 256
 // tile, 8 waves as 2 x 4 of 128 x 64, two register sets prefetching the next
 // two stages through buffer loads, double-buffered LDS, LDS-only barriers)
-// with 128 K per stage: 64-byte code rows (swz64; substep s of 64 K gives
-// lane half h chunk 2s + h) and, per row, the stage's four E8M0 bytes (one
+// with 256 K per stage: 128-byte code rows (swz128; substep s of 64 K gives
+// lane half h chunk 2s + h) and, per row, the stage's eight E8M0 bytes (one
 // per 32 K, from the even E4M3 byte of each MX pair).
 struct Fp4PipeStage {
-  uint4 x[2], w[2];  // codes: 2 x 16-byte chunks per operand per thread
-  uint32_t xs, ws;   // 4 E4M3 bytes (2 MX pairs) per operand per thread
+  uint4 x[4], w[4];  // codes: 4 x 16-byte chunks per operand per thread
+  uint2 xs, ws;      // 8 E4M3 bytes (4 MX pairs) per operand per thread
 };
 
-__device__ __forceinline__ uint32_t e8m0x2_from_pairs(uint32_t b) {
-  return e4m3_pow2_to_e8m0(b & 0xffu) | (e4m3_pow2_to_e8m0((b >> 16) & 0xffu) << 8);
+__device__ __forceinline__ uint32_t e8m0x4_from_pairs(uint2 b) {
+  return e4m3_pow2_to_e8m0(b.x & 0xffu) | (e4m3_pow2_to_e8m0((b.x >> 16) & 0xffu) << 8) |
+         (e4m3_pow2_to_e8m0(b.y & 0xffu) << 16) | (e4m3_pow2_to_e8m0((b.y >> 16) & 0xffu) << 24);
 }
 
 template <int OUT>
@@ -198,9 +199,9 @@ __global__ __launch_bounds__(512) void k_gemm_fp4mx_pipe(
     const uint8_t* __restrict__ wc, const uint8_t* __restrict__ wsc, const float* __restrict__ wts,
     void* __restrict__ Y, int M, int N, int K, const int32_t* __restrict__ decision, int32_t want) {
   if (decision != nullptr && *decision != want) return;
-  constexpr int BM = 256, BN = 256, BK = 128, WM_T = 4, WN_T = 2;
+  constexpr int BM = 256, BN = 256, BK = 256, WM_T = 4, WN_T = 2;
   constexpr int XB = BM * BK / 2, WB = BN * BK / 2;  // code bytes per stage
-  constexpr int SB = XB + WB + (BM + BN) * 4;         // + E8M0 bytes
+  constexpr int SB = XB + WB + (BM + BN) * 8;         // + E8M0 bytes
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -215,31 +216,31 @@ __global__ __launch_bounds__(512) void k_gemm_fp4mx_pipe(
   const __amdgpu_buffer_rsrc_t wres = make_rsrc(wc + (int64_t)n0 * ld, (uint32_t)((int64_t)(N - n0) * ld));
   const __amdgpu_buffer_rsrc_t xsres = make_rsrc(xsc + (int64_t)m0 * lds_, (uint32_t)((int64_t)(M - m0) * lds_));
   const __amdgpu_buffer_rsrc_t wsres = make_rsrc(wsc + (int64_t)n0 * lds_, (uint32_t)((int64_t)(N - n0) * lds_));
-  const int cr = tid >> 2, cc = tid & 3;  // code chunks: 4 threads per row, 128 rows per round
+  const int cr = tid >> 3, cc = tid & 7;  // code chunks: 8 threads per row, 64 rows per round
   const uint32_t cvoff = (uint32_t)(cr * ld + 16 * cc);
-  const int cdst = cr * 64 + 16 * (cc ^ swz64(cr));
-  const int sr = tid >> 1, sc = tid & 1;  // scales: 2 threads per row, 4 bytes each
-  const uint32_t svoff = (uint32_t)(sr * lds_ + 4 * sc);
-  const int sdst = sr * 4 + 2 * sc;
+  const int cdst = cr * 128 + 16 * (cc ^ swz128(cr));
+  const int sr = tid >> 1, sc = tid & 1;  // scales: 2 threads per row, 8 bytes each
+  const uint32_t svoff = (uint32_t)(sr * lds_ + 8 * sc);
+  const int sdst = sr * 8 + 4 * sc;
 
   auto load = [&](Fp4PipeStage& st, int kt) {
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      st.x[p] = buf_load16(xres, cvoff, kt * (BK / 2) + p * 128 * ld);
-      st.w[p] = buf_load16(wres, cvoff, kt * (BK / 2) + p * 128 * ld);
+    for (int p = 0; p < 4; ++p) {
+      st.x[p] = buf_load16(xres, cvoff, kt * (BK / 2) + p * 64 * ld);
+      st.w[p] = buf_load16(wres, cvoff, kt * (BK / 2) + p * 64 * ld);
     }
-    st.xs = __builtin_amdgcn_raw_buffer_load_b32(xsres, (int)svoff, kt * (BK / 16), 0);
-    st.ws = __builtin_amdgcn_raw_buffer_load_b32(wsres, (int)svoff, kt * (BK / 16), 0);
+    st.xs = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(xsres, (int)svoff, kt * (BK / 16), 0));
+    st.ws = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(wsres, (int)svoff, kt * (BK / 16), 0));
   };
   auto store = [&](const Fp4PipeStage& st, int buf) {
     uint8_t* base = smem + buf * SB;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      *reinterpret_cast<uint4*>(base + cdst + p * 128 * 64) = st.x[p];
-      *reinterpret_cast<uint4*>(base + XB + cdst + p * 128 * 64) = st.w[p];
+    for (int p = 0; p < 4; ++p) {
+      *reinterpret_cast<uint4*>(base + cdst + p * 64 * 128) = st.x[p];
+      *reinterpret_cast<uint4*>(base + XB + cdst + p * 64 * 128) = st.w[p];
     }
-    *reinterpret_cast<uint16_t*>(base + XB + WB + sdst) = (uint16_t)e8m0x2_from_pairs(st.xs);
-    *reinterpret_cast<uint16_t*>(base + XB + WB + BM * 4 + sdst) = (uint16_t)e8m0x2_from_pairs(st.ws);
+    *reinterpret_cast<uint32_t*>(base + XB + WB + sdst) = e8m0x4_from_pairs(st.xs);
+    *reinterpret_cast<uint32_t*>(base + XB + WB + BM * 8 + sdst) = e8m0x4_from_pairs(st.ws);
   };
 
   v16f acc[WN_T][WM_T];
@@ -255,12 +256,7 @@ __global__ __launch_bounds__(512) void k_gemm_fp4mx_pipe(
     const uint8_t* lx = smem + buf * SB;
     const uint8_t* lw = lx + XB;
     const uint8_t* lxs = lx + XB + WB;
-    const uint8_t* lws = lxs + BM * 4;
-    uint32_t xe4[WM_T], we4[WN_T];
-#pragma unroll
-    for (int i = 0; i < WM_T; ++i) xe4[i] = *reinterpret_cast<const uint32_t*>(lxs + (wm * WM_T * 32 + i * 32 + r32) * 4);
-#pragma unroll
-    for (int j = 0; j < WN_T; ++j) we4[j] = *reinterpret_cast<const uint32_t*>(lws + (wn * WN_T * 32 + j * 32 + r32) * 4);
+    const uint8_t* lws = lxs + BM * 8;
 #pragma unroll 1  // unrolled, the two substeps' fragments overflow 256 VGPRs
     for (int ks = 0; ks < BK / 64; ++ks) {
       const int g = 2 * ks + h;  // this lane's 32-K group within the stage
@@ -269,16 +265,16 @@ __global__ __launch_bounds__(512) void k_gemm_fp4mx_pipe(
 #pragma unroll
       for (int i = 0; i < WM_T; ++i) {
         const int r = wm * WM_T * 32 + i * 32 + r32;
-        const v4i v = *reinterpret_cast<const v4i*>(lx + r * 64 + 16 * (g ^ swz64(r)));
+        const v4i v = *reinterpret_cast<const v4i*>(lx + r * 128 + 16 * (g ^ swz128(r)));
         xf[i] = v8i{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
-        xe[i] = (int)((xe4[i] >> (8 * g)) & 0xffu);
+        xe[i] = lxs[r * 8 + g];
       }
 #pragma unroll
       for (int j = 0; j < WN_T; ++j) {
         const int r = wn * WN_T * 32 + j * 32 + r32;
-        const v4i v = *reinterpret_cast<const v4i*>(lw + r * 64 + 16 * (g ^ swz64(r)));
+        const v4i v = *reinterpret_cast<const v4i*>(lw + r * 128 + 16 * (g ^ swz128(r)));
         wf[j] = v8i{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
-        we[j] = (int)((we4[j] >> (8 * g)) & 0xffu);
+        we[j] = lws[r * 8 + g];
       }
 #pragma unroll
       for (int j = 0; j < WN_T; ++j)
@@ -347,7 +343,7 @@ static hipError_t launch_fp4_pipe(const uint8_t* xc, const uint8_t* xs, const fl
                                   const uint8_t* wc, const uint8_t* ws, const float* wts, void* y,
                                   int64_t M, int64_t N, int64_t K, const int32_t* decision,
                                   int32_t want, hipStream_t s) {
-  constexpr size_t lds = 2 * (size_t)(256 * 64 * 2 + 512 * 4);
+  constexpr size_t lds = 2 * (size_t)(256 * 128 * 2 + 512 * 8);
   auto kern = k_gemm_fp4mx_pipe<OUT>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -362,8 +358,8 @@ hipError_t launch_gemm_nvfp4_mx(const uint8_t* xc, const uint8_t* xs, const floa
                                 const uint8_t* wc, const uint8_t* ws, const float* wts,
                                 void* y, int out_dtype, int64_t M, int64_t N, int64_t K,
                                 const int32_t* decision, int32_t want, hipStream_t s) {
-  // The pipelined kernel needs K % 128 == 0 and 32-bit buffer offsets.
-  if (K % 128 == 0 && M * K / 2 < (1ll << 31) && N * K / 2 < (1ll << 31)) {
+  // The pipelined kernel needs K % 256 == 0 and 32-bit buffer offsets.
+  if (K % 256 == 0 && M * K / 2 < (1ll << 31) && N * K / 2 < (1ll << 31)) {
     if (out_dtype == kOutF32)
       return launch_fp4_pipe<kOutF32>(xc, xs, xts, wc, ws, wts, y, M, N, K, decision, want, s);
     return launch_fp4_pipe<kOutBf16>(xc, xs, xts, wc, ws, wts, y, M, N, K, decision, want, s);

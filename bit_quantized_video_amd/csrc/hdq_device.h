@@ -62,14 +62,42 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // ---- block Hadamard rotation --------------------------------------------
-// Each lane holds 8 consecutive elements of a row; for a block size hb >= 8
-// the hb/8 lanes (lane & ~(hb/8 - 1)) .. hold one aligned block, for hb < 8
-// each lane holds 8/hb whole blocks.  Fast Walsh-Hadamard butterfly with
-// strides h = 1, 2, 4, ... ascending: the pair (i, i + h), i & h == 0,
-// becomes (u + v, u - v).  Strides 1..4 are inside the lane; stride 8g pairs
-// lane l with lane l ^ g: the lower lane keeps u + v, the upper lane forms
-// u - v as partner + (-own), which IEEE rounds exactly like u - v.  The
-// result is unnormalised (times sqrt(hb)).  hb is wave-uniform.
+// Fast Walsh-Hadamard butterfly on blocks of hb (2..128) consecutive
+// elements, strides h = 1, 2, 4, ... ascending: the pair (i, i + h),
+// i & h == 0, becomes (u + v, u - v), evaluated in float32 exactly as that
+// sequence (every rotated value is bit-identical to it).
+//
+// Each lane holds one 8-element chunk of a block; strides 1..4 run inside
+// the lane.  For hb >= 16 the hb/8 lanes of a block exchange values, and
+// lane l of the group does not hold chunk l but chunk fwht_chunk(l): lanes
+// are numbered so that chunk bit k is lane mask m_k = 1, 2, 7, 15 (a linear
+// relabelling over GF(2)), because lane ^ m_k is exactly what DPP reaches in
+// one instruction (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror,
+// row_mirror).  Stride 8 * 2^k is then one v_fmac_f32_dpp per element:
+//   x <- partner * S + x,  S = +1 on the lane whose chunk has bit k clear
+// (u + v) and -1 on the other, which computes -(u - v): each lane carries a
+// sign it knows (its lane partner always carries the same one), multiplying
+// by +-1 is exact, and the one rounding is that of u + v or u - v.  The
+// returned sign (+-1, the parity of the lane's chunk bits) restores the
+// values; callers fold it into the 1/sqrt(hb) multiply.
+__device__ __forceinline__ int fwht_lanes(int hb) { return hb >= 16 ? hb >> 3 : 1; }
+
+// The chunk of its block that lane l holds (0 for hb <= 8).
+__device__ __forceinline__ int fwht_chunk(int lane, int hb) {
+  const int nl = fwht_lanes(hb);
+  int L = lane & (nl - 1), c = 0;
+  if (nl >= 16 && (L & 8)) { c |= 8; L ^= 15; }
+  if (nl >= 8 && (L & 4)) { c |= 4; L ^= 7; }
+  return c | L;
+}
+
+// Index of the chunk lane `lane` loads, given the natural index `idx` of
+// chunk lane-slot `lane` (blocks of fwht_lanes(hb) slots are aligned).
+__device__ __forceinline__ int64_t fwht_src(int64_t idx, int lane, int hb) {
+  const int nl = fwht_lanes(hb);
+  return (idx & ~(int64_t)(nl - 1)) + fwht_chunk(lane, hb);
+}
+
 template <int H>
 __device__ __forceinline__ void fwht_stage_in(float (&x)[8]) {
 #pragma unroll
@@ -82,23 +110,50 @@ __device__ __forceinline__ void fwht_stage_in(float (&x)[8]) {
   }
 }
 
-template <int G>
-__device__ __forceinline__ void fwht_stage_x(float (&x)[8], int lane) {
-  const uint32_t flip = (lane & G) ? 0x80000000u : 0u;
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    x[i] = xor_lane<G>(x[i]) + __uint_as_float(__float_as_uint(x[i]) ^ flip);
-}
+// x <- dpp(x) * s + x for the 8 values.  The leading s_nop gives the two
+// wait states a DPP read needs after a VALU write of the same register;
+// inside and between these blocks every register is written >= 7
+// instructions before it is read again.
+#define HDQ_FMAC_DPP8(CTRL, NOP)                                                             \
+  asm(NOP                                                                                    \
+      "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"       \
+      "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"       \
+      "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"       \
+      "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"       \
+      "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"       \
+      "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"       \
+      "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"       \
+      "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1"           \
+      : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]),  \
+        "+v"(x[7])                                                                           \
+      : "v"(s))
 
-__device__ __forceinline__ void fwht8(float (&x)[8], int lane, int hb) {
+// Rotates the chunk held by this lane (see above); returns its sign.
+__device__ __forceinline__ float fwht8(float (&x)[8], int lane, int hb) {
   if (hb >= 2) fwht_stage_in<1>(x);
   if (hb >= 4) fwht_stage_in<2>(x);
   if (hb >= 8) fwht_stage_in<4>(x);
-  if (hb >= 16) fwht_stage_x<1>(x, lane);
-  if (hb >= 32) fwht_stage_x<2>(x, lane);
-  if (hb >= 64) fwht_stage_x<4>(x, lane);
-  if (hb >= 128) fwht_stage_x<8>(x, lane);
+  if (hb < 16) return 1.0f;
+  const int c = fwht_chunk(lane, hb);
+  {
+    const float s = (c & 1) ? -1.0f : 1.0f;
+    HDQ_FMAC_DPP8("quad_perm:[1,0,3,2]", "s_nop 1\n\t");
+  }
+  if (hb >= 32) {
+    const float s = (c & 2) ? -1.0f : 1.0f;
+    HDQ_FMAC_DPP8("quad_perm:[2,3,0,1]", "");
+  }
+  if (hb >= 64) {
+    const float s = (c & 4) ? -1.0f : 1.0f;
+    HDQ_FMAC_DPP8("row_half_mirror", "");
+  }
+  if (hb >= 128) {
+    const float s = (c & 8) ? -1.0f : 1.0f;
+    HDQ_FMAC_DPP8("row_mirror", "");
+  }
+  return (__builtin_popcount(c) & 1) ? -1.0f : 1.0f;
 }
+#undef HDQ_FMAC_DPP8
 
 // ---- FP8 E4M3 block scales (unsigned) -------------------------------------
 // Nearest E4M3 value of t >= 0, ties to even, saturating at 448 (0x7e).

@@ -15,7 +15,8 @@
 //    (CPT 8-element chunks per thread).
 //  * k_quant_nvfp4: NVFP4 needs only the tensor amax (given) and a 16- or
 //    32-element block max, so it is a flat grid-stride kernel with no
-//    workgroup synchronisation; each wave owns 64 consecutive chunks.
+//    workgroup synchronisation; each wave owns 128 consecutive chunks per
+//    iteration (two per lane, loads issued first).
 #include "hdq_device.h"
 #include "hdq_internal.h"
 
@@ -45,24 +46,24 @@ __global__ __launch_bounds__(BLOCK) void k_quant_int_rows(
   const int64_t nch = cols >> 3;
   const uint4* xr = reinterpret_cast<const uint4*>(x + row * cols);
 
+  // Lane tid holds chunk fwht_src(c * BLOCK + tid) of the row: whole
+  // Hadamard blocks sit in aligned lane groups (BLOCK is a multiple of 16
+  // lanes), and a block past the row end is entirely zero-filled.
   float v[CPT][8];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
-    const int64_t idx = (int64_t)c * BLOCK + tid;
+    const int64_t idx = fwht_src((int64_t)c * BLOCK + tid, lane, hb);
     uint4 w = make_uint4(0u, 0u, 0u, 0u);
     if (idx < nch) w = xr[idx];
     bf16x8_to_f32(w, v[c]);
   }
-  // Rotate: whole Hadamard blocks sit in aligned lane groups (BLOCK is a
-  // multiple of 16 lanes), and a chunk index past the row end only ever
-  // meets zero-filled partners.
   float amax = 0.0f;
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
-    fwht8(v[c], lane, hb);
+    const float sc = fwht8(v[c], lane, hb) * c_b;  // sign * c_b: exact
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      v[c][i] = v[c][i] * c_b;
+      v[c][i] = v[c][i] * sc;
       amax = fmaxf(amax, fabsf(v[c][i]));
     }
   }
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(BLOCK) void k_quant_int_rows(
   const float kMagic = 12582912.0f;
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
-    const int64_t idx = (int64_t)c * BLOCK + tid;
+    const int64_t idx = fwht_src((int64_t)c * BLOCK + tid, lane, hb);
     if (idx < nch) {
       uint32_t b[8];
 #pragma unroll
@@ -137,14 +138,14 @@ __global__ __launch_bounds__(256) void k_quant_int_rows_long(
   const uint4* xr = reinterpret_cast<const uint4*>(x + row * cols);
   float amax = 0.0f;
   for (int64_t base = 0; base < nch; base += 256) {
-    const int64_t idx = base + tid;
+    const int64_t idx = fwht_src(base + tid, lane, hb);
     float v[8];
     uint4 w = make_uint4(0u, 0u, 0u, 0u);
     if (idx < nch) w = xr[idx];
     bf16x8_to_f32(w, v);
-    fwht8(v, lane, hb);
+    const float sc = fwht8(v, lane, hb) * c_b;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i] * c_b));
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i] * sc));
   }
   amax = wave_max(amax);
   __shared__ float red[4];
@@ -160,16 +161,16 @@ __global__ __launch_bounds__(256) void k_quant_int_rows_long(
   if (tid == 0) row_scale[row] = s;
   const float kMagic = 12582912.0f;
   for (int64_t base = 0; base < nch; base += 256) {
-    const int64_t idx = base + tid;
+    const int64_t idx = fwht_src(base + tid, lane, hb);
     float v[8];
     uint4 w = make_uint4(0u, 0u, 0u, 0u);
     if (idx < nch) w = xr[idx];
     bf16x8_to_f32(w, v);
-    fwht8(v, lane, hb);
+    const float sc = fwht8(v, lane, hb) * c_b;
     if (idx < nch) {
       uint32_t b[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) b[i] = __float_as_uint((v[i] * c_b) * inv + kMagic);
+      for (int i = 0; i < 8; ++i) b[i] = __float_as_uint((v[i] * sc) * inv + kMagic);
       if constexpr (INT4) {
         uint32_t p = 0;
 #pragma unroll
@@ -213,9 +214,36 @@ hipError_t launch_quant_int_rows(const uint16_t* x, int64_t rows, int64_t cols, 
 
 // ---------------------------------------------------------------- NVFP4
 
-// One 8-element chunk per lane per iteration; a wave covers 64 consecutive
-// chunks (512 elements), so every Hadamard block (<= 128) and every 16- or
-// 32-element scale block lies inside aligned lane groups of one wave.
+// Quantizes one 8-element chunk held by this lane (already rotated and
+// scaled); returns its 4 code bytes and sets *e to its 16-block's scale byte.
+template <bool MX>
+__device__ __forceinline__ uint32_t nvfp4_chunk(float (&v)[8], float s_t, float six_st, uint32_t* e_out) {
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
+  // the two chunks of a 16-element block sit on lanes l and l ^ 1, the four
+  // of a 32-element group on l ^ {0, 1, 2, 3} (fwht_chunk keeps chunk bits
+  // 0 and 1 on lane bits 0 and 1)
+  a = fmaxf(a, xor_lane<1>(a));
+  if constexpr (MX) a = fmaxf(a, xor_lane<2>(a));
+  uint32_t e = 0u;
+  float d = 0.0f;
+  if (s_t > 0.0f) {
+    const float t = a / six_st;
+    e = MX ? e4m3_encode(pow2_ceil_clamped(t)) : e4m3_encode(t);
+    d = e4m3_decode(e) * s_t;
+  }
+  *e_out = e;
+  if (d == 0.0f) return 0u;
+  const float inv = 1.0f / d;
+  return e2m1x2_encode(v[0] * inv, v[1] * inv) | (e2m1x2_encode(v[2] * inv, v[3] * inv) << 8) |
+         (e2m1x2_encode(v[4] * inv, v[5] * inv) << 16) | (e2m1x2_encode(v[6] * inv, v[7] * inv) << 24);
+}
+
+// UNROLL 8-element chunks per lane per iteration, loads issued first; a wave
+// covers UNROLL x 64 consecutive chunks, so every Hadamard block (<= 128)
+// and every 16- or 32-element scale block lies inside aligned lane groups of
+// one wave.
 template <bool MX>
 __global__ __launch_bounds__(256) void k_quant_nvfp4(
     const uint16_t* __restrict__ x, int64_t nch, int hb, float c_b,
@@ -223,6 +251,7 @@ __global__ __launch_bounds__(256) void k_quant_nvfp4(
     uint8_t* __restrict__ blk_scale, float* __restrict__ tensor_scale,
     const int32_t* __restrict__ decision, int32_t want) {
   if (decision != nullptr && *decision != want) return;
+  constexpr int UNROLL = 2;
   const int lane = threadIdx.x & 63;
   const float A = *amax_ptr;
   // s_t = amax / (6 * 448) for NVFP4 (the largest block maps to E4M3's top
@@ -236,39 +265,28 @@ __global__ __launch_bounds__(256) void k_quant_nvfp4(
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   uint32_t* cv = reinterpret_cast<uint32_t*>(codes);
 
-  for (int64_t base = wave * 64; base < nch; base += nwaves * 64) {
-    const int64_t idx = base + lane;
-    const bool ok = idx < nch;
-    float v[8];
-    uint4 w = make_uint4(0u, 0u, 0u, 0u);
-    if (ok) w = xv[idx];
-    bf16x8_to_f32(w, v);
-    fwht8(v, lane, hb);
-    float a = 0.0f;
+  for (int64_t base = wave * 64 * UNROLL; base < nch; base += nwaves * 64 * UNROLL) {
+    uint4 w[UNROLL];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      v[i] = v[i] * c_b;
-      a = fmaxf(a, fabsf(v[i]));
+    for (int u = 0; u < UNROLL; ++u) {
+      const int64_t idx = fwht_src(base + 64 * u + lane, lane, hb);
+      w[u] = (idx < nch) ? xv[idx] : make_uint4(0u, 0u, 0u, 0u);
     }
-    a = fmaxf(a, xor_lane<1>(a));        // 16-element block = lane pair
-    if constexpr (MX) a = fmaxf(a, xor_lane<2>(a));   // 32-element group
-    uint32_t e = 0u;
-    float d = 0.0f;
-    if (s_t > 0.0f) {
-      const float t = a / six_st;
-      e = MX ? e4m3_encode(pow2_ceil_clamped(t)) : e4m3_encode(t);
-      d = e4m3_decode(e) * s_t;
-    }
-    uint32_t packed = 0u;
-    if (d != 0.0f) {
-      const float inv = 1.0f / d;
-      packed = e2m1x2_encode(v[0] * inv, v[1] * inv) | (e2m1x2_encode(v[2] * inv, v[3] * inv) << 8) |
-               (e2m1x2_encode(v[4] * inv, v[5] * inv) << 16) |
-               (e2m1x2_encode(v[6] * inv, v[7] * inv) << 24);
-    }
-    if (ok) {
-      cv[idx] = packed;
-      if ((lane & 1) == 0) blk_scale[idx >> 1] = (uint8_t)e;
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int64_t idx = fwht_src(base + 64 * u + lane, lane, hb);
+      float v[8];
+      bf16x8_to_f32(w[u], v);
+      const float sc = fwht8(v, lane, hb) * c_b;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = v[i] * sc;
+      uint32_t e;
+      const uint32_t packed = nvfp4_chunk<MX>(v, s_t, six_st, &e);
+      if (idx < nch) {
+        cv[idx] = packed;
+        // the lane with the even chunk of the 16-element block writes its scale
+        if ((idx & 1) == 0) blk_scale[idx >> 1] = (uint8_t)e;
+      }
     }
   }
 }
@@ -278,7 +296,7 @@ hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t rows, int64_t cols, int
                               float* tensor_scale, const int32_t* decision, int32_t want,
                               hipStream_t s) {
   const int64_t nch = rows * cols / 8;
-  const int64_t waves_needed = (nch + 63) / 64;
+  const int64_t waves_needed = (nch + 127) / 128;
   // 8 waves per CU x 256 CUs of 4-wave workgroups keeps enough loads in
   // flight; a grid-stride loop covers the rest.
   int64_t blocks = (waves_needed + 3) / 4;

@@ -50,11 +50,27 @@ __global__ __launch_bounds__(256) void k_stats_partial(
     const int64_t nch = n_prev >> 3;
     const uint4* a4 = reinterpret_cast<const uint4*>(prev_in);
     const uint4* o4 = reinterpret_cast<const uint4*>(prev_out);
-    for (int64_t j = gtid; j < nch; j += gthreads) {
+    // two chunks per thread per iteration: four loads in flight
+    for (int64_t j = gtid; j < nch; j += 2 * gthreads) {
+      const int64_t j2 = j + gthreads;
+      const uint4 ra = a4[j], ro = o4[j];
+      const uint4 ra2 = j2 < nch ? a4[j2] : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 ro2 = j2 < nch ? o4[j2] : make_uint4(0u, 0u, 0u, 0u);
       float a[8], o[8];
-      bf16x8_to_f32(a4[j], a);
-      bf16x8_to_f32(o4[j], o);
+      bf16x8_to_f32(ra, a);
+      bf16x8_to_f32(ro, o);
       float d8 = 0.0f, b8 = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        d8 += fabsf(o[i] - a[i]);
+        b8 += fabsf(a[i]);
+      }
+      diff += d8;
+      base += b8;
+      bf16x8_to_f32(ra2, a);
+      bf16x8_to_f32(ro2, o);
+      d8 = 0.0f;
+      b8 = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         d8 += fabsf(o[i] - a[i]);
@@ -82,26 +98,34 @@ __global__ __launch_bounds__(256) void k_stats_partial(
     const int64_t nch = n_cur >> 3;
     const uint4* c4 = reinterpret_cast<const uint4*>(cur);
     const int64_t wave = gtid >> 6, nwaves = gthreads >> 6;
-    for (int64_t b0 = wave * 64; b0 < nch; b0 += nwaves * 64) {
-      const int64_t j = b0 + lane;
-      uint4 w = make_uint4(0u, 0u, 0u, 0u);
-      if (j < nch) w = c4[j];
-      const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+    // two chunks per lane per iteration (loads first); a wave covers 128
+    // consecutive chunks, keeping Hadamard blocks inside aligned lane groups
+    for (int64_t b0 = wave * 128; b0 < nch; b0 += nwaves * 128) {
+      uint4 w2[2];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        maxbits = max(maxbits, wd[q] & 0x7fffu);
-        maxbits = max(maxbits, (wd[q] >> 16) & 0x7fffu);
+      for (int u = 0; u < 2; ++u) {
+        const int64_t j = hb > 0 ? fwht_src(b0 + 64 * u + lane, lane, hb) : b0 + 64 * u + lane;
+        w2[u] = (j < nch) ? c4[j] : make_uint4(0u, 0u, 0u, 0u);
       }
-      float v[8];
-      bf16x8_to_f32(w, v);
-      float s8 = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) s8 += fabsf(v[i]);
-      sumabs += s8;
-      if (hb > 0) {
-        fwht8(v, lane, hb);
+      for (int u = 0; u < 2; ++u) {
+        const uint32_t wd[4] = {w2[u].x, w2[u].y, w2[u].z, w2[u].w};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) rotmax = fmaxf(rotmax, fabsf(v[i]));
+        for (int q = 0; q < 4; ++q) {
+          maxbits = max(maxbits, wd[q] & 0x7fffu);
+          maxbits = max(maxbits, (wd[q] >> 16) & 0x7fffu);
+        }
+        float v[8];
+        bf16x8_to_f32(w2[u], v);
+        float s8 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s8 += fabsf(v[i]);
+        sumabs += s8;
+        if (hb > 0) {
+          fwht8(v, lane, hb);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) rotmax = fmaxf(rotmax, fabsf(v[i]));
+        }
       }
     }
     const int64_t tail = n_cur - (nch << 3);
