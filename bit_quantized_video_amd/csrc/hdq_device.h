@@ -191,15 +191,27 @@ __device__ __forceinline__ uint32_t e2m1x2_encode(float a, float b) {
 // so a 16-byte fragment read of 8 consecutive rows touches distinct banks.
 __device__ __forceinline__ int lds_off64(int r, int c) { return r * 64 + 16 * (c ^ ((r >> 1) & 3)); }
 
-// Logical tile of this workgroup: contiguous tile ranges per XCD.
+// Logical tile of this workgroup.  Workgroups go round-robin to the 8 XCDs
+// (blockIdx % 8), each with its own L2, so every XCD takes a contiguous range
+// of the logical order.  The logical order walks groups of kGroupM tile rows
+// column by column: the ~32 tiles an XCD runs at once then span kGroupM rows
+// x 32/kGroupM columns and share their A and B strips in that XCD's L2,
+// instead of one A strip and 32 B strips.
+#ifndef HDQ_GROUP_M
+#define HDQ_GROUP_M 4
+#endif
+constexpr int kGroupM = HDQ_GROUP_M;
 __device__ __forceinline__ void xcd_tile(int tiles_m, int tiles_n, int& tm, int& tn) {
   const int total = tiles_m * tiles_n;
   const int bid = blockIdx.x;
   const int xcd = bid & 7, local = bid >> 3;
   const int q = total >> 3, r = total & 7;
   const int logical = xcd * q + (xcd < r ? xcd : r) + local;
-  tm = logical / tiles_n;
-  tn = logical - tm * tiles_n;
+  const int per_group = kGroupM * tiles_n;
+  const int g = logical / per_group, in_g = logical - g * per_group;
+  const int rows = min(kGroupM, tiles_m - g * kGroupM);
+  tn = in_g / rows;
+  tm = g * kGroupM + (in_g - tn * rows);
 }
 
 // ---- multi-stage LDS pipelines ------------------------------------------------
