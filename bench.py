@@ -72,11 +72,13 @@ class KernelTimes:
     def __init__(self):
         self.t = {}
         self.work = {}
+        self.bytes = {}
         self.n = {}
 
-    def add(self, kind, ms, work):
+    def add(self, kind, ms, work, nbytes=0.0):
         self.t[kind] = self.t.get(kind, 0.0) + ms
         self.work[kind] = self.work.get(kind, 0.0) + work
+        self.bytes[kind] = self.bytes.get(kind, 0.0) + nbytes
         self.n[kind] = self.n.get(kind, 0) + 1
 
     def summary(self):
@@ -84,6 +86,7 @@ class KernelTimes:
         for k in sorted(self.t):
             out[k] = {"launches": self.n[k], "total_ms": round(self.t[k], 3),
                       "avg_us": round(1e3 * self.t[k] / self.n[k], 2),
+                      "bytes_per_launch": self.bytes[k] / self.n[k],
                       "rate": self.work[k] / (self.t[k] * 1e-3) if self.t[k] > 0 else 0.0}
         return out
 
@@ -99,6 +102,22 @@ def stats_bytes(M, K):
     return 3 * 2 * M * K
 
 
+def gemm_bytes(M, N, K, prec, fp4):
+    """Algorithmic HBM bytes of one GEMM launch: each operand read once
+    (codes + scales) and the bf16 output written once."""
+    if prec == "int8":
+        a, b = M * K + 4 * M, N * K // 2 + 4 * N
+    elif prec == "bf16":
+        a, b = 2 * M * K, 2 * N * K
+    else:  # NVFP4: packed E2M1 + one scale byte per 16 (plain) or 32 (MX) elements
+        g = 32 if fp4 == "mx" else 16
+        a, b = M * K // 2 + M * K // g, N * K // 2 + N * K // g
+    return a + b + 2 * M * N
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "schedule_hbm_traffic.txt")
+
+
 # ------------------------------------------------------------------ copy
 
 def profile_copy():
@@ -110,6 +129,26 @@ def profile_copy():
         y.copy_(x)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 5}))
+
+
+def measure_copy_gbps(nbytes=1 << 30, reps=10):
+    """Bandwidth of a plain device-to-device copy (read + write bytes / time),
+    the practical ceiling for the HBM-bound kernels."""
+    x = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    y = torch.empty_like(x)
+    for _ in range(2):
+        y.copy_(x)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del x, y
+    torch.cuda.empty_cache()
+    return 2.0 * nbytes / (ms * 1e-3) / 1e9
 
 
 # ------------------------------------------------------------ schedule (5)
@@ -187,7 +226,7 @@ def run_schedule_step(S, args, hdq, recipe, events=None):
     return k
 
 
-def schedule_kernel_times(S, args, events_per_step, synth):
+def schedule_kernel_times(S, args, events_per_step, synth, recipe):
     """Per-kernel durations from the recorded events, attributed by the
     device decision of each layer call."""
     M = S["M"]
@@ -203,14 +242,17 @@ def schedule_kernel_times(S, args, events_per_step, synth):
                     d = int(decisions[t, b, li])
                     dt = [ev[i].elapsed_time(ev[i + 1]) for i in range(6)]
                     flops = 2.0 * M * N * K
-                    kt.add("select_stats", dt[0], stats_bytes(M, K))
+                    kt.add("select_stats", dt[0], stats_bytes(M, K), stats_bytes(M, K))
+                    q8, q4 = quant_bytes(M, K, "int8"), quant_bytes(M, K, "nvfp4")
                     kt.add("quant_int8" if d == 1 else "quant_int8_gated_off", dt[1],
-                           quant_bytes(M, K, "int8") if d == 1 else 0)
+                           q8 if d == 1 else 0, q8 if d == 1 else 0)
                     kt.add("quant_nvfp4" if d == 0 else "quant_nvfp4_gated_off", dt[2],
-                           quant_bytes(M, K, "nvfp4") if d == 0 else 0)
-                    kt.add("gemm_int8" if d == 1 else "gemm_int8_gated_off", dt[3], flops if d == 1 else 0)
-                    kt.add("gemm_nvfp4" if d == 0 else "gemm_nvfp4_gated_off", dt[4], flops if d == 0 else 0)
-                    kt.add("gemm_bf16" if d == 2 else "gemm_bf16_gated_off", dt[5], flops if d == 2 else 0)
+                           q4 if d == 0 else 0, q4 if d == 0 else 0)
+                    for kind, prec, dd, i in (("gemm_int8", "int8", 1, 3), ("gemm_nvfp4", "nvfp4", 0, 4),
+                                              ("gemm_bf16", "bf16", 2, 5)):
+                        on = d == dd
+                        kt.add(kind if on else kind + "_gated_off", dt[i], flops if on else 0,
+                               gemm_bytes(M, N, K, prec, recipe) if on else 0)
     return kt, decisions
 
 
@@ -220,7 +262,9 @@ def cpu_baseline_schedule(S, args, synth):
     quantize + GEMM on the first R rows in the decided precision, scaled to
     all M rows.  Weight preparation is excluded (as on the GPU)."""
     import oracle as O
-    M, R = S["M"], 32
+    M = S["M"]
+    rows = np.r_[0:256, M - 112:M]  # first 256 rows and the ragged last 112
+    R = len(rows)
     fp4_mx = args.fp4 == "mx"
     t_total = 0.0
     flops_total = 0.0
@@ -236,7 +280,7 @@ def cpu_baseline_schedule(S, args, synth):
         st = O.stats(pi, po, x, HB)
         d = O.decide(True, st[0], st[1], DELTA_T, RATIO_T)
         t_stats = time.perf_counter() - t0
-        xs = np.ascontiguousarray(x[:R])
+        xs = np.ascontiguousarray(x[rows])
         t0 = time.perf_counter()
         if d == O.INT8:
             qa, sa = O.quant_int(xs, HB, 127)
@@ -254,8 +298,8 @@ def cpu_baseline_schedule(S, args, synth):
             "kind": "oracle",
             "sample": (f"block 0 x 4 layers at timestep 0: selection statistics over the full "
                        f"[17776, K] tensors (1 thread), rotate+quantize and GEMM in the decided "
-                       f"precision on the first {R} of 17776 rows (GEMM loops OpenMP), scaled "
-                       f"linearly to all rows; weight preparation untimed")}
+                       f"precision on {R} of 17776 rows (the first 256 and the last 112; GEMM loops "
+                       f"OpenMP), time scaled linearly to all rows; weight preparation untimed")}
 
 
 def time_schedule(S, args, hdq, synth, recipe):
@@ -273,7 +317,7 @@ def time_schedule(S, args, hdq, synth, recipe):
         run_schedule_step(S, args, hdq, recipe, events[s])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    kt, decisions = schedule_kernel_times(S, args, events, synth)
+    kt, decisions = schedule_kernel_times(S, args, events, synth, recipe)
     return 1e3 * elapsed / args.steps, kt, decisions
 
 
@@ -296,6 +340,8 @@ def schedule_quality(S, hdq):
 
 
 def bench_schedule(args, hdq, synth):
+    copy_gbps = measure_copy_gbps()
+    log(f"device copy: {copy_gbps:.0f} GB/s")
     S = build_schedule(args, hdq, synth)
     M = S["M"]
     flops_step = sum(2.0 * M * N * K for _, K, N in synth.SCHEDULE_LAYERS) * args.blocks * args.timesteps
@@ -308,7 +354,7 @@ def bench_schedule(args, hdq, synth):
     # dominant kernel: the selected-path kernel with the most time
     main_kinds = ["gemm_int8", "gemm_nvfp4", "gemm_bf16", "quant_int8", "quant_nvfp4", "select_stats"]
     dom = max((k for k in main_kinds if k in ks), key=lambda k: ks[k]["total_ms"])
-    roof = roofline_for(dom, ks[dom], args.fp4)
+    roof = roofline_for(dom, ks[dom], args.fp4, copy_gbps)
     q_bytes = sum(kt.work[k] for k in ("quant_int8", "quant_nvfp4") if k in kt.work)
     q_ms = sum(kt.t[k] for k in ("quant_int8", "quant_nvfp4") if k in kt.t)
     # effective TOPS of the fused quant + linear alone (selected kernels only)
@@ -332,10 +378,15 @@ def bench_schedule(args, hdq, synth):
                    "global_batch": M, "layer_calls_per_step": n_calls},
         "roofline": roof,
         "quant_gbps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1) if q_ms > 0 else None,
+        "copy_gbps": round(copy_gbps, 1),
+        "quant_roofline": {k: roofline_for(k, ks[k], args.fp4, copy_gbps)
+                           for k in ("quant_int8", "quant_nvfp4", "select_stats") if k in ks},
         "fused_quant_linear_tops": round(ql_flops / (ql_ms * 1e-3) / 1e12, 2) if ql_ms > 0 else None,
         "decisions": counts,
         "kernels": {k: {"launches": v["launches"], "total_ms": v["total_ms"], "avg_us": v["avg_us"],
-                        "rate": round(v["rate"] / 1e12, 3)}
+                        "rate": round(v["rate"] / 1e12, 3),
+                        "rate_unit": ("TB/s" if k.startswith(("quant", "select")) else
+                                      "TOP/s" if k.startswith("gemm_int8") else "TFLOP/s")}
                     for k, v in ks.items()},
         "other_recipe": {"recipe": other,
                          "value": round(flops_step / (o_ms * 1e-3) / 1e12, 2),
@@ -352,7 +403,22 @@ def bench_schedule(args, hdq, synth):
     return result
 
 
-def roofline_for(kind, k, recipe):
+def stored_traffic(kind, recipe):
+    """HBM bytes per launch for a bench kernel kind from the committed
+    FETCH_SIZE/WRITE_SIZE summary, or None (absent, or the kernel changed
+    since the counters were taken)."""
+    from bit_quantized_video_amd import profsum
+    pkind = kind + "_mx" if recipe == "mx" and kind in ("gemm_nvfp4", "quant_nvfp4") else kind
+    try:
+        return profsum.current_traffic(TRAFFIC_PROFILE, pkind)
+    except (OSError, KeyError):
+        return None
+
+
+def roofline_for(kind, k, recipe, copy_gbps=None):
+    traffic = stored_traffic(kind, recipe)
+    traffic = None if traffic is None else round(traffic)
+    alg = round(k["bytes_per_launch"])
     if kind.startswith("gemm"):
         dt = {"gemm_int8": "int8", "gemm_bf16": "bf16",
               "gemm_nvfp4": "fp4" if recipe == "mx" else "bf16"}[kind]
@@ -360,10 +426,13 @@ def roofline_for(kind, k, recipe):
         ach = k["rate"]
         return {"kernel": kind, "bound": "mfma", "dtype": dt, "achieved": round(ach / 1e12, 1),
                 "peak": round(peak / 1e12, 1), "unit": "TFLOP/s" if dt != "int8" else "TOP/s",
-                "frac": round(ach / peak, 4), "traffic": None}
+                "frac": round(ach / peak, 4), "traffic": traffic, "traffic_unit": "bytes/launch",
+                "algorithmic_bytes": alg, "avg_launch_us": k["avg_us"]}
     ach = k["rate"]
     return {"kernel": kind, "bound": "hbm", "achieved": round(ach / 1e9, 1), "peak": 8000.0,
-            "unit": "GB/s", "frac": round(ach / PEAK["hbm"], 4), "traffic": None}
+            "unit": "GB/s", "frac": round(ach / PEAK["hbm"], 4),
+            "frac_of_copy": round(ach / 1e9 / copy_gbps, 4) if copy_gbps else None, "traffic": traffic,
+            "traffic_unit": "bytes/launch", "algorithmic_bytes": alg, "avg_launch_us": k["avg_us"]}
 
 
 # ---------------------------------------------------------- single layer

@@ -1,0 +1,39 @@
+"""Host logic of the rocprofv3 summarizer: kernel classification, the
+schedule window and the source-hash guard on stored traffic figures."""
+from bit_quantized_video_amd import profsum as P
+
+
+def test_classify_kernel_names():
+    cases = {
+        "hdq::k_stats_partial(unsigned short const*)": "select_stats",
+        "hdq::k_stats_final(double const*)": "select_final",
+        "void hdq::k_quant_int_rows<128, 3, false>(int)": "quant_int8",
+        "void hdq::k_quant_int_rows<256, 6, true>(int)": None,  # INT4 weight preparation
+        "void hdq::k_quant_nvfp4<true>(int)": "quant_nvfp4_mx",
+        "void hdq::k_quant_nvfp4<false>(int)": "quant_nvfp4",
+        "void hdq::k_gemm_i8i4_pipe<2, 4, 4, 2, 1>(int)": "gemm_int8",
+        "void hdq::k_gemm_i8i4_pipe<2, 4, 4, 2, 0>(int)": None,  # f32 output: quality check
+        "void hdq::k_gemm_fp4mx_pipe<1>(int)": "gemm_nvfp4_mx",
+        "void hdq::k_gemm_bf16_pipe<1, 1>(int)": "gemm_nvfp4",
+        "void hdq::k_gemm_bf16_pipe<0, 1>(int)": "gemm_bf16",
+        "__amd_rocclr_copyBuffer": None,
+    }
+    for name, kind in cases.items():
+        assert P.classify(name) == kind, name
+
+
+def test_schedule_window_starts_after_weight_prep():
+    rows = [(0, "void hdq::k_quant_int_rows<128, 3, true>"), (1, "hdq::k_stats_partial"),
+            (2, "void hdq::k_quant_int_rows<128, 3, true>"), (3, "hdq::k_stats_partial"),
+            (4, "void hdq::k_gemm_i8i4_pipe<2, 4, 4, 2, 1>"), (5, "void hdq::k_gemm_i8i4_pipe<2, 4, 4, 2, 0>")]
+    assert [r[0] for r in P.schedule_window(rows)] == [3, 4]
+
+
+def test_stored_traffic_guarded_by_source_hash(tmp_path):
+    f = tmp_path / "t.txt"
+    f.write_text(f"header\ntraffic gemm_int8 123 {P.sources_hash('gemm_int8')}\n"
+                 f"traffic quant_int8 456 0000000000000000\n")
+    assert P.current_traffic(str(f), "gemm_int8") == 123.0
+    assert P.current_traffic(str(f), "quant_int8") is None  # sources changed
+    assert P.current_traffic(str(f), "gemm_bf16") is None  # never measured
+    assert P.current_traffic(str(tmp_path / "missing.txt"), "gemm_int8") is None
