@@ -432,3 +432,78 @@ def test_config1_full_oracle():
     wc, we, wst = O.quant_nvfp4(w16, hb)
     ref = O.gemm_nvfp4(ac, ae, ast, wc, we, wst, 1024).astype(np.float32)
     assert rel_fro(y.cpu().numpy(), ref) <= REL_TOL
+
+
+# ------------------------------ the mixed-precision schedule, full size
+
+def schedule_call(prev_in, prev_out, x, W, hb, fmt4):
+    """One layer call as the schedule enqueues it: selection, then both
+    quantizers and all three GEMMs behind the device-side decision."""
+    M, K = x.shape
+    dec, st = hdq.select_precision(prev_in, prev_out, x, hb, 0.1, 50.0)
+    xq8 = hdq.quantize(x, hb, hdq.FMT_INT8_ROW, decision=dec)
+    xq4 = hdq.quantize(x, hb, fmt4, tensor_amax=st[4:5], decision=dec)
+    y = torch.zeros(M, W.N, dtype=torch.bfloat16, device=DEV)
+    hdq.linear(hdq.PREC_INT8, None, W, decision=dec, xq=xq8, y=y)
+    hdq.linear(hdq.PREC_NVFP4, None, W, decision=dec, xq=xq4, y=y)
+    hdq.linear(hdq.PREC_BF16, x, W, decision=dec, y=y)
+    torch.cuda.synchronize()
+    return int(dec.item()), st.cpu().numpy().astype(np.float64), y
+
+
+@pytest.mark.parametrize("layer", range(len(synth.SCHEDULE_LAYERS)))
+def test_schedule_layer_calls_match_oracle(layer):
+    """CogVideoX-5B block layers at M = 17776 tokens: a low-noise step
+    (NVFP4), a high-noise step (INT8) and, on the first layer, an input with
+    outlier channels (bf16 fallback).  Inputs come from the seeded device
+    generator; the oracle reads byte copies of what the GPU consumed."""
+    name, K, N = synth.SCHEDULE_LAYERS[layer]
+    M, hb = synth.M_COGVIDEOX, 128
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(1000 + layer)
+    x = synth.device_gaussian((M, K), 1.0, gen, DEV)
+    w = synth.device_gaussian((N, K), 0.02, gen, DEV)
+    W = hdq.LinearWeights(w, hb, fp4_fmt=hdq.FMT_NVFP4_MX)
+    w16 = bf16_to_np(w)
+    rows = sample_rows(M, 24, 24)
+    cols = np.unique(np.concatenate([np.arange(32), np.linspace(0, N - 1, 64).astype(np.int64)]))
+    ws = np.ascontiguousarray(w16[cols])
+    qw, sw = O.quant_int(ws, hb, 7)
+    wc, we, wst = O.quant_nvfp4(ws, hb, amax=O.rotated_amax(w16, hb), mx=True)
+    cases = [("low noise", 0.03, None), ("high noise", 0.25, None)]
+    if layer == 0:
+        cases.append(("outlier channels", 0.03, 400.0))
+    for what, s, outlier in cases:
+        xi = x
+        if outlier is not None:
+            xi = x.clone()
+            xi[:, 7] *= outlier
+        prev_out = synth.device_noisy_copy(xi, s, gen)
+        dec, st, y = schedule_call(xi.clone(), prev_out, xi, W, hb, hdq.FMT_NVFP4_MX)
+        x16, po16 = bf16_to_np(xi), bf16_to_np(prev_out)
+        ref = O.stats(x16, po16, x16, hb)
+        say(f"schedule {name} {what}: decision {dec}, delta {st[0]:.4f}, ratio {st[1]:.2f}")
+        assert abs(st[0] - ref[0]) <= 2e-6 * ref[0]
+        assert abs(st[1] - ref[1]) <= 2e-6 * ref[1]
+        assert st[4] == np.float32(ref[4])
+        assert decision_ok(dec, ref, True)
+        want = {"low noise": hdq.PREC_NVFP4, "high noise": hdq.PREC_INT8,
+                "outlier channels": hdq.PREC_BF16}[what]
+        assert dec == want
+        xs = np.ascontiguousarray(x16[rows])
+        if dec == hdq.PREC_INT8:
+            qa, sa = O.quant_int(xs, hb, 127)
+            r, _ = O.gemm_int(qa, sa, qw, sw)
+            r = r.astype(np.float64)
+        elif dec == hdq.PREC_NVFP4:
+            ac, ae, ast = O.quant_nvfp4(xs, hb, amax=np.float32(ref[4]), mx=True)
+            r = O.gemm_nvfp4(ac, ae, ast, wc, we, wst, K)
+        else:
+            r = O.gemm_bf16(xs, ws)
+        r = round_like(r, hdq.DTYPE_BF16)
+        got = y_np(y)[np.ix_(rows, cols)]
+        err = rel_fro(got, r)
+        say(f"schedule {name} {what}: rel fro {err:.3e}")
+        assert err <= REL_TOL
+        if dec == hdq.PREC_INT8:
+            assert np.array_equal(got, r)
