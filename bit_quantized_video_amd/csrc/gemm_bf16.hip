@@ -13,10 +13,11 @@
 // * bf16 x bf16 on the unrotated operands: the full-precision path that the
 //   summary's section three (purified delta refresh) falls back to.
 //
-// Tiling as in gemm_i8.hip: 256 x 128 (tokens x features) per workgroup,
-// 4 waves of 128 x 64, v_mfma_f32_32x32x16_bf16 with the instruction's A
-// operand on the weights and B on the activations, K advancing 32 elements
-// (64-byte LDS rows) per double-buffered stage.
+// v_mfma_f32_32x32x16_bf16 with the instruction's A operand on the weights
+// and B on the activations.  Two kernels, as in gemm_i8.hip: a pipelined one
+// for K % 64 == 0 (256 x 256 tiles, 8 waves, see below) and a fallback for
+// any K % 32 == 0 (256 x 128 tiles, 4 waves of 128 x 64, K advancing 32
+// elements per double-buffered stage).
 #include "hdq_device.h"
 #include "hdq_internal.h"
 

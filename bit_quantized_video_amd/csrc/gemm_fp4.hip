@@ -13,7 +13,7 @@
 // Every product and block sum is exact; only the float32 accumulation rounds.
 //
 // Two kernels: a pipelined one (the INT8 kernel's structure, see below) for
-// K % 128 == 0, and a simple double-buffered one for any K % 32 == 0.  In
+// K % 256 == 0, and a simple double-buffered one for any K % 32 == 0.  In
 // both the per-row E8M0 bytes of a stage sit in LDS next to the codes.
 #include "hdq_device.h"
 #include "hdq_internal.h"

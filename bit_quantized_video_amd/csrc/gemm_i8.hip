@@ -12,20 +12,22 @@
 //    The instruction's A operand is a 32-row slice of W and its B operand a
 //    32-row slice of X, so each output lane holds one token row m and four
 //    consecutive output features n (8- or 16-byte stores).
-//  * Workgroup tile BM x BN (tokens x features), 4 waves as 2 x 2, each wave
-//    WM x WN subtiles of 32 x 32; K advances 64 bytes per stage.
-//  * Global -> registers -> LDS, double-buffered, one barrier per stage.
-//    INT4 weights are unpacked to int8 while being written to LDS: nibble q
-//    is placed in the high half of its byte (value 16 q), the interleaved
+//  * INT4 weights are unpacked to int8 on their way into LDS: nibble q is
+//    placed in the high half of its byte (value 16 q), the interleaved
 //    low/high nibbles are put back in k order with two v_perm_b32, and the
 //    epilogue divides the exact int32 sum by 16 (|16 acc| < 2^31 for
 //    K < 150000).
-//  * LDS rows are 64 bytes; 16-byte chunk c of row r is stored at chunk
-//    c ^ ((r >> 1) & 3) so the fragment reads of 8 consecutive rows hit
-//    distinct banks.
-//  * Tiles are dealt to the 8 XCDs in contiguous ranges (workgroup i runs on
-//    XCD i % 8), features fastest, so the tiles sharing an X panel run on
-//    one XCD and share its L2.
+//  * Two kernels.  The pipelined one (K % 128 == 0, every CogVideoX shape):
+//    256 x 256 tiles, 8 waves (two per SIMD), buffer loads two stages ahead
+//    in registers, double-buffered LDS with XOR-swizzled rows, LDS-only
+//    barriers; see its own comment below.  The fallback (any K % 32 == 0):
+//    4 waves as 2 x 2, 64-byte LDS rows with 16-byte chunk c of row r at
+//    chunk c ^ ((r >> 1) & 3), K advancing 64 bytes per double-buffered
+//    stage.
+//  * Tile order (xcd_tile): workgroup i runs on XCD i % 8, each XCD takes a
+//    contiguous range of a grouped order (4 tile rows walked column by
+//    column), so the ~32 tiles an XCD runs at once share 4 X panels and 8 W
+//    panels in its L2.
 #include "hdq_device.h"
 #include "hdq_internal.h"
 
