@@ -12,11 +12,14 @@
 //     y = s_tx * s_tw * sum_32-blocks 2^(ex + ew) sum_k e2m1_x e2m1_w.
 // Every product and block sum is exact; only the float32 accumulation rounds.
 //
-// Two kernels: a pipelined one (the INT8 kernel's structure, see below) for
-// K % 256 == 0, and a simple double-buffered one for any K % 32 == 0.  In
-// both the per-row E8M0 bytes of a stage sit in LDS next to the codes.
+// Two kernels: a pipelined, persistent one (the INT8 kernel's structure, see
+// below) for K % 256 == 0, and a simple double-buffered one for any
+// K % 32 == 0.  In both the per-row E8M0 bytes of a stage sit in LDS next to
+// the codes.
 #include "hdq_device.h"
 #include "hdq_internal.h"
+
+#include <type_traits>
 
 namespace hdq {
 
@@ -178,19 +181,24 @@ __global__ __launch_bounds__(256) void k_gemm_fp4mx(
 
 // ---------------------------------------------------------------------------
 // Pipelined kernel for K % 256 == 0: the INT8 kernel's structure (256 x 256
-// tile, 8 waves as 2 x 4 of 128 x 64, two register sets prefetching the next
-// two stages through buffer loads, double-buffered LDS, LDS-only barriers)
-// with 256 K per stage: 128-byte code rows (swz128; substep s of 64 K gives
-// lane half h chunk 2s + h) and, per row, the stage's eight E8M0 bytes (one
-// per 32 K, from the even E4M3 byte of each MX pair).
+// tiles, 8 waves as 2 x 4 of 128 x 64, a persistent tile loop, buffer loads
+// prefetching across tile boundaries, double-buffered LDS, LDS-only
+// barriers) with 256 K per stage and one register set: stage g + 1 is
+// loaded while stage g is computed (a second set would not fit beside the
+// unrolled substeps' fragments in 256 VGPRs).  Per stage:
+// 128-byte code rows (swz128; substep s of 64 K gives lane half h chunk
+// 2s + h) and, per row, the stage's eight E8M0 bytes (one per 32 K, from the
+// even E4M3 byte of each MX pair) stored as two words, [g0 g2 g4 g6] and
+// [g1 g3 g5 g7]: lane half h reads word h once per stage and substep s takes
+// its byte through the instruction's scale byte select.
 struct Fp4PipeStage {
   uint4 x[4], w[4];  // codes: 4 x 16-byte chunks per operand per thread
-  uint2 xs, ws;      // 8 E4M3 bytes (4 MX pairs) per operand per thread
+  uint4 sc;          // the 16 E4M3 bytes of one X or W row (8 MX pairs)
 };
 
-__device__ __forceinline__ uint32_t e8m0x4_from_pairs(uint2 b) {
-  return e4m3_pow2_to_e8m0(b.x & 0xffu) | (e4m3_pow2_to_e8m0((b.x >> 16) & 0xffu) << 8) |
-         (e4m3_pow2_to_e8m0(b.y & 0xffu) << 16) | (e4m3_pow2_to_e8m0((b.y >> 16) & 0xffu) << 24);
+template <int KS>
+__device__ __forceinline__ v16f mfma_fp4(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, KS, sa, KS, sb);
 }
 
 template <int OUT>
@@ -207,30 +215,44 @@ __global__ __launch_bounds__(512) void k_gemm_fp4mx_pipe(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % 2, wn = wave / 2;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  int tm, tn;
-  xcd_tile(tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  const TileSeq seq = tile_seq(tiles_m * tiles_n);
+  const int nk = K / BK;
+  const int G = seq.count * nk;
+  if (G == 0) return;
   const int ld = K / 2, lds_ = K / 16;
 
-  const __amdgpu_buffer_rsrc_t xres = make_rsrc(xc + (int64_t)m0 * ld, (uint32_t)((int64_t)(M - m0) * ld));
-  const __amdgpu_buffer_rsrc_t wres = make_rsrc(wc + (int64_t)n0 * ld, (uint32_t)((int64_t)(N - n0) * ld));
-  const __amdgpu_buffer_rsrc_t xsres = make_rsrc(xsc + (int64_t)m0 * lds_, (uint32_t)((int64_t)(M - m0) * lds_));
-  const __amdgpu_buffer_rsrc_t wsres = make_rsrc(wsc + (int64_t)n0 * lds_, (uint32_t)((int64_t)(N - n0) * lds_));
   const int cr = tid >> 3, cc = tid & 7;  // code chunks: 8 threads per row, 64 rows per round
   const uint32_t cvoff = (uint32_t)(cr * ld + 16 * cc);
   const int cdst = cr * 128 + 16 * (cc ^ swz128(cr));
-  const int sr = tid >> 1, sc = tid & 1;  // scales: 2 threads per row, 8 bytes each
-  const uint32_t svoff = (uint32_t)(sr * lds_ + 8 * sc);
-  const int sdst = sr * 8 + 4 * sc;
+  // scales: waves 0-3 take the 256 X rows, waves 4-7 the 256 W rows
+  const int sw_ = __builtin_amdgcn_readfirstlane(tid >> 8), srow = tid & 255;
+  const uint32_t svoff = (uint32_t)(srow * lds_);
+  const int sdst = XB + WB + sw_ * BM * 8 + srow * 8;
 
-  auto load = [&](Fp4PipeStage& st, int kt) {
+  int l_logical = seq.first, l_kt = 0;
+  __amdgpu_buffer_rsrc_t xres, wres, sres;
+  auto open_tile = [&]() {
+    int tm, tn;
+    grouped_tile(l_logical, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    xres = make_rsrc(xc + (int64_t)m0 * ld, (uint32_t)((int64_t)(M - m0) * ld));
+    wres = make_rsrc(wc + (int64_t)n0 * ld, (uint32_t)((int64_t)(N - n0) * ld));
+    sres = sw_ ? make_rsrc(wsc + (int64_t)n0 * lds_, (uint32_t)((int64_t)(N - n0) * lds_))
+               : make_rsrc(xsc + (int64_t)m0 * lds_, (uint32_t)((int64_t)(M - m0) * lds_));
+  };
+  open_tile();
+  auto load = [&](Fp4PipeStage& st) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      st.x[p] = buf_load16(xres, cvoff, kt * (BK / 2) + p * 64 * ld);
-      st.w[p] = buf_load16(wres, cvoff, kt * (BK / 2) + p * 64 * ld);
+      st.x[p] = buf_load16(xres, cvoff, l_kt * (BK / 2) + p * 64 * ld);
+      st.w[p] = buf_load16(wres, cvoff, l_kt * (BK / 2) + p * 64 * ld);
     }
-    st.xs = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(xsres, (int)svoff, kt * (BK / 16), 0));
-    st.ws = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(wsres, (int)svoff, kt * (BK / 16), 0));
+    st.sc = buf_load16(sres, svoff, l_kt * (BK / 16));
+    if (++l_kt == nk) {
+      l_kt = 0;
+      l_logical += seq.stride;
+      if (l_logical < tiles_m * tiles_n) open_tile();
+    }
   };
   auto store = [&](const Fp4PipeStage& st, int buf) {
     uint8_t* base = smem + buf * SB;
@@ -239,17 +261,27 @@ __global__ __launch_bounds__(512) void k_gemm_fp4mx_pipe(
       *reinterpret_cast<uint4*>(base + cdst + p * 64 * 128) = st.x[p];
       *reinterpret_cast<uint4*>(base + XB + cdst + p * 64 * 128) = st.w[p];
     }
-    *reinterpret_cast<uint32_t*>(base + XB + WB + sdst) = e8m0x4_from_pairs(st.xs);
-    *reinterpret_cast<uint32_t*>(base + XB + WB + BM * 8 + sdst) = e8m0x4_from_pairs(st.ws);
+    // E8M0 of group g comes from E4M3 byte 2g; word h holds g = h, h+2, h+4, h+6
+    const uint32_t d[4] = {st.sc.x, st.sc.y, st.sc.z, st.sc.w};
+    uint32_t w0 = 0u, w1 = 0u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      w0 |= e4m3_pow2_to_e8m0(d[q] & 0xffu) << (8 * q);
+      w1 |= e4m3_pow2_to_e8m0((d[q] >> 16) & 0xffu) << (8 * q);
+    }
+    *reinterpret_cast<uint2*>(base + sdst) = make_uint2(w0, w1);
   };
 
   v16f acc[WN_T][WM_T];
+  auto zero_acc = [&]() {
 #pragma unroll
-  for (int j = 0; j < WN_T; ++j)
+    for (int j = 0; j < WN_T; ++j)
 #pragma unroll
-    for (int i = 0; i < WM_T; ++i)
+      for (int i = 0; i < WM_T; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.0f;
+        for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.0f;
+  };
+  zero_acc();
 
   const int h = lane >> 5, r32 = lane & 31;
   auto compute = [&](int buf) {
@@ -257,84 +289,108 @@ __global__ __launch_bounds__(512) void k_gemm_fp4mx_pipe(
     const uint8_t* lw = lx + XB;
     const uint8_t* lxs = lx + XB + WB;
     const uint8_t* lws = lxs + BM * 8;
-#pragma unroll 1  // unrolled, the two substeps' fragments overflow 256 VGPRs
-    for (int ks = 0; ks < BK / 64; ++ks) {
+    int xe[WM_T], we[WN_T];
+#pragma unroll
+    for (int i = 0; i < WM_T; ++i)
+      xe[i] = *reinterpret_cast<const int*>(lxs + (wm * WM_T * 32 + i * 32 + r32) * 8 + 4 * h);
+#pragma unroll
+    for (int j = 0; j < WN_T; ++j)
+      we[j] = *reinterpret_cast<const int*>(lws + (wn * WN_T * 32 + j * 32 + r32) * 8 + 4 * h);
+    auto substep = [&](auto ksc) {
+      constexpr int ks = decltype(ksc)::value;
       const int g = 2 * ks + h;  // this lane's 32-K group within the stage
       v8i xf[WM_T], wf[WN_T];
-      int xe[WM_T], we[WN_T];
 #pragma unroll
       for (int i = 0; i < WM_T; ++i) {
         const int r = wm * WM_T * 32 + i * 32 + r32;
         const v4i v = *reinterpret_cast<const v4i*>(lx + r * 128 + 16 * (g ^ swz128(r)));
         xf[i] = v8i{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
-        xe[i] = lxs[r * 8 + g];
       }
 #pragma unroll
       for (int j = 0; j < WN_T; ++j) {
         const int r = wn * WN_T * 32 + j * 32 + r32;
         const v4i v = *reinterpret_cast<const v4i*>(lw + r * 128 + 16 * (g ^ swz128(r)));
         wf[j] = v8i{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
-        we[j] = lws[r * 8 + g];
       }
 #pragma unroll
       for (int j = 0; j < WN_T; ++j)
 #pragma unroll
-        for (int i = 0; i < WM_T; ++i)
-          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[j], xf[i], acc[j][i], 4, 4, 0,
-                                                                        we[j], 0, xe[i]);
-    }
+        for (int i = 0; i < WM_T; ++i) acc[j][i] = mfma_fp4<ks>(wf[j], xf[i], acc[j][i], we[j], xe[i]);
+    };
+    substep(std::integral_constant<int, 0>{});
+    substep(std::integral_constant<int, 1>{});
+    substep(std::integral_constant<int, 2>{});
+    substep(std::integral_constant<int, 3>{});
   };
 
-  const int nk = K / BK;
-  Fp4PipeStage ra, rb;
-  load(ra, 0);
-  if (nk > 1) load(rb, 1);
-  store(ra, 0);
-  lds_barrier();
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    if (kt + 2 < nk) load(ra, kt + 2);
-    compute(0);
-    store(rb, 1);
-    lds_barrier();
-    if (kt + 3 < nk) load(rb, kt + 3);
-    compute(1);
-    if (kt + 2 < nk) store(ra, 0);
-    lds_barrier();
-  }
-  if (kt < nk) compute(0);
-
   const float scale = (*xts) * (*wts);
-  const bool full_n = n0 + BN <= N && (N & 3) == 0;
+  auto epilogue = [&](int logical) {
+    int tm, tn;
+    grouped_tile(logical, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const bool full_n = n0 + BN <= N && (N & 3) == 0;
 #pragma unroll
-  for (int i = 0; i < WM_T; ++i) {
-    const int m = m0 + wm * WM_T * 32 + i * 32 + r32;
-    if (m >= M) continue;
+    for (int i = 0; i < WM_T; ++i) {
+      const int m = m0 + wm * WM_T * 32 + i * 32 + r32;
+      if (m >= M) continue;
 #pragma unroll
-    for (int j = 0; j < WN_T; ++j) {
+      for (int j = 0; j < WN_T; ++j) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * WN_T * 32 + j * 32 + 8 * g + 4 * h;
-        const int64_t off = (int64_t)m * N + n;
-        float y[4];
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * WN_T * 32 + j * 32 + 8 * g + 4 * h;
+          const int64_t off = (int64_t)m * N + n;
+          float y[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) y[r] = acc[j][i][4 * g + r] * scale;
-        if (full_n) {
-          if constexpr (OUT == kOutF32)
-            *reinterpret_cast<float4*>(reinterpret_cast<float*>(Y) + off) = make_float4(y[0], y[1], y[2], y[3]);
-          else
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(Y) + off) =
-                make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
-        } else {
-          for (int r = 0; r < 4 && n + r < N; ++r) {
+          for (int r = 0; r < 4; ++r) y[r] = acc[j][i][4 * g + r] * scale;
+          if (full_n) {
             if constexpr (OUT == kOutF32)
-              reinterpret_cast<float*>(Y)[off + r] = y[r];
+              *reinterpret_cast<float4*>(reinterpret_cast<float*>(Y) + off) = make_float4(y[0], y[1], y[2], y[3]);
             else
-              reinterpret_cast<uint16_t*>(Y)[off + r] = __builtin_bit_cast(uint16_t, (__bf16)y[r]);
+              *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(Y) + off) =
+                  make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+          } else {
+            for (int r = 0; r < 4 && n + r < N; ++r) {
+              if constexpr (OUT == kOutF32)
+                reinterpret_cast<float*>(Y)[off + r] = y[r];
+              else
+                reinterpret_cast<uint16_t*>(Y)[off + r] = __builtin_bit_cast(uint16_t, (__bf16)y[r]);
+            }
           }
         }
       }
     }
+  };
+
+  int ckt = 0, clogical = seq.first;
+  auto finish_stage = [&]() {
+    if (++ckt == nk) {
+      epilogue(clogical);
+      zero_acc();
+      ckt = 0;
+      clogical += seq.stride;
+    }
+  };
+
+  Fp4PipeStage ra;
+  load(ra);
+  store(ra, 0);
+  lds_barrier();
+  int g = 0;
+  for (; g + 1 < G; g += 2) {
+    load(ra);
+    compute(0);
+    finish_stage();
+    store(ra, 1);
+    lds_barrier();
+    if (g + 2 < G) load(ra);
+    compute(1);
+    finish_stage();
+    if (g + 2 < G) store(ra, 0);
+    lds_barrier();
+  }
+  if (g < G) {
+    compute(0);
+    finish_stage();
   }
 }
 
@@ -349,8 +405,8 @@ static hipError_t launch_fp4_pipe(const uint8_t* xc, const uint8_t* xs, const fl
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(512), lds, s, xc, xs, xts, wc, ws, wts, y, (int)M,
-                     (int)N, (int)K, decision, want);
+  hipLaunchKernelGGL(kern, dim3((unsigned)persistent_grid(tiles)), dim3(512), lds, s, xc, xs, xts, wc, ws,
+                     wts, y, (int)M, (int)N, (int)K, decision, want);
   return hipGetLastError();
 }
 

@@ -31,7 +31,24 @@
 #include "hdq_device.h"
 #include "hdq_internal.h"
 
+#include <atomic>
+
 namespace hdq {
+
+int64_t persistent_grid(int64_t tiles) {
+  static std::atomic<int> cus[64];  // per device; 0 = not read yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    int cu = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu < 8)
+      cu = 256;
+    n = cu & ~7;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return tiles <= n ? tiles : n;
+}
 
 // 32 packed INT4 (uint4) -> 32 int8 holding 16 * q, in k order.
 __device__ __forceinline__ void unpack_int4x32(const uint4 p, uint4& lo, uint4& hi) {
@@ -212,6 +229,7 @@ __global__ __launch_bounds__(256) void k_gemm_i8i4(
 //    16-byte read of packed nibbles unpacked to the two substeps' fragments,
 //    for X two 16-byte reads.  (Any assignment of K to lanes works as long as
 //    both operands use the same one.)
+
 template <int WAVES_M, int WAVES_N, int WM_T, int WN_T>
 struct I8Cfg {
   static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
@@ -242,27 +260,52 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_i8i4_pipe(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WAVES_M, wn = wave / WAVES_M;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  int tm, tn;
-  xcd_tile(tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  const TileSeq seq = tile_seq(tiles_m * tiles_n);
+  const int nk = K / BK;
+  const int G = seq.count * nk;  // K-stages of this workgroup, over all its tiles
+  if (G == 0) return;
   const int ldw = K >> 1;
 
-  // Buffer resources over this tile's rows; 8 threads per 128-byte X row and
-  // 4 per W row (coalesced).  Load round p is XROWS (WROWS) rows further on,
-  // a multiple of 16, which leaves the swizzle unchanged: LDS destinations
-  // are a base plus an immediate.
-  const __amdgpu_buffer_rsrc_t xres = make_rsrc(X + (int64_t)m0 * K, (uint32_t)((int64_t)(M - m0) * K));
-  const __amdgpu_buffer_rsrc_t wres = make_rsrc(W4 + (int64_t)n0 * ldw, (uint32_t)((int64_t)(N - n0) * ldw));
+  // Operands arrive through buffer resources over the current tile's rows;
+  // 8 threads per 128-byte X row and 4 per W row (coalesced).  Load round p
+  // is XROWS (WROWS) rows further on, a multiple of 16, which leaves the
+  // swizzle unchanged: LDS destinations are a base plus an immediate.
   const int xr0 = tid >> 3, xc0 = tid & 7, wr0 = tid >> 2, wc0 = tid & 3;
   const uint32_t xvoff = (uint32_t)(xr0 * K + 16 * xc0);
   const uint32_t wvoff = (uint32_t)(wr0 * ldw + 16 * wc0);
   const int xdst = xr0 * 128 + 16 * (xc0 ^ swz128(xr0));
   const int wdst = XB + wr0 * 64 + 16 * (wc0 ^ swz64(wr0));
-  auto load = [&](Stage& st, int kt) {
+
+  // Load cursor: the tile and K-stage the next load reads.  It runs two
+  // stages ahead of the computation, across tile boundaries, so the next
+  // tile's first stages are in flight during this tile's epilogue.
+  int l_logical = seq.first, l_kt = 0;
+  auto tile_x = [&](int logical) {
+    int tm, tn;
+    grouped_tile(logical, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM;
+    return make_rsrc(X + (int64_t)m0 * K, (uint32_t)((int64_t)(M - m0) * K));
+  };
+  auto tile_w = [&](int logical) {
+    int tm, tn;
+    grouped_tile(logical, tiles_m, tiles_n, tm, tn);
+    const int n0 = tn * BN;
+    return make_rsrc(W4 + (int64_t)n0 * ldw, (uint32_t)((int64_t)(N - n0) * ldw));
+  };
+  __amdgpu_buffer_rsrc_t xres = tile_x(l_logical), wres = tile_w(l_logical);
+  auto load = [&](Stage& st) {
 #pragma unroll
-    for (int p = 0; p < C::XC; ++p) st.x[p] = buf_load16(xres, xvoff, kt * BK + p * C::XROWS * K);
+    for (int p = 0; p < C::XC; ++p) st.x[p] = buf_load16(xres, xvoff, l_kt * BK + p * C::XROWS * K);
 #pragma unroll
-    for (int p = 0; p < C::WC; ++p) st.w[p] = buf_load16(wres, wvoff, kt * (BK / 2) + p * C::WROWS * ldw);
+    for (int p = 0; p < C::WC; ++p) st.w[p] = buf_load16(wres, wvoff, l_kt * (BK / 2) + p * C::WROWS * ldw);
+    if (++l_kt == nk) {
+      l_kt = 0;
+      l_logical += seq.stride;
+      if (l_logical < tiles_m * tiles_n) {
+        xres = tile_x(l_logical);
+        wres = tile_w(l_logical);
+      }
+    }
   };
   auto store = [&](const Stage& st, int buf) {
     uint8_t* base = smem + buf * SB;
@@ -273,12 +316,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_i8i4_pipe(
   };
 
   v16i acc[WN_T][WM_T];
+  auto zero_acc = [&]() {
 #pragma unroll
-  for (int j = 0; j < WN_T; ++j)
+    for (int j = 0; j < WN_T; ++j)
 #pragma unroll
-    for (int i = 0; i < WM_T; ++i)
+      for (int i = 0; i < WM_T; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[j][i][e] = 0;
+        for (int e = 0; e < 16; ++e) acc[j][i][e] = 0;
+  };
+  zero_acc();
 
   const int h = lane >> 5, r32 = lane & 31;
   auto compute = [&](int buf) {
@@ -312,75 +358,95 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_i8i4_pipe(
     }
   };
 
-  const int nk = K / BK;
-  Stage ra, rb;
-  load(ra, 0);
-  if (nk > 1) load(rb, 1);
-  store(ra, 0);
-  lds_barrier();
-  // Pairs of stages; one loop exit keeps the accumulators in one register
-  // allocation.  An odd last stage (left in LDS buffer 0) follows the loop.
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    // stage kt in LDS buffer 0, stage kt + 1 in rb
-    if (kt + 2 < nk) load(ra, kt + 2);
-    compute(0);
-    store(rb, 1);
-    lds_barrier();
-    // stage kt + 1 in LDS buffer 1, stage kt + 2 in ra
-    if (kt + 3 < nk) load(rb, kt + 3);
-    compute(1);
-    if (kt + 2 < nk) store(ra, 0);
-    lds_barrier();
-  }
-  if (kt < nk) compute(0);
-
-  // Epilogue: lane holds token m = ... + (lane & 31) and, for g = 0..3,
-  // features n = 8g + 4h + 0..3 of each 32 x 32 subtile.
-  const bool full_n = n0 + BN <= N && (N & 3) == 0;
+  // Epilogue of one tile: lane holds token m = ... + (lane & 31) and, for
+  // g = 0..3, features n = 8g + 4h + 0..3 of each 32 x 32 subtile.
+  auto epilogue = [&](int logical) {
+    int tm, tn;
+    grouped_tile(logical, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const bool full_n = n0 + BN <= N && (N & 3) == 0;
 #pragma unroll
-  for (int i = 0; i < WM_T; ++i) {
-    const int m = m0 + wm * WM_T * 32 + i * 32 + r32;
-    if (m >= M) continue;
-    const float sxm = sx[m];
+    for (int i = 0; i < WM_T; ++i) {
+      const int m = m0 + wm * WM_T * 32 + i * 32 + r32;
+      if (m >= M) continue;
+      const float sxm = sx[m];
 #pragma unroll
-    for (int j = 0; j < WN_T; ++j) {
+      for (int j = 0; j < WN_T; ++j) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * WN_T * 32 + j * 32 + 8 * g + 4 * h;
-        const int64_t off = (int64_t)m * N + n;
-        int32_t a[4];
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * WN_T * 32 + j * 32 + 8 * g + 4 * h;
+          const int64_t off = (int64_t)m * N + n;
+          int32_t a[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) a[r] = acc[j][i][4 * g + r] >> 4;
-        if (full_n) {
-          if constexpr (OUT == kOutI32) {
-            *reinterpret_cast<int4*>(reinterpret_cast<int32_t*>(Y) + off) = make_int4(a[0], a[1], a[2], a[3]);
-          } else {
-            const float4 swn = *reinterpret_cast<const float4*>(sw + n);
-            const float y0 = ((float)a[0] * sxm) * swn.x, y1 = ((float)a[1] * sxm) * swn.y;
-            const float y2 = ((float)a[2] * sxm) * swn.z, y3 = ((float)a[3] * sxm) * swn.w;
-            if constexpr (OUT == kOutF32)
-              *reinterpret_cast<float4*>(reinterpret_cast<float*>(Y) + off) = make_float4(y0, y1, y2, y3);
-            else
-              *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(Y) + off) =
-                  make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
-          }
-        } else {
-          for (int r = 0; r < 4; ++r) {
-            if (n + r >= N) break;
+          for (int r = 0; r < 4; ++r) a[r] = acc[j][i][4 * g + r] >> 4;
+          if (full_n) {
             if constexpr (OUT == kOutI32) {
-              reinterpret_cast<int32_t*>(Y)[off + r] = a[r];
+              *reinterpret_cast<int4*>(reinterpret_cast<int32_t*>(Y) + off) = make_int4(a[0], a[1], a[2], a[3]);
             } else {
-              const float y = ((float)a[r] * sxm) * sw[n + r];
+              const float4 swn = *reinterpret_cast<const float4*>(sw + n);
+              const float y0 = ((float)a[0] * sxm) * swn.x, y1 = ((float)a[1] * sxm) * swn.y;
+              const float y2 = ((float)a[2] * sxm) * swn.z, y3 = ((float)a[3] * sxm) * swn.w;
               if constexpr (OUT == kOutF32)
-                reinterpret_cast<float*>(Y)[off + r] = y;
+                *reinterpret_cast<float4*>(reinterpret_cast<float*>(Y) + off) = make_float4(y0, y1, y2, y3);
               else
-                reinterpret_cast<uint16_t*>(Y)[off + r] = __builtin_bit_cast(uint16_t, (__bf16)y);
+                *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(Y) + off) =
+                    make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
+            }
+          } else {
+            for (int r = 0; r < 4; ++r) {
+              if (n + r >= N) break;
+              if constexpr (OUT == kOutI32) {
+                reinterpret_cast<int32_t*>(Y)[off + r] = a[r];
+              } else {
+                const float y = ((float)a[r] * sxm) * sw[n + r];
+                if constexpr (OUT == kOutF32)
+                  reinterpret_cast<float*>(Y)[off + r] = y;
+                else
+                  reinterpret_cast<uint16_t*>(Y)[off + r] = __builtin_bit_cast(uint16_t, (__bf16)y);
+              }
             }
           }
         }
       }
     }
+  };
+
+  // Compute cursor: after a tile's last K-stage, write it out and start over.
+  int ckt = 0, clogical = seq.first;
+  auto finish_stage = [&]() {
+    if (++ckt == nk) {
+      epilogue(clogical);
+      zero_acc();
+      ckt = 0;
+      clogical += seq.stride;
+    }
+  };
+
+  Stage ra, rb;
+  load(ra);
+  if (G > 1) load(rb);
+  store(ra, 0);
+  lds_barrier();
+  // Pairs of stages; one loop exit keeps the accumulators in one register
+  // allocation.  An odd last stage (left in LDS buffer 0) follows the loop.
+  int g = 0;
+  for (; g + 1 < G; g += 2) {
+    // stage g in LDS buffer 0, stage g + 1 in rb
+    if (g + 2 < G) load(ra);
+    compute(0);
+    finish_stage();
+    store(rb, 1);
+    lds_barrier();
+    // stage g + 1 in LDS buffer 1, stage g + 2 in ra
+    if (g + 3 < G) load(rb);
+    compute(1);
+    finish_stage();
+    if (g + 2 < G) store(ra, 0);
+    lds_barrier();
+  }
+  if (g < G) {
+    compute(0);
+    finish_stage();
   }
 }
 
@@ -395,7 +461,8 @@ static hipError_t launch_pipe(const int8_t* x, const float* sx, const uint8_t* w
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int64_t tiles = ((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
-  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(C::THREADS), lds, s, x, sx, w4, sw, y, (int)M,
+  const int64_t grid = persistent_grid(tiles);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::THREADS), lds, s, x, sx, w4, sw, y, (int)M,
                      (int)N, (int)K, decision, want);
   return hipGetLastError();
 }

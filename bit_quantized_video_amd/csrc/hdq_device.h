@@ -191,27 +191,56 @@ __device__ __forceinline__ uint32_t e2m1x2_encode(float a, float b) {
 // so a 16-byte fragment read of 8 consecutive rows touches distinct banks.
 __device__ __forceinline__ int lds_off64(int r, int c) { return r * 64 + 16 * (c ^ ((r >> 1) & 3)); }
 
-// Logical tile of this workgroup.  Workgroups go round-robin to the 8 XCDs
-// (blockIdx % 8), each with its own L2, so every XCD takes a contiguous range
-// of the logical order.  The logical order walks groups of kGroupM tile rows
-// column by column: the ~32 tiles an XCD runs at once then span kGroupM rows
-// x 32/kGroupM columns and share their A and B strips in that XCD's L2,
+// Tile order.  Workgroups go round-robin to the 8 XCDs (blockIdx % 8), each
+// with its own L2, so every XCD takes a contiguous range of the logical
+// order.  The logical order walks groups of kGroupM tile rows column by
+// column: the ~32 tiles an XCD runs at once then span kGroupM rows x
+// 32/kGroupM columns and share their A and B strips in that XCD's L2,
 // instead of one A strip and 32 B strips.
 #ifndef HDQ_GROUP_M
 #define HDQ_GROUP_M 4
 #endif
 constexpr int kGroupM = HDQ_GROUP_M;
-__device__ __forceinline__ void xcd_tile(int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int total = tiles_m * tiles_n;
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7, local = bid >> 3;
-  const int q = total >> 3, r = total & 7;
-  const int logical = xcd * q + (xcd < r ? xcd : r) + local;
+
+// Logical tile index -> (tile row, tile column) in the grouped order.
+__device__ __forceinline__ void grouped_tile(int logical, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int per_group = kGroupM * tiles_n;
   const int g = logical / per_group, in_g = logical - g * per_group;
   const int rows = min(kGroupM, tiles_m - g * kGroupM);
   tn = in_g / rows;
   tm = g * kGroupM + (in_g - tn * rows);
+}
+
+// XCD x's contiguous range [lo, hi) of the logical order.
+__device__ __forceinline__ void xcd_range(int total, int xcd, int& lo, int& hi) {
+  const int q = total >> 3, r = total & 7;
+  lo = xcd * q + (xcd < r ? xcd : r);
+  hi = lo + q + (xcd < r ? 1 : 0);
+}
+
+// Logical tile of a workgroup in a grid of one workgroup per tile.
+__device__ __forceinline__ void xcd_tile(int tiles_m, int tiles_n, int& tm, int& tn) {
+  int lo, hi;
+  xcd_range(tiles_m * tiles_n, blockIdx.x & 7, lo, hi);
+  grouped_tile(lo + (blockIdx.x >> 3), tiles_m, tiles_n, tm, tn);
+}
+
+// Tiles of a persistent workgroup: logical tiles first, first + stride, ...
+// below end.  With one workgroup per tile (gridDim.x == total) that is the
+// xcd_tile tile alone; otherwise gridDim.x is a multiple of 8 and the
+// gridDim.x / 8 workgroups of an XCD deal its range round-robin, so the ones
+// running at the same time hold consecutive logical tiles.
+struct TileSeq {
+  int first, stride, count;
+};
+__device__ __forceinline__ TileSeq tile_seq(int total) {
+  int lo, hi;
+  xcd_range(total, blockIdx.x & 7, lo, hi);
+  const int local = blockIdx.x >> 3;
+  if ((int)gridDim.x >= total) return TileSeq{lo + local, 1, 1};
+  const int per = gridDim.x >> 3;
+  const int n = hi - lo - local;
+  return TileSeq{lo + local, per, n > 0 ? (n + per - 1) / per : 0};
 }
 
 // ---- multi-stage LDS pipelines ------------------------------------------------

@@ -19,6 +19,11 @@ enum OutDtype : int { kOutF32 = 0, kOutBf16 = 1, kOutI32 = 2 };
 // nearest 1/sqrt(hb).
 float hadamard_scale(int hb);
 
+// Grid of a persistent GEMM whose workgroups fill a CU each: `tiles` when
+// that is at most the current device's CU count, else the CU count rounded
+// down to a multiple of 8 (the workgroups then loop over tiles).
+int64_t persistent_grid(int64_t tiles);
+
 // ---- quantize (quant.hip) ----
 // INT8 / INT4 per-row: codes int8 [rows, cols] or packed uint8 [rows, cols/2],
 // row_scale fp32 [rows].
