@@ -235,6 +235,8 @@ struct I8Cfg {
   static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
   static constexpr int BM = WAVES_M * WM_T * 32, BN = WAVES_N * WN_T * 32, BK = 128;
   static constexpr int XB = BM * BK, SB = XB + BN * BK / 2;  // LDS bytes per stage
+  static constexpr int OUT_PITCH = BN * 2 + 16;              // bf16 output row in LDS, padded
+  static constexpr int LDS = (2 * SB > BM * OUT_PITCH) ? 2 * SB : BM * OUT_PITCH;
   static constexpr int XC = XB / 16 / THREADS;                // 16-byte loads per thread
   static constexpr int WC = BN * BK / 2 / 16 / THREADS;
   static constexpr int XROWS = THREADS / 8, WROWS = THREADS / 4;  // rows per load round
@@ -254,6 +256,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_i8i4_pipe(
   if (decision != nullptr && *decision != want) return;
   using C = I8Cfg<WAVES_M, WAVES_N, WM_T, WN_T>;
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, XB = C::XB, SB = C::SB;
+  constexpr int kOutPitch = C::OUT_PITCH;
   using Stage = I8Stage<C::XC, C::WC>;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
@@ -262,8 +265,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_i8i4_pipe(
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   const TileSeq seq = tile_seq(tiles_m * tiles_n);
   const int nk = K / BK;
-  const int G = seq.count * nk;  // K-stages of this workgroup, over all its tiles
-  if (G == 0) return;
   const int ldw = K >> 1;
 
   // Operands arrive through buffer resources over the current tile's rows;
@@ -276,36 +277,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_i8i4_pipe(
   const int xdst = xr0 * 128 + 16 * (xc0 ^ swz128(xr0));
   const int wdst = XB + wr0 * 64 + 16 * (wc0 ^ swz64(wr0));
 
-  // Load cursor: the tile and K-stage the next load reads.  It runs two
-  // stages ahead of the computation, across tile boundaries, so the next
-  // tile's first stages are in flight during this tile's epilogue.
-  int l_logical = seq.first, l_kt = 0;
-  auto tile_x = [&](int logical) {
-    int tm, tn;
-    grouped_tile(logical, tiles_m, tiles_n, tm, tn);
-    const int m0 = tm * BM;
-    return make_rsrc(X + (int64_t)m0 * K, (uint32_t)((int64_t)(M - m0) * K));
-  };
-  auto tile_w = [&](int logical) {
-    int tm, tn;
-    grouped_tile(logical, tiles_m, tiles_n, tm, tn);
-    const int n0 = tn * BN;
-    return make_rsrc(W4 + (int64_t)n0 * ldw, (uint32_t)((int64_t)(N - n0) * ldw));
-  };
-  __amdgpu_buffer_rsrc_t xres = tile_x(l_logical), wres = tile_w(l_logical);
-  auto load = [&](Stage& st) {
+  // Buffer resources over the current tile's rows.
+  __amdgpu_buffer_rsrc_t xres, wres;
+  auto load = [&](Stage& st, int kt) {
 #pragma unroll
-    for (int p = 0; p < C::XC; ++p) st.x[p] = buf_load16(xres, xvoff, l_kt * BK + p * C::XROWS * K);
+    for (int p = 0; p < C::XC; ++p) st.x[p] = buf_load16(xres, xvoff, kt * BK + p * C::XROWS * K);
 #pragma unroll
-    for (int p = 0; p < C::WC; ++p) st.w[p] = buf_load16(wres, wvoff, l_kt * (BK / 2) + p * C::WROWS * ldw);
-    if (++l_kt == nk) {
-      l_kt = 0;
-      l_logical += seq.stride;
-      if (l_logical < tiles_m * tiles_n) {
-        xres = tile_x(l_logical);
-        wres = tile_w(l_logical);
-      }
-    }
+    for (int p = 0; p < C::WC; ++p) st.w[p] = buf_load16(wres, wvoff, kt * (BK / 2) + p * C::WROWS * ldw);
   };
   auto store = [&](const Stage& st, int buf) {
     uint8_t* base = smem + buf * SB;
@@ -364,6 +342,54 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_i8i4_pipe(
     int tm, tn;
     grouped_tile(logical, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
+    if constexpr (OUT == kOutBf16) {
+      // Stage the bf16 tile in LDS (both pipeline buffers are free at a tile
+      // boundary once every wave is past the last stage), then write whole
+      // rows: 32 lanes x 16 bytes per 512-byte row.
+      lds_barrier();
+      // Scales through buffer loads: rows past M and columns past N read 0.
+      const __amdgpu_buffer_rsrc_t sxres = make_rsrc(sx, (uint32_t)M * 4u);
+      const __amdgpu_buffer_rsrc_t swres = make_rsrc(sw, (uint32_t)N * 4u);
+      const int rl0 = wm * WM_T * 32 + r32, nl0 = wn * WN_T * 32 + 4 * h;
+      uint8_t* const lrow = smem + rl0 * kOutPitch + 2 * nl0;
+#pragma unroll
+      for (int i = 0; i < WM_T; ++i) {
+        const float sxm = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(sxres, 4 * (rl0 + i * 32), 4 * m0, 0));
+#pragma unroll
+        for (int j = 0; j < WN_T; ++j) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float4 swn = __builtin_bit_cast(
+                float4, __builtin_amdgcn_raw_buffer_load_b128(swres, 4 * (nl0 + j * 32 + 8 * g), 4 * n0, 0));
+            const float y0 = ((float)(acc[j][i][4 * g + 0] >> 4) * sxm) * swn.x;
+            const float y1 = ((float)(acc[j][i][4 * g + 1] >> 4) * sxm) * swn.y;
+            const float y2 = ((float)(acc[j][i][4 * g + 2] >> 4) * sxm) * swn.z;
+            const float y3 = ((float)(acc[j][i][4 * g + 3] >> 4) * sxm) * swn.w;
+            *reinterpret_cast<uint2*>(lrow + i * 32 * kOutPitch + 2 * (j * 32 + 8 * g)) =
+                make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
+          }
+        }
+      }
+      lds_barrier();
+      uint16_t* y16 = reinterpret_cast<uint16_t*>(Y);
+      const int n = n0 + 8 * (tid & 31);
+      const bool vec = n + 8 <= N && (N & 7) == 0;
+#pragma unroll 4
+      for (int r = tid >> 5; r < BM; r += C::THREADS / 32) {
+        const uint8_t* src = smem + r * kOutPitch + 16 * (tid & 31);
+        if (m0 + r < M) {
+          uint16_t* dst = y16 + (int64_t)(m0 + r) * N + n;
+          if (vec) {
+            *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+          } else {
+            for (int e = 0; e < 8 && n + e < N; ++e) dst[e] = reinterpret_cast<const uint16_t*>(src)[e];
+          }
+        }
+      }
+      lds_barrier();  // the next stage may overwrite the staged tile
+      return;
+    }
     const bool full_n = n0 + BN <= N && (N & 3) == 0;
 #pragma unroll
     for (int i = 0; i < WM_T; ++i) {
@@ -411,42 +437,40 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void k_gemm_i8i4_pipe(
     }
   };
 
-  // Compute cursor: after a tile's last K-stage, write it out and start over.
-  int ckt = 0, clogical = seq.first;
-  auto finish_stage = [&]() {
-    if (++ckt == nk) {
-      epilogue(clogical);
-      zero_acc();
-      ckt = 0;
-      clogical += seq.stride;
+  // Persistent loop over this workgroup's tiles; per tile, the K-stages run
+  // through the two-stage register prefetch and the double-buffered LDS.
+  for (int t = 0; t < seq.count; ++t) {
+    const int logical = seq.first + t * seq.stride;
+    {
+      int tm, tn;
+      grouped_tile(logical, tiles_m, tiles_n, tm, tn);
+      const int m0 = tm * BM, n0 = tn * BN;
+      xres = make_rsrc(X + (int64_t)m0 * K, (uint32_t)((int64_t)(M - m0) * K));
+      wres = make_rsrc(W4 + (int64_t)n0 * ldw, (uint32_t)((int64_t)(N - n0) * ldw));
     }
-  };
-
-  Stage ra, rb;
-  load(ra);
-  if (G > 1) load(rb);
-  store(ra, 0);
-  lds_barrier();
-  // Pairs of stages; one loop exit keeps the accumulators in one register
-  // allocation.  An odd last stage (left in LDS buffer 0) follows the loop.
-  int g = 0;
-  for (; g + 1 < G; g += 2) {
-    // stage g in LDS buffer 0, stage g + 1 in rb
-    if (g + 2 < G) load(ra);
-    compute(0);
-    finish_stage();
-    store(rb, 1);
+    Stage ra, rb;
+    load(ra, 0);
+    if (nk > 1) load(rb, 1);
+    store(ra, 0);
     lds_barrier();
-    // stage g + 1 in LDS buffer 1, stage g + 2 in ra
-    if (g + 3 < G) load(rb);
-    compute(1);
-    finish_stage();
-    if (g + 2 < G) store(ra, 0);
-    lds_barrier();
-  }
-  if (g < G) {
-    compute(0);
-    finish_stage();
+    // Pairs of stages; one loop exit keeps the accumulators in one register
+    // allocation.  An odd last stage (left in LDS buffer 0) follows the loop.
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      // stage kt in LDS buffer 0, stage kt + 1 in rb
+      if (kt + 2 < nk) load(ra, kt + 2);
+      compute(0);
+      store(rb, 1);
+      lds_barrier();
+      // stage kt + 1 in LDS buffer 1, stage kt + 2 in ra
+      if (kt + 3 < nk) load(rb, kt + 3);
+      compute(1);
+      if (kt + 2 < nk) store(ra, 0);
+      lds_barrier();
+    }
+    if (kt < nk) compute(0);
+    epilogue(logical);
+    zero_acc();
   }
 }
 
@@ -455,7 +479,7 @@ static hipError_t launch_pipe(const int8_t* x, const float* sx, const uint8_t* w
                               void* y, int64_t M, int64_t N, int64_t K, const int32_t* decision,
                               int32_t want, hipStream_t s) {
   using C = I8Cfg<WAVES_M, WAVES_N, WM_T, WN_T>;
-  constexpr size_t lds = 2 * (size_t)C::SB;
+  constexpr size_t lds = (size_t)C::LDS;
   auto kern = k_gemm_i8i4_pipe<WAVES_M, WAVES_N, WM_T, WN_T, OUT>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
