@@ -210,6 +210,8 @@ __global__ __launch_bounds__(512) void k_gemm_fp4mx_pipe(
   constexpr int BM = 256, BN = 256, BK = 256, WM_T = 4, WN_T = 2;
   constexpr int XB = BM * BK / 2, WB = BN * BK / 2;  // code bytes per stage
   constexpr int SB = XB + WB + (BM + BN) * 8;         // + E8M0 bytes
+  constexpr int kOutPitch = BN * 2 + 16;              // bf16 output row staged in LDS
+  static_assert(BM * kOutPitch <= 2 * SB, "output tile must fit the pipeline buffers");
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -328,32 +330,59 @@ __global__ __launch_bounds__(512) void k_gemm_fp4mx_pipe(
     int tm, tn;
     grouped_tile(logical, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const bool full_n = n0 + BN <= N && (N & 3) == 0;
+    if constexpr (OUT == kOutBf16) {
+      // Stage the bf16 tile in LDS (both pipeline buffers are free once every
+      // wave is past this stage; the next stage is still in registers), then
+      // write whole 512-byte rows with 16-byte stores.
+      lds_barrier();
+      uint8_t* const lrow = smem + (wm * WM_T * 32 + r32) * kOutPitch + 2 * (wn * WN_T * 32 + 4 * h);
 #pragma unroll
-    for (int i = 0; i < WM_T; ++i) {
-      const int m = m0 + wm * WM_T * 32 + i * 32 + r32;
-      if (m >= M) continue;
+      for (int i = 0; i < WM_T; ++i)
 #pragma unroll
-      for (int j = 0; j < WN_T; ++j) {
+        for (int j = 0; j < WN_T; ++j)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn * WN_T * 32 + j * 32 + 8 * g + 4 * h;
-          const int64_t off = (int64_t)m * N + n;
-          float y[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) y[r] = acc[j][i][4 * g + r] * scale;
-          if (full_n) {
-            if constexpr (OUT == kOutF32)
-              *reinterpret_cast<float4*>(reinterpret_cast<float*>(Y) + off) = make_float4(y[0], y[1], y[2], y[3]);
-            else
-              *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(Y) + off) =
-                  make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+          for (int g = 0; g < 4; ++g) {
+            const v16f& a = acc[j][i];
+            *reinterpret_cast<uint2*>(lrow + i * 32 * kOutPitch + 2 * (j * 32 + 8 * g)) =
+                make_uint2(pack_bf16x2(a[4 * g] * scale, a[4 * g + 1] * scale),
+                           pack_bf16x2(a[4 * g + 2] * scale, a[4 * g + 3] * scale));
+          }
+      lds_barrier();
+      uint16_t* y16 = reinterpret_cast<uint16_t*>(Y);
+      const int n = n0 + 8 * (tid & 31);
+      const bool vec = n + 8 <= N && (N & 7) == 0;
+#pragma unroll 4
+      for (int r = tid >> 5; r < BM; r += 16) {
+        const uint8_t* src = smem + r * kOutPitch + 16 * (tid & 31);
+        if (m0 + r < M) {
+          uint16_t* dst = y16 + (int64_t)(m0 + r) * N + n;
+          if (vec) {
+            *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
           } else {
-            for (int r = 0; r < 4 && n + r < N; ++r) {
-              if constexpr (OUT == kOutF32)
-                reinterpret_cast<float*>(Y)[off + r] = y[r];
-              else
-                reinterpret_cast<uint16_t*>(Y)[off + r] = __builtin_bit_cast(uint16_t, (__bf16)y[r]);
+            for (int e = 0; e < 8 && n + e < N; ++e) dst[e] = reinterpret_cast<const uint16_t*>(src)[e];
+          }
+        }
+      }
+      lds_barrier();  // the next stage may overwrite the staged tile
+    } else {
+      const bool full_n = n0 + BN <= N && (N & 3) == 0;
+#pragma unroll
+      for (int i = 0; i < WM_T; ++i) {
+        const int m = m0 + wm * WM_T * 32 + i * 32 + r32;
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < WN_T; ++j) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int n = n0 + wn * WN_T * 32 + j * 32 + 8 * g + 4 * h;
+            const int64_t off = (int64_t)m * N + n;
+            float y[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) y[r] = acc[j][i][4 * g + r] * scale;
+            if (full_n) {
+              *reinterpret_cast<float4*>(reinterpret_cast<float*>(Y) + off) = make_float4(y[0], y[1], y[2], y[3]);
+            } else {
+              for (int r = 0; r < 4 && n + r < N; ++r) reinterpret_cast<float*>(Y)[off + r] = y[r];
             }
           }
         }
