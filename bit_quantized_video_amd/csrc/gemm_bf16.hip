@@ -194,11 +194,18 @@ __global__ __launch_bounds__(256) void k_gemm_bf16mfma(
 // Pipelined kernel for K % 64 == 0: 256 x 256 tile, 8 waves as 2 (tokens) x
 // 4 (features), each 128 x 64 (4 x 2 subtiles of 32 x 32), 64 K per stage,
 // two register sets prefetching the next two stages through buffer loads
-// (rows past M or N read as zero), double-buffered LDS, LDS-only barriers
-// -- the structure of the INT8 kernel.  LDS holds bf16: 128-byte rows per
+// (rows past M or N read as zero), double-buffered LDS, LDS-only barriers,
+// a persistent tile loop and bf16 output tiles staged in LDS -- the
+// structure of the INT8 kernel.  LDS holds bf16: 128-byte rows per
 // stage (swz128), substep s (16 K) giving lane half h the 16-byte chunk
 // 2s + h.  NVFP4 operands are decoded to exact bf16 when their registers are
 // written to LDS, once per workgroup rather than once per wave.
+// LDS: two 64 KB stages, or one staged 256 x 256 bf16 output tile with a
+// padded row pitch, whichever is larger.
+constexpr int kBf16OutPitch = 256 * 2 + 16;
+constexpr size_t kBf16PipeLds =
+    (2 * 2 * 256 * 64 * 2 > 256 * kBf16OutPitch) ? 2 * 2 * 256 * 64 * 2 : 256 * kBf16OutPitch;
+
 template <int SRC>
 struct Bf16Stage;
 template <>
@@ -219,37 +226,43 @@ __global__ __launch_bounds__(512) void k_gemm_bf16_pipe(
   if (decision != nullptr && *decision != want) return;
   constexpr int BM = 256, BN = 256, BK = 64, WM_T = 4, WN_T = 2;
   constexpr int XB = BM * BK * 2, SB = XB + BN * BK * 2;  // LDS bytes per stage
+  constexpr int kOutPitch = kBf16OutPitch;                // bf16 output row staged in LDS
   using Stage = Bf16Stage<SRC>;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % 2, wn = wave / 2;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  int tm, tn;
-  xcd_tile(tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  const TileSeq seq = tile_seq(tiles_m * tiles_n);
+  const int nk = K / BK;
 
+  // Buffer resources over the current tile's rows; per-thread offsets.
   __amdgpu_buffer_rsrc_t xres, wres, xsres, wsres;
   uint32_t xvoff, wvoff, svoff = 0;
   int dst;  // LDS byte offset of this thread's first chunk (same for X and W)
   if constexpr (SRC == kSrcBf16) {
-    const int64_t ld = 2 * (int64_t)K;
-    xres = make_rsrc(reinterpret_cast<const uint8_t*>(X) + m0 * ld, (uint32_t)((M - m0) * ld));
-    wres = make_rsrc(reinterpret_cast<const uint8_t*>(W) + n0 * ld, (uint32_t)((N - n0) * ld));
     const int r = tid >> 3, c = tid & 7;  // 8 threads per 128-byte row, 64 rows per round
-    xvoff = wvoff = (uint32_t)(r * ld + 16 * c);
+    xvoff = wvoff = (uint32_t)(r * 2 * K + 16 * c);
     dst = r * 128 + 16 * (c ^ swz128(r));
   } else {
-    const int64_t ld = K / 2, lds_ = K / 16;
-    xres = make_rsrc(reinterpret_cast<const uint8_t*>(X) + m0 * ld, (uint32_t)((M - m0) * ld));
-    wres = make_rsrc(reinterpret_cast<const uint8_t*>(W) + n0 * ld, (uint32_t)((N - n0) * ld));
-    xsres = make_rsrc(xsc + m0 * lds_, (uint32_t)((M - m0) * lds_));
-    wsres = make_rsrc(wsc + n0 * lds_, (uint32_t)((N - n0) * lds_));
     const int r = tid >> 1, c = tid & 1;  // 2 threads per row: 32 elements each
-    xvoff = wvoff = (uint32_t)(r * ld + 16 * c);
-    svoff = (uint32_t)(r * lds_ + 2 * c);
+    xvoff = wvoff = (uint32_t)(r * (K / 2) + 16 * c);
+    svoff = (uint32_t)(r * (K / 16) + 2 * c);
     dst = r * 128 + 64 * c;  // chunks 4c .. 4c + 3 of the row (swizzled at store)
   }
+  auto open_tile = [&](int m0, int n0) {
+    if constexpr (SRC == kSrcBf16) {
+      const int64_t ld = 2 * (int64_t)K;
+      xres = make_rsrc(reinterpret_cast<const uint8_t*>(X) + m0 * ld, (uint32_t)((M - m0) * ld));
+      wres = make_rsrc(reinterpret_cast<const uint8_t*>(W) + n0 * ld, (uint32_t)((N - n0) * ld));
+    } else {
+      const int64_t ld = K / 2, lds_ = K / 16;
+      xres = make_rsrc(reinterpret_cast<const uint8_t*>(X) + m0 * ld, (uint32_t)((M - m0) * ld));
+      wres = make_rsrc(reinterpret_cast<const uint8_t*>(W) + n0 * ld, (uint32_t)((N - n0) * ld));
+      xsres = make_rsrc(xsc + m0 * lds_, (uint32_t)((M - m0) * lds_));
+      wsres = make_rsrc(wsc + n0 * lds_, (uint32_t)((N - n0) * lds_));
+    }
+  };
   auto load = [&](Stage& st, int kt) {
     if constexpr (SRC == kSrcBf16) {
 #pragma unroll
@@ -290,12 +303,15 @@ __global__ __launch_bounds__(512) void k_gemm_bf16_pipe(
   };
 
   v16f acc[WN_T][WM_T];
+  auto zero_acc = [&]() {
 #pragma unroll
-  for (int j = 0; j < WN_T; ++j)
+    for (int j = 0; j < WN_T; ++j)
 #pragma unroll
-    for (int i = 0; i < WM_T; ++i)
+      for (int i = 0; i < WM_T; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.0f;
+        for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.0f;
+  };
+  zero_acc();
 
   const int h = lane >> 5, r32 = lane & 31;
   auto compute = [&](int buf) {
@@ -322,56 +338,94 @@ __global__ __launch_bounds__(512) void k_gemm_bf16_pipe(
     }
   };
 
-  const int nk = K / BK;
-  Stage ra, rb;
-  load(ra, 0);
-  if (nk > 1) load(rb, 1);
-  store(ra, 0);
-  lds_barrier();
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    if (kt + 2 < nk) load(ra, kt + 2);
-    compute(0);
-    store(rb, 1);
-    lds_barrier();
-    if (kt + 3 < nk) load(rb, kt + 3);
-    compute(1);
-    if (kt + 2 < nk) store(ra, 0);
-    lds_barrier();
-  }
-  if (kt < nk) compute(0);
-
   const float scale = (SRC == kSrcNvfp4) ? (*xts) * (*wts) : 1.0f;
-  const bool full_n = n0 + BN <= N && (N & 3) == 0;
+  auto epilogue = [&](int m0, int n0) {
+    if constexpr (OUT == kOutBf16) {
+      // Stage the bf16 tile in LDS (both pipeline buffers are free once every
+      // wave is past the last stage), then write whole 512-byte rows with
+      // 16-byte stores.
+      lds_barrier();
+      uint8_t* const lrow = smem + (wm * WM_T * 32 + r32) * kOutPitch + 2 * (wn * WN_T * 32 + 4 * h);
 #pragma unroll
-  for (int i = 0; i < WM_T; ++i) {
-    const int m = m0 + wm * WM_T * 32 + i * 32 + r32;
-    if (m >= M) continue;
+      for (int i = 0; i < WM_T; ++i)
 #pragma unroll
-    for (int j = 0; j < WN_T; ++j) {
+        for (int j = 0; j < WN_T; ++j)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * WN_T * 32 + j * 32 + 8 * g + 4 * h;
-        const int64_t off = (int64_t)m * N + n;
-        float y[4];
+          for (int g = 0; g < 4; ++g) {
+            const v16f& a = acc[j][i];
+            *reinterpret_cast<uint2*>(lrow + i * 32 * kOutPitch + 2 * (j * 32 + 8 * g)) =
+                make_uint2(pack_bf16x2(a[4 * g] * scale, a[4 * g + 1] * scale),
+                           pack_bf16x2(a[4 * g + 2] * scale, a[4 * g + 3] * scale));
+          }
+      lds_barrier();
+      uint16_t* y16 = reinterpret_cast<uint16_t*>(Y);
+      const int n = n0 + 8 * (tid & 31);
+      const bool vec = n + 8 <= N && (N & 7) == 0;
+#pragma unroll 4
+      for (int r = tid >> 5; r < BM; r += 16) {
+        const uint8_t* src = smem + r * kOutPitch + 16 * (tid & 31);
+        if (m0 + r < M) {
+          uint16_t* dst16 = y16 + (int64_t)(m0 + r) * N + n;
+          if (vec) {
+            *reinterpret_cast<uint4*>(dst16) = *reinterpret_cast<const uint4*>(src);
+          } else {
+            for (int e = 0; e < 8 && n + e < N; ++e) dst16[e] = reinterpret_cast<const uint16_t*>(src)[e];
+          }
+        }
+      }
+      lds_barrier();  // the next tile's first stage may overwrite the staged tile
+    } else {
+      const bool full_n = n0 + BN <= N && (N & 3) == 0;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) y[r] = acc[j][i][4 * g + r] * scale;
-        if (full_n) {
-          if constexpr (OUT == kOutF32)
-            *reinterpret_cast<float4*>(reinterpret_cast<float*>(Y) + off) = make_float4(y[0], y[1], y[2], y[3]);
-          else
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(Y) + off) =
-                make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
-        } else {
-          for (int r = 0; r < 4 && n + r < N; ++r) {
-            if constexpr (OUT == kOutF32)
-              reinterpret_cast<float*>(Y)[off + r] = y[r];
-            else
-              reinterpret_cast<uint16_t*>(Y)[off + r] = __builtin_bit_cast(uint16_t, (__bf16)y[r]);
+      for (int i = 0; i < WM_T; ++i) {
+        const int m = m0 + wm * WM_T * 32 + i * 32 + r32;
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < WN_T; ++j) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int n = n0 + wn * WN_T * 32 + j * 32 + 8 * g + 4 * h;
+            const int64_t off = (int64_t)m * N + n;
+            float y[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) y[r] = acc[j][i][4 * g + r] * scale;
+            if (full_n) {
+              *reinterpret_cast<float4*>(reinterpret_cast<float*>(Y) + off) = make_float4(y[0], y[1], y[2], y[3]);
+            } else {
+              for (int r = 0; r < 4 && n + r < N; ++r) reinterpret_cast<float*>(Y)[off + r] = y[r];
+            }
           }
         }
       }
     }
+  };
+
+  // Persistent loop over this workgroup's tiles; per tile, the K-stages run
+  // through the two-stage register prefetch and the double-buffered LDS.
+  for (int t = 0; t < seq.count; ++t) {
+    int tm, tn;
+    grouped_tile(seq.first + t * seq.stride, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    open_tile(m0, n0);
+    Stage ra, rb;
+    load(ra, 0);
+    if (nk > 1) load(rb, 1);
+    store(ra, 0);
+    lds_barrier();
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      if (kt + 2 < nk) load(ra, kt + 2);
+      compute(0);
+      store(rb, 1);
+      lds_barrier();
+      if (kt + 3 < nk) load(rb, kt + 3);
+      compute(1);
+      if (kt + 2 < nk) store(ra, 0);
+      lds_barrier();
+    }
+    if (kt < nk) compute(0);
+    epilogue(m0, n0);
+    zero_acc();
   }
 }
 
@@ -379,14 +433,14 @@ template <int SRC, int OUT>
 static hipError_t launch_bf16_pipe(const void* x, const uint8_t* xs, const float* xts, const void* w,
                                    const uint8_t* ws, const float* wts, void* y, int64_t M, int64_t N,
                                    int64_t K, const int32_t* decision, int32_t want, hipStream_t s) {
-  constexpr size_t lds = 2 * (size_t)(256 * 64 * 2 * 2);
+  constexpr size_t lds = kBf16PipeLds;
   auto kern = k_gemm_bf16_pipe<SRC, OUT>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(512), lds, s, x, xs, xts, w, ws, wts, y, (int)M,
-                     (int)N, (int)K, decision, want);
+  hipLaunchKernelGGL(kern, dim3((unsigned)persistent_grid(tiles)), dim3(512), lds, s, x, xs, xts, w, ws,
+                     wts, y, (int)M, (int)N, (int)K, decision, want);
   return hipGetLastError();
 }
 
