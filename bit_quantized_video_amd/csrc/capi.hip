@@ -130,6 +130,34 @@ int hdq_select_precision(const void* prev_in, const void* prev_out, int64_t prev
                                  static_cast<double*>(ws), nullptr, 0, s));
 }
 
+int hdq_delta_sums(const void* prev_in, const void* prev_out, int64_t numel, double* sums_dev,
+                   void* ws, size_t ws_bytes, void* stream) {
+  if (prev_in == nullptr || prev_out == nullptr || sums_dev == nullptr) return HDQ_ERR_INVALID;
+  if (numel <= 0) return HDQ_ERR_SHAPE;
+  if (ws == nullptr || ws_bytes < align_up(kStatsPartialBytes)) return HDQ_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(launch_stats(static_cast<const uint16_t*>(prev_in),
+                                 static_cast<const uint16_t*>(prev_out), numel, nullptr, 0, 0, 0.0f,
+                                 0.0f, nullptr, nullptr, nullptr, static_cast<double*>(ws), nullptr, 0,
+                                 s, nullptr, sums_dev));
+}
+
+int hdq_select_precision_sums(const double* delta_sums_dev, const void* cur_in, int64_t rows,
+                              int64_t cols, int32_t had_block, float delta_thresh,
+                              float ratio_thresh, int32_t* decision_dev, float* stats_dev, void* ws,
+                              size_t ws_bytes, void* stream) {
+  if (cur_in == nullptr || decision_dev == nullptr || stats_dev == nullptr) return HDQ_ERR_INVALID;
+  if (rows <= 0 || cols <= 0) return HDQ_ERR_SHAPE;
+  if (had_block != 0 && (!valid_block(had_block) || cols % had_block != 0 || cols % 8 != 0))
+    return HDQ_ERR_SHAPE;
+  if (ws == nullptr || ws_bytes < align_up(kStatsPartialBytes)) return HDQ_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(launch_stats(nullptr, nullptr, 0, static_cast<const uint16_t*>(cur_in),
+                                 rows * cols, had_block, delta_thresh, ratio_thresh, decision_dev,
+                                 stats_dev, nullptr, static_cast<double*>(ws), nullptr, 0, s,
+                                 delta_sums_dev, nullptr));
+}
+
 int hdq_quantize(const void* x, int64_t rows, int64_t cols, int32_t had_block, int32_t fmt,
                  const float* tensor_amax, const int32_t* decision_dev, hdq_qtensor* out,
                  void* ws, size_t ws_bytes, void* stream) {

@@ -40,13 +40,16 @@ hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t rows, int64_t cols, int
 // ---- statistics (stats.hip) ----
 constexpr int kStatsMaxBlocks = 1024;
 constexpr size_t kStatsPartialBytes = (size_t)kStatsMaxBlocks * 6 * sizeof(double);
-// Partial sums over prev_in/prev_out (may be null) and cur, then a one-block
-// finalize that writes the five statistics, the decision and/or the rotated
-// amax (any output pointer may be null).
+// Partial sums over prev_in/prev_out (may be null) and cur (may be null with
+// cur_numel 0), then a one-block finalize that writes the five statistics,
+// the decision and/or the rotated amax (any output pointer may be null).
+// delta_sums_out (double[2]): write only the difference sums.  delta_sums_in
+// (double[2]): take the difference sums from there (history present).
 hipError_t launch_stats(const uint16_t* prev_in, const uint16_t* prev_out, int64_t prev_numel,
                         const uint16_t* cur, int64_t cur_numel, int hb, float delta_thresh,
                         float ratio_thresh, int32_t* decision, float* stats, float* amax_out,
-                        double* partials, const int32_t* gate, int32_t want, hipStream_t s);
+                        double* partials, const int32_t* gate, int32_t want, hipStream_t s,
+                        const double* delta_sums_in = nullptr, double* delta_sums_out = nullptr);
 
 // ---- GEMMs ----
 // INT8 activations [M, K] x INT4 weights packed [N, K/2]: y = (acc*sx)*sw.

@@ -158,11 +158,17 @@ __global__ __launch_bounds__(256) void k_stats_partial(
   }
 }
 
+// Finalize.  With sums_out, only the two difference sums are written
+// (sums_out[0] = sum|prev_out - prev_in|, sums_out[1] = sum|prev_in|).  With
+// sums_in, those two sums come from an earlier difference-only pass instead
+// of this pass's partials (which then hold the current input alone).  The
+// reduction order is the same in every mode, so the split passes give the
+// same bits as one pass over all three tensors on the same grid.
 __global__ __launch_bounds__(256) void k_stats_final(
     const double* __restrict__ part, int nparts, int64_t n_cur, int has_history, float c_b,
     float delta_thresh, float ratio_thresh, int32_t* __restrict__ decision,
     float* __restrict__ stats, float* __restrict__ amax_out, const int32_t* __restrict__ gate,
-    int32_t want) {
+    int32_t want, const double* __restrict__ sums_in, double* __restrict__ sums_out) {
   if (gate != nullptr && *gate != want) return;
   const int tid = threadIdx.x;
   double acc[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
@@ -188,7 +194,14 @@ __global__ __launch_bounds__(256) void k_stats_final(
     __syncthreads();
   }
   if (tid != 0) return;
-  const double diff = red[0][0], base = red[0][1], sumabs = red[0][2];
+  if (sums_out != nullptr) {
+    sums_out[0] = red[0][0];
+    sums_out[1] = red[0][1];
+    return;
+  }
+  const double diff = sums_in != nullptr ? sums_in[0] : red[0][0];
+  const double base = sums_in != nullptr ? sums_in[1] : red[0][1];
+  const double sumabs = red[0][2];
   const uint32_t maxbits = (uint32_t)red[0][3];
   const bool nonfinite = maxbits >= 0x7f80u;
   const double maxabs = (double)bf16_lo(maxbits);
@@ -232,7 +245,8 @@ __global__ __launch_bounds__(256) void k_stats_final(
 hipError_t launch_stats(const uint16_t* prev_in, const uint16_t* prev_out, int64_t prev_numel,
                         const uint16_t* cur, int64_t cur_numel, int hb, float delta_thresh,
                         float ratio_thresh, int32_t* decision, float* stats, float* amax_out,
-                        double* partials, const int32_t* gate, int32_t want, hipStream_t s) {
+                        double* partials, const int32_t* gate, int32_t want, hipStream_t s,
+                        const double* delta_sums_in, double* delta_sums_out) {
   const int64_t work = (prev_numel > cur_numel ? prev_numel : cur_numel) / 8;
   int64_t blocks = (work + 255) / 256;
   if (blocks > kStatsMaxBlocks) blocks = kStatsMaxBlocks;
@@ -245,8 +259,8 @@ hipError_t launch_stats(const uint16_t* prev_in, const uint16_t* prev_out, int64
   if (e != hipSuccess) return e;
   const float c_b = hb > 0 ? hadamard_scale(hb) : 0.0f;
   hipLaunchKernelGGL(k_stats_final, dim3(1), dim3(256), 0, s, partials, (int)blocks, cur_numel,
-                     hist ? 1 : 0, c_b, delta_thresh, ratio_thresh, decision, stats, amax_out,
-                     gate, want);
+                     (hist || delta_sums_in != nullptr) ? 1 : 0, c_b, delta_thresh, ratio_thresh,
+                     decision, stats, amax_out, gate, want, delta_sums_in, delta_sums_out);
   return hipGetLastError();
 }
 

@@ -26,7 +26,8 @@ DTYPE_F32, DTYPE_BF16, DTYPE_I32 = 0, 1, 2
 # workspace ops
 OP_SELECT, OP_QUANTIZE, OP_LINEAR = 0, 1, 2
 
-EXPORTS = ("hdq_select_precision", "hdq_quantize", "hdq_linear", "hdq_workspace_bytes",
+EXPORTS = ("hdq_select_precision", "hdq_delta_sums", "hdq_select_precision_sums", "hdq_quantize",
+           "hdq_linear", "hdq_workspace_bytes",
            "hdq_status_string", "hdq_version")
 
 _c = ctypes
@@ -53,6 +54,11 @@ def _load():
     L.hdq_select_precision.restype = _c.c_int
     L.hdq_select_precision.argtypes = [_p, _p, _c.c_int64, _p, _c.c_int64, _c.c_int64, _c.c_int32,
                                        _c.c_float, _c.c_float, _p, _p, _p, _c.c_size_t, _p]
+    L.hdq_delta_sums.restype = _c.c_int
+    L.hdq_delta_sums.argtypes = [_p, _p, _c.c_int64, _p, _p, _c.c_size_t, _p]
+    L.hdq_select_precision_sums.restype = _c.c_int
+    L.hdq_select_precision_sums.argtypes = [_p, _p, _c.c_int64, _c.c_int64, _c.c_int32, _c.c_float,
+                                            _c.c_float, _p, _p, _p, _c.c_size_t, _p]
     L.hdq_quantize.restype = _c.c_int
     L.hdq_quantize.argtypes = [_p, _c.c_int64, _c.c_int64, _c.c_int32, _c.c_int32, _p, _p,
                                _c.POINTER(QTensorDesc), _p, _c.c_size_t, _p]
@@ -154,6 +160,39 @@ def select_precision(prev_in, prev_out, cur_in, had_block=0, delta_thresh=0.1, r
                                   had_block, delta_thresh, ratio_thresh, _ptr(decision),
                                   _ptr(stats), _ptr(ws), ws.numel(), _stream(stream))
     _check("hdq_select_precision", st)
+    return decision, stats
+
+
+def delta_sums(prev_in, prev_out, sums=None, ws=None, stream=None):
+    """hdq_delta_sums: device double[2] {sum|prev_out - prev_in|, sum|prev_in|}."""
+    _bf16(prev_in, "prev_in")
+    _bf16(prev_out, "prev_out")
+    if prev_in.numel() != prev_out.numel():
+        raise ValueError("prev_in and prev_out differ in size")
+    n = prev_in.numel()
+    dev = prev_in.device
+    sums = torch.empty(2, dtype=torch.float64, device=dev) if sums is None else sums
+    ws = _workspace(ws, workspace_bytes(OP_SELECT, 1, n, n), dev)
+    st = lib.hdq_delta_sums(_ptr(prev_in), _ptr(prev_out), n, _ptr(sums), _ptr(ws), ws.numel(),
+                            _stream(stream))
+    _check("hdq_delta_sums", st)
+    return sums
+
+
+def select_precision_sums(delta_sums, cur_in, had_block=0, delta_thresh=0.1, ratio_thresh=50.0,
+                          decision=None, stats=None, ws=None, stream=None):
+    """hdq_select_precision_sums: the selection with the difference sums of
+    delta_sums() (None = no history).  Returns (decision, stats)."""
+    cur_in = _bf16(cur_in, "cur_in")
+    rows, cols = cur_in.shape
+    dev = cur_in.device
+    decision = torch.empty(1, dtype=torch.int32, device=dev) if decision is None else decision
+    stats = torch.empty(5, dtype=torch.float32, device=dev) if stats is None else stats
+    ws = _workspace(ws, workspace_bytes(OP_SELECT, rows, cols, 0), dev)
+    st = lib.hdq_select_precision_sums(_ptr(delta_sums), _ptr(cur_in), rows, cols, had_block,
+                                       delta_thresh, ratio_thresh, _ptr(decision), _ptr(stats),
+                                       _ptr(ws), ws.numel(), _stream(stream))
+    _check("hdq_select_precision_sums", st)
     return decision, stats
 
 

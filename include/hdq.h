@@ -150,6 +150,37 @@ int hdq_select_precision(const void *prev_in, const void *prev_out, int64_t prev
                          float *stats_dev, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * hdq_delta_sums and hdq_select_precision_sums -- step 1 in two parts (same
+ * sources as hdq_select_precision).  The difference statistic depends only
+ * on the previous step's tensors, so it can be computed off the critical
+ * path (e.g. on a second stream while earlier layers' GEMMs run), leaving
+ * only the current input for the selection proper.
+ *
+ * hdq_delta_sums:
+ *   prev_in, prev_out : device bf16 [numel] each (the module's previous-step
+ *                       input and output).
+ *   sums_dev          : device double[2] <- {sum|prev_out - prev_in|,
+ *                       sum|prev_in|}.
+ *   ws, ws_bytes      : device scratch, >= hdq_workspace_bytes(HDQ_OP_SELECT,
+ *                       1, numel, numel, 0) bytes.
+ * hdq_select_precision_sums:
+ *   delta_sums_dev    : device double[2] from hdq_delta_sums (complete
+ *                       before this call's kernels run: same stream or an
+ *                       event), or NULL for no history.
+ *   the other arguments are those of hdq_select_precision.
+ * The two calls together write what hdq_select_precision writes for the
+ * same tensors, bit for bit when numel == rows * cols (the statistics'
+ * per-workgroup partials and their fixed-order reduction are the same); for
+ * other sizes, equal up to the rounding of the double sums.
+ */
+int hdq_delta_sums(const void *prev_in, const void *prev_out, int64_t numel, double *sums_dev,
+                   void *ws, size_t ws_bytes, void *stream);
+int hdq_select_precision_sums(const double *delta_sums_dev, const void *cur_in, int64_t rows,
+                              int64_t cols, int32_t had_block, float delta_thresh,
+                              float ratio_thresh, int32_t *decision_dev, float *stats_dev,
+                              void *ws, size_t ws_bytes, void *stream);
+
+/*
  * hdq_quantize -- step 2: block-Hadamard rotation fused with quantization
  * (summary sections one and four).  Also prepares weights offline.
  *

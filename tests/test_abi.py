@@ -26,7 +26,8 @@ def hdq():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for fn in ("hdq_select_precision", "hdq_quantize", "hdq_linear", "hdq_workspace_bytes",
+    for fn in ("hdq_select_precision", "hdq_delta_sums", "hdq_select_precision_sums", "hdq_quantize",
+               "hdq_linear", "hdq_workspace_bytes",
                "hdq_status_string", "hdq_version"):
         assert fn in names
 
@@ -69,6 +70,16 @@ def test_validation_happens_before_any_launch(hdq):
     assert L.hdq_select_precision(None, None, 0, fake, 4, 60, 16, 0.1, 50.0, fake, fake, fake, 1 << 20, None) == hdq.ERR_SHAPE
     assert L.hdq_select_precision(None, None, 0, fake, 0, 64, 0, 0.1, 50.0, fake, fake, fake, 1 << 20, None) == hdq.ERR_SHAPE
     assert L.hdq_select_precision(None, None, 0, fake, 4, 64, 0, 0.1, 50.0, fake, fake, None, 0, None) == hdq.ERR_WORKSPACE
+    # the two-part selection: null tensors, bad sizes, missing workspace
+    assert L.hdq_delta_sums(None, fake, 64, fake, fake, 1 << 20, None) == hdq.ERR_INVALID
+    assert L.hdq_delta_sums(fake, fake, 64, None, fake, 1 << 20, None) == hdq.ERR_INVALID
+    assert L.hdq_delta_sums(fake, fake, 0, fake, fake, 1 << 20, None) == hdq.ERR_SHAPE
+    assert L.hdq_delta_sums(fake, fake, 64, fake, None, 0, None) == hdq.ERR_WORKSPACE
+    assert L.hdq_select_precision_sums(fake, None, 4, 64, 0, 0.1, 50.0, fake, fake, fake, 1 << 20, None) == hdq.ERR_INVALID
+    assert L.hdq_select_precision_sums(None, fake, 4, 64, 0, 0.1, 50.0, None, fake, fake, 1 << 20, None) == hdq.ERR_INVALID
+    assert L.hdq_select_precision_sums(None, fake, 4, 60, 16, 0.1, 50.0, fake, fake, fake, 1 << 20, None) == hdq.ERR_SHAPE
+    assert L.hdq_select_precision_sums(None, fake, 0, 64, 0, 0.1, 50.0, fake, fake, fake, 1 << 20, None) == hdq.ERR_SHAPE
+    assert L.hdq_select_precision_sums(fake, fake, 4, 64, 0, 0.1, 50.0, fake, fake, None, 0, None) == hdq.ERR_WORKSPACE
     # quantize: bad fmt, bad shapes, missing buffers, missing workspace for the amax pre-pass
     q = hdq.QTensorDesc(0, 0, 0, 0, fake, fake, fake, fake)
     assert L.hdq_quantize(fake, 4, 64, 16, 9, None, None, ctypes.byref(q), None, 0, None) == hdq.ERR_INVALID

@@ -198,6 +198,31 @@ def test_stats_match_oracle(M, K, s):
     assert decision_ok(dec, ref, True)
 
 
+@pytest.mark.parametrize("M,K,hb,s", [(333, 3072, 128, 0.2), (64, 1024, 0, 0.05), (17, 12288, 128, 0.1),
+                                      (1000, 128, 64, 0.0999), (17776, 3072, 128, 0.08)])
+def test_two_part_selection_matches_one_pass(M, K, hb, s):
+    """hdq_delta_sums + hdq_select_precision_sums write the same bits as
+    hdq_select_precision; the sums themselves match the oracle's."""
+    say(f"two-part selection M={M} K={K} hb={hb}")
+    rng = synth.rng_for(112, M)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x16 = synth.to_bf16_bits(x)
+    po16 = synth.to_bf16_bits(x + rng.standard_normal((M, K)).astype(np.float32) * np.float32(s))
+    xd, pid, pod = to_dev(x16), to_dev(x16.copy()), to_dev(po16)
+    bits = lambda t: t.view(torch.int32).cpu().numpy()
+    d1, s1 = hdq.select_precision(pid, pod, xd, hb)
+    sums = hdq.delta_sums(pid, pod)
+    d2, s2 = hdq.select_precision_sums(sums, xd, hb)
+    d3, s3 = hdq.select_precision(None, None, xd, hb)
+    d4, s4 = hdq.select_precision_sums(None, xd, hb)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(s1), bits(s2)) and int(d1.item()) == int(d2.item())
+    assert np.array_equal(bits(s3), bits(s4)) and int(d3.item()) == int(d4.item())
+    ref = O.stats(x16, po16, x16, hb)
+    got = sums.cpu().numpy()
+    assert abs(got[0] / got[1] - ref[0]) <= 2e-6 * ref[0]
+
+
 def test_stats_hand_cases():
     ones = np.ones((4, 64), np.float32)
     b = synth.to_bf16_bits
