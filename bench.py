@@ -59,6 +59,12 @@ def parse():
                     help="NVFP4 recipe of the headline run: MX-compatible (FP4 MFMA, default) or "
                          "plain (exact, bf16 MFMA); the schedule also times the other one")
     ap.add_argument("--config", type=int, default=5, help="5: schedule; 1-4: one linear layer")
+    ap.add_argument("--delta", choices=["overlap", "inline"], default="overlap",
+                    help="previous-step difference on a second stream ahead of each layer call "
+                         "(overlap, default) or inside the selection pass (inline)")
+    ap.add_argument("--delta-ahead", type=int, default=2,
+                    help="with --delta overlap: the difference of call k + D runs beside the GEMMs "
+                         "of call k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-copy", action="store_true")
     return ap.parse_args()
@@ -189,50 +195,93 @@ def build_schedule(args, hdq, synth):
     T, B, L = args.timesteps, args.blocks, len(synth.SCHEDULE_LAYERS)
     dec = torch.full((T, B, L, 1), -1, dtype=torch.int32, device=dev)
     sts = torch.zeros((T, B, L, 5), dtype=torch.float32, device=dev)
+    # previous-step difference sums, computed on a second stream (default
+    # priority) ahead of the layer calls that need them
+    sums = torch.zeros((T, B, L, 2), dtype=torch.float64, device=dev)
+    ws_delta = torch.empty_like(ws_sel)
+    side = torch.cuda.Stream(device=dev)
     return dict(M=M, recipes=recipes, blocks=blocks, shared=shared, ws_sel=ws_sel, dec=dec, sts=sts,
-                s_levels=s_levels)
+                s_levels=s_levels, sums=sums, ws_delta=ws_delta, side=side)
 
 
-def run_schedule_step(S, args, hdq, recipe, events=None):
+def run_schedule_step(S, args, hdq, recipe, events=None, side_events=None):
     """One step: every timestep, block and layer, NVFP4 layers in `recipe`.
-    With `events`, records 7 HIP events per layer call (stream order:
-    select | q8 | q4 | g8 | g4 | gbf)."""
-    M = S["M"]
-    k = 0
-    for t in range(args.timesteps):
-        for b, layers in enumerate(S["blocks"]):
-            for li, L in enumerate(layers):
-                sh = S["shared"][li]
-                d = S["dec"][t, b, li]
-                st = S["sts"][t, b, li]
-                ev = events[k] if events is not None else None
-                k += 1
-                if ev: ev[0].record()
-                hdq.select_precision(L["prev_in"], L["prev_out"][t], L["x"], HB, DELTA_T, RATIO_T,
-                                     decision=d, stats=st, ws=S["ws_sel"])
-                if ev: ev[1].record()
-                hdq.quantize(L["x"], HB, hdq.FMT_INT8_ROW, out=sh["xq8"], decision=d)
-                if ev: ev[2].record()
-                hdq.quantize(L["x"], HB, S["recipes"][recipe], tensor_amax=st[4:5], out=sh["xq4"][recipe],
-                             decision=d)
-                if ev: ev[3].record()
-                W = L["W"][recipe]
-                hdq.linear(hdq.PREC_INT8, None, W, decision=d, xq=sh["xq8"], y=sh["y"])
-                if ev: ev[4].record()
-                hdq.linear(hdq.PREC_NVFP4, None, W, decision=d, xq=sh["xq4"][recipe], y=sh["y"])
-                if ev: ev[5].record()
-                hdq.linear(hdq.PREC_BF16, L["x"], W, decision=d, y=sh["y"])
-                if ev: ev[6].record()
-    return k
+    With `events`, records 7 HIP events per layer call on the main stream
+    (select | q8 | q4 | g8 | g4 | gbf) and, with --delta overlap, 2 per call
+    on the difference stream (`side_events`)."""
+    calls = [(t, b, li) for t in range(args.timesteps) for b in range(len(S["blocks"]))
+             for li in range(len(S["blocks"][b]))]
+    main = torch.cuda.current_stream()
+    side = S["side"]
+    overlap = args.delta == "overlap"
+    done = [None] * len(calls)
+
+    def enqueue_delta(k, gate=None):
+        t, b, li = calls[k]
+        L = S["blocks"][b][li]
+        if gate is not None:
+            side.wait_event(gate)
+        with torch.cuda.stream(side):
+            se = side_events[k] if side_events is not None else None
+            if se: se[0].record(side)
+            hdq.delta_sums(L["prev_in"], L["prev_out"][t], sums=S["sums"][t, b, li], ws=S["ws_delta"],
+                           stream=side)
+            if se: se[1].record(side)
+            ev = torch.cuda.Event()
+            ev.record(side)
+        done[k] = ev
+
+    ahead = max(1, args.delta_ahead)
+    if overlap:
+        side.wait_stream(main)  # the previous step's readers of the sums are enqueued before
+        for k in range(min(ahead, len(calls))):
+            enqueue_delta(k)
+    for k, (t, b, li) in enumerate(calls):
+        L = S["blocks"][b][li]
+        sh = S["shared"][li]
+        d = S["dec"][t, b, li]
+        st = S["sts"][t, b, li]
+        ev = events[k] if events is not None else None
+        if overlap:
+            main.wait_event(done[k])
+        if ev: ev[0].record()
+        if overlap:
+            hdq.select_precision_sums(S["sums"][t, b, li], L["x"], HB, DELTA_T, RATIO_T, decision=d,
+                                      stats=st, ws=S["ws_sel"])
+        else:
+            hdq.select_precision(L["prev_in"], L["prev_out"][t], L["x"], HB, DELTA_T, RATIO_T,
+                                 decision=d, stats=st, ws=S["ws_sel"])
+        if ev: ev[1].record()
+        hdq.quantize(L["x"], HB, hdq.FMT_INT8_ROW, out=sh["xq8"], decision=d)
+        if ev: ev[2].record()
+        hdq.quantize(L["x"], HB, S["recipes"][recipe], tensor_amax=st[4:5], out=sh["xq4"][recipe],
+                     decision=d)
+        if ev: ev[3].record()
+        if overlap and k + ahead < len(calls):
+            # the difference of a later call streams beside this call's
+            # compute-bound GEMMs rather than beside its memory-bound passes
+            gate = torch.cuda.Event()
+            gate.record(main)
+            enqueue_delta(k + ahead, gate)
+        W = L["W"][recipe]
+        hdq.linear(hdq.PREC_INT8, None, W, decision=d, xq=sh["xq8"], y=sh["y"])
+        if ev: ev[4].record()
+        hdq.linear(hdq.PREC_NVFP4, None, W, decision=d, xq=sh["xq4"][recipe], y=sh["y"])
+        if ev: ev[5].record()
+        hdq.linear(hdq.PREC_BF16, L["x"], W, decision=d, y=sh["y"])
+        if ev: ev[6].record()
+    return len(calls)
 
 
-def schedule_kernel_times(S, args, events_per_step, synth, recipe):
+def schedule_kernel_times(S, args, events_per_step, synth, recipe, side_per_step=None):
     """Per-kernel durations from the recorded events, attributed by the
     device decision of each layer call."""
     M = S["M"]
     decisions = S["dec"].cpu().numpy().reshape(args.timesteps, args.blocks, -1)
     kt = KernelTimes()
-    for evs in events_per_step:
+    inline = args.delta == "inline"
+    for s_i, evs in enumerate(events_per_step):
+        side = side_per_step[s_i] if side_per_step is not None else None
         k = 0
         for t in range(args.timesteps):
             for b in range(args.blocks):
@@ -242,7 +291,11 @@ def schedule_kernel_times(S, args, events_per_step, synth, recipe):
                     d = int(decisions[t, b, li])
                     dt = [ev[i].elapsed_time(ev[i + 1]) for i in range(6)]
                     flops = 2.0 * M * N * K
-                    kt.add("select_stats", dt[0], stats_bytes(M, K), stats_bytes(M, K))
+                    sel = stats_bytes(M, K) if inline else 2 * M * K
+                    kt.add("select_stats", dt[0], sel, sel)
+                    if side is not None:
+                        kt.add("delta_sums", side[k - 1][0].elapsed_time(side[k - 1][1]), 4 * M * K,
+                               4 * M * K)
                     q8, q4 = quant_bytes(M, K, "int8"), quant_bytes(M, K, "nvfp4")
                     kt.add("quant_int8" if d == 1 else "quant_int8_gated_off", dt[1],
                            q8 if d == 1 else 0, q8 if d == 1 else 0)
@@ -310,14 +363,18 @@ def time_schedule(S, args, hdq, synth, recipe):
     n_calls = args.timesteps * args.blocks * len(synth.SCHEDULE_LAYERS)
     events = [[[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(n_calls)]
               for _ in range(args.steps)]
+    side = None
+    if args.delta == "overlap":
+        side = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_calls)]
+                for _ in range(args.steps)]
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps ({recipe})")
     t0 = time.perf_counter()
     for s in range(args.steps):
-        run_schedule_step(S, args, hdq, recipe, events[s])
+        run_schedule_step(S, args, hdq, recipe, events[s], side[s] if side else None)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    kt, decisions = schedule_kernel_times(S, args, events, synth, recipe)
+    kt, decisions = schedule_kernel_times(S, args, events, synth, recipe, side)
     return 1e3 * elapsed / args.steps, kt, decisions
 
 
@@ -352,7 +409,8 @@ def bench_schedule(args, hdq, synth):
     ks = kt.summary()
     counts = {p: int((decisions == v).sum()) for p, v in (("nvfp4", 0), ("int8", 1), ("bf16", 2))}
     # dominant kernel: the selected-path kernel with the most time
-    main_kinds = ["gemm_int8", "gemm_nvfp4", "gemm_bf16", "quant_int8", "quant_nvfp4", "select_stats"]
+    main_kinds = ["gemm_int8", "gemm_nvfp4", "gemm_bf16", "quant_int8", "quant_nvfp4", "select_stats",
+                  "delta_sums"]
     dom = max((k for k in main_kinds if k in ks), key=lambda k: ks[k]["total_ms"])
     roof = roofline_for(dom, ks[dom], args.fp4, copy_gbps)
     q_bytes = sum(kt.work[k] for k in ("quant_int8", "quant_nvfp4") if k in kt.work)
@@ -380,7 +438,7 @@ def bench_schedule(args, hdq, synth):
         "quant_gbps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1) if q_ms > 0 else None,
         "copy_gbps": round(copy_gbps, 1),
         "quant_roofline": {k: roofline_for(k, ks[k], args.fp4, copy_gbps)
-                           for k in ("quant_int8", "quant_nvfp4", "select_stats") if k in ks},
+                           for k in ("quant_int8", "quant_nvfp4", "select_stats", "delta_sums") if k in ks},
         "fused_quant_linear_tops": round(ql_flops / (ql_ms * 1e-3) / 1e12, 2) if ql_ms > 0 else None,
         "decisions": counts,
         "kernels": {k: {"launches": v["launches"], "total_ms": v["total_ms"], "avg_us": v["avg_us"],

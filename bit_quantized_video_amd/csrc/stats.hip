@@ -34,6 +34,12 @@ __device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
   return v;
 }
 
+// MODE: 0 both passes (prev_in may be null), 1 the difference pass alone,
+// 2 the current-input pass alone.  The modes share the loops, so a split
+// pair of launches gives the partials of one combined launch bit for bit.
+enum { kPassBoth = 0, kPassDelta = 1, kPassCur = 2 };
+
+template <int MODE>
 __global__ __launch_bounds__(256) void k_stats_partial(
     const uint16_t* __restrict__ prev_in, const uint16_t* __restrict__ prev_out, int64_t n_prev,
     const uint16_t* __restrict__ cur, int64_t n_cur, int hb, double* __restrict__ part,
@@ -46,7 +52,7 @@ __global__ __launch_bounds__(256) void k_stats_partial(
   // --- relative L1 difference of the previous step's input and output.
   // float32 sums over each 8-element chunk, double across chunks.
   double diff = 0.0, base = 0.0;
-  if (prev_in != nullptr) {
+  if (MODE != kPassCur && prev_in != nullptr) {
     const int64_t nch = n_prev >> 3;
     const uint4* a4 = reinterpret_cast<const uint4*>(prev_in);
     const uint4* o4 = reinterpret_cast<const uint4*>(prev_out);
@@ -94,7 +100,7 @@ __global__ __launch_bounds__(256) void k_stats_partial(
   uint32_t maxbits = 0u;
   double sumabs = 0.0;
   float rotmax = 0.0f;
-  {
+  if (MODE != kPassDelta) {
     const int64_t nch = n_cur >> 3;
     const uint4* c4 = reinterpret_cast<const uint4*>(cur);
     const int64_t wave = gtid >> 6, nwaves = gthreads >> 6;
@@ -252,9 +258,11 @@ hipError_t launch_stats(const uint16_t* prev_in, const uint16_t* prev_out, int64
   if (blocks > kStatsMaxBlocks) blocks = kStatsMaxBlocks;
   if (blocks < 1) blocks = 1;
   const bool hist = prev_in != nullptr && prev_out != nullptr;
-  hipLaunchKernelGGL(k_stats_partial, dim3((unsigned)blocks), dim3(256), 0, s,
-                     hist ? prev_in : nullptr, hist ? prev_out : nullptr, hist ? prev_numel : 0,
-                     cur, cur_numel, hb, partials, gate, want);
+  auto kern = !hist ? k_stats_partial<kPassCur>
+                    : (cur == nullptr ? k_stats_partial<kPassDelta> : k_stats_partial<kPassBoth>);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, s, hist ? prev_in : nullptr,
+                     hist ? prev_out : nullptr, hist ? prev_numel : 0, cur, cur_numel, hb, partials,
+                     gate, want);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float c_b = hb > 0 ? hadamard_scale(hb) : 0.0f;

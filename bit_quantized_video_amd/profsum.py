@@ -41,7 +41,8 @@ CSRC = os.path.join(HERE, "csrc")
 # Step of the path -> kernel-name pattern (bf16-output GEMMs only: the
 # schedule writes bf16; the f32-output variants belong to the quality check).
 KINDS = OrderedDict([
-    ("select_stats", r"k_stats_partial"),
+    ("delta_sums", r"k_stats_partial<1>"),
+    ("select_stats", r"k_stats_partial(<[02]>)?"),
     ("select_final", r"k_stats_final"),
     ("quant_int8", r"k_quant_int_rows(_long)?<\d+, \d+, false>"),
     ("quant_nvfp4_mx", r"k_quant_nvfp4<true>"),
@@ -53,7 +54,7 @@ KINDS = OrderedDict([
 ])
 # Sources each kind is built from (any change voids a stored traffic figure).
 SOURCES = {
-    "select_stats": ["stats.hip"], "select_final": ["stats.hip"],
+    "delta_sums": ["stats.hip"], "select_stats": ["stats.hip"], "select_final": ["stats.hip"],
     "quant_int8": ["quant.hip"], "quant_nvfp4_mx": ["quant.hip"], "quant_nvfp4": ["quant.hip"],
     "gemm_int8": ["gemm_i8.hip"], "gemm_nvfp4_mx": ["gemm_fp4.hip"],
     "gemm_nvfp4": ["gemm_bf16.hip"], "gemm_bf16": ["gemm_bf16.hip"],

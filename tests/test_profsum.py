@@ -6,6 +6,9 @@ from bit_quantized_video_amd import profsum as P
 def test_classify_kernel_names():
     cases = {
         "hdq::k_stats_partial(unsigned short const*)": "select_stats",
+        "void hdq::k_stats_partial<0>(unsigned short const*)": "select_stats",
+        "void hdq::k_stats_partial<2>(unsigned short const*)": "select_stats",
+        "void hdq::k_stats_partial<1>(unsigned short const*)": "delta_sums",
         "hdq::k_stats_final(double const*)": "select_final",
         "void hdq::k_quant_int_rows<128, 3, false>(int)": "quant_int8",
         "void hdq::k_quant_int_rows<256, 6, true>(int)": None,  # INT4 weight preparation
