@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--delta", choices=["overlap", "inline"], default="overlap",
                     help="previous-step difference on a second stream ahead of each layer call "
                          "(overlap, default) or inside the selection pass (inline)")
+    ap.add_argument("--fuse", choices=["on", "off"], default="on",
+                    help="selection fused with the INT8 per-token quantization of the input (on, "
+                         "default; the codes are written whatever the decision) or separate")
     ap.add_argument("--delta-ahead", type=int, default=2,
                     help="with --delta overlap: the difference of call k + D runs beside the GEMMs "
                          "of call k")
@@ -199,9 +202,10 @@ def build_schedule(args, hdq, synth):
     # priority) ahead of the layer calls that need them
     sums = torch.zeros((T, B, L, 2), dtype=torch.float64, device=dev)
     ws_delta = torch.empty_like(ws_sel)
+    ws_sq8 = torch.empty(hdq.workspace_bytes(hdq.OP_SELECT_Q8, M, 12288), dtype=torch.uint8, device=dev)
     side = torch.cuda.Stream(device=dev)
     return dict(M=M, recipes=recipes, blocks=blocks, shared=shared, ws_sel=ws_sel, dec=dec, sts=sts,
-                s_levels=s_levels, sums=sums, ws_delta=ws_delta, side=side)
+                s_levels=s_levels, sums=sums, ws_delta=ws_delta, ws_sq8=ws_sq8, side=side)
 
 
 def run_schedule_step(S, args, hdq, recipe, events=None, side_events=None):
@@ -244,15 +248,23 @@ def run_schedule_step(S, args, hdq, recipe, events=None, side_events=None):
         ev = events[k] if events is not None else None
         if overlap:
             main.wait_event(done[k])
+        fused = args.fuse == "on"
+        if fused and not overlap:
+            # the difference on the main stream, right before the selection
+            hdq.delta_sums(L["prev_in"], L["prev_out"][t], sums=S["sums"][t, b, li], ws=S["ws_delta"])
         if ev: ev[0].record()
-        if overlap:
+        if fused:
+            hdq.select_quantize_int8(S["sums"][t, b, li], L["x"], HB, DELTA_T, RATIO_T, decision=d,
+                                     stats=st, out=sh["xq8"], ws=S["ws_sq8"])
+        elif overlap:
             hdq.select_precision_sums(S["sums"][t, b, li], L["x"], HB, DELTA_T, RATIO_T, decision=d,
                                       stats=st, ws=S["ws_sel"])
         else:
             hdq.select_precision(L["prev_in"], L["prev_out"][t], L["x"], HB, DELTA_T, RATIO_T,
                                  decision=d, stats=st, ws=S["ws_sel"])
         if ev: ev[1].record()
-        hdq.quantize(L["x"], HB, hdq.FMT_INT8_ROW, out=sh["xq8"], decision=d)
+        if not fused:
+            hdq.quantize(L["x"], HB, hdq.FMT_INT8_ROW, out=sh["xq8"], decision=d)
         if ev: ev[2].record()
         hdq.quantize(L["x"], HB, S["recipes"][recipe], tensor_amax=st[4:5], out=sh["xq4"][recipe],
                      decision=d)
@@ -280,6 +292,7 @@ def schedule_kernel_times(S, args, events_per_step, synth, recipe, side_per_step
     decisions = S["dec"].cpu().numpy().reshape(args.timesteps, args.blocks, -1)
     kt = KernelTimes()
     inline = args.delta == "inline"
+    fused = args.fuse == "on"
     for s_i, evs in enumerate(events_per_step):
         side = side_per_step[s_i] if side_per_step is not None else None
         k = 0
@@ -291,14 +304,18 @@ def schedule_kernel_times(S, args, events_per_step, synth, recipe, side_per_step
                     d = int(decisions[t, b, li])
                     dt = [ev[i].elapsed_time(ev[i + 1]) for i in range(6)]
                     flops = 2.0 * M * N * K
-                    sel = stats_bytes(M, K) if inline else 2 * M * K
-                    kt.add("select_stats", dt[0], sel, sel)
+                    q8, q4 = quant_bytes(M, K, "int8"), quant_bytes(M, K, "nvfp4")
+                    if fused:
+                        # one pass: x read once, INT8 codes written
+                        kt.add("select_quant_int8", dt[0], q8, q8)
+                    else:
+                        sel = stats_bytes(M, K) if inline else 2 * M * K
+                        kt.add("select_stats", dt[0], sel, sel)
+                        kt.add("quant_int8" if d == 1 else "quant_int8_gated_off", dt[1],
+                               q8 if d == 1 else 0, q8 if d == 1 else 0)
                     if side is not None:
                         kt.add("delta_sums", side[k - 1][0].elapsed_time(side[k - 1][1]), 4 * M * K,
                                4 * M * K)
-                    q8, q4 = quant_bytes(M, K, "int8"), quant_bytes(M, K, "nvfp4")
-                    kt.add("quant_int8" if d == 1 else "quant_int8_gated_off", dt[1],
-                           q8 if d == 1 else 0, q8 if d == 1 else 0)
                     kt.add("quant_nvfp4" if d == 0 else "quant_nvfp4_gated_off", dt[2],
                            q4 if d == 0 else 0, q4 if d == 0 else 0)
                     for kind, prec, dd, i in (("gemm_int8", "int8", 1, 3), ("gemm_nvfp4", "nvfp4", 0, 4),
@@ -410,11 +427,13 @@ def bench_schedule(args, hdq, synth):
     counts = {p: int((decisions == v).sum()) for p, v in (("nvfp4", 0), ("int8", 1), ("bf16", 2))}
     # dominant kernel: the selected-path kernel with the most time
     main_kinds = ["gemm_int8", "gemm_nvfp4", "gemm_bf16", "quant_int8", "quant_nvfp4", "select_stats",
-                  "delta_sums"]
+                  "select_quant_int8", "delta_sums"]
     dom = max((k for k in main_kinds if k in ks), key=lambda k: ks[k]["total_ms"])
     roof = roofline_for(dom, ks[dom], args.fp4, copy_gbps)
-    q_bytes = sum(kt.work[k] for k in ("quant_int8", "quant_nvfp4") if k in kt.work)
-    q_ms = sum(kt.t[k] for k in ("quant_int8", "quant_nvfp4") if k in kt.t)
+    # quantization passes (with --fuse on, the INT8 one is the selection pass)
+    q_kinds = ("quant_int8", "select_quant_int8", "quant_nvfp4")
+    q_bytes = sum(kt.work[k] for k in q_kinds if k in kt.work)
+    q_ms = sum(kt.t[k] for k in q_kinds if k in kt.t)
     # effective TOPS of the fused quant + linear alone (selected kernels only)
     ql_ms = q_ms + sum(kt.t.get(k, 0.0) for k in ("gemm_int8", "gemm_nvfp4", "gemm_bf16"))
     ql_flops = sum(kt.work.get(k, 0.0) for k in ("gemm_int8", "gemm_nvfp4", "gemm_bf16"))
@@ -438,7 +457,8 @@ def bench_schedule(args, hdq, synth):
         "quant_gbps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1) if q_ms > 0 else None,
         "copy_gbps": round(copy_gbps, 1),
         "quant_roofline": {k: roofline_for(k, ks[k], args.fp4, copy_gbps)
-                           for k in ("quant_int8", "quant_nvfp4", "select_stats", "delta_sums") if k in ks},
+                           for k in ("quant_int8", "quant_nvfp4", "select_stats", "select_quant_int8",
+                                     "delta_sums") if k in ks},
         "fused_quant_linear_tops": round(ql_flops / (ql_ms * 1e-3) / 1e12, 2) if ql_ms > 0 else None,
         "decisions": counts,
         "kernels": {k: {"launches": v["launches"], "total_ms": v["total_ms"], "avg_us": v["avg_us"],

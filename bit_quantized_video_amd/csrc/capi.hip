@@ -100,6 +100,11 @@ size_t hdq_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N, int32_t 
     case HDQ_OP_QUANTIZE:
       if (!valid_fmt(fmt)) return 0;
       return is_fp4(fmt) ? amax_prepass_bytes() : 0;
+    case HDQ_OP_SELECT_Q8: {
+      // one statistics partial per row (or the two-pass route's partials)
+      const size_t per_row = (size_t)(M > 0 ? M : 0) * 6 * sizeof(double);
+      return align_up(per_row > kStatsPartialBytes ? per_row : kStatsPartialBytes);
+    }
     case HDQ_OP_LINEAR: {
       (void)N;
       size_t b = qtensor_bytes(M, K, HDQ_FMT_INT8_ROW);
@@ -156,6 +161,46 @@ int hdq_select_precision_sums(const double* delta_sums_dev, const void* cur_in, 
                                  rows * cols, had_block, delta_thresh, ratio_thresh, decision_dev,
                                  stats_dev, nullptr, static_cast<double*>(ws), nullptr, 0, s,
                                  delta_sums_dev, nullptr));
+}
+
+int hdq_select_quantize_int8(const double* delta_sums_dev, const void* cur_in, int64_t rows,
+                             int64_t cols, int32_t had_block, float delta_thresh, float ratio_thresh,
+                             int32_t* decision_dev, float* stats_dev, hdq_qtensor* xq8, void* ws,
+                             size_t ws_bytes, void* stream) {
+  if (cur_in == nullptr || decision_dev == nullptr || stats_dev == nullptr || xq8 == nullptr)
+    return HDQ_ERR_INVALID;
+  if (xq8->codes == nullptr || xq8->row_scale == nullptr) return HDQ_ERR_INVALID;
+  if (had_block == 0) return HDQ_ERR_SHAPE;
+  int st = check_quant_shape(rows, cols, had_block, HDQ_FMT_INT8_ROW);
+  if (st != HDQ_OK) return st;
+  if (cols % 8 != 0) return HDQ_ERR_SHAPE;
+  if (ws == nullptr || ws_bytes < hdq_workspace_bytes(HDQ_OP_SELECT_Q8, rows, cols, 0, 0))
+    return HDQ_ERR_WORKSPACE;
+  xq8->fmt = HDQ_FMT_INT8_ROW;
+  xq8->had_block = had_block;
+  xq8->rows = rows;
+  xq8->cols = cols;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint16_t* xb = static_cast<const uint16_t*>(cur_in);
+  double* part = static_cast<double*>(ws);
+  if (cols <= 16384) {
+    // per-row partials, struct-of-arrays: sums, magnitude bits, rotated maxima
+    uint32_t* pbits = reinterpret_cast<uint32_t*>(part + rows);
+    float* ptmax = reinterpret_cast<float*>(pbits + rows);
+    hipError_t e = launch_quant_int8_stats(xb, rows, cols, had_block, xq8->codes, xq8->row_scale, part,
+                                           pbits, ptmax, s);
+    if (e != hipSuccess) return HDQ_ERR_HIP;
+    return hip_status(launch_stats_finalize_rows(part, pbits, ptmax, rows, rows * cols, had_block,
+                                                 delta_thresh, ratio_thresh, decision_dev, stats_dev,
+                                                 delta_sums_dev, s));
+  }
+  // rows too long to keep in registers: the two passes separately
+  hipError_t e = launch_stats(nullptr, nullptr, 0, xb, rows * cols, had_block, delta_thresh, ratio_thresh,
+                              decision_dev, stats_dev, nullptr, part, nullptr, 0, s, delta_sums_dev,
+                              nullptr);
+  if (e != hipSuccess) return HDQ_ERR_HIP;
+  return hip_status(launch_quant_int_rows(xb, rows, cols, had_block, HDQ_FMT_INT8_ROW, xq8->codes,
+                                          xq8->row_scale, nullptr, 0, s));
 }
 
 int hdq_quantize(const void* x, int64_t rows, int64_t cols, int32_t had_block, int32_t fmt,

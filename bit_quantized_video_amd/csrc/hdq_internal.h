@@ -51,6 +51,18 @@ hipError_t launch_stats(const uint16_t* prev_in, const uint16_t* prev_out, int64
                         double* partials, const int32_t* gate, int32_t want, hipStream_t s,
                         const double* delta_sums_in = nullptr, double* delta_sums_out = nullptr);
 
+// The finalize over one partial per row, struct-of-arrays: psum = sum |x|,
+// pbits = max bf16 magnitude bits, ptmax = max |rotated x| (scaled).
+hipError_t launch_stats_finalize_rows(const double* psum, const uint32_t* pbits, const float* ptmax,
+                                      int64_t rows, int64_t cur_numel, int hb, float delta_thresh,
+                                      float ratio_thresh, int32_t* decision, float* stats,
+                                      const double* delta_sums_in, hipStream_t s);
+// INT8 per-row quantization that also writes those per-row partials;
+// cols <= 16384.
+hipError_t launch_quant_int8_stats(const uint16_t* x, int64_t rows, int64_t cols, int hb, void* codes,
+                                   float* row_scale, double* psum, uint32_t* pbits, float* ptmax,
+                                   hipStream_t s);
+
 // ---- GEMMs ----
 // INT8 activations [M, K] x INT4 weights packed [N, K/2]: y = (acc*sx)*sw.
 hipError_t launch_gemm_i8i4(const int8_t* x, const float* sx, const uint8_t* w4, const float* sw,

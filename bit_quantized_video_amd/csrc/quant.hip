@@ -35,10 +35,17 @@ __device__ __forceinline__ uint32_t low_bytes4(uint32_t a, uint32_t b, uint32_t 
   return ab | cd;
 }
 
-template <int BLOCK, int CPT, bool INT4>
+// STATS (INT8 only): also the selection statistics of the current input,
+// one partial per row, struct-of-arrays (psum[row] = sum |x|, pbits[row] =
+// max bf16 magnitude bits, ptmax[row] = the row's max |rotated x|, which is
+// the row absmax the quantizer needs anyway), so selection and quantization
+// read x once.
+template <int BLOCK, int CPT, bool INT4, bool STATS = false>
 __global__ __launch_bounds__(BLOCK) void k_quant_int_rows(
     const uint16_t* __restrict__ x, int64_t cols, int hb, float c_b, void* __restrict__ codes,
-    float* __restrict__ row_scale, const int32_t* __restrict__ decision, int32_t want) {
+    float* __restrict__ row_scale, const int32_t* __restrict__ decision, int32_t want,
+    double* __restrict__ psum = nullptr, uint32_t* __restrict__ pbits = nullptr,
+    float* __restrict__ ptmax = nullptr) {
   if (decision != nullptr && *decision != want) return;
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
@@ -50,12 +57,27 @@ __global__ __launch_bounds__(BLOCK) void k_quant_int_rows(
   // Hadamard blocks sit in aligned lane groups (BLOCK is a multiple of 16
   // lanes), and a block past the row end is entirely zero-filled.
   float v[CPT][8];
+  uint32_t maxbits = 0u;
+  double sumabs = 0.0;
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     const int64_t idx = fwht_src((int64_t)c * BLOCK + tid, lane, hb);
     uint4 w = make_uint4(0u, 0u, 0u, 0u);
     if (idx < nch) w = xr[idx];
     bf16x8_to_f32(w, v[c]);
+  }
+  if constexpr (STATS) {
+    // bf16 widens to float exactly: a float's top 16 bits are its bf16 pattern
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      float s8 = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        maxbits = max(maxbits, (__float_as_uint(v[c][i]) >> 16) & 0x7fffu);
+        s8 += fabsf(v[c][i]);
+      }
+      sumabs += s8;
+    }
   }
   float amax = 0.0f;
 #pragma unroll
@@ -75,6 +97,31 @@ __global__ __launch_bounds__(BLOCK) void k_quant_int_rows(
     amax = red[0];
 #pragma unroll
     for (int w = 1; w < BLOCK / 64; ++w) amax = fmaxf(amax, red[w]);
+  }
+  if constexpr (STATS) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      sumabs += __shfl_xor(sumabs, o);
+      maxbits = max(maxbits, (uint32_t)__shfl_xor((int)maxbits, o));
+    }
+    __shared__ double rs[BLOCK / 64];
+    __shared__ uint32_t rb[BLOCK / 64];
+    if (lane == 0) {
+      rs[tid >> 6] = sumabs;
+      rb[tid >> 6] = maxbits;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      double sa = rs[0];
+      uint32_t mb = rb[0];
+      for (int w = 1; w < BLOCK / 64; ++w) {
+        sa += rs[w];
+        mb = max(mb, rb[w]);
+      }
+      psum[row] = sa;
+      pbits[row] = mb;
+      ptmax[row] = amax;
+    }
   }
   constexpr float QMAX = INT4 ? 7.0f : 127.0f;
   float inv = 0.0f, s = 0.0f;
@@ -123,6 +170,46 @@ static hipError_t launch_int_rows_t(const uint16_t* x, int64_t rows, int64_t col
     hipLaunchKernelGGL((k_quant_int_rows<BLOCK, CPT, false>), dim3((unsigned)rows), dim3(BLOCK), 0,
                        s, x, cols, hb, c_b, codes, sc, dec, want);
   return hipGetLastError();
+}
+
+template <int BLOCK, int CPT>
+static hipError_t launch_select_q8_t(const uint16_t* x, int64_t rows, int64_t cols, int hb,
+                                     void* codes, float* sc, double* psum, uint32_t* pbits,
+                                     float* ptmax, hipStream_t s) {
+  hipLaunchKernelGGL((k_quant_int_rows<BLOCK, CPT, false, true>), dim3((unsigned)rows), dim3(BLOCK), 0,
+                     s, x, cols, hb, hadamard_scale(hb), codes, sc, nullptr, 0, psum, pbits, ptmax);
+  return hipGetLastError();
+}
+
+// Threads per row for CPT chunks each: the smallest instantiated multiple
+// of 64 that covers the row.
+template <int CPT>
+static hipError_t launch_select_q8_cpt(const uint16_t* x, int64_t rows, int64_t cols, int hb,
+                                       void* codes, float* sc, double* psum, uint32_t* pbits,
+                                       float* ptmax, hipStream_t s) {
+  const int64_t nch = cols >> 3;
+#define HDQ_SQ8_CASE(B) \
+  if (nch <= (B) * CPT) return launch_select_q8_t<B, CPT>(x, rows, cols, hb, codes, sc, psum, pbits, ptmax, s);
+  HDQ_SQ8_CASE(64)
+  HDQ_SQ8_CASE(128)
+  HDQ_SQ8_CASE(192)
+  HDQ_SQ8_CASE(256)
+  HDQ_SQ8_CASE(384)
+  HDQ_SQ8_CASE(512)
+  HDQ_SQ8_CASE(768)
+  HDQ_SQ8_CASE(1024)
+#undef HDQ_SQ8_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_quant_int8_stats(const uint16_t* x, int64_t rows, int64_t cols, int hb, void* codes,
+                                   float* row_scale, double* psum, uint32_t* pbits, float* ptmax,
+                                   hipStream_t s) {
+  // The rows kept in registers, up to 16384 columns (beyond, callers take
+  // the two-pass route), two chunks per thread: the statistics need
+  // registers of their own, and more chunks per thread measured slower.
+  if ((cols >> 3) > 2048) return hipErrorInvalidValue;
+  return launch_select_q8_cpt<2>(x, rows, cols, hb, codes, row_scale, psum, pbits, ptmax, s);
 }
 
 // Two-pass variant for rows too long to keep in registers: pass one finds

@@ -164,6 +164,49 @@ __global__ __launch_bounds__(256) void k_stats_partial(
   }
 }
 
+// The statistics and the decision from the reduced sums (one thread).
+__device__ void finish_stats(double diff, double base, double sumabs, uint32_t maxbits, float tmax,
+                             int64_t n_cur, int has_history, float c_b, float delta_thresh,
+                             float ratio_thresh, int32_t* decision, float* stats, float* amax_out) {
+  const bool nonfinite = maxbits >= 0x7f80u;
+  const double maxabs = (double)bf16_lo(maxbits);
+  double delta;
+  if (!has_history)
+    delta = __builtin_nan("");
+  else if (base == 0.0)
+    delta = (diff == 0.0) ? 0.0 : __builtin_inf();
+  else
+    delta = diff / base;
+  const double mean = sumabs / (double)n_cur;
+  double ratio;
+  if (nonfinite)
+    ratio = __builtin_nan("");
+  else
+    ratio = (sumabs == 0.0) ? 0.0 : maxabs / mean;
+  // max over fl32(|t| * c_b) equals fl32(max |t| * c_b): rounding is monotone.
+  const float rot_amax = nonfinite ? 0.0f : tmax * c_b;
+  if (stats != nullptr) {
+    stats[0] = (float)delta;
+    stats[1] = (float)ratio;
+    stats[2] = (float)maxabs;
+    stats[3] = (float)mean;
+    stats[4] = rot_amax;
+  }
+  if (amax_out != nullptr) *amax_out = rot_amax;
+  if (decision != nullptr) {
+    int32_t d;
+    if (!(ratio <= (double)ratio_thresh))
+      d = kPrecBf16;  // purified delta refresh: outliers -> full precision
+    else if (!has_history)
+      d = kPrecInt8;  // no previous-step difference -> INT8
+    else if (!(delta < (double)delta_thresh))
+      d = kPrecInt8;  // large previous-step difference -> INT8
+    else
+      d = kPrecNvfp4;
+    *decision = d;
+  }
+}
+
 // Finalize.  With sums_out, only the two difference sums are written
 // (sums_out[0] = sum|prev_out - prev_in|, sums_out[1] = sum|prev_in|).  With
 // sums_in, those two sums come from an earlier difference-only pass instead
@@ -207,45 +250,60 @@ __global__ __launch_bounds__(256) void k_stats_final(
   }
   const double diff = sums_in != nullptr ? sums_in[0] : red[0][0];
   const double base = sums_in != nullptr ? sums_in[1] : red[0][1];
-  const double sumabs = red[0][2];
-  const uint32_t maxbits = (uint32_t)red[0][3];
-  const bool nonfinite = maxbits >= 0x7f80u;
-  const double maxabs = (double)bf16_lo(maxbits);
-  double delta;
-  if (!has_history)
-    delta = __builtin_nan("");
-  else if (base == 0.0)
-    delta = (diff == 0.0) ? 0.0 : __builtin_inf();
-  else
-    delta = diff / base;
-  const double mean = sumabs / (double)n_cur;
-  double ratio;
-  if (nonfinite)
-    ratio = __builtin_nan("");
-  else
-    ratio = (sumabs == 0.0) ? 0.0 : maxabs / mean;
-  // max over fl32(|t| * c_b) equals fl32(max |t| * c_b): rounding is monotone.
-  const float rot_amax = nonfinite ? 0.0f : (float)red[0][4] * c_b;
-  if (stats != nullptr) {
-    stats[0] = (float)delta;
-    stats[1] = (float)ratio;
-    stats[2] = (float)maxabs;
-    stats[3] = (float)mean;
-    stats[4] = rot_amax;
+  finish_stats(diff, base, red[0][2], (uint32_t)red[0][3], (float)red[0][4], n_cur, has_history, c_b,
+               delta_thresh, ratio_thresh, decision, stats, amax_out);
+}
+
+// Finalize over one partial per row, struct-of-arrays (sum |x| doubles, max
+// bf16 magnitude bits, max |rotated x| times c_b -- c_b is then 1), as the
+// selection fused with INT8 quantization writes them: 1024 threads,
+// coalesced, fixed order.
+__global__ __launch_bounds__(1024) void k_stats_final_rows(
+    const double* __restrict__ psum, const uint32_t* __restrict__ pbits,
+    const float* __restrict__ ptmax, int nrows, int64_t n_cur, float c_b, float delta_thresh,
+    float ratio_thresh, int32_t* __restrict__ decision, float* __restrict__ stats,
+    const double* __restrict__ sums_in) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  // four independent accumulators (fixed order) keep several loads in flight
+  double s4[4] = {0.0, 0.0, 0.0, 0.0};
+  uint32_t mb = 0u;
+  float tm = 0.0f;
+  int r = tid;
+  for (; r + 3 * 1024 < nrows; r += 4 * 1024) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      s4[u] += psum[r + u * 1024];
+      mb = max(mb, pbits[r + u * 1024]);
+      tm = fmaxf(tm, ptmax[r + u * 1024]);
+    }
   }
-  if (amax_out != nullptr) *amax_out = rot_amax;
-  if (decision != nullptr) {
-    int32_t d;
-    if (!(ratio <= (double)ratio_thresh))
-      d = kPrecBf16;  // purified delta refresh: outliers -> full precision
-    else if (!has_history)
-      d = kPrecInt8;  // no previous-step difference -> INT8
-    else if (!(delta < (double)delta_thresh))
-      d = kPrecInt8;  // large previous-step difference -> INT8
-    else
-      d = kPrecNvfp4;
-    *decision = d;
+  for (int u = 0; r < nrows; r += 1024, ++u) {
+    s4[u] += psum[r];
+    mb = max(mb, pbits[r]);
+    tm = fmaxf(tm, ptmax[r]);
   }
+  double sa = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+  sa = wave_sum_d(sa);
+  mb = wave_max_u(mb);
+  tm = wave_max(tm);
+  __shared__ double rs[16];
+  __shared__ uint32_t rb[16];
+  __shared__ float rt[16];
+  if (lane == 0) {
+    rs[tid >> 6] = sa;
+    rb[tid >> 6] = mb;
+    rt[tid >> 6] = tm;
+  }
+  __syncthreads();
+  if (tid != 0) return;
+  for (int w = 1; w < 16; ++w) {
+    rs[0] += rs[w];
+    rb[0] = max(rb[0], rb[w]);
+    rt[0] = fmaxf(rt[0], rt[w]);
+  }
+  const bool hist = sums_in != nullptr;
+  finish_stats(hist ? sums_in[0] : 0.0, hist ? sums_in[1] : 0.0, rs[0], rb[0], rt[0], n_cur,
+               hist ? 1 : 0, c_b, delta_thresh, ratio_thresh, decision, stats, nullptr);
 }
 
 hipError_t launch_stats(const uint16_t* prev_in, const uint16_t* prev_out, int64_t prev_numel,
@@ -269,6 +327,18 @@ hipError_t launch_stats(const uint16_t* prev_in, const uint16_t* prev_out, int64
   hipLaunchKernelGGL(k_stats_final, dim3(1), dim3(256), 0, s, partials, (int)blocks, cur_numel,
                      (hist || delta_sums_in != nullptr) ? 1 : 0, c_b, delta_thresh, ratio_thresh,
                      decision, stats, amax_out, gate, want, delta_sums_in, delta_sums_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_stats_finalize_rows(const double* psum, const uint32_t* pbits, const float* ptmax,
+                                      int64_t rows, int64_t cur_numel, int hb, float delta_thresh,
+                                      float ratio_thresh, int32_t* decision, float* stats,
+                                      const double* delta_sums_in, hipStream_t s) {
+  // ptmax holds rows' max |rotated x| already scaled by fl32(1/sqrt(hb)):
+  // fl32(max |t| * c_b) = max fl32(|t| * c_b), so the finalize scales by 1
+  (void)hb;
+  hipLaunchKernelGGL(k_stats_final_rows, dim3(1), dim3(1024), 0, s, psum, pbits, ptmax, (int)rows,
+                     cur_numel, 1.0f, delta_thresh, ratio_thresh, decision, stats, delta_sums_in);
   return hipGetLastError();
 }
 

@@ -24,9 +24,10 @@ PREC_NVFP4, PREC_INT8, PREC_BF16 = 0, 1, 2
 # output dtypes
 DTYPE_F32, DTYPE_BF16, DTYPE_I32 = 0, 1, 2
 # workspace ops
-OP_SELECT, OP_QUANTIZE, OP_LINEAR = 0, 1, 2
+OP_SELECT, OP_QUANTIZE, OP_LINEAR, OP_SELECT_Q8 = 0, 1, 2, 3
 
-EXPORTS = ("hdq_select_precision", "hdq_delta_sums", "hdq_select_precision_sums", "hdq_quantize",
+EXPORTS = ("hdq_select_precision", "hdq_delta_sums", "hdq_select_precision_sums",
+           "hdq_select_quantize_int8", "hdq_quantize",
            "hdq_linear", "hdq_workspace_bytes",
            "hdq_status_string", "hdq_version")
 
@@ -59,6 +60,10 @@ def _load():
     L.hdq_select_precision_sums.restype = _c.c_int
     L.hdq_select_precision_sums.argtypes = [_p, _p, _c.c_int64, _c.c_int64, _c.c_int32, _c.c_float,
                                             _c.c_float, _p, _p, _p, _c.c_size_t, _p]
+    L.hdq_select_quantize_int8.restype = _c.c_int
+    L.hdq_select_quantize_int8.argtypes = [_p, _p, _c.c_int64, _c.c_int64, _c.c_int32, _c.c_float,
+                                           _c.c_float, _p, _p, _c.POINTER(QTensorDesc), _p, _c.c_size_t,
+                                           _p]
     L.hdq_quantize.restype = _c.c_int
     L.hdq_quantize.argtypes = [_p, _c.c_int64, _c.c_int64, _c.c_int32, _c.c_int32, _p, _p,
                                _c.POINTER(QTensorDesc), _p, _c.c_size_t, _p]
@@ -194,6 +199,27 @@ def select_precision_sums(delta_sums, cur_in, had_block=0, delta_thresh=0.1, rat
                                        _ptr(ws), ws.numel(), _stream(stream))
     _check("hdq_select_precision_sums", st)
     return decision, stats
+
+
+def select_quantize_int8(delta_sums, cur_in, had_block, delta_thresh=0.1, ratio_thresh=50.0,
+                         decision=None, stats=None, out=None, ws=None, stream=None):
+    """hdq_select_quantize_int8: the selection (difference sums from
+    delta_sums(), None = no history) fused with the INT8 per-token
+    quantization of cur_in.  Returns (decision, stats, QuantizedTensor)."""
+    cur_in = _bf16(cur_in, "cur_in")
+    rows, cols = cur_in.shape
+    dev = cur_in.device
+    decision = torch.empty(1, dtype=torch.int32, device=dev) if decision is None else decision
+    stats = torch.empty(5, dtype=torch.float32, device=dev) if stats is None else stats
+    out = QuantizedTensor(FMT_INT8_ROW, rows, cols, had_block, dev) if out is None else out
+    ws = _workspace(ws, workspace_bytes(OP_SELECT_Q8, rows, cols, 0), dev)
+    d = out.desc()
+    st = lib.hdq_select_quantize_int8(_ptr(delta_sums), _ptr(cur_in), rows, cols, had_block,
+                                      delta_thresh, ratio_thresh, _ptr(decision), _ptr(stats),
+                                      _c.byref(d), _ptr(ws), ws.numel(), _stream(stream))
+    _check("hdq_select_quantize_int8", st)
+    out.fmt, out.had_block, out.rows, out.cols = d.fmt, d.had_block, d.rows, d.cols
+    return decision, stats, out
 
 
 def quantize(x, had_block, fmt, tensor_amax=None, out=None, ws=None, stream=None, decision=None):

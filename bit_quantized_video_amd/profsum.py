@@ -44,7 +44,8 @@ KINDS = OrderedDict([
     ("delta_sums", r"k_stats_partial<1>"),
     ("select_stats", r"k_stats_partial(<[02]>)?"),
     ("select_final", r"k_stats_final"),
-    ("quant_int8", r"k_quant_int_rows(_long)?<\d+, \d+, false>"),
+    ("select_quant_int8", r"k_quant_int_rows<\d+, \d+, false, true>"),
+    ("quant_int8", r"k_quant_int_rows(_long)?<\d+, \d+, false(, false)?>"),
     ("quant_nvfp4_mx", r"k_quant_nvfp4<true>"),
     ("quant_nvfp4", r"k_quant_nvfp4<false>"),
     ("gemm_int8", r"k_gemm_i8i4(_pipe)?<[\d, ]*1>"),
@@ -56,11 +57,12 @@ KINDS = OrderedDict([
 SOURCES = {
     "delta_sums": ["stats.hip"], "select_stats": ["stats.hip"], "select_final": ["stats.hip"],
     "quant_int8": ["quant.hip"], "quant_nvfp4_mx": ["quant.hip"], "quant_nvfp4": ["quant.hip"],
+    "select_quant_int8": ["quant.hip", "stats.hip"],
     "gemm_int8": ["gemm_i8.hip"], "gemm_nvfp4_mx": ["gemm_fp4.hip"],
     "gemm_nvfp4": ["gemm_bf16.hip"], "gemm_bf16": ["gemm_bf16.hip"],
 }
 COMMON_SOURCES = ["hdq_device.h", "hdq_internal.h", "../build.py"]
-WEIGHT_PREP = r"k_quant_int_rows(_long)?<\d+, \d+, true>"
+WEIGHT_PREP = r"k_quant_int_rows(_long)?<\d+, \d+, true(, false)?>"
 # A launch that did work: longer than this (trace) / moved more than this (PMC).
 MIN_WORK_NS = 20_000
 MIN_WORK_KIB = 1024.0

@@ -96,6 +96,7 @@ extern "C" {
 #define HDQ_OP_SELECT 0
 #define HDQ_OP_QUANTIZE 1
 #define HDQ_OP_LINEAR 2
+#define HDQ_OP_SELECT_Q8 3
 
 /* A quantized tensor.  The caller allocates every buffer (device memory)
  * and fills the pointers; hdq_quantize fills fmt, had_block, rows, cols. */
@@ -181,6 +182,29 @@ int hdq_select_precision_sums(const double *delta_sums_dev, const void *cur_in, 
                               void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * hdq_select_quantize_int8 -- hdq_select_precision_sums fused with the INT8
+ * per-token quantization of the same input (steps 1 and 2 for the INT8
+ * path): x is read once, the INT8 codes are written whatever the decision
+ * turns out to be (a caller then runs the INT8 GEMM gated on the decision).
+ *   delta_sums_dev, cur_in, rows, cols, thresholds, decision_dev, stats_dev:
+ *                 as for hdq_select_precision_sums; had_block must be > 0.
+ *   xq8         : caller-allocated INT8_ROW buffers (codes int8 [rows, cols],
+ *                 row_scale fp32 [rows]); fmt, had_block, rows, cols are
+ *                 written.
+ *   ws, ws_bytes: >= hdq_workspace_bytes(HDQ_OP_SELECT_Q8, rows, cols, 0, 0)
+ *                 bytes (one partial per row).
+ * The codes equal hdq_quantize's INT8_ROW codes bit for bit; the decision,
+ * delta, max|x| and rotated amax equal hdq_select_precision_sums'; mean |x|
+ * and the ratio agree up to the order of the double sum of |x| (per row
+ * here, per chunk range there).  Rows over 16384 columns run the two passes
+ * one after the other.
+ */
+int hdq_select_quantize_int8(const double *delta_sums_dev, const void *cur_in, int64_t rows,
+                             int64_t cols, int32_t had_block, float delta_thresh, float ratio_thresh,
+                             int32_t *decision_dev, float *stats_dev, hdq_qtensor *xq8, void *ws,
+                             size_t ws_bytes, void *stream);
+
+/*
  * hdq_quantize -- step 2: block-Hadamard rotation fused with quantization
  * (summary sections one and four).  Also prepares weights offline.
  *
@@ -244,7 +268,8 @@ int hdq_linear(int32_t precision, const int32_t *decision_dev, const void *x,
                void *stream);
 
 /* Scratch bytes an entry point needs.  op = HDQ_OP_SELECT: (M = rows,
- * K = cols, N = prev_numel); HDQ_OP_QUANTIZE: (M = rows, K = cols, fmt);
+ * K = cols, N = prev_numel); HDQ_OP_SELECT_Q8: (M = rows, K = cols);
+ * HDQ_OP_QUANTIZE: (M = rows, K = cols, fmt);
  * HDQ_OP_LINEAR: (M, K, N, fmt = the weights' FP4 format, or -1 when only
  * INT8/BF16 will run).  Returns 0 on bad arguments. */
 size_t hdq_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N, int32_t fmt);

@@ -15,7 +15,7 @@ HEADER = os.path.join(ROOT, "include", "hdq.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(hdq_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(hdq_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -26,7 +26,8 @@ def hdq():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for fn in ("hdq_select_precision", "hdq_delta_sums", "hdq_select_precision_sums", "hdq_quantize",
+    for fn in ("hdq_select_precision", "hdq_delta_sums", "hdq_select_precision_sums",
+               "hdq_select_quantize_int8", "hdq_quantize",
                "hdq_linear", "hdq_workspace_bytes",
                "hdq_status_string", "hdq_version"):
         assert fn in names
@@ -80,6 +81,19 @@ def test_validation_happens_before_any_launch(hdq):
     assert L.hdq_select_precision_sums(None, fake, 4, 60, 16, 0.1, 50.0, fake, fake, fake, 1 << 20, None) == hdq.ERR_SHAPE
     assert L.hdq_select_precision_sums(None, fake, 0, 64, 0, 0.1, 50.0, fake, fake, fake, 1 << 20, None) == hdq.ERR_SHAPE
     assert L.hdq_select_precision_sums(fake, fake, 4, 64, 0, 0.1, 50.0, fake, fake, None, 0, None) == hdq.ERR_WORKSPACE
+    # selection fused with INT8 quantization: no rotation, bad shapes, missing buffers or workspace
+    q8 = hdq.QTensorDesc(0, 0, 0, 0, fake, fake, None, None)
+    sq = lambda hb=16, cols=64, rows=4, q=q8, ws=fake, wsb=1 << 20: L.hdq_select_quantize_int8(
+        None, fake, rows, cols, hb, 0.1, 50.0, fake, fake, ctypes.byref(q) if q is not None else None, ws,
+        wsb, None)
+    assert sq(q=None) == hdq.ERR_INVALID
+    assert sq(q=hdq.QTensorDesc(0, 0, 0, 0, None, fake, None, None)) == hdq.ERR_INVALID
+    assert sq(hb=0) == hdq.ERR_SHAPE
+    assert sq(hb=12) == hdq.ERR_SHAPE
+    assert sq(rows=0) == hdq.ERR_SHAPE
+    assert sq(ws=None, wsb=0) == hdq.ERR_WORKSPACE
+    assert sq(rows=100000, wsb=1 << 20) == hdq.ERR_WORKSPACE      # one partial per row does not fit
+    assert L.hdq_workspace_bytes(hdq.OP_SELECT_Q8, 17776, 3072, 0, 0) >= 17776 * 48
     # quantize: bad fmt, bad shapes, missing buffers, missing workspace for the amax pre-pass
     q = hdq.QTensorDesc(0, 0, 0, 0, fake, fake, fake, fake)
     assert L.hdq_quantize(fake, 4, 64, 16, 9, None, None, ctypes.byref(q), None, 0, None) == hdq.ERR_INVALID

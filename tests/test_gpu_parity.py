@@ -223,6 +223,38 @@ def test_two_part_selection_matches_one_pass(M, K, hb, s):
     assert abs(got[0] / got[1] - ref[0]) <= 2e-6 * ref[0]
 
 
+@pytest.mark.parametrize("M,K,hb,s,hist", [(333, 3072, 128, 0.2, True), (64, 1024, 64, 0.05, True),
+                                            (9, 12288, 128, 0.1, True), (5, 20480, 128, 0.03, True),
+                                            (17776, 3072, 128, 0.08, True), (100, 512, 32, 0.0, False)])
+def test_select_fused_with_int8_quantization(M, K, hb, s, hist):
+    """hdq_select_quantize_int8 = hdq_select_precision_sums + INT8 hdq_quantize:
+    codes and row scales bit for bit, the decision and delta, max and rotated
+    amax exactly, mean |x| and the ratio up to the double sum order."""
+    say(f"select+int8 M={M} K={K} hb={hb}")
+    rng = synth.rng_for(113, M + K)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x16 = synth.to_bf16_bits(x)
+    po16 = synth.to_bf16_bits(x + rng.standard_normal((M, K)).astype(np.float32) * np.float32(s))
+    xd, pid, pod = to_dev(x16), to_dev(x16.copy()), to_dev(po16)
+    sums = hdq.delta_sums(pid, pod) if hist else None
+    d1, s1 = hdq.select_precision_sums(sums, xd, hb)
+    q1 = hdq.quantize(xd, hb, hdq.FMT_INT8_ROW)
+    d2, s2, q2 = hdq.select_quantize_int8(sums, xd, hb)
+    torch.cuda.synchronize()
+    assert int(d1.item()) == int(d2.item())
+    assert torch.equal(q1.codes, q2.codes) and torch.equal(q1.row_scale, q2.row_scale)
+    a, b = s1.cpu().numpy().astype(np.float64), s2.cpu().numpy().astype(np.float64)
+    for i in (0, 2, 4):
+        assert (math.isnan(a[i]) and math.isnan(b[i])) or a[i] == b[i], i
+    for i in (1, 3):
+        assert abs(a[i] - b[i]) <= 1e-6 * abs(a[i]), i
+    # and the oracle: codes and the statistics
+    ref = O.stats(x16 if hist else None, po16 if hist else None, x16, hb)
+    qa, sa = O.quant_int(x16[:64], hb, 127)
+    assert_codes_equal(q2.codes.cpu().numpy()[:64], qa, "codes")
+    assert abs(b[1] - ref[1]) <= 2e-6 * ref[1] and b[4] == np.float32(ref[4])
+
+
 def test_stats_hand_cases():
     ones = np.ones((4, 64), np.float32)
     b = synth.to_bf16_bits

@@ -12,6 +12,9 @@ def test_classify_kernel_names():
         "hdq::k_stats_final(double const*)": "select_final",
         "void hdq::k_quant_int_rows<128, 3, false>(int)": "quant_int8",
         "void hdq::k_quant_int_rows<256, 6, true>(int)": None,  # INT4 weight preparation
+        "void hdq::k_quant_int_rows<256, 6, true, false>(int)": None,
+        "void hdq::k_quant_int_rows<128, 3, false, false>(int)": "quant_int8",
+        "void hdq::k_quant_int_rows<128, 3, false, true>(int)": "select_quant_int8",
         "void hdq::k_quant_nvfp4<true>(int)": "quant_nvfp4_mx",
         "void hdq::k_quant_nvfp4<false>(int)": "quant_nvfp4",
         "void hdq::k_gemm_i8i4_pipe<2, 4, 4, 2, 1>(int)": "gemm_int8",
@@ -27,7 +30,7 @@ def test_classify_kernel_names():
 
 def test_schedule_window_starts_after_weight_prep():
     rows = [(0, "void hdq::k_quant_int_rows<128, 3, true>"), (1, "hdq::k_stats_partial"),
-            (2, "void hdq::k_quant_int_rows<128, 3, true>"), (3, "hdq::k_stats_partial"),
+            (2, "void hdq::k_quant_int_rows<128, 3, true, false>"), (3, "hdq::k_stats_partial"),
             (4, "void hdq::k_gemm_i8i4_pipe<2, 4, 4, 2, 1>"), (5, "void hdq::k_gemm_i8i4_pipe<2, 4, 4, 2, 0>")]
     assert [r[0] for r in P.schedule_window(rows)] == [3, 4]
 
