@@ -32,9 +32,15 @@
 #include "hdq_internal.h"
 
 #include <atomic>
+#include <cstdlib>
 
 namespace hdq {
 
+// Persistent GEMMs leave two CUs per XCD free (HDQ_GEMM_FREE_CUS overrides
+// the total, a multiple of 8): their workgroups each fill a CU's register
+// file, so without free CUs no kernel on another stream (such as the
+// previous-step difference pass) could run beside them.  On MI355X the
+// GEMMs are power-bound, and 240 workgroups run them as fast as 256.
 int64_t persistent_grid(int64_t tiles) {
   static std::atomic<int> cus[64];  // per device; 0 = not read yet
   int dev = 0;
@@ -44,7 +50,10 @@ int64_t persistent_grid(int64_t tiles) {
     int cu = 0;
     if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu < 8)
       cu = 256;
-    n = cu & ~7;
+    int free_cus = cu >= 128 ? 16 : 0;
+    if (const char* e = std::getenv("HDQ_GEMM_FREE_CUS")) free_cus = std::atoi(e) & ~7;
+    n = (cu & ~7) - free_cus;
+    if (n < 8) n = cu & ~7;
     cus[dev].store(n, std::memory_order_relaxed);
   }
   return tiles <= n ? tiles : n;

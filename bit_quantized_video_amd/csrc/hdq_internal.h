@@ -20,8 +20,10 @@ enum OutDtype : int { kOutF32 = 0, kOutBf16 = 1, kOutI32 = 2 };
 float hadamard_scale(int hb);
 
 // Grid of a persistent GEMM whose workgroups fill a CU each: `tiles` when
-// that is at most the current device's CU count, else the CU count rounded
-// down to a multiple of 8 (the workgroups then loop over tiles).
+// that is at most the workgroups it may use, else that number -- the
+// current device's CU count rounded down to a multiple of 8, less 16 CUs
+// left free for other streams (HDQ_GEMM_FREE_CUS) -- and the workgroups
+// loop over tiles.
 int64_t persistent_grid(int64_t tiles);
 
 // ---- quantize (quant.hip) ----

@@ -43,6 +43,7 @@ CSRC = os.path.join(HERE, "csrc")
 KINDS = OrderedDict([
     ("delta_sums", r"k_stats_partial<1>"),
     ("select_stats", r"k_stats_partial(<[02]>)?"),
+    ("select_final_rows", r"k_stats_final_rows"),
     ("select_final", r"k_stats_final"),
     ("select_quant_int8", r"k_quant_int_rows<\d+, \d+, false, true>"),
     ("quant_int8", r"k_quant_int_rows(_long)?<\d+, \d+, false(, false)?>"),
@@ -56,6 +57,7 @@ KINDS = OrderedDict([
 # Sources each kind is built from (any change voids a stored traffic figure).
 SOURCES = {
     "delta_sums": ["stats.hip"], "select_stats": ["stats.hip"], "select_final": ["stats.hip"],
+    "select_final_rows": ["stats.hip"],
     "quant_int8": ["quant.hip"], "quant_nvfp4_mx": ["quant.hip"], "quant_nvfp4": ["quant.hip"],
     "select_quant_int8": ["quant.hip", "stats.hip"],
     "gemm_int8": ["gemm_i8.hip"], "gemm_nvfp4_mx": ["gemm_fp4.hip"],
@@ -63,9 +65,16 @@ SOURCES = {
 }
 COMMON_SOURCES = ["hdq_device.h", "hdq_internal.h", "../build.py"]
 WEIGHT_PREP = r"k_quant_int_rows(_long)?<\d+, \d+, true(, false)?>"
-# A launch that did work: longer than this (trace) / moved more than this (PMC).
-MIN_WORK_NS = 20_000
+# A launch that did work: longer than this (trace; gated-off launches take a
+# few microseconds, more when a concurrent stream shares the GPU, and the
+# smallest GEMM that does work takes over 100) / moved more than this (PMC).
+MIN_WORK_NS = {"gemm": 60_000, "quant": 12_000}
+MIN_WORK_NS_DEFAULT = 12_000
 MIN_WORK_KIB = 1024.0
+
+
+def min_work_ns(kind):
+    return MIN_WORK_NS.get(kind.split("_")[0], MIN_WORK_NS_DEFAULT)
 
 
 def code_only(text):
@@ -127,16 +136,17 @@ def trace_summary(db, bench_json=None, command=None):
     win = schedule_window(rows)
     out.append("")
     out.append(f"schedule window: {len(win)} dispatches (after the last weight preparation)")
-    out.append(f"launches that did work (> {MIN_WORK_NS / 1e3:.0f} us) vs gated off, per step of the path:")
+    out.append("launches that did work (GEMMs > 60 us, others > 12 us; finalize and difference passes")
+    out.append("always) vs gated off, per step of the path:")
     out.append(f"  {'kind':<16} {'work':>6} {'avg us':>10} {'total ms':>10} {'off':>6} {'off avg us':>11}")
     per = OrderedDict((k, ([], [])) for k in KINDS)
     for _, name, dur, _ in win:
         k = classify(name)
         if k is None:
             continue
-        # the one-workgroup finalize is always short and never gated off
-        # unless its statistics pass was
-        per[k][0 if dur > MIN_WORK_NS or k == "select_final" else 1].append(dur)
+        # the finalize and the difference pass are never gated off
+        ungated = k.startswith("select_final") or k == "delta_sums"
+        per[k][0 if ungated or dur > min_work_ns(k) else 1].append(dur)
     summary = {}
     for k, (w, off) in per.items():
         if not w and not off:
