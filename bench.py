@@ -464,7 +464,7 @@ def bench_schedule(args, hdq, synth):
         "decisions": counts,
         "kernels": {k: {"launches": v["launches"], "total_ms": v["total_ms"], "avg_us": v["avg_us"],
                         "rate": round(v["rate"] / 1e12, 3),
-                        "rate_unit": ("TB/s" if k.startswith(("quant", "select")) else
+                        "rate_unit": ("TB/s" if k.startswith(("quant", "select", "delta")) else
                                       "TOP/s" if k.startswith("gemm_int8") else "TFLOP/s")}
                     for k, v in ks.items()},
         "other_recipe": {"recipe": other,
