@@ -65,10 +65,15 @@ def parse():
     ap.add_argument("--fuse", choices=["on", "off"], default="on",
                     help="selection fused with the INT8 per-token quantization of the input (on, "
                          "default; the codes are written whatever the decision) or separate")
+    ap.add_argument("--dispatch", choices=["on", "off"], default="on",
+                    help="one GEMM launch per layer call for the decided precision (on, default) "
+                         "or one gated launch per precision")
     ap.add_argument("--delta-ahead", type=int, default=2,
                     help="with --delta overlap: the difference of call k + D runs beside the GEMMs "
                          "of call k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decisions-out", help="write the per-call precision decisions (call order) as JSON, "
+                                            "for attributing one-launch GEMMs in profiles")
     ap.add_argument("--profile-copy", action="store_true")
     return ap.parse_args()
 
@@ -276,12 +281,19 @@ def run_schedule_step(S, args, hdq, recipe, events=None, side_events=None):
             gate.record(main)
             enqueue_delta(k + ahead, gate)
         W = L["W"][recipe]
-        hdq.linear(hdq.PREC_INT8, None, W, decision=d, xq=sh["xq8"], y=sh["y"])
-        if ev: ev[4].record()
-        hdq.linear(hdq.PREC_NVFP4, None, W, decision=d, xq=sh["xq4"][recipe], y=sh["y"])
-        if ev: ev[5].record()
-        hdq.linear(hdq.PREC_BF16, L["x"], W, decision=d, y=sh["y"])
-        if ev: ev[6].record()
+        if args.dispatch == "on":
+            hdq.linear_dispatch(d, L["x"], sh["xq8"], sh["xq4"][recipe], W, y=sh["y"])
+            if ev:
+                ev[4].record()
+                ev[5].record()
+                ev[6].record()
+        else:
+            hdq.linear(hdq.PREC_INT8, None, W, decision=d, xq=sh["xq8"], y=sh["y"])
+            if ev: ev[4].record()
+            hdq.linear(hdq.PREC_NVFP4, None, W, decision=d, xq=sh["xq4"][recipe], y=sh["y"])
+            if ev: ev[5].record()
+            hdq.linear(hdq.PREC_BF16, L["x"], W, decision=d, y=sh["y"])
+            if ev: ev[6].record()
     return len(calls)
 
 
@@ -293,6 +305,7 @@ def schedule_kernel_times(S, args, events_per_step, synth, recipe, side_per_step
     kt = KernelTimes()
     inline = args.delta == "inline"
     fused = args.fuse == "on"
+    dispatch = args.dispatch == "on"
     for s_i, evs in enumerate(events_per_step):
         side = side_per_step[s_i] if side_per_step is not None else None
         k = 0
@@ -321,6 +334,11 @@ def schedule_kernel_times(S, args, events_per_step, synth, recipe, side_per_step
                     for kind, prec, dd, i in (("gemm_int8", "int8", 1, 3), ("gemm_nvfp4", "nvfp4", 0, 4),
                                               ("gemm_bf16", "bf16", 2, 5)):
                         on = d == dd
+                        if dispatch:
+                            # one launch (slot 3) ran the decided precision's GEMM
+                            if on:
+                                kt.add(kind, dt[3], flops, gemm_bytes(M, N, K, prec, recipe))
+                            continue
                         kt.add(kind if on else kind + "_gated_off", dt[i], flops if on else 0,
                                gemm_bytes(M, N, K, prec, recipe) if on else 0)
     return kt, decisions
@@ -423,6 +441,9 @@ def bench_schedule(args, hdq, synth):
     other = "nvfp4" if args.fp4 == "mx" else "mx"
     runs = {r: time_schedule(S, args, hdq, synth, r) for r in (args.fp4, other)}
     ms_per_step, kt, decisions = runs[args.fp4]
+    if args.decisions_out:
+        with open(args.decisions_out, "w") as fh:
+            json.dump({"decisions": [int(v) for v in decisions.reshape(-1)]}, fh)
     ks = kt.summary()
     counts = {p: int((decisions == v).sum()) for p, v in (("nvfp4", 0), ("int8", 1), ("bf16", 2))}
     # dominant kernel: the critical-path kernel with the most time (the

@@ -203,6 +203,51 @@ int hdq_select_quantize_int8(const double* delta_sums_dev, const void* cur_in, i
                                           xq8->row_scale, nullptr, 0, s));
 }
 
+int hdq_linear_dispatch(const int32_t* decision_dev, const void* x, const hdq_qtensor* xq8,
+                        const hdq_qtensor* xq4, int64_t M, int64_t K, const hdq_weights* w, void* y,
+                        int32_t y_dtype, void* stream) {
+  if (decision_dev == nullptr || x == nullptr || xq8 == nullptr || xq4 == nullptr || w == nullptr ||
+      y == nullptr)
+    return HDQ_ERR_INVALID;
+  if (y_dtype != HDQ_DTYPE_F32 && y_dtype != HDQ_DTYPE_BF16) return HDQ_ERR_UNSUPPORTED;
+  if (M <= 0 || K <= 0 || w->N <= 0 || M > 0x7fffffff || K > 0x7fffffff || w->N > 0x7fffffff)
+    return HDQ_ERR_SHAPE;
+  if (w->K != K) return HDQ_ERR_SHAPE;
+  const int64_t N = w->N;
+  const int32_t f = w->w_fp4.fmt;
+  int st;
+  if ((st = check_qtensor(w->w_int4, HDQ_FMT_INT4_ROW, N, K)) != HDQ_OK) return st;
+  if ((st = check_qtensor(*xq8, HDQ_FMT_INT8_ROW, M, K)) != HDQ_OK) return st;
+  if (!is_fp4(f)) return HDQ_ERR_UNSUPPORTED;
+  if ((st = check_qtensor(w->w_fp4, f, N, K)) != HDQ_OK) return st;
+  if ((st = check_qtensor(*xq4, f, M, K)) != HDQ_OK) return st;
+  if (w->w_bf16 == nullptr) return HDQ_ERR_INVALID;
+  if (K % 32 != 0 || xq8->had_block != w->w_int4.had_block || xq4->had_block != w->w_fp4.had_block)
+    return HDQ_ERR_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const uint16_t* wb = static_cast<const uint16_t*>(w->w_bf16);
+  hipError_t e = launch_gemm_dispatch(
+      decision_dev, static_cast<const int8_t*>(xq8->codes), xq8->row_scale,
+      static_cast<const uint8_t*>(w->w_int4.codes), w->w_int4.row_scale,
+      static_cast<const uint8_t*>(xq4->codes), xq4->blk_scale, xq4->tensor_scale,
+      static_cast<const uint8_t*>(w->w_fp4.codes), w->w_fp4.blk_scale, w->w_fp4.tensor_scale,
+      f == HDQ_FMT_NVFP4_MX, xb, wb, y, y_dtype, M, N, K, s);
+  if (e == hipSuccess) return HDQ_OK;
+  if (e != hipErrorNotSupported) return HDQ_ERR_HIP;
+  // shapes the pipelined bodies do not take: the three gated GEMMs
+  if (launch_gemm_i8i4(static_cast<const int8_t*>(xq8->codes), xq8->row_scale,
+                       static_cast<const uint8_t*>(w->w_int4.codes), w->w_int4.row_scale, y, y_dtype,
+                       M, N, K, decision_dev, HDQ_PREC_INT8, s) != hipSuccess)
+    return HDQ_ERR_HIP;
+  auto fp4 = f == HDQ_FMT_NVFP4_MX ? launch_gemm_nvfp4_mx : launch_gemm_nvfp4_bf16;
+  if (fp4(static_cast<const uint8_t*>(xq4->codes), xq4->blk_scale, xq4->tensor_scale,
+          static_cast<const uint8_t*>(w->w_fp4.codes), w->w_fp4.blk_scale, w->w_fp4.tensor_scale, y,
+          y_dtype, M, N, K, decision_dev, HDQ_PREC_NVFP4, s) != hipSuccess)
+    return HDQ_ERR_HIP;
+  return hip_status(launch_gemm_bf16(xb, wb, y, y_dtype, M, N, K, decision_dev, HDQ_PREC_BF16, s));
+}
+
 int hdq_quantize(const void* x, int64_t rows, int64_t cols, int32_t had_block, int32_t fmt,
                  const float* tensor_amax, const int32_t* decision_dev, hdq_qtensor* out,
                  void* ws, size_t ws_bytes, void* stream) {

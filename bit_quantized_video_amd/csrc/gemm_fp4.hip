@@ -16,17 +16,13 @@
 // below) for K % 256 == 0, and a simple double-buffered one for any
 // K % 32 == 0.  In both the per-row E8M0 bytes of a stage sit in LDS next to
 // the codes.
+#include "gemm_fp4_pipe.h"
 #include "hdq_device.h"
 #include "hdq_internal.h"
 
 #include <type_traits>
 
 namespace hdq {
-
-// Power-of-two E4M3 byte (0x01, 0x02, 0x04 subnormal; 8..0x7e normal) -> E8M0.
-__device__ __forceinline__ uint32_t e4m3_pow2_to_e8m0(uint32_t b) {
-  return b >= 8u ? (b >> 3) + 120u : 118u + (31u - (uint32_t)__builtin_clz(b | 1u));
-}
 
 template <int ROWS>
 struct Fp4Stager {
@@ -179,248 +175,14 @@ __global__ __launch_bounds__(256) void k_gemm_fp4mx(
   }
 }
 
-// ---------------------------------------------------------------------------
-// Pipelined kernel for K % 256 == 0: the INT8 kernel's structure (256 x 256
-// tiles, 8 waves as 2 x 4 of 128 x 64, a persistent tile loop, buffer loads
-// prefetching across tile boundaries, double-buffered LDS, LDS-only
-// barriers) with 256 K per stage and one register set: stage g + 1 is
-// loaded while stage g is computed (a second set would not fit beside the
-// unrolled substeps' fragments in 256 VGPRs).  Per stage:
-// 128-byte code rows (swz128; substep s of 64 K gives lane half h chunk
-// 2s + h) and, per row, the stage's eight E8M0 bytes (one per 32 K, from the
-// even E4M3 byte of each MX pair) stored as two words, [g0 g2 g4 g6] and
-// [g1 g3 g5 g7]: lane half h reads word h once per stage and substep s takes
-// its byte through the instruction's scale byte select.
-struct Fp4PipeStage {
-  uint4 x[4], w[4];  // codes: 4 x 16-byte chunks per operand per thread
-  uint4 sc;          // the 16 E4M3 bytes of one X or W row (8 MX pairs)
-};
-
-template <int KS>
-__device__ __forceinline__ v16f mfma_fp4(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, KS, sa, KS, sb);
-}
-
+// The gated kernel around the pipelined body (gemm_fp4_pipe.h).
 template <int OUT>
 __global__ __launch_bounds__(512) void k_gemm_fp4mx_pipe(
     const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xsc, const float* __restrict__ xts,
     const uint8_t* __restrict__ wc, const uint8_t* __restrict__ wsc, const float* __restrict__ wts,
     void* __restrict__ Y, int M, int N, int K, const int32_t* __restrict__ decision, int32_t want) {
   if (decision != nullptr && *decision != want) return;
-  constexpr int BM = 256, BN = 256, BK = 256, WM_T = 4, WN_T = 2;
-  constexpr int XB = BM * BK / 2, WB = BN * BK / 2;  // code bytes per stage
-  constexpr int SB = XB + WB + (BM + BN) * 8;         // + E8M0 bytes
-  constexpr int kOutPitch = BN * 2 + 16;              // bf16 output row staged in LDS
-  static_assert(BM * kOutPitch <= 2 * SB, "output tile must fit the pipeline buffers");
-  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave % 2, wn = wave / 2;
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const TileSeq seq = tile_seq(tiles_m * tiles_n);
-  const int nk = K / BK;
-  const int G = seq.count * nk;
-  if (G == 0) return;
-  const int ld = K / 2, lds_ = K / 16;
-
-  const int cr = tid >> 3, cc = tid & 7;  // code chunks: 8 threads per row, 64 rows per round
-  const uint32_t cvoff = (uint32_t)(cr * ld + 16 * cc);
-  const int cdst = cr * 128 + 16 * (cc ^ swz128(cr));
-  // scales: waves 0-3 take the 256 X rows, waves 4-7 the 256 W rows
-  const int sw_ = __builtin_amdgcn_readfirstlane(tid >> 8), srow = tid & 255;
-  const uint32_t svoff = (uint32_t)(srow * lds_);
-  const int sdst = XB + WB + sw_ * BM * 8 + srow * 8;
-
-  int l_logical = seq.first, l_kt = 0;
-  __amdgpu_buffer_rsrc_t xres, wres, sres;
-  auto open_tile = [&]() {
-    int tm, tn;
-    grouped_tile(l_logical, tiles_m, tiles_n, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    xres = make_rsrc(xc + (int64_t)m0 * ld, (uint32_t)((int64_t)(M - m0) * ld));
-    wres = make_rsrc(wc + (int64_t)n0 * ld, (uint32_t)((int64_t)(N - n0) * ld));
-    sres = sw_ ? make_rsrc(wsc + (int64_t)n0 * lds_, (uint32_t)((int64_t)(N - n0) * lds_))
-               : make_rsrc(xsc + (int64_t)m0 * lds_, (uint32_t)((int64_t)(M - m0) * lds_));
-  };
-  open_tile();
-  auto load = [&](Fp4PipeStage& st) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      st.x[p] = buf_load16(xres, cvoff, l_kt * (BK / 2) + p * 64 * ld);
-      st.w[p] = buf_load16(wres, cvoff, l_kt * (BK / 2) + p * 64 * ld);
-    }
-    st.sc = buf_load16(sres, svoff, l_kt * (BK / 16));
-    if (++l_kt == nk) {
-      l_kt = 0;
-      l_logical += seq.stride;
-      if (l_logical < tiles_m * tiles_n) open_tile();
-    }
-  };
-  auto store = [&](const Fp4PipeStage& st, int buf) {
-    uint8_t* base = smem + buf * SB;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      *reinterpret_cast<uint4*>(base + cdst + p * 64 * 128) = st.x[p];
-      *reinterpret_cast<uint4*>(base + XB + cdst + p * 64 * 128) = st.w[p];
-    }
-    // E8M0 of group g comes from E4M3 byte 2g; word h holds g = h, h+2, h+4, h+6
-    const uint32_t d[4] = {st.sc.x, st.sc.y, st.sc.z, st.sc.w};
-    uint32_t w0 = 0u, w1 = 0u;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      w0 |= e4m3_pow2_to_e8m0(d[q] & 0xffu) << (8 * q);
-      w1 |= e4m3_pow2_to_e8m0((d[q] >> 16) & 0xffu) << (8 * q);
-    }
-    *reinterpret_cast<uint2*>(base + sdst) = make_uint2(w0, w1);
-  };
-
-  v16f acc[WN_T][WM_T];
-  auto zero_acc = [&]() {
-#pragma unroll
-    for (int j = 0; j < WN_T; ++j)
-#pragma unroll
-      for (int i = 0; i < WM_T; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.0f;
-  };
-  zero_acc();
-
-  const int h = lane >> 5, r32 = lane & 31;
-  auto compute = [&](int buf) {
-    const uint8_t* lx = smem + buf * SB;
-    const uint8_t* lw = lx + XB;
-    const uint8_t* lxs = lx + XB + WB;
-    const uint8_t* lws = lxs + BM * 8;
-    int xe[WM_T], we[WN_T];
-#pragma unroll
-    for (int i = 0; i < WM_T; ++i)
-      xe[i] = *reinterpret_cast<const int*>(lxs + (wm * WM_T * 32 + i * 32 + r32) * 8 + 4 * h);
-#pragma unroll
-    for (int j = 0; j < WN_T; ++j)
-      we[j] = *reinterpret_cast<const int*>(lws + (wn * WN_T * 32 + j * 32 + r32) * 8 + 4 * h);
-    auto substep = [&](auto ksc) {
-      constexpr int ks = decltype(ksc)::value;
-      const int g = 2 * ks + h;  // this lane's 32-K group within the stage
-      v8i xf[WM_T], wf[WN_T];
-#pragma unroll
-      for (int i = 0; i < WM_T; ++i) {
-        const int r = wm * WM_T * 32 + i * 32 + r32;
-        const v4i v = *reinterpret_cast<const v4i*>(lx + r * 128 + 16 * (g ^ swz128(r)));
-        xf[i] = v8i{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int j = 0; j < WN_T; ++j) {
-        const int r = wn * WN_T * 32 + j * 32 + r32;
-        const v4i v = *reinterpret_cast<const v4i*>(lw + r * 128 + 16 * (g ^ swz128(r)));
-        wf[j] = v8i{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int j = 0; j < WN_T; ++j)
-#pragma unroll
-        for (int i = 0; i < WM_T; ++i) acc[j][i] = mfma_fp4<ks>(wf[j], xf[i], acc[j][i], we[j], xe[i]);
-    };
-    substep(std::integral_constant<int, 0>{});
-    substep(std::integral_constant<int, 1>{});
-    substep(std::integral_constant<int, 2>{});
-    substep(std::integral_constant<int, 3>{});
-  };
-
-  const float scale = (*xts) * (*wts);
-  auto epilogue = [&](int logical) {
-    int tm, tn;
-    grouped_tile(logical, tiles_m, tiles_n, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    if constexpr (OUT == kOutBf16) {
-      // Stage the bf16 tile in LDS (both pipeline buffers are free once every
-      // wave is past this stage; the next stage is still in registers), then
-      // write whole 512-byte rows with 16-byte stores.
-      lds_barrier();
-      uint8_t* const lrow = smem + (wm * WM_T * 32 + r32) * kOutPitch + 2 * (wn * WN_T * 32 + 4 * h);
-#pragma unroll
-      for (int i = 0; i < WM_T; ++i)
-#pragma unroll
-        for (int j = 0; j < WN_T; ++j)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const v16f& a = acc[j][i];
-            *reinterpret_cast<uint2*>(lrow + i * 32 * kOutPitch + 2 * (j * 32 + 8 * g)) =
-                make_uint2(pack_bf16x2(a[4 * g] * scale, a[4 * g + 1] * scale),
-                           pack_bf16x2(a[4 * g + 2] * scale, a[4 * g + 3] * scale));
-          }
-      lds_barrier();
-      uint16_t* y16 = reinterpret_cast<uint16_t*>(Y);
-      const int n = n0 + 8 * (tid & 31);
-      const bool vec = n + 8 <= N && (N & 7) == 0;
-#pragma unroll 4
-      for (int r = tid >> 5; r < BM; r += 16) {
-        const uint8_t* src = smem + r * kOutPitch + 16 * (tid & 31);
-        if (m0 + r < M) {
-          uint16_t* dst = y16 + (int64_t)(m0 + r) * N + n;
-          if (vec) {
-            *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
-          } else {
-            for (int e = 0; e < 8 && n + e < N; ++e) dst[e] = reinterpret_cast<const uint16_t*>(src)[e];
-          }
-        }
-      }
-      lds_barrier();  // the next stage may overwrite the staged tile
-    } else {
-      const bool full_n = n0 + BN <= N && (N & 3) == 0;
-#pragma unroll
-      for (int i = 0; i < WM_T; ++i) {
-        const int m = m0 + wm * WM_T * 32 + i * 32 + r32;
-        if (m >= M) continue;
-#pragma unroll
-        for (int j = 0; j < WN_T; ++j) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int n = n0 + wn * WN_T * 32 + j * 32 + 8 * g + 4 * h;
-            const int64_t off = (int64_t)m * N + n;
-            float y[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) y[r] = acc[j][i][4 * g + r] * scale;
-            if (full_n) {
-              *reinterpret_cast<float4*>(reinterpret_cast<float*>(Y) + off) = make_float4(y[0], y[1], y[2], y[3]);
-            } else {
-              for (int r = 0; r < 4 && n + r < N; ++r) reinterpret_cast<float*>(Y)[off + r] = y[r];
-            }
-          }
-        }
-      }
-    }
-  };
-
-  int ckt = 0, clogical = seq.first;
-  auto finish_stage = [&]() {
-    if (++ckt == nk) {
-      epilogue(clogical);
-      zero_acc();
-      ckt = 0;
-      clogical += seq.stride;
-    }
-  };
-
-  Fp4PipeStage ra;
-  load(ra);
-  store(ra, 0);
-  lds_barrier();
-  int g = 0;
-  for (; g + 1 < G; g += 2) {
-    load(ra);
-    compute(0);
-    finish_stage();
-    store(ra, 1);
-    lds_barrier();
-    if (g + 2 < G) load(ra);
-    compute(1);
-    finish_stage();
-    if (g + 2 < G) store(ra, 0);
-    lds_barrier();
-  }
-  if (g < G) {
-    compute(0);
-    finish_stage();
-  }
+  gemm_fp4mx_pipe_body<OUT>(xc, xsc, xts, wc, wsc, wts, Y, M, N, K);
 }
 
 template <int OUT>

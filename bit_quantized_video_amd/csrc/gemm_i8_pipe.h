@@ -1,0 +1,290 @@
+// gemm_i8_pipe.h -- the pipelined INT8 x INT4 GEMM body (gfx950), shared by
+// the gated INT8 kernel and the single-launch precision dispatch kernel.
+// See gemm_i8.hip for the design.
+#ifndef HDQ_GEMM_I8_PIPE_H
+#define HDQ_GEMM_I8_PIPE_H
+
+#include "hdq_device.h"
+#include "hdq_internal.h"
+
+namespace hdq {
+
+// 32 packed INT4 (uint4) -> 32 int8 holding 16 * q, in k order.
+__device__ __forceinline__ void unpack_int4x32(const uint4 p, uint4& lo, uint4& hi) {
+  const uint32_t d[4] = {p.x, p.y, p.z, p.w};
+  uint32_t o[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t even = (d[i] << 4) & 0xf0f0f0f0u;  // k = 8i, 8i+2, 8i+4, 8i+6
+    const uint32_t odd = d[i] & 0xf0f0f0f0u;          // k = 8i+1, ...
+    o[2 * i] = __builtin_amdgcn_perm(odd, even, 0x05010400u);
+    o[2 * i + 1] = __builtin_amdgcn_perm(odd, even, 0x07030602u);
+  }
+  lo = make_uint4(o[0], o[1], o[2], o[3]);
+  hi = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
+// ---------------------------------------------------------------------------
+// Pipelined kernel for K % 128 == 0 (every CogVideoX shape).
+//  * Workgroup tile BM tokens x BN features; WAVES_M x WAVES_N waves, each
+//    wave WM_T x WN_T subtiles of 32 x 32.  With 8 waves (two per SIMD) one
+//    wave's LDS / global / barrier waits overlap the other wave's MFMAs.
+//  * K advances 128 per stage.  Two register sets hold the global loads of
+//    the next two stages (the loop is unrolled by two so the sets alternate
+//    without copies); LDS is double-buffered.  Loads for stage kt + 2 are
+//    issued before stage kt is computed and written to LDS after stage
+//    kt + 1 is, so two stages of compute cover their latency.  Barriers
+//    order LDS only (lds_barrier), leaving the prefetches in flight.
+//  * Operands arrive through buffer loads (rows past M or N read as zero;
+//    their outputs are not stored).  X rows are 128 bytes in LDS (swz128),
+//    packed INT4 W rows 64 bytes (swz64).  Within a stage, k-substep pair p
+//    (64 K) gives lane half h the K range [64p + 32h, +32): for W one
+//    16-byte read of packed nibbles unpacked to the two substeps' fragments,
+//    for X two 16-byte reads.  (Any assignment of K to lanes works as long as
+//    both operands use the same one.)
+
+template <int WAVES_M, int WAVES_N, int WM_T, int WN_T>
+struct I8Cfg {
+  static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
+  static constexpr int BM = WAVES_M * WM_T * 32, BN = WAVES_N * WN_T * 32, BK = 128;
+  static constexpr int XB = BM * BK, SB = XB + BN * BK / 2;  // LDS bytes per stage
+  static constexpr int OUT_PITCH = BN * 2 + 16;              // bf16 output row in LDS, padded
+  static constexpr int LDS = (2 * SB > BM * OUT_PITCH) ? 2 * SB : BM * OUT_PITCH;
+  static constexpr int XC = XB / 16 / THREADS;                // 16-byte loads per thread
+  static constexpr int WC = BN * BK / 2 / 16 / THREADS;
+  static constexpr int XROWS = THREADS / 8, WROWS = THREADS / 4;  // rows per load round
+  static_assert(XC >= 1 && WC >= 1, "tile too small for the workgroup");
+};
+
+template <int XC, int WC>
+struct I8Stage {
+  uint4 x[XC], w[WC];
+};
+
+template <int WAVES_M, int WAVES_N, int WM_T, int WN_T, int OUT>
+__device__ __forceinline__ void gemm_i8i4_pipe_body(
+    const int8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ W4,
+    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K) {
+  using C = I8Cfg<WAVES_M, WAVES_N, WM_T, WN_T>;
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, XB = C::XB, SB = C::SB;
+  constexpr int kOutPitch = C::OUT_PITCH;
+  using Stage = I8Stage<C::XC, C::WC>;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WAVES_M, wn = wave / WAVES_M;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const TileSeq seq = tile_seq(tiles_m * tiles_n);
+  const int nk = K / BK;
+  const int ldw = K >> 1;
+
+  // Operands arrive through buffer resources over the current tile's rows;
+  // 8 threads per 128-byte X row and 4 per W row (coalesced).  Load round p
+  // is XROWS (WROWS) rows further on, a multiple of 16, which leaves the
+  // swizzle unchanged: LDS destinations are a base plus an immediate.
+  const int xr0 = tid >> 3, xc0 = tid & 7, wr0 = tid >> 2, wc0 = tid & 3;
+  const uint32_t xvoff = (uint32_t)(xr0 * K + 16 * xc0);
+  const uint32_t wvoff = (uint32_t)(wr0 * ldw + 16 * wc0);
+  const int xdst = xr0 * 128 + 16 * (xc0 ^ swz128(xr0));
+  const int wdst = XB + wr0 * 64 + 16 * (wc0 ^ swz64(wr0));
+
+  // Buffer resources over the current tile's rows.
+  __amdgpu_buffer_rsrc_t xres, wres;
+  auto load = [&](Stage& st, int kt) {
+#pragma unroll
+    for (int p = 0; p < C::XC; ++p) st.x[p] = buf_load16(xres, xvoff, kt * BK + p * C::XROWS * K);
+#pragma unroll
+    for (int p = 0; p < C::WC; ++p) st.w[p] = buf_load16(wres, wvoff, kt * (BK / 2) + p * C::WROWS * ldw);
+  };
+  auto store = [&](const Stage& st, int buf) {
+    uint8_t* base = smem + buf * SB;
+#pragma unroll
+    for (int p = 0; p < C::XC; ++p) *reinterpret_cast<uint4*>(base + xdst + C::XROWS * 128 * p) = st.x[p];
+#pragma unroll
+    for (int p = 0; p < C::WC; ++p) *reinterpret_cast<uint4*>(base + wdst + C::WROWS * 64 * p) = st.w[p];
+  };
+
+  v16i acc[WN_T][WM_T];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int j = 0; j < WN_T; ++j)
+#pragma unroll
+      for (int i = 0; i < WM_T; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[j][i][e] = 0;
+  };
+  zero_acc();
+
+  const int h = lane >> 5, r32 = lane & 31;
+  auto compute = [&](int buf) {
+    const uint8_t* lx = smem + buf * SB;
+    const uint8_t* lw = lx + XB;
+#pragma unroll
+    for (int p = 0; p < BK / 64; ++p) {
+      v4i xf[WM_T][2];
+#pragma unroll
+      for (int i = 0; i < WM_T; ++i) {
+        const int r = wm * WM_T * 32 + i * 32 + r32;
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          xf[i][s] = *reinterpret_cast<const v4i*>(lx + r * 128 + 16 * ((4 * p + 2 * h + s) ^ swz128(r)));
+      }
+#pragma unroll
+      for (int j = 0; j < WN_T; ++j) {
+        const int r = wn * WN_T * 32 + j * 32 + r32;
+        const uint4 packed = *reinterpret_cast<const uint4*>(lw + r * 64 + 16 * ((2 * p + h) ^ swz64(r)));
+        uint4 lo, hi;
+        unpack_int4x32(packed, lo, hi);
+        const v4i w0 = v4i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w};
+        const v4i w1 = v4i{(int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+#pragma unroll
+        for (int i = 0; i < WM_T; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(w0, xf[i][0], acc[j][i], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < WM_T; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(w1, xf[i][1], acc[j][i], 0, 0, 0);
+      }
+    }
+  };
+
+  // Epilogue of one tile: lane holds token m = ... + (lane & 31) and, for
+  // g = 0..3, features n = 8g + 4h + 0..3 of each 32 x 32 subtile.
+  auto epilogue = [&](int logical) {
+    int tm, tn;
+    grouped_tile(logical, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    if constexpr (OUT == kOutBf16) {
+      // Stage the bf16 tile in LDS (both pipeline buffers are free at a tile
+      // boundary once every wave is past the last stage), then write whole
+      // rows: 32 lanes x 16 bytes per 512-byte row.
+      lds_barrier();
+      // Scales through buffer loads: rows past M and columns past N read 0.
+      const __amdgpu_buffer_rsrc_t sxres = make_rsrc(sx, (uint32_t)M * 4u);
+      const __amdgpu_buffer_rsrc_t swres = make_rsrc(sw, (uint32_t)N * 4u);
+      const int rl0 = wm * WM_T * 32 + r32, nl0 = wn * WN_T * 32 + 4 * h;
+      uint8_t* const lrow = smem + rl0 * kOutPitch + 2 * nl0;
+#pragma unroll
+      for (int i = 0; i < WM_T; ++i) {
+        const float sxm = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(sxres, 4 * (rl0 + i * 32), 4 * m0, 0));
+#pragma unroll
+        for (int j = 0; j < WN_T; ++j) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float4 swn = __builtin_bit_cast(
+                float4, __builtin_amdgcn_raw_buffer_load_b128(swres, 4 * (nl0 + j * 32 + 8 * g), 4 * n0, 0));
+            const float y0 = ((float)(acc[j][i][4 * g + 0] >> 4) * sxm) * swn.x;
+            const float y1 = ((float)(acc[j][i][4 * g + 1] >> 4) * sxm) * swn.y;
+            const float y2 = ((float)(acc[j][i][4 * g + 2] >> 4) * sxm) * swn.z;
+            const float y3 = ((float)(acc[j][i][4 * g + 3] >> 4) * sxm) * swn.w;
+            *reinterpret_cast<uint2*>(lrow + i * 32 * kOutPitch + 2 * (j * 32 + 8 * g)) =
+                make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
+          }
+        }
+      }
+      lds_barrier();
+      uint16_t* y16 = reinterpret_cast<uint16_t*>(Y);
+      const int n = n0 + 8 * (tid & 31);
+      const bool vec = n + 8 <= N && (N & 7) == 0;
+#pragma unroll 4
+      for (int r = tid >> 5; r < BM; r += C::THREADS / 32) {
+        const uint8_t* src = smem + r * kOutPitch + 16 * (tid & 31);
+        if (m0 + r < M) {
+          uint16_t* dst = y16 + (int64_t)(m0 + r) * N + n;
+          if (vec) {
+            *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+          } else {
+            for (int e = 0; e < 8 && n + e < N; ++e) dst[e] = reinterpret_cast<const uint16_t*>(src)[e];
+          }
+        }
+      }
+      lds_barrier();  // the next stage may overwrite the staged tile
+      return;
+    }
+    const bool full_n = n0 + BN <= N && (N & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < WM_T; ++i) {
+      const int m = m0 + wm * WM_T * 32 + i * 32 + r32;
+      if (m >= M) continue;
+      const float sxm = sx[m];
+#pragma unroll
+      for (int j = 0; j < WN_T; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * WN_T * 32 + j * 32 + 8 * g + 4 * h;
+          const int64_t off = (int64_t)m * N + n;
+          int32_t a[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) a[r] = acc[j][i][4 * g + r] >> 4;
+          if (full_n) {
+            if constexpr (OUT == kOutI32) {
+              *reinterpret_cast<int4*>(reinterpret_cast<int32_t*>(Y) + off) = make_int4(a[0], a[1], a[2], a[3]);
+            } else {
+              const float4 swn = *reinterpret_cast<const float4*>(sw + n);
+              const float y0 = ((float)a[0] * sxm) * swn.x, y1 = ((float)a[1] * sxm) * swn.y;
+              const float y2 = ((float)a[2] * sxm) * swn.z, y3 = ((float)a[3] * sxm) * swn.w;
+              if constexpr (OUT == kOutF32)
+                *reinterpret_cast<float4*>(reinterpret_cast<float*>(Y) + off) = make_float4(y0, y1, y2, y3);
+              else
+                *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(Y) + off) =
+                    make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
+            }
+          } else {
+            for (int r = 0; r < 4; ++r) {
+              if (n + r >= N) break;
+              if constexpr (OUT == kOutI32) {
+                reinterpret_cast<int32_t*>(Y)[off + r] = a[r];
+              } else {
+                const float y = ((float)a[r] * sxm) * sw[n + r];
+                if constexpr (OUT == kOutF32)
+                  reinterpret_cast<float*>(Y)[off + r] = y;
+                else
+                  reinterpret_cast<uint16_t*>(Y)[off + r] = __builtin_bit_cast(uint16_t, (__bf16)y);
+              }
+            }
+          }
+        }
+      }
+    }
+  };
+
+  // Persistent loop over this workgroup's tiles; per tile, the K-stages run
+  // through the two-stage register prefetch and the double-buffered LDS.
+  for (int t = 0; t < seq.count; ++t) {
+    const int logical = seq.first + t * seq.stride;
+    {
+      int tm, tn;
+      grouped_tile(logical, tiles_m, tiles_n, tm, tn);
+      const int m0 = tm * BM, n0 = tn * BN;
+      xres = make_rsrc(X + (int64_t)m0 * K, (uint32_t)((int64_t)(M - m0) * K));
+      wres = make_rsrc(W4 + (int64_t)n0 * ldw, (uint32_t)((int64_t)(N - n0) * ldw));
+    }
+    Stage ra, rb;
+    load(ra, 0);
+    if (nk > 1) load(rb, 1);
+    store(ra, 0);
+    lds_barrier();
+    // Pairs of stages; one loop exit keeps the accumulators in one register
+    // allocation.  An odd last stage (left in LDS buffer 0) follows the loop.
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      // stage kt in LDS buffer 0, stage kt + 1 in rb
+      if (kt + 2 < nk) load(ra, kt + 2);
+      compute(0);
+      store(rb, 1);
+      lds_barrier();
+      // stage kt + 1 in LDS buffer 1, stage kt + 2 in ra
+      if (kt + 3 < nk) load(rb, kt + 3);
+      compute(1);
+      if (kt + 2 < nk) store(ra, 0);
+      lds_barrier();
+    }
+    if (kt < nk) compute(0);
+    epilogue(logical);
+    zero_acc();
+  }
+}
+
+}  // namespace hdq
+
+#endif  // HDQ_GEMM_I8_PIPE_H

@@ -80,6 +80,16 @@ hipError_t launch_gemm_nvfp4_mx(const uint8_t* xc, const uint8_t* xs, const floa
                                 const uint8_t* wc, const uint8_t* ws, const float* wts,
                                 void* y, int out_dtype, int64_t M, int64_t N, int64_t K,
                                 const int32_t* decision, int32_t want, hipStream_t s);
+// One launch running the GEMM the device decision names (INT8, NVFP4 -- on
+// the FP4 MFMA when fp4_mx, else decoded to bf16 -- or bf16); every path's
+// operands must be given.  hipErrorNotSupported when a shape does not fit
+// the pipelined bodies (callers then launch the three gated GEMMs).
+hipError_t launch_gemm_dispatch(const int32_t* decision, const int8_t* x8, const float* sx,
+                                const uint8_t* w4, const float* sw, const uint8_t* xc,
+                                const uint8_t* xsc, const float* xts, const uint8_t* wc,
+                                const uint8_t* wsc, const float* wts, bool fp4_mx,
+                                const uint16_t* xb, const uint16_t* wb, void* y, int out_dtype,
+                                int64_t M, int64_t N, int64_t K, hipStream_t s);
 // bf16 x bf16 (full-precision fallback).
 hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* w, void* y, int out_dtype,
                             int64_t M, int64_t N, int64_t K, const int32_t* decision,

@@ -27,7 +27,7 @@ DTYPE_F32, DTYPE_BF16, DTYPE_I32 = 0, 1, 2
 OP_SELECT, OP_QUANTIZE, OP_LINEAR, OP_SELECT_Q8 = 0, 1, 2, 3
 
 EXPORTS = ("hdq_select_precision", "hdq_delta_sums", "hdq_select_precision_sums",
-           "hdq_select_quantize_int8", "hdq_quantize",
+           "hdq_select_quantize_int8", "hdq_linear_dispatch", "hdq_quantize",
            "hdq_linear", "hdq_workspace_bytes",
            "hdq_status_string", "hdq_version")
 
@@ -64,6 +64,9 @@ def _load():
     L.hdq_select_quantize_int8.argtypes = [_p, _p, _c.c_int64, _c.c_int64, _c.c_int32, _c.c_float,
                                            _c.c_float, _p, _p, _c.POINTER(QTensorDesc), _p, _c.c_size_t,
                                            _p]
+    L.hdq_linear_dispatch.restype = _c.c_int
+    L.hdq_linear_dispatch.argtypes = [_p, _p, _c.POINTER(QTensorDesc), _c.POINTER(QTensorDesc),
+                                      _c.c_int64, _c.c_int64, _c.POINTER(WeightsDesc), _p, _c.c_int32, _p]
     L.hdq_quantize.restype = _c.c_int
     L.hdq_quantize.argtypes = [_p, _c.c_int64, _c.c_int64, _c.c_int32, _c.c_int32, _p, _p,
                                _c.POINTER(QTensorDesc), _p, _c.c_size_t, _p]
@@ -107,6 +110,21 @@ def _bf16(t, name):
     if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous bfloat16 CUDA tensor")
     return t
+
+
+def linear_dispatch(decision, x, xq8, xq4, w, y=None, y_dtype=DTYPE_BF16, stream=None):
+    """hdq_linear_dispatch: the GEMM of the device decision's precision in
+    one launch (INT8 from xq8, NVFP4 from xq4, bf16 from x)."""
+    x = _bf16(x, "x")
+    M, K = x.shape
+    if y is None:
+        dt = {DTYPE_F32: torch.float32, DTYPE_BF16: torch.bfloat16}[y_dtype]
+        y = torch.empty(M, w.N, dtype=dt, device=x.device)
+    wd, d8, d4 = w.desc(), xq8.desc(), xq4.desc()
+    st = lib.hdq_linear_dispatch(_ptr(decision), _ptr(x), _c.byref(d8), _c.byref(d4), M, K,
+                                 _c.byref(wd), _ptr(y), y_dtype, _stream(stream))
+    _check("hdq_linear_dispatch", st)
+    return y
 
 
 def workspace_bytes(op, M, K, N=0, fmt=-1):

@@ -20,11 +20,13 @@ The summary ends with machine-readable ``traffic`` lines (kind, bytes per
 launch, hash of the sources the kernel is built from) that the benchmark reads
 to fill its roofline record; it reports null once those sources changed.
 
-Usage (paths are the rocprofv3 output databases):
-  python3 -m bit_quantized_video_amd.profsum trace DB [--bench-json F] [--command C]
+Usage (paths are the rocprofv3 output databases; --decisions F is the
+benchmark's --decisions-out file, which attributes each one-launch GEMM to
+the precision its layer call decided):
+  python3 -m bit_quantized_video_amd.profsum trace DB [--bench-json F] [--decisions F]
   python3 -m bit_quantized_video_amd.profsum traffic --fetch DB --write DB
-          --copy-fetch DB --copy-write DB --copy-bytes N [--command C]
-  python3 -m bit_quantized_video_amd.profsum mfma DB [--command C]
+          --copy-fetch DB --copy-write DB --copy-bytes N [--decisions F]
+  python3 -m bit_quantized_video_amd.profsum mfma DB [--decisions F]
 """
 import argparse
 import hashlib
@@ -60,9 +62,43 @@ SOURCES = {
     "select_final_rows": ["stats.hip"],
     "quant_int8": ["quant.hip"], "quant_nvfp4_mx": ["quant.hip"], "quant_nvfp4": ["quant.hip"],
     "select_quant_int8": ["quant.hip", "stats.hip"],
-    "gemm_int8": ["gemm_i8.hip"], "gemm_nvfp4_mx": ["gemm_fp4.hip"],
-    "gemm_nvfp4": ["gemm_bf16.hip"], "gemm_bf16": ["gemm_bf16.hip"],
+    "gemm_int8": ["gemm_i8.hip", "gemm_i8_pipe.h", "gemm_dispatch.hip"],
+    "gemm_nvfp4_mx": ["gemm_fp4.hip", "gemm_fp4_pipe.h", "gemm_dispatch.hip"],
+    "gemm_nvfp4": ["gemm_bf16.hip", "gemm_bf16_pipe.h", "gemm_dispatch.hip"],
+    "gemm_bf16": ["gemm_bf16.hip", "gemm_bf16_pipe.h", "gemm_dispatch.hip"],
+    "gemm_dispatch": ["gemm_dispatch.hip", "gemm_i8_pipe.h", "gemm_fp4_pipe.h", "gemm_bf16_pipe.h"],
 }
+# One-launch GEMMs (bf16 output) that run the decided precision: the kind
+# comes from the decision of the layer call (DECISIONS, in call order).
+DISPATCH = r"k_gemm_dispatch<1, (true|false)>"
+DECISIONS = None
+
+
+def load_decisions(path):
+    global DECISIONS
+    if path:
+        with open(path) as fh:
+            DECISIONS = json.load(fh)["decisions"]
+
+
+class Classifier:
+    """Kernel name -> kind, counting one-launch GEMMs per recipe so that the
+    i-th one takes the i-th layer call's decision."""
+
+    def __init__(self):
+        self.seen = {}
+
+    def __call__(self, name):
+        m = re.search(DISPATCH, name)
+        if m is None:
+            return classify(name)
+        if not DECISIONS:
+            return "gemm_dispatch"
+        mx = m.group(1) == "true"
+        i = self.seen.get(mx, 0)
+        self.seen[mx] = i + 1
+        d = DECISIONS[i % len(DECISIONS)]
+        return {1: "gemm_int8", 0: "gemm_nvfp4_mx" if mx else "gemm_nvfp4", 2: "gemm_bf16"}[d]
 COMMON_SOURCES = ["hdq_device.h", "hdq_internal.h", "../build.py"]
 WEIGHT_PREP = r"k_quant_int_rows(_long)?<\d+, \d+, true(, false)?>"
 # A launch that did work: longer than this (trace; gated-off launches take a
@@ -106,7 +142,8 @@ def schedule_window(rows):
     at the first dispatch after the last weight preparation (INT4 weight
     quantization) and ends at the last bf16-output GEMM."""
     last_prep = max((i for i, r in enumerate(rows) if re.search(WEIGHT_PREP, r[1])), default=-1)
-    gemm = [i for i, r in enumerate(rows) if classify(r[1]) and classify(r[1]).startswith("gemm")]
+    is_gemm = lambda n: re.search(DISPATCH, n) or (classify(n) or "").startswith("gemm")
+    gemm = [i for i, r in enumerate(rows) if is_gemm(r[1])]
     end = max(gemm) if gemm else len(rows) - 1
     return rows[last_prep + 1:end + 1]
 
@@ -139,9 +176,10 @@ def trace_summary(db, bench_json=None, command=None):
     out.append("launches that did work (GEMMs > 60 us, others > 12 us; finalize and difference passes")
     out.append("always) vs gated off, per step of the path:")
     out.append(f"  {'kind':<16} {'work':>6} {'avg us':>10} {'total ms':>10} {'off':>6} {'off avg us':>11}")
-    per = OrderedDict((k, ([], [])) for k in KINDS)
+    per = OrderedDict((k, ([], [])) for k in list(KINDS) + ["gemm_dispatch"])
+    cls = Classifier()
     for _, name, dur, _ in win:
-        k = classify(name)
+        k = cls(name)
         if k is None:
             continue
         # the finalize and the difference pass are never gated off
@@ -209,8 +247,9 @@ def traffic_summary(fetch_db, write_db, copy_fetch_db, copy_write_db, copy_bytes
     if [r[1] for r in fwin] != [r[1] for r in wwin]:
         raise SystemExit("FETCH_SIZE and WRITE_SIZE runs dispatched different kernel sequences")
     per = {}
+    cls = Classifier()
     for (_, name, fkib, _), (_, _, wkib, _) in zip(fwin, wwin):
-        k = classify(name)
+        k = cls(name)
         if k is None:
             continue
         d = per.setdefault(k, {"FETCH_SIZE": [], "WRITE_SIZE": [], "off": 0})
@@ -222,7 +261,7 @@ def traffic_summary(fetch_db, write_db, copy_fetch_db, copy_write_db, copy_bytes
     out.append("per launch that did work (schedule window; gated-off launches read < 1 MiB):")
     out.append(f"  {'kind':<16} {'launches':>8} {'FETCH KiB':>12} {'WRITE KiB':>12} {'HBM MB':>10}")
     lines = []
-    for k in KINDS:
+    for k in list(KINDS) + ["gemm_dispatch"]:
         if k not in per:
             continue
         d = per[k]
@@ -278,8 +317,9 @@ def mfma_summary(db, command=None):
         disp.setdefault(d, [d, name, {}])[2][cn] = v
     win = schedule_window(list(disp.values()))
     per = OrderedDict()
+    cls = Classifier()
     for _, name, cnt in win:
-        k = classify(name)
+        k = cls(name)
         if k is None or not k.startswith("gemm"):
             continue
         mops = sum(cnt.get(n, 0.0) for n in MFMA_COUNTERS[2:])
@@ -310,6 +350,7 @@ def main(argv=None):
     t.add_argument("db")
     t.add_argument("--bench-json")
     t.add_argument("--command")
+    t.add_argument("--decisions")
     f = sub.add_parser("traffic")
     f.add_argument("--fetch", required=True)
     f.add_argument("--write", required=True)
@@ -317,10 +358,13 @@ def main(argv=None):
     f.add_argument("--copy-write", required=True)
     f.add_argument("--copy-bytes", type=int, required=True)
     f.add_argument("--command")
+    f.add_argument("--decisions")
     m = sub.add_parser("mfma")
     m.add_argument("db")
     m.add_argument("--command")
+    m.add_argument("--decisions")
     a = ap.parse_args(argv)
+    load_decisions(a.decisions)
     if a.mode == "trace":
         sys.stdout.write(trace_summary(a.db, a.bench_json, a.command))
     elif a.mode == "mfma":

@@ -267,6 +267,22 @@ int hdq_linear(int32_t precision, const int32_t *decision_dev, const void *x,
                const hdq_weights *w, void *y, int32_t y_dtype, void *ws, size_t ws_bytes,
                void *stream);
 
+/*
+ * hdq_linear_dispatch -- step 3 for a device-side decision in one launch:
+ * the GEMM of the precision decision_dev names (summary section one: INT8
+ * or NVFP4 activations against 4-bit weights; section three: full
+ * precision), with every path's operands already prepared -- xq8 (INT8_ROW
+ * from hdq_quantize or hdq_select_quantize_int8), xq4 (the weights' FP4
+ * format), x (bf16, unrotated) and all three weight forms.  Results equal
+ * hdq_linear(P, decision_dev, x or xq, ...) of the decided P, bit for bit.
+ * One kernel reads the decision and runs that GEMM (K a multiple of 256 and
+ * 2 * K * max(M, N) < 2^31); other shapes enqueue the three gated GEMMs.
+ * y_dtype F32 or BF16.  No workspace.
+ */
+int hdq_linear_dispatch(const int32_t *decision_dev, const void *x, const hdq_qtensor *xq8,
+                        const hdq_qtensor *xq4, int64_t M, int64_t K, const hdq_weights *w,
+                        void *y, int32_t y_dtype, void *stream);
+
 /* Scratch bytes an entry point needs.  op = HDQ_OP_SELECT: (M = rows,
  * K = cols, N = prev_numel); HDQ_OP_SELECT_Q8: (M = rows, K = cols);
  * HDQ_OP_QUANTIZE: (M = rows, K = cols, fmt);

@@ -126,6 +126,22 @@ def test_validation_happens_before_any_launch(hdq):
     assert ok(0, w=badfp) == hdq.ERR_SHAPE
     xq = hdq.QTensorDesc(hdq.FMT_INT8_ROW, 32, 8, 64, fake, fake, None, None)
     assert ok(1, xq=ctypes.byref(xq)) == hdq.ERR_SHAPE     # block differs from the weights'
+    # one-launch linear: every operand the decision may pick must be present and consistent
+    x8 = hdq.QTensorDesc(hdq.FMT_INT8_ROW, 16, 8, 64, fake, fake, None, None)
+    x4 = hdq.QTensorDesc(hdq.FMT_NVFP4, 16, 8, 64, fake, None, fake, fake)
+    dsp = lambda **kw: L.hdq_linear_dispatch(
+        kw.get("dec", fake), kw.get("x", fake), ctypes.byref(kw.get("x8", x8)), ctypes.byref(kw.get("x4", x4)),
+        kw.get("M", 8), kw.get("K", 64), ctypes.byref(kw.get("w", w)), fake, kw.get("dt", 1), None)
+    assert dsp(dec=None) == hdq.ERR_INVALID                 # the decision is read on the device
+    assert dsp(x=None) == hdq.ERR_INVALID                   # the bf16 choice needs x
+    assert dsp(dt=2) == hdq.ERR_UNSUPPORTED                 # int32 output has no one-launch form
+    assert dsp(M=0) == hdq.ERR_SHAPE
+    assert dsp(K=32) == hdq.ERR_SHAPE                       # w.K != K
+    assert dsp(x8=hdq.QTensorDesc(hdq.FMT_INT8_ROW, 16, 7, 64, fake, fake, None, None)) == hdq.ERR_SHAPE
+    assert dsp(x8=hdq.QTensorDesc(hdq.FMT_INT8_ROW, 32, 8, 64, fake, fake, None, None)) == hdq.ERR_SHAPE
+    assert dsp(x4=hdq.QTensorDesc(hdq.FMT_NVFP4_MX, 16, 8, 64, fake, None, fake, fake)) == hdq.ERR_UNSUPPORTED
+    assert dsp(w=bad4) == hdq.ERR_UNSUPPORTED
+    assert dsp(w=hdq.WeightsDesc(32, 64, None, w4, wf)) == hdq.ERR_INVALID
 
 
 def test_product_path_never_uses_the_oracle():

@@ -405,6 +405,37 @@ def test_device_predicated_linear_matches_fixed(case):
     assert torch.equal(y_dyn.view(torch.int16), y_fix.view(torch.int16))
 
 
+@pytest.mark.parametrize("M,N,K", [(300, 384, 512), (1000, 600, 1024), (37, 19, 96), (17776, 3072, 3072)])
+@pytest.mark.parametrize("fmt", ["nvfp4", "nvfp4_mx"])
+@pytest.mark.parametrize("y_dtype", [hdq.DTYPE_BF16, hdq.DTYPE_F32])
+def test_linear_dispatch_matches_fixed_precision(M, N, K, fmt, y_dtype):
+    """hdq_linear_dispatch runs the decided precision's GEMM (one launch, or
+    three gated ones for shapes the single kernel does not take) with the
+    same bits as hdq_linear at that precision."""
+    if M == 17776 and y_dtype == hdq.DTYPE_F32:
+        pytest.skip("full size checked with bf16 output")
+    say(f"linear dispatch M={M} N={N} K={K} {fmt} y={y_dtype}")
+    hb = 32
+    x16 = synth.lognormal_tokens(M, K, synth.rng_for(114, M + N))
+    w16 = synth.gaussian(N, K, 0.02, synth.rng_for(114, K))
+    f = hdq.FMT_NVFP4_MX if fmt == "nvfp4_mx" else hdq.FMT_NVFP4
+    W = hdq.LinearWeights(to_dev(w16), hb, fp4_fmt=f)
+    xd = to_dev(x16)
+    xq8 = hdq.quantize(xd, hb, hdq.FMT_INT8_ROW)
+    xq4 = hdq.quantize(xd, hb, f)
+    dec = torch.empty(1, dtype=torch.int32, device=DEV)
+    for prec in (hdq.PREC_INT8, hdq.PREC_NVFP4, hdq.PREC_BF16):
+        dec.fill_(prec)
+        y = hdq.linear_dispatch(dec, xd, xq8, xq4, W, y_dtype=y_dtype)
+        if prec == hdq.PREC_BF16:
+            ref = hdq.linear(prec, xd, W, y_dtype=y_dtype)
+        else:
+            ref = hdq.linear(prec, None, W, xq=xq8 if prec == hdq.PREC_INT8 else xq4, y_dtype=y_dtype)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16) if y.dtype == torch.bfloat16 else y.view(torch.int32),
+                           ref.view(torch.int16) if ref.dtype == torch.bfloat16 else ref.view(torch.int32)), prec
+
+
 def test_repeat_runs_are_bitwise_identical():
     M, N, K, hb = 513, 384, 1024, 128
     x16 = synth.lognormal_tokens(M, K, synth.rng_for(111, 0))

@@ -43,3 +43,18 @@ def test_stored_traffic_guarded_by_source_hash(tmp_path):
     assert P.current_traffic(str(f), "quant_int8") is None  # sources changed
     assert P.current_traffic(str(f), "gemm_bf16") is None  # never measured
     assert P.current_traffic(str(tmp_path / "missing.txt"), "gemm_int8") is None
+
+
+def test_one_launch_gemms_take_their_calls_decisions():
+    P.DECISIONS = [1, 0, 2, 1]
+    try:
+        c = P.Classifier()
+        mx = "void hdq::k_gemm_dispatch<1, true>(int const*)"
+        plain = "void hdq::k_gemm_dispatch<1, false>(int const*)"
+        got = [c(mx) for _ in range(5)] + [c(plain) for _ in range(3)]
+        assert got == ["gemm_int8", "gemm_nvfp4_mx", "gemm_bf16", "gemm_int8", "gemm_int8",
+                       "gemm_int8", "gemm_nvfp4", "gemm_bf16"]
+        assert c("void hdq::k_gemm_dispatch<0, true>(int const*)") is None  # f32 output: not the schedule
+    finally:
+        P.DECISIONS = None
+    assert P.Classifier()("void hdq::k_gemm_dispatch<1, true>(int const*)") == "gemm_dispatch"
