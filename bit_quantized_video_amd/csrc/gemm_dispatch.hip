@@ -44,11 +44,12 @@ static hipError_t launch_dispatch_t(const int32_t* decision, const int8_t* x8, c
                                     const uint8_t* wsc, const float* wts, const uint16_t* xb,
                                     const uint16_t* wb, void* y, int64_t M, int64_t N, int64_t K,
                                     hipStream_t s) {
-  // Dynamic LDS: the largest body's (FP4: two 68 KB stages; the others stage
-  // a 256 x 256 bf16 output tile of 528-byte rows).
+  // Dynamic LDS: the largest body's (INT8: three 48 KB stages; FP4: two
+  // 68 KB stages; bf16: a 256 x 256 bf16 output tile of 528-byte rows).
   constexpr size_t fp4_lds = 2 * (256 * 128 * 2 + 512 * 8);
-  constexpr size_t lds = fp4_lds > kBf16PipeLds ? fp4_lds : kBf16PipeLds;
-  static_assert(I8Cfg<2, 4, 4, 2>::LDS <= (int)lds, "INT8 body needs more LDS");
+  constexpr size_t i8_lds = (size_t)I8Cfg<2, 4, 4, 2>::LDS;
+  constexpr size_t lds0 = fp4_lds > kBf16PipeLds ? fp4_lds : kBf16PipeLds;
+  constexpr size_t lds = i8_lds > lds0 ? i8_lds : lds0;
   auto kern = k_gemm_dispatch<OUT, FP4MX>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -12,15 +12,15 @@
 //    The instruction's A operand is a 32-row slice of W and its B operand a
 //    32-row slice of X, so each output lane holds one token row m and four
 //    consecutive output features n (8- or 16-byte stores).
-//  * INT4 weights are unpacked to int8 on their way into LDS: nibble q is
-//    placed in the high half of its byte (value 16 q), the interleaved
-//    low/high nibbles are put back in k order with two v_perm_b32, and the
-//    epilogue divides the exact int32 sum by 16 (|16 acc| < 2^31 for
-//    K < 150000).
+//  * INT4 weights stay packed in LDS and are unpacked to int8 after the
+//    fragment read: nibble q is placed in the high half of its byte (value
+//    16 q), the interleaved low/high nibbles are put back in k order with two
+//    v_perm_b32, and the epilogue divides the exact int32 sum by 16
+//    (|16 acc| < 2^31 for K < 150000).
 //  * Two kernels.  The pipelined one (K % 128 == 0, every CogVideoX shape):
-//    256 x 256 tiles, 8 waves (two per SIMD), buffer loads two stages ahead
-//    in registers, double-buffered LDS with XOR-swizzled rows, LDS-only
-//    barriers; see its own comment below.  The fallback (any K % 32 == 0):
+//    256 x 256 tiles, 8 waves (two per SIMD), LDS-DMA buffer loads two stages
+//    ahead into three LDS stages with XOR-swizzled rows, one barrier per
+//    stage; see gemm_i8_pipe.h.  The fallback (any K % 32 == 0):
 //    4 waves as 2 x 2, 64-byte LDS rows with 16-byte chunk c of row r at
 //    chunk c ^ ((r >> 1) & 3), K advancing 64 bytes per double-buffered
 //    stage.

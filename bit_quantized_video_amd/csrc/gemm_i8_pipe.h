@@ -7,6 +7,8 @@
 #include "hdq_device.h"
 #include "hdq_internal.h"
 
+#include <type_traits>
+
 namespace hdq {
 
 // 32 packed INT4 (uint4) -> 32 int8 holding 16 * q, in k order.
@@ -29,15 +31,15 @@ __device__ __forceinline__ void unpack_int4x32(const uint4 p, uint4& lo, uint4& 
 //  * Workgroup tile BM tokens x BN features; WAVES_M x WAVES_N waves, each
 //    wave WM_T x WN_T subtiles of 32 x 32.  With 8 waves (two per SIMD) one
 //    wave's LDS / global / barrier waits overlap the other wave's MFMAs.
-//  * K advances 128 per stage.  Two register sets hold the global loads of
-//    the next two stages (the loop is unrolled by two so the sets alternate
-//    without copies); LDS is double-buffered.  Loads for stage kt + 2 are
-//    issued before stage kt is computed and written to LDS after stage
-//    kt + 1 is, so two stages of compute cover their latency.  Barriers
-//    order LDS only (lds_barrier), leaving the prefetches in flight.
-//  * Operands arrive through buffer loads (rows past M or N read as zero;
-//    their outputs are not stored).  X rows are 128 bytes in LDS (swz128),
-//    packed INT4 W rows 64 bytes (swz64).  Within a stage, k-substep pair p
+//  * K advances 128 per stage.  Operands go from global memory straight to
+//    LDS with LDS-DMA buffer loads (no register staging, no LDS writes by
+//    the waves), into three LDS stage buffers: stage kt + 2 is issued right
+//    after the barrier that opens stage kt, so two stages of compute cover
+//    its latency, and that barrier is the only one per stage (it also
+//    retires the buffer of stage kt - 1, which kt + 2 reuses).
+//  * Rows past M or N read as zero (buffer range); their outputs are not
+//    stored.  X rows are 128 bytes in LDS (swz128), packed INT4 W rows 64
+//    bytes (swz64).  Within a stage, k-substep pair p
 //    (64 K) gives lane half h the K range [64p + 32h, +32): for W one
 //    16-byte read of packed nibbles unpacked to the two substeps' fragments,
 //    for X two 16-byte reads.  (Any assignment of K to lanes works as long as
@@ -49,16 +51,11 @@ struct I8Cfg {
   static constexpr int BM = WAVES_M * WM_T * 32, BN = WAVES_N * WN_T * 32, BK = 128;
   static constexpr int XB = BM * BK, SB = XB + BN * BK / 2;  // LDS bytes per stage
   static constexpr int OUT_PITCH = BN * 2 + 16;              // bf16 output row in LDS, padded
-  static constexpr int LDS = (2 * SB > BM * OUT_PITCH) ? 2 * SB : BM * OUT_PITCH;
-  static constexpr int XC = XB / 16 / THREADS;                // 16-byte loads per thread
-  static constexpr int WC = BN * BK / 2 / 16 / THREADS;
-  static constexpr int XROWS = THREADS / 8, WROWS = THREADS / 4;  // rows per load round
-  static_assert(XC >= 1 && WC >= 1, "tile too small for the workgroup");
-};
-
-template <int XC, int WC>
-struct I8Stage {
-  uint4 x[XC], w[WC];
+  static constexpr int NS = 3;                                // LDS stage buffers
+  static constexpr int LDS = (NS * SB > BM * OUT_PITCH) ? NS * SB : BM * OUT_PITCH;
+  // LDS-DMA instructions (1 KB each) per wave and stage: X, then W
+  static constexpr int XI = XB / 1024 / (THREADS / 64), WI = BN * BK / 2 / 1024 / (THREADS / 64);
+  static_assert(THREADS == 512 && BM == 256 && BN == 256, "the DMA row mapping assumes 8 waves, 256 x 256");
 };
 
 template <int WAVES_M, int WAVES_N, int WM_T, int WN_T, int OUT>
@@ -68,7 +65,6 @@ __device__ __forceinline__ void gemm_i8i4_pipe_body(
   using C = I8Cfg<WAVES_M, WAVES_N, WM_T, WN_T>;
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, XB = C::XB, SB = C::SB;
   constexpr int kOutPitch = C::OUT_PITCH;
-  using Stage = I8Stage<C::XC, C::WC>;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -78,30 +74,23 @@ __device__ __forceinline__ void gemm_i8i4_pipe_body(
   const int nk = K / BK;
   const int ldw = K >> 1;
 
-  // Operands arrive through buffer resources over the current tile's rows;
-  // 8 threads per 128-byte X row and 4 per W row (coalesced).  Load round p
-  // is XROWS (WROWS) rows further on, a multiple of 16, which leaves the
-  // swizzle unchanged: LDS destinations are a base plus an immediate.
-  const int xr0 = tid >> 3, xc0 = tid & 7, wr0 = tid >> 2, wc0 = tid & 3;
-  const uint32_t xvoff = (uint32_t)(xr0 * K + 16 * xc0);
-  const uint32_t wvoff = (uint32_t)(wr0 * ldw + 16 * wc0);
-  const int xdst = xr0 * 128 + 16 * (xc0 ^ swz128(xr0));
-  const int wdst = XB + wr0 * 64 + 16 * (wc0 ^ swz64(wr0));
-
-  // Buffer resources over the current tile's rows.
-  __amdgpu_buffer_rsrc_t xres, wres;
-  auto load = [&](Stage& st, int kt) {
+  // LDS-DMA staging: one wave instruction writes 1 KB of LDS, lane i's 16
+  // bytes at byte 16 i.  X instruction p of wave w fills LDS rows
+  // 64p + 8w + (i >> 3), slot i & 7, with logical chunk (i & 7) ^ swz128(row):
+  // the swizzled layout the fragment reads expect.  W instruction p fills
+  // rows 128p + 16w + (i >> 2), slot i & 3, with chunk (i & 3) ^ swz64(row).
+  // Both swizzles depend on the lane only, so the instructions of a stage
+  // differ by scalar offsets.
+  const int xrow = 8 * wave + (lane >> 3), wrow = 16 * wave + (lane >> 2);
+  const uint32_t xvoff = (uint32_t)(xrow * K + 16 * ((lane & 7) ^ swz128(xrow)));
+  const uint32_t wvoff = (uint32_t)(wrow * ldw + 16 * ((lane & 3) ^ swz64(wrow)));
+  __amdgpu_buffer_rsrc_t xres, wres;  // over the current tile's rows
+  auto issue = [&](int kt, int buf) {
+    uint8_t* base = smem + buf * SB + 1024 * wave;
 #pragma unroll
-    for (int p = 0; p < C::XC; ++p) st.x[p] = buf_load16(xres, xvoff, kt * BK + p * C::XROWS * K);
+    for (int p = 0; p < C::XI; ++p) lds_dma16(xres, base + 8192 * p, xvoff, kt * BK + p * 64 * K);
 #pragma unroll
-    for (int p = 0; p < C::WC; ++p) st.w[p] = buf_load16(wres, wvoff, kt * (BK / 2) + p * C::WROWS * ldw);
-  };
-  auto store = [&](const Stage& st, int buf) {
-    uint8_t* base = smem + buf * SB;
-#pragma unroll
-    for (int p = 0; p < C::XC; ++p) *reinterpret_cast<uint4*>(base + xdst + C::XROWS * 128 * p) = st.x[p];
-#pragma unroll
-    for (int p = 0; p < C::WC; ++p) *reinterpret_cast<uint4*>(base + wdst + C::WROWS * 64 * p) = st.w[p];
+    for (int p = 0; p < C::WI; ++p) lds_dma16(wres, base + XB + 8192 * p, wvoff, kt * (BK / 2) + p * 128 * ldw);
   };
 
   v16i acc[WN_T][WM_T];
@@ -154,7 +143,7 @@ __device__ __forceinline__ void gemm_i8i4_pipe_body(
     grouped_tile(logical, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     if constexpr (OUT == kOutBf16) {
-      // Stage the bf16 tile in LDS (both pipeline buffers are free at a tile
+      // Stage the bf16 tile in LDS (the stage buffers are free at a tile
       // boundary once every wave is past the last stage), then write whole
       // rows: 32 lanes x 16 bytes per 512-byte row.
       lds_barrier();
@@ -248,8 +237,11 @@ __device__ __forceinline__ void gemm_i8i4_pipe_body(
     }
   };
 
-  // Persistent loop over this workgroup's tiles; per tile, the K-stages run
-  // through the two-stage register prefetch and the double-buffered LDS.
+  // Persistent loop over this workgroup's tiles.  Per tile, stages 0 and 1
+  // are issued; stage kt waits for its own loads (those of kt + 1 may stay
+  // in flight: C::XI + C::WI per wave), passes the barrier, issues kt + 2
+  // into the buffer of kt - 1 and is computed.  Unrolled by three, so each
+  // buffer index is a constant.
   for (int t = 0; t < seq.count; ++t) {
     const int logical = seq.first + t * seq.stride;
     {
@@ -259,27 +251,22 @@ __device__ __forceinline__ void gemm_i8i4_pipe_body(
       xres = make_rsrc(X + (int64_t)m0 * K, (uint32_t)((int64_t)(M - m0) * K));
       wres = make_rsrc(W4 + (int64_t)n0 * ldw, (uint32_t)((int64_t)(N - n0) * ldw));
     }
-    Stage ra, rb;
-    load(ra, 0);
-    if (nk > 1) load(rb, 1);
-    store(ra, 0);
-    lds_barrier();
-    // Pairs of stages; one loop exit keeps the accumulators in one register
-    // allocation.  An odd last stage (left in LDS buffer 0) follows the loop.
-    int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-      // stage kt in LDS buffer 0, stage kt + 1 in rb
-      if (kt + 2 < nk) load(ra, kt + 2);
-      compute(0);
-      store(rb, 1);
-      lds_barrier();
-      // stage kt + 1 in LDS buffer 1, stage kt + 2 in ra
-      if (kt + 3 < nk) load(rb, kt + 3);
-      compute(1);
-      if (kt + 2 < nk) store(ra, 0);
-      lds_barrier();
+    issue(0, 0);
+    if (nk > 1) issue(1, 1);
+    auto step = [&](int kt, auto bufc) {
+      constexpr int b = decltype(bufc)::value;
+      if (kt + 1 < nk)
+        dma_barrier<C::XI + C::WI>();
+      else
+        dma_barrier<0>();
+      if (kt + 2 < nk) issue(kt + 2, (b + 2) % 3);
+      compute(b);
+    };
+    for (int kt = 0; kt < nk; kt += 3) {
+      step(kt, std::integral_constant<int, 0>{});
+      if (kt + 1 < nk) step(kt + 1, std::integral_constant<int, 1>{});
+      if (kt + 2 < nk) step(kt + 2, std::integral_constant<int, 2>{});
     }
-    if (kt < nk) compute(0);
     epilogue(logical);
     zero_acc();
   }

@@ -261,6 +261,22 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Barrier for LDS filled by LDS-DMA loads (lds_dma16): wait until at most
+// PENDING of this wave's vector memory operations are outstanding (they
+// complete in order, so the older ones have landed in LDS), then s_barrier.
+// No fence: a workgroup LDS fence would wait for every DMA load in flight.
+// The empty asm statements keep the compiler from moving LDS accesses
+// across the barrier.
+template <int PENDING>
+__device__ __forceinline__ void dma_barrier() {
+  static_assert(PENDING >= 0 && PENDING < 64, "vmcnt has six bits");
+  // s_waitcnt: vmcnt bits [3:0] and [15:14], expcnt and lgkmcnt left at max.
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (PENDING & 15) | ((PENDING >> 4) << 14));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ---- buffer loads ----------------------------------------------------------------
 // Raw buffer resource over [base, base + bytes): loads at offsets >= bytes
 // return zeros, so tile rows past the end of a tensor read as zero.  The
@@ -270,6 +286,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+// LDS-DMA buffer load: the wave's 64 lanes each read 16 bytes (at voff + soff
+// of the resource; past its end they read zero) and write them to LDS at
+// lds + 16 * lane.  lds must be the same for the whole wave.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)voff,
+                                           (int)soff, 0, 0);
 }
 
 }  // namespace hdq
