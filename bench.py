@@ -71,6 +71,11 @@ def parse():
     ap.add_argument("--delta-ahead", type=int, default=2,
                     help="with --delta overlap: the difference of call k + D runs beside the GEMMs "
                          "of call k")
+    ap.add_argument("--events", choices=["gemm", "all"], default="gemm",
+                    help="HIP events in the timed steps: around each layer call's GEMM launch only "
+                         "(default; the other kernels are timed in one instrumented step after the timed "
+                         "ones), or around every kernel (each event record adds a marker to the stream, "
+                         "which costs the step several percent)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decisions-out", help="write the per-call precision decisions (call order) as JSON, "
                                             "for attributing one-launch GEMMs in profiles")
@@ -213,11 +218,18 @@ def build_schedule(args, hdq, synth):
                 s_levels=s_levels, sums=sums, ws_delta=ws_delta, ws_sq8=ws_sq8, side=side)
 
 
+def rec(ev, i):
+    """Records event i of a layer call's list, if that list has one."""
+    if ev is not None and ev[i] is not None:
+        ev[i].record()
+
+
 def run_schedule_step(S, args, hdq, recipe, events=None, side_events=None):
     """One step: every timestep, block and layer, NVFP4 layers in `recipe`.
-    With `events`, records 7 HIP events per layer call on the main stream
-    (select | q8 | q4 | g8 | g4 | gbf) and, with --delta overlap, 2 per call
-    on the difference stream (`side_events`)."""
+    With `events`, records up to 7 HIP events per layer call on the main
+    stream (select | q8 | q4 | g8 | g4 | gbf; None entries are skipped) and,
+    with --delta overlap, 2 per call on the difference stream
+    (`side_events`)."""
     calls = [(t, b, li) for t in range(args.timesteps) for b in range(len(S["blocks"]))
              for li in range(len(S["blocks"][b]))]
     main = torch.cuda.current_stream()
@@ -257,7 +269,7 @@ def run_schedule_step(S, args, hdq, recipe, events=None, side_events=None):
         if fused and not overlap:
             # the difference on the main stream, right before the selection
             hdq.delta_sums(L["prev_in"], L["prev_out"][t], sums=S["sums"][t, b, li], ws=S["ws_delta"])
-        if ev: ev[0].record()
+        rec(ev, 0)
         if fused:
             hdq.select_quantize_int8(S["sums"][t, b, li], L["x"], HB, DELTA_T, RATIO_T, decision=d,
                                      stats=st, out=sh["xq8"], ws=S["ws_sq8"])
@@ -267,13 +279,13 @@ def run_schedule_step(S, args, hdq, recipe, events=None, side_events=None):
         else:
             hdq.select_precision(L["prev_in"], L["prev_out"][t], L["x"], HB, DELTA_T, RATIO_T,
                                  decision=d, stats=st, ws=S["ws_sel"])
-        if ev: ev[1].record()
+        rec(ev, 1)
         if not fused:
             hdq.quantize(L["x"], HB, hdq.FMT_INT8_ROW, out=sh["xq8"], decision=d)
-        if ev: ev[2].record()
+        rec(ev, 2)
         hdq.quantize(L["x"], HB, S["recipes"][recipe], tensor_amax=st[4:5], out=sh["xq4"][recipe],
                      decision=d)
-        if ev: ev[3].record()
+        rec(ev, 3)
         if overlap and k + ahead < len(calls):
             # the difference of a later call streams beside this call's
             # compute-bound GEMMs rather than beside its memory-bound passes
@@ -283,17 +295,14 @@ def run_schedule_step(S, args, hdq, recipe, events=None, side_events=None):
         W = L["W"][recipe]
         if args.dispatch == "on":
             hdq.linear_dispatch(d, L["x"], sh["xq8"], sh["xq4"][recipe], W, y=sh["y"])
-            if ev:
-                ev[4].record()
-                ev[5].record()
-                ev[6].record()
+            rec(ev, 4)
         else:
             hdq.linear(hdq.PREC_INT8, None, W, decision=d, xq=sh["xq8"], y=sh["y"])
-            if ev: ev[4].record()
+            rec(ev, 4)
             hdq.linear(hdq.PREC_NVFP4, None, W, decision=d, xq=sh["xq4"][recipe], y=sh["y"])
-            if ev: ev[5].record()
+            rec(ev, 5)
             hdq.linear(hdq.PREC_BF16, L["x"], W, decision=d, y=sh["y"])
-            if ev: ev[6].record()
+            rec(ev, 6)
     return len(calls)
 
 
@@ -315,10 +324,13 @@ def schedule_kernel_times(S, args, events_per_step, synth, recipe, side_per_step
                     ev = evs[k]
                     k += 1
                     d = int(decisions[t, b, li])
-                    dt = [ev[i].elapsed_time(ev[i + 1]) for i in range(6)]
+                    dt = [ev[i].elapsed_time(ev[i + 1]) if ev[i] is not None and ev[i + 1] is not None
+                          else None for i in range(6)]
                     flops = 2.0 * M * N * K
                     q8, q4 = quant_bytes(M, K, "int8"), quant_bytes(M, K, "nvfp4")
-                    if fused:
+                    if dt[0] is None:
+                        pass  # GEMM events only
+                    elif fused:
                         # one pass: x read once, INT8 codes written
                         kt.add("select_quant_int8", dt[0], q8, q8)
                     else:
@@ -329,18 +341,20 @@ def schedule_kernel_times(S, args, events_per_step, synth, recipe, side_per_step
                     if side is not None:
                         kt.add("delta_sums", side[k - 1][0].elapsed_time(side[k - 1][1]), 4 * M * K,
                                4 * M * K)
-                    kt.add("quant_nvfp4" if d == 0 else "quant_nvfp4_gated_off", dt[2],
-                           q4 if d == 0 else 0, q4 if d == 0 else 0)
+                    if dt[2] is not None:
+                        kt.add("quant_nvfp4" if d == 0 else "quant_nvfp4_gated_off", dt[2],
+                               q4 if d == 0 else 0, q4 if d == 0 else 0)
                     for kind, prec, dd, i in (("gemm_int8", "int8", 1, 3), ("gemm_nvfp4", "nvfp4", 0, 4),
                                               ("gemm_bf16", "bf16", 2, 5)):
                         on = d == dd
                         if dispatch:
                             # one launch (slot 3) ran the decided precision's GEMM
-                            if on:
+                            if on and dt[3] is not None:
                                 kt.add(kind, dt[3], flops, gemm_bytes(M, N, K, prec, recipe))
                             continue
-                        kt.add(kind if on else kind + "_gated_off", dt[i], flops if on else 0,
-                               gemm_bytes(M, N, K, prec, recipe) if on else 0)
+                        if dt[i] is not None:
+                            kt.add(kind if on else kind + "_gated_off", dt[i], flops if on else 0,
+                                   gemm_bytes(M, N, K, prec, recipe) if on else 0)
     return kt, decisions
 
 
@@ -391,26 +405,49 @@ def cpu_baseline_schedule(S, args, synth):
 
 
 def time_schedule(S, args, hdq, synth, recipe):
-    """Warmup, then exactly args.steps timed steps; per-kernel event times."""
+    """Warmup, then exactly args.steps timed steps with HIP events around
+    each layer call's GEMM launch (--events gemm) or every kernel (all).
+    With gemm events, one instrumented step after the timed ones times the
+    other kernels.  Returns ms/step, per-kernel times, the decisions, and
+    which step each kernel's times come from."""
     log(f"warmup ({recipe})")
     for _ in range(args.warmup):
         run_schedule_step(S, args, hdq, recipe)
     n_calls = args.timesteps * args.blocks * len(synth.SCHEDULE_LAYERS)
-    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(n_calls)]
-              for _ in range(args.steps)]
-    side = None
-    if args.delta == "overlap":
-        side = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_calls)]
-                for _ in range(args.steps)]
+    overlap = args.delta == "overlap"
+    gemm_slots = (3, 4) if args.dispatch == "on" else (3, 4, 5, 6)
+
+    def make(slots):
+        return [[torch.cuda.Event(enable_timing=True) if i in slots else None for i in range(7)]
+                for _ in range(n_calls)]
+
+    def make_side():
+        return [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_calls)]
+
+    all_slots = tuple(range(5 if args.dispatch == "on" else 7))
+    timed_slots = gemm_slots if args.events == "gemm" else all_slots
+    events = [make(timed_slots) for _ in range(args.steps)]
+    side = [make_side() for _ in range(args.steps)] if overlap and args.events == "all" else None
     torch.cuda.synchronize()
-    log(f"timing {args.steps} steps ({recipe})")
+    log(f"timing {args.steps} steps ({recipe}, events: {args.events})")
     t0 = time.perf_counter()
     for s in range(args.steps):
         run_schedule_step(S, args, hdq, recipe, events[s], side[s] if side else None)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     kt, decisions = schedule_kernel_times(S, args, events, synth, recipe, side)
-    return 1e3 * elapsed / args.steps, kt, decisions
+    source = {k: "timed steps" for k in kt.t}
+    if args.events == "gemm":
+        # the other kernels: one instrumented (untimed) step
+        ev1, side1 = [make(all_slots)], [make_side()] if overlap else None
+        run_schedule_step(S, args, hdq, recipe, ev1[0], side1[0] if side1 else None)
+        torch.cuda.synchronize()
+        kt1, _ = schedule_kernel_times(S, args, ev1, synth, recipe, side1)
+        for k in list(kt1.t):
+            if not k.startswith("gemm"):
+                kt.t[k], kt.work[k], kt.bytes[k], kt.n[k] = kt1.t[k], kt1.work[k], kt1.bytes[k], kt1.n[k]
+                source[k] = "instrumented step"
+    return 1e3 * elapsed / args.steps, kt, decisions, source
 
 
 def schedule_quality(S, hdq):
@@ -440,7 +477,7 @@ def bench_schedule(args, hdq, synth):
     n_calls = args.timesteps * args.blocks * len(synth.SCHEDULE_LAYERS)
     other = "nvfp4" if args.fp4 == "mx" else "mx"
     runs = {r: time_schedule(S, args, hdq, synth, r) for r in (args.fp4, other)}
-    ms_per_step, kt, decisions = runs[args.fp4]
+    ms_per_step, kt, decisions, source = runs[args.fp4]
     if args.decisions_out:
         with open(args.decisions_out, "w") as fh:
             json.dump({"decisions": [int(v) for v in decisions.reshape(-1)]}, fh)
@@ -459,7 +496,7 @@ def bench_schedule(args, hdq, synth):
     # effective TOPS of the fused quant + linear alone (selected kernels only)
     ql_ms = q_ms + sum(kt.t.get(k, 0.0) for k in ("gemm_int8", "gemm_nvfp4", "gemm_bf16"))
     ql_flops = sum(kt.work.get(k, 0.0) for k in ("gemm_int8", "gemm_nvfp4", "gemm_bf16"))
-    o_ms, o_kt, _ = runs[other]
+    o_ms, o_kt, _, _ = runs[other]
     o_ks = o_kt.summary()
     result = {
         "metric": METRIC,
@@ -484,7 +521,7 @@ def bench_schedule(args, hdq, synth):
         "fused_quant_linear_tops": round(ql_flops / (ql_ms * 1e-3) / 1e12, 2) if ql_ms > 0 else None,
         "decisions": counts,
         "kernels": {k: {"launches": v["launches"], "total_ms": v["total_ms"], "avg_us": v["avg_us"],
-                        "rate": round(v["rate"] / 1e12, 3),
+                        "rate": round(v["rate"] / 1e12, 3), "timed_in": source.get(k),
                         "rate_unit": ("TB/s" if k.startswith(("quant", "select", "delta")) else
                                       "TOP/s" if k.startswith("gemm_int8") else "TFLOP/s")}
                     for k, v in ks.items()},
