@@ -233,6 +233,9 @@ __device__ __forceinline__ void gemm_bf16_pipe_body(
           }
         }
       }
+      // Every wave is past the last stage (in buffer 0 when nk is odd) before
+      // the next tile's first stage is stored there.
+      lds_barrier();
     }
   };
 

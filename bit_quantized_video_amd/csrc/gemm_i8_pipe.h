@@ -235,6 +235,10 @@ __device__ __forceinline__ void gemm_i8i4_pipe_body(
         }
       }
     }
+    // Every wave is past the last stage before the next tile's first stages
+    // are issued into the stage buffers (one of which the last stage used
+    // unless nk is a multiple of three).
+    lds_barrier();
   };
 
   // Persistent loop over this workgroup's tiles.  Per tile, stages 0 and 1

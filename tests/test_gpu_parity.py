@@ -313,6 +313,41 @@ def test_int_gemm_i32_bitexact(M, N, K):
     assert np.array_equal(y.cpu().numpy().astype(np.int64), acc)
 
 
+# More 256 x 256 tiles (17 x 16 = 272) than persistent workgroups (at most
+# one per CU), so some workgroups run a second tile right after the last
+# K-stage of their first; K covers every count of K-stages modulo the LDS
+# stage rotation.  Sampled rows reach every tile row.
+MT_M, MT_N = 17 * 256, 16 * 256
+MT_ROWS = np.r_[np.arange(0, MT_M, 17), MT_M - 1]
+
+
+@pytest.mark.parametrize("K", [128, 256, 384, 512])
+def test_int_gemm_multi_tile_workgroups(K):
+    say(f"int gemm i32 multi-tile M={MT_M} N={MT_N} K={K}")
+    hb = 32
+    x16, w16 = int_operands(MT_M, MT_N, K, hb, K)
+    W = hdq.LinearWeights(to_dev(w16), hb, fp4_fmt=None)
+    xq = hdq.quantize(to_dev(x16), hb, hdq.FMT_INT8_ROW)
+    y = hdq.linear(hdq.PREC_INT8, None, W, xq=xq, y_dtype=hdq.DTYPE_I32)
+    torch.cuda.synchronize()
+    qa, sa = O.quant_int(x16[MT_ROWS], hb, 127)
+    qw, sw = O.quant_int(w16, hb, 7)
+    _, acc = O.gemm_int(qa, sa, qw, sw)
+    assert np.array_equal(y.cpu().numpy()[MT_ROWS].astype(np.int64), acc)
+
+
+@pytest.mark.parametrize("K", [64, 128, 192])
+def test_bf16_gemm_multi_tile_workgroups(K):
+    say(f"bf16 gemm f32 multi-tile M={MT_M} N={MT_N} K={K}")
+    x16 = synth.gaussian_outliers(MT_M, K, 0.01, 20.0, synth.rng_for(108, K))
+    w16 = synth.gaussian(MT_N, K, 0.02, synth.rng_for(109, K))
+    W = hdq.LinearWeights(to_dev(w16), 32, fp4_fmt=None)
+    y = hdq.linear(hdq.PREC_BF16, to_dev(x16), W, y_dtype=hdq.DTYPE_F32)
+    torch.cuda.synchronize()
+    ref = round_like(O.gemm_bf16(x16[MT_ROWS], w16), hdq.DTYPE_F32)
+    assert rel_fro(y_np(y)[MT_ROWS], ref) <= REL_TOL
+
+
 @pytest.mark.parametrize("M,N,K", GEMM_CASES[1:])
 @pytest.mark.parametrize("y_dtype", [hdq.DTYPE_F32, hdq.DTYPE_BF16])
 def test_linear_int8_matches_oracle(M, N, K, y_dtype):
