@@ -196,7 +196,7 @@ def unpack_int4(p, cols):
     return q
 
 
-def quant_nvfp4_rotated(y, amax, mx=False):
+def quant_nvfp4_rotated(y, amax, mx=0):
     y = _c(y, np.float32)
     rows, cols = y.shape
     codes = np.zeros((rows, cols // 2), np.uint8)
@@ -207,8 +207,10 @@ def quant_nvfp4_rotated(y, amax, mx=False):
     return codes, scales, np.float32(st[0])
 
 
-def quant_nvfp4(x16, b, amax=None, mx=False):
-    """Rotate then quantize to NVFP4 (mx=True: the MX-compatible recipe).
+def quant_nvfp4(x16, b, amax=None, mx=0):
+    """Rotate then quantize to NVFP4.  mx: 0 plain, 1 (or True) the
+    MX-compatible recipe (a power-of-two scale shared by each pair of
+    16-blocks), 2 power-of-two scales per 16-block.
     amax=None takes the rotated amax of the rows given.  Returns
     (codes uint8 [rows, cols/2], E4M3 scales uint8 [rows, cols/16], s_t)."""
     x16 = _c(x16, np.uint16)

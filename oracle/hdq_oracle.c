@@ -313,6 +313,10 @@ void orc_unpack_int4(const uint8_t *p, int64_t rows, int64_t cols, int8_t *q)
  *   a = max |y|; t = a / (6 * s_t); E = the smallest power of two >= t,
  *   clamped to [2^-9, 2^8] (all E4M3-representable); both 16-blocks of the
  *   group store E; then d and codes as above.
+ * mx == 2, power-of-two scales per 16-block: as mx == 1 with each aligned
+ *   16-block taking its own E (a = max over the 16).  Still valid NVFP4; a
+ *   scaled-FP4 matrix instruction with one scale per 32 elements computes it
+ *   exactly in two passes, one per 16-block half.
  * A below ORC_TINY: s_t = 0 and every code and scale byte is 0.
  * Layout: codes [rows, cols/2] (even k in the low nibble); scales
  * [rows, cols/16]. */
@@ -330,7 +334,7 @@ void orc_quant_nvfp4_rotated(const float *y, int64_t rows, int64_t cols,
     float s_t = mx ? amax / 1536.0f : amax / 2688.0f;
     *s_t_out = s_t;
     float six_st = 6.0f * s_t;
-    int group = mx ? 32 : 16;
+    int group = mx == 1 ? 32 : 16;
     for (int64_t r = 0; r < rows; r++) {
         const float *yr = y + r * cols;
         for (int64_t g0 = 0; g0 < cols; g0 += group) {

@@ -249,7 +249,7 @@ def nvfp4_error_bound(v_abs, d):
     return step * d
 
 
-@pytest.mark.parametrize("mx", [False, True])
+@pytest.mark.parametrize("mx", [0, 1, 2])
 def test_nvfp4_error_bound(mx):
     x16 = synth.lognormal_tokens(48, 1024, synth.rng_for(9, 1))
     y = O.rotate_f32(x16, 128)
@@ -269,11 +269,49 @@ def test_nvfp4_error_bound(mx):
     sat = ~inrange & normal
     assert np.all(err[sat] <= 0.4 * d[sat] * (1 + 1e-5))
     if mx:
-        # pairs of 16-blocks share one power-of-two scale
-        assert np.array_equal(sc[:, 0::2], sc[:, 1::2])
+        # power-of-two scales (per pair of 16-blocks for mx == 1) and nothing
+        # saturates: the scale is never below the block's need
+        if mx == 1:
+            assert np.array_equal(sc[:, 0::2], sc[:, 1::2])
+        else:
+            assert not np.array_equal(sc[:, 0::2], sc[:, 1::2])
         vals = O.e4m3_decode(sc)
         assert np.all(np.log2(vals) == np.round(np.log2(vals)))
-        assert np.all(v <= 6 * (1 + 1e-6))          # nothing saturates
+        assert np.all(v <= 6 * (1 + 1e-6))
+
+
+def test_nvfp4_p2_scale_is_the_smallest_sufficient_power_of_two():
+    # per 16-block: E = 2^e with E * 6 * s_t >= max |y| (no code saturates)
+    # and E / 2 * 6 * s_t < max |y| (a smaller power would saturate), unless
+    # E sits at a clamp (2^-9 or 2^8)
+    x16 = synth.lognormal_tokens(32, 512, synth.rng_for(9, 21), sigma=1.0)
+    y = O.rotate_f32(x16, 128).astype(np.float64)
+    c, sc, st = O.quant_nvfp4(x16, 128, mx=2)
+    assert st == np.float32(np.abs(y).max()) / np.float32(1536.0)
+    E = O.e4m3_decode(sc).astype(np.float64)
+    a = np.abs(y).reshape(32, 32, 16).max(axis=2)
+    six_st = 6.0 * float(st)
+    assert np.all((E * six_st >= a * (1 - 1e-6)) | (E == 2.0 ** 8))
+    assert np.all((E / 2 * six_st < a * (1 + 1e-6)) | (E == 2.0 ** -9))
+    # the largest block lands exactly on 2^8: A / (6 s_t) = 256
+    assert E.max() == 2.0 ** 8
+
+
+def test_nvfp4_p2_equals_mx_when_both_halves_share_the_block_max():
+    # a 32-group whose two 16-blocks have the same max |y| gets the same
+    # power of two per block (mx == 2) as per pair (mx == 1): same bytes
+    rng = np.random.default_rng(22)
+    h = rng.standard_normal((6, 8, 16)).astype(np.float32)
+    y = np.concatenate([h, -h[:, :, ::-1]], axis=2).reshape(6, 256)
+    amax = np.abs(y).max()
+    c1, e1, s1 = O.quant_nvfp4_rotated(y, amax, mx=1)
+    c2, e2, s2 = O.quant_nvfp4_rotated(y, amax, mx=2)
+    assert s1 == s2 and np.array_equal(e1, e2) and np.array_equal(c1, c2)
+    # and when the halves differ by more than a factor two, the scales differ
+    y2 = y.copy().reshape(6, 8, 32)
+    y2[:, :, 16:] *= np.float32(0.2)
+    c3, e3, _ = O.quant_nvfp4_rotated(y2.reshape(6, 256), amax, mx=2)
+    assert np.all(e3[:, 1::2] < e3[:, 0::2])
 
 
 def test_nvfp4_zero_tensor_and_zero_blocks():
@@ -310,7 +348,7 @@ def test_int4_pack_round_trip_and_layout():
     assert np.array_equal(O.unpack_int4(O.pack_int4(q), 64), q)
 
 
-@pytest.mark.parametrize("mx", [False, True])
+@pytest.mark.parametrize("mx", [0, 1, 2])
 def test_nvfp4_gemm_matches_dequantized_product(mx):
     xa = synth.lognormal_tokens(9, 256, synth.rng_for(9, 2))
     xw = synth.gaussian(11, 256, 0.02, synth.rng_for(9, 3))
@@ -454,13 +492,30 @@ def test_int8_requantize_is_idempotent():
     assert np.array_equal(q, q2)
 
 
-def test_nvfp4_requantize_is_idempotent_on_normal_scales():
+def test_nvfp4_p2_requantize_reproduces_the_values():
+    # with power-of-two scales a block's dequantized values may fit a smaller
+    # power (max code <= 3), so the scale bytes can change on requantizing,
+    # but every dequantized value is representable on the new grid: the
+    # values come back exactly
+    x16 = synth.lognormal_tokens(16, 512, synth.rng_for(9, 23), sigma=0.3)
+    y = O.rotate_f32(x16, 128)
+    amax = np.abs(y).max()
+    c, e, st = O.quant_nvfp4_rotated(y, amax, mx=2)
+    deq = O.dequant_nvfp4(c, e, st, 512)
+    c2, e2, st2 = O.quant_nvfp4_rotated(deq, amax, mx=2)
+    assert st2 == st
+    assert np.array_equal(O.dequant_nvfp4(c2, e2, st2, 512), deq)
+    assert np.all(e2 <= e)
+
+
+@pytest.mark.parametrize("mx", [0])
+def test_nvfp4_requantize_is_idempotent_on_normal_scales(mx):
     x16 = synth.lognormal_tokens(16, 512, synth.rng_for(9, 14), sigma=0.3)
     y = O.rotate_f32(x16, 128)
     amax = np.abs(y).max()
-    c, e, st = O.quant_nvfp4_rotated(y, amax)
+    c, e, st = O.quant_nvfp4_rotated(y, amax, mx=mx)
     deq = O.dequant_nvfp4(c, e, st, 512)
-    c2, e2, st2 = O.quant_nvfp4_rotated(deq, amax)
+    c2, e2, st2 = O.quant_nvfp4_rotated(deq, amax, mx=mx)
     normal = e >= 0x08
     assert normal.mean() > 0.99
     assert np.array_equal(e[normal], e2[normal])
