@@ -55,9 +55,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--blocks", type=int, default=42)
     ap.add_argument("--timesteps", type=int, default=3)
-    ap.add_argument("--fp4", choices=["nvfp4", "mx"], default="mx",
-                    help="NVFP4 recipe of the headline run: MX-compatible (FP4 MFMA, default) or "
-                         "plain (exact, bf16 MFMA); the schedule also times the other one")
+    ap.add_argument("--fp4", choices=["nvfp4", "mx", "p2"], default="mx",
+                    help="NVFP4 recipe of the headline run: MX-compatible (FP4 MFMA, default), "
+                         "plain (exact, bf16 MFMA) or a power of two per 16-block (FP4 MFMA, two "
+                         "passes); the schedule also times the other two")
     ap.add_argument("--config", type=int, default=5, help="5: schedule; 1-4: one linear layer")
     ap.add_argument("--delta", choices=["overlap", "inline"], default="overlap",
                     help="previous-step difference on a second stream ahead of each layer call "
@@ -128,13 +129,19 @@ def gemm_bytes(M, N, K, prec, fp4):
         a, b = M * K + 4 * M, N * K // 2 + 4 * N
     elif prec == "bf16":
         a, b = 2 * M * K, 2 * N * K
-    else:  # NVFP4: packed E2M1 + one scale byte per 16 (plain) or 32 (MX) elements
+    else:  # NVFP4: packed E2M1 + one scale byte per 16 elements (the MX kernel reads one per 32)
         g = 32 if fp4 == "mx" else 16
         a, b = M * K // 2 + M * K // g, N * K // 2 + N * K // g
     return a + b + 2 * M * N
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "schedule_hbm_traffic.txt")
+
+# NVFP4 recipes: the oracle's mx argument, the format, a description
+RECIPE_MX = {"nvfp4": 0, "mx": 1, "p2": 2}
+RECIPE_FMT = {"nvfp4": lambda h: h.FMT_NVFP4, "mx": lambda h: h.FMT_NVFP4_MX, "p2": lambda h: h.FMT_NVFP4_P2}
+RECIPE_NAME = {"mx": "MX-compatible (FP4 MFMA)", "nvfp4": "plain (bf16 MFMA)",
+               "p2": "power of two per 16-block (FP4 MFMA, two passes)"}
 
 
 # ------------------------------------------------------------------ copy
@@ -177,7 +184,7 @@ def build_schedule(args, hdq, synth):
     M = synth.M_COGVIDEOX
     gen = torch.Generator(device=dev)
     gen.manual_seed(0)
-    recipes = {"mx": hdq.FMT_NVFP4_MX, "nvfp4": hdq.FMT_NVFP4}
+    recipes = {"mx": hdq.FMT_NVFP4_MX, "nvfp4": hdq.FMT_NVFP4, "p2": hdq.FMT_NVFP4_P2}
     s_levels = synth.schedule_noise_levels(args.blocks, args.timesteps)
     blocks = []
     t0 = time.time()
@@ -367,7 +374,7 @@ def cpu_baseline_schedule(S, args, synth):
     M = S["M"]
     rows = np.r_[0:256, M - 112:M]  # first 256 rows and the ragged last 112
     R = len(rows)
-    fp4_mx = args.fp4 == "mx"
+    fp4_mx = RECIPE_MX[args.fp4]
     t_total = 0.0
     flops_total = 0.0
     for li, (name, K, N) in enumerate(synth.SCHEDULE_LAYERS):
@@ -459,7 +466,8 @@ def schedule_quality(S, hdq):
     out = {}
     for name, prec, W in (("bf16", hdq.PREC_BF16, L["W"]["mx"]), ("int8", hdq.PREC_INT8, L["W"]["mx"]),
                           ("nvfp4_mx", hdq.PREC_NVFP4, L["W"]["mx"]),
-                          ("nvfp4", hdq.PREC_NVFP4, L["W"]["nvfp4"])):
+                          ("nvfp4", hdq.PREC_NVFP4, L["W"]["nvfp4"]),
+                          ("nvfp4_p2", hdq.PREC_NVFP4, L["W"]["p2"])):
         y = hdq.linear(prec, x, W, y_dtype=hdq.DTYPE_F32)
         if ref is None:
             ref = y
@@ -475,8 +483,8 @@ def bench_schedule(args, hdq, synth):
     M = S["M"]
     flops_step = sum(2.0 * M * N * K for _, K, N in synth.SCHEDULE_LAYERS) * args.blocks * args.timesteps
     n_calls = args.timesteps * args.blocks * len(synth.SCHEDULE_LAYERS)
-    other = "nvfp4" if args.fp4 == "mx" else "mx"
-    runs = {r: time_schedule(S, args, hdq, synth, r) for r in (args.fp4, other)}
+    others = [r for r in ("mx", "nvfp4", "p2") if r != args.fp4]
+    runs = {r: time_schedule(S, args, hdq, synth, r) for r in [args.fp4] + others}
     ms_per_step, kt, decisions, source = runs[args.fp4]
     if args.decisions_out:
         with open(args.decisions_out, "w") as fh:
@@ -496,8 +504,14 @@ def bench_schedule(args, hdq, synth):
     # effective TOPS of the fused quant + linear alone (selected kernels only)
     ql_ms = q_ms + sum(kt.t.get(k, 0.0) for k in ("gemm_int8", "gemm_nvfp4", "gemm_bf16"))
     ql_flops = sum(kt.work.get(k, 0.0) for k in ("gemm_int8", "gemm_nvfp4", "gemm_bf16"))
-    o_ms, o_kt, _, _ = runs[other]
-    o_ks = o_kt.summary()
+    def other_line(r):
+        o_ms, o_kt, _, _ = runs[r]
+        o_ks = o_kt.summary()
+        g = o_ks.get("gemm_nvfp4")
+        return {"recipe": r, "value": round(flops_step / (o_ms * 1e-3) / 1e12, 2),
+                "ms_per_step": round(o_ms, 3),
+                "gemm_nvfp4": ({k: g[k] for k in ("launches", "total_ms", "avg_us")}
+                               | {"rate_tflops": round(g["rate"] / 1e12, 1)}) if g else None}
     result = {
         "metric": METRIC,
         "value": round(flops_step / (ms_per_step * 1e-3) / 1e12, 2),
@@ -505,12 +519,12 @@ def bench_schedule(args, hdq, synth):
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int8+nvfp4_mx" if args.fp4 == "mx" else "int8+nvfp4",
+        "dtype": {"mx": "int8+nvfp4_mx", "nvfp4": "int8+nvfp4", "p2": "int8+nvfp4_p2"}[args.fp4],
         "data": "synthetic",
         "config": {"workload": (f"DMPQ schedule: {args.blocks} CogVideoX-5B blocks x (QKV 3072->9216, "
                                 f"out 3072->3072, FFN 3072->12288->3072) x {args.timesteps} timesteps, "
                                 f"M=17776 tokens, Hadamard block 128, delta thresh 0.1, ratio thresh 50, "
-                                f"NVFP4 recipe {'MX-compatible (FP4 MFMA)' if args.fp4 == 'mx' else 'plain (bf16 MFMA)'}"),
+                                f"NVFP4 recipe {RECIPE_NAME[args.fp4]}"),
                    "global_batch": M, "layer_calls_per_step": n_calls},
         "roofline": roof,
         "quant_gbps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1) if q_ms > 0 else None,
@@ -525,12 +539,7 @@ def bench_schedule(args, hdq, synth):
                         "rate_unit": ("TB/s" if k.startswith(("quant", "select", "delta")) else
                                       "TOP/s" if k.startswith("gemm_int8") else "TFLOP/s")}
                     for k, v in ks.items()},
-        "other_recipe": {"recipe": other,
-                         "value": round(flops_step / (o_ms * 1e-3) / 1e12, 2),
-                         "ms_per_step": round(o_ms, 3),
-                         "gemm_nvfp4": {k: o_ks["gemm_nvfp4"][k] for k in ("launches", "total_ms", "avg_us")}
-                         | {"rate_tflops": round(o_ks["gemm_nvfp4"]["rate"] / 1e12, 1)}
-                         if "gemm_nvfp4" in o_ks else None},
+        "other_recipes": [other_line(r) for r in others],
         "quality_rel_err_vs_bf16": schedule_quality(S, hdq),
     }
     if not args.no_cpu_baseline:
@@ -545,7 +554,8 @@ def stored_traffic(kind, recipe):
     FETCH_SIZE/WRITE_SIZE summary, or None (absent, or the kernel changed
     since the counters were taken)."""
     from bit_quantized_video_amd import profsum
-    pkind = kind + "_mx" if recipe == "mx" and kind in ("gemm_nvfp4", "quant_nvfp4") else kind
+    suffix = {"mx": "_mx", "p2": "_p2"}.get(recipe, "")
+    pkind = kind + suffix if kind in ("gemm_nvfp4", "quant_nvfp4") else kind
     try:
         return profsum.current_traffic(TRAFFIC_PROFILE, pkind)
     except (OSError, KeyError):
@@ -558,7 +568,7 @@ def roofline_for(kind, k, recipe, copy_gbps=None):
     alg = round(k["bytes_per_launch"])
     if kind.startswith("gemm"):
         dt = {"gemm_int8": "int8", "gemm_bf16": "bf16",
-              "gemm_nvfp4": "fp4" if recipe == "mx" else "bf16"}[kind]
+              "gemm_nvfp4": "bf16" if recipe == "nvfp4" else "fp4"}[kind]
         peak = PEAK[dt]
         ach = k["rate"]
         return {"kernel": kind, "bound": "mfma", "dtype": dt, "achieved": round(ach / 1e12, 1),
@@ -586,7 +596,7 @@ def bench_single(args, hdq, synth):
     to_dev = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
     xd = to_dev(x16)
     path = c["paths"][0] if args.fp4 == "nvfp4" else ("nvfp4" if "nvfp4" in c["paths"] else "int8")
-    fmt = hdq.FMT_INT8_ROW if path == "int8" else (hdq.FMT_NVFP4_MX if args.fp4 == "mx" else hdq.FMT_NVFP4)
+    fmt = hdq.FMT_INT8_ROW if path == "int8" else RECIPE_FMT[args.fp4](hdq)
     W = hdq.LinearWeights(to_dev(w16), hb, fp4_fmt=None if path == "int8" else fmt)
     prec = hdq.PREC_INT8 if path == "int8" else hdq.PREC_NVFP4
     y_dtype = hdq.DTYPE_F32 if c["out"] == "f32" else hdq.DTYPE_BF16
@@ -614,7 +624,7 @@ def bench_single(args, hdq, synth):
     tg = np.mean([e[1].elapsed_time(e[2]) for e in evs])
     flops = 2.0 * M * N * K
     qb = quant_bytes(M, K, "int8" if path == "int8" else "nvfp4")
-    dt = "int8" if path == "int8" else ("fp4" if args.fp4 == "mx" else "bf16")
+    dt = "int8" if path == "int8" else ("bf16" if args.fp4 == "nvfp4" else "fp4")
     res = {"metric": METRIC, "value": round(flops / ((tq + tg) * 1e-3) / 1e12, 2), "unit": "TOPS",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(1e3 * elapsed / args.steps, 3), "higher_is_better": True,

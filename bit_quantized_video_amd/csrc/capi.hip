@@ -22,13 +22,25 @@ bool valid_block(int32_t hb) { return hb >= 2 && hb <= 128 && (hb & (hb - 1)) ==
 int check_quant_shape(int64_t rows, int64_t cols, int32_t hb, int32_t fmt) {
   if (rows <= 0 || cols <= 0 || rows > 0x7fffffff || !valid_block(hb)) return HDQ_ERR_SHAPE;
   if (cols % 8 != 0 || cols % hb != 0) return HDQ_ERR_SHAPE;
-  if (fmt == HDQ_FMT_NVFP4 && cols % 16 != 0) return HDQ_ERR_SHAPE;
+  if ((fmt == HDQ_FMT_NVFP4 || fmt == HDQ_FMT_NVFP4_P2) && cols % 16 != 0) return HDQ_ERR_SHAPE;
   if (fmt == HDQ_FMT_NVFP4_MX && cols % 32 != 0) return HDQ_ERR_SHAPE;
   return HDQ_OK;
 }
 
-bool valid_fmt(int32_t fmt) { return fmt >= HDQ_FMT_INT8_ROW && fmt <= HDQ_FMT_NVFP4_MX; }
-bool is_fp4(int32_t fmt) { return fmt == HDQ_FMT_NVFP4 || fmt == HDQ_FMT_NVFP4_MX; }
+bool valid_fmt(int32_t fmt) { return fmt >= HDQ_FMT_INT8_ROW && fmt <= HDQ_FMT_NVFP4_P2; }
+bool is_fp4(int32_t fmt) {
+  return fmt == HDQ_FMT_NVFP4 || fmt == HDQ_FMT_NVFP4_MX || fmt == HDQ_FMT_NVFP4_P2;
+}
+
+// The NVFP4 GEMM for the weights' format: FP4 MFMA (one pass per 32
+// elements for MX, two for per-16 powers of two) or exact bf16 MFMA.
+using Fp4Gemm = hipError_t (*)(const uint8_t*, const uint8_t*, const float*, const uint8_t*,
+                               const uint8_t*, const float*, void*, int, int64_t, int64_t, int64_t,
+                               const int32_t*, int32_t, hipStream_t);
+Fp4Gemm fp4_gemm_for(int32_t fmt) {
+  return fmt == HDQ_FMT_NVFP4_MX ? launch_gemm_nvfp4_mx
+       : fmt == HDQ_FMT_NVFP4_P2 ? launch_gemm_nvfp4_p2 : launch_gemm_nvfp4_bf16;
+}
 
 // Bytes of one quantized activation tensor [M, K] in `fmt` (codes and scales).
 size_t qtensor_bytes(int64_t M, int64_t K, int32_t fmt) {
@@ -232,7 +244,7 @@ int hdq_linear_dispatch(const int32_t* decision_dev, const void* x, const hdq_qt
       static_cast<const uint8_t*>(w->w_int4.codes), w->w_int4.row_scale,
       static_cast<const uint8_t*>(xq4->codes), xq4->blk_scale, xq4->tensor_scale,
       static_cast<const uint8_t*>(w->w_fp4.codes), w->w_fp4.blk_scale, w->w_fp4.tensor_scale,
-      f == HDQ_FMT_NVFP4_MX, xb, wb, y, y_dtype, M, N, K, s);
+      f, xb, wb, y, y_dtype, M, N, K, s);
   if (e == hipSuccess) return HDQ_OK;
   if (e != hipErrorNotSupported) return HDQ_ERR_HIP;
   // shapes the pipelined bodies do not take: the three gated GEMMs
@@ -240,7 +252,7 @@ int hdq_linear_dispatch(const int32_t* decision_dev, const void* x, const hdq_qt
                        static_cast<const uint8_t*>(w->w_int4.codes), w->w_int4.row_scale, y, y_dtype,
                        M, N, K, decision_dev, HDQ_PREC_INT8, s) != hipSuccess)
     return HDQ_ERR_HIP;
-  auto fp4 = f == HDQ_FMT_NVFP4_MX ? launch_gemm_nvfp4_mx : launch_gemm_nvfp4_bf16;
+  auto fp4 = fp4_gemm_for(f);
   if (fp4(static_cast<const uint8_t*>(xq4->codes), xq4->blk_scale, xq4->tensor_scale,
           static_cast<const uint8_t*>(w->w_fp4.codes), w->w_fp4.blk_scale, w->w_fp4.tensor_scale, y,
           y_dtype, M, N, K, decision_dev, HDQ_PREC_NVFP4, s) != hipSuccess)
@@ -375,12 +387,8 @@ int hdq_linear(int32_t precision, const int32_t* decision_dev, const void* x,
     }
     const uint8_t* xc = static_cast<const uint8_t*>(q.codes);
     const uint8_t* wc = static_cast<const uint8_t*>(w->w_fp4.codes);
-    if (f == HDQ_FMT_NVFP4_MX)
-      e = launch_gemm_nvfp4_mx(xc, q.blk_scale, q.tensor_scale, wc, w->w_fp4.blk_scale,
-                               w->w_fp4.tensor_scale, y, y_dtype, M, N, K, gate, HDQ_PREC_NVFP4, s);
-    else
-      e = launch_gemm_nvfp4_bf16(xc, q.blk_scale, q.tensor_scale, wc, w->w_fp4.blk_scale,
-                                 w->w_fp4.tensor_scale, y, y_dtype, M, N, K, gate, HDQ_PREC_NVFP4, s);
+    e = fp4_gemm_for(f)(xc, q.blk_scale, q.tensor_scale, wc, w->w_fp4.blk_scale, w->w_fp4.tensor_scale,
+                        y, y_dtype, M, N, K, gate, HDQ_PREC_NVFP4, s);
     if (e != hipSuccess) return HDQ_ERR_HIP;
   }
   if (run_bf16) {

@@ -175,23 +175,24 @@ __global__ __launch_bounds__(256) void k_gemm_fp4mx(
   }
 }
 
-// The gated kernel around the pipelined body (gemm_fp4_pipe.h).
-template <int OUT>
+// The gated kernel around the pipelined body (gemm_fp4_pipe.h); P2: the
+// two-pass form for a power-of-two scale per 16-block.
+template <int OUT, bool P2>
 __global__ __launch_bounds__(512) void k_gemm_fp4mx_pipe(
     const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xsc, const float* __restrict__ xts,
     const uint8_t* __restrict__ wc, const uint8_t* __restrict__ wsc, const float* __restrict__ wts,
     void* __restrict__ Y, int M, int N, int K, const int32_t* __restrict__ decision, int32_t want) {
   if (decision != nullptr && *decision != want) return;
-  gemm_fp4mx_pipe_body<OUT>(xc, xsc, xts, wc, wsc, wts, Y, M, N, K);
+  gemm_fp4mx_pipe_body<OUT, P2>(xc, xsc, xts, wc, wsc, wts, Y, M, N, K);
 }
 
-template <int OUT>
+template <int OUT, bool P2>
 static hipError_t launch_fp4_pipe(const uint8_t* xc, const uint8_t* xs, const float* xts,
                                   const uint8_t* wc, const uint8_t* ws, const float* wts, void* y,
                                   int64_t M, int64_t N, int64_t K, const int32_t* decision,
                                   int32_t want, hipStream_t s) {
-  constexpr size_t lds = 2 * (size_t)(256 * 128 * 2 + 512 * 8);
-  auto kern = k_gemm_fp4mx_pipe<OUT>;
+  constexpr size_t lds = (size_t)fp4_pipe_lds<P2>();
+  auto kern = k_gemm_fp4mx_pipe<OUT, P2>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -208,8 +209,8 @@ hipError_t launch_gemm_nvfp4_mx(const uint8_t* xc, const uint8_t* xs, const floa
   // The pipelined kernel needs K % 256 == 0 and 32-bit buffer offsets.
   if (K % 256 == 0 && M * K / 2 < (1ll << 31) && N * K / 2 < (1ll << 31)) {
     if (out_dtype == kOutF32)
-      return launch_fp4_pipe<kOutF32>(xc, xs, xts, wc, ws, wts, y, M, N, K, decision, want, s);
-    return launch_fp4_pipe<kOutBf16>(xc, xs, xts, wc, ws, wts, y, M, N, K, decision, want, s);
+      return launch_fp4_pipe<kOutF32, false>(xc, xs, xts, wc, ws, wts, y, M, N, K, decision, want, s);
+    return launch_fp4_pipe<kOutBf16, false>(xc, xs, xts, wc, ws, wts, y, M, N, K, decision, want, s);
   }
   constexpr int WM = 4, WN = 2;
   constexpr int BM = 64 * WM, BN = 64 * WN;
@@ -217,6 +218,21 @@ hipError_t launch_gemm_nvfp4_mx(const uint8_t* xc, const uint8_t* xs, const floa
   hipLaunchKernelGGL((k_gemm_fp4mx<WM, WN>), dim3((unsigned)tiles), dim3(256), 0, s, xc, xs, xts, wc,
                      ws, wts, y, out_dtype, (int)M, (int)N, (int)K, decision, want);
   return hipGetLastError();
+}
+
+// NVFP4 with a power-of-two scale per 16-block: the two-pass pipelined FP4
+// kernel, or (shapes it does not take) the exact bf16-MFMA kernel, which
+// takes any NVFP4 bytes.
+hipError_t launch_gemm_nvfp4_p2(const uint8_t* xc, const uint8_t* xs, const float* xts,
+                                const uint8_t* wc, const uint8_t* ws, const float* wts,
+                                void* y, int out_dtype, int64_t M, int64_t N, int64_t K,
+                                const int32_t* decision, int32_t want, hipStream_t s) {
+  if (K % 256 == 0 && M * K / 2 < (1ll << 31) && N * K / 2 < (1ll << 31)) {
+    if (out_dtype == kOutF32)
+      return launch_fp4_pipe<kOutF32, true>(xc, xs, xts, wc, ws, wts, y, M, N, K, decision, want, s);
+    return launch_fp4_pipe<kOutBf16, true>(xc, xs, xts, wc, ws, wts, y, M, N, K, decision, want, s);
+  }
+  return launch_gemm_nvfp4_bf16(xc, xs, xts, wc, ws, wts, y, out_dtype, M, N, K, decision, want, s);
 }
 
 }  // namespace hdq

@@ -28,6 +28,13 @@ __device__ __forceinline__ uint32_t e4m3_pow2_to_e8m0(uint32_t b) {
 // even E4M3 byte of each MX pair) stored as two words, [g0 g2 g4 g6] and
 // [g1 g3 g5 g7]: lane half h reads word h once per stage and substep s takes
 // its byte through the instruction's scale byte select.
+//
+// P2 (NVFP4 with a power-of-two scale per 16-block): each 32-group's two
+// 16-blocks have their own scales, so every MFMA runs twice, once with the
+// X fragment's second half zeroed and the first block's scales, once with
+// its first half zeroed and the second block's: exact, at twice the MFMA
+// work.  Per row and stage the 16 E8M0 bytes are stored as four words:
+// first blocks of lane half 0's and 1's groups, then their second blocks.
 struct Fp4PipeStage {
   uint4 x[4], w[4];  // codes: 4 x 16-byte chunks per operand per thread
   uint4 sc;          // the 16 E4M3 bytes of one X or W row (8 MX pairs)
@@ -38,14 +45,22 @@ __device__ __forceinline__ v16f mfma_fp4(const v8i& a, const v8i& b, const v16f&
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, KS, sa, KS, sb);
 }
 
-template <int OUT>
+// LDS bytes of the pipelined FP4 body: two stages of codes and E8M0 words.
+template <bool P2>
+constexpr int fp4_pipe_lds() {
+  return 2 * (256 * 128 * 2 + 512 * (P2 ? 16 : 8));
+}
+
+template <int OUT, bool P2 = false>
 __device__ __forceinline__ void gemm_fp4mx_pipe_body(
     const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xsc, const float* __restrict__ xts,
     const uint8_t* __restrict__ wc, const uint8_t* __restrict__ wsc, const float* __restrict__ wts,
     void* __restrict__ Y, int M, int N, int K) {
   constexpr int BM = 256, BN = 256, BK = 256, WM_T = 4, WN_T = 2;
   constexpr int XB = BM * BK / 2, WB = BN * BK / 2;  // code bytes per stage
-  constexpr int SB = XB + WB + (BM + BN) * 8;         // + E8M0 bytes
+  constexpr int SCB = P2 ? 16 : 8;                    // E8M0 bytes per row and stage
+  constexpr int SB = XB + WB + (BM + BN) * SCB;       // + E8M0 bytes
+  static_assert(2 * SB == fp4_pipe_lds<P2>(), "LDS size");
   constexpr int kOutPitch = BN * 2 + 16;              // bf16 output row staged in LDS
   static_assert(BM * kOutPitch <= 2 * SB, "output tile must fit the pipeline buffers");
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
@@ -65,7 +80,7 @@ __device__ __forceinline__ void gemm_fp4mx_pipe_body(
   // scales: waves 0-3 take the 256 X rows, waves 4-7 the 256 W rows
   const int sw_ = __builtin_amdgcn_readfirstlane(tid >> 8), srow = tid & 255;
   const uint32_t svoff = (uint32_t)(srow * lds_);
-  const int sdst = XB + WB + sw_ * BM * 8 + srow * 8;
+  const int sdst = XB + WB + sw_ * BM * SCB + srow * SCB;
 
   int l_logical = seq.first, l_kt = 0;
   __amdgpu_buffer_rsrc_t xres, wres, sres;
@@ -99,15 +114,23 @@ __device__ __forceinline__ void gemm_fp4mx_pipe_body(
       *reinterpret_cast<uint4*>(base + cdst + p * 64 * 128) = st.x[p];
       *reinterpret_cast<uint4*>(base + XB + cdst + p * 64 * 128) = st.w[p];
     }
-    // E8M0 of group g comes from E4M3 byte 2g; word h holds g = h, h+2, h+4, h+6
+    // E8M0 of group g comes from E4M3 byte 2g (P2: and 2g + 1); word h holds
+    // g = h, h+2, h+4, h+6
     const uint32_t d[4] = {st.sc.x, st.sc.y, st.sc.z, st.sc.w};
-    uint32_t w0 = 0u, w1 = 0u;
+    uint32_t w0 = 0u, w1 = 0u, w2 = 0u, w3 = 0u;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       w0 |= e4m3_pow2_to_e8m0(d[q] & 0xffu) << (8 * q);
       w1 |= e4m3_pow2_to_e8m0((d[q] >> 16) & 0xffu) << (8 * q);
+      if constexpr (P2) {
+        w2 |= e4m3_pow2_to_e8m0((d[q] >> 8) & 0xffu) << (8 * q);
+        w3 |= e4m3_pow2_to_e8m0(d[q] >> 24) << (8 * q);
+      }
     }
-    *reinterpret_cast<uint2*>(base + sdst) = make_uint2(w0, w1);
+    if constexpr (P2)
+      *reinterpret_cast<uint4*>(base + sdst) = make_uint4(w0, w1, w2, w3);
+    else
+      *reinterpret_cast<uint2*>(base + sdst) = make_uint2(w0, w1);
   };
 
   v16f acc[WN_T][WM_T];
@@ -126,34 +149,61 @@ __device__ __forceinline__ void gemm_fp4mx_pipe_body(
     const uint8_t* lx = smem + buf * SB;
     const uint8_t* lw = lx + XB;
     const uint8_t* lxs = lx + XB + WB;
-    const uint8_t* lws = lxs + BM * 8;
-    int xe[WM_T], we[WN_T];
+    const uint8_t* lws = lxs + BM * SCB;
+    int xe[WM_T], we[WN_T], xo[WM_T], wo[WN_T];  // xo, wo: the second blocks' (P2)
 #pragma unroll
-    for (int i = 0; i < WM_T; ++i)
-      xe[i] = *reinterpret_cast<const int*>(lxs + (wm * WM_T * 32 + i * 32 + r32) * 8 + 4 * h);
+    for (int i = 0; i < WM_T; ++i) {
+      const uint8_t* p = lxs + (wm * WM_T * 32 + i * 32 + r32) * SCB + 4 * h;
+      xe[i] = *reinterpret_cast<const int*>(p);
+      if constexpr (P2) xo[i] = *reinterpret_cast<const int*>(p + 8);
+    }
 #pragma unroll
-    for (int j = 0; j < WN_T; ++j)
-      we[j] = *reinterpret_cast<const int*>(lws + (wn * WN_T * 32 + j * 32 + r32) * 8 + 4 * h);
+    for (int j = 0; j < WN_T; ++j) {
+      const uint8_t* p = lws + (wn * WN_T * 32 + j * 32 + r32) * SCB + 4 * h;
+      we[j] = *reinterpret_cast<const int*>(p);
+      if constexpr (P2) wo[j] = *reinterpret_cast<const int*>(p + 8);
+    }
     auto substep = [&](auto ksc) {
       constexpr int ks = decltype(ksc)::value;
       const int g = 2 * ks + h;  // this lane's 32-K group within the stage
-      v8i xf[WM_T], wf[WN_T];
+      auto load_w = [&](v8i (&wf)[WN_T]) {
 #pragma unroll
-      for (int i = 0; i < WM_T; ++i) {
-        const int r = wm * WM_T * 32 + i * 32 + r32;
-        const v4i v = *reinterpret_cast<const v4i*>(lx + r * 128 + 16 * (g ^ swz128(r)));
-        xf[i] = v8i{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+        for (int j = 0; j < WN_T; ++j) {
+          const int r = wn * WN_T * 32 + j * 32 + r32;
+          const v4i v = *reinterpret_cast<const v4i*>(lw + r * 128 + 16 * (g ^ swz128(r)));
+          wf[j] = v8i{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+        }
+      };
+      v8i wf[WN_T];
+      if constexpr (P2) {
+        // one X fragment at a time: its two halves are two operands
+        load_w(wf);
+#pragma unroll
+        for (int i = 0; i < WM_T; ++i) {
+          const int r = wm * WM_T * 32 + i * 32 + r32;
+          const v4i v = *reinterpret_cast<const v4i*>(lx + r * 128 + 16 * (g ^ swz128(r)));
+          const v8i xf = v8i{v[0], v[1], 0, 0, 0, 0, 0, 0};
+          const v8i xg = v8i{0, 0, v[2], v[3], 0, 0, 0, 0};
+#pragma unroll
+          for (int j = 0; j < WN_T; ++j) {
+            acc[j][i] = mfma_fp4<ks>(wf[j], xf, acc[j][i], we[j], xe[i]);
+            acc[j][i] = mfma_fp4<ks>(wf[j], xg, acc[j][i], wo[j], xo[i]);
+          }
+        }
+      } else {
+        v8i xf[WM_T];
+#pragma unroll
+        for (int i = 0; i < WM_T; ++i) {
+          const int r = wm * WM_T * 32 + i * 32 + r32;
+          const v4i v = *reinterpret_cast<const v4i*>(lx + r * 128 + 16 * (g ^ swz128(r)));
+          xf[i] = v8i{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+        }
+        load_w(wf);
+#pragma unroll
+        for (int j = 0; j < WN_T; ++j)
+#pragma unroll
+          for (int i = 0; i < WM_T; ++i) acc[j][i] = mfma_fp4<ks>(wf[j], xf[i], acc[j][i], we[j], xe[i]);
       }
-#pragma unroll
-      for (int j = 0; j < WN_T; ++j) {
-        const int r = wn * WN_T * 32 + j * 32 + r32;
-        const v4i v = *reinterpret_cast<const v4i*>(lw + r * 128 + 16 * (g ^ swz128(r)));
-        wf[j] = v8i{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int j = 0; j < WN_T; ++j)
-#pragma unroll
-        for (int i = 0; i < WM_T; ++i) acc[j][i] = mfma_fp4<ks>(wf[j], xf[i], acc[j][i], we[j], xe[i]);
     };
     substep(std::integral_constant<int, 0>{});
     substep(std::integral_constant<int, 1>{});

@@ -11,7 +11,7 @@
 
 namespace hdq {
 
-enum QFmt : int { kInt8Row = 0, kInt4Row = 1, kNvfp4 = 2, kNvfp4Mx = 3 };
+enum QFmt : int { kInt8Row = 0, kInt4Row = 1, kNvfp4 = 2, kNvfp4Mx = 3, kNvfp4P2 = 4 };
 enum Prec : int { kPrecNvfp4 = 0, kPrecInt8 = 1, kPrecBf16 = 2 };
 enum OutDtype : int { kOutF32 = 0, kOutBf16 = 1, kOutI32 = 2 };
 
@@ -80,6 +80,11 @@ hipError_t launch_gemm_nvfp4_mx(const uint8_t* xc, const uint8_t* xs, const floa
                                 const uint8_t* wc, const uint8_t* ws, const float* wts,
                                 void* y, int out_dtype, int64_t M, int64_t N, int64_t K,
                                 const int32_t* decision, int32_t want, hipStream_t s);
+// NVFP4 with a power-of-two scale per 16-block: the FP4 MFMA in two passes.
+hipError_t launch_gemm_nvfp4_p2(const uint8_t* xc, const uint8_t* xs, const float* xts,
+                                const uint8_t* wc, const uint8_t* ws, const float* wts,
+                                void* y, int out_dtype, int64_t M, int64_t N, int64_t K,
+                                const int32_t* decision, int32_t want, hipStream_t s);
 // One launch running the GEMM the device decision names (INT8, NVFP4 -- on
 // the FP4 MFMA when fp4_mx, else decoded to bf16 -- or bf16); every path's
 // operands must be given.  hipErrorNotSupported when a shape does not fit
@@ -87,7 +92,7 @@ hipError_t launch_gemm_nvfp4_mx(const uint8_t* xc, const uint8_t* xs, const floa
 hipError_t launch_gemm_dispatch(const int32_t* decision, const int8_t* x8, const float* sx,
                                 const uint8_t* w4, const float* sw, const uint8_t* xc,
                                 const uint8_t* xsc, const float* xts, const uint8_t* wc,
-                                const uint8_t* wsc, const float* wts, bool fp4_mx,
+                                const uint8_t* wsc, const float* wts, int fp4_fmt,
                                 const uint16_t* xb, const uint16_t* wb, void* y, int out_dtype,
                                 int64_t M, int64_t N, int64_t K, hipStream_t s);
 // bf16 x bf16 (full-precision fallback).

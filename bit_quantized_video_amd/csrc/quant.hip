@@ -14,7 +14,8 @@
 //    first code, so one workgroup owns one row and keeps it in registers
 //    (CPT 8-element chunks per thread).
 //  * k_quant_nvfp4: NVFP4 needs only the tensor amax (given) and a 16- or
-//    32-element block max, so it is a flat grid-stride kernel with no
+//    32-element block max (E4M3 scale per 16, or a power of two per 16 or
+//    per 32), so it is a flat grid-stride kernel with no
 //    workgroup synchronisation; each wave owns 128 consecutive chunks per
 //    iteration (two per lane, loads issued first).
 #include "hdq_device.h"
@@ -303,7 +304,9 @@ hipError_t launch_quant_int_rows(const uint16_t* x, int64_t rows, int64_t cols, 
 
 // Quantizes one 8-element chunk held by this lane (already rotated and
 // scaled); returns its 4 code bytes and sets *e to its 16-block's scale byte.
-template <bool MX>
+// FMT: kNvfp4 (E4M3 scale per 16), kNvfp4Mx (a power of two per aligned
+// pair of 16-blocks), kNvfp4P2 (a power of two per 16-block).
+template <int FMT>
 __device__ __forceinline__ uint32_t nvfp4_chunk(float (&v)[8], float s_t, float six_st, uint32_t* e_out) {
   float a = 0.0f;
 #pragma unroll
@@ -312,12 +315,12 @@ __device__ __forceinline__ uint32_t nvfp4_chunk(float (&v)[8], float s_t, float 
   // of a 32-element group on l ^ {0, 1, 2, 3} (fwht_chunk keeps chunk bits
   // 0 and 1 on lane bits 0 and 1)
   a = fmaxf(a, xor_lane<1>(a));
-  if constexpr (MX) a = fmaxf(a, xor_lane<2>(a));
+  if constexpr (FMT == kNvfp4Mx) a = fmaxf(a, xor_lane<2>(a));
   uint32_t e = 0u;
   float d = 0.0f;
   if (s_t > 0.0f) {
     const float t = a / six_st;
-    e = MX ? e4m3_encode(pow2_ceil_clamped(t)) : e4m3_encode(t);
+    e = FMT == kNvfp4 ? e4m3_encode(t) : e4m3_encode(pow2_ceil_clamped(t));
     d = e4m3_decode(e) * s_t;
   }
   *e_out = e;
@@ -331,7 +334,7 @@ __device__ __forceinline__ uint32_t nvfp4_chunk(float (&v)[8], float s_t, float 
 // covers UNROLL x 64 consecutive chunks, so every Hadamard block (<= 128)
 // and every 16- or 32-element scale block lies inside aligned lane groups of
 // one wave.
-template <bool MX>
+template <int FMT>
 __global__ __launch_bounds__(256) void k_quant_nvfp4(
     const uint16_t* __restrict__ x, int64_t nch, int hb, float c_b,
     const float* __restrict__ amax_ptr, uint8_t* __restrict__ codes,
@@ -342,9 +345,9 @@ __global__ __launch_bounds__(256) void k_quant_nvfp4(
   const int lane = threadIdx.x & 63;
   const float A = *amax_ptr;
   // s_t = amax / (6 * 448) for NVFP4 (the largest block maps to E4M3's top
-  // value), amax / (6 * 256) for the MX-compatible variant (the largest
-  // power-of-two block scale is 2^8).
-  const float s_t = (A >= kTiny) ? A / (MX ? 1536.0f : 2688.0f) : 0.0f;
+  // value), amax / (6 * 256) with power-of-two block scales (the largest is
+  // 2^8).
+  const float s_t = (A >= kTiny) ? A / (FMT == kNvfp4 ? 2688.0f : 1536.0f) : 0.0f;
   if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = s_t;
   const float six_st = 6.0f * s_t;
   const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
@@ -368,7 +371,7 @@ __global__ __launch_bounds__(256) void k_quant_nvfp4(
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = v[i] * sc;
       uint32_t e;
-      const uint32_t packed = nvfp4_chunk<MX>(v, s_t, six_st, &e);
+      const uint32_t packed = nvfp4_chunk<FMT>(v, s_t, six_st, &e);
       if (idx < nch) {
         cv[idx] = packed;
         // the lane with the even chunk of the 16-element block writes its scale
@@ -390,12 +393,10 @@ hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t rows, int64_t cols, int
   if (blocks > 2048) blocks = 2048;
   if (blocks < 1) blocks = 1;
   const float c_b = hadamard_scale(hb);
-  if (fmt == kNvfp4Mx)
-    hipLaunchKernelGGL(k_quant_nvfp4<true>, dim3((unsigned)blocks), dim3(256), 0, s, x, nch, hb, c_b,
-                       amax, codes, blk_scale, tensor_scale, decision, want);
-  else
-    hipLaunchKernelGGL(k_quant_nvfp4<false>, dim3((unsigned)blocks), dim3(256), 0, s, x, nch, hb,
-                       c_b, amax, codes, blk_scale, tensor_scale, decision, want);
+  auto kern = fmt == kNvfp4Mx ? k_quant_nvfp4<kNvfp4Mx>
+             : fmt == kNvfp4P2 ? k_quant_nvfp4<kNvfp4P2> : k_quant_nvfp4<kNvfp4>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, s, x, nch, hb, c_b, amax, codes,
+                     blk_scale, tensor_scale, decision, want);
   return hipGetLastError();
 }
 

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libhdq.so")
 # status codes
 OK, ERR_INVALID, ERR_SHAPE, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, -1, -2, -3, -4, -5
 # formats
-FMT_INT8_ROW, FMT_INT4_ROW, FMT_NVFP4, FMT_NVFP4_MX = 0, 1, 2, 3
+FMT_INT8_ROW, FMT_INT4_ROW, FMT_NVFP4, FMT_NVFP4_MX, FMT_NVFP4_P2 = 0, 1, 2, 3, 4
 # precisions
 PREC_NVFP4, PREC_INT8, PREC_BF16 = 0, 1, 2
 # output dtypes

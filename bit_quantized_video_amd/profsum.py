@@ -49,10 +49,12 @@ KINDS = OrderedDict([
     ("select_final", r"k_stats_final"),
     ("select_quant_int8", r"k_quant_int_rows<\d+, \d+, false, true>"),
     ("quant_int8", r"k_quant_int_rows(_long)?<\d+, \d+, false(, false)?>"),
-    ("quant_nvfp4_mx", r"k_quant_nvfp4<true>"),
-    ("quant_nvfp4", r"k_quant_nvfp4<false>"),
+    ("quant_nvfp4_mx", r"k_quant_nvfp4<3>"),
+    ("quant_nvfp4_p2", r"k_quant_nvfp4<4>"),
+    ("quant_nvfp4", r"k_quant_nvfp4<2>"),
     ("gemm_int8", r"k_gemm_i8i4(_pipe)?<[\d, ]*1>"),
-    ("gemm_nvfp4_mx", r"k_gemm_fp4mx(_pipe)?<1>"),
+    ("gemm_nvfp4_mx", r"k_gemm_fp4mx_pipe<1, false>"),
+    ("gemm_nvfp4_p2", r"k_gemm_fp4mx_pipe<1, true>"),
     ("gemm_nvfp4", r"k_gemm_bf16(_pipe|mfma)<1, 1>"),
     ("gemm_bf16", r"k_gemm_bf16(_pipe|mfma)<0, 1>"),
 ])
@@ -61,16 +63,21 @@ SOURCES = {
     "delta_sums": ["stats.hip"], "select_stats": ["stats.hip"], "select_final": ["stats.hip"],
     "select_final_rows": ["stats.hip"],
     "quant_int8": ["quant.hip"], "quant_nvfp4_mx": ["quant.hip"], "quant_nvfp4": ["quant.hip"],
+    "quant_nvfp4_p2": ["quant.hip"],
     "select_quant_int8": ["quant.hip", "stats.hip"],
     "gemm_int8": ["gemm_i8.hip", "gemm_i8_pipe.h", "gemm_dispatch.hip"],
     "gemm_nvfp4_mx": ["gemm_fp4.hip", "gemm_fp4_pipe.h", "gemm_dispatch.hip"],
+    "gemm_nvfp4_p2": ["gemm_fp4.hip", "gemm_fp4_pipe.h", "gemm_dispatch.hip"],
     "gemm_nvfp4": ["gemm_bf16.hip", "gemm_bf16_pipe.h", "gemm_dispatch.hip"],
     "gemm_bf16": ["gemm_bf16.hip", "gemm_bf16_pipe.h", "gemm_dispatch.hip"],
     "gemm_dispatch": ["gemm_dispatch.hip", "gemm_i8_pipe.h", "gemm_fp4_pipe.h", "gemm_bf16_pipe.h"],
 }
 # One-launch GEMMs (bf16 output) that run the decided precision: the kind
-# comes from the decision of the layer call (DECISIONS, in call order).
-DISPATCH = r"k_gemm_dispatch<1, (true|false)>"
+# comes from the decision of the layer call (DECISIONS, in call order); the
+# second template argument is the NVFP4 weights' format (2 plain, 3 MX, 4
+# per-16 powers of two).
+DISPATCH = r"k_gemm_dispatch<1, ([234])>"
+FP4_KIND = {"2": "gemm_nvfp4", "3": "gemm_nvfp4_mx", "4": "gemm_nvfp4_p2"}
 DECISIONS = None
 
 
@@ -94,11 +101,11 @@ class Classifier:
             return classify(name)
         if not DECISIONS:
             return "gemm_dispatch"
-        mx = m.group(1) == "true"
-        i = self.seen.get(mx, 0)
-        self.seen[mx] = i + 1
+        fmt = m.group(1)
+        i = self.seen.get(fmt, 0)
+        self.seen[fmt] = i + 1
         d = DECISIONS[i % len(DECISIONS)]
-        return {1: "gemm_int8", 0: "gemm_nvfp4_mx" if mx else "gemm_nvfp4", 2: "gemm_bf16"}[d]
+        return {1: "gemm_int8", 0: FP4_KIND[fmt], 2: "gemm_bf16"}[d]
 COMMON_SOURCES = ["hdq_device.h", "hdq_internal.h", "../build.py"]
 WEIGHT_PREP = r"k_quant_int_rows(_long)?<\d+, \d+, true(, false)?>"
 # A launch that did work: longer than this (trace; gated-off launches take a

@@ -81,6 +81,12 @@ extern "C" {
  * fits the pair): a valid NVFP4 tensor that is also MXFP4-shaped, so the
  * GEMM runs on gfx950's block-scaled FP4 matrix instructions. */
 #define HDQ_FMT_NVFP4_MX 3
+/* NVFP4 bytes restricted so that every aligned 16-block's scale is a power
+ * of two (its own: s_t = amax / 1536, scale = smallest power of two that
+ * fits the block): valid NVFP4, computed exactly on the block-scaled FP4
+ * matrix instructions in two passes per 32 elements (one per 16-block half),
+ * so at up to half the MX recipe's rate. */
+#define HDQ_FMT_NVFP4_P2 4
 
 /* ---- precisions (decisions) ---- */
 #define HDQ_PREC_NVFP4 0

@@ -101,6 +101,8 @@ def test_validation_happens_before_any_launch(hdq):
     assert L.hdq_quantize(fake, 4, 64, 256, 0, None, None, ctypes.byref(q), None, 0, None) == hdq.ERR_SHAPE
     assert L.hdq_quantize(fake, 4, 72, 16, 0, None, None, ctypes.byref(q), None, 0, None) == hdq.ERR_SHAPE
     assert L.hdq_quantize(fake, 4, 48, 16, hdq.FMT_NVFP4_MX, None, None, ctypes.byref(q), None, 0, None) == hdq.ERR_SHAPE
+    assert L.hdq_quantize(fake, 4, 72, 8, hdq.FMT_NVFP4_P2, None, None, ctypes.byref(q), None, 0, None) == hdq.ERR_SHAPE
+    assert L.hdq_quantize(fake, 4, 64, 16, hdq.FMT_NVFP4_P2 + 1, None, None, ctypes.byref(q), None, 0, None) == hdq.ERR_INVALID
     assert L.hdq_quantize(fake, 4, 64, 16, hdq.FMT_NVFP4, None, None, ctypes.byref(q), None, 0, None) == hdq.ERR_WORKSPACE
     q0 = hdq.QTensorDesc(0, 0, 0, 0, None, fake, fake, fake)
     assert L.hdq_quantize(fake, 4, 64, 16, 0, None, None, ctypes.byref(q0), None, 0, None) == hdq.ERR_INVALID

@@ -139,14 +139,18 @@ def test_quantize_int_zero_and_tiny_rows():
 NV_CASES = [(1, 64, 16), (37, 128, 32), (130, 1024, 64), (301, 3072, 128), (5, 12288, 128)]
 
 
+# NVFP4 recipes: the oracle's mx argument for each format
+FP4_FMTS = {hdq.FMT_NVFP4: 0, hdq.FMT_NVFP4_MX: 1, hdq.FMT_NVFP4_P2: 2}
+
+
 @pytest.mark.parametrize("M,K,hb", NV_CASES)
-@pytest.mark.parametrize("mx", [False, True])
+@pytest.mark.parametrize("fmt", list(FP4_FMTS))
 @pytest.mark.parametrize("amax_given", [False, True])
-def test_quantize_nvfp4_bitexact(M, K, hb, mx, amax_given):
-    say(f"quantize nvfp4 mx={mx} M={M} K={K} hb={hb} amax_given={amax_given}")
+def test_quantize_nvfp4_bitexact(M, K, hb, fmt, amax_given):
+    mx = FP4_FMTS[fmt]
+    say(f"quantize nvfp4 fmt={fmt} M={M} K={K} hb={hb} amax_given={amax_given}")
     x16 = synth.lognormal_tokens(M, K, synth.rng_for(101, M * 7 + K))
     amax = O.rotated_amax(x16, hb)
-    fmt = hdq.FMT_NVFP4_MX if mx else hdq.FMT_NVFP4
     am = torch.tensor([amax], dtype=torch.float32, device=DEV) if amax_given else None
     q = hdq.quantize(to_dev(x16), hb, fmt, tensor_amax=am)
     torch.cuda.synchronize()
@@ -348,6 +352,23 @@ def test_bf16_gemm_multi_tile_workgroups(K):
     assert rel_fro(y_np(y)[MT_ROWS], ref) <= REL_TOL
 
 
+@pytest.mark.parametrize("fmt", [hdq.FMT_NVFP4_MX, hdq.FMT_NVFP4_P2])
+@pytest.mark.parametrize("K", [256, 768])
+def test_fp4_gemm_multi_tile_workgroups(fmt, K):
+    say(f"fp4 gemm f32 multi-tile fmt={fmt} M={MT_M} N={MT_N} K={K}")
+    hb = 32
+    x16 = synth.lognormal_tokens(MT_M, K, synth.rng_for(105, K))
+    w16 = synth.gaussian(MT_N, K, 0.02, synth.rng_for(106, K))
+    W = hdq.LinearWeights(to_dev(w16), hb, fp4_fmt=fmt)
+    y = hdq.linear(hdq.PREC_NVFP4, to_dev(x16), W, y_dtype=hdq.DTYPE_F32)
+    torch.cuda.synchronize()
+    mx = FP4_FMTS[fmt]
+    ac, ae, ast = O.quant_nvfp4(x16[MT_ROWS], hb, amax=O.rotated_amax(x16, hb), mx=mx)
+    wc, we, wst = O.quant_nvfp4(w16, hb, mx=mx)
+    ref = round_like(O.gemm_nvfp4(ac, ae, ast, wc, we, wst, K), hdq.DTYPE_F32)
+    assert rel_fro(y_np(y)[MT_ROWS], ref) <= REL_TOL
+
+
 @pytest.mark.parametrize("M,N,K", GEMM_CASES[1:])
 @pytest.mark.parametrize("y_dtype", [hdq.DTYPE_F32, hdq.DTYPE_BF16])
 def test_linear_int8_matches_oracle(M, N, K, y_dtype):
@@ -366,15 +387,16 @@ def test_linear_int8_matches_oracle(M, N, K, y_dtype):
     assert np.array_equal(got, ref)      # same float32 epilogue order: exact
 
 
-@pytest.mark.parametrize("M,N,K", [(37, 19, 64), (300, 200, 96), (257, 129, 1024), (64, 640, 3072)])
-@pytest.mark.parametrize("mx", [False, True])
+@pytest.mark.parametrize("M,N,K", [(37, 19, 64), (300, 200, 96), (257, 129, 1024), (64, 640, 3072),
+                                   (600, 520, 768)])
+@pytest.mark.parametrize("fmt", list(FP4_FMTS))
 @pytest.mark.parametrize("y_dtype", [hdq.DTYPE_F32, hdq.DTYPE_BF16])
-def test_linear_nvfp4_matches_oracle(M, N, K, mx, y_dtype):
-    say(f"linear nvfp4 mx={mx} M={M} N={N} K={K} y={y_dtype}")
+def test_linear_nvfp4_matches_oracle(M, N, K, fmt, y_dtype):
+    mx = FP4_FMTS[fmt]
+    say(f"linear nvfp4 fmt={fmt} M={M} N={N} K={K} y={y_dtype}")
     hb = 32
     x16 = synth.lognormal_tokens(M, K, synth.rng_for(105, M + N))
     w16 = synth.gaussian(N, K, 0.02, synth.rng_for(106, M + N))
-    fmt = hdq.FMT_NVFP4_MX if mx else hdq.FMT_NVFP4
     W = hdq.LinearWeights(to_dev(w16), hb, fp4_fmt=fmt)
     y = hdq.linear(hdq.PREC_NVFP4, to_dev(x16), W, y_dtype=y_dtype)
     torch.cuda.synchronize()
@@ -384,14 +406,15 @@ def test_linear_nvfp4_matches_oracle(M, N, K, mx, y_dtype):
     assert rel_fro(y_np(y), ref) <= REL_TOL
 
 
-def test_nvfp4_exact_kernel_accepts_mx_bytes():
-    # MX-compatible bytes are valid NVFP4: the exact (bf16-MFMA) kernel on
-    # them must agree with the block-scaled FP4 kernel
+@pytest.mark.parametrize("fmt", [hdq.FMT_NVFP4_MX, hdq.FMT_NVFP4_P2])
+def test_nvfp4_exact_kernel_accepts_mx_bytes(fmt):
+    # MX-compatible and per-16 power-of-two bytes are valid NVFP4: the exact
+    # (bf16-MFMA) kernel on them must agree with the block-scaled FP4 kernel
     M, N, K, hb = 200, 160, 512, 64
     x16 = synth.lognormal_tokens(M, K, synth.rng_for(107, 1))
     w16 = synth.gaussian(N, K, 0.02, synth.rng_for(107, 2))
-    Wmx = hdq.LinearWeights(to_dev(w16), hb, fp4_fmt=hdq.FMT_NVFP4_MX)
-    xq = hdq.quantize(to_dev(x16), hb, hdq.FMT_NVFP4_MX)
+    Wmx = hdq.LinearWeights(to_dev(w16), hb, fp4_fmt=fmt)
+    xq = hdq.quantize(to_dev(x16), hb, fmt)
     y_mx = hdq.linear(hdq.PREC_NVFP4, None, Wmx, xq=xq, y_dtype=hdq.DTYPE_F32)
     Wmx.w_fp4.fmt = hdq.FMT_NVFP4
     xq.fmt = hdq.FMT_NVFP4
@@ -441,7 +464,7 @@ def test_device_predicated_linear_matches_fixed(case):
 
 
 @pytest.mark.parametrize("M,N,K", [(300, 384, 512), (1000, 600, 1024), (37, 19, 96), (17776, 3072, 3072)])
-@pytest.mark.parametrize("fmt", ["nvfp4", "nvfp4_mx"])
+@pytest.mark.parametrize("fmt", ["nvfp4", "nvfp4_mx", "nvfp4_p2"])
 @pytest.mark.parametrize("y_dtype", [hdq.DTYPE_BF16, hdq.DTYPE_F32])
 def test_linear_dispatch_matches_fixed_precision(M, N, K, fmt, y_dtype):
     """hdq_linear_dispatch runs the decided precision's GEMM (one launch, or
@@ -453,7 +476,7 @@ def test_linear_dispatch_matches_fixed_precision(M, N, K, fmt, y_dtype):
     hb = 32
     x16 = synth.lognormal_tokens(M, K, synth.rng_for(114, M + N))
     w16 = synth.gaussian(N, K, 0.02, synth.rng_for(114, K))
-    f = hdq.FMT_NVFP4_MX if fmt == "nvfp4_mx" else hdq.FMT_NVFP4
+    f = {"nvfp4": hdq.FMT_NVFP4, "nvfp4_mx": hdq.FMT_NVFP4_MX, "nvfp4_p2": hdq.FMT_NVFP4_P2}[fmt]
     W = hdq.LinearWeights(to_dev(w16), hb, fp4_fmt=f)
     xd = to_dev(x16)
     xq8 = hdq.quantize(xd, hb, hdq.FMT_INT8_ROW)
@@ -476,7 +499,7 @@ def test_repeat_runs_are_bitwise_identical():
     x16 = synth.lognormal_tokens(M, K, synth.rng_for(111, 0))
     w16 = synth.gaussian(N, K, 0.02, synth.rng_for(111, 1))
     xd = to_dev(x16)
-    for fmt in (hdq.FMT_NVFP4, hdq.FMT_NVFP4_MX):
+    for fmt in FP4_FMTS:
         W = hdq.LinearWeights(to_dev(w16), hb, fp4_fmt=fmt)
         for prec in (hdq.PREC_INT8, hdq.PREC_NVFP4, hdq.PREC_BF16):
             a = hdq.linear(prec, xd, W, y_dtype=hdq.DTYPE_F32)
@@ -498,7 +521,8 @@ def run_config(cfg, path, n_cols=384):
     x16 = synth.config_activations(cfg)
     w16 = synth.config_weights(cfg)
     y_dtype = hdq.DTYPE_F32 if c["out"] == "f32" else hdq.DTYPE_BF16
-    fmt = {"int8": None, "nvfp4": hdq.FMT_NVFP4, "nvfp4_mx": hdq.FMT_NVFP4_MX}[path]
+    fmt = {"int8": None, "nvfp4": hdq.FMT_NVFP4, "nvfp4_mx": hdq.FMT_NVFP4_MX,
+           "nvfp4_p2": hdq.FMT_NVFP4_P2}[path]
     W = hdq.LinearWeights(to_dev(w16), hb, fp4_fmt=fmt)
     xd = to_dev(x16)
     prec = hdq.PREC_INT8 if path == "int8" else hdq.PREC_NVFP4
@@ -522,7 +546,7 @@ def run_config(cfg, path, n_cols=384):
         assert np.array_equal(gq.row_scale.cpu().numpy()[rows], sa)
         assert_codes_equal(gq.codes.cpu().numpy()[rows], qa, "codes")
     else:
-        mx = path == "nvfp4_mx"
+        mx = FP4_FMTS[fmt]
         amax = O.rotated_amax(x16, hb)          # tensor amax over all rows
         wamax = O.rotated_amax(w16, hb)
         ac, ae, ast = O.quant_nvfp4(xs, hb, amax=amax, mx=mx)
@@ -537,8 +561,9 @@ def run_config(cfg, path, n_cols=384):
         assert np.array_equal(got, ref)
 
 
-@pytest.mark.parametrize("cfg,path", [(1, "int8"), (1, "nvfp4"), (1, "nvfp4_mx"), (2, "int8"),
-                                      (3, "nvfp4"), (3, "nvfp4_mx"), (4, "int8")])
+@pytest.mark.parametrize("cfg,path", [(1, "int8"), (1, "nvfp4"), (1, "nvfp4_mx"), (1, "nvfp4_p2"),
+                                      (2, "int8"), (3, "nvfp4"), (3, "nvfp4_mx"), (3, "nvfp4_p2"),
+                                      (4, "int8")])
 def test_config_full_size_sampled(cfg, path):
     run_config(cfg, path)
 

@@ -15,11 +15,13 @@ def test_classify_kernel_names():
         "void hdq::k_quant_int_rows<256, 6, true, false>(int)": None,
         "void hdq::k_quant_int_rows<128, 3, false, false>(int)": "quant_int8",
         "void hdq::k_quant_int_rows<128, 3, false, true>(int)": "select_quant_int8",
-        "void hdq::k_quant_nvfp4<true>(int)": "quant_nvfp4_mx",
-        "void hdq::k_quant_nvfp4<false>(int)": "quant_nvfp4",
+        "void hdq::k_quant_nvfp4<3>(int)": "quant_nvfp4_mx",
+        "void hdq::k_quant_nvfp4<4>(int)": "quant_nvfp4_p2",
+        "void hdq::k_quant_nvfp4<2>(int)": "quant_nvfp4",
         "void hdq::k_gemm_i8i4_pipe<2, 4, 4, 2, 1>(int)": "gemm_int8",
         "void hdq::k_gemm_i8i4_pipe<2, 4, 4, 2, 0>(int)": None,  # f32 output: quality check
-        "void hdq::k_gemm_fp4mx_pipe<1>(int)": "gemm_nvfp4_mx",
+        "void hdq::k_gemm_fp4mx_pipe<1, false>(int)": "gemm_nvfp4_mx",
+        "void hdq::k_gemm_fp4mx_pipe<1, true>(int)": "gemm_nvfp4_p2",
         "void hdq::k_gemm_bf16_pipe<1, 1>(int)": "gemm_nvfp4",
         "void hdq::k_gemm_bf16_pipe<0, 1>(int)": "gemm_bf16",
         "__amd_rocclr_copyBuffer": None,
@@ -49,12 +51,12 @@ def test_one_launch_gemms_take_their_calls_decisions():
     P.DECISIONS = [1, 0, 2, 1]
     try:
         c = P.Classifier()
-        mx = "void hdq::k_gemm_dispatch<1, true>(int const*)"
-        plain = "void hdq::k_gemm_dispatch<1, false>(int const*)"
+        mx = "void hdq::k_gemm_dispatch<1, 3>(int const*)"
+        plain = "void hdq::k_gemm_dispatch<1, 2>(int const*)"
         got = [c(mx) for _ in range(5)] + [c(plain) for _ in range(3)]
         assert got == ["gemm_int8", "gemm_nvfp4_mx", "gemm_bf16", "gemm_int8", "gemm_int8",
                        "gemm_int8", "gemm_nvfp4", "gemm_bf16"]
-        assert c("void hdq::k_gemm_dispatch<0, true>(int const*)") is None  # f32 output: not the schedule
+        assert c("void hdq::k_gemm_dispatch<0, 3>(int const*)") is None  # f32 output: not the schedule
     finally:
         P.DECISIONS = None
-    assert P.Classifier()("void hdq::k_gemm_dispatch<1, true>(int const*)") == "gemm_dispatch"
+    assert P.Classifier()("void hdq::k_gemm_dispatch<1, 3>(int const*)") == "gemm_dispatch"
