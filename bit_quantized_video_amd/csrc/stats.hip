@@ -342,4 +342,46 @@ hipError_t launch_stats_finalize_rows(const double* psum, const uint32_t* pbits,
   return hipGetLastError();
 }
 
+// ---------------------------------------------------- temporal delta cache
+
+// The temporal delta cache's skip rule (summary on vetunion.cn, section
+// two; gist.science explainer, section three), one thread per module: a
+// module computed at this step (state 1: no earlier output; 2: with one,
+// sums = {sum|new - earlier|, sum|earlier|}) resets its accumulator and
+// takes a new relative change c; every module then reuses its cache at the
+// next step when c < tau_skip and fl32(acc + c) <= tau_acc, adding c to acc.
+__global__ __launch_bounds__(256) void k_tdc_decide(const double* __restrict__ sums,
+                                                    const int32_t* __restrict__ state,
+                                                    float* __restrict__ c, float* __restrict__ acc,
+                                                    int32_t* __restrict__ skip, int n, float tau_skip,
+                                                    float tau_acc) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
+    const int st = state[i];
+    float ci = c[i], ai = acc[i];
+    if (st != 0) {
+      ai = 0.0f;
+      if (st == 1) {
+        ci = __builtin_nanf("");
+      } else {
+        const double diff = sums[2 * i], base = sums[2 * i + 1];
+        ci = (float)(base == 0.0 ? (diff == 0.0 ? 0.0 : __builtin_inf()) : diff / base);
+      }
+    }
+    const float next = ai + ci;
+    const bool s = ci < tau_skip && next <= tau_acc;
+    c[i] = ci;
+    acc[i] = s ? next : ai;
+    skip[i] = s ? 1 : 0;
+  }
+}
+
+hipError_t launch_tdc_decide(const double* sums, const int32_t* state, float* c, float* acc,
+                             int32_t* skip, int64_t n, float tau_skip, float tau_acc, hipStream_t s) {
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(k_tdc_decide, dim3((unsigned)blocks), dim3(256), 0, s, sums, state, c, acc, skip,
+                     (int)n, tau_skip, tau_acc);
+  return hipGetLastError();
+}
+
 }  // namespace hdq

@@ -27,7 +27,7 @@ DTYPE_F32, DTYPE_BF16, DTYPE_I32 = 0, 1, 2
 OP_SELECT, OP_QUANTIZE, OP_LINEAR, OP_SELECT_Q8 = 0, 1, 2, 3
 
 EXPORTS = ("hdq_select_precision", "hdq_delta_sums", "hdq_select_precision_sums",
-           "hdq_select_quantize_int8", "hdq_linear_dispatch", "hdq_quantize",
+           "hdq_select_quantize_int8", "hdq_linear_dispatch", "hdq_tdc_decide", "hdq_quantize",
            "hdq_linear", "hdq_workspace_bytes",
            "hdq_status_string", "hdq_version")
 
@@ -67,6 +67,8 @@ def _load():
     L.hdq_linear_dispatch.restype = _c.c_int
     L.hdq_linear_dispatch.argtypes = [_p, _p, _c.POINTER(QTensorDesc), _c.POINTER(QTensorDesc),
                                       _c.c_int64, _c.c_int64, _c.POINTER(WeightsDesc), _p, _c.c_int32, _p]
+    L.hdq_tdc_decide.restype = _c.c_int
+    L.hdq_tdc_decide.argtypes = [_p, _p, _p, _p, _p, _c.c_int64, _c.c_float, _c.c_float, _p]
     L.hdq_quantize.restype = _c.c_int
     L.hdq_quantize.argtypes = [_p, _c.c_int64, _c.c_int64, _c.c_int32, _c.c_int32, _p, _p,
                                _c.POINTER(QTensorDesc), _p, _c.c_size_t, _p]
@@ -200,6 +202,21 @@ def delta_sums(prev_in, prev_out, sums=None, ws=None, stream=None):
                             _stream(stream))
     _check("hdq_delta_sums", st)
     return sums
+
+
+def tdc_decide(sums, state, c, acc, skip=None, tau_skip=0.05, tau_acc=0.15, stream=None):
+    """hdq_tdc_decide over n modules: sums float64 [n, 2], state int32 [n],
+    c and acc float32 [n] (updated in place); returns skip int32 [n]."""
+    n = state.numel()
+    for t, dt, shape in ((sums, torch.float64, (n, 2)), (state, torch.int32, (n,)),
+                         (c, torch.float32, (n,)), (acc, torch.float32, (n,))):
+        if t.dtype != dt or tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"tdc_decide: expected {dt} {shape} contiguous, got {t.dtype} {tuple(t.shape)}")
+    skip = torch.empty(n, dtype=torch.int32, device=state.device) if skip is None else skip
+    st = lib.hdq_tdc_decide(_ptr(sums), _ptr(state), _ptr(c), _ptr(acc), _ptr(skip), n,
+                            float(tau_skip), float(tau_acc), _stream(stream))
+    _check("hdq_tdc_decide", st)
+    return skip
 
 
 def select_precision_sums(delta_sums, cur_in, had_block=0, delta_thresh=0.1, ratio_thresh=50.0,

@@ -289,6 +289,33 @@ int hdq_linear_dispatch(const int32_t *decision_dev, const void *x, const hdq_qt
                         const hdq_qtensor *xq4, int64_t M, int64_t K, const hdq_weights *w,
                         void *y, int32_t y_dtype, void *stream);
 
+/*
+ * hdq_tdc_decide -- the temporal delta cache's skip rule (summary on
+ * vetunion.cn, section two; gist.science explainer, section three), for n
+ * modules at once, once per diffusion step.  A module whose output changed
+ * little between its last two computed steps reuses its cached output at
+ * the next step; an accumulator adds the predicted change of every skipped
+ * step and forces a computation once it would pass its budget.
+ *   sums_dev : device double [n][2]; for a module computed at this step
+ *              with an earlier output, {sum|new - earlier|, sum|earlier|}
+ *              (hdq_delta_sums(earlier, new, ...) writes exactly this);
+ *              ignored otherwise.
+ *   state_dev: device int32 [n]: 0 skipped at this step, 1 computed with no
+ *              earlier output, 2 computed with one (sums valid).
+ *   c_dev    : device float [n], in/out: relative change between the last
+ *              two computed outputs (NaN: none yet); rewritten when state
+ *              is 1 (NaN) or 2 (diff / base in double, then float; base 0
+ *              gives 0 if diff is 0, else +inf).
+ *   acc_dev  : device float [n], in/out: reset to 0 when state != 0.
+ *   skip_dev : device int32 [n] <- 1 when the next step reuses the cache:
+ *              c < tau_skip and fl32(acc + c) <= tau_acc (NaN is false);
+ *              acc then becomes fl32(acc + c).
+ * Errors: HDQ_ERR_INVALID for a null pointer, HDQ_ERR_SHAPE for n <= 0 or
+ * n >= 2^31.  The state arrays are the caller's; one call per step.
+ */
+int hdq_tdc_decide(const double *sums_dev, const int32_t *state_dev, float *c_dev, float *acc_dev,
+                   int32_t *skip_dev, int64_t n, float tau_skip, float tau_acc, void *stream);
+
 /* Scratch bytes an entry point needs.  op = HDQ_OP_SELECT: (M = rows,
  * K = cols, N = prev_numel); HDQ_OP_SELECT_Q8: (M = rows, K = cols);
  * HDQ_OP_QUANTIZE: (M = rows, K = cols, fmt);

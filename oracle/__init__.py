@@ -55,6 +55,7 @@ def lib():
             "orc_gemm_bf16": (None, [_p, _p, _i64, _i64, _i64, _p]),
             "orc_stats": (None, [_p, _p, _i64, _p, _i64, _i64, _int, _p]),
             "orc_decide": (_int, [_int, _f64, _f64, _f64, _f64]),
+            "orc_tdc_decide": (None, [_p, _p, _p, _p, _p, _i64, _f32, _f32]),
             "orc_num_threads": (_int, []),
         }
         for name, (res, args) in sig.items():
@@ -289,3 +290,21 @@ def stats(prev_in16, prev_out16, cur16, b):
 def decide(has_history, delta, ratio, delta_thresh=0.1, ratio_thresh=50.0):
     return lib().orc_decide(int(bool(has_history)), float(delta), float(ratio),
                             float(np.float32(delta_thresh)), float(np.float32(ratio_thresh)))
+
+
+# ---------------------------------------------- temporal delta cache
+
+def tdc_decide(sums, state, c, acc, tau_skip=0.05, tau_acc=0.15):
+    """One step of the TDC skip rule over n modules (see orc_tdc_decide).
+    sums float64 [n, 2], state int32 [n] (0 skipped, 1 computed first, 2
+    computed with a previous output), c and acc float32 [n] (updated in
+    place).  Returns skip int32 [n] for the next step."""
+    sums = _c(sums, np.float64)
+    state = _c(state, np.int32)
+    assert c.dtype == np.float32 and acc.dtype == np.float32 and c.flags.c_contiguous
+    n = state.size
+    skip = np.zeros(n, np.int32)
+    lib().orc_tdc_decide(_ptr(sums), _ptr(state), _ptr(c), _ptr(acc), _ptr(skip), n,
+                         float(np.float32(tau_skip)), float(np.float32(tau_acc)))
+    return skip
+

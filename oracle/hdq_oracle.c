@@ -541,6 +541,47 @@ int orc_decide(int has_history, double delta, double ratio, double delta_thresh,
     return 0;
 }
 
+/* ----------------------------------------- temporal delta cache (TDC) */
+
+/* Skip decision of the temporal delta cache [S2, G3], per module, once per
+ * diffusion step.  A module whose output changed little between its last
+ * two computed steps is predicted to change little again: the next step
+ * reuses the cached output instead of computing.  An accumulator adds the
+ * predicted change of every skipped step and forces a computation once the
+ * sum would pass its budget; a computation resets it.
+ *   state[i]: 0 the module was skipped at this step; 1 computed, with no
+ *             earlier output to compare with; 2 computed, sums[2i] =
+ *             sum |new - previous output|, sums[2i + 1] = sum |previous|.
+ *   c[i]    : float32, relative change between the last two computed
+ *             outputs (NaN: none yet); updated when state is 1 or 2.
+ *   acc[i]  : float32 accumulator, reset to 0 on a computation.
+ *   skip[i] : 1 when the next step reuses the cache:
+ *             c < tau_skip and fl32(acc + c) <= tau_acc (NaN compares
+ *             false); then acc = fl32(acc + c).
+ * c = diff / base in double, rounded to float32; base == 0 gives 0 when
+ * diff == 0, else +inf (the same conventions as the difference statistic). */
+void orc_tdc_decide(const double *sums, const int32_t *state, float *c, float *acc,
+                    int32_t *skip, int64_t n, float tau_skip, float tau_acc)
+{
+    for (int64_t i = 0; i < n; i++) {
+        if (state[i] != 0) {
+            acc[i] = 0.0f;
+            if (state[i] == 1) {
+                c[i] = NAN;
+            } else {
+                double diff = sums[2 * i], base = sums[2 * i + 1];
+                double r = (base == 0.0) ? ((diff == 0.0) ? 0.0 : INFINITY) : diff / base;
+                c[i] = (float)r;
+            }
+        }
+        float next = acc[i] + c[i];
+        int s = (c[i] < tau_skip) && (next <= tau_acc);
+        if (s)
+            acc[i] = next;
+        skip[i] = s;
+    }
+}
+
 #ifdef _OPENMP
 #include <omp.h>
 #endif

@@ -655,3 +655,85 @@ def test_schedule_layer_calls_match_oracle(layer):
         assert err <= REL_TOL
         if dec == hdq.PREC_INT8:
             assert np.array_equal(got, r)
+
+
+# ------------------------------------------------- temporal delta cache
+
+def test_tdc_decide_matches_oracle():
+    say("tdc decide random states")
+    rng = np.random.default_rng(120)
+    n = 5000
+    state = rng.integers(0, 3, n).astype(np.int32)
+    base = rng.uniform(0.0, 10.0, n)
+    base[rng.random(n) < 0.05] = 0.0
+    diff = base * rng.uniform(0.0, 0.12, n)
+    diff[rng.random(n) < 0.05] = 0.0
+    diff[(base == 0) & (rng.random(n) < 0.5)] = 1.0
+    sums = np.stack([diff, base], axis=1)
+    c = rng.uniform(0.0, 0.1, n).astype(np.float32)
+    c[rng.random(n) < 0.1] = np.nan
+    acc = rng.uniform(0.0, 0.15, n).astype(np.float32)
+    gc, gacc = torch.from_numpy(c.copy()).to(DEV), torch.from_numpy(acc.copy()).to(DEV)
+    skip = hdq.tdc_decide(torch.from_numpy(sums).to(DEV), torch.from_numpy(state).to(DEV), gc, gacc)
+    torch.cuda.synchronize()
+    ref = O.tdc_decide(sums, state, c, acc)
+    assert np.array_equal(skip.cpu().numpy(), ref)
+    assert np.array_equal(gc.cpu().numpy().view(np.uint32), c.view(np.uint32))
+    assert np.array_equal(gacc.cpu().numpy().view(np.uint32), acc.view(np.uint32))
+    assert 0.1 < ref.mean() < 0.9
+
+
+def test_tdc_trajectory_matches_oracle():
+    """Three linear modules over a trajectory whose input changes shrink step
+    by step: computed modules run the INT8 linear, the change statistic of
+    each new output against the earlier one comes from hdq_delta_sums, and
+    the GPU rule's skip pattern, c and acc equal the oracle rule's on the
+    same sums; the sums themselves equal the oracle's relative L1 change."""
+    say("tdc trajectory")
+    M, K, N, hb, T = 300, 256, 192, 64, 14
+    mods = []
+    for m in range(3):
+        rng = synth.rng_for(121, m)
+        x0 = rng.standard_normal((M, K)).astype(np.float32)
+        d = rng.standard_normal((M, K)).astype(np.float32)
+        w16 = synth.gaussian(N, K, 0.02, synth.rng_for(122, m))
+        mods.append(dict(x0=x0, d=d, W=hdq.LinearWeights(to_dev(w16), hb, fp4_fmt=None), y=None))
+    n = len(mods)
+    gc = torch.full((n,), float("nan"), dtype=torch.float32, device=DEV)
+    gacc = torch.zeros(n, dtype=torch.float32, device=DEV)
+    c = np.full(n, np.nan, np.float32)
+    acc = np.zeros(n, np.float32)
+    skip = np.zeros(n, np.int32)
+    a = 0.0
+    skips = 0
+    for t in range(T):
+        a += 0.3 * 0.6 ** t                      # the input moves less every step
+        sums = np.zeros((n, 2), np.float64)
+        gsums = torch.zeros((n, 2), dtype=torch.float64, device=DEV)
+        state = np.zeros(n, np.int32)
+        for i, md in enumerate(mods):
+            if skip[i]:
+                skips += 1
+                continue
+            x16 = synth.to_bf16_bits(md["x0"] + np.float32(a) * md["d"])
+            y = hdq.linear(hdq.PREC_INT8, to_dev(x16), md["W"], y_dtype=hdq.DTYPE_BF16)
+            if md["y"] is None:
+                state[i] = 1
+            else:
+                state[i] = 2
+                hdq.delta_sums(md["y"], y, sums=gsums[i])
+                torch.cuda.synchronize()
+                y_old = md["y"].view(torch.int16).cpu().numpy().view(np.uint16)
+                y_new = y.view(torch.int16).cpu().numpy().view(np.uint16)
+                o = O.stats(y_old, y_new, y_new, 0)[0]
+                g = gsums[i].cpu().numpy()
+                assert abs(g[0] / g[1] - o) <= 1e-12 * max(o, 1e-30), (t, i)
+                sums[i] = g
+            md["y"] = y
+        gskip = hdq.tdc_decide(gsums, torch.from_numpy(state).to(DEV), gc, gacc)
+        skip = O.tdc_decide(sums, state, c, acc)
+        torch.cuda.synchronize()
+        assert np.array_equal(gskip.cpu().numpy(), skip), t
+        assert np.array_equal(gc.cpu().numpy().view(np.uint32), c.view(np.uint32)), t
+        assert np.array_equal(gacc.cpu().numpy().view(np.uint32), acc.view(np.uint32)), t
+    assert skips > 0            # the smoothing trajectory does reuse the cache

@@ -521,3 +521,75 @@ def test_nvfp4_requantize_is_idempotent_on_normal_scales(mx):
     assert np.array_equal(e[normal], e2[normal])
     nb = np.repeat(normal, 8, axis=1)        # 8 code bytes per 16-block
     assert np.array_equal(c[nb], c2[nb])
+
+
+# ------------------------------------------- temporal delta cache rule
+
+def tdc_run(changes, tau_skip=0.05, tau_acc=0.15):
+    """Drives one module through the TDC rule: changes[t] is the relative
+    change its output would show if computed at step t (as diff / base with
+    base = 1).  Returns the list of steps computed."""
+    c = np.zeros(1, np.float32)
+    acc = np.zeros(1, np.float32)
+    skip = np.zeros(1, np.int32)
+    computed = []
+    first = True
+    for t, ch in enumerate(changes):
+        if skip[0]:
+            state = 0
+        else:
+            computed.append(t)
+            state = 1 if first else 2
+            first = False
+        skip = O.tdc_decide(np.array([[ch, 1.0]]), np.array([state], np.int32), c, acc,
+                            tau_skip, tau_acc)
+    return computed
+
+
+def test_tdc_constant_change_gives_periodic_skips():
+    # c = 2^-6 per computed step, budget 0.1: the accumulator grows by 2^-6 per
+    # skipped step, so floor(0.1 / 2^-6) = 6 skips follow each computation (all
+    # sums exact in float32); the first step computes and has no history, the
+    # second computes to get one
+    comp = tdc_run([2.0 ** -6] * 30, tau_skip=0.05, tau_acc=0.1)
+    assert comp == [0, 1, 8, 15, 22, 29]
+    # budgets that are exact multiples: k = tau_acc / c skips per period
+    for k_log, tau in ((-5, 0.25), (-4, 0.5), (-7, 2.0 ** -4)):
+        c = 2.0 ** k_log
+        k = int(tau / c)
+        comp = tdc_run([c] * 40, tau_skip=1.0, tau_acc=tau)
+        gaps = np.diff(comp[1:])
+        assert np.all(gaps == k + 1), (k_log, tau, comp)
+
+
+def test_tdc_large_change_never_skips_and_edge_cases():
+    assert tdc_run([0.2] * 10) == list(range(10))            # above tau_skip
+    assert tdc_run([0.05] * 10) == list(range(10))           # at tau_skip: compute
+    c = np.full(4, np.nan, np.float32)
+    acc = np.zeros(4, np.float32)
+    sums = np.array([[0.0, 0.0], [1.0, 0.0], [0.0, 4.0], [1.0, 64.0]])
+    skip = O.tdc_decide(sums, np.array([2, 2, 2, 1], np.int32), c, acc, 0.05, 0.15)
+    # 0/0 -> 0 (skip), x/0 -> +inf (compute), 0/4 -> 0 (skip), first output -> NaN
+    assert skip.tolist() == [1, 0, 1, 0]
+    assert c[0] == 0 and np.isinf(c[1]) and c[2] == 0 and np.isnan(c[3])
+    # a skipped module keeps c and grows acc; a computed one resets acc
+    c = np.array([0.04], np.float32)
+    acc = np.array([0.1], np.float32)
+    skip = O.tdc_decide(np.zeros((1, 2)), np.array([0], np.int32), c, acc, 0.05, 0.15)
+    assert skip[0] == 1 and acc[0] == np.float32(np.float32(0.1) + np.float32(0.04))
+    skip = O.tdc_decide(np.zeros((1, 2)), np.array([0], np.int32), c, acc, 0.05, 0.15)
+    assert skip[0] == 0 and acc[0] == np.float32(np.float32(0.1) + np.float32(0.04))
+    skip = O.tdc_decide(np.array([[3.0, 100.0]]), np.array([2], np.int32), c, acc, 0.05, 0.15)
+    assert skip[0] == 1 and c[0] == np.float32(0.03) and acc[0] == np.float32(0.03)
+
+
+def test_tdc_shrinking_changes_skip_more_later():
+    # a trajectory that smooths out (changes halving every 3 steps): later
+    # steps skip more, and the accumulator bounds the run of skips
+    changes = [0.2 * 0.5 ** (t / 3) for t in range(40)]
+    comp = tdc_run(changes, tau_skip=0.05, tau_acc=0.15)
+    first_half = sum(1 for t in comp if t < 20)
+    second_half = sum(1 for t in comp if t >= 20)
+    assert first_half > second_half
+    assert comp[:7] == list(range(7))                         # changes >= 0.05 at first
+
