@@ -77,6 +77,11 @@ def parse():
                          "(default; the other kernels are timed in one instrumented step after the timed "
                          "ones), or around every kernel (each event record adds a marker to the stream, "
                          "which costs the step several percent)")
+    ap.add_argument("--tdc-steps", type=int, default=12,
+                    help="steps of the temporal-delta-cache trajectory measured after the schedule "
+                         "(0: none)")
+    ap.add_argument("--tdc-blocks", type=int, default=8,
+                    help="blocks (x 4 linear modules) in the temporal-delta-cache trajectory")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decisions-out", help="write the per-call precision decisions (call order) as JSON, "
                                             "for attributing one-launch GEMMs in profiles")
@@ -457,6 +462,117 @@ def time_schedule(S, args, hdq, synth, recipe):
     return 1e3 * elapsed / args.steps, kt, decisions, source
 
 
+TDC_TAU_SKIP, TDC_TAU_ACC = 0.05, 0.15
+
+
+def tdc_trajectory(S, args, hdq, synth, recipe, use_tdc, dirs):
+    """One synthetic denoising trajectory over the first args.tdc_blocks
+    blocks' modules.  Module input at step t: x + a_t * d (d a fixed seeded
+    direction, increments a_t - a_(t-1) = 0.3 * 0.6^t, so the trajectory
+    smooths out).  A computed module runs the DMPQ path of the schedule
+    (selection fused with INT8 quantization -- history: the schedule's
+    difference sums when the module ran at the previous step, none after a
+    skip -- the gated NVFP4 quantizer and the one-launch GEMM) into a fresh
+    output buffer.  With use_tdc, the change of each new output against the
+    module's cached one (hdq_delta_sums) and the skip rule (hdq_tdc_decide,
+    once per step for all modules, read back with one synchronization) decide
+    which modules the next step skips.  HIP events time the hot path (input
+    formation excluded); returns per-step milliseconds and skip counts."""
+    dev = torch.device("cuda:0")
+    M = S["M"]
+    mods = [(b, li) for b in range(args.tdc_blocks) for li in range(len(synth.SCHEDULE_LAYERS))]
+    n = len(mods)
+    ybuf = [[torch.empty(M, synth.SCHEDULE_LAYERS[li][2], dtype=torch.bfloat16, device=dev)
+             for _ in range(2)] for _, li in mods]
+    cur = [None] * n                      # index of the cached output buffer
+    ran_prev = [False] * n
+    sums = torch.zeros((n, 2), dtype=torch.float64, device=dev)
+    state = torch.zeros(n, dtype=torch.int32, device=dev)
+    c = torch.full((n,), float("nan"), dtype=torch.float32, device=dev)
+    acc = torch.zeros(n, dtype=torch.float32, device=dev)
+    skip = torch.zeros(n, dtype=torch.int32, device=dev)
+    skip_h = [0] * n
+    dec_t = torch.zeros((n, 1), dtype=torch.int32, device=dev)
+    sts_t = torch.zeros((n, 5), dtype=torch.float32, device=dev)
+    xin = {li: torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+           for li, (_, K, _) in enumerate(synth.SCHEDULE_LAYERS)}
+    per_step, skips, change_ms, decide_ms = [], [], [], []
+    a = 0.0
+    for t in range(args.tdc_steps):
+        a += 0.3 * 0.6 ** t
+        evs = []
+        state_h = [0] * n
+        for i, (b, li) in enumerate(mods):
+            if use_tdc and skip_h[i]:
+                ran_prev[i] = False
+                continue
+            L = S["blocks"][b][li]
+            sh = S["shared"][li]
+            torch.add(L["x"], dirs[i], alpha=a, out=xin[li])
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record()
+            hist = S["sums"][min(t, args.timesteps - 1), b, li] if ran_prev[i] else None
+            d, st = dec_t[i], sts_t[i]
+            hdq.select_quantize_int8(hist, xin[li], HB, DELTA_T, RATIO_T, decision=d, stats=st,
+                                     out=sh["xq8"], ws=S["ws_sq8"])
+            hdq.quantize(xin[li], HB, S["recipes"][recipe], tensor_amax=st[4:5], out=sh["xq4"][recipe],
+                         decision=d)
+            new = 0 if cur[i] is None else 1 - cur[i]
+            hdq.linear_dispatch(d, xin[li], sh["xq8"], sh["xq4"][recipe], L["W"][recipe], y=ybuf[i][new])
+            e[1].record()
+            if use_tdc:
+                if cur[i] is None:
+                    state_h[i] = 1
+                else:
+                    state_h[i] = 2
+                    hdq.delta_sums(ybuf[i][cur[i]], ybuf[i][new], sums=sums[i], ws=S["ws_delta"])
+            e[2].record()
+            evs.append(e)
+            cur[i] = new
+            ran_prev[i] = True
+        ed = None
+        if use_tdc:
+            state.copy_(torch.tensor(state_h, dtype=torch.int32))
+            ed = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ed[0].record()
+            hdq.tdc_decide(sums, state, c, acc, skip=skip, tau_skip=TDC_TAU_SKIP, tau_acc=TDC_TAU_ACC)
+            ed[1].record()
+            skip_h = skip.tolist()        # one synchronization per step
+        torch.cuda.synchronize()
+        path = sum(e[0].elapsed_time(e[1]) for e in evs)
+        chg = sum(e[1].elapsed_time(e[2]) for e in evs)
+        dec = ed[0].elapsed_time(ed[1]) if ed else 0.0
+        per_step.append(path + chg + dec)
+        change_ms.append(chg / max(1, len(evs)))
+        decide_ms.append(dec)
+        skips.append(n - len(evs))
+    return per_step, skips, change_ms, decide_ms
+
+
+def bench_tdc(S, args, hdq, synth):
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    n_mod = args.tdc_blocks * len(synth.SCHEDULE_LAYERS)
+    dirs = [synth.device_gaussian(S["blocks"][b][li]["x"].shape, 1.0, gen, dev)
+            for b in range(args.tdc_blocks) for li in range(len(synth.SCHEDULE_LAYERS))]
+    log(f"tdc trajectory: {n_mod} modules x {args.tdc_steps} steps")
+    full = tdc_trajectory(S, args, hdq, synth, args.fp4, False, dirs)
+    tdc = tdc_trajectory(S, args, hdq, synth, args.fp4, True, dirs)
+    del dirs
+    torch.cuda.empty_cache()
+    ms_full, ms_tdc = float(np.mean(full[0])), float(np.mean(tdc[0]))
+    return {"modules": n_mod, "steps": args.tdc_steps, "tau_skip": TDC_TAU_SKIP, "tau_acc": TDC_TAU_ACC,
+            "skip_fraction": round(sum(tdc[1]) / (n_mod * args.tdc_steps), 4),
+            "skips_per_step": tdc[1],
+            "ms_per_step_full": round(ms_full, 3), "ms_per_step_tdc": round(ms_tdc, 3),
+            "speedup": round(ms_full / ms_tdc, 3),
+            "change_stat_us_avg": round(1e3 * float(np.mean([v for v in tdc[2] if v > 0] or [0])), 2),
+            "decide_us_avg": round(1e3 * float(np.mean(tdc[3])), 2),
+            "input": "x + a_t d per module, a_t - a_(t-1) = 0.3 * 0.6^t; hot path timed with HIP "
+                     "events (input formation excluded)"}
+
+
 def schedule_quality(S, hdq):
     """Output error of each precision on one NVFP4-sized layer (block 0 FFN
     up-projection): relative Frobenius distance of the bf16 output from the
@@ -542,6 +658,8 @@ def bench_schedule(args, hdq, synth):
         "other_recipes": [other_line(r) for r in others],
         "quality_rel_err_vs_bf16": schedule_quality(S, hdq),
     }
+    if args.tdc_steps > 0:
+        result["tdc"] = bench_tdc(S, args, hdq, synth)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline_schedule(S, args, synth)
