@@ -154,7 +154,11 @@ __device__ __forceinline__ void gemm_i8i4_pipe_body(
       uint8_t* const lrow = smem + rl0 * kOutPitch + 2 * nl0;
 #pragma unroll
       for (int i = 0; i < WM_T; ++i) {
-        const float sxm = __builtin_bit_cast(
+        // acc = 16 * (the exact integer sum) and float(acc) is 16 times its
+        // float, so float(acc) * (s_x / 16) is the same real product as
+        // float(acc >> 4) * s_x: the same float, without the shifts (s_x / 16
+        // is exact: s_x is 0 or at least 2^-107)
+        const float sxm = 0.0625f * __builtin_bit_cast(
             float, __builtin_amdgcn_raw_buffer_load_b32(sxres, 4 * (rl0 + i * 32), 4 * m0, 0));
 #pragma unroll
         for (int j = 0; j < WN_T; ++j) {
@@ -162,10 +166,10 @@ __device__ __forceinline__ void gemm_i8i4_pipe_body(
           for (int g = 0; g < 4; ++g) {
             const float4 swn = __builtin_bit_cast(
                 float4, __builtin_amdgcn_raw_buffer_load_b128(swres, 4 * (nl0 + j * 32 + 8 * g), 4 * n0, 0));
-            const float y0 = ((float)(acc[j][i][4 * g + 0] >> 4) * sxm) * swn.x;
-            const float y1 = ((float)(acc[j][i][4 * g + 1] >> 4) * sxm) * swn.y;
-            const float y2 = ((float)(acc[j][i][4 * g + 2] >> 4) * sxm) * swn.z;
-            const float y3 = ((float)(acc[j][i][4 * g + 3] >> 4) * sxm) * swn.w;
+            const float y0 = ((float)acc[j][i][4 * g + 0] * sxm) * swn.x;
+            const float y1 = ((float)acc[j][i][4 * g + 1] * sxm) * swn.y;
+            const float y2 = ((float)acc[j][i][4 * g + 2] * sxm) * swn.z;
+            const float y3 = ((float)acc[j][i][4 * g + 3] * sxm) * swn.w;
             *reinterpret_cast<uint2*>(lrow + i * 32 * kOutPitch + 2 * (j * 32 + 8 * g)) =
                 make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
           }
