@@ -19,8 +19,9 @@
 //    (|16 acc| < 2^31 for K < 150000).
 //  * Two kernels.  The pipelined one (K % 128 == 0, every CogVideoX shape):
 //    256 x 256 tiles, 8 waves (two per SIMD), LDS-DMA buffer loads two stages
-//    ahead into three LDS stages with XOR-swizzled rows, one barrier per
-//    stage; see gemm_i8_pipe.h.  The fallback (any K % 32 == 0):
+//    ahead into three LDS stages with XOR-swizzled rows, and the two waves of
+//    each SIMD alternating between LDS-read and MFMA phases (ping-pong); see
+//    gemm_i8_pipe.h.  The fallback (any K % 32 == 0):
 //    4 waves as 2 x 2, 64-byte LDS rows with 16-byte chunk c of row r at
 //    chunk c ^ ((r >> 1) & 3), K advancing 64 bytes per double-buffered
 //    stage.

@@ -33,10 +33,19 @@ __device__ __forceinline__ void unpack_int4x32(const uint4 p, uint4& lo, uint4& 
 //    wave's LDS / global / barrier waits overlap the other wave's MFMAs.
 //  * K advances 128 per stage.  Operands go from global memory straight to
 //    LDS with LDS-DMA buffer loads (no register staging, no LDS writes by
-//    the waves), into three LDS stage buffers: stage kt + 2 is issued right
-//    after the barrier that opens stage kt, so two stages of compute cover
-//    its latency, and that barrier is the only one per stage (it also
-//    retires the buffer of stage kt - 1, which kt + 2 reuses).
+//    the waves), into three LDS stage buffers: stage kt + 2 is issued at the
+//    start of stage kt, into the buffer of stage kt - 1, so two stages of
+//    compute cover its latency.
+//  * Ping-pong phases: a stage is two pairs of 64 K, and each pair is a
+//    memory phase (this wave's fragment reads and W unpack; for the first
+//    pair also the DMA issue) followed by a compute phase (its 16 MFMAs),
+//    with a workgroup barrier after every phase.  Waves 0-3 and 4-7 (one of
+//    each per SIMD, as waves are dealt to SIMDs round-robin) run one phase
+//    apart: group 1 passes one extra barrier at the start of a tile and
+//    group 0 one at the end.  So while one wave of a SIMD reads LDS and
+//    unpacks, the other issues MFMAs, and the matrix core always has work.
+//    (With both waves in the same phase, both waited for their LDS reads
+//    after every barrier.)
 //  * Rows past M or N read as zero (buffer range); their outputs are not
 //    stored.  X rows are 128 bytes in LDS (swz128), packed INT4 W rows 64
 //    bytes (swz64).  Within a stage, k-substep pair p
@@ -105,36 +114,45 @@ __device__ __forceinline__ void gemm_i8i4_pipe_body(
   zero_acc();
 
   const int h = lane >> 5, r32 = lane & 31;
-  auto compute = [&](int buf) {
+  // Memory phase of k-substep pair p of the stage in LDS buffer buf: the X
+  // fragments and the unpacked W fragments into registers.  The reads have
+  // completed when it returns, so the buffer may be refilled after the next
+  // barrier.
+  v4i xf[WM_T][2], wf[WN_T][2];
+  auto load_frags = [&](int buf, int p) {
     const uint8_t* lx = smem + buf * SB;
     const uint8_t* lw = lx + XB;
 #pragma unroll
-    for (int p = 0; p < BK / 64; ++p) {
-      v4i xf[WM_T][2];
+    for (int i = 0; i < WM_T; ++i) {
+      const int r = wm * WM_T * 32 + i * 32 + r32;
 #pragma unroll
-      for (int i = 0; i < WM_T; ++i) {
-        const int r = wm * WM_T * 32 + i * 32 + r32;
+      for (int s = 0; s < 2; ++s)
+        xf[i][s] = *reinterpret_cast<const v4i*>(lx + r * 128 + 16 * ((4 * p + 2 * h + s) ^ swz128(r)));
+    }
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-          xf[i][s] = *reinterpret_cast<const v4i*>(lx + r * 128 + 16 * ((4 * p + 2 * h + s) ^ swz128(r)));
-      }
+    for (int j = 0; j < WN_T; ++j) {
+      const int r = wn * WN_T * 32 + j * 32 + r32;
+      const uint4 packed = *reinterpret_cast<const uint4*>(lw + r * 64 + 16 * ((2 * p + h) ^ swz64(r)));
+      uint4 lo, hi;
+      unpack_int4x32(packed, lo, hi);
+      wf[j][0] = v4i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w};
+      wf[j][1] = v4i{(int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+    wait_lds();
+  };
+  // Compute phase: the pair's 16 MFMAs.
+  auto mfmas = [&]() {
 #pragma unroll
-      for (int j = 0; j < WN_T; ++j) {
-        const int r = wn * WN_T * 32 + j * 32 + r32;
-        const uint4 packed = *reinterpret_cast<const uint4*>(lw + r * 64 + 16 * ((2 * p + h) ^ swz64(r)));
-        uint4 lo, hi;
-        unpack_int4x32(packed, lo, hi);
-        const v4i w0 = v4i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w};
-        const v4i w1 = v4i{(int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    for (int j = 0; j < WN_T; ++j) {
 #pragma unroll
-        for (int i = 0; i < WM_T; ++i)
-          acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(w0, xf[i][0], acc[j][i], 0, 0, 0);
+      for (int i = 0; i < WM_T; ++i)
+        acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[j][0], xf[i][0], acc[j][i], 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < WM_T; ++i)
-          acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(w1, xf[i][1], acc[j][i], 0, 0, 0);
-      }
+      for (int i = 0; i < WM_T; ++i)
+        acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[j][1], xf[i][1], acc[j][i], 0, 0, 0);
     }
   };
+  const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);
 
   // Epilogue of one tile: lane holds token m = ... + (lane & 31) and, for
   // g = 0..3, features n = 8g + 4h + 0..3 of each 32 x 32 subtile.
@@ -246,10 +264,18 @@ __device__ __forceinline__ void gemm_i8i4_pipe_body(
   };
 
   // Persistent loop over this workgroup's tiles.  Per tile, stages 0 and 1
-  // are issued; stage kt waits for its own loads (those of kt + 1 may stay
-  // in flight: C::XI + C::WI per wave), passes the barrier, issues kt + 2
-  // into the buffer of kt - 1 and is computed.  Unrolled by three, so each
-  // buffer index is a constant.
+  // are issued and stage 0 waited for (stage 1's loads, C::XI + C::WI per
+  // wave, may stay in flight).  Stage kt: memory phase of pair 0 with the
+  // issue of stage kt + 2 into the buffer of kt - 1, compute, memory phase of
+  // pair 1, compute, a barrier after each phase.  Stage kt + 1 is waited for
+  // before the barrier after which group 0 reads it: group 0 waits after its
+  // last compute phase of stage kt, group 1 after its last memory phase.
+  // The buffer of kt - 1 is last read by group 1's second memory phase of
+  // kt - 1, which ends before the barrier that opens group 0's first phase
+  // of kt.  Unrolled by three, so each buffer index is a constant.
+  //
+  // Barriers per tile: 1 + 4 nk + 1 for every wave (the extra one at the
+  // start for group 1, at the end for group 0).
   for (int t = 0; t < seq.count; ++t) {
     const int logical = seq.first + t * seq.stride;
     {
@@ -260,21 +286,39 @@ __device__ __forceinline__ void gemm_i8i4_pipe_body(
       wres = make_rsrc(W4 + (int64_t)n0 * ldw, (uint32_t)((int64_t)(N - n0) * ldw));
     }
     issue(0, 0);
-    if (nk > 1) issue(1, 1);
+    if (nk > 1) {
+      issue(1, 1);
+      dma_barrier<C::XI + C::WI>();
+    } else {
+      dma_barrier<0>();
+    }
+    if (grp == 1) phase_barrier();
+    auto wait_next = [&](int kt) {
+      if (kt + 2 < nk)
+        wait_vmem<C::XI + C::WI>();
+      else if (kt + 1 < nk)
+        wait_vmem<0>();
+    };
     auto step = [&](int kt, auto bufc) {
       constexpr int b = decltype(bufc)::value;
-      if (kt + 1 < nk)
-        dma_barrier<C::XI + C::WI>();
-      else
-        dma_barrier<0>();
+      load_frags(b, 0);
       if (kt + 2 < nk) issue(kt + 2, (b + 2) % 3);
-      compute(b);
+      phase_barrier();
+      mfmas();
+      phase_barrier();
+      load_frags(b, 1);
+      if (grp == 1) wait_next(kt);
+      phase_barrier();
+      mfmas();
+      if (grp == 0) wait_next(kt);
+      phase_barrier();
     };
     for (int kt = 0; kt < nk; kt += 3) {
       step(kt, std::integral_constant<int, 0>{});
       if (kt + 1 < nk) step(kt + 1, std::integral_constant<int, 1>{});
       if (kt + 2 < nk) step(kt + 2, std::integral_constant<int, 2>{});
     }
+    if (grp == 0) phase_barrier();
     epilogue(logical);
     zero_acc();
   }

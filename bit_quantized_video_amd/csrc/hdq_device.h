@@ -277,6 +277,29 @@ __device__ __forceinline__ void dma_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Wait until at most PENDING of this wave's vector memory operations are
+// outstanding (LDS-DMA loads complete in order).
+template <int PENDING>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(PENDING >= 0 && PENDING < 64, "vmcnt has six bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (PENDING & 15) | ((PENDING >> 4) << 14));
+}
+
+// Wait for all of this wave's LDS reads (lgkmcnt(0), the other counters at
+// their maximum).
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Bare workgroup barrier for a phase-scheduled loop: the compiler may move
+// no instruction across it (sched_barrier) and no memory access (empty asm
+// with a memory clobber); no fence and no wait.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // ---- buffer loads ----------------------------------------------------------------
 // Raw buffer resource over [base, base + bytes): loads at offsets >= bytes
 // return zeros, so tile rows past the end of a tensor read as zero.  The
