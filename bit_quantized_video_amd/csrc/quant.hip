@@ -40,14 +40,16 @@ __device__ __forceinline__ uint32_t low_bytes4(uint32_t a, uint32_t b, uint32_t 
 // one partial per row, struct-of-arrays (psum[row] = sum |x|, pbits[row] =
 // max bf16 magnitude bits, ptmax[row] = the row's max |rotated x|, which is
 // the row absmax the quantizer needs anyway), so selection and quantization
-// read x once.
-template <int BLOCK, int CPT, bool INT4, bool STATS = false>
+// read x once.  HB > 0: the Hadamard block is HB (the argument is ignored),
+// so the rotation's block-size branches fold away at compile time.
+template <int BLOCK, int CPT, bool INT4, bool STATS = false, int HB = 0>
 __global__ __launch_bounds__(BLOCK) void k_quant_int_rows(
-    const uint16_t* __restrict__ x, int64_t cols, int hb, float c_b, void* __restrict__ codes,
+    const uint16_t* __restrict__ x, int64_t cols, int hb_arg, float c_b, void* __restrict__ codes,
     float* __restrict__ row_scale, const int32_t* __restrict__ decision, int32_t want,
     double* __restrict__ psum = nullptr, uint32_t* __restrict__ pbits = nullptr,
     float* __restrict__ ptmax = nullptr) {
   if (decision != nullptr && *decision != want) return;
+  const int hb = HB > 0 ? HB : hb_arg;
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -167,6 +169,9 @@ static hipError_t launch_int_rows_t(const uint16_t* x, int64_t rows, int64_t col
   if (int4)
     hipLaunchKernelGGL((k_quant_int_rows<BLOCK, CPT, true>), dim3((unsigned)rows), dim3(BLOCK), 0,
                        s, x, cols, hb, c_b, codes, sc, dec, want);
+  else if (hb == 128)
+    hipLaunchKernelGGL((k_quant_int_rows<BLOCK, CPT, false, false, 128>), dim3((unsigned)rows), dim3(BLOCK), 0,
+                       s, x, cols, hb, c_b, codes, sc, dec, want);
   else
     hipLaunchKernelGGL((k_quant_int_rows<BLOCK, CPT, false>), dim3((unsigned)rows), dim3(BLOCK), 0,
                        s, x, cols, hb, c_b, codes, sc, dec, want);
@@ -177,8 +182,12 @@ template <int BLOCK, int CPT>
 static hipError_t launch_select_q8_t(const uint16_t* x, int64_t rows, int64_t cols, int hb,
                                      void* codes, float* sc, double* psum, uint32_t* pbits,
                                      float* ptmax, hipStream_t s) {
-  hipLaunchKernelGGL((k_quant_int_rows<BLOCK, CPT, false, true>), dim3((unsigned)rows), dim3(BLOCK), 0,
-                     s, x, cols, hb, hadamard_scale(hb), codes, sc, nullptr, 0, psum, pbits, ptmax);
+  if (hb == 128)
+    hipLaunchKernelGGL((k_quant_int_rows<BLOCK, CPT, false, true, 128>), dim3((unsigned)rows), dim3(BLOCK), 0,
+                       s, x, cols, hb, hadamard_scale(hb), codes, sc, nullptr, 0, psum, pbits, ptmax);
+  else
+    hipLaunchKernelGGL((k_quant_int_rows<BLOCK, CPT, false, true>), dim3((unsigned)rows), dim3(BLOCK), 0,
+                       s, x, cols, hb, hadamard_scale(hb), codes, sc, nullptr, 0, psum, pbits, ptmax);
   return hipGetLastError();
 }
 
@@ -333,14 +342,15 @@ __device__ __forceinline__ uint32_t nvfp4_chunk(float (&v)[8], float s_t, float 
 // UNROLL 8-element chunks per lane per iteration, loads issued first; a wave
 // covers UNROLL x 64 consecutive chunks, so every Hadamard block (<= 128)
 // and every 16- or 32-element scale block lies inside aligned lane groups of
-// one wave.
-template <int FMT>
+// one wave.  HB > 0: the Hadamard block is HB (the argument is ignored).
+template <int FMT, int HB = 0>
 __global__ __launch_bounds__(256) void k_quant_nvfp4(
-    const uint16_t* __restrict__ x, int64_t nch, int hb, float c_b,
+    const uint16_t* __restrict__ x, int64_t nch, int hb_arg, float c_b,
     const float* __restrict__ amax_ptr, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ blk_scale, float* __restrict__ tensor_scale,
     const int32_t* __restrict__ decision, int32_t want) {
   if (decision != nullptr && *decision != want) return;
+  const int hb = HB > 0 ? HB : hb_arg;
   constexpr int UNROLL = 2;
   const int lane = threadIdx.x & 63;
   const float A = *amax_ptr;
@@ -393,8 +403,12 @@ hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t rows, int64_t cols, int
   if (blocks > 2048) blocks = 2048;
   if (blocks < 1) blocks = 1;
   const float c_b = hadamard_scale(hb);
-  auto kern = fmt == kNvfp4Mx ? k_quant_nvfp4<kNvfp4Mx>
-             : fmt == kNvfp4P2 ? k_quant_nvfp4<kNvfp4P2> : k_quant_nvfp4<kNvfp4>;
+  auto kern = hb == 128 ? (fmt == kNvfp4Mx   ? k_quant_nvfp4<kNvfp4Mx, 128>
+                           : fmt == kNvfp4P2 ? k_quant_nvfp4<kNvfp4P2, 128>
+                                             : k_quant_nvfp4<kNvfp4, 128>)
+                        : (fmt == kNvfp4Mx   ? k_quant_nvfp4<kNvfp4Mx>
+                           : fmt == kNvfp4P2 ? k_quant_nvfp4<kNvfp4P2>
+                                             : k_quant_nvfp4<kNvfp4>);
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, s, x, nch, hb, c_b, amax, codes,
                      blk_scale, tensor_scale, decision, want);
   return hipGetLastError();

@@ -352,8 +352,8 @@ def test_bf16_gemm_multi_tile_workgroups(K):
     assert rel_fro(y_np(y)[MT_ROWS], ref) <= REL_TOL
 
 
-@pytest.mark.parametrize("fmt", [hdq.FMT_NVFP4_MX, hdq.FMT_NVFP4_P2])
-@pytest.mark.parametrize("K", [256, 768])
+@pytest.mark.parametrize("fmt,K", [(hdq.FMT_NVFP4_MX, K) for K in (256, 512, 768)] +
+                         [(hdq.FMT_NVFP4_P2, K) for K in (256, 768)])
 def test_fp4_gemm_multi_tile_workgroups(fmt, K):
     say(f"fp4 gemm f32 multi-tile fmt={fmt} M={MT_M} N={MT_N} K={K}")
     hb = 32
@@ -367,6 +367,34 @@ def test_fp4_gemm_multi_tile_workgroups(fmt, K):
     wc, we, wst = O.quant_nvfp4(w16, hb, mx=mx)
     ref = round_like(O.gemm_nvfp4(ac, ae, ast, wc, we, wst, K), hdq.DTYPE_F32)
     assert rel_fro(y_np(y)[MT_ROWS], ref) <= REL_TOL
+
+
+@pytest.mark.parametrize("fmt", [hdq.FMT_NVFP4_MX, hdq.FMT_NVFP4_P2])
+def test_fp4_gemm_subnormal_block_scales(fmt):
+    # rows scaled by 2^-13 ... 2^-18 and a zero row: their blocks' power-of-two
+    # E4M3 scales are the subnormal codes 2^-7, 2^-8 and 2^-9 (also the clamp,
+    # and the zero row's), which the FP4 kernels turn into E8M0 exponents
+    M, N, K, hb = 300, 272, 512, 32
+    rows = np.arange(M)
+    scale = np.where(rows % 8 == 0, 1.0, 2.0 ** -(12 + rows % 8)).astype(np.float32)
+    scale[7] = 0.0
+    x = synth.bf16_bits_to_f32(synth.gaussian(M, K, 1.0, synth.rng_for(110, fmt)))
+    x16 = synth.to_bf16_bits(x * scale[:, None])       # exact: powers of two
+    w16 = synth.gaussian(N, K, 0.02, synth.rng_for(111, fmt))
+    W = hdq.LinearWeights(to_dev(w16), hb, fp4_fmt=fmt)
+    xq = hdq.quantize(to_dev(x16), hb, fmt)
+    y = hdq.linear(hdq.PREC_NVFP4, None, W, xq=xq, y_dtype=hdq.DTYPE_F32)
+    torch.cuda.synchronize()
+    mx = FP4_FMTS[fmt]
+    ac, ae, ast = O.quant_nvfp4(x16, hb, mx=mx)
+    assert np.isin([1, 2, 4], ae).all()     # the subnormal scales occur
+    assert np.array_equal(xq.blk_scale.cpu().numpy().reshape(ae.shape), ae)
+    wc, we, wst = O.quant_nvfp4(w16, hb, mx=mx)
+    ref = round_like(O.gemm_nvfp4(ac, ae, ast, wc, we, wst, K), hdq.DTYPE_F32)
+    got = y_np(y)
+    for r in range(8):       # every row class separately: the tiny rows carry tiny outputs
+        sel = rows % 8 == r
+        assert rel_fro(got[sel], ref[sel]) <= REL_TOL, r
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_CASES[1:])
