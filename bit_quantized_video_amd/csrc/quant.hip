@@ -60,7 +60,7 @@ __global__ __launch_bounds__(BLOCK) void k_quant_int_rows(
   // Hadamard blocks sit in aligned lane groups (BLOCK is a multiple of 16
   // lanes), and a block past the row end is entirely zero-filled.
   float v[CPT][8];
-  uint32_t maxbits = 0u;
+  float maxabs = 0.0f;
   double sumabs = 0.0;
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
@@ -70,13 +70,14 @@ __global__ __launch_bounds__(BLOCK) void k_quant_int_rows(
     bf16x8_to_f32(w, v[c]);
   }
   if constexpr (STATS) {
-    // bf16 widens to float exactly: a float's top 16 bits are its bf16 pattern
+    // max |x| with IEEE-2019 maximum, which propagates NaN (v_maximum3_f32
+    // takes two elements per instruction)
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       float s8 = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        maxbits = max(maxbits, (__float_as_uint(v[c][i]) >> 16) & 0x7fffu);
+        maxabs = __builtin_elementwise_maximum(maxabs, fabsf(v[c][i]));
         s8 += fabsf(v[c][i]);
       }
       sumabs += s8;
@@ -102,6 +103,9 @@ __global__ __launch_bounds__(BLOCK) void k_quant_int_rows(
     for (int w = 1; w < BLOCK / 64; ++w) amax = fmaxf(amax, red[w]);
   }
   if constexpr (STATS) {
+    // bf16 widens to float exactly: |x|'s top 16 bits are its bf16 pattern
+    // (a NaN's are above every number's)
+    uint32_t maxbits = __float_as_uint(maxabs) >> 16;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
       sumabs += __shfl_xor(sumabs, o);
