@@ -18,6 +18,13 @@ def test_classify_kernel_names():
         "void hdq::k_quant_nvfp4<3>(int)": "quant_nvfp4_mx",
         "void hdq::k_quant_nvfp4<4>(int)": "quant_nvfp4_p2",
         "void hdq::k_quant_nvfp4<2>(int)": "quant_nvfp4",
+        # with the Hadamard block as a template argument
+        "void hdq::k_quant_int_rows<192, 2, false, true, 128>(int)": "select_quant_int8",
+        "void hdq::k_quant_int_rows<128, 3, false, false, 128>(int)": "quant_int8",
+        "void hdq::k_quant_int_rows<128, 3, true, false, 0>(int)": None,
+        "void hdq::k_quant_nvfp4<3, 128>(int)": "quant_nvfp4_mx",
+        "void hdq::k_quant_nvfp4<4, 0>(int)": "quant_nvfp4_p2",
+        "void hdq::k_quant_nvfp4<2, 128>(int)": "quant_nvfp4",
         "void hdq::k_gemm_i8i4_pipe<2, 4, 4, 2, 1>(int)": "gemm_int8",
         "void hdq::k_gemm_i8i4_pipe<2, 4, 4, 2, 0>(int)": None,  # f32 output: quality check
         "void hdq::k_gemm_fp4mx_pipe<1, false>(int)": "gemm_nvfp4_mx",
@@ -34,6 +41,8 @@ def test_schedule_window_starts_after_weight_prep():
     rows = [(0, "void hdq::k_quant_int_rows<128, 3, true>"), (1, "hdq::k_stats_partial"),
             (2, "void hdq::k_quant_int_rows<128, 3, true, false>"), (3, "hdq::k_stats_partial"),
             (4, "void hdq::k_gemm_i8i4_pipe<2, 4, 4, 2, 1>"), (5, "void hdq::k_gemm_i8i4_pipe<2, 4, 4, 2, 0>")]
+    assert [r[0] for r in P.schedule_window(rows)] == [3, 4]
+    rows[2] = (2, "void hdq::k_quant_int_rows<128, 3, true, false, 0>")
     assert [r[0] for r in P.schedule_window(rows)] == [3, 4]
 
 
