@@ -60,9 +60,11 @@ def parse():
                          "plain (exact, bf16 MFMA) or a power of two per 16-block (FP4 MFMA, two "
                          "passes); the schedule also times the other two")
     ap.add_argument("--config", type=int, default=5, help="5: schedule; 1-4: one linear layer")
-    ap.add_argument("--delta", choices=["overlap", "inline"], default="overlap",
-                    help="previous-step difference on a second stream ahead of each layer call "
-                         "(overlap, default) or inside the selection pass (inline)")
+    ap.add_argument("--delta", choices=["embed", "overlap", "inline"], default="embed",
+                    help="previous-step difference: in chunks on extra workgroups of earlier layer "
+                         "calls' GEMM launches (embed, default; needs --dispatch on), on a second "
+                         "stream ahead of each layer call (overlap) or inside the selection pass "
+                         "(inline)")
     ap.add_argument("--fuse", choices=["on", "off"], default="on",
                     help="selection fused with the INT8 per-token quantization of the input (on, "
                          "default; the codes are written whatever the decision) or separate")
@@ -226,8 +228,50 @@ def build_schedule(args, hdq, synth):
     ws_delta = torch.empty_like(ws_sel)
     ws_sq8 = torch.empty(hdq.workspace_bytes(hdq.OP_SELECT_Q8, M, 12288), dtype=torch.uint8, device=dev)
     side = torch.cuda.Stream(device=dev)
-    return dict(M=M, recipes=recipes, blocks=blocks, shared=shared, ws_sel=ws_sel, dec=dec, sts=sts,
-                s_levels=s_levels, sums=sums, ws_delta=ws_delta, ws_sq8=ws_sq8, side=side)
+    S = dict(M=M, recipes=recipes, blocks=blocks, shared=shared, ws_sel=ws_sel, dec=dec, sts=sts,
+             s_levels=s_levels, sums=sums, ws_delta=ws_delta, ws_sq8=ws_sq8, side=side)
+    if args.delta == "embed":
+        if args.dispatch != "on":
+            raise SystemExit("--delta embed needs --dispatch on")
+        S.update(embed_plan(args, hdq, synth, M, dev))
+    return S
+
+
+def embed_plan(args, hdq, synth, M, dev):
+    """--delta embed: which difference chunks each layer call's GEMM launch
+    carries.  The difference of call k is needed by call k's selection, so
+    its chunks must all have run by the GEMM launch of call k - 1 (call 0's
+    runs as a separate pass at the start of the step).  The chunks of calls
+    1.. form one queue in call order; launch k takes its share of the queue,
+    proportional to its GEMM's work (so most chunks run beside a GEMM on the
+    CUs it leaves free), or more when call k + 1's chunks would otherwise
+    not be done in time."""
+    calls = [(t, b, li) for t in range(args.timesteps) for b in range(args.blocks)
+             for li in range(len(synth.SCHEDULE_LAYERS))]
+    n = [hdq.delta_chunks(M * synth.SCHEDULE_LAYERS[li][1]) for _, _, li in calls]
+    work = [2.0 * M * synth.SCHEDULE_LAYERS[li][1] * synth.SCHEDULE_LAYERS[li][2] for _, _, li in calls]
+    offs = np.concatenate([[0], np.cumsum(n)]).astype(np.int64)
+    parts = torch.full((int(offs[-1]), 2), float("nan"), dtype=torch.float64, device=dev)
+    part_of = [parts[offs[k]:offs[k + 1]] for k in range(len(calls))]
+    # queue positions: call k's chunks are [offs[k] - offs[1], offs[k + 1] - offs[1])
+    total = int(offs[-1] - offs[1])
+    rate = total / sum(work)
+    plan, pos = [], 0
+    for k in range(len(calls)):
+        need = int(offs[k + 2] - offs[1]) - pos if k + 2 < len(offs) else 0
+        take = min(total - pos, max(int(round(rate * work[k])), need))
+        slices, end = [], pos + take
+        while pos < end:
+            j = int(np.searchsorted(offs[1:], pos + offs[1], side="right"))  # call owning queue pos
+            c0 = pos + int(offs[1]) - int(offs[j])
+            c1 = min(int(n[j]), end + int(offs[1]) - int(offs[j]))
+            slices.append((j, c0, c1))
+            pos += c1 - c0
+        if len(slices) > hdq.DELTA_MAX_SLICES:
+            raise SystemExit(f"embed plan: launch {k} spans {len(slices)} calls")
+        plan.append(slices)
+    assert pos == total
+    return dict(embed=plan, embed_parts=part_of, embed_queue=torch.zeros(2, dtype=torch.int32, device=dev))
 
 
 def rec(ev, i):
@@ -247,6 +291,7 @@ def run_schedule_step(S, args, hdq, recipe, events=None, side_events=None):
     main = torch.cuda.current_stream()
     side = S["side"]
     overlap = args.delta == "overlap"
+    embed = args.delta == "embed"
     done = [None] * len(calls)
 
     def enqueue_delta(k, gate=None):
@@ -269,6 +314,11 @@ def run_schedule_step(S, args, hdq, recipe, events=None, side_events=None):
         side.wait_stream(main)  # the previous step's readers of the sums are enqueued before
         for k in range(min(ahead, len(calls))):
             enqueue_delta(k)
+    if embed:
+        # call 0's difference on its own; the others ride along earlier GEMM launches
+        t, b, li = calls[0]
+        L = S["blocks"][b][li]
+        hdq.delta_sums(L["prev_in"], L["prev_out"][t], sums=S["sums"][t, b, li], ws=S["ws_delta"])
     for k, (t, b, li) in enumerate(calls):
         L = S["blocks"][b][li]
         sh = S["shared"][li]
@@ -278,15 +328,16 @@ def run_schedule_step(S, args, hdq, recipe, events=None, side_events=None):
         if overlap:
             main.wait_event(done[k])
         fused = args.fuse == "on"
-        if fused and not overlap:
+        if fused and args.delta == "inline":
             # the difference on the main stream, right before the selection
             hdq.delta_sums(L["prev_in"], L["prev_out"][t], sums=S["sums"][t, b, li], ws=S["ws_delta"])
         rec(ev, 0)
+        hist = S["embed_parts"][k] if embed and k > 0 else S["sums"][t, b, li]
         if fused:
-            hdq.select_quantize_int8(S["sums"][t, b, li], L["x"], HB, DELTA_T, RATIO_T, decision=d,
+            hdq.select_quantize_int8(hist, L["x"], HB, DELTA_T, RATIO_T, decision=d,
                                      stats=st, out=sh["xq8"], ws=S["ws_sq8"])
-        elif overlap:
-            hdq.select_precision_sums(S["sums"][t, b, li], L["x"], HB, DELTA_T, RATIO_T, decision=d,
+        elif overlap or embed:
+            hdq.select_precision_sums(hist, L["x"], HB, DELTA_T, RATIO_T, decision=d,
                                       stats=st, ws=S["ws_sel"])
         else:
             hdq.select_precision(L["prev_in"], L["prev_out"][t], L["x"], HB, DELTA_T, RATIO_T,
@@ -305,7 +356,16 @@ def run_schedule_step(S, args, hdq, recipe, events=None, side_events=None):
             gate.record(main)
             enqueue_delta(k + ahead, gate)
         W = L["W"][recipe]
-        if args.dispatch == "on":
+        if embed:
+            sl = []
+            for j, c0, c1 in S["embed"][k]:
+                tj, bj, lj = calls[j]
+                Lj = S["blocks"][bj][lj]
+                sl.append((Lj["prev_in"], Lj["prev_out"][tj], c0, c1, S["embed_parts"][j]))
+            hdq.linear_dispatch_delta(d, L["x"], sh["xq8"], sh["xq4"][recipe], W, sl, S["embed_queue"],
+                                      y=sh["y"])
+            rec(ev, 4)
+        elif args.dispatch == "on":
             hdq.linear_dispatch(d, L["x"], sh["xq8"], sh["xq4"][recipe], W, y=sh["y"])
             rec(ev, 4)
         else:
@@ -465,6 +525,15 @@ def time_schedule(S, args, hdq, synth, recipe):
 TDC_TAU_SKIP, TDC_TAU_ACC = 0.05, 0.15
 
 
+def schedule_history(S, args, t, b, li):
+    """The schedule's previous-step difference sums of call (t, b, li): its
+    chunk partials under --delta embed (except call 0's pair), else its pair."""
+    k = (t * args.blocks + b) * len(S["blocks"][b]) + li
+    if args.delta == "embed" and k > 0:
+        return S["embed_parts"][k]
+    return S["sums"][t, b, li]
+
+
 def tdc_trajectory(S, args, hdq, synth, recipe, use_tdc, dirs):
     """One synthetic denoising trajectory over the first args.tdc_blocks
     blocks' modules.  Module input at step t: x + a_t * d (d a fixed seeded
@@ -511,7 +580,7 @@ def tdc_trajectory(S, args, hdq, synth, recipe, use_tdc, dirs):
             torch.add(L["x"], dirs[i], alpha=a, out=xin[li])
             e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
             e[0].record()
-            hist = S["sums"][min(t, args.timesteps - 1), b, li] if ran_prev[i] else None
+            hist = schedule_history(S, args, min(t, args.timesteps - 1), b, li) if ran_prev[i] else None
             d, st = dec_t[i], sts_t[i]
             hdq.select_quantize_int8(hist, xin[li], HB, DELTA_T, RATIO_T, decision=d, stats=st,
                                      out=sh["xq8"], ws=S["ws_sq8"])

@@ -159,12 +159,13 @@ int hdq_delta_sums(const void* prev_in, const void* prev_out, int64_t numel, dou
                                  s, nullptr, sums_dev));
 }
 
-int hdq_select_precision_sums(const double* delta_sums_dev, const void* cur_in, int64_t rows,
-                              int64_t cols, int32_t had_block, float delta_thresh,
+int hdq_select_precision_sums(const double* delta_sums_dev, int64_t delta_parts, const void* cur_in,
+                              int64_t rows, int64_t cols, int32_t had_block, float delta_thresh,
                               float ratio_thresh, int32_t* decision_dev, float* stats_dev, void* ws,
                               size_t ws_bytes, void* stream) {
   if (cur_in == nullptr || decision_dev == nullptr || stats_dev == nullptr) return HDQ_ERR_INVALID;
   if (rows <= 0 || cols <= 0) return HDQ_ERR_SHAPE;
+  if (delta_sums_dev != nullptr && (delta_parts < 1 || delta_parts > 0x7fffffff)) return HDQ_ERR_SHAPE;
   if (had_block != 0 && (!valid_block(had_block) || cols % had_block != 0 || cols % 8 != 0))
     return HDQ_ERR_SHAPE;
   if (ws == nullptr || ws_bytes < align_up(kStatsPartialBytes)) return HDQ_ERR_WORKSPACE;
@@ -172,15 +173,16 @@ int hdq_select_precision_sums(const double* delta_sums_dev, const void* cur_in, 
   return hip_status(launch_stats(nullptr, nullptr, 0, static_cast<const uint16_t*>(cur_in),
                                  rows * cols, had_block, delta_thresh, ratio_thresh, decision_dev,
                                  stats_dev, nullptr, static_cast<double*>(ws), nullptr, 0, s,
-                                 delta_sums_dev, nullptr));
+                                 delta_sums_dev, nullptr, delta_parts));
 }
 
-int hdq_select_quantize_int8(const double* delta_sums_dev, const void* cur_in, int64_t rows,
-                             int64_t cols, int32_t had_block, float delta_thresh, float ratio_thresh,
-                             int32_t* decision_dev, float* stats_dev, hdq_qtensor* xq8, void* ws,
-                             size_t ws_bytes, void* stream) {
+int hdq_select_quantize_int8(const double* delta_sums_dev, int64_t delta_parts, const void* cur_in,
+                             int64_t rows, int64_t cols, int32_t had_block, float delta_thresh,
+                             float ratio_thresh, int32_t* decision_dev, float* stats_dev,
+                             hdq_qtensor* xq8, void* ws, size_t ws_bytes, void* stream) {
   if (cur_in == nullptr || decision_dev == nullptr || stats_dev == nullptr || xq8 == nullptr)
     return HDQ_ERR_INVALID;
+  if (delta_sums_dev != nullptr && (delta_parts < 1 || delta_parts > 0x7fffffff)) return HDQ_ERR_SHAPE;
   if (xq8->codes == nullptr || xq8->row_scale == nullptr) return HDQ_ERR_INVALID;
   if (had_block == 0) return HDQ_ERR_SHAPE;
   int st = check_quant_shape(rows, cols, had_block, HDQ_FMT_INT8_ROW);
@@ -204,12 +206,12 @@ int hdq_select_quantize_int8(const double* delta_sums_dev, const void* cur_in, i
     if (e != hipSuccess) return HDQ_ERR_HIP;
     return hip_status(launch_stats_finalize_rows(part, pbits, ptmax, rows, rows * cols, had_block,
                                                  delta_thresh, ratio_thresh, decision_dev, stats_dev,
-                                                 delta_sums_dev, s));
+                                                 delta_sums_dev, delta_parts, s));
   }
   // rows too long to keep in registers: the two passes separately
   hipError_t e = launch_stats(nullptr, nullptr, 0, xb, rows * cols, had_block, delta_thresh, ratio_thresh,
                               decision_dev, stats_dev, nullptr, part, nullptr, 0, s, delta_sums_dev,
-                              nullptr);
+                              nullptr, delta_parts);
   if (e != hipSuccess) return HDQ_ERR_HIP;
   return hip_status(launch_quant_int_rows(xb, rows, cols, had_block, HDQ_FMT_INT8_ROW, xq8->codes,
                                           xq8->row_scale, nullptr, 0, s));
@@ -268,6 +270,66 @@ int hdq_linear_dispatch(const int32_t* decision_dev, const void* x, const hdq_qt
           y_dtype, M, N, K, decision_dev, HDQ_PREC_NVFP4, s) != hipSuccess)
     return HDQ_ERR_HIP;
   return hip_status(launch_gemm_bf16(xb, wb, y, y_dtype, M, N, K, decision_dev, HDQ_PREC_BF16, s));
+}
+
+static_assert(HDQ_DELTA_CHUNK == kDeltaChunk && HDQ_DELTA_MAX_SLICES == kDeltaMaxSlices,
+              "the header's chunk size and slice count are the kernel's");
+
+int hdq_linear_dispatch_delta(const int32_t* decision_dev, const void* x, const hdq_qtensor* xq8,
+                              const hdq_qtensor* xq4, int64_t M, int64_t K, const hdq_weights* w,
+                              void* y, int32_t y_dtype, const hdq_delta_slice* slices,
+                              int32_t nslices, uint32_t* queue_dev, void* stream) {
+  if (nslices < 0 || nslices > HDQ_DELTA_MAX_SLICES) return HDQ_ERR_SHAPE;
+  if (nslices > 0 && (slices == nullptr || queue_dev == nullptr)) return HDQ_ERR_INVALID;
+  DeltaWork dw{};
+  dw.queue = queue_dev;
+  for (int i = 0; i < nslices; ++i) {
+    const hdq_delta_slice& q = slices[i];
+    if (q.prev_in == nullptr || q.prev_out == nullptr || q.partials == nullptr) return HDQ_ERR_INVALID;
+    if (q.numel <= 0 || q.numel % 8 != 0 || q.numel > ((int64_t)1 << 40)) return HDQ_ERR_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(q.prev_in) | reinterpret_cast<uintptr_t>(q.prev_out)) % 16 != 0)
+      return HDQ_ERR_SHAPE;
+    const int64_t nchunks = (q.numel + HDQ_DELTA_CHUNK - 1) / HDQ_DELTA_CHUNK;
+    if (q.chunk_begin < 0 || q.chunk_end > nchunks || q.chunk_begin > q.chunk_end) return HDQ_ERR_SHAPE;
+    dw.s[i] = DeltaSlice{static_cast<const uint16_t*>(q.prev_in), static_cast<const uint16_t*>(q.prev_out),
+                         q.numel, q.chunk_begin, q.chunk_end, q.partials};
+    dw.total += q.chunk_end - q.chunk_begin;
+  }
+  dw.n = nslices;
+  if (dw.total > 0x7fffffff) return HDQ_ERR_SHAPE;
+  // one workgroup per CU: the pipelined bodies' LDS admits no second one
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  dw.delta_wgs = (int)(dw.total < cus ? dw.total : cus);
+  if (decision_dev == nullptr || x == nullptr || xq8 == nullptr || xq4 == nullptr || w == nullptr ||
+      y == nullptr)
+    return HDQ_ERR_INVALID;
+  if (y_dtype != HDQ_DTYPE_F32 && y_dtype != HDQ_DTYPE_BF16) return HDQ_ERR_UNSUPPORTED;
+  if (M <= 0 || K <= 0 || w->N <= 0 || M > 0x7fffffff || K > 0x7fffffff || w->N > 0x7fffffff)
+    return HDQ_ERR_SHAPE;
+  if (w->K != K) return HDQ_ERR_SHAPE;
+  const int64_t N = w->N;
+  const int32_t f = w->w_fp4.fmt;
+  int st;
+  if ((st = check_qtensor(w->w_int4, HDQ_FMT_INT4_ROW, N, K)) != HDQ_OK) return st;
+  if ((st = check_qtensor(*xq8, HDQ_FMT_INT8_ROW, M, K)) != HDQ_OK) return st;
+  if (!is_fp4(f)) return HDQ_ERR_UNSUPPORTED;
+  if ((st = check_qtensor(w->w_fp4, f, N, K)) != HDQ_OK) return st;
+  if ((st = check_qtensor(*xq4, f, M, K)) != HDQ_OK) return st;
+  if (w->w_bf16 == nullptr) return HDQ_ERR_INVALID;
+  if (xq8->had_block != w->w_int4.had_block || xq4->had_block != w->w_fp4.had_block) return HDQ_ERR_SHAPE;
+  // the one-launch kernel only (the difference runs on its extra workgroups)
+  if (K % 256 != 0 || M * 2 * K >= (1ll << 31) || N * 2 * K >= (1ll << 31)) return HDQ_ERR_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(launch_gemm_dispatch(
+      decision_dev, static_cast<const int8_t*>(xq8->codes), xq8->row_scale,
+      static_cast<const uint8_t*>(w->w_int4.codes), w->w_int4.row_scale,
+      static_cast<const uint8_t*>(xq4->codes), xq4->blk_scale, xq4->tensor_scale,
+      static_cast<const uint8_t*>(w->w_fp4.codes), w->w_fp4.blk_scale, w->w_fp4.tensor_scale, f,
+      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w->w_bf16), y, y_dtype, M, N, K, s,
+      &dw));
 }
 
 int hdq_quantize(const void* x, int64_t rows, int64_t cols, int32_t had_block, int32_t fmt,

@@ -59,7 +59,7 @@ template <int SRC, int OUT>
 __device__ __forceinline__ void gemm_bf16_pipe_body(
     const void* __restrict__ X, const uint8_t* __restrict__ xsc, const float* __restrict__ xts,
     const void* __restrict__ W, const uint8_t* __restrict__ wsc, const float* __restrict__ wts,
-    void* __restrict__ Y, int M, int N, int K) {
+    void* __restrict__ Y, int M, int N, int K, int nwg = 0) {
   constexpr int BM = 256, BN = 256, BK = 64, WM_T = 4, WN_T = 2;
   constexpr int XB = BM * BK * 2, SB = XB + BN * BK * 2;  // LDS bytes per stage
   constexpr int kOutPitch = kBf16OutPitch;                // bf16 output row staged in LDS
@@ -69,7 +69,7 @@ __device__ __forceinline__ void gemm_bf16_pipe_body(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % 2, wn = wave / 2;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const TileSeq seq = tile_seq(tiles_m * tiles_n);
+  const TileSeq seq = tile_seq(tiles_m * tiles_n, nwg);
   const int nk = K / BK;
 
   // Buffer resources over the current tile's rows; per-thread offsets.

@@ -55,7 +55,7 @@ template <int OUT, bool P2 = false>
 __device__ __forceinline__ void gemm_fp4mx_pipe_body(
     const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xsc, const float* __restrict__ xts,
     const uint8_t* __restrict__ wc, const uint8_t* __restrict__ wsc, const float* __restrict__ wts,
-    void* __restrict__ Y, int M, int N, int K) {
+    void* __restrict__ Y, int M, int N, int K, int nwg = 0) {
   constexpr int BM = 256, BN = 256, BK = 256, WM_T = 4, WN_T = 2;
   constexpr int XB = BM * BK / 2, WB = BN * BK / 2;  // code bytes per stage
   constexpr int SCB = P2 ? 16 : 8;                    // E8M0 bytes per row and stage
@@ -68,7 +68,7 @@ __device__ __forceinline__ void gemm_fp4mx_pipe_body(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % 2, wn = wave / 2;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const TileSeq seq = tile_seq(tiles_m * tiles_n);
+  const TileSeq seq = tile_seq(tiles_m * tiles_n, nwg);
   const int nk = K / BK;
   const int G = seq.count * nk;
   if (G == 0) return;

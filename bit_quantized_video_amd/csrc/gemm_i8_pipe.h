@@ -70,7 +70,7 @@ struct I8Cfg {
 template <int WAVES_M, int WAVES_N, int WM_T, int WN_T, int OUT>
 __device__ __forceinline__ void gemm_i8i4_pipe_body(
     const int8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ W4,
-    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K) {
+    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K, int nwg = 0) {
   using C = I8Cfg<WAVES_M, WAVES_N, WM_T, WN_T>;
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, XB = C::XB, SB = C::SB;
   constexpr int kOutPitch = C::OUT_PITCH;
@@ -79,7 +79,7 @@ __device__ __forceinline__ void gemm_i8i4_pipe_body(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WAVES_M, wn = wave / WAVES_M;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  const TileSeq seq = tile_seq(tiles_m * tiles_n);
+  const TileSeq seq = tile_seq(tiles_m * tiles_n, nwg);
   const int nk = K / BK;
   const int ldw = K >> 1;
 

@@ -226,19 +226,22 @@ __device__ __forceinline__ void xcd_tile(int tiles_m, int tiles_n, int& tm, int&
 }
 
 // Tiles of a persistent workgroup: logical tiles first, first + stride, ...
-// below end.  With one workgroup per tile (gridDim.x == total) that is the
-// xcd_tile tile alone; otherwise gridDim.x is a multiple of 8 and the
-// gridDim.x / 8 workgroups of an XCD deal its range round-robin, so the ones
-// running at the same time hold consecutive logical tiles.
+// below end.  With one workgroup per tile (nwg == total) that is the
+// xcd_tile tile alone; otherwise nwg is a multiple of 8 and the nwg / 8
+// workgroups of an XCD deal its range round-robin, so the ones running at
+// the same time hold consecutive logical tiles.
 struct TileSeq {
   int first, stride, count;
 };
-__device__ __forceinline__ TileSeq tile_seq(int total) {
+// nwg: the workgroups that share the tiles (0: the whole grid), a multiple of
+// 8 when smaller than total; workgroups beyond them do other work.
+__device__ __forceinline__ TileSeq tile_seq(int total, int nwg = 0) {
+  if (nwg <= 0) nwg = (int)gridDim.x;
   int lo, hi;
   xcd_range(total, blockIdx.x & 7, lo, hi);
   const int local = blockIdx.x >> 3;
-  if ((int)gridDim.x >= total) return TileSeq{lo + local, 1, 1};
-  const int per = gridDim.x >> 3;
+  if (nwg >= total) return TileSeq{lo + local, 1, 1};
+  const int per = nwg >> 3;
   const int n = hi - lo - local;
   return TileSeq{lo + local, per, n > 0 ? (n + per - 1) / per : 0};
 }

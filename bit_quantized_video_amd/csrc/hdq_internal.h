@@ -11,6 +11,27 @@
 
 namespace hdq {
 
+// Difference sums run by extra workgroups of a GEMM launch (gemm_dispatch.hip).
+// A slice is the chunk range [c0, c1) of one pair of previous-step tensors;
+// chunk c covers elements [c * kDeltaChunk, (c + 1) * kDeltaChunk) and its
+// {sum |out - in|, sum |in|} go to parts[2c], parts[2c + 1].
+constexpr int64_t kDeltaChunk = 65536;
+constexpr int kDeltaMaxSlices = 4;
+struct DeltaSlice {
+  const uint16_t* in;
+  const uint16_t* out;
+  int64_t numel;
+  int64_t c0, c1;
+  double* parts;
+};
+struct DeltaWork {
+  DeltaSlice s[kDeltaMaxSlices];
+  int n;               // slices
+  int64_t total;       // chunks over all slices
+  uint32_t* queue;     // {next chunk, workgroups done}: zero on entry and on exit
+  int delta_wgs;       // workgroups after the GEMM's
+};
+
 enum QFmt : int { kInt8Row = 0, kInt4Row = 1, kNvfp4 = 2, kNvfp4Mx = 3, kNvfp4P2 = 4 };
 enum Prec : int { kPrecNvfp4 = 0, kPrecInt8 = 1, kPrecBf16 = 2 };
 enum OutDtype : int { kOutF32 = 0, kOutBf16 = 1, kOutI32 = 2 };
@@ -46,12 +67,14 @@ constexpr size_t kStatsPartialBytes = (size_t)kStatsMaxBlocks * 6 * sizeof(doubl
 // cur_numel 0), then a one-block finalize that writes the five statistics,
 // the decision and/or the rotated amax (any output pointer may be null).
 // delta_sums_out (double[2]): write only the difference sums.  delta_sums_in
-// (double[2]): take the difference sums from there (history present).
+// (double[2 * delta_parts]): take the difference sums from there (history
+// present), the pairs summed in order.
 hipError_t launch_stats(const uint16_t* prev_in, const uint16_t* prev_out, int64_t prev_numel,
                         const uint16_t* cur, int64_t cur_numel, int hb, float delta_thresh,
                         float ratio_thresh, int32_t* decision, float* stats, float* amax_out,
                         double* partials, const int32_t* gate, int32_t want, hipStream_t s,
-                        const double* delta_sums_in = nullptr, double* delta_sums_out = nullptr);
+                        const double* delta_sums_in = nullptr, double* delta_sums_out = nullptr,
+                        int64_t delta_parts = 1);
 
 // The finalize over one partial per row, struct-of-arrays: psum = sum |x|,
 // pbits = max bf16 magnitude bits, ptmax = max |rotated x| (scaled).
@@ -61,7 +84,7 @@ hipError_t launch_tdc_decide(const double* sums, const int32_t* state, float* c,
 hipError_t launch_stats_finalize_rows(const double* psum, const uint32_t* pbits, const float* ptmax,
                                       int64_t rows, int64_t cur_numel, int hb, float delta_thresh,
                                       float ratio_thresh, int32_t* decision, float* stats,
-                                      const double* delta_sums_in, hipStream_t s);
+                                      const double* delta_sums_in, int64_t delta_parts, hipStream_t s);
 // INT8 per-row quantization that also writes those per-row partials;
 // cols <= 16384.
 hipError_t launch_quant_int8_stats(const uint16_t* x, int64_t rows, int64_t cols, int hb, void* codes,
@@ -97,7 +120,8 @@ hipError_t launch_gemm_dispatch(const int32_t* decision, const int8_t* x8, const
                                 const uint8_t* xsc, const float* xts, const uint8_t* wc,
                                 const uint8_t* wsc, const float* wts, int fp4_fmt,
                                 const uint16_t* xb, const uint16_t* wb, void* y, int out_dtype,
-                                int64_t M, int64_t N, int64_t K, hipStream_t s);
+                                int64_t M, int64_t N, int64_t K, hipStream_t s,
+                                const struct DeltaWork* delta = nullptr);
 // bf16 x bf16 (full-precision fallback).
 hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* w, void* y, int out_dtype,
                             int64_t M, int64_t N, int64_t K, const int32_t* decision,

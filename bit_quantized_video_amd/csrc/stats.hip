@@ -34,6 +34,33 @@ __device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
   return v;
 }
 
+// Sums of the pairs {p[2i], p[2i + 1]}, i < n, in a fixed order: thread t
+// adds i = t, t + T, ... in turn, then a fixed tree over the threads (red:
+// 2T doubles of LDS).  Every thread calls it; thread 0 gets the sums.  One
+// pair (n = 1) comes out exactly as stored.
+template <int T>
+__device__ __forceinline__ void pair_sums(const double* __restrict__ p, int64_t n, double* red, double& d,
+                                          double& b) {
+  const int tid = threadIdx.x;
+  double x = 0.0, y = 0.0;
+  for (int64_t i = tid; i < n; i += T) {
+    x += p[2 * i];
+    y += p[2 * i + 1];
+  }
+  red[2 * tid] = x;
+  red[2 * tid + 1] = y;
+  __syncthreads();
+  for (int h = T / 2; h >= 1; h >>= 1) {
+    if (tid < h) {
+      red[2 * tid] += red[2 * (tid + h)];
+      red[2 * tid + 1] += red[2 * (tid + h) + 1];
+    }
+    __syncthreads();
+  }
+  d = red[0];
+  b = red[1];
+}
+
 // MODE: 0 both passes (prev_in may be null), 1 the difference pass alone,
 // 2 the current-input pass alone.  The modes share the loops, so a split
 // pair of launches gives the partials of one combined launch bit for bit.
@@ -217,9 +244,12 @@ __global__ __launch_bounds__(256) void k_stats_final(
     const double* __restrict__ part, int nparts, int64_t n_cur, int has_history, float c_b,
     float delta_thresh, float ratio_thresh, int32_t* __restrict__ decision,
     float* __restrict__ stats, float* __restrict__ amax_out, const int32_t* __restrict__ gate,
-    int32_t want, const double* __restrict__ sums_in, double* __restrict__ sums_out) {
+    int32_t want, const double* __restrict__ sums_in, double* __restrict__ sums_out, int64_t sums_parts) {
   if (gate != nullptr && *gate != want) return;
   const int tid = threadIdx.x;
+  __shared__ double pr[2 * 256];
+  double din = 0.0, bin = 0.0;
+  if (sums_in != nullptr) pair_sums<256>(sums_in, sums_parts, pr, din, bin);
   double acc[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
   for (int p = tid; p < nparts; p += 256) {
     acc[0] += part[p * P_COUNT + 0];
@@ -248,8 +278,8 @@ __global__ __launch_bounds__(256) void k_stats_final(
     sums_out[1] = red[0][1];
     return;
   }
-  const double diff = sums_in != nullptr ? sums_in[0] : red[0][0];
-  const double base = sums_in != nullptr ? sums_in[1] : red[0][1];
+  const double diff = sums_in != nullptr ? din : red[0][0];
+  const double base = sums_in != nullptr ? bin : red[0][1];
   finish_stats(diff, base, red[0][2], (uint32_t)red[0][3], (float)red[0][4], n_cur, has_history, c_b,
                delta_thresh, ratio_thresh, decision, stats, amax_out);
 }
@@ -262,8 +292,11 @@ __global__ __launch_bounds__(1024) void k_stats_final_rows(
     const double* __restrict__ psum, const uint32_t* __restrict__ pbits,
     const float* __restrict__ ptmax, int nrows, int64_t n_cur, float c_b, float delta_thresh,
     float ratio_thresh, int32_t* __restrict__ decision, float* __restrict__ stats,
-    const double* __restrict__ sums_in) {
+    const double* __restrict__ sums_in, int64_t sums_parts) {
   const int tid = threadIdx.x, lane = tid & 63;
+  __shared__ double pr[2 * 1024];
+  double din = 0.0, bin = 0.0;
+  if (sums_in != nullptr) pair_sums<1024>(sums_in, sums_parts, pr, din, bin);
   // four independent accumulators (fixed order) keep several loads in flight
   double s4[4] = {0.0, 0.0, 0.0, 0.0};
   uint32_t mb = 0u;
@@ -302,7 +335,7 @@ __global__ __launch_bounds__(1024) void k_stats_final_rows(
     rt[0] = fmaxf(rt[0], rt[w]);
   }
   const bool hist = sums_in != nullptr;
-  finish_stats(hist ? sums_in[0] : 0.0, hist ? sums_in[1] : 0.0, rs[0], rb[0], rt[0], n_cur,
+  finish_stats(din, bin, rs[0], rb[0], rt[0], n_cur,
                hist ? 1 : 0, c_b, delta_thresh, ratio_thresh, decision, stats, nullptr);
 }
 
@@ -310,7 +343,7 @@ hipError_t launch_stats(const uint16_t* prev_in, const uint16_t* prev_out, int64
                         const uint16_t* cur, int64_t cur_numel, int hb, float delta_thresh,
                         float ratio_thresh, int32_t* decision, float* stats, float* amax_out,
                         double* partials, const int32_t* gate, int32_t want, hipStream_t s,
-                        const double* delta_sums_in, double* delta_sums_out) {
+                        const double* delta_sums_in, double* delta_sums_out, int64_t delta_parts) {
   const int64_t work = (prev_numel > cur_numel ? prev_numel : cur_numel) / 8;
   int64_t blocks = (work + 255) / 256;
   if (blocks > kStatsMaxBlocks) blocks = kStatsMaxBlocks;
@@ -326,19 +359,19 @@ hipError_t launch_stats(const uint16_t* prev_in, const uint16_t* prev_out, int64
   const float c_b = hb > 0 ? hadamard_scale(hb) : 0.0f;
   hipLaunchKernelGGL(k_stats_final, dim3(1), dim3(256), 0, s, partials, (int)blocks, cur_numel,
                      (hist || delta_sums_in != nullptr) ? 1 : 0, c_b, delta_thresh, ratio_thresh,
-                     decision, stats, amax_out, gate, want, delta_sums_in, delta_sums_out);
+                     decision, stats, amax_out, gate, want, delta_sums_in, delta_sums_out, delta_parts);
   return hipGetLastError();
 }
 
 hipError_t launch_stats_finalize_rows(const double* psum, const uint32_t* pbits, const float* ptmax,
                                       int64_t rows, int64_t cur_numel, int hb, float delta_thresh,
                                       float ratio_thresh, int32_t* decision, float* stats,
-                                      const double* delta_sums_in, hipStream_t s) {
+                                      const double* delta_sums_in, int64_t delta_parts, hipStream_t s) {
   // ptmax holds rows' max |rotated x| already scaled by fl32(1/sqrt(hb)):
   // fl32(max |t| * c_b) = max fl32(|t| * c_b), so the finalize scales by 1
   (void)hb;
   hipLaunchKernelGGL(k_stats_final_rows, dim3(1), dim3(1024), 0, s, psum, pbits, ptmax, (int)rows,
-                     cur_numel, 1.0f, delta_thresh, ratio_thresh, decision, stats, delta_sums_in);
+                     cur_numel, 1.0f, delta_thresh, ratio_thresh, decision, stats, delta_sums_in, delta_parts);
   return hipGetLastError();
 }
 

@@ -27,7 +27,8 @@ DTYPE_F32, DTYPE_BF16, DTYPE_I32 = 0, 1, 2
 OP_SELECT, OP_QUANTIZE, OP_LINEAR, OP_SELECT_Q8 = 0, 1, 2, 3
 
 EXPORTS = ("hdq_select_precision", "hdq_delta_sums", "hdq_select_precision_sums",
-           "hdq_select_quantize_int8", "hdq_linear_dispatch", "hdq_tdc_decide", "hdq_quantize",
+           "hdq_select_quantize_int8", "hdq_linear_dispatch", "hdq_linear_dispatch_delta",
+           "hdq_tdc_decide", "hdq_quantize",
            "hdq_linear", "hdq_workspace_bytes",
            "hdq_status_string", "hdq_version")
 
@@ -40,6 +41,21 @@ class QTensorDesc(_c.Structure):
     _fields_ = [("fmt", _c.c_int32), ("had_block", _c.c_int32), ("rows", _c.c_int64),
                 ("cols", _c.c_int64), ("codes", _p), ("row_scale", _p), ("blk_scale", _p),
                 ("tensor_scale", _p)]
+
+
+class DeltaSlice(_c.Structure):
+    """hdq_delta_slice."""
+    _fields_ = [("prev_in", _p), ("prev_out", _p), ("numel", _c.c_int64), ("chunk_begin", _c.c_int64),
+                ("chunk_end", _c.c_int64), ("partials", _p)]
+
+
+DELTA_CHUNK = 65536       # HDQ_DELTA_CHUNK
+DELTA_MAX_SLICES = 4      # HDQ_DELTA_MAX_SLICES
+
+
+def delta_chunks(numel):
+    """Chunks (and partial pairs) of a module's difference statistic."""
+    return (numel + DELTA_CHUNK - 1) // DELTA_CHUNK
 
 
 class WeightsDesc(_c.Structure):
@@ -58,15 +74,19 @@ def _load():
     L.hdq_delta_sums.restype = _c.c_int
     L.hdq_delta_sums.argtypes = [_p, _p, _c.c_int64, _p, _p, _c.c_size_t, _p]
     L.hdq_select_precision_sums.restype = _c.c_int
-    L.hdq_select_precision_sums.argtypes = [_p, _p, _c.c_int64, _c.c_int64, _c.c_int32, _c.c_float,
-                                            _c.c_float, _p, _p, _p, _c.c_size_t, _p]
+    L.hdq_select_precision_sums.argtypes = [_p, _c.c_int64, _p, _c.c_int64, _c.c_int64, _c.c_int32,
+                                            _c.c_float, _c.c_float, _p, _p, _p, _c.c_size_t, _p]
     L.hdq_select_quantize_int8.restype = _c.c_int
-    L.hdq_select_quantize_int8.argtypes = [_p, _p, _c.c_int64, _c.c_int64, _c.c_int32, _c.c_float,
-                                           _c.c_float, _p, _p, _c.POINTER(QTensorDesc), _p, _c.c_size_t,
-                                           _p]
+    L.hdq_select_quantize_int8.argtypes = [_p, _c.c_int64, _p, _c.c_int64, _c.c_int64, _c.c_int32,
+                                           _c.c_float, _c.c_float, _p, _p, _c.POINTER(QTensorDesc), _p,
+                                           _c.c_size_t, _p]
     L.hdq_linear_dispatch.restype = _c.c_int
     L.hdq_linear_dispatch.argtypes = [_p, _p, _c.POINTER(QTensorDesc), _c.POINTER(QTensorDesc),
                                       _c.c_int64, _c.c_int64, _c.POINTER(WeightsDesc), _p, _c.c_int32, _p]
+    L.hdq_linear_dispatch_delta.restype = _c.c_int
+    L.hdq_linear_dispatch_delta.argtypes = [_p, _p, _c.POINTER(QTensorDesc), _c.POINTER(QTensorDesc),
+                                            _c.c_int64, _c.c_int64, _c.POINTER(WeightsDesc), _p,
+                                            _c.c_int32, _c.POINTER(DeltaSlice), _c.c_int32, _p, _p]
     L.hdq_tdc_decide.restype = _c.c_int
     L.hdq_tdc_decide.argtypes = [_p, _p, _p, _p, _p, _c.c_int64, _c.c_float, _c.c_float, _p]
     L.hdq_quantize.restype = _c.c_int
@@ -126,6 +146,38 @@ def linear_dispatch(decision, x, xq8, xq4, w, y=None, y_dtype=DTYPE_BF16, stream
     st = lib.hdq_linear_dispatch(_ptr(decision), _ptr(x), _c.byref(d8), _c.byref(d4), M, K,
                                  _c.byref(wd), _ptr(y), y_dtype, _stream(stream))
     _check("hdq_linear_dispatch", st)
+    return y
+
+
+def linear_dispatch_delta(decision, x, xq8, xq4, w, slices, queue, y=None, y_dtype=DTYPE_BF16,
+                          stream=None):
+    """hdq_linear_dispatch_delta: linear_dispatch's GEMM, plus the chunk
+    partials of difference statistics on extra workgroups of the launch.
+    slices: up to DELTA_MAX_SLICES tuples (prev_in, prev_out, chunk_begin,
+    chunk_end, partials), partials float64 [delta_chunks(numel), 2];
+    queue: int32 [2] on the device, zero before the first call (each call
+    leaves it zero)."""
+    x = _bf16(x, "x")
+    M, K = x.shape
+    if y is None:
+        dt = {DTYPE_F32: torch.float32, DTYPE_BF16: torch.bfloat16}[y_dtype]
+        y = torch.empty(M, w.N, dtype=dt, device=x.device)
+    arr = (DeltaSlice * max(1, len(slices)))()
+    for i, (pi, po, c0, c1, parts) in enumerate(slices):
+        _bf16(pi, "prev_in")
+        _bf16(po, "prev_out")
+        if pi.numel() != po.numel():
+            raise ValueError("prev_in and prev_out differ in size")
+        if parts.dtype != torch.float64 or parts.numel() < 2 * delta_chunks(pi.numel()):
+            raise ValueError("partials: float64 [delta_chunks(numel), 2] expected")
+        arr[i] = DeltaSlice(_ptr(pi), _ptr(po), pi.numel(), c0, c1, _ptr(parts))
+    if queue.dtype != torch.int32 or queue.numel() < 2:
+        raise ValueError("queue: int32 [2] expected")
+    wd, d8, d4 = w.desc(), xq8.desc(), xq4.desc()
+    st = lib.hdq_linear_dispatch_delta(_ptr(decision), _ptr(x), _c.byref(d8), _c.byref(d4), M, K,
+                                       _c.byref(wd), _ptr(y), y_dtype, arr, len(slices), _ptr(queue),
+                                       _stream(stream))
+    _check("hdq_linear_dispatch_delta", st)
     return y
 
 
@@ -219,6 +271,18 @@ def tdc_decide(sums, state, c, acc, skip=None, tau_skip=0.05, tau_acc=0.15, stre
     return skip
 
 
+def _delta_parts(delta_sums):
+    """(pointer, pairs) of a difference-sums argument: None, or float64 with
+    an even number of elements -- one pair from delta_sums(), or the chunk
+    partials of linear_dispatch_delta()."""
+    if delta_sums is None:
+        return None, 0
+    if delta_sums.dtype != torch.float64 or not delta_sums.is_contiguous() or delta_sums.numel() % 2 or \
+            delta_sums.numel() == 0:
+        raise ValueError("delta sums: expected contiguous float64 pairs")
+    return _ptr(delta_sums), delta_sums.numel() // 2
+
+
 def select_precision_sums(delta_sums, cur_in, had_block=0, delta_thresh=0.1, ratio_thresh=50.0,
                           decision=None, stats=None, ws=None, stream=None):
     """hdq_select_precision_sums: the selection with the difference sums of
@@ -229,7 +293,8 @@ def select_precision_sums(delta_sums, cur_in, had_block=0, delta_thresh=0.1, rat
     decision = torch.empty(1, dtype=torch.int32, device=dev) if decision is None else decision
     stats = torch.empty(5, dtype=torch.float32, device=dev) if stats is None else stats
     ws = _workspace(ws, workspace_bytes(OP_SELECT, rows, cols, 0), dev)
-    st = lib.hdq_select_precision_sums(_ptr(delta_sums), _ptr(cur_in), rows, cols, had_block,
+    dp, parts = _delta_parts(delta_sums)
+    st = lib.hdq_select_precision_sums(dp, parts, _ptr(cur_in), rows, cols, had_block,
                                        delta_thresh, ratio_thresh, _ptr(decision), _ptr(stats),
                                        _ptr(ws), ws.numel(), _stream(stream))
     _check("hdq_select_precision_sums", st)
@@ -249,7 +314,8 @@ def select_quantize_int8(delta_sums, cur_in, had_block, delta_thresh=0.1, ratio_
     out = QuantizedTensor(FMT_INT8_ROW, rows, cols, had_block, dev) if out is None else out
     ws = _workspace(ws, workspace_bytes(OP_SELECT_Q8, rows, cols, 0), dev)
     d = out.desc()
-    st = lib.hdq_select_quantize_int8(_ptr(delta_sums), _ptr(cur_in), rows, cols, had_block,
+    dp, parts = _delta_parts(delta_sums)
+    st = lib.hdq_select_quantize_int8(dp, parts, _ptr(cur_in), rows, cols, had_block,
                                       delta_thresh, ratio_thresh, _ptr(decision), _ptr(stats),
                                       _c.byref(d), _ptr(ws), ws.numel(), _stream(stream))
     _check("hdq_select_quantize_int8", st)

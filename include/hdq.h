@@ -171,9 +171,15 @@ int hdq_select_precision(const void *prev_in, const void *prev_out, int64_t prev
  *   ws, ws_bytes      : device scratch, >= hdq_workspace_bytes(HDQ_OP_SELECT,
  *                       1, numel, numel, 0) bytes.
  * hdq_select_precision_sums:
- *   delta_sums_dev    : device double[2] from hdq_delta_sums (complete
- *                       before this call's kernels run: same stream or an
+ *   delta_sums_dev    : device double[2 * delta_parts]: delta_parts pairs
+ *                       {sum|prev_out - prev_in|, sum|prev_in|} over parts
+ *                       of the tensors, summed in order (delta_parts = 1:
+ *                       the double[2] of hdq_delta_sums; more: the chunk
+ *                       partials of hdq_linear_dispatch_delta).  Complete
+ *                       before this call's kernels run (same stream or an
  *                       event), or NULL for no history.
+ *   delta_parts       : >= 1 when delta_sums_dev is given (HDQ_ERR_SHAPE
+ *                       otherwise); ignored for NULL.
  *   the other arguments are those of hdq_select_precision.
  * The two calls together write what hdq_select_precision writes for the
  * same tensors, bit for bit when numel == rows * cols (the statistics'
@@ -182,8 +188,8 @@ int hdq_select_precision(const void *prev_in, const void *prev_out, int64_t prev
  */
 int hdq_delta_sums(const void *prev_in, const void *prev_out, int64_t numel, double *sums_dev,
                    void *ws, size_t ws_bytes, void *stream);
-int hdq_select_precision_sums(const double *delta_sums_dev, const void *cur_in, int64_t rows,
-                              int64_t cols, int32_t had_block, float delta_thresh,
+int hdq_select_precision_sums(const double *delta_sums_dev, int64_t delta_parts, const void *cur_in,
+                              int64_t rows, int64_t cols, int32_t had_block, float delta_thresh,
                               float ratio_thresh, int32_t *decision_dev, float *stats_dev,
                               void *ws, size_t ws_bytes, void *stream);
 
@@ -192,7 +198,8 @@ int hdq_select_precision_sums(const double *delta_sums_dev, const void *cur_in, 
  * per-token quantization of the same input (steps 1 and 2 for the INT8
  * path): x is read once, the INT8 codes are written whatever the decision
  * turns out to be (a caller then runs the INT8 GEMM gated on the decision).
- *   delta_sums_dev, cur_in, rows, cols, thresholds, decision_dev, stats_dev:
+ *   delta_sums_dev, delta_parts, cur_in, rows, cols, thresholds,
+ *   decision_dev, stats_dev:
  *                 as for hdq_select_precision_sums; had_block must be > 0.
  *   xq8         : caller-allocated INT8_ROW buffers (codes int8 [rows, cols],
  *                 row_scale fp32 [rows]); fmt, had_block, rows, cols are
@@ -205,10 +212,10 @@ int hdq_select_precision_sums(const double *delta_sums_dev, const void *cur_in, 
  * here, per chunk range there).  Rows over 16384 columns run the two passes
  * one after the other.
  */
-int hdq_select_quantize_int8(const double *delta_sums_dev, const void *cur_in, int64_t rows,
-                             int64_t cols, int32_t had_block, float delta_thresh, float ratio_thresh,
-                             int32_t *decision_dev, float *stats_dev, hdq_qtensor *xq8, void *ws,
-                             size_t ws_bytes, void *stream);
+int hdq_select_quantize_int8(const double *delta_sums_dev, int64_t delta_parts, const void *cur_in,
+                             int64_t rows, int64_t cols, int32_t had_block, float delta_thresh,
+                             float ratio_thresh, int32_t *decision_dev, float *stats_dev,
+                             hdq_qtensor *xq8, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * hdq_quantize -- step 2: block-Hadamard rotation fused with quantization
@@ -288,6 +295,56 @@ int hdq_linear(int32_t precision, const int32_t *decision_dev, const void *x,
 int hdq_linear_dispatch(const int32_t *decision_dev, const void *x, const hdq_qtensor *xq8,
                         const hdq_qtensor *xq4, int64_t M, int64_t K, const hdq_weights *w,
                         void *y, int32_t y_dtype, void *stream);
+
+/*
+ * hdq_linear_dispatch_delta -- hdq_linear_dispatch that also computes part
+ * of step 1's difference statistic (summary section one: the previous
+ * step's input/output difference) for later layer calls, inside the same
+ * launch.  The difference depends only on earlier tensors, so it can run
+ * beside this call's compute-bound GEMM: on workgroups appended after the
+ * GEMM's persistent ones, which hold the CUs the GEMM leaves free and,
+ * once its workgroups retire, every CU, claiming chunks from a queue until
+ * none is left.  The launch ends when both are done, so the difference
+ * never shares the GPU with the memory-bound passes of the next call.
+ *
+ * The tensors of one module are split into chunks of HDQ_DELTA_CHUNK
+ * elements; chunk c's {sum|prev_out - prev_in|, sum|prev_in|} (float over
+ * each 8 elements, double beyond, in a fixed order: the same whichever
+ * workgroup runs it) go to partials[2c], partials[2c + 1].  A module's
+ * chunks may be spread over several calls; once all of them have run,
+ * partials is the delta_sums_dev input of hdq_select_quantize_int8 or
+ * hdq_select_precision_sums with delta_parts = ceil(numel / HDQ_DELTA_CHUNK).
+ *
+ *   decision_dev ... stream: as for hdq_linear_dispatch, except that only
+ *              the one-launch kernel's shapes are taken (K a multiple of 256,
+ *              2 * K * max(M, N) < 2^31; HDQ_ERR_SHAPE otherwise).
+ *   slices   : nslices (0..HDQ_DELTA_MAX_SLICES) chunk ranges:
+ *     prev_in, prev_out : device bf16 [numel] each, 16-byte aligned.
+ *     numel             : elements per tensor, a positive multiple of 8.
+ *     chunk_begin/end   : the chunks [chunk_begin, chunk_end) to run here,
+ *                         within [0, ceil(numel / HDQ_DELTA_CHUNK)].
+ *     partials          : device double [2 * ceil(numel / HDQ_DELTA_CHUNK)].
+ *   queue_dev: device uint32[2], zero before the first call; every call
+ *              with work leaves it zero again.  Calls that may overlap
+ *              (other streams) need their own queue.
+ * With nslices = 0 (or empty ranges) this is hdq_linear_dispatch's GEMM
+ * alone.  The GEMM output equals hdq_linear_dispatch's bit for bit.
+ */
+#define HDQ_DELTA_CHUNK 65536
+#define HDQ_DELTA_MAX_SLICES 4
+typedef struct hdq_delta_slice {
+  const void *prev_in;
+  const void *prev_out;
+  int64_t numel;
+  int64_t chunk_begin;
+  int64_t chunk_end;
+  double *partials;
+} hdq_delta_slice;
+
+int hdq_linear_dispatch_delta(const int32_t *decision_dev, const void *x, const hdq_qtensor *xq8,
+                              const hdq_qtensor *xq4, int64_t M, int64_t K, const hdq_weights *w,
+                              void *y, int32_t y_dtype, const hdq_delta_slice *slices,
+                              int32_t nslices, uint32_t *queue_dev, void *stream);
 
 /*
  * hdq_tdc_decide -- the temporal delta cache's skip rule (summary on

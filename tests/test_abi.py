@@ -76,15 +76,16 @@ def test_validation_happens_before_any_launch(hdq):
     assert L.hdq_delta_sums(fake, fake, 64, None, fake, 1 << 20, None) == hdq.ERR_INVALID
     assert L.hdq_delta_sums(fake, fake, 0, fake, fake, 1 << 20, None) == hdq.ERR_SHAPE
     assert L.hdq_delta_sums(fake, fake, 64, fake, None, 0, None) == hdq.ERR_WORKSPACE
-    assert L.hdq_select_precision_sums(fake, None, 4, 64, 0, 0.1, 50.0, fake, fake, fake, 1 << 20, None) == hdq.ERR_INVALID
-    assert L.hdq_select_precision_sums(None, fake, 4, 64, 0, 0.1, 50.0, None, fake, fake, 1 << 20, None) == hdq.ERR_INVALID
-    assert L.hdq_select_precision_sums(None, fake, 4, 60, 16, 0.1, 50.0, fake, fake, fake, 1 << 20, None) == hdq.ERR_SHAPE
-    assert L.hdq_select_precision_sums(None, fake, 0, 64, 0, 0.1, 50.0, fake, fake, fake, 1 << 20, None) == hdq.ERR_SHAPE
-    assert L.hdq_select_precision_sums(fake, fake, 4, 64, 0, 0.1, 50.0, fake, fake, None, 0, None) == hdq.ERR_WORKSPACE
+    assert L.hdq_select_precision_sums(fake, 1, None, 4, 64, 0, 0.1, 50.0, fake, fake, fake, 1 << 20, None) == hdq.ERR_INVALID
+    assert L.hdq_select_precision_sums(None, 0, fake, 4, 64, 0, 0.1, 50.0, None, fake, fake, 1 << 20, None) == hdq.ERR_INVALID
+    assert L.hdq_select_precision_sums(None, 0, fake, 4, 60, 16, 0.1, 50.0, fake, fake, fake, 1 << 20, None) == hdq.ERR_SHAPE
+    assert L.hdq_select_precision_sums(None, 0, fake, 0, 64, 0, 0.1, 50.0, fake, fake, fake, 1 << 20, None) == hdq.ERR_SHAPE
+    assert L.hdq_select_precision_sums(fake, 0, fake, 4, 64, 0, 0.1, 50.0, fake, fake, fake, 1 << 20, None) == hdq.ERR_SHAPE
+    assert L.hdq_select_precision_sums(fake, 1, fake, 4, 64, 0, 0.1, 50.0, fake, fake, None, 0, None) == hdq.ERR_WORKSPACE
     # selection fused with INT8 quantization: no rotation, bad shapes, missing buffers or workspace
     q8 = hdq.QTensorDesc(0, 0, 0, 0, fake, fake, None, None)
-    sq = lambda hb=16, cols=64, rows=4, q=q8, ws=fake, wsb=1 << 20: L.hdq_select_quantize_int8(
-        None, fake, rows, cols, hb, 0.1, 50.0, fake, fake, ctypes.byref(q) if q is not None else None, ws,
+    sq = lambda hb=16, cols=64, rows=4, q=q8, ws=fake, wsb=1 << 20, ds=None, parts=0: L.hdq_select_quantize_int8(
+        ds, parts, fake, rows, cols, hb, 0.1, 50.0, fake, fake, ctypes.byref(q) if q is not None else None, ws,
         wsb, None)
     assert sq(q=None) == hdq.ERR_INVALID
     assert sq(q=hdq.QTensorDesc(0, 0, 0, 0, None, fake, None, None)) == hdq.ERR_INVALID
@@ -93,6 +94,7 @@ def test_validation_happens_before_any_launch(hdq):
     assert sq(rows=0) == hdq.ERR_SHAPE
     assert sq(ws=None, wsb=0) == hdq.ERR_WORKSPACE
     assert sq(rows=100000, wsb=1 << 20) == hdq.ERR_WORKSPACE      # one partial per row does not fit
+    assert sq(ds=fake, parts=0) == hdq.ERR_SHAPE                  # difference sums need >= 1 pair
     assert L.hdq_workspace_bytes(hdq.OP_SELECT_Q8, 17776, 3072, 0, 0) >= 17776 * 48
     # quantize: bad fmt, bad shapes, missing buffers, missing workspace for the amax pre-pass
     q = hdq.QTensorDesc(0, 0, 0, 0, fake, fake, fake, fake)
@@ -149,6 +151,29 @@ def test_validation_happens_before_any_launch(hdq):
     assert dsp(x4=hdq.QTensorDesc(hdq.FMT_NVFP4_MX, 16, 8, 64, fake, None, fake, fake)) == hdq.ERR_UNSUPPORTED
     assert dsp(w=bad4) == hdq.ERR_UNSUPPORTED
     assert dsp(w=hdq.WeightsDesc(32, 64, None, w4, wf)) == hdq.ERR_INVALID
+    # the one-launch linear with difference chunks: slice count, tensors, chunk ranges, shapes
+    x4mx = hdq.QTensorDesc(hdq.FMT_NVFP4_MX, 16, 8, 256, fake, None, fake, fake)
+    w256 = hdq.WeightsDesc(32, 256, fake, hdq.QTensorDesc(hdq.FMT_INT4_ROW, 16, 32, 256, fake, fake, None, None),
+                           hdq.QTensorDesc(hdq.FMT_NVFP4_MX, 16, 32, 256, fake, None, fake, fake))
+    x8k = hdq.QTensorDesc(hdq.FMT_INT8_ROW, 16, 8, 256, fake, fake, None, None)
+    big = ctypes.c_void_p(0x100000)   # 16-byte aligned stand-ins, never dereferenced
+
+    def dd(sl=None, n=1, queue=fake, K=256, w=w256):
+        sl = sl if sl is not None else hdq.DeltaSlice(big, big, 1 << 17, 0, 2, big)
+        arr = (hdq.DeltaSlice * 1)(sl)
+        return L.hdq_linear_dispatch_delta(fake, fake, ctypes.byref(x8k), ctypes.byref(x4mx), 8, K,
+                                           ctypes.byref(w), fake, 1, arr, n, queue, None)
+    assert dd(n=-1) == hdq.ERR_SHAPE
+    assert dd(n=hdq.DELTA_MAX_SLICES + 1) == hdq.ERR_SHAPE
+    assert dd(queue=None) == hdq.ERR_INVALID
+    assert dd(sl=hdq.DeltaSlice(None, big, 1 << 17, 0, 2, big)) == hdq.ERR_INVALID
+    assert dd(sl=hdq.DeltaSlice(big, big, 1 << 17, 0, 2, None)) == hdq.ERR_INVALID
+    assert dd(sl=hdq.DeltaSlice(big, big, 100, 0, 1, big)) == hdq.ERR_SHAPE        # numel % 8
+    assert dd(sl=hdq.DeltaSlice(big, big, 1 << 17, 0, 3, big)) == hdq.ERR_SHAPE    # past the last chunk
+    assert dd(sl=hdq.DeltaSlice(big, big, 1 << 17, 2, 1, big)) == hdq.ERR_SHAPE    # begin > end
+    assert dd(sl=hdq.DeltaSlice(ctypes.c_void_p(0x100008), big, 1 << 17, 0, 2, big)) == hdq.ERR_SHAPE  # alignment
+    w64 = hdq.WeightsDesc(32, 64, fake, w4, hdq.QTensorDesc(hdq.FMT_NVFP4_MX, 16, 32, 64, fake, None, fake, fake))
+    assert dd(K=64, w=w64) == hdq.ERR_SHAPE                 # only the one-launch kernel's shapes
 
 
 def test_product_path_never_uses_the_oracle():

@@ -522,6 +522,102 @@ def test_linear_dispatch_matches_fixed_precision(M, N, K, fmt, y_dtype):
                            ref.view(torch.int16) if ref.dtype == torch.bfloat16 else ref.view(torch.int32)), prec
 
 
+def _delta_pair(M, K, s, seed):
+    rng = synth.rng_for(115, seed)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    return synth.to_bf16_bits(x), synth.to_bf16_bits(x + rng.standard_normal((M, K)).astype(np.float32) * np.float32(s))
+
+
+def test_linear_dispatch_delta_chunks_across_launches():
+    """hdq_linear_dispatch_delta: the GEMM output is hdq_linear_dispatch's bit
+    for bit; the difference statistic of two modules, their chunks spread
+    over three launches (one of them empty), matches hdq_delta_sums and the
+    oracle, drives the fused selection as the one-pair sums do, and the queue
+    is left zero."""
+    M, N, K, hb = 600, 520, 512, 32
+    say(f"linear dispatch + delta chunks M={M} N={N} K={K}")
+    x16 = synth.lognormal_tokens(M, K, synth.rng_for(116, 0))
+    w16 = synth.gaussian(N, K, 0.02, synth.rng_for(116, 1))
+    W = hdq.LinearWeights(to_dev(w16), hb, fp4_fmt=hdq.FMT_NVFP4_MX)
+    xd = to_dev(x16)
+    xq8 = hdq.quantize(xd, hb, hdq.FMT_INT8_ROW)
+    xq4 = hdq.quantize(xd, hb, hdq.FMT_NVFP4_MX)
+    # module A: 300 x 1000 (5 chunks, the last partial); module B: 1024 x 2048 (32 chunks)
+    a_in, a_out = _delta_pair(300, 1000, 0.2, 1)
+    b_in, b_out = _delta_pair(1024, 2048, 0.07, 2)
+    ai, ao, bi, bo = (to_dev(t) for t in (a_in, a_out, b_in, b_out))
+    na, nb = hdq.delta_chunks(ai.numel()), hdq.delta_chunks(bi.numel())
+    assert (na, nb) == (5, 32)
+    pa = torch.full((na, 2), float("nan"), dtype=torch.float64, device=DEV)
+    pb = torch.full((nb, 2), float("nan"), dtype=torch.float64, device=DEV)
+    queue = torch.zeros(2, dtype=torch.int32, device=DEV)
+    dec = torch.empty(1, dtype=torch.int32, device=DEV)
+    plan = [(hdq.PREC_INT8, [(ai, ao, 0, na), (bi, bo, 0, 10)]),
+            (hdq.PREC_NVFP4, []),
+            (hdq.PREC_BF16, [(bi, bo, 10, 31), (bi, bo, 31, 32)])]
+    for prec, sl in plan:
+        dec.fill_(prec)
+        y = hdq.linear_dispatch_delta(dec, xd, xq8, xq4, W, [s + (pa if s[0] is ai else pb,) for s in sl], queue)
+        ref = hdq.linear_dispatch(dec, xd, xq8, xq4, W)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), ref.view(torch.int16)), prec
+        assert queue.cpu().tolist() == [0, 0]
+    for parts, pi, po, t_in, t_out in ((pa, ai, ao, a_in, a_out), (pb, bi, bo, b_in, b_out)):
+        got = parts.cpu().numpy()
+        assert np.isfinite(got).all()                       # every chunk ran once
+        one = hdq.delta_sums(pi, po).cpu().numpy()
+        tot = got.sum(axis=0)
+        assert np.allclose(tot, one, rtol=1e-12, atol=0)
+        ref = O.stats(t_in, t_out, t_in, 0)[0]     # no rotation: module A's 1000 columns
+        assert abs(tot[0] / tot[1] - ref) <= 2e-6 * ref
+    # the chunk partials as the selection's difference input: the same
+    # decision and statistics as with the one-pair sums, delta to rounding
+    cur16 = x16
+    cd = to_dev(cur16)
+    d1, s1, _ = hdq.select_quantize_int8(hdq.delta_sums(bi, bo), cd, hb)
+    d2, s2, _ = hdq.select_quantize_int8(pb, cd, hb)
+    torch.cuda.synchronize()
+    assert int(d1.item()) == int(d2.item())
+    s1, s2 = s1.cpu().numpy(), s2.cpu().numpy()
+    assert np.array_equal(s1[1:], s2[1:]) and abs(s1[0] - s2[0]) <= 1e-6 * s1[0]
+    d3, s3 = hdq.select_precision_sums(pb, cd, hb)
+    torch.cuda.synchronize()
+    assert int(d3.item()) == int(d1.item()) and abs(float(s3[0]) - s1[0]) <= 1e-6 * s1[0]
+
+
+def test_linear_dispatch_delta_full_size_schedule_shape():
+    """The schedule's largest difference (FFN-down input, 17776 x 12288: 3333
+    chunks) beside a full-size GEMM, in two launches; sums as hdq_delta_sums."""
+    M, N, K, hb = 17776, 3072, 3072, 128
+    say("linear dispatch + delta, full size")
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(5)
+    x = synth.device_gaussian((M, K), 1.0, gen, DEV)
+    w = synth.device_gaussian((N, K), 0.02, gen, DEV)
+    pi = synth.device_gaussian((M, 12288), 1.0, gen, DEV)
+    po = (pi.float() + 0.1 * synth.device_gaussian((M, 12288), 1.0, gen, DEV).float()).to(torch.bfloat16)
+    W = hdq.LinearWeights(w, hb, fp4_fmt=hdq.FMT_NVFP4_MX)
+    xq8 = hdq.quantize(x, hb, hdq.FMT_INT8_ROW)
+    xq4 = hdq.quantize(x, hb, hdq.FMT_NVFP4_MX)
+    n = hdq.delta_chunks(pi.numel())
+    parts = torch.full((n, 2), float("nan"), dtype=torch.float64, device=DEV)
+    queue = torch.zeros(2, dtype=torch.int32, device=DEV)
+    dec = torch.full((1,), hdq.PREC_INT8, dtype=torch.int32, device=DEV)
+    y1 = hdq.linear_dispatch_delta(dec, x, xq8, xq4, W, [(pi, po, 0, 1000, parts)], queue)
+    ref = hdq.linear_dispatch(dec, x, xq8, xq4, W)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), ref.view(torch.int16))
+    dec.fill_(hdq.PREC_NVFP4)
+    y2 = hdq.linear_dispatch_delta(dec, x, xq8, xq4, W, [(pi, po, 1000, n, parts)], queue)
+    ref = hdq.linear_dispatch(dec, x, xq8, xq4, W)
+    one = hdq.delta_sums(pi, po)
+    torch.cuda.synchronize()
+    assert torch.equal(y2.view(torch.int16), ref.view(torch.int16))
+    got = parts.cpu().numpy()
+    assert np.isfinite(got).all() and queue.cpu().tolist() == [0, 0]
+    assert np.allclose(got.sum(axis=0), one.cpu().numpy(), rtol=1e-12, atol=0)
+
+
 def test_repeat_runs_are_bitwise_identical():
     M, N, K, hb = 513, 384, 1024, 128
     x16 = synth.lognormal_tokens(M, K, synth.rng_for(111, 0))
