@@ -378,6 +378,24 @@ def run_schedule_step(S, args, hdq, recipe, events=None, side_events=None):
     return len(calls)
 
 
+def embed_bytes(S, args, synth):
+    """Per layer call: the difference bytes (both tensors) its GEMM launch
+    carries under --delta embed, else 0."""
+    calls = [(t, b, li) for t in range(args.timesteps) for b in range(args.blocks)
+             for li in range(len(synth.SCHEDULE_LAYERS))]
+    if args.delta != "embed":
+        return [0] * len(calls)
+    from bit_quantized_video_amd.hdq import DELTA_CHUNK as hdq_chunk
+    out = []
+    for slices in S["embed"]:
+        nb = 0
+        for j, c0, c1 in slices:
+            numel = S["M"] * synth.SCHEDULE_LAYERS[calls[j][2]][1]
+            nb += 4 * (min(c1 * hdq_chunk, numel) - c0 * hdq_chunk)
+        out.append(nb)
+    return out
+
+
 def schedule_kernel_times(S, args, events_per_step, synth, recipe, side_per_step=None):
     """Per-kernel durations from the recorded events, attributed by the
     device decision of each layer call."""
@@ -385,6 +403,7 @@ def schedule_kernel_times(S, args, events_per_step, synth, recipe, side_per_step
     decisions = S["dec"].cpu().numpy().reshape(args.timesteps, args.blocks, -1)
     kt = KernelTimes()
     inline = args.delta == "inline"
+    carried = embed_bytes(S, args, synth)
     fused = args.fuse == "on"
     dispatch = args.dispatch == "on"
     for s_i, evs in enumerate(events_per_step):
@@ -422,7 +441,7 @@ def schedule_kernel_times(S, args, events_per_step, synth, recipe, side_per_step
                         if dispatch:
                             # one launch (slot 3) ran the decided precision's GEMM
                             if on and dt[3] is not None:
-                                kt.add(kind, dt[3], flops, gemm_bytes(M, N, K, prec, recipe))
+                                kt.add(kind, dt[3], flops, gemm_bytes(M, N, K, prec, recipe) + carried[k - 1])
                             continue
                         if dt[i] is not None:
                             kt.add(kind if on else kind + "_gated_off", dt[i], flops if on else 0,
