@@ -217,14 +217,15 @@ int hdq_select_quantize_int8(const double* delta_sums_dev, int64_t delta_parts, 
                                           xq8->row_scale, nullptr, 0, s));
 }
 
-int hdq_tdc_decide(const double* sums_dev, const int32_t* state_dev, float* c_dev, float* acc_dev,
-                   int32_t* skip_dev, int64_t n, float tau_skip, float tau_acc, void* stream) {
+int hdq_tdc_decide(const double* sums_dev, const int64_t* parts_offsets_dev, const int32_t* state_dev,
+                   float* c_dev, float* acc_dev, int32_t* skip_dev, int64_t n, float tau_skip,
+                   float tau_acc, void* stream) {
   if (sums_dev == nullptr || state_dev == nullptr || c_dev == nullptr || acc_dev == nullptr ||
       skip_dev == nullptr)
     return HDQ_ERR_INVALID;
   if (n <= 0 || n > 0x7fffffff) return HDQ_ERR_SHAPE;
-  return hip_status(launch_tdc_decide(sums_dev, state_dev, c_dev, acc_dev, skip_dev, n, tau_skip,
-                                      tau_acc, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_tdc_decide(sums_dev, parts_offsets_dev, state_dev, c_dev, acc_dev, skip_dev, n,
+                                      tau_skip, tau_acc, static_cast<hipStream_t>(stream)));
 }
 
 int hdq_linear_dispatch(const int32_t* decision_dev, const void* x, const hdq_qtensor* xq8,

@@ -79,8 +79,11 @@ hipError_t launch_stats(const uint16_t* prev_in, const uint16_t* prev_out, int64
 // The finalize over one partial per row, struct-of-arrays: psum = sum |x|,
 // pbits = max bf16 magnitude bits, ptmax = max |rotated x| (scaled).
 // Temporal delta cache skip rule over n modules.
-hipError_t launch_tdc_decide(const double* sums, const int32_t* state, float* c, float* acc,
-                             int32_t* skip, int64_t n, float tau_skip, float tau_acc, hipStream_t s);
+// parts_off (device int64 [n + 1]) or null: module i's change sums are the
+// pairs [parts_off[i], parts_off[i + 1]) of sums, else sums[i].
+hipError_t launch_tdc_decide(const double* sums, const int64_t* parts_off, const int32_t* state, float* c,
+                             float* acc, int32_t* skip, int64_t n, float tau_skip, float tau_acc,
+                             hipStream_t s);
 hipError_t launch_stats_finalize_rows(const double* psum, const uint32_t* pbits, const float* ptmax,
                                       int64_t rows, int64_t cur_numel, int hb, float delta_thresh,
                                       float ratio_thresh, int32_t* decision, float* stats,

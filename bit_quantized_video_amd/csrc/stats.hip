@@ -383,6 +383,26 @@ hipError_t launch_stats_finalize_rows(const double* psum, const uint32_t* pbits,
 // sums = {sum|new - earlier|, sum|earlier|}) resets its accumulator and
 // takes a new relative change c; every module then reuses its cache at the
 // next step when c < tau_skip and fl32(acc + c) <= tau_acc, adding c to acc.
+// The rule for module i from its state, change sums and accumulator.
+__device__ __forceinline__ void tdc_rule(int i, int st, double diff, double base, float* __restrict__ c,
+                                         float* __restrict__ acc, int32_t* __restrict__ skip,
+                                         float tau_skip, float tau_acc) {
+  float ci = c[i], ai = acc[i];
+  if (st != 0) {
+    ai = 0.0f;
+    if (st == 1) {
+      ci = __builtin_nanf("");
+    } else {
+      ci = (float)(base == 0.0 ? (diff == 0.0 ? 0.0 : __builtin_inf()) : diff / base);
+    }
+  }
+  const float next = ai + ci;
+  const bool sk = ci < tau_skip && next <= tau_acc;
+  c[i] = ci;
+  acc[i] = sk ? next : ai;
+  skip[i] = sk ? 1 : 0;
+}
+
 __global__ __launch_bounds__(256) void k_tdc_decide(const double* __restrict__ sums,
                                                     const int32_t* __restrict__ state,
                                                     float* __restrict__ c, float* __restrict__ acc,
@@ -390,26 +410,35 @@ __global__ __launch_bounds__(256) void k_tdc_decide(const double* __restrict__ s
                                                     float tau_acc) {
   for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
     const int st = state[i];
-    float ci = c[i], ai = acc[i];
-    if (st != 0) {
-      ai = 0.0f;
-      if (st == 1) {
-        ci = __builtin_nanf("");
-      } else {
-        const double diff = sums[2 * i], base = sums[2 * i + 1];
-        ci = (float)(base == 0.0 ? (diff == 0.0 ? 0.0 : __builtin_inf()) : diff / base);
-      }
-    }
-    const float next = ai + ci;
-    const bool s = ci < tau_skip && next <= tau_acc;
-    c[i] = ci;
-    acc[i] = s ? next : ai;
-    skip[i] = s ? 1 : 0;
+    tdc_rule(i, st, st == 2 ? sums[2 * i] : 0.0, st == 2 ? sums[2 * i + 1] : 0.0, c, acc, skip, tau_skip,
+             tau_acc);
   }
 }
 
-hipError_t launch_tdc_decide(const double* sums, const int32_t* state, float* c, float* acc,
-                             int32_t* skip, int64_t n, float tau_skip, float tau_acc, hipStream_t s) {
+// Change sums given as pairs: module i's are pairs [off[i], off[i + 1]),
+// summed in a fixed order by the module's workgroup.
+__global__ __launch_bounds__(256) void k_tdc_decide_parts(const double* __restrict__ parts,
+                                                          const int64_t* __restrict__ off,
+                                                          const int32_t* __restrict__ state,
+                                                          float* __restrict__ c, float* __restrict__ acc,
+                                                          int32_t* __restrict__ skip, float tau_skip,
+                                                          float tau_acc) {
+  __shared__ double red[2 * 256];
+  const int i = blockIdx.x;
+  const int st = state[i];
+  double d = 0.0, b = 0.0;
+  if (st == 2) pair_sums<256>(parts + 2 * off[i], off[i + 1] - off[i], red, d, b);
+  if (threadIdx.x == 0) tdc_rule(i, st, d, b, c, acc, skip, tau_skip, tau_acc);
+}
+
+hipError_t launch_tdc_decide(const double* sums, const int64_t* parts_off, const int32_t* state, float* c,
+                             float* acc, int32_t* skip, int64_t n, float tau_skip, float tau_acc,
+                             hipStream_t s) {
+  if (parts_off != nullptr) {
+    hipLaunchKernelGGL(k_tdc_decide_parts, dim3((unsigned)n), dim3(256), 0, s, sums, parts_off, state, c,
+                       acc, skip, tau_skip, tau_acc);
+    return hipGetLastError();
+  }
   int64_t blocks = (n + 255) / 256;
   if (blocks > 1024) blocks = 1024;
   hipLaunchKernelGGL(k_tdc_decide, dim3((unsigned)blocks), dim3(256), 0, s, sums, state, c, acc, skip,

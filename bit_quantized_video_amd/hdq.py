@@ -88,7 +88,7 @@ def _load():
                                             _c.c_int64, _c.c_int64, _c.POINTER(WeightsDesc), _p,
                                             _c.c_int32, _c.POINTER(DeltaSlice), _c.c_int32, _p, _p]
     L.hdq_tdc_decide.restype = _c.c_int
-    L.hdq_tdc_decide.argtypes = [_p, _p, _p, _p, _p, _c.c_int64, _c.c_float, _c.c_float, _p]
+    L.hdq_tdc_decide.argtypes = [_p, _p, _p, _p, _p, _p, _c.c_int64, _c.c_float, _c.c_float, _p]
     L.hdq_quantize.restype = _c.c_int
     L.hdq_quantize.argtypes = [_p, _c.c_int64, _c.c_int64, _c.c_int32, _c.c_int32, _p, _p,
                                _c.POINTER(QTensorDesc), _p, _c.c_size_t, _p]
@@ -256,16 +256,22 @@ def delta_sums(prev_in, prev_out, sums=None, ws=None, stream=None):
     return sums
 
 
-def tdc_decide(sums, state, c, acc, skip=None, tau_skip=0.05, tau_acc=0.15, stream=None):
-    """hdq_tdc_decide over n modules: sums float64 [n, 2], state int32 [n],
-    c and acc float32 [n] (updated in place); returns skip int32 [n]."""
+def tdc_decide(sums, state, c, acc, skip=None, tau_skip=0.05, tau_acc=0.15, stream=None, offsets=None):
+    """hdq_tdc_decide over n modules: sums float64 [n, 2] (or, with offsets
+    int64 [n + 1], pairs [P, 2] of which module i's are rows offsets[i] ..
+    offsets[i + 1] - 1), state int32 [n], c and acc float32 [n] (updated in
+    place); returns skip int32 [n]."""
     n = state.numel()
-    for t, dt, shape in ((sums, torch.float64, (n, 2)), (state, torch.int32, (n,)),
-                         (c, torch.float32, (n,)), (acc, torch.float32, (n,))):
+    pairs = (n, 2) if offsets is None else (sums.shape[0], 2)
+    checks = [(sums, torch.float64, pairs), (state, torch.int32, (n,)),
+              (c, torch.float32, (n,)), (acc, torch.float32, (n,))]
+    if offsets is not None:
+        checks.append((offsets, torch.int64, (n + 1,)))
+    for t, dt, shape in checks:
         if t.dtype != dt or tuple(t.shape) != shape or not t.is_contiguous():
             raise ValueError(f"tdc_decide: expected {dt} {shape} contiguous, got {t.dtype} {tuple(t.shape)}")
     skip = torch.empty(n, dtype=torch.int32, device=state.device) if skip is None else skip
-    st = lib.hdq_tdc_decide(_ptr(sums), _ptr(state), _ptr(c), _ptr(acc), _ptr(skip), n,
+    st = lib.hdq_tdc_decide(_ptr(sums), _ptr(offsets), _ptr(state), _ptr(c), _ptr(acc), _ptr(skip), n,
                             float(tau_skip), float(tau_acc), _stream(stream))
     _check("hdq_tdc_decide", st)
     return skip

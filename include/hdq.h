@@ -356,7 +356,11 @@ int hdq_linear_dispatch_delta(const int32_t *decision_dev, const void *x, const 
  *   sums_dev : device double [n][2]; for a module computed at this step
  *              with an earlier output, {sum|new - earlier|, sum|earlier|}
  *              (hdq_delta_sums(earlier, new, ...) writes exactly this);
- *              ignored otherwise.
+ *              ignored otherwise.  With parts_offsets_dev: pairs of partial
+ *              sums, module i's being pairs [off[i], off[i + 1]), summed in a
+ *              fixed order (e.g. the chunk partials hdq_linear_dispatch_delta
+ *              writes for the two outputs while later modules' GEMMs run).
+ *   parts_offsets_dev: NULL, or device int64 [n + 1], nondecreasing.
  *   state_dev: device int32 [n]: 0 skipped at this step, 1 computed with no
  *              earlier output, 2 computed with one (sums valid).
  *   c_dev    : device float [n], in/out: relative change between the last
@@ -370,8 +374,9 @@ int hdq_linear_dispatch_delta(const int32_t *decision_dev, const void *x, const 
  * Errors: HDQ_ERR_INVALID for a null pointer, HDQ_ERR_SHAPE for n <= 0 or
  * n >= 2^31.  The state arrays are the caller's; one call per step.
  */
-int hdq_tdc_decide(const double *sums_dev, const int32_t *state_dev, float *c_dev, float *acc_dev,
-                   int32_t *skip_dev, int64_t n, float tau_skip, float tau_acc, void *stream);
+int hdq_tdc_decide(const double *sums_dev, const int64_t *parts_offsets_dev, const int32_t *state_dev,
+                   float *c_dev, float *acc_dev, int32_t *skip_dev, int64_t n, float tau_skip,
+                   float tau_acc, void *stream);
 
 /* Scratch bytes an entry point needs.  op = HDQ_OP_SELECT: (M = rows,
  * K = cols, N = prev_numel); HDQ_OP_SELECT_Q8: (M = rows, K = cols);

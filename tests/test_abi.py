@@ -131,10 +131,10 @@ def test_validation_happens_before_any_launch(hdq):
     xq = hdq.QTensorDesc(hdq.FMT_INT8_ROW, 32, 8, 64, fake, fake, None, None)
     assert ok(1, xq=ctypes.byref(xq)) == hdq.ERR_SHAPE     # block differs from the weights'
     # TDC rule: null pointers, bad module count
-    assert L.hdq_tdc_decide(None, fake, fake, fake, fake, 4, 0.05, 0.15, None) == hdq.ERR_INVALID
-    assert L.hdq_tdc_decide(fake, fake, fake, fake, None, 4, 0.05, 0.15, None) == hdq.ERR_INVALID
-    assert L.hdq_tdc_decide(fake, fake, fake, fake, fake, 0, 0.05, 0.15, None) == hdq.ERR_SHAPE
-    assert L.hdq_tdc_decide(fake, fake, fake, fake, fake, 1 << 31, 0.05, 0.15, None) == hdq.ERR_SHAPE
+    assert L.hdq_tdc_decide(None, None, fake, fake, fake, fake, 4, 0.05, 0.15, None) == hdq.ERR_INVALID
+    assert L.hdq_tdc_decide(fake, fake, fake, fake, fake, None, 4, 0.05, 0.15, None) == hdq.ERR_INVALID
+    assert L.hdq_tdc_decide(fake, None, fake, fake, fake, fake, 0, 0.05, 0.15, None) == hdq.ERR_SHAPE
+    assert L.hdq_tdc_decide(fake, fake, fake, fake, fake, fake, 1 << 31, 0.05, 0.15, None) == hdq.ERR_SHAPE
     # one-launch linear: every operand the decision may pick must be present and consistent
     x8 = hdq.QTensorDesc(hdq.FMT_INT8_ROW, 16, 8, 64, fake, fake, None, None)
     x4 = hdq.QTensorDesc(hdq.FMT_NVFP4, 16, 8, 64, fake, None, fake, fake)

@@ -807,6 +807,37 @@ def test_tdc_decide_matches_oracle():
     assert 0.1 < ref.mean() < 0.9
 
 
+def test_tdc_decide_with_partial_sums_matches_oracle():
+    """hdq_tdc_decide with change sums given as pairs per module (offsets): the
+    pairs are dyadic, so every summation order gives the totals exactly, and
+    the rule must match the oracle's on those totals bit for bit."""
+    say("tdc decide, partial sums")
+    rng = np.random.default_rng(121)
+    n = 700
+    state = rng.integers(0, 3, n).astype(np.int32)
+    counts = rng.integers(0, 40, n)
+    counts[state == 2] = np.maximum(counts[state == 2], 1)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    base_p = rng.integers(0, 2000, off[-1]).astype(np.float64) * 2.0 ** -10
+    diff_p = np.floor(base_p * rng.uniform(0.0, 0.12, off[-1]) * 1024.0) * 2.0 ** -10
+    parts = np.stack([diff_p, base_p], axis=1)
+    tot = np.stack([np.add.reduceat(parts[:, 0], off[:-1]) if off[-1] else np.zeros(n),
+                    np.add.reduceat(parts[:, 1], off[:-1]) if off[-1] else np.zeros(n)], axis=1)
+    tot[counts == 0] = 0.0                   # reduceat repeats the next value for empty ranges
+    c = rng.uniform(0.0, 0.1, n).astype(np.float32)
+    c[rng.random(n) < 0.1] = np.nan
+    acc = rng.uniform(0.0, 0.15, n).astype(np.float32)
+    gc, gacc = torch.from_numpy(c.copy()).to(DEV), torch.from_numpy(acc.copy()).to(DEV)
+    skip = hdq.tdc_decide(torch.from_numpy(parts).to(DEV), torch.from_numpy(state).to(DEV), gc, gacc,
+                          offsets=torch.from_numpy(off).to(DEV))
+    torch.cuda.synchronize()
+    ref = O.tdc_decide(tot, state, c, acc)
+    assert np.array_equal(skip.cpu().numpy(), ref)
+    assert np.array_equal(gc.cpu().numpy().view(np.uint32), c.view(np.uint32))
+    assert np.array_equal(gacc.cpu().numpy().view(np.uint32), acc.view(np.uint32))
+    assert 0.1 < ref.mean() < 0.9
+
+
 def test_tdc_trajectory_matches_oracle():
     """Three linear modules over a trajectory whose input changes shrink step
     by step: computed modules run the INT8 linear, the change statistic of
