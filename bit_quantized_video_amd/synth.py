@@ -64,6 +64,22 @@ def lognormal_tokens(M, K, rng, sigma=0.5, chunk=2048):
     return out
 
 
+def smooth_video_tokens(F, H, W, K, rng, outlier_frac=0.01, factor=20.0, noise=0.05):
+    """Video tokens of an F x H x W grid (frame outermost) whose values vary
+    slowly in space and time: per channel a base value (1% of channels x20),
+    linear ramps over frames, rows and columns, and a little independent
+    noise.  bf16 bits [F * H * W, K]."""
+    base = rng.standard_normal(K).astype(np.float32)
+    base[outlier_channels(K, outlier_frac, rng)] *= np.float32(factor)
+    ramps = rng.standard_normal((3, K)).astype(np.float32) * np.float32(0.3)
+    f = np.arange(F, dtype=np.float32)[:, None, None, None] / np.float32(max(F, 1))
+    h = np.arange(H, dtype=np.float32)[None, :, None, None] / np.float32(max(H, 1))
+    w = np.arange(W, dtype=np.float32)[None, None, :, None] / np.float32(max(W, 1))
+    x = base + f * ramps[0] + h * ramps[1] + w * ramps[2]
+    x = x + rng.standard_normal((F, H, W, K)).astype(np.float32) * np.float32(noise)
+    return to_bf16_bits(x.reshape(F * H * W, K))
+
+
 def gelu_student_t(M, K, rng, nu=3.0, chunk=1024):
     """GELU (exact erf form) of N(0, 1) plus unit-scale Student-t(nu) noise:
     the input of an FFN down-projection with heavy tails."""

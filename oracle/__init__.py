@@ -57,6 +57,10 @@ def lib():
             "orc_decide": (_int, [_int, _f64, _f64, _f64, _f64]),
             "orc_tdc_decide": (None, [_p, _p, _p, _p, _p, _i64, _f32, _f32]),
             "orc_num_threads": (_int, []),
+            "orc_dq_cube_of": (None, [_i64, _i64, _i64, _int, _int, _int, _p]),
+            "orc_e4m3s_decode": (_f32, [ctypes.c_uint8]),
+            "orc_dq_core": (None, [_p, _i64, _i64, _i64, _i64, _int, _int, _int, _p, _p]),
+            "orc_dq_delta": (None, [_p, _i64, _i64, _i64, _i64, _int, _int, _int, _p, _p, _p]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -267,6 +271,71 @@ def gemm_bf16(x16, w16):
     y = np.empty((M, N), np.float64)
     lib().orc_gemm_bf16(_ptr(x16), _ptr(w16), M, N, K, _ptr(y))
     return y
+
+
+# ----------------------------------------------------------- DeltaQuant
+# Cube-delta quantization of video tokens (the DeltaQuant abstract on the
+# paper-radar CVPR 2026 listing); the readings are stated in hdq_oracle.c.
+
+def dq_cubes(F, H, W, cube):
+    cf, ch, cw = cube
+    return -(-F // cf) * -(-H // ch) * -(-W // cw)
+
+
+def dq_cube_of(F, H, W, cube):
+    out = np.empty(F * H * W, np.int32)
+    lib().orc_dq_cube_of(F, H, W, *cube, _ptr(out))
+    return out
+
+
+def e4m3s_decode(codes):
+    """Signed E4M3 bytes to float32."""
+    L = lib()
+    table = np.array([L.orc_e4m3s_decode(c) for c in range(256)], np.float32)
+    return table[np.asarray(codes, np.uint8)]
+
+
+def dq_core(x16, F, H, W, cube):
+    """Core tokens: (signed E4M3 codes uint8 [cubes, K], scales float32 [cubes])."""
+    x16 = _c(x16, np.uint16)
+    K = x16.shape[1]
+    assert x16.shape[0] == F * H * W
+    n = dq_cubes(F, H, W, cube)
+    codes = np.empty((n, K), np.uint8)
+    scale = np.empty(n, np.float32)
+    lib().orc_dq_core(_ptr(x16), F, H, W, K, *cube, _ptr(codes), _ptr(scale))
+    return codes, scale
+
+
+def dq_delta(x16, F, H, W, cube, codes, scale):
+    """Each token minus its cube's stored core, float32 [F H W, K]."""
+    x16 = _c(x16, np.uint16)
+    codes = _c(codes, np.uint8)
+    scale = _c(scale, np.float32)
+    K = x16.shape[1]
+    d = np.empty((F * H * W, K), np.float32)
+    lib().orc_dq_delta(_ptr(x16), F, H, W, K, *cube, _ptr(codes), _ptr(scale), _ptr(d))
+    return d
+
+
+def dq_quantize(x16, F, H, W, cube, mx=0):
+    """The whole activation side: core codes and scales, the differences, and
+    their NVFP4 codes, block scales and tensor scale (amax of |difference|)."""
+    codes, scale = dq_core(x16, F, H, W, cube)
+    d = dq_delta(x16, F, H, W, cube, codes, scale)
+    amax = np.float32(np.abs(d).max()) if d.size else np.float32(0)
+    dc, de, st = quant_nvfp4_rotated(d, amax, mx)
+    return dict(core=codes, core_scale=scale, delta=d, delta_amax=amax, codes=dc, blk=de, s_t=st)
+
+
+def dq_linear(q, wc, we, wst, K, F, H, W, cube):
+    """y = (difference codes) x W^T + (its cube's FP8 core) x W^T for every
+    token, float64, W the NVFP4 weights (codes, block scales, tensor scale)."""
+    yd = gemm_nvfp4(q["codes"], q["blk"], q["s_t"], wc, we, wst, K)
+    wdec = dequant_nvfp4(wc, we, 1.0, K).astype(np.float64)       # e2m1 x block scale, exact
+    core = e4m3s_decode(q["core"]).astype(np.float64) * q["core_scale"].astype(np.float64)[:, None]
+    yc = (core @ wdec.T) * float(wst)
+    return yd + yc[dq_cube_of(F, H, W, cube)]
 
 
 # ------------------------------------------------------------ selection

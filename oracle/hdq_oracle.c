@@ -27,6 +27,11 @@
  *   [G2] "6Bit-Diffusion: Inference-Time Mixed-Precision Quantization for
  *        Video Diffusion Models" (gist.science explainer), section 2 (DMPQ:
  *        stable steps NVFP4, unstable steps INT8); [G4] its section 4 (PDR).
+ *   [D1] "DeltaQuant: 4-bit Video Diffusion Models with Spatiotemporal
+ *        Delta Smoothing" (paper-radar CVPR 2026 listing), abstract:
+ *        activations are grouped in local 3D spatiotemporal cubes; each
+ *        cube's mean token is the core token, kept in FP8; only the small
+ *        differences from it (delta tokens) are quantized to 4 bits.
  *   [OCP] The pages name NVFP4 but never define it.  Its element and scale
  *        encodings are the public OCP Microscaling Formats v1.0 ones: FP4
  *        E2M1 elements, FP8 E4M3 ("FN": no infinities, one NaN code)
@@ -580,6 +585,90 @@ void orc_tdc_decide(const double *sums, const int32_t *state, float *c, float *a
             acc[i] = next;
         skip[i] = s;
     }
+}
+
+/* ------------------------------------------------------------ DeltaQuant
+ * [D1].  Video tokens form a frames x height x width grid, row-major with the
+ * frame outermost (token (f, h, w) is row (f * H + h) * W + w).  Cubes are
+ * cf x ch x cw blocks of it, ragged at the far edges, numbered the same way
+ * over the cube grid.  Readings the abstract leaves open:
+ *   - the core token is the float32 mean: the tokens' values summed in token
+ *     order, then divided by their count;
+ *   - FP8 is E4M3 [OCP] with one fp32 scale per core token, s = max|c| / 448
+ *     (0 and all-zero codes when max|c| < ORC_TINY); a value's code is the
+ *     nearest E4M3 of |c| / s with the sign in bit 7 (a zero magnitude is
+ *     stored as +0);
+ *   - a token's difference is taken from the stored core: fl32(x - fl32(E * s));
+ *   - the differences are quantized to NVFP4 (4 bits [D1]; the format of this
+ *     path), without rotation.
+ */
+static int64_t orc_ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+/* Cube of every token. */
+void orc_dq_cube_of(int64_t F, int64_t H, int64_t W, int cf, int ch, int cw, int32_t *cube)
+{
+    int64_t nH = orc_ceil_div(H, ch), nW = orc_ceil_div(W, cw);
+    for (int64_t f = 0; f < F; f++)
+        for (int64_t h = 0; h < H; h++)
+            for (int64_t w = 0; w < W; w++)
+                cube[(f * H + h) * W + w] = (int32_t)(((f / cf) * nH + h / ch) * nW + w / cw);
+}
+
+/* Signed E4M3 byte. */
+float orc_e4m3s_decode(uint8_t c)
+{
+    float v = orc_e4m3_decode((uint8_t)(c & 0x7f));
+    return (c & 0x80) ? -v : v;
+}
+
+/* Core tokens: codes [ncubes, K] (signed E4M3), scale [ncubes]. */
+void orc_dq_core(const uint16_t *x, int64_t F, int64_t H, int64_t W, int64_t K, int cf, int ch, int cw,
+                 uint8_t *codes, float *scale)
+{
+    int64_t nF = orc_ceil_div(F, cf), nH = orc_ceil_div(H, ch), nW = orc_ceil_div(W, cw);
+    float *core = (float *)malloc((size_t)K * sizeof(float));
+    for (int64_t a = 0; a < nF; a++)
+        for (int64_t b = 0; b < nH; b++)
+            for (int64_t c = 0; c < nW; c++) {
+                int64_t cube = (a * nH + b) * nW + c;
+                for (int64_t k = 0; k < K; k++) {
+                    float sum = 0.0f;
+                    int n = 0;
+                    for (int64_t f = a * cf; f < F && f < (a + 1) * cf; f++)
+                        for (int64_t h = b * ch; h < H && h < (b + 1) * ch; h++)
+                            for (int64_t w = c * cw; w < W && w < (c + 1) * cw; w++) {
+                                sum = sum + orc_bf16_to_f32(x[((f * H + h) * W + w) * K + k]);
+                                n++;
+                            }
+                    core[k] = sum / (float)n;
+                }
+                float amax = 0.0f;
+                for (int64_t k = 0; k < K; k++)
+                    if (fabsf(core[k]) > amax)
+                        amax = fabsf(core[k]);
+                float s = (amax < ORC_TINY) ? 0.0f : amax / 448.0f;
+                scale[cube] = s;
+                for (int64_t k = 0; k < K; k++) {
+                    uint8_t m = (s == 0.0f) ? 0u : orc_e4m3_encode(fabsf(core[k]) / s);
+                    codes[cube * K + k] = (m != 0 && core[k] < 0.0f) ? (uint8_t)(m | 0x80) : m;
+                }
+            }
+    free(core);
+}
+
+/* Differences from the stored core, float32 [F * H * W, K]. */
+void orc_dq_delta(const uint16_t *x, int64_t F, int64_t H, int64_t W, int64_t K, int cf, int ch, int cw,
+                  const uint8_t *codes, const float *scale, float *d)
+{
+    int64_t M = F * H * W;
+    int32_t *cube = (int32_t *)malloc((size_t)M * sizeof(int32_t));
+    orc_dq_cube_of(F, H, W, cf, ch, cw, cube);
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t k = 0; k < K; k++) {
+            float core = orc_e4m3s_decode(codes[(int64_t)cube[m] * K + k]) * scale[cube[m]];
+            d[m * K + k] = orc_bf16_to_f32(x[m * K + k]) - core;
+        }
+    free(cube);
 }
 
 #ifdef _OPENMP

@@ -593,3 +593,145 @@ def test_tdc_shrinking_changes_skip_more_later():
     assert first_half > second_half
     assert comp[:7] == list(range(7))                         # changes >= 0.05 at first
 
+
+
+# ---------------------------------------------------------------- DeltaQuant
+# Cube-delta quantization (DeltaQuant abstract, paper-radar CVPR 2026 listing).
+
+@pytest.mark.parametrize("grid,cube", [((3, 5, 7), (2, 2, 2)), ((3, 5, 7), (1, 1, 1)),
+                                       ((3, 5, 7), (3, 5, 7)), ((4, 3, 5), (4, 2, 3)),
+                                       ((13, 2, 3), (2, 2, 2))])
+def test_dq_cube_partition_brute_force(grid, cube):
+    """Pins dq_cube_of / dq_cubes: every token in exactly one cube, cubes
+    numbered over the cube grid frame-outermost, ragged at the far edges
+    (brute force over the cubes' own extents)."""
+    F, H, W = grid
+    cf, ch, cw = cube
+    got = O.dq_cube_of(F, H, W, cube)
+    seen = np.full(F * H * W, -1)
+    n = 0
+    for a in range(0, F, cf):
+        for b in range(0, H, ch):
+            for c in range(0, W, cw):
+                for f in range(a, min(F, a + cf)):
+                    for h in range(b, min(H, b + ch)):
+                        for w in range(c, min(W, c + cw)):
+                            assert seen[(f * H + h) * W + w] == -1
+                            seen[(f * H + h) * W + w] = n
+                n += 1
+    assert n == O.dq_cubes(F, H, W, cube)
+    assert np.array_equal(got, seen)
+
+
+def test_dq_core_codes_match_torch_e4m3():
+    """Pins dq_core: the core is the mean of the cube's tokens (integer-valued
+    tokens over power-of-two cubes, so the float32 mean is exact), its scale
+    max|c| / 448, and its codes torch's E4M3 (FN) rounding of c / s, sign
+    included (a zero magnitude stored as +0)."""
+    F, H, W, K, cube = 4, 4, 4, 64, (2, 2, 2)
+    rng = np.random.default_rng(3)
+    x = rng.integers(-40, 41, size=(F * H * W, K)).astype(np.float32)
+    x16 = synth.to_bf16_bits(x)
+    codes, scale = O.dq_core(x16, F, H, W, cube)
+    cube_of = O.dq_cube_of(F, H, W, cube)
+    for c in range(O.dq_cubes(F, H, W, cube)):
+        core = x[cube_of == c].astype(np.float64).mean(axis=0)
+        assert (cube_of == c).sum() == 8
+        s = np.float32(np.float32(np.abs(core).max()) / np.float32(448.0))
+        assert scale[c] == s
+        ref = torch.from_numpy((core.astype(np.float32) / s).astype(np.float32)).to(torch.float8_e4m3fn)
+        ref = ref.view(torch.uint8).numpy().copy()
+        ref[ref == 0x80] = 0
+        assert np.array_equal(codes[c], ref)
+    dec = O.e4m3s_decode(codes)
+    assert np.array_equal(np.sign(dec[codes != 0]), np.sign(np.where(codes[codes != 0] & 0x80, -1.0, 1.0)))
+
+
+def test_dq_delta_exact_on_constructed_cubes():
+    """Pins dq_delta against a hand-built case: each cube holds c + e_t, with
+    the offsets e_t summing to zero over the cube and c on the E4M3 grid of
+    its scale, so the mean is c, the stored core is c exactly and every
+    difference is e_t exactly; tokens equal to c give zero differences, a zero
+    tensor scale and all-zero NVFP4 codes."""
+    F, H, W, K, cube = 2, 2, 4, 32, (2, 2, 2)
+    rng = np.random.default_rng(5)
+    M = F * H * W
+    cube_of = O.dq_cube_of(F, H, W, cube)
+    grid = np.array([1.0, 1.5, 2.0, 3.0, 4.0, 6.0, 8.0, 14.0], np.float32)
+    x = np.zeros((M, K), np.float32)
+    e = np.zeros((M, K), np.float32)
+    for c in range(O.dq_cubes(F, H, W, cube)):
+        core = rng.choice(grid, K) * rng.choice([-1.0, 1.0], K)
+        core[0] = 14.0                                 # max |c| = 14 = 448 / 32: scale 2^-5
+        idx = np.flatnonzero(cube_of == c)
+        off = rng.integers(-3, 4, size=(len(idx) // 2, K)).astype(np.float32) * np.float32(0.25)
+        off = np.concatenate([off, -off])              # sums to zero over the cube
+        x[idx] = core + off
+        e[idx] = off
+    q = O.dq_quantize(synth.to_bf16_bits(x), F, H, W, cube)
+    assert np.all(q["core_scale"] == np.float32(14.0 / 448.0))
+    assert np.array_equal(q["delta"], e)
+    flat = np.repeat((x - e)[:1], M, axis=0)          # every token one on-grid core: zero differences
+    q0 = O.dq_quantize(synth.to_bf16_bits(flat), F, H, W, cube)
+    assert q0["s_t"] == 0.0 and not q0["codes"].any() and not q0["blk"].any()
+
+
+def test_dq_reconstruction_bound_and_gain_on_smooth_video():
+    """Pins the composition: core (decoded) plus decoded NVFP4 difference
+    reconstructs each token within NVFP4's per-element bound (half the largest
+    E2M1 step of the block scale, plus what saturation clips), and on tokens
+    that vary slowly over space and time it beats NVFP4 of the tokens
+    themselves -- the property the method rests on."""
+    F, H, W, K, cube = 4, 6, 6, 64, (2, 2, 2)
+    x16 = synth.smooth_video_tokens(F, H, W, K, synth.rng_for(120, 0))
+    x = O.bf16_to_f32(x16)
+    q = O.dq_quantize(x16, F, H, W, cube)
+    cube_of = O.dq_cube_of(F, H, W, cube)
+    core = O.e4m3s_decode(q["core"]) * q["core_scale"][:, None]
+    dq = O.dequant_nvfp4(q["codes"], q["blk"], q["s_t"], K)
+    d = q["delta"]
+    db = np.repeat(O.e4m3_decode(q["blk"]) * q["s_t"], 16, axis=1)
+    err = np.abs(d - dq)
+    assert np.all(err <= db + np.maximum(0.0, np.abs(d) - 6 * db) + 1e-7 * np.abs(d))
+    rec = core[cube_of] + dq
+    plain_c, plain_e, plain_t = O.quant_nvfp4_rotated(x, np.float32(np.abs(x).max()))
+    plain = O.dequant_nvfp4(plain_c, plain_e, plain_t, K)
+    e_dq = np.linalg.norm(rec - x) / np.linalg.norm(x)
+    e_plain = np.linalg.norm(plain - x) / np.linalg.norm(x)
+    assert e_dq < 0.5 * e_plain, (e_dq, e_plain)
+
+
+def test_dq_linear_brute_force():
+    """Pins dq_linear: y[m, n] = sum_k (difference + its cube's core)[m, k] *
+    w[n, k] with every operand decoded by hand from the format definitions
+    (E2M1 x E4M3 block scale x tensor scale; signed E4M3 x core scale),
+    Python loops in double."""
+    F, H, W, K, N, cube = 2, 2, 3, 32, 5, (2, 2, 2)
+    x16 = synth.smooth_video_tokens(F, H, W, K, synth.rng_for(121, 0))
+    w16 = rnd_bf16((N, K), 7, 0.05)
+    q = O.dq_quantize(x16, F, H, W, cube)
+    wc, we, wst = O.quant_nvfp4_rotated(O.bf16_to_f32(w16), np.float32(np.abs(O.bf16_to_f32(w16)).max()))
+    y = O.dq_linear(q, wc, we, wst, K, F, H, W, cube)
+    e2m1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+    def fp4(codes, blk, st, r, k):
+        b = codes[r, k // 2]
+        c = (b >> 4) if k & 1 else (b & 15)
+        v = e2m1[c & 7] * (-1.0 if c & 8 else 1.0)
+        eb = int(blk[r, k // 16])
+        ev = (eb & 7) / 8.0 * 2.0 ** -6 if eb >> 3 == 0 else (1 + (eb & 7) / 8.0) * 2.0 ** ((eb >> 3) - 7)
+        return v * ev * float(st)
+
+    def e4m3s(b):
+        m = b & 0x7f
+        v = (m & 7) / 8.0 * 2.0 ** -6 if m >> 3 == 0 else (1 + (m & 7) / 8.0) * 2.0 ** ((m >> 3) - 7)
+        return -v if b & 0x80 else v
+
+    cube_of = O.dq_cube_of(F, H, W, cube)
+    for m in range(F * H * W):
+        c = cube_of[m]
+        for n in range(N):
+            ref = sum((fp4(q["codes"], q["blk"], q["s_t"], m, k) +
+                       e4m3s(int(q["core"][c, k])) * float(q["core_scale"][c])) * fp4(wc, we, wst, n, k)
+                      for k in range(K))
+            assert abs(y[m, n] - ref) <= 1e-12 * max(1.0, abs(ref))
