@@ -15,7 +15,7 @@ using namespace hdq;
 constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
-bool valid_block(int32_t hb) { return hb >= 2 && hb <= 128 && (hb & (hb - 1)) == 0; }
+bool valid_block(int32_t hb) { return hb >= 1 && hb <= 128 && (hb & (hb - 1)) == 0; }
 
 // Shape rules shared by the quantizers: cols a multiple of 8 (16-byte rows of
 // bf16 chunks) and of the Hadamard block and of the format's scale block.
@@ -117,6 +117,11 @@ size_t hdq_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N, int32_t 
       const size_t per_row = (size_t)(M > 0 ? M : 0) * 6 * sizeof(double);
       return align_up(per_row > kStatsPartialBytes ? per_row : kStatsPartialBytes);
     }
+    case HDQ_OP_DQ_QUANTIZE:
+      return 256;
+    case HDQ_OP_DQ_LINEAR:  // M = tokens, K = cubes
+      if (N <= 0) return 0;
+      return align_up((size_t)M * (size_t)N * 4) + align_up((size_t)K * (size_t)N * 4);
     case HDQ_OP_LINEAR: {
       (void)N;
       size_t b = qtensor_bytes(M, K, HDQ_FMT_INT8_ROW);
@@ -331,6 +336,90 @@ int hdq_linear_dispatch_delta(const int32_t* decision_dev, const void* x, const 
       static_cast<const uint8_t*>(w->w_fp4.codes), w->w_fp4.blk_scale, w->w_fp4.tensor_scale, f,
       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w->w_bf16), y, y_dtype, M, N, K, s,
       &dw));
+}
+
+// ---- DeltaQuant ----------------------------------------------------------
+static bool dq_grid(const hdq_dq_grid* g, DqGrid& d) {
+  if (g == nullptr || g->frames <= 0 || g->height <= 0 || g->width <= 0 || g->cube_f <= 0 || g->cube_h <= 0 ||
+      g->cube_w <= 0 || g->frames * g->height * g->width > 0x7fffffff)
+    return false;
+  d.F = (int)g->frames;
+  d.H = (int)g->height;
+  d.W = (int)g->width;
+  d.cf = g->cube_f;
+  d.ch = g->cube_h;
+  d.cw = g->cube_w;
+  d.nF = (d.F + d.cf - 1) / d.cf;
+  d.nH = (d.H + d.ch - 1) / d.ch;
+  d.nW = (d.W + d.cw - 1) / d.cw;
+  return true;
+}
+
+int64_t hdq_dq_cubes(const hdq_dq_grid* g) {
+  DqGrid d;
+  if (!dq_grid(g, d)) return -1;
+  return (int64_t)d.nF * d.nH * d.nW;
+}
+
+int hdq_dq_quantize(const void* x, int64_t K, const hdq_dq_grid* g, int32_t fmt, uint8_t* core_codes,
+                    float* core_scale, void* core_bf16, hdq_qtensor* delta, void* ws, size_t ws_bytes,
+                    void* stream) {
+  if (x == nullptr || core_codes == nullptr || core_scale == nullptr || delta == nullptr) return HDQ_ERR_INVALID;
+  if (!is_fp4(fmt)) return HDQ_ERR_UNSUPPORTED;
+  DqGrid d;
+  if (!dq_grid(g, d)) return HDQ_ERR_SHAPE;
+  const int64_t M = (int64_t)d.F * d.H * d.W;
+  if (K <= 0 || K % 32 != 0 || K > 32768 || M * K / 8 >= (1ll << 31)) return HDQ_ERR_SHAPE;
+  if (delta->fmt != fmt || delta->had_block != 1 || delta->rows != M || delta->cols != K) return HDQ_ERR_SHAPE;
+  if (delta->codes == nullptr || delta->blk_scale == nullptr || delta->tensor_scale == nullptr)
+    return HDQ_ERR_INVALID;
+  if (ws == nullptr || ws_bytes < 256) return HDQ_ERR_WORKSPACE;
+  return hip_status(launch_dq_quantize(static_cast<const uint16_t*>(x), K, d, fmt, core_codes, core_scale,
+                                       static_cast<uint16_t*>(core_bf16), static_cast<uint32_t*>(ws),
+                                       static_cast<uint8_t*>(delta->codes), delta->blk_scale,
+                                       delta->tensor_scale, static_cast<hipStream_t>(stream)));
+}
+
+int hdq_dq_decode_weights(const hdq_qtensor* w_fp4, void* w_dec, void* stream) {
+  if (w_fp4 == nullptr || w_dec == nullptr) return HDQ_ERR_INVALID;
+  if (!is_fp4(w_fp4->fmt)) return HDQ_ERR_UNSUPPORTED;
+  int st;
+  if ((st = check_qtensor(*w_fp4, w_fp4->fmt, w_fp4->rows, w_fp4->cols)) != HDQ_OK) return st;
+  if (w_fp4->cols % 16 != 0) return HDQ_ERR_SHAPE;
+  return hip_status(launch_dq_decode_w(static_cast<const uint8_t*>(w_fp4->codes), w_fp4->blk_scale, w_fp4->rows,
+                                       w_fp4->cols, static_cast<uint16_t*>(w_dec), static_cast<hipStream_t>(stream)));
+}
+
+int hdq_dq_linear(const hdq_dq_grid* g, const void* core_bf16, const float* core_scale, const hdq_qtensor* delta,
+                  const hdq_qtensor* w_fp4, const void* w_dec, void* y, int32_t y_dtype, void* ws, size_t ws_bytes,
+                  void* stream) {
+  if (core_bf16 == nullptr || core_scale == nullptr || delta == nullptr || w_fp4 == nullptr || w_dec == nullptr ||
+      y == nullptr)
+    return HDQ_ERR_INVALID;
+  if (y_dtype != HDQ_DTYPE_F32 && y_dtype != HDQ_DTYPE_BF16) return HDQ_ERR_UNSUPPORTED;
+  DqGrid d;
+  if (!dq_grid(g, d)) return HDQ_ERR_SHAPE;
+  const int64_t M = (int64_t)d.F * d.H * d.W, C = (int64_t)d.nF * d.nH * d.nW;
+  const int64_t K = delta->cols, N = w_fp4->rows;
+  if (!is_fp4(delta->fmt) || w_fp4->fmt != delta->fmt) return HDQ_ERR_UNSUPPORTED;
+  int st;
+  if ((st = check_qtensor(*delta, delta->fmt, M, K)) != HDQ_OK) return st;
+  if ((st = check_qtensor(*w_fp4, delta->fmt, N, K)) != HDQ_OK) return st;
+  if (delta->had_block != 1 || w_fp4->had_block != 1 || K % 32 != 0 || N % 4 != 0 || N > 0x7fffffff)
+    return HDQ_ERR_SHAPE;
+  const size_t yd_bytes = align_up((size_t)M * (size_t)N * 4);
+  if (ws == nullptr || ws_bytes < hdq_workspace_bytes(HDQ_OP_DQ_LINEAR, M, C, N, 0)) return HDQ_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* yd = static_cast<float*>(ws);
+  float* yc = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + yd_bytes);
+  if (fp4_gemm_for(delta->fmt)(static_cast<const uint8_t*>(delta->codes), delta->blk_scale, delta->tensor_scale,
+                               static_cast<const uint8_t*>(w_fp4->codes), w_fp4->blk_scale, w_fp4->tensor_scale,
+                               yd, HDQ_DTYPE_F32, M, N, K, nullptr, HDQ_PREC_NVFP4, s) != hipSuccess)
+    return HDQ_ERR_HIP;
+  if (launch_gemm_bf16(static_cast<const uint16_t*>(core_bf16), static_cast<const uint16_t*>(w_dec), yc,
+                       HDQ_DTYPE_F32, C, N, K, nullptr, HDQ_PREC_BF16, s) != hipSuccess)
+    return HDQ_ERR_HIP;
+  return hip_status(launch_dq_combine(yd, yc, core_scale, w_fp4->tensor_scale, d, N, y, y_dtype, s));
 }
 
 int hdq_quantize(const void* x, int64_t rows, int64_t cols, int32_t had_block, int32_t fmt,

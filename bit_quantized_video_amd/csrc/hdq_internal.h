@@ -125,6 +125,22 @@ hipError_t launch_gemm_dispatch(const int32_t* decision, const int8_t* x8, const
                                 const uint16_t* xb, const uint16_t* wb, void* y, int out_dtype,
                                 int64_t M, int64_t N, int64_t K, hipStream_t s,
                                 const struct DeltaWork* delta = nullptr);
+// DeltaQuant cube-delta quantization: the token grid (frame outermost), the
+// cube size and the cube grid.
+struct DqGrid {
+  int F, H, W, cf, ch, cw, nF, nH, nW;
+};
+// Core tokens (codes, scales, optional bf16 code values) and the differences
+// in NVFP4 format fmt; damax_bits: device uint32 scratch.
+hipError_t launch_dq_quantize(const uint16_t* x, int64_t K, const DqGrid& g, int fmt, uint8_t* ccodes,
+                              float* cscale, uint16_t* core_bf16, uint32_t* damax_bits, uint8_t* codes,
+                              uint8_t* blk_scale, float* tensor_scale, hipStream_t s);
+// NVFP4 weights [N, K] to bf16 E2M1 x block-scale values.
+hipError_t launch_dq_decode_w(const uint8_t* codes, const uint8_t* blk, int64_t N, int64_t K, uint16_t* out,
+                              hipStream_t s);
+// y = yd + (yc of the token's cube) x s_c x s_tw (N a multiple of 4).
+hipError_t launch_dq_combine(const float* yd, const float* yc, const float* cscale, const float* wts,
+                             const DqGrid& g, int64_t N, void* y, int out_dtype, hipStream_t s);
 // bf16 x bf16 (full-precision fallback).
 hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* w, void* y, int out_dtype,
                             int64_t M, int64_t N, int64_t K, const int32_t* decision,

@@ -418,4 +418,248 @@ hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t rows, int64_t cols, int
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------- DeltaQuant
+// Cube-delta quantization (DeltaQuant abstract, paper-radar CVPR 2026
+// listing): video tokens of an F x H x W grid (frame outermost) in cubes of
+// cf x ch x cw (ragged at the far edges); a cube's mean token (the core) is
+// kept in FP8 E4M3 with one fp32 scale, every token's difference from the
+// stored core in NVFP4 without rotation.  The core is the float32 sum of the
+// cube's tokens in token order divided by their count; its scale is
+// max|core| / 448 (0 below kTiny); a code is the nearest E4M3 of |c| / s with
+// the sign in bit 7 (a zero magnitude stored as +0).
+
+// Cube of token m.
+__device__ __forceinline__ int dq_cube(int m, const DqGrid& g) {
+  const int hw = g.H * g.W, f = m / hw, r = m - f * hw, h = r / g.W, w = r - h * g.W;
+  return ((f / g.cf) * g.nH + h / g.ch) * g.nW + w / g.cw;
+}
+
+// One workgroup per cube: the mean in LDS, its scale and codes, the decoded
+// code values as bf16 (exact: E4M3 has 4 significant bits) for the core
+// GEMM, and the largest |difference| of the cube's tokens into the running
+// maximum (float bits of a non-negative value order as unsigned integers).
+__global__ __launch_bounds__(256) void k_dq_core(const uint16_t* __restrict__ x, int K, const DqGrid g,
+                                                 uint8_t* __restrict__ codes, float* __restrict__ scale,
+                                                 uint16_t* __restrict__ core_bf16,
+                                                 uint32_t* __restrict__ damax_bits) {
+  extern __shared__ float lcore[];  // K floats: the mean, then the stored core
+  __shared__ float red[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cube = blockIdx.x, a = cube / (g.nH * g.nW), b = (cube / g.nW) % g.nH, c = cube % g.nW;
+  const int f0 = a * g.cf, f1 = min(g.F, f0 + g.cf), h0 = b * g.ch, h1 = min(g.H, h0 + g.ch);
+  const int w0 = c * g.cw, w1 = min(g.W, w0 + g.cw);
+  const float n = (float)((f1 - f0) * (h1 - h0) * (w1 - w0));
+  const int kq = K >> 3;
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  float amax = 0.0f;
+  for (int q = tid; q < kq; q += 256) {
+    float sum[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    for (int f = f0; f < f1; ++f)
+      for (int h = h0; h < h1; ++h)
+        for (int w = w0; w < w1; ++w) {
+          float v[8];
+          bf16x8_to_f32(xv[(int64_t)((f * g.H + h) * g.W + w) * kq + q], v);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) sum[i] = sum[i] + v[i];
+        }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float m = sum[i] / n;
+      lcore[8 * q + i] = m;
+      amax = fmaxf(amax, fabsf(m));
+    }
+  }
+  amax = wave_max(amax);
+  if (lane == 0) red[wave] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float sc = amax >= kTiny ? amax / 448.0f : 0.0f;
+  if (tid == 0) scale[cube] = sc;
+  for (int q = tid; q < kq; q += 256) {
+    uint32_t cw2[2] = {0u, 0u}, bw[4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float m = lcore[8 * q + i];
+      const uint32_t mag = sc == 0.0f ? 0u : e4m3_encode(fabsf(m) / sc);
+      const bool neg = mag != 0u && m < 0.0f;
+      const float e = neg ? -e4m3_decode(mag) : e4m3_decode(mag);
+      lcore[8 * q + i] = e * sc;
+      cw2[i >> 2] |= (mag | (neg ? 0x80u : 0u)) << (8 * (i & 3));
+      const uint32_t eb = __float_as_uint(e) >> 16;  // exact: 4 significant bits
+      if (i & 1) bw[i >> 1] |= eb << 16; else bw[i >> 1] = eb;
+    }
+    reinterpret_cast<uint2*>(codes)[(int64_t)cube * kq + q] = make_uint2(cw2[0], cw2[1]);
+    if (core_bf16 != nullptr)
+      reinterpret_cast<uint4*>(core_bf16)[(int64_t)cube * kq + q] = make_uint4(bw[0], bw[1], bw[2], bw[3]);
+  }
+  __syncthreads();
+  float dmax = 0.0f;
+  for (int f = f0; f < f1; ++f)
+    for (int h = h0; h < h1; ++h)
+      for (int w = w0; w < w1; ++w)
+        for (int q = tid; q < kq; q += 256) {
+          float v[8];
+          bf16x8_to_f32(xv[(int64_t)((f * g.H + h) * g.W + w) * kq + q], v);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) dmax = fmaxf(dmax, fabsf(v[i] - lcore[8 * q + i]));
+        }
+  dmax = wave_max(dmax);
+  __syncthreads();
+  if (lane == 0) red[wave] = dmax;
+  __syncthreads();
+  if (tid == 0) atomicMax(damax_bits, __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
+}
+
+__global__ void k_dq_zero(uint32_t* p) { *p = 0u; }
+
+// Every token's difference from its cube's stored core, quantized to NVFP4
+// with the tensor scale of the largest |difference|.  Chunks and lanes as in
+// k_quant_nvfp4 with no rotation (a 16-element block on lanes l, l ^ 1).
+template <int FMT>
+__global__ __launch_bounds__(256) void k_dq_delta(const uint16_t* __restrict__ x, int K, const DqGrid g,
+                                                  int64_t nch, const uint8_t* __restrict__ ccodes,
+                                                  const float* __restrict__ cscale,
+                                                  const uint32_t* __restrict__ damax_bits,
+                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ blk_scale,
+                                                  float* __restrict__ tensor_scale) {
+  constexpr int UNROLL = 2;
+  const int lane = threadIdx.x & 63, kq = K >> 3;
+  const float A = __uint_as_float(*damax_bits);
+  const float s_t = (A >= kTiny) ? A / (FMT == kNvfp4 ? 2688.0f : 1536.0f) : 0.0f;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = s_t;
+  const float six_st = 6.0f * s_t;
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  const uint2* cv2 = reinterpret_cast<const uint2*>(ccodes);
+  uint32_t* cv = reinterpret_cast<uint32_t*>(codes);
+  for (int64_t base = wave * 64 * UNROLL; base < nch; base += nwaves * 64 * UNROLL) {
+    uint4 w[UNROLL];
+    uint2 cc[UNROLL];
+    float sc[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int64_t idx = base + 64 * u + lane;
+      if (idx < nch) {
+        const int m = (int)(idx / kq), q = (int)(idx - (int64_t)m * kq), cb = dq_cube(m, g);
+        w[u] = xv[idx];
+        cc[u] = cv2[(int64_t)cb * kq + q];
+        sc[u] = cscale[cb];
+      } else {
+        w[u] = make_uint4(0u, 0u, 0u, 0u);
+        cc[u] = make_uint2(0u, 0u);
+        sc[u] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int64_t idx = base + 64 * u + lane;
+      float v[8];
+      bf16x8_to_f32(w[u], v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t b = ((i < 4 ? cc[u].x : cc[u].y) >> (8 * (i & 3))) & 0xffu;
+        const float e = e4m3_decode(b & 0x7fu);
+        v[i] = v[i] - ((b & 0x80u) ? -e : e) * sc[u];
+      }
+      uint32_t e;
+      const uint32_t packed = nvfp4_chunk<FMT>(v, s_t, six_st, &e);
+      if (idx < nch) {
+        cv[idx] = packed;
+        if ((idx & 1) == 0) blk_scale[idx >> 1] = (uint8_t)e;
+      }
+    }
+  }
+}
+
+hipError_t launch_dq_quantize(const uint16_t* x, int64_t K, const DqGrid& g, int fmt, uint8_t* ccodes,
+                              float* cscale, uint16_t* core_bf16, uint32_t* damax_bits, uint8_t* codes,
+                              uint8_t* blk_scale, float* tensor_scale, hipStream_t s) {
+  const int64_t ncubes = (int64_t)g.nF * g.nH * g.nW;
+  const size_t lds = (size_t)K * sizeof(float);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_dq_core),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_dq_zero, dim3(1), dim3(1), 0, s, damax_bits);
+  hipLaunchKernelGGL(k_dq_core, dim3((unsigned)ncubes), dim3(256), lds, s, x, (int)K, g, ccodes, cscale,
+                     core_bf16, damax_bits);
+  const int64_t nch = (int64_t)g.F * g.H * g.W * K / 8;
+  int64_t blocks = ((nch + 127) / 128 + 3) / 4;
+  if (blocks > 2048) blocks = 2048;
+  if (blocks < 1) blocks = 1;
+  auto kern = fmt == kNvfp4Mx ? k_dq_delta<kNvfp4Mx> : fmt == kNvfp4P2 ? k_dq_delta<kNvfp4P2> : k_dq_delta<kNvfp4>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, s, x, (int)K, g, nch, ccodes, cscale,
+                     damax_bits, codes, blk_scale, tensor_scale);
+  return hipGetLastError();
+}
+
+// NVFP4 weights to bf16 values of E2M1 x block scale (exact: at most six
+// significant bits), the tensor scale left out: the core GEMM's operand.
+__global__ __launch_bounds__(256) void k_dq_decode_w(const uint8_t* __restrict__ codes,
+                                                     const uint8_t* __restrict__ blk, int64_t nch,
+                                                     uint16_t* __restrict__ out) {
+  const uint32_t* cv = reinterpret_cast<const uint32_t*>(codes);
+  uint4* ov = reinterpret_cast<uint4*>(out);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nch; i += (int64_t)gridDim.x * 256) {
+    const uint32_t p = cv[i];
+    const float e = e4m3_decode(blk[i >> 1]);
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = (p >> (8 * j)) & 15u, hi = (p >> (8 * j + 4)) & 15u;
+      o[j] = (__float_as_uint(e2m1_value(lo) * e) >> 16) | ((__float_as_uint(e2m1_value(hi) * e) >> 16) << 16);
+    }
+    ov[i] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+hipError_t launch_dq_decode_w(const uint8_t* codes, const uint8_t* blk, int64_t N, int64_t K, uint16_t* out,
+                              hipStream_t s) {
+  const int64_t nch = N * K / 8;
+  int64_t blocks = (nch + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_dq_decode_w, dim3((unsigned)blocks), dim3(256), 0, s, codes, blk, nch, out);
+  return hipGetLastError();
+}
+
+// y[m, n] = yd[m, n] + fl32(fl32(yc[cube(m), n] * s_c) * s_tw): the
+// differences' GEMM plus the core GEMM of the token's cube, 4 columns a thread.
+template <int OUT>
+__global__ __launch_bounds__(256) void k_dq_combine(const float* __restrict__ yd, const float* __restrict__ yc,
+                                                    const float* __restrict__ cscale,
+                                                    const float* __restrict__ wts, const DqGrid g, int M,
+                                                    int N, void* __restrict__ y) {
+  const int nq = N >> 2;
+  const float stw = *wts;
+  const int64_t total = (int64_t)M * nq;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int m = (int)(i / nq), q = (int)(i - (int64_t)m * nq), cb = dq_cube(m, g);
+    const float4 d = reinterpret_cast<const float4*>(yd)[i];
+    const float4 c = reinterpret_cast<const float4*>(yc)[(int64_t)cb * nq + q];
+    const float s = cscale[cb];
+    const float r0 = d.x + (c.x * s) * stw, r1 = d.y + (c.y * s) * stw;
+    const float r2 = d.z + (c.z * s) * stw, r3 = d.w + (c.w * s) * stw;
+    if constexpr (OUT == kOutF32)
+      reinterpret_cast<float4*>(y)[i] = make_float4(r0, r1, r2, r3);
+    else
+      reinterpret_cast<uint2*>(y)[i] = make_uint2(pack_bf16x2(r0, r1), pack_bf16x2(r2, r3));
+  }
+}
+
+hipError_t launch_dq_combine(const float* yd, const float* yc, const float* cscale, const float* wts,
+                             const DqGrid& g, int64_t N, void* y, int out_dtype, hipStream_t s) {
+  const int64_t M = (int64_t)g.F * g.H * g.W, total = M * (N / 4);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  if (out_dtype == kOutF32)
+    hipLaunchKernelGGL(k_dq_combine<kOutF32>, dim3((unsigned)blocks), dim3(256), 0, s, yd, yc, cscale, wts, g,
+                       (int)M, (int)N, y);
+  else
+    hipLaunchKernelGGL(k_dq_combine<kOutBf16>, dim3((unsigned)blocks), dim3(256), 0, s, yd, yc, cscale, wts, g,
+                       (int)M, (int)N, y);
+  return hipGetLastError();
+}
+
 }  // namespace hdq

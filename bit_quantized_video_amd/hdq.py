@@ -24,11 +24,12 @@ PREC_NVFP4, PREC_INT8, PREC_BF16 = 0, 1, 2
 # output dtypes
 DTYPE_F32, DTYPE_BF16, DTYPE_I32 = 0, 1, 2
 # workspace ops
-OP_SELECT, OP_QUANTIZE, OP_LINEAR, OP_SELECT_Q8 = 0, 1, 2, 3
+OP_SELECT, OP_QUANTIZE, OP_LINEAR, OP_SELECT_Q8, OP_DQ_QUANTIZE, OP_DQ_LINEAR = 0, 1, 2, 3, 4, 5
 
 EXPORTS = ("hdq_select_precision", "hdq_delta_sums", "hdq_select_precision_sums",
            "hdq_select_quantize_int8", "hdq_linear_dispatch", "hdq_linear_dispatch_delta",
-           "hdq_tdc_decide", "hdq_quantize",
+           "hdq_tdc_decide", "hdq_quantize", "hdq_dq_cubes", "hdq_dq_quantize", "hdq_dq_decode_weights",
+           "hdq_dq_linear",
            "hdq_linear", "hdq_workspace_bytes",
            "hdq_status_string", "hdq_version")
 
@@ -56,6 +57,12 @@ DELTA_MAX_SLICES = 4      # HDQ_DELTA_MAX_SLICES
 def delta_chunks(numel):
     """Chunks (and partial pairs) of a module's difference statistic."""
     return (numel + DELTA_CHUNK - 1) // DELTA_CHUNK
+
+
+class DqGridDesc(_c.Structure):
+    """hdq_dq_grid."""
+    _fields_ = [("frames", _c.c_int64), ("height", _c.c_int64), ("width", _c.c_int64),
+                ("cube_f", _c.c_int32), ("cube_h", _c.c_int32), ("cube_w", _c.c_int32)]
 
 
 class WeightsDesc(_c.Structure):
@@ -96,6 +103,16 @@ def _load():
     L.hdq_linear.argtypes = [_c.c_int32, _p, _p, _c.POINTER(QTensorDesc), _p, _c.c_int64,
                              _c.c_int64, _c.POINTER(WeightsDesc), _p, _c.c_int32, _p,
                              _c.c_size_t, _p]
+    L.hdq_dq_cubes.restype = _c.c_int64
+    L.hdq_dq_cubes.argtypes = [_c.POINTER(DqGridDesc)]
+    L.hdq_dq_quantize.restype = _c.c_int
+    L.hdq_dq_quantize.argtypes = [_p, _c.c_int64, _c.POINTER(DqGridDesc), _c.c_int32, _p, _p, _p,
+                                  _c.POINTER(QTensorDesc), _p, _c.c_size_t, _p]
+    L.hdq_dq_decode_weights.restype = _c.c_int
+    L.hdq_dq_decode_weights.argtypes = [_c.POINTER(QTensorDesc), _p, _p]
+    L.hdq_dq_linear.restype = _c.c_int
+    L.hdq_dq_linear.argtypes = [_c.POINTER(DqGridDesc), _p, _p, _c.POINTER(QTensorDesc),
+                                _c.POINTER(QTensorDesc), _p, _p, _c.c_int32, _p, _c.c_size_t, _p]
     L.hdq_workspace_bytes.restype = _c.c_size_t
     L.hdq_workspace_bytes.argtypes = [_c.c_int32, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int32]
     L.hdq_status_string.restype = _c.c_char_p
@@ -343,6 +360,69 @@ def quantize(x, had_block, fmt, tensor_amax=None, out=None, ws=None, stream=None
                           _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
     _check("hdq_quantize", st)
     return out
+
+
+# ---- DeltaQuant cube-delta quantization --------------------------------------
+
+def dq_cubes(grid):
+    """Cubes of grid = (frames, height, width, (cube_f, cube_h, cube_w))."""
+    n = lib.hdq_dq_cubes(_c.byref(_dq_grid(grid)))
+    if n < 0:
+        raise ValueError(f"bad DeltaQuant grid {grid}")
+    return n
+
+
+def _dq_grid(grid):
+    F, H, W, (cf, ch, cw) = grid
+    return DqGridDesc(F, H, W, cf, ch, cw)
+
+
+class DqActivations:
+    """hdq_dq_quantize's outputs: core codes [cubes, K], core scales [cubes],
+    core code values as bf16 [cubes, K], and the differences' NVFP4 tensor."""
+
+    def __init__(self, grid, K, fmt, device):
+        self.grid, self.K = grid, K
+        n, M = dq_cubes(grid), grid[0] * grid[1] * grid[2]
+        self.core = torch.empty(n, K, dtype=torch.uint8, device=device)
+        self.core_scale = torch.empty(n, dtype=torch.float32, device=device)
+        self.core_bf16 = torch.empty(n, K, dtype=torch.bfloat16, device=device)
+        self.delta = QuantizedTensor(fmt, M, K, 1, device)
+
+
+def dq_quantize(x, grid, fmt, out=None, ws=None, stream=None):
+    """hdq_dq_quantize: cube cores in FP8 and the differences in NVFP4."""
+    x = _bf16(x, "x")
+    M, K = x.shape
+    out = DqActivations(grid, K, fmt, x.device) if out is None else out
+    ws = _workspace(ws, workspace_bytes(OP_DQ_QUANTIZE, M, K), x.device)
+    d = out.delta.desc()
+    st = lib.hdq_dq_quantize(_ptr(x), K, _c.byref(_dq_grid(grid)), fmt, _ptr(out.core), _ptr(out.core_scale),
+                             _ptr(out.core_bf16), _c.byref(d), _ptr(ws), ws.numel(), _stream(stream))
+    _check("hdq_dq_quantize", st)
+    return out
+
+
+def dq_decode_weights(w_fp4, stream=None):
+    """hdq_dq_decode_weights: bf16 [N, K] of E2M1 x block scale."""
+    out = torch.empty(w_fp4.rows, w_fp4.cols, dtype=torch.bfloat16, device=w_fp4.codes.device)
+    d = w_fp4.desc()
+    _check("hdq_dq_decode_weights", lib.hdq_dq_decode_weights(_c.byref(d), _ptr(out), _stream(stream)))
+    return out
+
+
+def dq_linear(a, w_fp4, w_dec, y=None, y_dtype=DTYPE_BF16, ws=None, stream=None):
+    """hdq_dq_linear: y = differences x W^T + cube cores x W^T."""
+    M, N = a.delta.rows, w_fp4.rows
+    if y is None:
+        dt = {DTYPE_F32: torch.float32, DTYPE_BF16: torch.bfloat16}[y_dtype]
+        y = torch.empty(M, N, dtype=dt, device=a.core.device)
+    ws = _workspace(ws, workspace_bytes(OP_DQ_LINEAR, M, dq_cubes(a.grid), N), a.core.device)
+    dd, wd = a.delta.desc(), w_fp4.desc()
+    st = lib.hdq_dq_linear(_c.byref(_dq_grid(a.grid)), _ptr(a.core_bf16), _ptr(a.core_scale), _c.byref(dd),
+                           _c.byref(wd), _ptr(w_dec), _ptr(y), y_dtype, _ptr(ws), ws.numel(), _stream(stream))
+    _check("hdq_dq_linear", st)
+    return y
 
 
 class LinearWeights:

@@ -35,7 +35,8 @@
  *    K is multiplied by H_b / sqrt(b), H_b the Sylvester Hadamard matrix, in
  *    float32 by the fast Walsh-Hadamard butterfly (strides 1, 2, 4, ... in
  *    that order) and one multiply by fl32(1/sqrt(b)).  Weights and
- *    activations are rotated alike, so (XQ)(WQ)^T = XW^T.
+ *    activations are rotated alike, so (XQ)(WQ)^T = XW^T.  had_block 1
+ *    rotates nothing.
  *  - Quantized codes use round-half-to-even.  Non-finite inputs are outside
  *    the quantizers' contract; hdq_select_precision routes them to BF16.
  */
@@ -54,7 +55,7 @@ extern "C" {
 #define HDQ_ERR_INVALID (-1)     /* NULL pointer, bad enum or bad struct field  */
 #define HDQ_ERR_SHAPE (-2)       /* size <= 0, K not a multiple of had_block or */
                                  /* of the format's block, had_block not a      */
-                                 /* power of two in [2, 128], shapes disagree   */
+                                 /* power of two in [1, 128], shapes disagree   */
 #define HDQ_ERR_UNSUPPORTED (-3) /* precision/format/output-dtype combination   */
 #define HDQ_ERR_HIP (-4)         /* a kernel launch failed                      */
 #define HDQ_ERR_WORKSPACE (-5)   /* ws NULL or ws_bytes below what is required  */
@@ -103,6 +104,8 @@ extern "C" {
 #define HDQ_OP_QUANTIZE 1
 #define HDQ_OP_LINEAR 2
 #define HDQ_OP_SELECT_Q8 3
+#define HDQ_OP_DQ_QUANTIZE 4
+#define HDQ_OP_DQ_LINEAR 5
 
 /* A quantized tensor.  The caller allocates every buffer (device memory)
  * and fills the pointers; hdq_quantize fills fmt, had_block, rows, cols. */
@@ -378,11 +381,73 @@ int hdq_tdc_decide(const double *sums_dev, const int64_t *parts_offsets_dev, con
                    float *c_dev, float *acc_dev, int32_t *skip_dev, int64_t n, float tau_skip,
                    float tau_acc, void *stream);
 
+/* ---- DeltaQuant cube-delta quantization (a second workload) ---------------
+ * DeltaQuant (paper-radar CVPR 2026 listing, abstract): video activations are
+ * grouped in local 3D spatiotemporal cubes; each cube's mean token (the core)
+ * is kept in FP8 and only each token's difference from it is quantized to 4
+ * bits.  Here: the tokens of a frames x height x width grid are the rows of
+ * x, frame outermost ((f * height + h) * width + w); cubes are cube_f x
+ * cube_h x cube_w blocks, ragged at the far edges, numbered the same way over
+ * the cube grid.  The core is the float32 sum of its tokens in that order
+ * divided by their count; it is stored as E4M3 with one fp32 scale per cube,
+ * max|core| / 448 (0 below 2^-100), each code the nearest E4M3 of |c| / s
+ * (ties to even) with the sign in bit 7 and a zero magnitude stored as +0.  A
+ * token's difference fl32(x - fl32(E * s)) is quantized to NVFP4 (fmt) with
+ * no rotation (had_block 1) and the tensor scale of the largest |difference|.
+ */
+typedef struct hdq_dq_grid {
+  int64_t frames, height, width;
+  int32_t cube_f, cube_h, cube_w;
+} hdq_dq_grid;
+
+/* Cubes of the grid, -1 for a bad grid (a size <= 0, or over 2^31 - 1 tokens). */
+int64_t hdq_dq_cubes(const hdq_dq_grid *g);
+
+/*
+ * hdq_dq_quantize -- the activation side.
+ *   x          : device bf16 [tokens, K], K a multiple of 32, at most 32768.
+ *   fmt        : HDQ_FMT_NVFP4, _NVFP4_MX or _NVFP4_P2 for the differences.
+ *   core_codes : device uint8 [cubes, K] (signed E4M3); core_scale: fp32 [cubes].
+ *   core_bf16  : NULL, or device bf16 [cubes, K]: the signed E4M3 code values
+ *                (exact), the core GEMM's operand.
+ *   delta      : fmt, had_block 1, rows = tokens, cols = K, with codes,
+ *                blk_scale and tensor_scale set (written).
+ *   ws, ws_bytes: device scratch >= hdq_workspace_bytes(HDQ_OP_DQ_QUANTIZE, ...)
+ *                (256 bytes).
+ */
+int hdq_dq_quantize(const void *x, int64_t K, const hdq_dq_grid *g, int32_t fmt, uint8_t *core_codes,
+                    float *core_scale, void *core_bf16, hdq_qtensor *delta, void *ws, size_t ws_bytes,
+                    void *stream);
+
+/* NVFP4 weights (any of the three formats, [N, K]) to device bf16 [N, K]
+ * holding E2M1 x block scale per element (exact), the tensor scale left out:
+ * the core GEMM's weight operand, made once per layer. */
+int hdq_dq_decode_weights(const hdq_qtensor *w_fp4, void *w_dec, void *stream);
+
+/*
+ * hdq_dq_linear -- y = (differences) x W^T + (the token's cube core) x W^T.
+ *   delta       : from hdq_dq_quantize; w_fp4: the layer's NVFP4 weights in
+ *                 the same format with had_block 1 (hdq_quantize with
+ *                 had_block 1 rotates nothing), N a multiple of 4; w_dec: from
+ *                 hdq_dq_decode_weights.
+ *   core_bf16, core_scale: from hdq_dq_quantize.
+ *   y, y_dtype  : device [tokens, N], HDQ_DTYPE_F32 or _BF16.
+ *   ws, ws_bytes: >= hdq_workspace_bytes(HDQ_OP_DQ_LINEAR, tokens, cubes, N, 0).
+ * The difference GEMM is the NVFP4 GEMM of the format (fp32 into ws); the
+ * core GEMM multiplies the E4M3 values by the decoded weights on the bf16
+ * MFMA with float32 accumulation (exact products); then
+ * y = fl(yd + fl32(fl32(yc * s_core) * s_w)).
+ */
+int hdq_dq_linear(const hdq_dq_grid *g, const void *core_bf16, const float *core_scale, const hdq_qtensor *delta,
+                  const hdq_qtensor *w_fp4, const void *w_dec, void *y, int32_t y_dtype, void *ws, size_t ws_bytes,
+                  void *stream);
+
 /* Scratch bytes an entry point needs.  op = HDQ_OP_SELECT: (M = rows,
  * K = cols, N = prev_numel); HDQ_OP_SELECT_Q8: (M = rows, K = cols);
  * HDQ_OP_QUANTIZE: (M = rows, K = cols, fmt);
  * HDQ_OP_LINEAR: (M, K, N, fmt = the weights' FP4 format, or -1 when only
- * INT8/BF16 will run).  Returns 0 on bad arguments. */
+ * INT8/BF16 will run); HDQ_OP_DQ_QUANTIZE: 256; HDQ_OP_DQ_LINEAR: (M = tokens,
+ * K = cubes, N).  Returns 0 on bad arguments. */
 size_t hdq_workspace_bytes(int32_t op, int64_t M, int64_t K, int64_t N, int32_t fmt);
 
 /* Static text for a status code. */

@@ -29,7 +29,8 @@ def test_header_declares_the_boundary():
     for fn in ("hdq_select_precision", "hdq_delta_sums", "hdq_select_precision_sums",
                "hdq_select_quantize_int8", "hdq_quantize", "hdq_tdc_decide",
                "hdq_linear", "hdq_linear_dispatch", "hdq_workspace_bytes",
-               "hdq_status_string", "hdq_version"):
+               "hdq_status_string", "hdq_version", "hdq_dq_cubes", "hdq_dq_quantize",
+               "hdq_dq_decode_weights", "hdq_dq_linear"):
         assert fn in names
 
 
@@ -174,6 +175,43 @@ def test_validation_happens_before_any_launch(hdq):
     assert dd(sl=hdq.DeltaSlice(ctypes.c_void_p(0x100008), big, 1 << 17, 0, 2, big)) == hdq.ERR_SHAPE  # alignment
     w64 = hdq.WeightsDesc(32, 64, fake, w4, hdq.QTensorDesc(hdq.FMT_NVFP4_MX, 16, 32, 64, fake, None, fake, fake))
     assert dd(K=64, w=w64) == hdq.ERR_SHAPE                 # only the one-launch kernel's shapes
+
+
+def test_deltaquant_validation(hdq):
+    """DeltaQuant entry points: grid, format, shape and workspace checks (no
+    kernel runs: every call fails before a launch)."""
+    L = hdq.lib
+    fake = ctypes.c_void_p(0x1000)
+    g = hdq.DqGridDesc(3, 5, 7, 2, 2, 2)
+    assert L.hdq_dq_cubes(ctypes.byref(g)) == 2 * 3 * 4
+    assert L.hdq_dq_cubes(ctypes.byref(hdq.DqGridDesc(3, 5, 7, 0, 2, 2))) == -1
+    assert L.hdq_dq_cubes(None) == -1
+    M, K = 105, 64
+    delta = hdq.QTensorDesc(hdq.FMT_NVFP4_MX, 1, M, K, fake, None, fake, fake)
+    q = lambda x=fake, K=K, g=g, fmt=hdq.FMT_NVFP4_MX, d=delta, ws=fake, wsb=256: L.hdq_dq_quantize(
+        x, K, ctypes.byref(g), fmt, fake, fake, None, ctypes.byref(d), ws, wsb, None)
+    assert q(x=None) == hdq.ERR_INVALID
+    assert q(fmt=hdq.FMT_INT8_ROW) == hdq.ERR_UNSUPPORTED
+    assert q(K=48) == hdq.ERR_SHAPE
+    assert q(g=hdq.DqGridDesc(3, 5, 0, 2, 2, 2)) == hdq.ERR_SHAPE
+    assert q(d=hdq.QTensorDesc(hdq.FMT_NVFP4_MX, 16, M, K, fake, None, fake, fake)) == hdq.ERR_SHAPE
+    assert q(d=hdq.QTensorDesc(hdq.FMT_NVFP4, 1, M, K, fake, None, fake, fake)) == hdq.ERR_SHAPE
+    assert q(d=hdq.QTensorDesc(hdq.FMT_NVFP4_MX, 1, M, K, fake, None, None, fake)) == hdq.ERR_INVALID
+    assert q(wsb=255) == hdq.ERR_WORKSPACE
+    assert L.hdq_workspace_bytes(hdq.OP_DQ_QUANTIZE, M, K, 0, 0) == 256
+    N, C = 40, 24
+    need = L.hdq_workspace_bytes(hdq.OP_DQ_LINEAR, M, C, N, 0)
+    assert need >= (M * N + C * N) * 4
+    w = hdq.QTensorDesc(hdq.FMT_NVFP4_MX, 1, N, K, fake, None, fake, fake)
+    lin = lambda d=delta, w=w, dt=1, ws=fake, wsb=need: L.hdq_dq_linear(
+        ctypes.byref(g), fake, fake, ctypes.byref(d), ctypes.byref(w), fake, fake, dt, ws, wsb, None)
+    assert lin(dt=2) == hdq.ERR_UNSUPPORTED
+    assert lin(w=hdq.QTensorDesc(hdq.FMT_NVFP4, 1, N, K, fake, None, fake, fake)) == hdq.ERR_UNSUPPORTED
+    assert lin(w=hdq.QTensorDesc(hdq.FMT_NVFP4_MX, 1, 42, K, fake, None, fake, fake)) == hdq.ERR_SHAPE
+    assert lin(w=hdq.QTensorDesc(hdq.FMT_NVFP4_MX, 2, N, K, fake, None, fake, fake)) == hdq.ERR_SHAPE
+    assert lin(d=hdq.QTensorDesc(hdq.FMT_NVFP4_MX, 1, M + 1, K, fake, None, fake, fake)) == hdq.ERR_SHAPE
+    assert lin(wsb=need - 1) == hdq.ERR_WORKSPACE
+    assert L.hdq_dq_decode_weights(None, fake, None) == hdq.ERR_INVALID
 
 
 def test_product_path_never_uses_the_oracle():
