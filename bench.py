@@ -79,6 +79,9 @@ def parse():
                          "(default; the other kernels are timed in one instrumented step after the timed "
                          "ones), or around every kernel (each event record adds a marker to the stream, "
                          "which costs the step several percent)")
+    ap.add_argument("--dq-steps", type=int, default=10,
+                    help="timed calls of the DeltaQuant cube-delta path (quantize, linear) on the "
+                         "13x30x45-token video grid, K 3072 -> N 12288; 0 skips it")
     ap.add_argument("--tdc-steps", type=int, default=12,
                     help="steps of the temporal-delta-cache trajectory measured after the schedule "
                          "(0: none)")
@@ -772,11 +775,77 @@ def bench_schedule(args, hdq, synth):
     }
     if args.tdc_steps > 0:
         result["tdc"] = bench_tdc(S, args, hdq, synth)
+    if args.dq_steps > 0:
+        result["deltaquant"] = bench_deltaquant(args, hdq, synth)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline_schedule(S, args, synth)
         result["cpu_baseline"]["value"] = round(result["cpu_baseline"]["value"], 6)
     return result
+
+
+def bench_deltaquant(args, hdq, synth):
+    """DeltaQuant's cube-delta path on one FFN up-projection of the CogVideoX-5B
+    video tokens (13 x 30 x 45 grid, K 3072 -> N 12288, 2 x 2 x 2 cubes, MX
+    NVFP4 differences): per-call times of the activation quantization and of
+    the linear, their rates against the roofline, and the output's relative
+    error against the bf16 product beside plain NVFP4 (no cubes, no rotation)."""
+    log("deltaquant")
+    F, H, W, K, N, cube, fmt = 13, 30, 45, 3072, 12288, (2, 2, 2), hdq.FMT_NVFP4_MX
+    grid = (F, H, W, cube)
+    M, C = F * H * W, hdq.dq_cubes(grid)
+    dev = torch.device("cuda:0")
+    x16 = synth.smooth_video_tokens(F, H, W, K, synth.rng_for(140, 0))
+    x = torch.from_numpy(x16.view(np.int16)).to(dev).view(torch.bfloat16)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(140)
+    w = synth.device_gaussian((N, K), 0.02, gen, dev)
+    W1 = hdq.LinearWeights(w, 1, fp4_fmt=fmt)    # no rotation: had_block 1
+    wq = W1.w_fp4
+    wdec = hdq.dq_decode_weights(wq)
+    a = hdq.dq_quantize(x, grid, fmt)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(hdq.workspace_bytes(hdq.OP_DQ_LINEAR, M, C, N), dtype=torch.uint8, device=dev)
+
+    def timed(fn, n):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    q_ms = timed(lambda: hdq.dq_quantize(x, grid, fmt, out=a), args.dq_steps)
+    l_ms = timed(lambda: hdq.dq_linear(a, wq, wdec, y=y, ws=ws), args.dq_steps)
+    # algorithmic bytes of the quantization: x once, the difference codes and
+    # block scales, the core codes, scales and bf16 code values
+    q_bytes = M * K * 2 + M * K // 2 + M * K // 16 + C * K * 3 + C * 4
+    flops = 2.0 * M * N * K + 2.0 * C * N * K
+    ref = x.float() @ w.float().T
+    plain = hdq.linear(hdq.PREC_NVFP4, None, W1, xq=hdq.quantize(x, 1, fmt), y_dtype=hdq.DTYPE_F32)
+    yd = hdq.dq_linear(a, wq, wdec, y_dtype=hdq.DTYPE_F32, ws=ws)
+    nref = float(torch.linalg.vector_norm(ref))
+    err = lambda t: round(float(torch.linalg.vector_norm(t - ref)) / nref, 5)
+    out = {"workload": "DeltaQuant cube-delta linear: 13x30x45 video tokens (17550), K 3072 -> N 12288, "
+                       "2x2x2 cubes (3105, ragged), FP8 E4M3 cores, NVFP4-MX differences, bf16 output",
+           "quantize_us": round(q_ms * 1e3, 1),
+           "quantize_gbps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
+           "quantize_roofline": {"bound": "hbm", "achieved": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
+                                 "peak": 8000.0, "unit": "GB/s",
+                                 "frac": round(q_bytes / (q_ms * 1e-3) / 1e9 / 8000.0, 3),
+                                 "traffic": None},
+           "linear_us": round(l_ms * 1e3, 1),
+           "linear_tflops": round(flops / (l_ms * 1e-3) / 1e12, 1),
+           "linear_roofline": {"bound": "mfma", "achieved": round(flops / (l_ms * 1e-3) / 1e12, 1),
+                               "peak": 10100.0, "unit": "TFLOP/s",
+                               "frac": round(flops / (l_ms * 1e-3) / 1e12 / 10100.0, 3), "traffic": None},
+           "rel_err_vs_bf16": err(yd), "plain_nvfp4_rel_err_vs_bf16": err(plain)}
+    del ref, plain, yd
+    return out
 
 
 def stored_traffic(kind, recipe):

@@ -412,12 +412,21 @@ int hdq_dq_linear(const hdq_dq_grid* g, const void* core_bf16, const float* core
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* yd = static_cast<float*>(ws);
   float* yc = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + yd_bytes);
+  // the core GEMM, then (MX and P2 formats, K % 256 == 0) the difference GEMM
+  // with the broadcast core term added in its epilogue
+  if (launch_gemm_bf16(static_cast<const uint16_t*>(core_bf16), static_cast<const uint16_t*>(w_dec), yc,
+                       HDQ_DTYPE_F32, C, N, K, nullptr, HDQ_PREC_BF16, s) != hipSuccess)
+    return HDQ_ERR_HIP;
+  const CoreAdd add{yc, core_scale, w_fp4->tensor_scale, d};
+  const hipError_t fe = launch_gemm_fp4_core_add(
+      static_cast<const uint8_t*>(delta->codes), delta->blk_scale, delta->tensor_scale,
+      static_cast<const uint8_t*>(w_fp4->codes), w_fp4->blk_scale, w_fp4->tensor_scale, delta->fmt, add, y, y_dtype,
+      M, N, K, s);
+  if (fe == hipSuccess) return HDQ_OK;
+  if (fe != hipErrorNotSupported) return HDQ_ERR_HIP;
   if (fp4_gemm_for(delta->fmt)(static_cast<const uint8_t*>(delta->codes), delta->blk_scale, delta->tensor_scale,
                                static_cast<const uint8_t*>(w_fp4->codes), w_fp4->blk_scale, w_fp4->tensor_scale,
                                yd, HDQ_DTYPE_F32, M, N, K, nullptr, HDQ_PREC_NVFP4, s) != hipSuccess)
-    return HDQ_ERR_HIP;
-  if (launch_gemm_bf16(static_cast<const uint16_t*>(core_bf16), static_cast<const uint16_t*>(w_dec), yc,
-                       HDQ_DTYPE_F32, C, N, K, nullptr, HDQ_PREC_BF16, s) != hipSuccess)
     return HDQ_ERR_HIP;
   return hip_status(launch_dq_combine(yd, yc, core_scale, w_fp4->tensor_scale, d, N, y, y_dtype, s));
 }

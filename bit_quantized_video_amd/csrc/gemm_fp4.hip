@@ -202,6 +202,44 @@ static hipError_t launch_fp4_pipe(const uint8_t* xc, const uint8_t* xs, const fl
   return hipGetLastError();
 }
 
+// The pipelined body with DeltaQuant's broadcast core term in its epilogue.
+template <int OUT, bool P2>
+__global__ __launch_bounds__(512) void k_gemm_fp4_core_add(
+    const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xsc, const float* __restrict__ xts,
+    const uint8_t* __restrict__ wc, const uint8_t* __restrict__ wsc, const float* __restrict__ wts,
+    void* __restrict__ Y, int M, int N, int K, const CoreAdd add) {
+  gemm_fp4mx_pipe_body<OUT, P2, true>(xc, xsc, xts, wc, wsc, wts, Y, M, N, K, 0, &add);
+}
+
+template <int OUT, bool P2>
+static hipError_t launch_core_add_t(const uint8_t* xc, const uint8_t* xs, const float* xts, const uint8_t* wc,
+                                    const uint8_t* ws, const float* wts, const CoreAdd& add, void* y, int64_t M,
+                                    int64_t N, int64_t K, hipStream_t s) {
+  constexpr size_t lds = (size_t)fp4_pipe_lds<P2>();
+  auto kern = k_gemm_fp4_core_add<OUT, P2>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  hipLaunchKernelGGL(kern, dim3((unsigned)persistent_grid(tiles)), dim3(512), lds, s, xc, xs, xts, wc, ws, wts, y,
+                     (int)M, (int)N, (int)K, add);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_fp4_core_add(const uint8_t* xc, const uint8_t* xs, const float* xts, const uint8_t* wc,
+                                    const uint8_t* ws, const float* wts, int fmt, const CoreAdd& add, void* y,
+                                    int out_dtype, int64_t M, int64_t N, int64_t K, hipStream_t s) {
+  if (K % 256 != 0 || M * K / 2 >= (1ll << 31) || N * K / 2 >= (1ll << 31) || N % 4 != 0)
+    return hipErrorNotSupported;
+  if (fmt == kNvfp4Mx)
+    return out_dtype == kOutF32 ? launch_core_add_t<kOutF32, false>(xc, xs, xts, wc, ws, wts, add, y, M, N, K, s)
+                                : launch_core_add_t<kOutBf16, false>(xc, xs, xts, wc, ws, wts, add, y, M, N, K, s);
+  if (fmt == kNvfp4P2)
+    return out_dtype == kOutF32 ? launch_core_add_t<kOutF32, true>(xc, xs, xts, wc, ws, wts, add, y, M, N, K, s)
+                                : launch_core_add_t<kOutBf16, true>(xc, xs, xts, wc, ws, wts, add, y, M, N, K, s);
+  return hipErrorNotSupported;
+}
+
 hipError_t launch_gemm_nvfp4_mx(const uint8_t* xc, const uint8_t* xs, const float* xts,
                                 const uint8_t* wc, const uint8_t* ws, const float* wts,
                                 void* y, int out_dtype, int64_t M, int64_t N, int64_t K,

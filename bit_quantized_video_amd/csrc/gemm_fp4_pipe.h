@@ -51,11 +51,12 @@ constexpr int fp4_pipe_lds() {
   return 2 * (256 * 128 * 2 + 512 * (P2 ? 16 : 8));
 }
 
-template <int OUT, bool P2 = false>
+// ADD: the output also gets the broadcast core term of `add` (N % 4 == 0).
+template <int OUT, bool P2 = false, bool ADD = false>
 __device__ __forceinline__ void gemm_fp4mx_pipe_body(
     const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xsc, const float* __restrict__ xts,
     const uint8_t* __restrict__ wc, const uint8_t* __restrict__ wsc, const float* __restrict__ wts,
-    void* __restrict__ Y, int M, int N, int K, int nwg = 0) {
+    void* __restrict__ Y, int M, int N, int K, int nwg = 0, const CoreAdd* add = nullptr) {
   constexpr int BM = 256, BN = 256, BK = 256, WM_T = 4, WN_T = 2;
   constexpr int XB = BM * BK / 2, WB = BN * BK / 2;  // code bytes per stage
   constexpr int SCB = P2 ? 16 : 8;                    // E8M0 bytes per row and stage
@@ -212,6 +213,22 @@ __device__ __forceinline__ void gemm_fp4mx_pipe_body(
   };
 
   const float scale = (*xts) * (*wts);
+  // fragment (i, j, g) of this lane: row wm * WM_T * 32 + 32 i + r32 of the
+  // tile, columns wn * WN_T * 32 + 32 j + 8 g + 4 h + 0..3; y[r] += the core term
+  auto core_add = [&](int m0, int n0, int i, int j, int g, float (&y)[4]) {
+    if constexpr (ADD) {
+      const int m = m0 + wm * WM_T * 32 + i * 32 + r32, n = n0 + wn * WN_T * 32 + j * 32 + 8 * g + 4 * h;
+      if (m < M && n < N) {
+        const int cb = dq_cube(m, add->g);
+        const float4 c = *reinterpret_cast<const float4*>(add->yc + (int64_t)cb * N + n);
+        const float cs = add->cs[cb], stw = *add->wts;
+        y[0] = y[0] + (c.x * cs) * stw;
+        y[1] = y[1] + (c.y * cs) * stw;
+        y[2] = y[2] + (c.z * cs) * stw;
+        y[3] = y[3] + (c.w * cs) * stw;
+      }
+    }
+  };
   auto epilogue = [&](int logical) {
     int tm, tn;
     grouped_tile(logical, tiles_m, tiles_n, tm, tn);
@@ -229,9 +246,10 @@ __device__ __forceinline__ void gemm_fp4mx_pipe_body(
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const v16f& a = acc[j][i];
+            float y[4] = {a[4 * g] * scale, a[4 * g + 1] * scale, a[4 * g + 2] * scale, a[4 * g + 3] * scale};
+            core_add(m0, n0, i, j, g, y);
             *reinterpret_cast<uint2*>(lrow + i * 32 * kOutPitch + 2 * (j * 32 + 8 * g)) =
-                make_uint2(pack_bf16x2(a[4 * g] * scale, a[4 * g + 1] * scale),
-                           pack_bf16x2(a[4 * g + 2] * scale, a[4 * g + 3] * scale));
+                make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
           }
       lds_barrier();
       uint16_t* y16 = reinterpret_cast<uint16_t*>(Y);
@@ -265,6 +283,7 @@ __device__ __forceinline__ void gemm_fp4mx_pipe_body(
             float y[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) y[r] = acc[j][i][4 * g + r] * scale;
+            core_add(m0, n0, i, j, g, y);
             if (full_n) {
               *reinterpret_cast<float4*>(reinterpret_cast<float*>(Y) + off) = make_float4(y[0], y[1], y[2], y[3]);
             } else {

@@ -130,6 +130,19 @@ hipError_t launch_gemm_dispatch(const int32_t* decision, const int8_t* x8, const
 struct DqGrid {
   int F, H, W, cf, ch, cw, nF, nH, nW;
 };
+// Cube of token m.
+__device__ __forceinline__ int dq_cube(int m, const DqGrid& g) {
+  const int hw = g.H * g.W, f = m / hw, r = m - f * hw, h = r / g.W, w = r - h * g.W;
+  return ((f / g.cf) * g.nH + h / g.ch) * g.nW + w / g.cw;
+}
+// The broadcast core term an NVFP4 GEMM adds to its output:
+// y[m, n] += fl32(fl32(yc[cube(m), n] * cs[cube(m)]) * wts[0]).
+struct CoreAdd {
+  const float* yc;
+  const float* cs;
+  const float* wts;
+  DqGrid g;
+};
 // Core tokens (codes, scales, optional bf16 code values) and the differences
 // in NVFP4 format fmt; damax_bits: device uint32 scratch.
 hipError_t launch_dq_quantize(const uint16_t* x, int64_t K, const DqGrid& g, int fmt, uint8_t* ccodes,
@@ -138,6 +151,11 @@ hipError_t launch_dq_quantize(const uint16_t* x, int64_t K, const DqGrid& g, int
 // NVFP4 weights [N, K] to bf16 E2M1 x block-scale values.
 hipError_t launch_dq_decode_w(const uint8_t* codes, const uint8_t* blk, int64_t N, int64_t K, uint16_t* out,
                               hipStream_t s);
+// NVFP4-MX / P2 GEMM (pipelined shapes: K % 256 == 0) whose output also
+// gets the broadcast core term; hipErrorNotSupported for other shapes.
+hipError_t launch_gemm_fp4_core_add(const uint8_t* xc, const uint8_t* xs, const float* xts, const uint8_t* wc,
+                                    const uint8_t* ws, const float* wts, int fmt, const CoreAdd& add, void* y,
+                                    int out_dtype, int64_t M, int64_t N, int64_t K, hipStream_t s);
 // y = yd + (yc of the token's cube) x s_c x s_tw (N a multiple of 4).
 hipError_t launch_dq_combine(const float* yd, const float* yc, const float* cscale, const float* wts,
                              const DqGrid& g, int64_t N, void* y, int out_dtype, hipStream_t s);

@@ -428,12 +428,6 @@ hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t rows, int64_t cols, int
 // max|core| / 448 (0 below kTiny); a code is the nearest E4M3 of |c| / s with
 // the sign in bit 7 (a zero magnitude stored as +0).
 
-// Cube of token m.
-__device__ __forceinline__ int dq_cube(int m, const DqGrid& g) {
-  const int hw = g.H * g.W, f = m / hw, r = m - f * hw, h = r / g.W, w = r - h * g.W;
-  return ((f / g.cf) * g.nH + h / g.ch) * g.nW + w / g.cw;
-}
-
 // One workgroup per cube: the mean in LDS, its scale and codes, the decoded
 // code values as bf16 (exact: E4M3 has 4 significant bits) for the core
 // GEMM, and the largest |difference| of the cube's tokens into the running
