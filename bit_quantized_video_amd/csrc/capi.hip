@@ -341,7 +341,8 @@ int hdq_linear_dispatch_delta(const int32_t* decision_dev, const void* x, const 
 // ---- DeltaQuant ----------------------------------------------------------
 static bool dq_grid(const hdq_dq_grid* g, DqGrid& d) {
   if (g == nullptr || g->frames <= 0 || g->height <= 0 || g->width <= 0 || g->cube_f <= 0 || g->cube_h <= 0 ||
-      g->cube_w <= 0 || g->frames * g->height * g->width > 0x7fffffff)
+      g->cube_w <= 0 || g->frames * g->height * g->width > 0x7fffffff ||
+      (int64_t)g->cube_f * g->cube_h * g->cube_w > kDqMaxCube)
     return false;
   d.F = (int)g->frames;
   d.H = (int)g->height;

@@ -214,14 +214,31 @@ __device__ __forceinline__ void gemm_fp4mx_pipe_body(
 
   const float scale = (*xts) * (*wts);
   // fragment (i, j, g) of this lane: row wm * WM_T * 32 + 32 i + r32 of the
-  // tile, columns wn * WN_T * 32 + 32 j + 8 g + 4 h + 0..3; y[r] += the core term
-  auto core_add = [&](int m0, int n0, int i, int j, int g, float (&y)[4]) {
+  // tile, columns wn * WN_T * 32 + 32 j + 8 g + 4 h + 0..3.  The core rows and
+  // scales of the lane's WM_T rows are looked up once per tile.
+  const float* crow[WM_T];
+  float ccs[WM_T];
+  auto core_rows = [&](int m0) {
     if constexpr (ADD) {
-      const int m = m0 + wm * WM_T * 32 + i * 32 + r32, n = n0 + wn * WN_T * 32 + j * 32 + 8 * g + 4 * h;
-      if (m < M && n < N) {
-        const int cb = dq_cube(m, add->g);
-        const float4 c = *reinterpret_cast<const float4*>(add->yc + (int64_t)cb * N + n);
-        const float cs = add->cs[cb], stw = *add->wts;
+#pragma unroll
+      for (int i = 0; i < WM_T; ++i) {
+        const int m = m0 + wm * WM_T * 32 + i * 32 + r32;
+        crow[i] = nullptr;
+        ccs[i] = 0.0f;
+        if (m < M) {
+          const int cb = dq_cube(m, add->g);
+          crow[i] = add->yc + (int64_t)cb * N;
+          ccs[i] = add->cs[cb];
+        }
+      }
+    }
+  };
+  auto core_add = [&](int n0, int i, int j, int g, float (&y)[4]) {
+    if constexpr (ADD) {
+      const int n = n0 + wn * WN_T * 32 + j * 32 + 8 * g + 4 * h;
+      if (crow[i] != nullptr && n < N) {
+        const float4 c = *reinterpret_cast<const float4*>(crow[i] + n);
+        const float cs = ccs[i], stw = *add->wts;
         y[0] = y[0] + (c.x * cs) * stw;
         y[1] = y[1] + (c.y * cs) * stw;
         y[2] = y[2] + (c.z * cs) * stw;
@@ -233,6 +250,7 @@ __device__ __forceinline__ void gemm_fp4mx_pipe_body(
     int tm, tn;
     grouped_tile(logical, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
+    if constexpr (ADD) core_rows(m0);
     if constexpr (OUT == kOutBf16) {
       // Stage the bf16 tile in LDS (both pipeline buffers are free once every
       // wave is past this stage; the next stage is still in registers), then
@@ -246,10 +264,16 @@ __device__ __forceinline__ void gemm_fp4mx_pipe_body(
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const v16f& a = acc[j][i];
-            float y[4] = {a[4 * g] * scale, a[4 * g + 1] * scale, a[4 * g + 2] * scale, a[4 * g + 3] * scale};
-            core_add(m0, n0, i, j, g, y);
-            *reinterpret_cast<uint2*>(lrow + i * 32 * kOutPitch + 2 * (j * 32 + 8 * g)) =
-                make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+            if constexpr (ADD) {
+              float y[4] = {a[4 * g] * scale, a[4 * g + 1] * scale, a[4 * g + 2] * scale, a[4 * g + 3] * scale};
+              core_add(n0, i, j, g, y);
+              *reinterpret_cast<uint2*>(lrow + i * 32 * kOutPitch + 2 * (j * 32 + 8 * g)) =
+                  make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+            } else {
+              *reinterpret_cast<uint2*>(lrow + i * 32 * kOutPitch + 2 * (j * 32 + 8 * g)) =
+                  make_uint2(pack_bf16x2(a[4 * g] * scale, a[4 * g + 1] * scale),
+                             pack_bf16x2(a[4 * g + 2] * scale, a[4 * g + 3] * scale));
+            }
           }
       lds_barrier();
       uint16_t* y16 = reinterpret_cast<uint16_t*>(Y);
@@ -283,7 +307,7 @@ __device__ __forceinline__ void gemm_fp4mx_pipe_body(
             float y[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) y[r] = acc[j][i][4 * g + r] * scale;
-            core_add(m0, n0, i, j, g, y);
+            if constexpr (ADD) core_add(n0, i, j, g, y);
             if (full_n) {
               *reinterpret_cast<float4*>(reinterpret_cast<float*>(Y) + off) = make_float4(y[0], y[1], y[2], y[3]);
             } else {

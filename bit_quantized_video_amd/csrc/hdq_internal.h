@@ -130,6 +130,7 @@ hipError_t launch_gemm_dispatch(const int32_t* decision, const int8_t* x8, const
 struct DqGrid {
   int F, H, W, cf, ch, cw, nF, nH, nW;
 };
+constexpr int kDqMaxCube = 256;  // tokens per cube (one per thread of a workgroup)
 // Cube of token m.
 __device__ __forceinline__ int dq_cube(int m, const DqGrid& g) {
   const int hw = g.H * g.W, f = m / hw, r = m - f * hw, h = r / g.W, w = r - h * g.W;

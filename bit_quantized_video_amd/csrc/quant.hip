@@ -428,34 +428,55 @@ hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t rows, int64_t cols, int
 // max|core| / 448 (0 below kTiny); a code is the nearest E4M3 of |c| / s with
 // the sign in bit 7 (a zero magnitude stored as +0).
 
-// One workgroup per cube: the mean in LDS, its scale and codes, the decoded
-// code values as bf16 (exact: E4M3 has 4 significant bits) for the core
-// GEMM, and the largest |difference| of the cube's tokens into the running
-// maximum (float bits of a non-negative value order as unsigned integers).
+// The rows of a cube's tokens in token order (at most kDqMaxCube tokens).
+__device__ __forceinline__ int dq_rows(const DqGrid& g, int cube, int* rows) {
+  const int a = cube / (g.nH * g.nW), b = (cube / g.nW) % g.nH, c = cube % g.nW;
+  const int f0 = a * g.cf, h0 = b * g.ch, w0 = c * g.cw;
+  const int nf = min(g.F, f0 + g.cf) - f0, nh = min(g.H, h0 + g.ch) - h0, nw = min(g.W, w0 + g.cw) - w0;
+  const int nt = nf * nh * nw, t = threadIdx.x;
+  if (t < nt) {
+    const int f = t / (nh * nw), r = t - f * nh * nw, h = r / nw, w = r - h * nw;
+    rows[t] = ((f0 + f) * g.H + h0 + h) * g.W + w0 + w;
+  }
+  __syncthreads();
+  return nt;
+}
+
+// One workgroup per cube: the mean in LDS (eight tokens' loads in flight,
+// added in token order), its scale and codes, the decoded code values as bf16
+// (exact: E4M3 has 4 significant bits) for the core GEMM, and the largest
+// |difference| of the cube's tokens into the running maximum (float bits of a
+// non-negative value order as unsigned integers).
 __global__ __launch_bounds__(256) void k_dq_core(const uint16_t* __restrict__ x, int K, const DqGrid g,
                                                  uint8_t* __restrict__ codes, float* __restrict__ scale,
                                                  uint16_t* __restrict__ core_bf16,
                                                  uint32_t* __restrict__ damax_bits) {
   extern __shared__ float lcore[];  // K floats: the mean, then the stored core
   __shared__ float red[4];
+  __shared__ int rows[kDqMaxCube];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int cube = blockIdx.x, a = cube / (g.nH * g.nW), b = (cube / g.nW) % g.nH, c = cube % g.nW;
-  const int f0 = a * g.cf, f1 = min(g.F, f0 + g.cf), h0 = b * g.ch, h1 = min(g.H, h0 + g.ch);
-  const int w0 = c * g.cw, w1 = min(g.W, w0 + g.cw);
-  const float n = (float)((f1 - f0) * (h1 - h0) * (w1 - w0));
+  const int cube = blockIdx.x, nt = dq_rows(g, cube, rows);
+  const float n = (float)nt;
   const int kq = K >> 3;
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   float amax = 0.0f;
   for (int q = tid; q < kq; q += 256) {
     float sum[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-    for (int f = f0; f < f1; ++f)
-      for (int h = h0; h < h1; ++h)
-        for (int w = w0; w < w1; ++w) {
+    for (int t0 = 0; t0 < nt; t0 += 8) {
+      uint4 w[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        w[u] = t0 + u < nt ? xv[(int64_t)rows[t0 + u] * kq + q] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (t0 + u < nt) {
           float v[8];
-          bf16x8_to_f32(xv[(int64_t)((f * g.H + h) * g.W + w) * kq + q], v);
+          bf16x8_to_f32(w[u], v);
 #pragma unroll
           for (int i = 0; i < 8; ++i) sum[i] = sum[i] + v[i];
         }
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float m = sum[i] / n;
@@ -488,15 +509,23 @@ __global__ __launch_bounds__(256) void k_dq_core(const uint16_t* __restrict__ x,
   }
   __syncthreads();
   float dmax = 0.0f;
-  for (int f = f0; f < f1; ++f)
-    for (int h = h0; h < h1; ++h)
-      for (int w = w0; w < w1; ++w)
-        for (int q = tid; q < kq; q += 256) {
+  for (int q = tid; q < kq; q += 256) {
+    for (int t0 = 0; t0 < nt; t0 += 8) {
+      uint4 w[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        w[u] = t0 + u < nt ? xv[(int64_t)rows[t0 + u] * kq + q] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (t0 + u < nt) {
           float v[8];
-          bf16x8_to_f32(xv[(int64_t)((f * g.H + h) * g.W + w) * kq + q], v);
+          bf16x8_to_f32(w[u], v);
 #pragma unroll
           for (int i = 0; i < 8; ++i) dmax = fmaxf(dmax, fabsf(v[i] - lcore[8 * q + i]));
         }
+      }
+    }
+  }
   dmax = wave_max(dmax);
   __syncthreads();
   if (lane == 0) red[wave] = dmax;
@@ -506,61 +535,57 @@ __global__ __launch_bounds__(256) void k_dq_core(const uint16_t* __restrict__ x,
 
 __global__ void k_dq_zero(uint32_t* p) { *p = 0u; }
 
-// Every token's difference from its cube's stored core, quantized to NVFP4
-// with the tensor scale of the largest |difference|.  Chunks and lanes as in
-// k_quant_nvfp4 with no rotation (a 16-element block on lanes l, l ^ 1).
+// One workgroup per cube: each token's difference from the stored core,
+// quantized to NVFP4 with the tensor scale of the largest |difference|.  A
+// wave covers 64 consecutive chunks of one token row, so a 16-element block
+// sits on lanes l, l ^ 1 and a 32-element group on l ^ {0..3}; every lane
+// runs the block code (zeros past the row), only the stores are predicated.
 template <int FMT>
 __global__ __launch_bounds__(256) void k_dq_delta(const uint16_t* __restrict__ x, int K, const DqGrid g,
-                                                  int64_t nch, const uint8_t* __restrict__ ccodes,
+                                                  const uint8_t* __restrict__ ccodes,
                                                   const float* __restrict__ cscale,
                                                   const uint32_t* __restrict__ damax_bits,
                                                   uint8_t* __restrict__ codes, uint8_t* __restrict__ blk_scale,
                                                   float* __restrict__ tensor_scale) {
-  constexpr int UNROLL = 2;
-  const int lane = threadIdx.x & 63, kq = K >> 3;
+  extern __shared__ float lcore[];  // the stored core, K floats
+  __shared__ int rows[kDqMaxCube];
+  const int tid = threadIdx.x, kq = K >> 3, cube = blockIdx.x;
   const float A = __uint_as_float(*damax_bits);
   const float s_t = (A >= kTiny) ? A / (FMT == kNvfp4 ? 2688.0f : 1536.0f) : 0.0f;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = s_t;
-  const float six_st = 6.0f * s_t;
-  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  if (cube == 0 && tid == 0) *tensor_scale = s_t;
+  const float six_st = 6.0f * s_t, sc = cscale[cube];
+  for (int k = tid; k < K; k += 256) {
+    const uint32_t b = ccodes[(int64_t)cube * K + k];
+    const float e = e4m3_decode(b & 0x7fu);
+    lcore[k] = ((b & 0x80u) ? -e : e) * sc;
+  }
+  const int nt = dq_rows(g, cube, rows);  // its barrier also publishes lcore
   const uint4* xv = reinterpret_cast<const uint4*>(x);
-  const uint2* cv2 = reinterpret_cast<const uint2*>(ccodes);
   uint32_t* cv = reinterpret_cast<uint32_t*>(codes);
-  for (int64_t base = wave * 64 * UNROLL; base < nch; base += nwaves * 64 * UNROLL) {
-    uint4 w[UNROLL];
-    uint2 cc[UNROLL];
-    float sc[UNROLL];
+  for (int q0 = 0; q0 < kq; q0 += 256) {
+    const int q = q0 + tid;
+    const bool ok = q < kq;
+    for (int t0 = 0; t0 < nt; t0 += 4) {
+      uint4 w[4];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int64_t idx = base + 64 * u + lane;
-      if (idx < nch) {
-        const int m = (int)(idx / kq), q = (int)(idx - (int64_t)m * kq), cb = dq_cube(m, g);
-        w[u] = xv[idx];
-        cc[u] = cv2[(int64_t)cb * kq + q];
-        sc[u] = cscale[cb];
-      } else {
-        w[u] = make_uint4(0u, 0u, 0u, 0u);
-        cc[u] = make_uint2(0u, 0u);
-        sc[u] = 0.0f;
-      }
-    }
+      for (int u = 0; u < 4; ++u)
+        w[u] = ok && t0 + u < nt ? xv[(int64_t)rows[t0 + u] * kq + q] : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int64_t idx = base + 64 * u + lane;
-      float v[8];
-      bf16x8_to_f32(w[u], v);
+      for (int u = 0; u < 4; ++u) {
+        if (t0 + u >= nt) break;  // uniform
+        float v[8];
+        bf16x8_to_f32(w[u], v);
+        if (ok) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t b = ((i < 4 ? cc[u].x : cc[u].y) >> (8 * (i & 3))) & 0xffu;
-        const float e = e4m3_decode(b & 0x7fu);
-        v[i] = v[i] - ((b & 0x80u) ? -e : e) * sc[u];
-      }
-      uint32_t e;
-      const uint32_t packed = nvfp4_chunk<FMT>(v, s_t, six_st, &e);
-      if (idx < nch) {
-        cv[idx] = packed;
-        if ((idx & 1) == 0) blk_scale[idx >> 1] = (uint8_t)e;
+          for (int i = 0; i < 8; ++i) v[i] = v[i] - lcore[8 * q + i];
+        }
+        uint32_t e;
+        const uint32_t packed = nvfp4_chunk<FMT>(v, s_t, six_st, &e);
+        if (ok) {
+          const int64_t idx = (int64_t)rows[t0 + u] * kq + q;
+          cv[idx] = packed;
+          if ((q & 1) == 0) blk_scale[idx >> 1] = (uint8_t)e;
+        }
       }
     }
   }
@@ -571,19 +596,16 @@ hipError_t launch_dq_quantize(const uint16_t* x, int64_t K, const DqGrid& g, int
                               uint8_t* blk_scale, float* tensor_scale, hipStream_t s) {
   const int64_t ncubes = (int64_t)g.nF * g.nH * g.nW;
   const size_t lds = (size_t)K * sizeof(float);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_dq_core),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
+  auto kdelta = fmt == kNvfp4Mx ? k_dq_delta<kNvfp4Mx> : fmt == kNvfp4P2 ? k_dq_delta<kNvfp4P2> : k_dq_delta<kNvfp4>;
+  for (const void* k : {reinterpret_cast<const void*>(k_dq_core), reinterpret_cast<const void*>(kdelta)}) {
+    hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(k_dq_zero, dim3(1), dim3(1), 0, s, damax_bits);
   hipLaunchKernelGGL(k_dq_core, dim3((unsigned)ncubes), dim3(256), lds, s, x, (int)K, g, ccodes, cscale,
                      core_bf16, damax_bits);
-  const int64_t nch = (int64_t)g.F * g.H * g.W * K / 8;
-  int64_t blocks = ((nch + 127) / 128 + 3) / 4;
-  if (blocks > 2048) blocks = 2048;
-  if (blocks < 1) blocks = 1;
-  auto kern = fmt == kNvfp4Mx ? k_dq_delta<kNvfp4Mx> : fmt == kNvfp4P2 ? k_dq_delta<kNvfp4P2> : k_dq_delta<kNvfp4>;
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, s, x, (int)K, g, nch, ccodes, cscale,
-                     damax_bits, codes, blk_scale, tensor_scale);
+  hipLaunchKernelGGL(kdelta, dim3((unsigned)ncubes), dim3(256), lds, s, x, (int)K, g, ccodes, cscale, damax_bits,
+                     codes, blk_scale, tensor_scale);
   return hipGetLastError();
 }
 

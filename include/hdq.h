@@ -400,7 +400,8 @@ typedef struct hdq_dq_grid {
   int32_t cube_f, cube_h, cube_w;
 } hdq_dq_grid;
 
-/* Cubes of the grid, -1 for a bad grid (a size <= 0, or over 2^31 - 1 tokens). */
+/* Cubes of the grid, -1 for a bad grid (a size <= 0, over 2^31 - 1 tokens, or
+ * more than 256 tokens per cube). */
 int64_t hdq_dq_cubes(const hdq_dq_grid *g);
 
 /*

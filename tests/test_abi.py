@@ -186,6 +186,7 @@ def test_deltaquant_validation(hdq):
     assert L.hdq_dq_cubes(ctypes.byref(g)) == 2 * 3 * 4
     assert L.hdq_dq_cubes(ctypes.byref(hdq.DqGridDesc(3, 5, 7, 0, 2, 2))) == -1
     assert L.hdq_dq_cubes(None) == -1
+    assert L.hdq_dq_cubes(ctypes.byref(hdq.DqGridDesc(13, 30, 45, 8, 8, 8))) == -1   # > 256 tokens per cube
     M, K = 105, 64
     delta = hdq.QTensorDesc(hdq.FMT_NVFP4_MX, 1, M, K, fake, None, fake, fake)
     q = lambda x=fake, K=K, g=g, fmt=hdq.FMT_NVFP4_MX, d=delta, ws=fake, wsb=256: L.hdq_dq_quantize(
