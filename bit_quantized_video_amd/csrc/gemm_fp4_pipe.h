@@ -233,18 +233,24 @@ __device__ __forceinline__ void gemm_fp4mx_pipe_body(
       }
     }
   };
-  auto core_add = [&](int n0, int i, int j, int g, float (&y)[4]) {
-    if constexpr (ADD) {
-      const int n = n0 + wn * WN_T * 32 + j * 32 + 8 * g + 4 * h;
-      if (crow[i] != nullptr && n < N) {
-        const float4 c = *reinterpret_cast<const float4*>(crow[i] + n);
-        const float cs = ccs[i], stw = *add->wts;
-        y[0] = y[0] + (c.x * cs) * stw;
-        y[1] = y[1] + (c.y * cs) * stw;
-        y[2] = y[2] + (c.z * cs) * stw;
-        y[3] = y[3] + (c.w * cs) * stw;
+  // The core terms of row i's 4 * WN_T column groups, loaded together before
+  // they are used (one wait per row instead of one per group).
+  auto core_load = [&](int n0, int i, float4 (&cv)[WN_T][4]) {
+#pragma unroll
+    for (int j = 0; j < WN_T; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * WN_T * 32 + j * 32 + 8 * g + 4 * h;
+        cv[j][g] = crow[i] != nullptr && n < N ? *reinterpret_cast<const float4*>(crow[i] + n)
+                                               : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
       }
-    }
+  };
+  auto core_add = [&](const float4& c, int i, float (&y)[4]) {
+    const float cs = ccs[i], stw = *add->wts;
+    y[0] = y[0] + (c.x * cs) * stw;
+    y[1] = y[1] + (c.y * cs) * stw;
+    y[2] = y[2] + (c.z * cs) * stw;
+    y[3] = y[3] + (c.w * cs) * stw;
   };
   auto epilogue = [&](int logical) {
     int tm, tn;
@@ -258,7 +264,9 @@ __device__ __forceinline__ void gemm_fp4mx_pipe_body(
       lds_barrier();
       uint8_t* const lrow = smem + (wm * WM_T * 32 + r32) * kOutPitch + 2 * (wn * WN_T * 32 + 4 * h);
 #pragma unroll
-      for (int i = 0; i < WM_T; ++i)
+      for (int i = 0; i < WM_T; ++i) {
+        float4 cv[ADD ? WN_T : 1][4];
+        if constexpr (ADD) core_load(n0, i, cv);
 #pragma unroll
         for (int j = 0; j < WN_T; ++j)
 #pragma unroll
@@ -266,7 +274,7 @@ __device__ __forceinline__ void gemm_fp4mx_pipe_body(
             const v16f& a = acc[j][i];
             if constexpr (ADD) {
               float y[4] = {a[4 * g] * scale, a[4 * g + 1] * scale, a[4 * g + 2] * scale, a[4 * g + 3] * scale};
-              core_add(n0, i, j, g, y);
+              core_add(cv[j][g], i, y);
               *reinterpret_cast<uint2*>(lrow + i * 32 * kOutPitch + 2 * (j * 32 + 8 * g)) =
                   make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
             } else {
@@ -275,6 +283,7 @@ __device__ __forceinline__ void gemm_fp4mx_pipe_body(
                              pack_bf16x2(a[4 * g + 2] * scale, a[4 * g + 3] * scale));
             }
           }
+      }
       lds_barrier();
       uint16_t* y16 = reinterpret_cast<uint16_t*>(Y);
       const int n = n0 + 8 * (tid & 31);
@@ -298,6 +307,8 @@ __device__ __forceinline__ void gemm_fp4mx_pipe_body(
       for (int i = 0; i < WM_T; ++i) {
         const int m = m0 + wm * WM_T * 32 + i * 32 + r32;
         if (m >= M) continue;
+        float4 cv[ADD ? WN_T : 1][4];
+        if constexpr (ADD) core_load(n0, i, cv);
 #pragma unroll
         for (int j = 0; j < WN_T; ++j) {
 #pragma unroll
@@ -307,7 +318,7 @@ __device__ __forceinline__ void gemm_fp4mx_pipe_body(
             float y[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) y[r] = acc[j][i][4 * g + r] * scale;
-            if constexpr (ADD) core_add(n0, i, j, g, y);
+            if constexpr (ADD) core_add(cv[j][g], i, y);
             if (full_n) {
               *reinterpret_cast<float4*>(reinterpret_cast<float*>(Y) + off) = make_float4(y[0], y[1], y[2], y[3]);
             } else {
