@@ -120,6 +120,52 @@ def test_spike_is_spread_flat(b):
         assert np.array_equal(np.sign(y[0]), H[j].astype(np.float32))
 
 
+# ------------------------------------------------------- bf16 rounding
+# Every bf16 expected value of the parity tests is the oracle's double or
+# float32 result put through orc_f32_to_bf16; torch's float32 -> bfloat16
+# cast (round to nearest, ties to even) is the independent codec.
+
+def bf16_probe_bits():
+    """float32 bit patterns around every rounding decision of the cast."""
+    rng = np.random.default_rng(40)
+    keeps = np.concatenate([
+        np.arange(0x0000, 0x0100), np.arange(0x3f00, 0x4100), np.arange(0x7e80, 0x7f80),
+        rng.integers(0, 0x7f80, 4000)]).astype(np.uint32)
+    keeps = np.concatenate([keeps, keeps | 0x8000])               # both signs
+    rests = np.array([0x0000, 0x0001, 0x7fff, 0x8000, 0x8001, 0xffff], np.uint32)
+    grid = (keeps[:, None] << 16 | rests[None, :]).ravel()
+    special = np.array([0x00000000, 0x80000000, 0x7f800000, 0xff800000,       # +-0, +-inf
+                        0x7f7f7fff, 0x7f7f8000, 0x7f7fffff, 0xff7f8000,       # overflow ties
+                        0x7f7e8000, 0x00008000, 0x00018000, 0x80008000,       # even/odd ties
+                        0x007fffff, 0x00800000, 0x0000ffff], np.uint32)
+    rand = rng.integers(0, 2 ** 32, 200000, dtype=np.uint64).astype(np.uint32)
+    return np.concatenate([grid, special, rand])
+
+
+def test_bf16_rounding_matches_torch_cast():
+    bits = bf16_probe_bits()
+    f = bits.view(np.float32)
+    nan = np.isnan(f)
+    got = O.f32_to_bf16(f)
+    ref = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # NaN stays NaN (quiet): exponent all ones, mantissa nonzero, quiet bit set
+    g = got[nan]
+    assert np.all((g & 0x7f80) == 0x7f80) and np.all((g & 0x0040) != 0)
+    # the scalar entry point is the same codec
+    for b in bits[:: 997]:
+        v = np.array([b], np.uint32).view(np.float32)
+        if not np.isnan(v[0]):
+            assert O.lib().orc_f32_to_bf16(float(v[0])) == O.f32_to_bf16(v)[0]
+    # hand cases: ties to even in both directions, overflow to infinity
+    case = lambda u: int(O.f32_to_bf16(np.array([u], np.uint32).view(np.float32))[0])
+    assert case(0x3f808000) == 0x3f80 and case(0x3f818000) == 0x3f82
+    assert case(0x3f807fff) == 0x3f80 and case(0x3f808001) == 0x3f81
+    assert case(0x7f7f8000) == 0x7f80 and case(0xff7f8000) == 0xff80
+    assert case(0x7f7f7fff) == 0x7f7f
+    assert case(0x00008000) == 0x0000 and case(0x00018000) == 0x0002 and case(0x80008000) == 0x8000
+
+
 # ------------------------------------------------------- P3 E2M1 codec
 
 def load_e2m1_golden():
@@ -321,6 +367,46 @@ def test_nvfp4_zero_tensor_and_zero_blocks():
     x16[0, :32] = synth.to_bf16_bits(np.full(32, 3.0, np.float32))
     codes, sc, st = O.quant_nvfp4(x16, 32)
     assert sc[1].sum() == 0 and codes[1].sum() == 0   # zero row -> zero blocks
+
+
+def test_nvfp4_plain_block_scales_and_codes_match_independent_codecs():
+    """Plain NVFP4, each 16-block on its own: the scale byte is torch's
+    float8_e4m3fn cast of t = a_blk / (6 s_t) (clamped at 448, where the cast
+    would give NaN), s_t = amax / 2688; every code is the nearest E2M1 grid
+    point of y * fl32(1/d), d = E * s_t, ties to the even code.  Rows scaled
+    by 2^-1 ... 2^-23 walk t through the normal, subnormal and flushed E4M3
+    ranges."""
+    M, K, b = 48, 512, 64
+    x = synth.bf16_bits_to_f32(synth.lognormal_tokens(M, K, synth.rng_for(9, 41), sigma=0.7))
+    x = x * (2.0 ** -(np.arange(M) % 24)).astype(np.float32)[:, None]   # exact: powers of two
+    x16 = synth.to_bf16_bits(x)
+    y = O.rotate_f32(x16, b)
+    codes, sc, st = O.quant_nvfp4(x16, b, mx=0)
+    amax = np.float32(np.abs(y).max())
+    assert st == amax / np.float32(2688.0)
+    six_st = np.float32(6.0) * st
+    a_blk = np.abs(y).reshape(M, K // 16, 16).max(axis=2)
+    t = np.minimum(a_blk / six_st, np.float32(448.0)).astype(np.float32)
+    ref = torch.from_numpy(t.copy()).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(sc, ref)
+    # the walk does reach subnormal scales (exponent field 0) and flushed blocks
+    assert ((sc > 0) & (sc < 0x08)).any() and (sc == 0).any() and (sc >= 0x70).any()
+    # codes: brute-force nearest on the E2M1 grid, independent of the oracle's encoder
+    d = (torch.from_numpy(sc.copy()).view(torch.float8_e4m3fn).float().numpy() * st).astype(np.float32)
+    inv = np.where(d > 0, np.float32(1.0) / np.where(d > 0, d, 1), 0).astype(np.float32)
+    v = (y.reshape(M, K // 16, 16) * inv[:, :, None]).astype(np.float32).reshape(M, K)
+    grid = np.array([e2m1_from_bits(c) for c in range(8)])
+    mag = np.minimum(np.abs(v.astype(np.float64)), 6.0)
+    dist = np.abs(mag[..., None] - grid)
+    near = dist.min(-1, keepdims=True)
+    cand = dist == near
+    # ties: the candidate with the even code (mantissa bit 0)
+    pick = np.where(cand.sum(-1) > 1, np.argmax(cand & (np.arange(8) % 2 == 0), -1), np.argmax(cand, -1))
+    want = (pick | np.where(np.signbit(v), 8, 0)).astype(np.uint8)
+    want[np.repeat(d == 0, 16, axis=1)] = 0
+    got = np.stack([codes & 0xF, codes >> 4], -1).reshape(M, K)
+    same = (got == want) | (((got & 7) == 0) & ((want & 7) == 0))      # +-0 by value
+    assert same.all()
 
 
 # ------------------------------------------------------ P6 GEMMs
