@@ -328,14 +328,16 @@ def dq_quantize(x16, F, H, W, cube, mx=0):
     return dict(core=codes, core_scale=scale, delta=d, delta_amax=amax, codes=dc, blk=de, s_t=st)
 
 
-def dq_linear(q, wc, we, wst, K, F, H, W, cube):
+def dq_linear(q, wc, we, wst, K, F, H, W, cube, rows=None):
     """y = (difference codes) x W^T + (its cube's FP8 core) x W^T for every
-    token, float64, W the NVFP4 weights (codes, block scales, tensor scale)."""
-    yd = gemm_nvfp4(q["codes"], q["blk"], q["s_t"], wc, we, wst, K)
+    token (or the tokens `rows`), float64, W the NVFP4 weights (codes, block
+    scales, tensor scale)."""
+    rows = np.arange(F * H * W) if rows is None else np.asarray(rows)
+    yd = gemm_nvfp4(q["codes"][rows], q["blk"][rows], q["s_t"], wc, we, wst, K)
     wdec = dequant_nvfp4(wc, we, 1.0, K).astype(np.float64)       # e2m1 x block scale, exact
     core = e4m3s_decode(q["core"]).astype(np.float64) * q["core_scale"].astype(np.float64)[:, None]
     yc = (core @ wdec.T) * float(wst)
-    return yd + yc[dq_cube_of(F, H, W, cube)]
+    return yd + yc[dq_cube_of(F, H, W, cube)[rows]]
 
 
 # ------------------------------------------------------------ selection

@@ -92,37 +92,50 @@ def test_dq_decode_weights_exact(fmt):
 
 
 def linear_case(F, H, W, K, N, cube, fmt, rows=None, y_dtype=hdq.DTYPE_BF16, seed=0):
+    """The GPU linear against the oracle's double result computed from the
+    oracle's own codes (rows: the tokens compared; all when None).  Returns the
+    relative Frobenius error; asserts the GPU's codes on those rows are the
+    oracle's and the per-element bound: float32 accumulation over K (c u S,
+    c = max(4, 2 sqrt(K / 16)), S = sum_k |d_k w_k| + sum_k |core_k w_k|), the
+    epilogue's roundings (4 u |ref|) and half a bf16 ulp for bf16 output."""
     x16 = synth.smooth_video_tokens(F, H, W, K, synth.rng_for(133, seed))
     w16 = synth.gaussian(N, K, 0.02, synth.rng_for(134, seed))
     a = hdq.dq_quantize(to_dev(x16), (F, H, W, cube), fmt)
     wq = hdq.quantize(to_dev(w16), 1, fmt)
     y = hdq.dq_linear(a, wq, hdq.dq_decode_weights(wq), y_dtype=y_dtype)
     torch.cuda.synchronize()
-    q = O.dq_quantize(x16, F, H, W, cube, MX[fmt]) if rows is None else None
+    rows = np.arange(F * H * W) if rows is None else np.asarray(rows)
+    q = O.dq_quantize(x16, F, H, W, cube, MX[fmt])
+    assert np.array_equal(u8(a.delta.codes)[rows], q["codes"][rows])
+    assert np.array_equal(u8(a.delta.blk_scale)[rows], q["blk"][rows])
+    assert np.array_equal(u8(a.core), q["core"]) and float(a.delta.tensor_scale.item()) == float(q["s_t"])
     wc, we, wst = O.quant_nvfp4(w16, 1, mx=MX[fmt])
-    if rows is None:
-        ref = O.dq_linear(q, wc, we, wst, K, F, H, W, cube)
-        got = y.float().cpu().numpy()
-    else:
-        # sampled rows: the GPU's own codes (bit-exact with the oracle's, checked
-        # above at this size) in the oracle's double GEMMs
-        cube_of = O.dq_cube_of(F, H, W, cube)
-        sub = dict(codes=u8(a.delta.codes)[rows], blk=u8(a.delta.blk_scale)[rows],
-                   s_t=np.float32(a.delta.tensor_scale.item()), core=u8(a.core), core_scale=a.core_scale.cpu().numpy())
-        yd = O.gemm_nvfp4(sub["codes"], sub["blk"], sub["s_t"], wc, we, wst, K)
-        cubes = cube_of[rows]
-        core = O.e4m3s_decode(sub["core"][cubes]).astype(np.float64) * sub["core_scale"][cubes].astype(np.float64)[:, None]
-        ref = yd + (core @ O.dequant_nvfp4(wc, we, 1.0, K).astype(np.float64).T) * float(wst)
-        got = y.float().cpu().numpy()[rows]
+    ref64 = O.dq_linear(q, wc, we, wst, K, F, H, W, cube, rows=rows)
+    got = y.float().cpu().numpy()[rows].astype(np.float64)
+    ref = ref64
     if y_dtype == hdq.DTYPE_BF16:      # the oracle's result rounded to the output dtype
-        ref = synth.bf16_bits_to_f32(synth.to_bf16_bits(ref.astype(np.float32))).astype(np.float64)
+        ref = synth.bf16_bits_to_f32(O.f32_to_bf16(ref64.astype(np.float32))).astype(np.float64)
     err = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    # per-element bound
+    wabs = np.abs(O.dequant_nvfp4(wc, we, wst, K).astype(np.float64))
+    dabs = np.abs(O.dequant_nvfp4(q["codes"][rows], q["blk"][rows], q["s_t"], K).astype(np.float64))
+    core = np.abs(O.e4m3s_decode(q["core"]).astype(np.float64) * q["core_scale"].astype(np.float64)[:, None])
+    S = dabs @ wabs.T + (core @ wabs.T)[O.dq_cube_of(F, H, W, cube)[rows]]
+    c = max(4.0, 2.0 * np.sqrt(K / 16.0))
+    tol = c * 2.0 ** -24 * S + 4 * 2.0 ** -24 * np.abs(ref64) + 1e-35
+    if y_dtype == hdq.DTYPE_BF16:
+        tol = tol + 2.0 ** -8 * 1.01 * np.abs(got)
+    bad = np.abs(got - ref64) > tol
+    assert not bad.any(), f"{int(bad.sum())} outputs beyond the per-element bound"
     return err
 
 
 @pytest.mark.parametrize("grid,cube,K,N,fmt", [((3, 5, 7), (2, 2, 2), 64, 40, "nvfp4"),
                                                ((4, 6, 10), (2, 2, 2), 256, 300, "mx"),
-                                               ((3, 8, 8), (1, 2, 2), 512, 96, "p2")])
+                                               ((3, 8, 8), (1, 2, 2), 512, 96, "p2"),
+                                               # four 256-token tiles of the fused epilogue
+                                               ((4, 12, 20), (2, 2, 2), 512, 520, "p2"),
+                                               ((4, 12, 20), (2, 3, 4), 512, 264, "mx")])
 @pytest.mark.parametrize("y_dtype", [hdq.DTYPE_BF16, hdq.DTYPE_F32])
 def test_dq_linear_matches_oracle(grid, cube, K, N, fmt, y_dtype):
     say(f"dq linear grid={grid} cube={cube} K={K} N={N} {fmt} y={y_dtype}")
@@ -132,7 +145,8 @@ def test_dq_linear_matches_oracle(grid, cube, K, N, fmt, y_dtype):
 
 def test_dq_linear_full_size_sampled_rows():
     """13 x 30 x 45 tokens, K 3072 -> N 12288 (the FFN up-projection's shape),
-    MX format: the first 256 and last 112 tokens against the oracle."""
+    MX format: the first 256 and last 112 tokens against the oracle's result
+    from its own codes of the whole grid."""
     say("dq linear full size")
     M = 13 * 30 * 45
     rows = np.r_[0:256, M - 112:M]

@@ -61,6 +61,40 @@ def rel_fro(got, ref):
     return np.linalg.norm(got - ref) / (den if den > 0 else 1.0)
 
 
+def abs_products_nvfp4(ac, ae, ast, wc, we, wst, K):
+    """S[m, n] = sum_k |a_k w_k| over the decoded NVFP4 operands (double)."""
+    a = np.abs(O.dequant_nvfp4(ac, ae, ast, K).astype(np.float64))
+    w = np.abs(O.dequant_nvfp4(wc, we, wst, K).astype(np.float64))
+    return a @ w.T
+
+
+def abs_products_bf16(x16, w16):
+    """S[m, n] = sum_k |x_k w_k| over the bf16 operands (double)."""
+    return np.abs(f32_from_bf16_np(x16).astype(np.float64)) @ np.abs(f32_from_bf16_np(w16).astype(np.float64)).T
+
+
+def assert_elementwise(got, ref64, S, K, bf16_out, what=""):
+    """Per-element bar beside the Frobenius one, so that a wrong tile whose
+    error is small next to the whole output's norm still fails.  got is the
+    GPU output, ref64 the oracle's unrounded double result, S = sum_k |a_k w_k|.
+    The GPU's only freedom is the float32 accumulation order over K: c u S
+    with c = max(4, 2 sqrt(K / 16)) (u = 2^-24; the probabilistic rounding-error
+    bound of a sum of K / 16 accumulated MFMA partials, with margin), plus
+    4 u |ref| for the epilogue's scale multiplies, plus half a bf16 ulp of the
+    stored value for bf16 output."""
+    got = np.asarray(got, np.float64)
+    ref64 = np.asarray(ref64, np.float64)
+    c = max(4.0, 2.0 * math.sqrt(K / 16.0))
+    tol = c * 2.0 ** -24 * S + 4 * 2.0 ** -24 * np.abs(ref64) + 1e-35
+    if bf16_out:
+        tol = tol + 2.0 ** -8 * 1.01 * np.abs(got)
+    err = np.abs(got - ref64)
+    worst = float((err / tol).max()) if err.size else 0.0
+    n_bad = int((err > tol).sum())
+    assert n_bad == 0, f"{what}: {n_bad} of {err.size} outputs beyond the per-element bound (worst {worst:.2f}x)"
+    return worst
+
+
 def round_like(ref64, y_dtype):
     if y_dtype == hdq.DTYPE_BF16:
         return f32_from_bf16_np(O.f32_to_bf16(ref64.astype(np.float32))).astype(np.float64)
@@ -291,6 +325,29 @@ def test_stats_hand_cases():
     assert st[0] == 0.25 and dec == hdq.PREC_INT8
 
 
+def test_delta_exactly_at_threshold_goes_int8():
+    """A difference exactly at the threshold takes the large-difference side
+    (INT8), a threshold one float32 step above it gives NVFP4: in = 8,
+    out = 9 gives delta = 1/8 exactly.  One-pass, two-part and fused
+    selection, and the oracle's rule, agree."""
+    b = synth.to_bf16_bits
+    pi, po = to_dev(b(np.full((4, 64), 8.0, np.float32))), to_dev(b(np.full((4, 64), 9.0, np.float32)))
+    cur16 = synth.gaussian(4, 64, 1.0, synth.rng_for(117, 0))
+    cur = to_dev(cur16)
+    above = float(np.nextafter(np.float32(0.125), np.float32(1)))
+    for th, want in ((0.125, hdq.PREC_INT8), (above, hdq.PREC_NVFP4)):
+        d1, s1 = hdq.select_precision(pi, po, cur, 64, delta_thresh=th)
+        sums = hdq.delta_sums(pi, po)
+        d2, s2 = hdq.select_precision_sums(sums, cur, 64, delta_thresh=th)
+        d3, s3, _ = hdq.select_quantize_int8(sums, cur, 64, delta_thresh=th)
+        torch.cuda.synchronize()
+        assert float(s1[0].item()) == 0.125 and float(s2[0].item()) == 0.125 and float(s3[0].item()) == 0.125
+        assert float(s1[1].item()) <= 50.0
+        assert int(d1.item()) == int(d2.item()) == int(d3.item()) == want, th
+        ref = O.stats(b(np.full((4, 64), 8.0, np.float32)), b(np.full((4, 64), 9.0, np.float32)), cur16, 64)
+        assert ref[0] == 0.125 and O.decide(True, ref[0], ref[1], th, 50.0) == want
+
+
 # ------------------------------------------------------------ GEMMs
 
 def int_operands(M, N, K, hb, seed):
@@ -348,8 +405,10 @@ def test_bf16_gemm_multi_tile_workgroups(K):
     W = hdq.LinearWeights(to_dev(w16), 32, fp4_fmt=None)
     y = hdq.linear(hdq.PREC_BF16, to_dev(x16), W, y_dtype=hdq.DTYPE_F32)
     torch.cuda.synchronize()
-    ref = round_like(O.gemm_bf16(x16[MT_ROWS], w16), hdq.DTYPE_F32)
+    ref64 = O.gemm_bf16(x16[MT_ROWS], w16)
+    ref = round_like(ref64, hdq.DTYPE_F32)
     assert rel_fro(y_np(y)[MT_ROWS], ref) <= REL_TOL
+    assert_elementwise(y_np(y)[MT_ROWS], ref64, abs_products_bf16(x16[MT_ROWS], w16), K, False, "bf16 multi-tile")
 
 
 @pytest.mark.parametrize("fmt,K", [(hdq.FMT_NVFP4_MX, K) for K in (256, 512, 768)] +
@@ -365,18 +424,26 @@ def test_fp4_gemm_multi_tile_workgroups(fmt, K):
     mx = FP4_FMTS[fmt]
     ac, ae, ast = O.quant_nvfp4(x16[MT_ROWS], hb, amax=O.rotated_amax(x16, hb), mx=mx)
     wc, we, wst = O.quant_nvfp4(w16, hb, mx=mx)
-    ref = round_like(O.gemm_nvfp4(ac, ae, ast, wc, we, wst, K), hdq.DTYPE_F32)
+    ref64 = O.gemm_nvfp4(ac, ae, ast, wc, we, wst, K)
+    ref = round_like(ref64, hdq.DTYPE_F32)
     assert rel_fro(y_np(y)[MT_ROWS], ref) <= REL_TOL
+    assert_elementwise(y_np(y)[MT_ROWS], ref64, abs_products_nvfp4(ac, ae, ast, wc, we, wst, K), K, False,
+                       "fp4 multi-tile")
 
 
-@pytest.mark.parametrize("fmt", [hdq.FMT_NVFP4_MX, hdq.FMT_NVFP4_P2])
+@pytest.mark.parametrize("fmt", [hdq.FMT_NVFP4, hdq.FMT_NVFP4_MX, hdq.FMT_NVFP4_P2])
 def test_fp4_gemm_subnormal_block_scales(fmt):
-    # rows scaled by 2^-13 ... 2^-18 and a zero row: their blocks' power-of-two
-    # E4M3 scales are the subnormal codes 2^-7, 2^-8 and 2^-9 (also the clamp,
-    # and the zero row's), which the FP4 kernels turn into E8M0 exponents
+    # Rows scaled by powers of two and one zero row.  MX / per-16 powers of
+    # two (rows x 2^-13 ... 2^-18): the blocks' power-of-two E4M3 scales are
+    # the subnormal codes 2^-7, 2^-8 and 2^-9 (also the clamp, and the zero
+    # row's), which the FP4 kernels turn into E8M0 exponents.  Plain NVFP4
+    # (rows x 2^-14 ... 2^-19): t = a_blk / (6 s_t) walks from the smallest
+    # normal E4M3 through the subnormal codes k 2^-9 to blocks flushed to 0,
+    # through hdq_quantize and the exact bf16-MFMA kernel.
     M, N, K, hb = 300, 272, 512, 32
     rows = np.arange(M)
-    scale = np.where(rows % 8 == 0, 1.0, 2.0 ** -(12 + rows % 8)).astype(np.float32)
+    first = 13 if fmt == hdq.FMT_NVFP4 else 12
+    scale = np.where(rows % 8 == 0, 1.0, 2.0 ** -(first + rows % 8)).astype(np.float32)
     scale[7] = 0.0
     x = synth.bf16_bits_to_f32(synth.gaussian(M, K, 1.0, synth.rng_for(110, fmt)))
     x16 = synth.to_bf16_bits(x * scale[:, None])       # exact: powers of two
@@ -387,14 +454,23 @@ def test_fp4_gemm_subnormal_block_scales(fmt):
     torch.cuda.synchronize()
     mx = FP4_FMTS[fmt]
     ac, ae, ast = O.quant_nvfp4(x16, hb, mx=mx)
-    assert np.isin([1, 2, 4], ae).all()     # the subnormal scales occur
+    if fmt == hdq.FMT_NVFP4:
+        sub = (ae > 0) & (ae < 0x08)
+        assert len(np.unique(ae[sub])) >= 4          # several subnormal scale codes occur
+        assert (ae[(rows % 8 == 5) | (rows % 8 == 6)] == 0).any()   # and flushed blocks in nonzero rows
+    else:
+        assert np.isin([1, 2, 4], ae).all()          # the subnormal scales occur
     assert np.array_equal(xq.blk_scale.cpu().numpy().reshape(ae.shape), ae)
+    assert xq.tensor_scale.item() == ast
+    nvfp4_codes_equal(xq.codes.cpu().numpy(), ac, "E2M1 codes")
     wc, we, wst = O.quant_nvfp4(w16, hb, mx=mx)
-    ref = round_like(O.gemm_nvfp4(ac, ae, ast, wc, we, wst, K), hdq.DTYPE_F32)
+    ref64 = O.gemm_nvfp4(ac, ae, ast, wc, we, wst, K)
+    ref = round_like(ref64, hdq.DTYPE_F32)
     got = y_np(y)
     for r in range(8):       # every row class separately: the tiny rows carry tiny outputs
         sel = rows % 8 == r
         assert rel_fro(got[sel], ref[sel]) <= REL_TOL, r
+    assert_elementwise(got, ref64, abs_products_nvfp4(ac, ae, ast, wc, we, wst, K), K, False, "subnormal scales")
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_CASES[1:])
@@ -430,8 +506,11 @@ def test_linear_nvfp4_matches_oracle(M, N, K, fmt, y_dtype):
     torch.cuda.synchronize()
     ac, ae, ast = O.quant_nvfp4(x16, hb, mx=mx)
     wc, we, wst = O.quant_nvfp4(w16, hb, mx=mx)
-    ref = round_like(O.gemm_nvfp4(ac, ae, ast, wc, we, wst, K), y_dtype)
+    ref64 = O.gemm_nvfp4(ac, ae, ast, wc, we, wst, K)
+    ref = round_like(ref64, y_dtype)
     assert rel_fro(y_np(y), ref) <= REL_TOL
+    assert_elementwise(y_np(y), ref64, abs_products_nvfp4(ac, ae, ast, wc, we, wst, K), K,
+                       y_dtype == hdq.DTYPE_BF16, "linear nvfp4")
 
 
 @pytest.mark.parametrize("fmt", [hdq.FMT_NVFP4_MX, hdq.FMT_NVFP4_P2])
@@ -460,8 +539,10 @@ def test_linear_bf16_matches_oracle(M, N, K, y_dtype):
     W = hdq.LinearWeights(to_dev(w16), 32, fp4_fmt=None)
     y = hdq.linear(hdq.PREC_BF16, to_dev(x16), W, y_dtype=y_dtype)
     torch.cuda.synchronize()
-    ref = round_like(O.gemm_bf16(x16, w16), y_dtype)
+    ref64 = O.gemm_bf16(x16, w16)
+    ref = round_like(ref64, y_dtype)
     assert rel_fro(y_np(y), ref) <= REL_TOL
+    assert_elementwise(y_np(y), ref64, abs_products_bf16(x16, w16), K, y_dtype == hdq.DTYPE_BF16, "linear bf16")
 
 
 # ---------------------------------------- device-predicated dispatch
@@ -676,6 +757,8 @@ def run_config(cfg, path, n_cols=384):
         ac, ae, ast = O.quant_nvfp4(xs, hb, amax=amax, mx=mx)
         wc, we, wst = O.quant_nvfp4(ws, hb, amax=wamax, mx=mx)
         ref = O.gemm_nvfp4(ac, ae, ast, wc, we, wst, K)
+        S = abs_products_nvfp4(ac, ae, ast, wc, we, wst, K)
+    ref64 = ref
     ref = round_like(ref, y_dtype)
     got = y_np(y)[np.ix_(rows, cols)]
     err = rel_fro(got, ref)
@@ -683,6 +766,9 @@ def run_config(cfg, path, n_cols=384):
     assert err <= REL_TOL
     if path == "int8":
         assert np.array_equal(got, ref)
+    else:
+        worst = assert_elementwise(got, ref64, S, K, y_dtype == hdq.DTYPE_BF16, f"config {cfg} {path}")
+        say(f"config {cfg} {path}: worst error / per-element bound {worst:.3f}")
 
 
 @pytest.mark.parametrize("cfg,path", [(1, "int8"), (1, "nvfp4"), (1, "nvfp4_mx"), (1, "nvfp4_p2"),
@@ -702,8 +788,10 @@ def test_config1_full_oracle():
     torch.cuda.synchronize()
     ac, ae, ast = O.quant_nvfp4(x16, hb)
     wc, we, wst = O.quant_nvfp4(w16, hb)
-    ref = O.gemm_nvfp4(ac, ae, ast, wc, we, wst, 1024).astype(np.float32)
+    ref64 = O.gemm_nvfp4(ac, ae, ast, wc, we, wst, 1024)
+    ref = ref64.astype(np.float32)
     assert rel_fro(y.cpu().numpy(), ref) <= REL_TOL
+    assert_elementwise(y_np(y), ref64, abs_products_nvfp4(ac, ae, ast, wc, we, wst, 1024), 1024, False, "config 1")
 
 
 # ------------------------------ the mixed-precision schedule, full size
@@ -763,6 +851,7 @@ def test_schedule_layer_calls_match_oracle(layer):
                 "outlier channels": hdq.PREC_BF16}[what]
         assert dec == want
         xs = np.ascontiguousarray(x16[rows])
+        S = None
         if dec == hdq.PREC_INT8:
             qa, sa = O.quant_int(xs, hb, 127)
             r, _ = O.gemm_int(qa, sa, qw, sw)
@@ -770,8 +859,11 @@ def test_schedule_layer_calls_match_oracle(layer):
         elif dec == hdq.PREC_NVFP4:
             ac, ae, ast = O.quant_nvfp4(xs, hb, amax=np.float32(ref[4]), mx=True)
             r = O.gemm_nvfp4(ac, ae, ast, wc, we, wst, K)
+            S = abs_products_nvfp4(ac, ae, ast, wc, we, wst, K)
         else:
             r = O.gemm_bf16(xs, ws)
+            S = abs_products_bf16(xs, ws)
+        r64 = r
         r = round_like(r, hdq.DTYPE_BF16)
         got = y_np(y)[np.ix_(rows, cols)]
         err = rel_fro(got, r)
@@ -779,6 +871,8 @@ def test_schedule_layer_calls_match_oracle(layer):
         assert err <= REL_TOL
         if dec == hdq.PREC_INT8:
             assert np.array_equal(got, r)
+        else:
+            assert_elementwise(got, r64, S, K, True, f"schedule {name} {what}")
 
 
 # ------------------------------------------------- temporal delta cache
