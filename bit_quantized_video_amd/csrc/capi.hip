@@ -8,6 +8,14 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
+// Fixed scratch of the allocation-free entry points: one copy per GPU, held
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// never the device memory: kernels and copies get the address that
+// hipGetSymbolAddress returns for the current device (noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[HDQ_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 using namespace hdq;
@@ -54,6 +62,23 @@ size_t amax_prepass_bytes() { return align_up(kStatsPartialBytes) + kAlign; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? HDQ_OK : HDQ_ERR_HIP; }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; null if HIP reports an error.
+void* noalloc_scratch() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    ptr[dev] = p;
+  }
+  return ptr[dev];
+}
+
 // Checks a quantized tensor's descriptor against a [rows, cols] operand.
 int check_qtensor(const hdq_qtensor& q, int32_t fmt, int64_t rows, int64_t cols) {
   if (q.fmt != fmt) return HDQ_ERR_UNSUPPORTED;
@@ -98,6 +123,7 @@ const char* hdq_status_string(int status) {
     case HDQ_ERR_UNSUPPORTED: return "unsupported precision / format / output dtype combination";
     case HDQ_ERR_HIP: return "HIP launch error";
     case HDQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case HDQ_ERR_TOO_LARGE: return "input too large for the allocation-free call's fixed scratch";
     default: return "unknown status";
   }
 }
@@ -181,10 +207,14 @@ int hdq_select_precision_sums(const double* delta_sums_dev, int64_t delta_parts,
                                  delta_sums_dev, nullptr, delta_parts));
 }
 
-int hdq_select_quantize_int8(const double* delta_sums_dev, int64_t delta_parts, const void* cur_in,
-                             int64_t rows, int64_t cols, int32_t had_block, float delta_thresh,
-                             float ratio_thresh, int32_t* decision_dev, float* stats_dev,
-                             hdq_qtensor* xq8, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of hdq_select_quantize_int8 (everything but the workspace).
+int check_select_q8(const double* delta_sums_dev, int64_t delta_parts, const void* cur_in, int64_t rows,
+                    int64_t cols, int32_t had_block, const int32_t* decision_dev, const float* stats_dev,
+                    const hdq_qtensor* xq8) {
   if (cur_in == nullptr || decision_dev == nullptr || stats_dev == nullptr || xq8 == nullptr)
     return HDQ_ERR_INVALID;
   if (delta_sums_dev != nullptr && (delta_parts < 1 || delta_parts > 0x7fffffff)) return HDQ_ERR_SHAPE;
@@ -193,13 +223,18 @@ int hdq_select_quantize_int8(const double* delta_sums_dev, int64_t delta_parts, 
   int st = check_quant_shape(rows, cols, had_block, HDQ_FMT_INT8_ROW);
   if (st != HDQ_OK) return st;
   if (cols % 8 != 0) return HDQ_ERR_SHAPE;
-  if (ws == nullptr || ws_bytes < hdq_workspace_bytes(HDQ_OP_SELECT_Q8, rows, cols, 0, 0))
-    return HDQ_ERR_WORKSPACE;
+  return HDQ_OK;
+}
+
+// Enqueues the fused selection + INT8 quantization (arguments checked; ws
+// holds the per-row partials).
+int enqueue_select_q8(const double* delta_sums_dev, int64_t delta_parts, const void* cur_in, int64_t rows,
+                      int64_t cols, int32_t had_block, float delta_thresh, float ratio_thresh,
+                      int32_t* decision_dev, float* stats_dev, hdq_qtensor* xq8, void* ws, hipStream_t s) {
   xq8->fmt = HDQ_FMT_INT8_ROW;
   xq8->had_block = had_block;
   xq8->rows = rows;
   xq8->cols = cols;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const uint16_t* xb = static_cast<const uint16_t*>(cur_in);
   double* part = static_cast<double*>(ws);
   if (cols <= 16384) {
@@ -220,6 +255,38 @@ int hdq_select_quantize_int8(const double* delta_sums_dev, int64_t delta_parts, 
   if (e != hipSuccess) return HDQ_ERR_HIP;
   return hip_status(launch_quant_int_rows(xb, rows, cols, had_block, HDQ_FMT_INT8_ROW, xq8->codes,
                                           xq8->row_scale, nullptr, 0, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int hdq_select_quantize_int8(const double* delta_sums_dev, int64_t delta_parts, const void* cur_in,
+                             int64_t rows, int64_t cols, int32_t had_block, float delta_thresh,
+                             float ratio_thresh, int32_t* decision_dev, float* stats_dev,
+                             hdq_qtensor* xq8, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_select_q8(delta_sums_dev, delta_parts, cur_in, rows, cols, had_block, decision_dev, stats_dev,
+                           xq8);
+  if (st != HDQ_OK) return st;
+  if (ws == nullptr || ws_bytes < hdq_workspace_bytes(HDQ_OP_SELECT_Q8, rows, cols, 0, 0))
+    return HDQ_ERR_WORKSPACE;
+  return enqueue_select_q8(delta_sums_dev, delta_parts, cur_in, rows, cols, had_block, delta_thresh,
+                           ratio_thresh, decision_dev, stats_dev, xq8, ws, static_cast<hipStream_t>(stream));
+}
+
+int hdq_select_quantize_int8_noalloc(const double* delta_sums_dev, int64_t delta_parts, const void* cur_in,
+                                     int64_t rows, int64_t cols, int32_t had_block, float delta_thresh,
+                                     float ratio_thresh, int32_t* decision_dev, float* stats_dev,
+                                     hdq_qtensor* xq8, void* stream) {
+  int st = check_select_q8(delta_sums_dev, delta_parts, cur_in, rows, cols, had_block, decision_dev, stats_dev,
+                           xq8);
+  if (st != HDQ_OK) return st;
+  if (hdq_workspace_bytes(HDQ_OP_SELECT_Q8, rows, cols, 0, 0) > HDQ_NOALLOC_SCRATCH_BYTES)
+    return HDQ_ERR_TOO_LARGE;
+  void* ws = noalloc_scratch();
+  if (ws == nullptr) return HDQ_ERR_HIP;
+  return enqueue_select_q8(delta_sums_dev, delta_parts, cur_in, rows, cols, had_block, delta_thresh,
+                           ratio_thresh, decision_dev, stats_dev, xq8, ws, static_cast<hipStream_t>(stream));
 }
 
 int hdq_tdc_decide(const double* sums_dev, const int64_t* parts_offsets_dev, const int32_t* state_dev,

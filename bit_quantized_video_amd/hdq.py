@@ -16,7 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libhdq.so")
 
 # status codes
-OK, ERR_INVALID, ERR_SHAPE, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE = 0, -1, -2, -3, -4, -5
+OK, ERR_INVALID, ERR_SHAPE, ERR_UNSUPPORTED, ERR_HIP, ERR_WORKSPACE, ERR_TOO_LARGE = 0, -1, -2, -3, -4, -5, -6
+NOALLOC_SCRATCH_BYTES = 2 << 20      # HDQ_NOALLOC_SCRATCH_BYTES
 # formats
 FMT_INT8_ROW, FMT_INT4_ROW, FMT_NVFP4, FMT_NVFP4_MX, FMT_NVFP4_P2 = 0, 1, 2, 3, 4
 # precisions
@@ -27,7 +28,7 @@ DTYPE_F32, DTYPE_BF16, DTYPE_I32 = 0, 1, 2
 OP_SELECT, OP_QUANTIZE, OP_LINEAR, OP_SELECT_Q8, OP_DQ_QUANTIZE, OP_DQ_LINEAR = 0, 1, 2, 3, 4, 5
 
 EXPORTS = ("hdq_select_precision", "hdq_delta_sums", "hdq_select_precision_sums",
-           "hdq_select_quantize_int8", "hdq_linear_dispatch", "hdq_linear_dispatch_delta",
+           "hdq_select_quantize_int8", "hdq_select_quantize_int8_noalloc", "hdq_linear_dispatch", "hdq_linear_dispatch_delta",
            "hdq_tdc_decide", "hdq_quantize", "hdq_dq_cubes", "hdq_dq_quantize", "hdq_dq_decode_weights",
            "hdq_dq_linear",
            "hdq_linear", "hdq_workspace_bytes",
@@ -87,6 +88,9 @@ def _load():
     L.hdq_select_quantize_int8.argtypes = [_p, _c.c_int64, _p, _c.c_int64, _c.c_int64, _c.c_int32,
                                            _c.c_float, _c.c_float, _p, _p, _c.POINTER(QTensorDesc), _p,
                                            _c.c_size_t, _p]
+    L.hdq_select_quantize_int8_noalloc.restype = _c.c_int
+    L.hdq_select_quantize_int8_noalloc.argtypes = [_p, _c.c_int64, _p, _c.c_int64, _c.c_int64, _c.c_int32,
+                                                   _c.c_float, _c.c_float, _p, _p, _c.POINTER(QTensorDesc), _p]
     L.hdq_linear_dispatch.restype = _c.c_int
     L.hdq_linear_dispatch.argtypes = [_p, _p, _c.POINTER(QTensorDesc), _c.POINTER(QTensorDesc),
                                       _c.c_int64, _c.c_int64, _c.POINTER(WeightsDesc), _p, _c.c_int32, _p]
@@ -342,6 +346,24 @@ def select_quantize_int8(delta_sums, cur_in, had_block, delta_thresh=0.1, ratio_
                                       delta_thresh, ratio_thresh, _ptr(decision), _ptr(stats),
                                       _c.byref(d), _ptr(ws), ws.numel(), _stream(stream))
     _check("hdq_select_quantize_int8", st)
+    out.fmt, out.had_block, out.rows, out.cols = d.fmt, d.had_block, d.rows, d.cols
+    return decision, stats, out
+
+
+def select_quantize_int8_noalloc(delta_sums, cur_in, had_block, decision, stats, out, delta_thresh=0.1,
+                                 ratio_thresh=50.0, stream=None):
+    """hdq_select_quantize_int8_noalloc: select_quantize_int8 with the
+    library's fixed per-GPU scratch instead of a workspace; the caller passes
+    every output (decision int32[1], stats float32[5], an INT8 QuantizedTensor),
+    so the call allocates nothing."""
+    cur_in = _bf16(cur_in, "cur_in")
+    rows, cols = cur_in.shape
+    d = out.desc()
+    dp, parts = _delta_parts(delta_sums)
+    st = lib.hdq_select_quantize_int8_noalloc(dp, parts, _ptr(cur_in), rows, cols, had_block,
+                                              delta_thresh, ratio_thresh, _ptr(decision), _ptr(stats),
+                                              _c.byref(d), _stream(stream))
+    _check("hdq_select_quantize_int8_noalloc", st)
     out.fmt, out.had_block, out.rows, out.cols = d.fmt, d.had_block, d.rows, d.cols
     return decision, stats, out
 

@@ -221,6 +221,34 @@ int hdq_select_quantize_int8(const double *delta_sums_dev, int64_t delta_parts, 
                              hdq_qtensor *xq8, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * hdq_select_quantize_int8_noalloc -- hdq_select_quantize_int8 with no
+ * workspace argument, for callers that cannot allocate device memory: code
+ * recorded under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments and results as hdq_select_quantize_int8
+ * (bit for bit), without ws / ws_bytes.
+ *   Scratch: the per-row statistics partials live in a static device array
+ *   of HDQ_NOALLOC_SCRATCH_BYTES bytes, one per GPU the library runs on,
+ *   held until the process ends.  Its address is looked up once per device
+ *   (hipGetSymbolAddress, with that device current) on the first call there;
+ *   the call allocates nothing.
+ *   Limit: hdq_workspace_bytes(HDQ_OP_SELECT_Q8, rows, cols, 0, 0) (48 bytes
+ *   per row, at least 48 KiB) must not exceed HDQ_NOALLOC_SCRATCH_BYTES, i.e.
+ *   rows <= 43690; larger inputs return HDQ_ERR_TOO_LARGE before anything is
+ *   enqueued.
+ *   Sharing: every call on one GPU uses that GPU's one array and overwrites
+ *   it (nothing in it needs to start at zero).  Calls that overlap on one GPU
+ *   (other streams or threads, with the earlier call's kernels not yet done)
+ *   race on it: order them on one stream or with events.
+ */
+#define HDQ_NOALLOC_SCRATCH_BYTES (2u << 20)
+#define HDQ_ERR_TOO_LARGE (-6)   /* input beyond an allocation-free call's fixed scratch */
+int hdq_select_quantize_int8_noalloc(const double *delta_sums_dev, int64_t delta_parts,
+                                     const void *cur_in, int64_t rows, int64_t cols,
+                                     int32_t had_block, float delta_thresh, float ratio_thresh,
+                                     int32_t *decision_dev, float *stats_dev, hdq_qtensor *xq8,
+                                     void *stream);
+
+/*
  * hdq_quantize -- step 2: block-Hadamard rotation fused with quantization
  * (summary sections one and four).  Also prepares weights offline.
  *

@@ -27,7 +27,7 @@ def hdq():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for fn in ("hdq_select_precision", "hdq_delta_sums", "hdq_select_precision_sums",
-               "hdq_select_quantize_int8", "hdq_quantize", "hdq_tdc_decide",
+               "hdq_select_quantize_int8", "hdq_select_quantize_int8_noalloc", "hdq_quantize", "hdq_tdc_decide",
                "hdq_linear", "hdq_linear_dispatch", "hdq_workspace_bytes",
                "hdq_status_string", "hdq_version", "hdq_dq_cubes", "hdq_dq_quantize",
                "hdq_dq_decode_weights", "hdq_dq_linear"):
@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(hdq):
 
 
 def test_status_strings_and_version(hdq):
-    for st in (0, -1, -2, -3, -4, -5):
+    for st in (0, -1, -2, -3, -4, -5, -6):
         assert hdq.lib.hdq_status_string(st)
     assert hdq.lib.hdq_status_string(99) == b"unknown status"
     assert hdq.lib.hdq_version() >= 10000
@@ -97,6 +97,17 @@ def test_validation_happens_before_any_launch(hdq):
     assert sq(rows=100000, wsb=1 << 20) == hdq.ERR_WORKSPACE      # one partial per row does not fit
     assert sq(ds=fake, parts=0) == hdq.ERR_SHAPE                  # difference sums need >= 1 pair
     assert L.hdq_workspace_bytes(hdq.OP_SELECT_Q8, 17776, 3072, 0, 0) >= 17776 * 48
+    # the allocation-free variant: the same checks, then the fixed scratch's limit (before any HIP call)
+    nq = lambda hb=16, cols=64, rows=4, q=q8, dec=fake: L.hdq_select_quantize_int8_noalloc(
+        None, 0, fake, rows, cols, hb, 0.1, 50.0, dec, fake, ctypes.byref(q) if q is not None else None, None)
+    assert nq(q=None) == hdq.ERR_INVALID
+    assert nq(dec=None) == hdq.ERR_INVALID
+    assert nq(hb=0) == hdq.ERR_SHAPE
+    assert nq(cols=60) == hdq.ERR_SHAPE
+    max_rows = hdq.NOALLOC_SCRATCH_BYTES // 48
+    assert nq(rows=max_rows + 1) == hdq.ERR_TOO_LARGE
+    assert nq(rows=17776 * 4, cols=12288) == hdq.ERR_TOO_LARGE
+    assert L.hdq_workspace_bytes(hdq.OP_SELECT_Q8, max_rows, 64, 0, 0) <= hdq.NOALLOC_SCRATCH_BYTES
     # quantize: bad fmt, bad shapes, missing buffers, missing workspace for the amax pre-pass
     q = hdq.QTensorDesc(0, 0, 0, 0, fake, fake, fake, fake)
     assert L.hdq_quantize(fake, 4, 64, 16, 9, None, None, ctypes.byref(q), None, 0, None) == hdq.ERR_INVALID
