@@ -57,6 +57,15 @@ size_t qtensor_bytes(int64_t M, int64_t K, int32_t fmt) {
   return 0;
 }
 
+// Scratch of hdq_dq_linear: the core GEMM's fp32 [cubes, N]; on the combine
+// route (shapes the fused core-add GEMM does not take) also the difference
+// GEMM's fp32 [tokens, N] after it.
+size_t dq_linear_ws(int64_t tokens, int64_t cubes, int64_t N, int64_t K, int32_t fmt) {
+  size_t b = align_up((size_t)cubes * (size_t)N * 4);
+  if (!fp4_core_add_applies(fmt, tokens, N, K)) b += align_up((size_t)tokens * (size_t)N * 4);
+  return b;
+}
+
 // Scratch of the NVFP4 tensor-amax pre-pass: the stats partials + one float.
 size_t amax_prepass_bytes() { return align_up(kStatsPartialBytes) + kAlign; }
 
@@ -458,6 +467,13 @@ int hdq_dq_decode_weights(const hdq_qtensor* w_fp4, void* w_dec, void* stream) {
                                        w_fp4->cols, static_cast<uint16_t*>(w_dec), static_cast<hipStream_t>(stream)));
 }
 
+size_t hdq_dq_linear_workspace_bytes(const hdq_dq_grid* g, int64_t K, int64_t N, int32_t fmt) {
+  DqGrid d;
+  if (!dq_grid(g, d) || K <= 0 || N <= 0 || !is_fp4(fmt)) return 0;
+  const int64_t M = (int64_t)d.F * d.H * d.W, C = (int64_t)d.nF * d.nH * d.nW;
+  return dq_linear_ws(M, C, N, K, fmt);
+}
+
 int hdq_dq_linear(const hdq_dq_grid* g, const void* core_bf16, const float* core_scale, const hdq_qtensor* delta,
                   const hdq_qtensor* w_fp4, const void* w_dec, void* y, int32_t y_dtype, void* ws, size_t ws_bytes,
                   void* stream) {
@@ -475,11 +491,11 @@ int hdq_dq_linear(const hdq_dq_grid* g, const void* core_bf16, const float* core
   if ((st = check_qtensor(*w_fp4, delta->fmt, N, K)) != HDQ_OK) return st;
   if (delta->had_block != 1 || w_fp4->had_block != 1 || K % 32 != 0 || N % 4 != 0 || N > 0x7fffffff)
     return HDQ_ERR_SHAPE;
-  const size_t yd_bytes = align_up((size_t)M * (size_t)N * 4);
-  if (ws == nullptr || ws_bytes < hdq_workspace_bytes(HDQ_OP_DQ_LINEAR, M, C, N, 0)) return HDQ_ERR_WORKSPACE;
+  if (ws == nullptr || ws_bytes < dq_linear_ws(M, C, N, K, delta->fmt)) return HDQ_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float* yd = static_cast<float*>(ws);
-  float* yc = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + yd_bytes);
+  // the core GEMM's output first; the combine route's difference output after it
+  float* yc = static_cast<float*>(ws);
+  float* yd = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align_up((size_t)C * (size_t)N * 4));
   // the core GEMM, then (MX and P2 formats, K % 256 == 0) the difference GEMM
   // with the broadcast core term added in its epilogue
   if (launch_gemm_bf16(static_cast<const uint16_t*>(core_bf16), static_cast<const uint16_t*>(w_dec), yc,
@@ -491,7 +507,9 @@ int hdq_dq_linear(const hdq_dq_grid* g, const void* core_bf16, const float* core
       static_cast<const uint8_t*>(w_fp4->codes), w_fp4->blk_scale, w_fp4->tensor_scale, delta->fmt, add, y, y_dtype,
       M, N, K, s);
   if (fe == hipSuccess) return HDQ_OK;
-  if (fe != hipErrorNotSupported) return HDQ_ERR_HIP;
+  // the workspace was sized for the fused route when it applies: never fall
+  // back to the combine route (whose fp32 output would not fit) there
+  if (fe != hipErrorNotSupported || fp4_core_add_applies(delta->fmt, M, N, K)) return HDQ_ERR_HIP;
   if (fp4_gemm_for(delta->fmt)(static_cast<const uint8_t*>(delta->codes), delta->blk_scale, delta->tensor_scale,
                                static_cast<const uint8_t*>(w_fp4->codes), w_fp4->blk_scale, w_fp4->tensor_scale,
                                yd, HDQ_DTYPE_F32, M, N, K, nullptr, HDQ_PREC_NVFP4, s) != hipSuccess)

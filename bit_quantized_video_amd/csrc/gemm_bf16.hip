@@ -189,8 +189,7 @@ static hipError_t launch_bf16_pipe(const void* x, const uint8_t* xs, const float
                                    int64_t K, const int32_t* decision, int32_t want, hipStream_t s) {
   constexpr size_t lds = kBf16PipeLds;
   auto kern = k_gemm_bf16_pipe<SRC, OUT>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = set_dynamic_lds_once<k_gemm_bf16_pipe<SRC, OUT>>(lds);
   if (e != hipSuccess) return e;
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
   hipLaunchKernelGGL(kern, dim3((unsigned)persistent_grid(tiles)), dim3(512), lds, s, x, xs, xts, w, ws,

@@ -203,7 +203,7 @@ __device__ __forceinline__ void gemm_bf16_pipe_body(
         if (m0 + r < M) {
           uint16_t* dst16 = y16 + (int64_t)(m0 + r) * N + n;
           if (vec) {
-            *reinterpret_cast<uint4*>(dst16) = *reinterpret_cast<const uint4*>(src);
+            store16_nt(dst16, src);
           } else {
             for (int e = 0; e < 8 && n + e < N; ++e) dst16[e] = reinterpret_cast<const uint16_t*>(src)[e];
           }

@@ -158,8 +158,7 @@ static hipError_t launch_dispatch_t(const int32_t* decision, const int8_t* x8, c
   constexpr size_t lds0 = fp4_lds > kBf16PipeLds ? fp4_lds : kBf16PipeLds;
   constexpr size_t lds = i8_lds > lds0 ? i8_lds : lds0;
   auto kern = k_gemm_dispatch<OUT, FP4>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = set_dynamic_lds_once<k_gemm_dispatch<OUT, FP4>>(lds);
   if (e != hipSuccess) return e;
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
   const int gemm_wgs = (int)persistent_grid(tiles);

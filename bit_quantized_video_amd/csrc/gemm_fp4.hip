@@ -193,8 +193,7 @@ static hipError_t launch_fp4_pipe(const uint8_t* xc, const uint8_t* xs, const fl
                                   int32_t want, hipStream_t s) {
   constexpr size_t lds = (size_t)fp4_pipe_lds<P2>();
   auto kern = k_gemm_fp4mx_pipe<OUT, P2>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = set_dynamic_lds_once<k_gemm_fp4mx_pipe<OUT, P2>>(lds);
   if (e != hipSuccess) return e;
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
   hipLaunchKernelGGL(kern, dim3((unsigned)persistent_grid(tiles)), dim3(512), lds, s, xc, xs, xts, wc, ws,
@@ -217,8 +216,7 @@ static hipError_t launch_core_add_t(const uint8_t* xc, const uint8_t* xs, const 
                                     int64_t N, int64_t K, hipStream_t s) {
   constexpr size_t lds = (size_t)fp4_pipe_lds<P2>();
   auto kern = k_gemm_fp4_core_add<OUT, P2>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = set_dynamic_lds_once<k_gemm_fp4_core_add<OUT, P2>>(lds);
   if (e != hipSuccess) return e;
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
   hipLaunchKernelGGL(kern, dim3((unsigned)persistent_grid(tiles)), dim3(512), lds, s, xc, xs, xts, wc, ws, wts, y,
@@ -229,8 +227,7 @@ static hipError_t launch_core_add_t(const uint8_t* xc, const uint8_t* xs, const 
 hipError_t launch_gemm_fp4_core_add(const uint8_t* xc, const uint8_t* xs, const float* xts, const uint8_t* wc,
                                     const uint8_t* ws, const float* wts, int fmt, const CoreAdd& add, void* y,
                                     int out_dtype, int64_t M, int64_t N, int64_t K, hipStream_t s) {
-  if (K % 256 != 0 || M * K / 2 >= (1ll << 31) || N * K / 2 >= (1ll << 31) || N % 4 != 0)
-    return hipErrorNotSupported;
+  if (!fp4_core_add_applies(fmt, M, N, K)) return hipErrorNotSupported;
   if (fmt == kNvfp4Mx)
     return out_dtype == kOutF32 ? launch_core_add_t<kOutF32, false>(xc, xs, xts, wc, ws, wts, add, y, M, N, K, s)
                                 : launch_core_add_t<kOutBf16, false>(xc, xs, xts, wc, ws, wts, add, y, M, N, K, s);

@@ -34,13 +34,11 @@
 #include "hdq_internal.h"
 
 #include <atomic>
-#include <cstdlib>
 
 namespace hdq {
 
-// Persistent GEMMs leave two CUs per XCD free (HDQ_GEMM_FREE_CUS overrides
-// the total, a multiple of 8): their workgroups each fill a CU's register
-// file, so without free CUs no kernel on another stream (such as the
+// Persistent GEMMs leave two CUs per XCD free: their workgroups each fill a
+// CU's register file, so without free CUs no kernel on another stream (such as the
 // previous-step difference pass) could run beside them.  On MI355X the
 // GEMMs are power-bound, and 240 workgroups run them as fast as 256.
 int64_t persistent_grid(int64_t tiles) {
@@ -52,8 +50,7 @@ int64_t persistent_grid(int64_t tiles) {
     int cu = 0;
     if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu < 8)
       cu = 256;
-    int free_cus = cu >= 128 ? 16 : 0;
-    if (const char* e = std::getenv("HDQ_GEMM_FREE_CUS")) free_cus = std::atoi(e) & ~7;
+    const int free_cus = cu >= 128 ? 16 : 0;
     n = (cu & ~7) - free_cus;
     if (n < 8) n = cu & ~7;
     cus[dev].store(n, std::memory_order_relaxed);
@@ -224,8 +221,7 @@ static hipError_t launch_pipe(const int8_t* x, const float* sx, const uint8_t* w
   using C = I8Cfg<WAVES_M, WAVES_N, WM_T, WN_T>;
   constexpr size_t lds = (size_t)C::LDS;
   auto kern = k_gemm_i8i4_pipe<WAVES_M, WAVES_N, WM_T, WN_T, OUT>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = set_dynamic_lds_once<k_gemm_i8i4_pipe<WAVES_M, WAVES_N, WM_T, WN_T, OUT>>(lds);
   if (e != hipSuccess) return e;
   const int64_t tiles = ((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
   const int64_t grid = persistent_grid(tiles);
@@ -236,21 +232,13 @@ static hipError_t launch_pipe(const int8_t* x, const float* sx, const uint8_t* w
 
 // 8 waves as 2 (tokens) x 4 (features), each 128 x 64: two waves per SIMD,
 // the fastest of the layouts measured on the CogVideoX shapes.
-#ifndef HDQ_I8_WAVES_M
-#define HDQ_I8_WAVES_M 2
-#define HDQ_I8_WAVES_N 4
-#define HDQ_I8_WM_T 4
-#define HDQ_I8_WN_T 2
-#endif
 
 static hipError_t launch_pipe_out(const int8_t* x, const float* sx, const uint8_t* w4, const float* sw,
                                   void* y, int out_dtype, int64_t M, int64_t N, int64_t K,
                                   const int32_t* decision, int32_t want, hipStream_t s) {
-#define HDQ_I8_CFG HDQ_I8_WAVES_M, HDQ_I8_WAVES_N, HDQ_I8_WM_T, HDQ_I8_WN_T
-  if (out_dtype == kOutF32) return launch_pipe<HDQ_I8_CFG, kOutF32>(x, sx, w4, sw, y, M, N, K, decision, want, s);
-  if (out_dtype == kOutBf16) return launch_pipe<HDQ_I8_CFG, kOutBf16>(x, sx, w4, sw, y, M, N, K, decision, want, s);
-  return launch_pipe<HDQ_I8_CFG, kOutI32>(x, sx, w4, sw, y, M, N, K, decision, want, s);
-#undef HDQ_I8_CFG
+  if (out_dtype == kOutF32) return launch_pipe<2, 4, 4, 2, kOutF32>(x, sx, w4, sw, y, M, N, K, decision, want, s);
+  if (out_dtype == kOutBf16) return launch_pipe<2, 4, 4, 2, kOutBf16>(x, sx, w4, sw, y, M, N, K, decision, want, s);
+  return launch_pipe<2, 4, 4, 2, kOutI32>(x, sx, w4, sw, y, M, N, K, decision, want, s);
 }
 
 hipError_t launch_gemm_i8i4(const int8_t* x, const float* sx, const uint8_t* w4, const float* sw,

@@ -6,10 +6,28 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace hdq {
+
+// Raises a kernel's dynamic LDS limit to `bytes` once per device (the
+// attribute is set on the first launch on each device, not on every launch).
+template <auto KERNEL>
+hipError_t set_dynamic_lds_once(size_t bytes) {
+  static std::atomic<uint64_t> done{0};  // one bit per device index below 64
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (1ull << dev) : 0ull;
+  if (bit != 0 && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(KERNEL),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
+
 
 // Difference sums run by extra workgroups of a GEMM launch (gemm_dispatch.hip).
 // A slice is the chunk range [c0, c1) of one pair of previous-step tensors;
@@ -152,6 +170,13 @@ hipError_t launch_dq_quantize(const uint16_t* x, int64_t K, const DqGrid& g, int
 // NVFP4 weights [N, K] to bf16 E2M1 x block-scale values.
 hipError_t launch_dq_decode_w(const uint8_t* codes, const uint8_t* blk, int64_t N, int64_t K, uint16_t* out,
                               hipStream_t s);
+// Whether launch_gemm_fp4_core_add takes a shape: the pipelined FP4 body
+// (MX or per-16 power-of-two format, K % 256 == 0, 32-bit operand offsets)
+// with N % 4 == 0.
+inline bool fp4_core_add_applies(int fmt, int64_t M, int64_t N, int64_t K) {
+  return (fmt == kNvfp4Mx || fmt == kNvfp4P2) && K % 256 == 0 && M * K / 2 < (1ll << 31) &&
+         N * K / 2 < (1ll << 31) && N % 4 == 0;
+}
 // NVFP4-MX / P2 GEMM (pipelined shapes: K % 256 == 0) whose output also
 // gets the broadcast core term; hipErrorNotSupported for other shapes.
 hipError_t launch_gemm_fp4_core_add(const uint8_t* xc, const uint8_t* xs, const float* xts, const uint8_t* wc,

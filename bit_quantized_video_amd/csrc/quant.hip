@@ -597,8 +597,12 @@ hipError_t launch_dq_quantize(const uint16_t* x, int64_t K, const DqGrid& g, int
   const int64_t ncubes = (int64_t)g.nF * g.nH * g.nW;
   const size_t lds = (size_t)K * sizeof(float);
   auto kdelta = fmt == kNvfp4Mx ? k_dq_delta<kNvfp4Mx> : fmt == kNvfp4P2 ? k_dq_delta<kNvfp4P2> : k_dq_delta<kNvfp4>;
-  for (const void* k : {reinterpret_cast<const void*>(k_dq_core), reinterpret_cast<const void*>(kdelta)}) {
-    hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  {
+    hipError_t e = set_dynamic_lds_once<k_dq_core>(lds);
+    if (e == hipSuccess)
+      e = fmt == kNvfp4Mx   ? set_dynamic_lds_once<k_dq_delta<kNvfp4Mx>>(lds)
+          : fmt == kNvfp4P2 ? set_dynamic_lds_once<k_dq_delta<kNvfp4P2>>(lds)
+                            : set_dynamic_lds_once<k_dq_delta<kNvfp4>>(lds);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(k_dq_zero, dim3(1), dim3(1), 0, s, damax_bits);

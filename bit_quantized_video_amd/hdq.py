@@ -30,7 +30,7 @@ OP_SELECT, OP_QUANTIZE, OP_LINEAR, OP_SELECT_Q8, OP_DQ_QUANTIZE, OP_DQ_LINEAR = 
 EXPORTS = ("hdq_select_precision", "hdq_delta_sums", "hdq_select_precision_sums",
            "hdq_select_quantize_int8", "hdq_select_quantize_int8_noalloc", "hdq_linear_dispatch", "hdq_linear_dispatch_delta",
            "hdq_tdc_decide", "hdq_quantize", "hdq_dq_cubes", "hdq_dq_quantize", "hdq_dq_decode_weights",
-           "hdq_dq_linear",
+           "hdq_dq_linear", "hdq_dq_linear_workspace_bytes",
            "hdq_linear", "hdq_workspace_bytes",
            "hdq_status_string", "hdq_version")
 
@@ -117,6 +117,8 @@ def _load():
     L.hdq_dq_linear.restype = _c.c_int
     L.hdq_dq_linear.argtypes = [_c.POINTER(DqGridDesc), _p, _p, _c.POINTER(QTensorDesc),
                                 _c.POINTER(QTensorDesc), _p, _p, _c.c_int32, _p, _c.c_size_t, _p]
+    L.hdq_dq_linear_workspace_bytes.restype = _c.c_size_t
+    L.hdq_dq_linear_workspace_bytes.argtypes = [_c.POINTER(DqGridDesc), _c.c_int64, _c.c_int64, _c.c_int32]
     L.hdq_workspace_bytes.restype = _c.c_size_t
     L.hdq_workspace_bytes.argtypes = [_c.c_int32, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int32]
     L.hdq_status_string.restype = _c.c_char_p
@@ -433,13 +435,18 @@ def dq_decode_weights(w_fp4, stream=None):
     return out
 
 
+def dq_linear_workspace_bytes(grid, K, N, fmt):
+    """hdq_dq_linear_workspace_bytes: the scratch hdq_dq_linear needs on its route."""
+    return lib.hdq_dq_linear_workspace_bytes(_c.byref(_dq_grid(grid)), K, N, fmt)
+
+
 def dq_linear(a, w_fp4, w_dec, y=None, y_dtype=DTYPE_BF16, ws=None, stream=None):
     """hdq_dq_linear: y = differences x W^T + cube cores x W^T."""
     M, N = a.delta.rows, w_fp4.rows
     if y is None:
         dt = {DTYPE_F32: torch.float32, DTYPE_BF16: torch.bfloat16}[y_dtype]
         y = torch.empty(M, N, dtype=dt, device=a.core.device)
-    ws = _workspace(ws, workspace_bytes(OP_DQ_LINEAR, M, dq_cubes(a.grid), N), a.core.device)
+    ws = _workspace(ws, dq_linear_workspace_bytes(a.grid, a.delta.cols, N, a.delta.fmt), a.core.device)
     dd, wd = a.delta.desc(), w_fp4.desc()
     st = lib.hdq_dq_linear(_c.byref(_dq_grid(a.grid)), _ptr(a.core_bf16), _ptr(a.core_scale), _c.byref(dd),
                            _c.byref(wd), _ptr(w_dec), _ptr(y), y_dtype, _ptr(ws), ws.numel(), _stream(stream))

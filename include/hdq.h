@@ -453,6 +453,13 @@ int hdq_dq_quantize(const void *x, int64_t K, const hdq_dq_grid *g, int32_t fmt,
  * the core GEMM's weight operand, made once per layer. */
 int hdq_dq_decode_weights(const hdq_qtensor *w_fp4, void *w_dec, void *stream);
 
+/* Scratch bytes hdq_dq_linear needs for this grid, reduction size K, N
+ * outputs and difference format fmt: the core GEMM's fp32 [cubes, N], plus an
+ * fp32 [tokens, N] only when the difference GEMM cannot add the core term in
+ * its own epilogue (plain NVFP4, K not a multiple of 256, N not a multiple of
+ * 4 or operands past 32-bit offsets).  0 on bad arguments. */
+size_t hdq_dq_linear_workspace_bytes(const hdq_dq_grid *g, int64_t K, int64_t N, int32_t fmt);
+
 /*
  * hdq_dq_linear -- y = (differences) x W^T + (the token's cube core) x W^T.
  *   delta       : from hdq_dq_quantize; w_fp4: the layer's NVFP4 weights in
@@ -461,11 +468,14 @@ int hdq_dq_decode_weights(const hdq_qtensor *w_fp4, void *w_dec, void *stream);
  *                 hdq_dq_decode_weights.
  *   core_bf16, core_scale: from hdq_dq_quantize.
  *   y, y_dtype  : device [tokens, N], HDQ_DTYPE_F32 or _BF16.
- *   ws, ws_bytes: >= hdq_workspace_bytes(HDQ_OP_DQ_LINEAR, tokens, cubes, N, 0).
- * The difference GEMM is the NVFP4 GEMM of the format (fp32 into ws); the
- * core GEMM multiplies the E4M3 values by the decoded weights on the bf16
- * MFMA with float32 accumulation (exact products); then
- * y = fl(yd + fl32(fl32(yc * s_core) * s_w)).
+ *   ws, ws_bytes: >= hdq_dq_linear_workspace_bytes(g, K, N, delta->fmt)
+ *                 (hdq_workspace_bytes(HDQ_OP_DQ_LINEAR, tokens, cubes, N, 0)
+ *                 is an upper bound for every route).
+ * The core GEMM multiplies the E4M3 values by the decoded weights on the bf16
+ * MFMA with float32 accumulation (exact products) into ws; the difference
+ * GEMM is the NVFP4 GEMM of the format, which adds the core term in its
+ * epilogue (MX and per-16 power-of-two formats) or writes fp32 into ws for a
+ * combine pass; either way y = fl(yd + fl32(fl32(yc * s_core) * s_w)).
  */
 int hdq_dq_linear(const hdq_dq_grid *g, const void *core_bf16, const float *core_scale, const hdq_qtensor *delta,
                   const hdq_qtensor *w_fp4, const void *w_dec, void *y, int32_t y_dtype, void *ws, size_t ws_bytes,

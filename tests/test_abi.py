@@ -223,6 +223,33 @@ def test_deltaquant_validation(hdq):
     assert lin(w=hdq.QTensorDesc(hdq.FMT_NVFP4_MX, 2, N, K, fake, None, fake, fake)) == hdq.ERR_SHAPE
     assert lin(d=hdq.QTensorDesc(hdq.FMT_NVFP4_MX, 1, M + 1, K, fake, None, fake, fake)) == hdq.ERR_SHAPE
     assert lin(wsb=need - 1) == hdq.ERR_WORKSPACE
+    # the route's exact scratch: the fused core-add route (MX or P2, K % 256 == 0) needs only the
+    # core GEMM's fp32 [cubes, N]; the combine route also the difference GEMM's fp32 [tokens, N]
+    big = hdq.DqGridDesc(13, 30, 45, 2, 2, 2)
+    toks, cubes = 13 * 30 * 45, L.hdq_dq_cubes(ctypes.byref(big))
+    fused = L.hdq_dq_linear_workspace_bytes(ctypes.byref(big), 3072, 12288, hdq.FMT_NVFP4_MX)
+    assert fused == L.hdq_dq_linear_workspace_bytes(ctypes.byref(big), 3072, 12288, hdq.FMT_NVFP4_P2)
+    assert cubes * 12288 * 4 <= fused < cubes * 12288 * 4 + 256
+    combine = L.hdq_dq_linear_workspace_bytes(ctypes.byref(big), 3072, 12288, hdq.FMT_NVFP4)
+    assert combine >= fused + toks * 12288 * 4
+    assert L.hdq_dq_linear_workspace_bytes(ctypes.byref(big), 3072 + 32, 12288, hdq.FMT_NVFP4_MX) >= combine
+    assert L.hdq_dq_linear_workspace_bytes(ctypes.byref(big), 3072, 12288, hdq.FMT_INT8_ROW) == 0
+    assert L.hdq_workspace_bytes(hdq.OP_DQ_LINEAR, toks, cubes, 12288, 0) >= combine
+    # K 256 (MX): the fused route; its exact need is accepted by the checks, one byte less is not
+    K2 = 256
+    d2 = hdq.QTensorDesc(hdq.FMT_NVFP4_MX, 1, M, K2, fake, None, fake, fake)
+    w2 = hdq.QTensorDesc(hdq.FMT_NVFP4_MX, 1, N, K2, fake, None, fake, fake)
+    need2 = L.hdq_dq_linear_workspace_bytes(ctypes.byref(g), K2, N, hdq.FMT_NVFP4_MX)
+    assert need2 < need
+    assert lin(d=d2, w=w2, wsb=need2 - 1) == hdq.ERR_WORKSPACE
+    # more rejections before any launch: cubes over 256 tokens, K over 32768, a bad grid
+    big_cube = hdq.DqGridDesc(13, 30, 45, 8, 8, 8)
+    assert L.hdq_dq_quantize(fake, K, ctypes.byref(big_cube), hdq.FMT_NVFP4_MX, fake, fake, None,
+                             ctypes.byref(delta), fake, 256, None) == hdq.ERR_SHAPE
+    assert L.hdq_dq_linear(ctypes.byref(big_cube), fake, fake, ctypes.byref(delta), ctypes.byref(w), fake, fake, 1,
+                           fake, need, None) == hdq.ERR_SHAPE
+    assert q(K=32768 + 32) == hdq.ERR_SHAPE
+    assert L.hdq_dq_linear_workspace_bytes(ctypes.byref(big_cube), K, N, hdq.FMT_NVFP4_MX) == 0
     assert L.hdq_dq_decode_weights(None, fake, None) == hdq.ERR_INVALID
 
 
