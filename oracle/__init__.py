@@ -57,6 +57,7 @@ def lib():
             "orc_decide": (_int, [_int, _f64, _f64, _f64, _f64]),
             "orc_tdc_decide": (None, [_p, _p, _p, _p, _p, _i64, _f32, _f32]),
             "orc_num_threads": (_int, []),
+            "orc_set_num_threads": (None, [_int]),
             "orc_dq_cube_of": (None, [_i64, _i64, _i64, _int, _int, _int, _p]),
             "orc_e4m3s_decode": (_f32, [ctypes.c_uint8]),
             "orc_dq_core": (None, [_p, _i64, _i64, _i64, _i64, _int, _int, _int, _p, _p]),
@@ -81,6 +82,11 @@ def _ptr(a):
 
 def num_threads():
     return lib().orc_num_threads()
+
+
+def set_num_threads(n):
+    """Threads of the GEMM loops from now on (results do not depend on it)."""
+    lib().orc_set_num_threads(int(n))
 
 
 # ---------------------------------------------------------------- bf16

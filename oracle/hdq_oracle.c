@@ -684,3 +684,16 @@ int orc_num_threads(void)
     return 1;
 #endif
 }
+
+/* Sets the threads of the GEMM loops (timing of the CPU baseline with one
+ * thread and with every core); no effect without OpenMP.  Changes no
+ * result: every GEMM output element is one thread's sequential sum. */
+void orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
