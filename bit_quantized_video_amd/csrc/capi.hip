@@ -474,12 +474,10 @@ size_t hdq_dq_linear_workspace_bytes(const hdq_dq_grid* g, int64_t K, int64_t N,
   return dq_linear_ws(M, C, N, K, fmt);
 }
 
-int hdq_dq_linear(const hdq_dq_grid* g, const void* core_bf16, const float* core_scale, const hdq_qtensor* delta,
-                  const hdq_qtensor* w_fp4, const void* w_dec, void* y, int32_t y_dtype, void* ws, size_t ws_bytes,
-                  void* stream) {
-  if (core_bf16 == nullptr || core_scale == nullptr || delta == nullptr || w_fp4 == nullptr || w_dec == nullptr ||
-      y == nullptr)
-    return HDQ_ERR_INVALID;
+int hdq_dq_linear(const hdq_dq_grid* g, const uint8_t* core_codes, const void* core_bf16, const float* core_scale,
+                  const hdq_qtensor* delta, const hdq_qtensor* w_fp4, const void* w_dec, void* y, int32_t y_dtype,
+                  void* ws, size_t ws_bytes, void* stream) {
+  if (core_scale == nullptr || delta == nullptr || w_fp4 == nullptr || y == nullptr) return HDQ_ERR_INVALID;
   if (y_dtype != HDQ_DTYPE_F32 && y_dtype != HDQ_DTYPE_BF16) return HDQ_ERR_UNSUPPORTED;
   DqGrid d;
   if (!dq_grid(g, d)) return HDQ_ERR_SHAPE;
@@ -491,6 +489,10 @@ int hdq_dq_linear(const hdq_dq_grid* g, const void* core_bf16, const float* core
   if ((st = check_qtensor(*w_fp4, delta->fmt, N, K)) != HDQ_OK) return st;
   if (delta->had_block != 1 || w_fp4->had_block != 1 || K % 32 != 0 || N % 4 != 0 || N > 0x7fffffff)
     return HDQ_ERR_SHAPE;
+  // the core GEMM: FP8 codes x FP4 weights when the weights' block scales are
+  // powers of two, else the bf16 code values x the decoded weights
+  const bool fp8_core = dq_core_fp8_applies(delta->fmt, C, N, K);
+  if (fp8_core ? core_codes == nullptr : (core_bf16 == nullptr || w_dec == nullptr)) return HDQ_ERR_INVALID;
   if (ws == nullptr || ws_bytes < dq_linear_ws(M, C, N, K, delta->fmt)) return HDQ_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // the core GEMM's output first; the combine route's difference output after it
@@ -498,9 +500,12 @@ int hdq_dq_linear(const hdq_dq_grid* g, const void* core_bf16, const float* core
   float* yd = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align_up((size_t)C * (size_t)N * 4));
   // the core GEMM, then (MX and P2 formats, K % 256 == 0) the difference GEMM
   // with the broadcast core term added in its epilogue
-  if (launch_gemm_bf16(static_cast<const uint16_t*>(core_bf16), static_cast<const uint16_t*>(w_dec), yc,
-                       HDQ_DTYPE_F32, C, N, K, nullptr, HDQ_PREC_BF16, s) != hipSuccess)
-    return HDQ_ERR_HIP;
+  const hipError_t ce =
+      fp8_core ? launch_gemm_dq_core(core_codes, static_cast<const uint8_t*>(w_fp4->codes), w_fp4->blk_scale,
+                                     delta->fmt, yc, C, N, K, s)
+               : launch_gemm_bf16(static_cast<const uint16_t*>(core_bf16), static_cast<const uint16_t*>(w_dec), yc,
+                                  HDQ_DTYPE_F32, C, N, K, nullptr, HDQ_PREC_BF16, s);
+  if (ce != hipSuccess) return HDQ_ERR_HIP;
   const CoreAdd add{yc, core_scale, w_fp4->tensor_scale, d};
   const hipError_t fe = launch_gemm_fp4_core_add(
       static_cast<const uint8_t*>(delta->codes), delta->blk_scale, delta->tensor_scale,

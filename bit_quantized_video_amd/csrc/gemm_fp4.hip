@@ -237,6 +237,244 @@ hipError_t launch_gemm_fp4_core_add(const uint8_t* xc, const uint8_t* xs, const 
   return hipErrorNotSupported;
 }
 
+// ---- DeltaQuant's core GEMM on the FP8 x FP4 scaled MFMA ------------------
+// DeltaQuant (paper-radar CVPR 2026 listing, abstract) keeps each cube's core
+// token in FP8 and multiplies it by the layer's 4-bit weights:
+//   yc[c, n] = sum_k e4m3(core[c, k]) * e2m1(w[n, k]) * 2^e(n, k)
+// with e the weights' power-of-two block scale (one per 32 k for the MX
+// format; one per 16 k for the per-16 format, which runs every MFMA twice
+// with the core operand's other 16-block zeroed).  The core codes are the
+// instruction's FP8 E4M3 operand as stored (unit scale), the weight codes its
+// FP4 operand with their E8M0 scales; every product is exact and only the
+// float32 accumulation rounds.  Operand layout of this mixed form (measured
+// on gfx950): per 64-K step an FP4 lane of half h holds k [32 h, 32 h + 32)
+// and takes one scale for them; an FP8 lane of half h holds k [16 h, 16 h + 16)
+// and [32 + 16 h, 48 + 16 h), and the scales follow the 32-k blocks.  The per-cube and tensor scales are applied
+// where yc is used (the difference GEMM's epilogue).
+//  * 256 x 256 tiles, 8 waves as 2 (cubes) x 4 (features) of 128 x 64, a
+//    persistent tile loop; K advances 128 per stage, register-staged into
+//    two LDS buffers (core rows 128 bytes, weight rows 64 bytes, both
+//    XOR-swizzled 16-byte chunks; per weight row the stage's E8M0 bytes as
+//    words that lane half h reads once per stage, byte ks selected per
+//    64-K substep ks); fp32 output stored from registers.
+template <bool P2>
+__global__ __launch_bounds__(512) void k_gemm_dq_core(const uint8_t* __restrict__ core, const uint8_t* __restrict__ wc,
+                                                     const uint8_t* __restrict__ wsc, float* __restrict__ Y, int C,
+                                                     int N, int K) {
+  constexpr int BM = 256, BN = 256, BK = 128, WM_T = 4, WN_T = 2;
+  constexpr int AB = BM * BK, WB = BN * BK / 2;  // core and weight code bytes per stage
+  constexpr int SCB = P2 ? 16 : 8;               // E8M0 bytes per weight row and stage
+  constexpr int SB = AB + WB + BN * SCB;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % 2, wn = wave / 2;
+  const int tiles_m = (C + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const TileSeq seq = tile_seq(tiles_m * tiles_n);
+  const int nk = K / BK;
+  const int G = seq.count * nk;
+  if (G == 0) return;
+  const int ldw = K / 2, lds_ = K / 16;
+  // core rows: 8 threads x 16 bytes, 64 rows per round; weight rows: 4
+  // threads x 16 bytes, 128 rows per round; weight scales: one row per
+  // thread of the first 256 (its 8 E4M3 bytes of the stage)
+  const int ar = tid >> 3, ac = tid & 7, wr = tid >> 2, wcc = tid & 3;
+  const uint32_t avoff = (uint32_t)(ar * K + 16 * ac), wvoff = (uint32_t)(wr * ldw + 16 * wcc);
+  const int adst = ar * 128 + 16 * (ac ^ swz128(ar)), wdst = wr * 64 + 16 * (wcc ^ swz64(wr));
+  const bool srow_t = tid < 256;
+  const uint32_t svoff = (uint32_t)((tid & 255) * lds_);
+
+  int l_logical = seq.first, l_kt = 0;
+  __amdgpu_buffer_rsrc_t ares, wres, sres;
+  auto open_tile = [&]() {
+    int tm, tn;
+    grouped_tile(l_logical, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    ares = make_rsrc(core + (int64_t)m0 * K, (uint32_t)((int64_t)(C - m0) * K));
+    wres = make_rsrc(wc + (int64_t)n0 * ldw, (uint32_t)((int64_t)(N - n0) * ldw));
+    sres = make_rsrc(wsc + (int64_t)n0 * lds_, (uint32_t)((int64_t)(N - n0) * lds_));
+  };
+  open_tile();
+  struct Stage {
+    uint4 a[4], w[2];
+    uint2 sc;
+  };
+  auto load = [&](Stage& st) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) st.a[p] = buf_load16(ares, avoff, l_kt * BK + p * 64 * K);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) st.w[p] = buf_load16(wres, wvoff, l_kt * (BK / 2) + p * 128 * ldw);
+    st.sc = srow_t ? __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(sres, (int)svoff, l_kt * (BK / 16), 0))
+                   : make_uint2(0u, 0u);
+    if (++l_kt == nk) {
+      l_kt = 0;
+      l_logical += seq.stride;
+      if (l_logical < tiles_m * tiles_n) open_tile();
+    }
+  };
+  auto store = [&](const Stage& st, int buf) {
+    uint8_t* base = smem + buf * SB;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) *reinterpret_cast<uint4*>(base + adst + p * 64 * 128) = st.a[p];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) *reinterpret_cast<uint4*>(base + AB + wdst + p * 128 * 64) = st.w[p];
+    if (srow_t) {
+      // E4M3 byte b of the stage scales k [16 b, 16 b + 16); group q (32 k)
+      // is bytes 2q, 2q + 1.  Word h holds groups h and h + 2 (MX: their
+      // first byte); P2 adds words 2 + h with their second bytes.
+      const uint32_t e[8] = {e4m3_pow2_to_e8m0(st.sc.x & 0xffu), e4m3_pow2_to_e8m0((st.sc.x >> 8) & 0xffu),
+                             e4m3_pow2_to_e8m0((st.sc.x >> 16) & 0xffu), e4m3_pow2_to_e8m0(st.sc.x >> 24),
+                             e4m3_pow2_to_e8m0(st.sc.y & 0xffu), e4m3_pow2_to_e8m0((st.sc.y >> 8) & 0xffu),
+                             e4m3_pow2_to_e8m0((st.sc.y >> 16) & 0xffu), e4m3_pow2_to_e8m0(st.sc.y >> 24)};
+      uint8_t* sp = base + AB + WB + (tid & 255) * SCB;
+      const uint32_t w0 = e[0] | (e[4] << 8), w1 = e[2] | (e[6] << 8);
+      if constexpr (P2)
+        *reinterpret_cast<uint4*>(sp) = make_uint4(w0, w1, e[1] | (e[5] << 8), e[3] | (e[7] << 8));
+      else
+        *reinterpret_cast<uint2*>(sp) = make_uint2(w0, w1);
+    }
+  };
+
+  v16f acc[WN_T][WM_T];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int j = 0; j < WN_T; ++j)
+#pragma unroll
+      for (int i = 0; i < WM_T; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[j][i][e] = 0.0f;
+  };
+  zero_acc();
+  const int h = lane >> 5, r32 = lane & 31;
+  constexpr int kUnitScale = 0x7f7f7f7f;  // E8M0 2^0 in every byte
+  auto compute = [&](int buf) {
+    const uint8_t* la = smem + buf * SB;
+    const uint8_t* lw = la + AB;
+    const uint8_t* ls = lw + WB;
+    int we[WN_T], wo[WN_T];
+#pragma unroll
+    for (int j = 0; j < WN_T; ++j) {
+      const uint8_t* p = ls + (wn * WN_T * 32 + j * 32 + r32) * SCB + 4 * h;
+      we[j] = *reinterpret_cast<const int*>(p);
+      if constexpr (P2) wo[j] = *reinterpret_cast<const int*>(p + 8);
+    }
+    auto substep = [&](auto ksc) {
+      constexpr int ks = decltype(ksc)::value;
+      v8i wf[WN_T];
+#pragma unroll
+      for (int j = 0; j < WN_T; ++j) {
+        const int r = wn * WN_T * 32 + j * 32 + r32;
+        const v4i v = *reinterpret_cast<const v4i*>(lw + r * 64 + 16 * ((2 * ks + h) ^ swz64(r)));
+        wf[j] = v8i{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int i = 0; i < WM_T; ++i) {
+        // the FP8 operand's 32 bytes per lane: k 64 ks + 16 h + [0, 16), then
+        // k 64 ks + 32 + 16 h + [0, 16)
+        const int r = wm * WM_T * 32 + i * 32 + r32;
+        const v4i lo = *reinterpret_cast<const v4i*>(la + r * 128 + 16 * ((4 * ks + h) ^ swz128(r)));
+        const v4i hi = *reinterpret_cast<const v4i*>(la + r * 128 + 16 * ((4 * ks + 2 + h) ^ swz128(r)));
+        const v8i af = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        if constexpr (P2) {
+          // lane half 0 holds the first 16-blocks of both 32-groups, half 1
+          // the second ones: pass 1 keeps half 0, pass 2 half 1
+          const int keep = h == 0 ? -1 : 0;
+          const v8i a0 = af & keep, a1 = af & ~keep;
+#pragma unroll
+          for (int j = 0; j < WN_T; ++j) {
+            acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[j], a0, acc[j][i], 4, 0, ks, we[j], 0,
+                                                                         kUnitScale);
+            acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[j], a1, acc[j][i], 4, 0, ks, wo[j], 0,
+                                                                         kUnitScale);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < WN_T; ++j)
+            acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[j], af, acc[j][i], 4, 0, ks, we[j], 0,
+                                                                         kUnitScale);
+        }
+      }
+    };
+    substep(std::integral_constant<int, 0>{});
+    substep(std::integral_constant<int, 1>{});
+  };
+  // lane: core row wm * 128 + 32 i + r32 of the tile, features
+  // wn * 64 + 32 j + 8 g + 4 h + 0..3
+  auto epilogue = [&](int logical) {
+    int tm, tn;
+    grouped_tile(logical, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const bool full_n = n0 + BN <= N && (N & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < WM_T; ++i) {
+      const int m = m0 + wm * WM_T * 32 + i * 32 + r32;
+      if (m >= C) continue;
+#pragma unroll
+      for (int j = 0; j < WN_T; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * WN_T * 32 + j * 32 + 8 * g + 4 * h;
+          float* dst = Y + (int64_t)m * N + n;
+          const v16f& a = acc[j][i];
+          if (full_n) {
+            *reinterpret_cast<float4*>(dst) = make_float4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
+          } else {
+            for (int r = 0; r < 4 && n + r < N; ++r) dst[r] = a[4 * g + r];
+          }
+        }
+    }
+  };
+  int ckt = 0, clogical = seq.first;
+  auto finish_stage = [&]() {
+    if (++ckt == nk) {
+      epilogue(clogical);
+      zero_acc();
+      ckt = 0;
+      clogical += seq.stride;
+    }
+  };
+  Stage ra;
+  load(ra);
+  store(ra, 0);
+  lds_barrier();
+  int g = 0;
+  for (; g + 1 < G; g += 2) {
+    load(ra);
+    compute(0);
+    finish_stage();
+    store(ra, 1);
+    lds_barrier();
+    if (g + 2 < G) load(ra);
+    compute(1);
+    finish_stage();
+    if (g + 2 < G) store(ra, 0);
+    lds_barrier();
+  }
+  if (g < G) {
+    compute(0);
+    finish_stage();
+  }
+}
+
+template <bool P2>
+static hipError_t launch_dq_core_t(const uint8_t* core, const uint8_t* wc, const uint8_t* ws, float* yc, int64_t C,
+                                   int64_t N, int64_t K, hipStream_t s) {
+  constexpr size_t lds = 2 * (size_t)(256 * 128 + 256 * 64 + 256 * (P2 ? 16 : 8));
+  hipError_t e = set_dynamic_lds_once<k_gemm_dq_core<P2>>(lds);
+  if (e != hipSuccess) return e;
+  const int64_t tiles = ((C + 255) / 256) * ((N + 255) / 256);
+  hipLaunchKernelGGL(k_gemm_dq_core<P2>, dim3((unsigned)persistent_grid(tiles)), dim3(512), lds, s, core, wc, ws, yc,
+                     (int)C, (int)N, (int)K);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_dq_core(const uint8_t* core, const uint8_t* wc, const uint8_t* ws, int fmt, float* yc,
+                               int64_t C, int64_t N, int64_t K, hipStream_t s) {
+  if (!dq_core_fp8_applies(fmt, C, N, K)) return hipErrorNotSupported;
+  return fmt == kNvfp4P2 ? launch_dq_core_t<true>(core, wc, ws, yc, C, N, K, s)
+                         : launch_dq_core_t<false>(core, wc, ws, yc, C, N, K, s);
+}
+
 hipError_t launch_gemm_nvfp4_mx(const uint8_t* xc, const uint8_t* xs, const float* xts,
                                 const uint8_t* wc, const uint8_t* ws, const float* wts,
                                 void* y, int out_dtype, int64_t M, int64_t N, int64_t K,

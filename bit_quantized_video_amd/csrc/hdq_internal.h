@@ -177,6 +177,17 @@ inline bool fp4_core_add_applies(int fmt, int64_t M, int64_t N, int64_t K) {
   return (fmt == kNvfp4Mx || fmt == kNvfp4P2) && K % 256 == 0 && M * K / 2 < (1ll << 31) &&
          N * K / 2 < (1ll << 31) && N % 4 == 0;
 }
+// Whether launch_gemm_dq_core takes a shape: weights with power-of-two
+// block scales (MX or per-16 format), K % 128 == 0, 32-bit operand offsets.
+inline bool dq_core_fp8_applies(int fmt, int64_t C, int64_t N, int64_t K) {
+  return (fmt == kNvfp4Mx || fmt == kNvfp4P2) && K % 128 == 0 && C * K < (1ll << 31) && N * K / 2 < (1ll << 31);
+}
+// DeltaQuant's core GEMM: yc [C, N] fp32 = E4M3 core codes [C, K] times the
+// NVFP4 weights' E2M1 codes with their power-of-two block scales (tensor
+// scale left out), on the FP8 x FP4 scaled MFMA; hipErrorNotSupported for
+// shapes dq_core_fp8_applies rejects.
+hipError_t launch_gemm_dq_core(const uint8_t* core, const uint8_t* wc, const uint8_t* ws, int fmt, float* yc,
+                               int64_t C, int64_t N, int64_t K, hipStream_t s);
 // NVFP4-MX / P2 GEMM (pipelined shapes: K % 256 == 0) whose output also
 // gets the broadcast core term; hipErrorNotSupported for other shapes.
 hipError_t launch_gemm_fp4_core_add(const uint8_t* xc, const uint8_t* xs, const float* xts, const uint8_t* wc,

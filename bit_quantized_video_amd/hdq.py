@@ -115,7 +115,7 @@ def _load():
     L.hdq_dq_decode_weights.restype = _c.c_int
     L.hdq_dq_decode_weights.argtypes = [_c.POINTER(QTensorDesc), _p, _p]
     L.hdq_dq_linear.restype = _c.c_int
-    L.hdq_dq_linear.argtypes = [_c.POINTER(DqGridDesc), _p, _p, _c.POINTER(QTensorDesc),
+    L.hdq_dq_linear.argtypes = [_c.POINTER(DqGridDesc), _p, _p, _p, _c.POINTER(QTensorDesc),
                                 _c.POINTER(QTensorDesc), _p, _p, _c.c_int32, _p, _c.c_size_t, _p]
     L.hdq_dq_linear_workspace_bytes.restype = _c.c_size_t
     L.hdq_dq_linear_workspace_bytes.argtypes = [_c.POINTER(DqGridDesc), _c.c_int64, _c.c_int64, _c.c_int32]
@@ -401,24 +401,34 @@ def _dq_grid(grid):
     return DqGridDesc(F, H, W, cf, ch, cw)
 
 
+def dq_core_needs_bf16(fmt, cubes, K):
+    """Whether hdq_dq_linear's core GEMM runs on the bf16 core values and
+    decoded weights: unless the weights' block scales are powers of two (MX
+    or per-16 format), K % 128 == 0 and the core codes fit 32-bit offsets."""
+    return not (fmt in (FMT_NVFP4_MX, FMT_NVFP4_P2) and K % 128 == 0 and cubes * K < 2 ** 31)
+
+
 class DqActivations:
     """hdq_dq_quantize's outputs: core codes [cubes, K], core scales [cubes],
-    core code values as bf16 [cubes, K], and the differences' NVFP4 tensor."""
+    the differences' NVFP4 tensor and, when asked for (by default when the
+    core GEMM needs them, see dq_core_needs_bf16), the core code values as
+    bf16 [cubes, K]."""
 
-    def __init__(self, grid, K, fmt, device):
+    def __init__(self, grid, K, fmt, device, core_bf16=None):
         self.grid, self.K = grid, K
         n, M = dq_cubes(grid), grid[0] * grid[1] * grid[2]
         self.core = torch.empty(n, K, dtype=torch.uint8, device=device)
         self.core_scale = torch.empty(n, dtype=torch.float32, device=device)
-        self.core_bf16 = torch.empty(n, K, dtype=torch.bfloat16, device=device)
+        want = dq_core_needs_bf16(fmt, n, K) if core_bf16 is None else core_bf16
+        self.core_bf16 = torch.empty(n, K, dtype=torch.bfloat16, device=device) if want else None
         self.delta = QuantizedTensor(fmt, M, K, 1, device)
 
 
-def dq_quantize(x, grid, fmt, out=None, ws=None, stream=None):
+def dq_quantize(x, grid, fmt, out=None, ws=None, stream=None, core_bf16=None):
     """hdq_dq_quantize: cube cores in FP8 and the differences in NVFP4."""
     x = _bf16(x, "x")
     M, K = x.shape
-    out = DqActivations(grid, K, fmt, x.device) if out is None else out
+    out = DqActivations(grid, K, fmt, x.device, core_bf16) if out is None else out
     ws = _workspace(ws, workspace_bytes(OP_DQ_QUANTIZE, M, K), x.device)
     d = out.delta.desc()
     st = lib.hdq_dq_quantize(_ptr(x), K, _c.byref(_dq_grid(grid)), fmt, _ptr(out.core), _ptr(out.core_scale),
@@ -440,15 +450,16 @@ def dq_linear_workspace_bytes(grid, K, N, fmt):
     return lib.hdq_dq_linear_workspace_bytes(_c.byref(_dq_grid(grid)), K, N, fmt)
 
 
-def dq_linear(a, w_fp4, w_dec, y=None, y_dtype=DTYPE_BF16, ws=None, stream=None):
-    """hdq_dq_linear: y = differences x W^T + cube cores x W^T."""
+def dq_linear(a, w_fp4, w_dec=None, y=None, y_dtype=DTYPE_BF16, ws=None, stream=None):
+    """hdq_dq_linear: y = differences x W^T + cube cores x W^T (w_dec and
+    the activations' bf16 core values are needed for plain NVFP4 only)."""
     M, N = a.delta.rows, w_fp4.rows
     if y is None:
         dt = {DTYPE_F32: torch.float32, DTYPE_BF16: torch.bfloat16}[y_dtype]
         y = torch.empty(M, N, dtype=dt, device=a.core.device)
     ws = _workspace(ws, dq_linear_workspace_bytes(a.grid, a.delta.cols, N, a.delta.fmt), a.core.device)
     dd, wd = a.delta.desc(), w_fp4.desc()
-    st = lib.hdq_dq_linear(_c.byref(_dq_grid(a.grid)), _ptr(a.core_bf16), _ptr(a.core_scale), _c.byref(dd),
+    st = lib.hdq_dq_linear(_c.byref(_dq_grid(a.grid)), _ptr(a.core), _ptr(a.core_bf16), _ptr(a.core_scale), _c.byref(dd),
                            _c.byref(wd), _ptr(w_dec), _ptr(y), y_dtype, _ptr(ws), ws.numel(), _stream(stream))
     _check("hdq_dq_linear", st)
     return y

@@ -464,22 +464,29 @@ size_t hdq_dq_linear_workspace_bytes(const hdq_dq_grid *g, int64_t K, int64_t N,
  * hdq_dq_linear -- y = (differences) x W^T + (the token's cube core) x W^T.
  *   delta       : from hdq_dq_quantize; w_fp4: the layer's NVFP4 weights in
  *                 the same format with had_block 1 (hdq_quantize with
- *                 had_block 1 rotates nothing), N a multiple of 4; w_dec: from
- *                 hdq_dq_decode_weights.
- *   core_bf16, core_scale: from hdq_dq_quantize.
+ *                 had_block 1 rotates nothing), N a multiple of 4.
+ *   core_codes, core_scale: from hdq_dq_quantize.
+ *   core_bf16, w_dec: the bf16 core values (hdq_dq_quantize) and decoded
+ *                 weights (hdq_dq_decode_weights); needed only when the
+ *                 weights' block scales are not powers of two or K is not a
+ *                 multiple of 128 (plain NVFP4), may be NULL otherwise.
  *   y, y_dtype  : device [tokens, N], HDQ_DTYPE_F32 or _BF16.
  *   ws, ws_bytes: >= hdq_dq_linear_workspace_bytes(g, K, N, delta->fmt)
  *                 (hdq_workspace_bytes(HDQ_OP_DQ_LINEAR, tokens, cubes, N, 0)
  *                 is an upper bound for every route).
- * The core GEMM multiplies the E4M3 values by the decoded weights on the bf16
- * MFMA with float32 accumulation (exact products) into ws; the difference
- * GEMM is the NVFP4 GEMM of the format, which adds the core term in its
- * epilogue (MX and per-16 power-of-two formats) or writes fp32 into ws for a
- * combine pass; either way y = fl(yd + fl32(fl32(yc * s_core) * s_w)).
+ * The core GEMM yc = sum_k core * w (exact products, float32 accumulation)
+ * runs on the FP8 x FP4 scaled matrix instructions straight from the core's
+ * E4M3 codes and the weights' E2M1 codes with their power-of-two block
+ * scales (MX and per-16 power-of-two formats, K % 128 == 0), else on the
+ * bf16 ones from core_bf16 and w_dec; the difference GEMM is the NVFP4 GEMM
+ * of the format, which adds the core term in its epilogue (MX and per-16
+ * formats, K % 256 == 0) or writes fp32 into ws for a combine pass; either
+ * way y = fl(yd + fl32(fl32(yc * s_core) * s_w)).  Errors: HDQ_ERR_INVALID
+ * for a NULL pointer the route needs.
  */
-int hdq_dq_linear(const hdq_dq_grid *g, const void *core_bf16, const float *core_scale, const hdq_qtensor *delta,
-                  const hdq_qtensor *w_fp4, const void *w_dec, void *y, int32_t y_dtype, void *ws, size_t ws_bytes,
-                  void *stream);
+int hdq_dq_linear(const hdq_dq_grid *g, const uint8_t *core_codes, const void *core_bf16, const float *core_scale,
+                  const hdq_qtensor *delta, const hdq_qtensor *w_fp4, const void *w_dec, void *y, int32_t y_dtype,
+                  void *ws, size_t ws_bytes, void *stream);
 
 /* Scratch bytes an entry point needs.  op = HDQ_OP_SELECT: (M = rows,
  * K = cols, N = prev_numel); HDQ_OP_SELECT_Q8: (M = rows, K = cols);

@@ -215,8 +215,8 @@ def test_deltaquant_validation(hdq):
     need = L.hdq_workspace_bytes(hdq.OP_DQ_LINEAR, M, C, N, 0)
     assert need >= (M * N + C * N) * 4
     w = hdq.QTensorDesc(hdq.FMT_NVFP4_MX, 1, N, K, fake, None, fake, fake)
-    lin = lambda d=delta, w=w, dt=1, ws=fake, wsb=need: L.hdq_dq_linear(
-        ctypes.byref(g), fake, fake, ctypes.byref(d), ctypes.byref(w), fake, fake, dt, ws, wsb, None)
+    lin = lambda d=delta, w=w, dt=1, ws=fake, wsb=need, cc=fake, cb=fake, wd=fake: L.hdq_dq_linear(
+        ctypes.byref(g), cc, cb, fake, ctypes.byref(d), ctypes.byref(w), wd, fake, dt, ws, wsb, None)
     assert lin(dt=2) == hdq.ERR_UNSUPPORTED
     assert lin(w=hdq.QTensorDesc(hdq.FMT_NVFP4, 1, N, K, fake, None, fake, fake)) == hdq.ERR_UNSUPPORTED
     assert lin(w=hdq.QTensorDesc(hdq.FMT_NVFP4_MX, 1, 42, K, fake, None, fake, fake)) == hdq.ERR_SHAPE
@@ -242,11 +242,18 @@ def test_deltaquant_validation(hdq):
     need2 = L.hdq_dq_linear_workspace_bytes(ctypes.byref(g), K2, N, hdq.FMT_NVFP4_MX)
     assert need2 < need
     assert lin(d=d2, w=w2, wsb=need2 - 1) == hdq.ERR_WORKSPACE
+    # which buffers each core-GEMM route needs: K 256 with MX runs on the FP8 codes (the bf16 values
+    # and decoded weights may be NULL, the codes may not); K 64, or plain NVFP4, on the bf16 values
+    assert lin(d=d2, w=w2, wsb=need2 - 1, cb=None, wd=None) == hdq.ERR_WORKSPACE   # accepted, then stopped
+    assert lin(d=d2, w=w2, cc=None) == hdq.ERR_INVALID
+    assert lin(cb=None) == hdq.ERR_INVALID
+    assert lin(wd=None) == hdq.ERR_INVALID
+    assert lin(cc=None, wsb=need - 1) == hdq.ERR_WORKSPACE                          # codes unused at K 64
     # more rejections before any launch: cubes over 256 tokens, K over 32768, a bad grid
     big_cube = hdq.DqGridDesc(13, 30, 45, 8, 8, 8)
     assert L.hdq_dq_quantize(fake, K, ctypes.byref(big_cube), hdq.FMT_NVFP4_MX, fake, fake, None,
                              ctypes.byref(delta), fake, 256, None) == hdq.ERR_SHAPE
-    assert L.hdq_dq_linear(ctypes.byref(big_cube), fake, fake, ctypes.byref(delta), ctypes.byref(w), fake, fake, 1,
+    assert L.hdq_dq_linear(ctypes.byref(big_cube), fake, fake, fake, ctypes.byref(delta), ctypes.byref(w), fake, fake, 1,
                            fake, need, None) == hdq.ERR_SHAPE
     assert q(K=32768 + 32) == hdq.ERR_SHAPE
     assert L.hdq_dq_linear_workspace_bytes(ctypes.byref(big_cube), K, N, hdq.FMT_NVFP4_MX) == 0

@@ -37,7 +37,7 @@ def u8(t):
 
 
 def check_quantize(x16, F, H, W, cube, fmt):
-    a = hdq.dq_quantize(to_dev(x16), (F, H, W, cube), fmt)
+    a = hdq.dq_quantize(to_dev(x16), (F, H, W, cube), fmt, core_bf16=True)
     q = O.dq_quantize(x16, F, H, W, cube, MX[fmt])
     torch.cuda.synchronize()
     assert np.array_equal(u8(a.core), q["core"])
@@ -91,6 +91,23 @@ def test_dq_decode_weights_exact(fmt):
     assert np.array_equal(dec.float().cpu().numpy(), O.dequant_nvfp4(c, e, 1.0, K))
 
 
+def core_fp8_mfma_bound(core, wabs, fmt):
+    """Error bound of the core GEMM on the FP8 x FP4 scaled MFMA, [cubes, N].
+    That instruction does not sum its 64 products at float32 precision: on
+    gfx950 the error of one instruction measured at most 2^-10.1 of its
+    largest |product| (random and one-signed codes over the whole E4M3 range,
+    65536 outputs per pattern), consistent with products aligned to the
+    largest one's exponent and kept to at least 14 fraction bits, which bounds
+    64 products by 2^-8 max|p|.  Per 64-k step: 2^-8 max_k |core_k w_k|, twice
+    for the per-16 format's two passes."""
+    C, K = core.shape
+    out = np.zeros((C, wabs.shape[0]))
+    for k0 in range(0, K, 64):
+        pm = np.max(core[:, None, k0:k0 + 64] * wabs[None, :, k0:k0 + 64], axis=2)
+        out += pm
+    return (2.0 if fmt == hdq.FMT_NVFP4_P2 else 1.0) * 2.0 ** -8 * out
+
+
 def linear_case(F, H, W, K, N, cube, fmt, rows=None, y_dtype=hdq.DTYPE_BF16, seed=0):
     """The GPU linear against the oracle's double result computed from the
     oracle's own codes (rows: the tokens compared; all when None).  Returns the
@@ -120,9 +137,12 @@ def linear_case(F, H, W, K, N, cube, fmt, rows=None, y_dtype=hdq.DTYPE_BF16, see
     wabs = np.abs(O.dequant_nvfp4(wc, we, wst, K).astype(np.float64))
     dabs = np.abs(O.dequant_nvfp4(q["codes"][rows], q["blk"][rows], q["s_t"], K).astype(np.float64))
     core = np.abs(O.e4m3s_decode(q["core"]).astype(np.float64) * q["core_scale"].astype(np.float64)[:, None])
-    S = dabs @ wabs.T + (core @ wabs.T)[O.dq_cube_of(F, H, W, cube)[rows]]
+    cube_of = O.dq_cube_of(F, H, W, cube)[rows]
+    S = dabs @ wabs.T + (core @ wabs.T)[cube_of]
     c = max(4.0, 2.0 * np.sqrt(K / 16.0))
     tol = c * 2.0 ** -24 * S + 4 * 2.0 ** -24 * np.abs(ref64) + 1e-35
+    if not hdq.dq_core_needs_bf16(fmt, core.shape[0], K):
+        tol = tol + core_fp8_mfma_bound(core, wabs, fmt)[cube_of]
     if y_dtype == hdq.DTYPE_BF16:
         tol = tol + 2.0 ** -8 * 1.01 * np.abs(got)
     bad = np.abs(got - ref64) > tol
@@ -131,6 +151,8 @@ def linear_case(F, H, W, K, N, cube, fmt, rows=None, y_dtype=hdq.DTYPE_BF16, see
 
 
 @pytest.mark.parametrize("grid,cube,K,N,fmt", [((3, 5, 7), (2, 2, 2), 64, 40, "nvfp4"),
+                                               # K 96: the bf16 core GEMM and the combine route for MX
+                                               ((3, 5, 7), (2, 2, 2), 96, 40, "mx"),
                                                ((4, 6, 10), (2, 2, 2), 256, 300, "mx"),
                                                ((3, 8, 8), (1, 2, 2), 512, 96, "p2"),
                                                # four 256-token tiles of the fused epilogue
@@ -140,7 +162,12 @@ def linear_case(F, H, W, K, N, cube, fmt, rows=None, y_dtype=hdq.DTYPE_BF16, see
 def test_dq_linear_matches_oracle(grid, cube, K, N, fmt, y_dtype):
     say(f"dq linear grid={grid} cube={cube} K={K} N={N} {fmt} y={y_dtype}")
     err = linear_case(*grid, K, N, cube, FMTS[fmt], y_dtype=y_dtype)
-    assert err <= (1e-3 if y_dtype == hdq.DTYPE_BF16 else 1e-5), err
+    say(f"  relative Frobenius error {err:.3g}")
+    # float32 output: 1e-5 where the core GEMM accumulates at float32
+    # precision (bf16 route); the FP8 x FP4 MFMA's narrower sum (bounded per
+    # element above) measures about 1.5e-5 on these inputs, so 1e-4 there
+    fp8 = not hdq.dq_core_needs_bf16(FMTS[fmt], hdq.dq_cubes((*grid, cube)), K)
+    assert err <= (1e-3 if y_dtype == hdq.DTYPE_BF16 else 1e-4 if fp8 else 1e-5), err
 
 
 def test_dq_linear_full_size_sampled_rows():
