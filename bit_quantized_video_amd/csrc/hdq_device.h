@@ -170,6 +170,17 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
   return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
 }
 
+// Four signed E4M3 bytes of w (byte i -> out[i]) as float32: the hardware
+// conversion (OCP E4M3 on gfx950), exact.
+__device__ __forceinline__ void e4m3x4_to_f32(uint32_t w, float* out) {
+  const float2 lo = __builtin_bit_cast(float2, __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false));
+  const float2 hi = __builtin_bit_cast(float2, __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true));
+  out[0] = lo.x;
+  out[1] = lo.y;
+  out[2] = hi.x;
+  out[3] = hi.y;
+}
+
 // Smallest power of two >= t, clamped to [2^-9, 2^8] (t >= 0).
 __device__ __forceinline__ float pow2_ceil_clamped(float t) {
   if (!(t > 0x1p-9f)) return 0x1p-9f;

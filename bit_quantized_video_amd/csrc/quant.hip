@@ -442,11 +442,191 @@ __device__ __forceinline__ int dq_rows(const DqGrid& g, int cube, int* rows) {
   return nt;
 }
 
-// One workgroup per cube: the mean in LDS (eight tokens' loads in flight,
-// added in token order), its scale and codes, the decoded code values as bf16
-// (exact: E4M3 has 4 significant bits) for the core GEMM, and the largest
-// |difference| of the cube's tokens into the running maximum (float bits of a
-// non-negative value order as unsigned integers).
+// A core mean or a difference that is not finite (a NaN or infinite token
+// element, or a sum that overflows) sets the running maximum to a NaN, whose
+// bits exceed those of every other value, and the difference pass turns that
+// into a NaN tensor scale: the caller's flag that the codes are meaningless.
+constexpr uint32_t kDqNonFinite = 0x7fc00000u;
+__device__ __forceinline__ bool dq_finite(float v) { return fabsf(v) <= 3.40282347e38f; }
+
+// The rows of cube `cube`'s first 8 tokens in token order (thread t < 8
+// computes row t; nt is the cube's token count).
+__device__ __forceinline__ int dq_rows8(const DqGrid& g, int cube, int t, int* nt_out) {
+  const int a = cube / (g.nH * g.nW), b = (cube / g.nW) % g.nH, c = cube % g.nW;
+  const int f0 = a * g.cf, h0 = b * g.ch, w0 = c * g.cw;
+  const int nf = min(g.F, f0 + g.cf) - f0, nh = min(g.H, h0 + g.ch) - h0, nw = min(g.W, w0 + g.cw) - w0;
+  *nt_out = nf * nh * nw;
+  const int f = t / (nh * nw), r = t - f * nh * nw, h = r / nw, w = r - h * nw;
+  return ((f0 + f) * g.H + h0 + h) * g.W + w0 + w;
+}
+
+// One workgroup per cube of at most 8 tokens, blockDim.x (a multiple of 64,
+// at most MAXT) times ITER chunk columns covering K / 8: every thread keeps
+// its columns of all the cube's tokens in registers (eight 16-byte loads per
+// column in flight), so the mean (added in token order), the codes and
+// scale, the bf16 code values for the bf16 core GEMM and the largest
+// |difference| from the stored core all come from one read of the tokens.
+// PIPE (ITER 1): persistent over cubes blockIdx.x, + gridDim.x, ..., the
+// next cube's tokens loaded into a second register set as soon as its rows
+// are known (after the current cube's first barrier), so the loads overlap
+// the current cube's arithmetic and reductions.
+template <int ITER, int MAXT, bool PIPE>
+__global__ __launch_bounds__(MAXT) void k_dq_core_reg(const uint16_t* __restrict__ x, int K, const DqGrid g,
+                                                     int ncubes, uint8_t* __restrict__ codes,
+                                                     float* __restrict__ scale, uint16_t* __restrict__ core_bf16,
+                                                     uint32_t* __restrict__ damax_bits) {
+  static_assert(!PIPE || ITER == 1, "the pipelined form holds one column per thread");
+  __shared__ float red[16];
+  __shared__ float redd[16];
+  __shared__ int rows[8];
+  __shared__ int nts;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
+  const int kq = K >> 3;
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  const int step = PIPE ? (int)gridDim.x : ncubes;
+  // a cube's rows into rows[] and its token count into nts
+  auto cube_rows = [&](int cb) {
+    if (tid < 8 && cb < ncubes) {
+      int ntc;
+      const int r = dq_rows8(g, cb, tid, &ntc);
+      if (tid < ntc) rows[tid] = r;
+      if (tid == 0) nts = ntc;
+    }
+  };
+  uint4 wn[ITER][8];
+  int ntn = 0;  // the token count of the cube in wn (read with its rows)
+  auto load = [&]() {
+    const int ntc = nts;
+    ntn = ntc;
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const int q = tid + it * (int)blockDim.x;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        wn[it][u] = q < kq && u < ntc ? xv[(int64_t)rows[u] * kq + q] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  int cube = blockIdx.x;
+  cube_rows(cube);
+  __syncthreads();
+  load();
+  if (PIPE) __syncthreads();  // rows and nts read by every wave before the next cube's are written
+  do {
+    const int nt = ntn;
+    uint4 w[ITER][8];
+#pragma unroll
+    for (int it = 0; it < ITER; ++it)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) w[it][u] = wn[it][u];
+    // the next cube's rows (the current cube's were last read by its loads,
+    // before the previous cube's last barrier); its loads follow the first
+    // barrier below
+    if (PIPE) cube_rows(cube + step);
+    const float n = (float)nt;
+    float c[ITER][8];  // the mean, then the stored core
+    float amax = 0.0f;
+    bool bad = false;
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      float sum[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (u < nt) {
+          float v[8];
+          bf16x8_to_f32(w[it][u], v);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) sum[i] = sum[i] + v[i];
+        }
+      }
+      // sum / n: a product with the exact reciprocal when n is a power of
+      // two (the same correctly rounded quotient), else the division
+      if ((nt & (nt - 1)) == 0) {
+        const float rn = 1.0f / n;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[it][i] = sum[i] * rn;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[it][i] = sum[i] / n;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        amax = fmaxf(amax, fabsf(c[it][i]));
+        bad |= !dq_finite(c[it][i]);
+      }
+    }
+    // the tokens stay packed until the difference step converts them again
+    // (otherwise the compiler keeps all their float values live)
+#pragma unroll
+    for (int it = 0; it < ITER; ++it)
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        asm volatile("" : "+v"(w[it][u].x), "+v"(w[it][u].y), "+v"(w[it][u].z), "+v"(w[it][u].w));
+    amax = wave_max(amax);
+    if (lane == 0) red[wave] = amax;
+    __syncthreads();  // also publishes the next cube's rows
+    if (PIPE && cube + step < ncubes) load();
+    amax = 0.0f;
+    for (int i = 0; i < nwaves; ++i) amax = fmaxf(amax, red[i]);
+    const float sc = amax >= kTiny ? amax / 448.0f : 0.0f;
+    if (tid == 0) scale[cube] = sc;
+    float dmax = 0.0f;
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const int q = tid + it * (int)blockDim.x;
+      uint32_t cw2[2] = {0u, 0u}, bw[4];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float m = c[it][i];
+        const uint32_t mag = sc == 0.0f ? 0u : e4m3_encode(fabsf(m) / sc);
+        const bool neg = mag != 0u && m < 0.0f;
+        cw2[i >> 2] |= (mag | (neg ? 0x80u : 0u)) << (8 * (i & 3));
+      }
+      // the signed code values (the hardware conversion, exact), the stored
+      // core and the values' bf16 bits (exact: 4 significant bits)
+      float e[8];
+      e4m3x4_to_f32(cw2[0], &e[0]);
+      e4m3x4_to_f32(cw2[1], &e[4]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        c[it][i] = e[i] * sc;
+        const uint32_t eb = __float_as_uint(e[i]) >> 16;
+        if (i & 1) bw[i >> 1] |= eb << 16; else bw[i >> 1] = eb;
+      }
+      if (q < kq) {
+        reinterpret_cast<uint2*>(codes)[(int64_t)cube * kq + q] = make_uint2(cw2[0], cw2[1]);
+        if (core_bf16 != nullptr)
+          reinterpret_cast<uint4*>(core_bf16)[(int64_t)cube * kq + q] = make_uint4(bw[0], bw[1], bw[2], bw[3]);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (u < nt) {
+            float v[8];
+            bf16x8_to_f32(w[it][u], v);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) dmax = fmaxf(dmax, fabsf(v[i] - c[it][i]));
+          }
+        }
+      }
+    }
+    // a NaN difference needs a non-finite token element or stored core, and
+    // so a non-finite mean (flagged above); an overflowing one is infinite and
+    // reaches the maximum
+    bad |= !dq_finite(dmax);
+    dmax = wave_max(dmax);
+    if (lane == 0) redd[wave] = dmax;
+    bad = __syncthreads_or(bad);  // also: every wave has read red and (for its loads) rows
+    if (tid == 0) {
+      float m = 0.0f;
+      for (int i = 0; i < nwaves; ++i) m = fmaxf(m, redd[i]);
+      atomicMax(damax_bits, bad ? kDqNonFinite : __float_as_uint(m));
+    }
+    __syncthreads();  // redd, rows and nts read before the next cube rewrites them
+    cube += step;
+  } while (PIPE && cube < ncubes);
+}
+
+// The same for any cube (up to kDqMaxCube tokens) and K: the mean in LDS
+// (eight tokens' loads in flight, added in token order), then a second read
+// of the tokens for the largest |difference|.
 __global__ __launch_bounds__(256) void k_dq_core(const uint16_t* __restrict__ x, int K, const DqGrid g,
                                                  uint8_t* __restrict__ codes, float* __restrict__ scale,
                                                  uint16_t* __restrict__ core_bf16,
@@ -460,6 +640,7 @@ __global__ __launch_bounds__(256) void k_dq_core(const uint16_t* __restrict__ x,
   const int kq = K >> 3;
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   float amax = 0.0f;
+  bool bad = false;
   for (int q = tid; q < kq; q += 256) {
     float sum[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
     for (int t0 = 0; t0 < nt; t0 += 8) {
@@ -482,6 +663,7 @@ __global__ __launch_bounds__(256) void k_dq_core(const uint16_t* __restrict__ x,
       const float m = sum[i] / n;
       lcore[8 * q + i] = m;
       amax = fmaxf(amax, fabsf(m));
+      bad |= !dq_finite(m);
     }
   }
   amax = wave_max(amax);
@@ -521,95 +703,137 @@ __global__ __launch_bounds__(256) void k_dq_core(const uint16_t* __restrict__ x,
           float v[8];
           bf16x8_to_f32(w[u], v);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) dmax = fmaxf(dmax, fabsf(v[i] - lcore[8 * q + i]));
+          for (int i = 0; i < 8; ++i) {
+            const float d = fabsf(v[i] - lcore[8 * q + i]);
+            dmax = fmaxf(dmax, d);
+            bad |= !dq_finite(d);
+          }
         }
       }
     }
   }
   dmax = wave_max(dmax);
-  __syncthreads();
+  bad = __syncthreads_or(bad);
   if (lane == 0) red[wave] = dmax;
   __syncthreads();
-  if (tid == 0) atomicMax(damax_bits, __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
+  if (tid == 0)
+    atomicMax(damax_bits, bad ? kDqNonFinite : __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
 }
 
 __global__ void k_dq_zero(uint32_t* p) { *p = 0u; }
 
-// One workgroup per cube: each token's difference from the stored core,
-// quantized to NVFP4 with the tensor scale of the largest |difference|.  A
-// wave covers 64 consecutive chunks of one token row, so a 16-element block
-// sits on lanes l, l ^ 1 and a 32-element group on l ^ {0..3}; every lane
+// Each token's difference from the stored core, quantized to NVFP4 with the
+// tensor scale of the largest |difference| (a NaN when that is not finite).
+// A streaming pass, one wave per token row at a time (rows wave, + all
+// waves, ...): lane l takes chunk columns l, l + 64, ... (8 loads of the
+// token and 8 of the cube's E4M3 codes in flight), the stored core decoded
+// per element as code value x scale.  A 16-element block sits on lanes
+// l, l ^ 1 and a 32-element group on l ^ {0..3} (K % 32 == 0); every lane
 // runs the block code (zeros past the row), only the stores are predicated.
 template <int FMT>
-__global__ __launch_bounds__(256) void k_dq_delta(const uint16_t* __restrict__ x, int K, const DqGrid g,
+__global__ __launch_bounds__(256) void k_dq_delta(const uint16_t* __restrict__ x, int K, const DqGrid g, int M,
                                                   const uint8_t* __restrict__ ccodes,
                                                   const float* __restrict__ cscale,
                                                   const uint32_t* __restrict__ damax_bits,
                                                   uint8_t* __restrict__ codes, uint8_t* __restrict__ blk_scale,
                                                   float* __restrict__ tensor_scale) {
-  extern __shared__ float lcore[];  // the stored core, K floats
-  __shared__ int rows[kDqMaxCube];
-  const int tid = threadIdx.x, kq = K >> 3, cube = blockIdx.x;
+  constexpr int U = 8;
+  const int tid = threadIdx.x, lane = tid & 63, kq = K >> 3;
   const float A = __uint_as_float(*damax_bits);
-  const float s_t = (A >= kTiny) ? A / (FMT == kNvfp4 ? 2688.0f : 1536.0f) : 0.0f;
-  if (cube == 0 && tid == 0) *tensor_scale = s_t;
-  const float six_st = 6.0f * s_t, sc = cscale[cube];
-  for (int k = tid; k < K; k += 256) {
-    const uint32_t b = ccodes[(int64_t)cube * K + k];
-    const float e = e4m3_decode(b & 0x7fu);
-    lcore[k] = ((b & 0x80u) ? -e : e) * sc;
-  }
-  const int nt = dq_rows(g, cube, rows);  // its barrier also publishes lcore
+  const float s_t = (A >= kTiny) ? A / (FMT == kNvfp4 ? 2688.0f : 1536.0f) : (A == A ? 0.0f : A);
+  if (blockIdx.x == 0 && tid == 0) *tensor_scale = s_t;
+  const float six_st = 6.0f * s_t;
   const uint4* xv = reinterpret_cast<const uint4*>(x);
+  const uint2* cc = reinterpret_cast<const uint2*>(ccodes);
   uint32_t* cv = reinterpret_cast<uint32_t*>(codes);
-  for (int q0 = 0; q0 < kq; q0 += 256) {
-    const int q = q0 + tid;
-    const bool ok = q < kq;
-    for (int t0 = 0; t0 < nt; t0 += 4) {
-      uint4 w[4];
+  const int nwaves = (int)gridDim.x * 4;
+  for (int row = __builtin_amdgcn_readfirstlane((int)blockIdx.x * 4 + (tid >> 6)); row < M; row += nwaves) {
+    const int cube = dq_cube(row, g);
+    const float sc = cscale[cube];
+    const int64_t xb = (int64_t)row * kq, cb = (int64_t)cube * kq;
+    for (int q0 = 0; q0 < kq; q0 += 64 * U) {
+      uint4 w[U];
+      uint2 e8[U];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        w[u] = ok && t0 + u < nt ? xv[(int64_t)rows[t0 + u] * kq + q] : make_uint4(0u, 0u, 0u, 0u);
+      for (int j = 0; j < U; ++j) {
+        const int q = q0 + 64 * j + lane;
+        const bool ok = q < kq;
+        w[j] = ok ? xv[xb + q] : make_uint4(0u, 0u, 0u, 0u);
+        e8[j] = ok ? cc[cb + q] : make_uint2(0u, 0u);
+      }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (t0 + u >= nt) break;  // uniform
+      for (int j = 0; j < U; ++j) {
+        if (q0 + 64 * j >= kq) break;  // uniform
+        const int q = q0 + 64 * j + lane;
         float v[8];
-        bf16x8_to_f32(w[u], v);
-        if (ok) {
+        bf16x8_to_f32(w[j], v);
+        // the stored core: signed E4M3 value (the hardware conversion, exact)
+        // times the cube's scale
+        float e[8];
+        e4m3x4_to_f32(e8[j].x, &e[0]);
+        e4m3x4_to_f32(e8[j].y, &e[4]);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) v[i] = v[i] - lcore[8 * q + i];
-        }
-        uint32_t e;
-        const uint32_t packed = nvfp4_chunk<FMT>(v, s_t, six_st, &e);
-        if (ok) {
-          const int64_t idx = (int64_t)rows[t0 + u] * kq + q;
-          cv[idx] = packed;
-          if ((q & 1) == 0) blk_scale[idx >> 1] = (uint8_t)e;
+        for (int i = 0; i < 8; ++i) v[i] = v[i] - e[i] * sc;
+        uint32_t eb;
+        const uint32_t packed = nvfp4_chunk<FMT>(v, s_t, six_st, &eb);
+        if (q < kq) {
+          cv[xb + q] = packed;
+          if ((q & 1) == 0) blk_scale[(xb + q) >> 1] = (uint8_t)eb;
         }
       }
     }
   }
 }
 
+// Workgroups of `kern` (threads each, lds dynamic bytes) resident per CU
+// times the CUs: the grid of a persistent pass (at least 1).
+template <auto KERNEL>
+static int64_t resident_grid(int threads, size_t lds) {
+  int dev = 0, cus = 0, per = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, KERNEL, threads, lds) != hipSuccess || per < 1) per = 1;
+  return (int64_t)cus * per;
+}
+
 hipError_t launch_dq_quantize(const uint16_t* x, int64_t K, const DqGrid& g, int fmt, uint8_t* ccodes,
                               float* cscale, uint16_t* core_bf16, uint32_t* damax_bits, uint8_t* codes,
                               uint8_t* blk_scale, float* tensor_scale, hipStream_t s) {
-  const int64_t ncubes = (int64_t)g.nF * g.nH * g.nW;
+  const int64_t ncubes = (int64_t)g.nF * g.nH * g.nW, M = (int64_t)g.F * g.H * g.W;
   const size_t lds = (size_t)K * sizeof(float);
-  auto kdelta = fmt == kNvfp4Mx ? k_dq_delta<kNvfp4Mx> : fmt == kNvfp4P2 ? k_dq_delta<kNvfp4P2> : k_dq_delta<kNvfp4>;
-  {
-    hipError_t e = set_dynamic_lds_once<k_dq_core>(lds);
-    if (e == hipSuccess)
-      e = fmt == kNvfp4Mx   ? set_dynamic_lds_once<k_dq_delta<kNvfp4Mx>>(lds)
-          : fmt == kNvfp4P2 ? set_dynamic_lds_once<k_dq_delta<kNvfp4P2>>(lds)
-                            : set_dynamic_lds_once<k_dq_delta<kNvfp4>>(lds);
+  const int kq = (int)(K >> 3);
+  // cubes of at most 8 tokens and K <= 16384: the register-resident core pass
+  // (one column per thread, pipelined over cubes, up to K 8192; else one cube
+  // per workgroup with four columns per thread)
+  const bool reg = g.cf * g.ch * g.cw <= 8 && kq <= 2048;
+  const int iter = kq <= 1024 ? 1 : 4;
+  const int threads = (((kq + iter - 1) / iter) + 63) / 64 * 64;
+  if (!reg) {
+    const hipError_t e = set_dynamic_lds_once<k_dq_core>(lds);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(k_dq_zero, dim3(1), dim3(1), 0, s, damax_bits);
-  hipLaunchKernelGGL(k_dq_core, dim3((unsigned)ncubes), dim3(256), lds, s, x, (int)K, g, ccodes, cscale,
-                     core_bf16, damax_bits);
-  hipLaunchKernelGGL(kdelta, dim3((unsigned)ncubes), dim3(256), lds, s, x, (int)K, g, ccodes, cscale, damax_bits,
-                     codes, blk_scale, tensor_scale);
+  if (reg && iter == 1) {
+    const int64_t slots = resident_grid<k_dq_core_reg<1, 1024, true>>(threads, 0);
+    auto kern = k_dq_core_reg<1, 1024, true>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(ncubes < slots ? ncubes : slots)), dim3((unsigned)threads), 0, s, x,
+                       (int)K, g, (int)ncubes, ccodes, cscale, core_bf16, damax_bits);
+  } else if (reg) {
+    auto kern = k_dq_core_reg<4, 512, false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)ncubes), dim3((unsigned)threads), 0, s, x, (int)K, g, (int)ncubes,
+                       ccodes, cscale, core_bf16, damax_bits);
+  } else {
+    hipLaunchKernelGGL(k_dq_core, dim3((unsigned)ncubes), dim3(256), lds, s, x, (int)K, g, ccodes, cscale,
+                       core_bf16, damax_bits);
+  }
+  auto kdelta = fmt == kNvfp4Mx ? k_dq_delta<kNvfp4Mx> : fmt == kNvfp4P2 ? k_dq_delta<kNvfp4P2> : k_dq_delta<kNvfp4>;
+  const int64_t dslots = fmt == kNvfp4Mx   ? resident_grid<k_dq_delta<kNvfp4Mx>>(256, 0)
+                         : fmt == kNvfp4P2 ? resident_grid<k_dq_delta<kNvfp4P2>>(256, 0)
+                                           : resident_grid<k_dq_delta<kNvfp4>>(256, 0);
+  const int64_t dblocks = (M + 3) / 4;
+  hipLaunchKernelGGL(kdelta, dim3((unsigned)(dblocks < dslots ? dblocks : dslots)), dim3(256), 0, s, x, (int)K, g,
+                     (int)M, ccodes, cscale, damax_bits, codes, blk_scale, tensor_scale);
   return hipGetLastError();
 }
 

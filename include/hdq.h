@@ -438,11 +438,18 @@ int64_t hdq_dq_cubes(const hdq_dq_grid *g);
  *   fmt        : HDQ_FMT_NVFP4, _NVFP4_MX or _NVFP4_P2 for the differences.
  *   core_codes : device uint8 [cubes, K] (signed E4M3); core_scale: fp32 [cubes].
  *   core_bf16  : NULL, or device bf16 [cubes, K]: the signed E4M3 code values
- *                (exact), the core GEMM's operand.
+ *                (exact), the bf16 core GEMM's operand (plain NVFP4, or K not
+ *                a multiple of 128).
  *   delta      : fmt, had_block 1, rows = tokens, cols = K, with codes,
  *                blk_scale and tensor_scale set (written).
  *   ws, ws_bytes: device scratch >= hdq_workspace_bytes(HDQ_OP_DQ_QUANTIZE, ...)
  *                (256 bytes).
+ * Non-finite values (not covered by the method's description): when any
+ * difference is not finite -- which a NaN or infinite element of x, or a
+ * cube sum or a difference beyond the float32 range, always causes -- the
+ * tensor scale *delta->tensor_scale is written as NaN, a flag on the device;
+ * the codes and scales are then unspecified (a linear layer on them yields
+ * NaN outputs).  Finite inputs never raise it.
  */
 int hdq_dq_quantize(const void *x, int64_t K, const hdq_dq_grid *g, int32_t fmt, uint8_t *core_codes,
                     float *core_scale, void *core_bf16, hdq_qtensor *delta, void *ws, size_t ws_bytes,

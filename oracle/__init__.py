@@ -326,9 +326,19 @@ def dq_delta(x16, F, H, W, cube, codes, scale):
 
 def dq_quantize(x16, F, H, W, cube, mx=0):
     """The whole activation side: core codes and scales, the differences, and
-    their NVFP4 codes, block scales and tensor scale (amax of |difference|)."""
+    their NVFP4 codes, block scales and tensor scale (amax of |difference|).
+    Non-finite values (the abstract does not speak of them; this reading):
+    when any difference is not finite -- which a NaN or infinite token
+    element, or a cube sum or a difference that overflows float32, always
+    causes -- the tensor scale is NaN, the flag that the codes (left zero
+    here) mean nothing."""
     codes, scale = dq_core(x16, F, H, W, cube)
     d = dq_delta(x16, F, H, W, cube, codes, scale)
+    if not np.isfinite(d).all():
+        M, K = d.shape
+        return dict(core=codes, core_scale=scale, delta=d, delta_amax=np.float32(np.nan),
+                    codes=np.zeros((M, K // 2), np.uint8), blk=np.zeros((M, K // 16), np.uint8),
+                    s_t=np.float32(np.nan))
     amax = np.float32(np.abs(d).max()) if d.size else np.float32(0)
     dc, de, st = quant_nvfp4_rotated(d, amax, mx)
     return dict(core=codes, core_scale=scale, delta=d, delta_amax=amax, codes=dc, blk=de, s_t=st)

@@ -13,6 +13,8 @@ import torch
 import oracle as O
 from bit_quantized_video_amd import synth
 
+import dq_cases
+
 pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():
     pytest.skip("needs a GPU", allow_module_level=True)
@@ -52,7 +54,12 @@ def check_quantize(x16, F, H, W, cube, fmt):
 
 @pytest.mark.parametrize("grid,cube,K,fmt", [
     ((3, 5, 7), (2, 2, 2), 64, "nvfp4"), ((3, 5, 7), (2, 2, 2), 64, "mx"), ((3, 5, 7), (1, 1, 1), 96, "p2"),
-    ((4, 6, 10), (2, 3, 4), 256, "mx"), ((2, 3, 3), (2, 3, 3), 32, "nvfp4"), ((5, 4, 9), (4, 4, 4), 512, "mx")])
+    ((4, 6, 10), (2, 3, 4), 256, "mx"), ((2, 3, 3), (2, 3, 3), 32, "nvfp4"), ((5, 4, 9), (4, 4, 4), 512, "mx"),
+    # cubes of <= 8 tokens take the register-resident core pass: one chunk
+    # column per thread up to K 8192 (1024 threads), four up to 16384; past
+    # that, and for larger cubes, the two-read pass
+    ((3, 3, 5), (2, 2, 2), 8192, "mx"), ((2, 3, 3), (2, 2, 2), 12288, "p2"), ((2, 2, 3), (2, 2, 2), 16416, "nvfp4"),
+    ((3, 5, 6), (1, 2, 2), 3072, "mx")])
 def test_dq_quantize_bit_exact(grid, cube, K, fmt):
     F, H, W = grid
     say(f"dq quantize grid={grid} cube={cube} K={K} {fmt}")
@@ -77,6 +84,28 @@ def test_dq_quantize_full_size_video_grid():
     say("dq quantize full size")
     x16 = synth.smooth_video_tokens(F, H, W, K, synth.rng_for(131, 0))
     check_quantize(x16, F, H, W, (2, 2, 2), hdq.FMT_NVFP4_MX)
+
+
+@pytest.mark.parametrize("cube", [(2, 2, 2), (2, 2, 4)])
+@pytest.mark.parametrize("fmt", ["mx", "nvfp4"])
+def test_dq_nonfinite_flag_and_extreme_values(cube, fmt):
+    """Non-finite tokens: wherever the oracle flags a non-finite difference
+    (a NaN or infinite element, a cube sum or a difference past float32's
+    range) the GPU's tensor scale is NaN too; the finite extreme case (a cube
+    summing to the largest bf16, a bf16 subnormal) matches the oracle byte for
+    byte.  Cubes of 8 tokens take the register-resident pass, of 16 the
+    two-read pass."""
+    F, H, W, K, cases = dq_cases.nonfinite_cases()
+    for name, (x, _) in cases.items():
+        say(f"dq non-finite case {name!r} cube={cube} {fmt}")
+        x16 = synth.to_bf16_bits(x)
+        q = O.dq_quantize(x16, F, H, W, cube, MX[FMTS[fmt]])
+        if np.isnan(q["s_t"]):
+            a = hdq.dq_quantize(to_dev(x16), (F, H, W, cube), FMTS[fmt])
+            torch.cuda.synchronize()
+            assert np.isnan(float(a.delta.tensor_scale.item())), name
+        else:
+            check_quantize(x16, F, H, W, cube, FMTS[fmt])
 
 
 @pytest.mark.parametrize("fmt", ["nvfp4", "mx", "p2"])

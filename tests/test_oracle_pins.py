@@ -19,6 +19,8 @@ import torch
 import oracle as O
 from bit_quantized_video_amd import synth
 
+import dq_cases
+
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 BLOCKS = [2, 4, 8, 16, 32, 64, 128]
 
@@ -760,6 +762,35 @@ def test_dq_delta_exact_on_constructed_cubes():
     flat = np.repeat((x - e)[:1], M, axis=0)          # every token one on-grid core: zero differences
     q0 = O.dq_quantize(synth.to_bf16_bits(flat), F, H, W, cube)
     assert q0["s_t"] == 0.0 and not q0["codes"].any() and not q0["blk"].any()
+
+
+def test_dq_nonfinite_flag():
+    """Pins the non-finite reading: a NaN or infinite token element, a cube
+    sum past the float32 range and a difference past it each give a NaN
+    tensor scale (with a non-finite difference, checked independently of the
+    flag); finite sums and differences, however extreme, give a finite scale
+    and codes that reconstruct the differences within NVFP4's bound."""
+    F, H, W, K, cases = dq_cases.nonfinite_cases()
+    cube = (2, 2, 2)
+    for name, (x, flagged) in cases.items():
+        q = O.dq_quantize(synth.to_bf16_bits(x), F, H, W, cube, mx=1)
+        assert np.isnan(q["s_t"]) == flagged, name
+        assert (not np.isfinite(q["delta"]).all()) == flagged, name
+        if not flagged:
+            d = q["delta"]
+            dq = O.dequant_nvfp4(q["codes"], q["blk"], q["s_t"], K)
+            db = np.repeat(O.e4m3_decode(q["blk"]) * q["s_t"], 16, axis=1)
+            assert np.all(np.abs(d - dq) <= db + np.maximum(0.0, np.abs(d) - 6 * db) + 1e-7 * np.abs(d)), name
+    # the two overflow cases overflow where their names say
+    with np.errstate(over="ignore"):
+        x, _ = cases["cube sum overflows"]
+        assert np.isinf(np.float32(x[0, 4]) + np.float32(x[0, 4]))
+        x, _ = cases["difference overflows"]
+        q = O.dq_quantize(synth.to_bf16_bits(x), F, H, W, cube, mx=1)
+        s = np.float32(0)
+        for v in x[np.flatnonzero(O.dq_cube_of(F, H, W, cube) == 0), 4]:
+            s = np.float32(s + v)
+        assert np.isfinite(s) and np.isfinite(q["core_scale"]).all() and np.isinf(q["delta"][0, 4])
 
 
 def test_dq_reconstruction_bound_and_gain_on_smooth_video():
