@@ -41,7 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "effective TOPS of fused Hadamard-quant+linear (CogVideoX-5B shapes); quant GB/s"
-PEAK = {"int8": 5.0e15, "bf16": 2.5e15, "fp4": 10.1e15, "hbm": 8.0e12}
+PEAK = {"int8": 5.0e15, "bf16": 2.5e15, "fp8": 5.0e15, "fp4": 10.1e15, "hbm": 8.0e12}
 HB = 128
 DELTA_T, RATIO_T = 0.1, 50.0
 
@@ -1026,7 +1026,8 @@ def bench_deltaquant(args, hdq, synth):
     w = synth.device_gaussian((N, K), 0.02, gen, dev)
     W1 = hdq.LinearWeights(w, 1, fp4_fmt=fmt)    # no rotation: had_block 1
     wq = W1.w_fp4
-    wdec = hdq.dq_decode_weights(wq) if hdq.dq_core_needs_bf16(fmt, C, K) else None
+    bf16_core = hdq.dq_core_needs_bf16(fmt, C, K)
+    wdec = hdq.dq_decode_weights(wq) if bf16_core else None
     a = hdq.dq_quantize(x, grid, fmt)
     y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
     ws = torch.empty(hdq.dq_linear_workspace_bytes(grid, K, N, fmt), dtype=torch.uint8, device=dev)
@@ -1046,16 +1047,23 @@ def bench_deltaquant(args, hdq, synth):
     q_ms = timed(lambda: hdq.dq_quantize(x, grid, fmt, out=a), args.dq_steps)
     l_ms = timed(lambda: hdq.dq_linear(a, wq, wdec, y=y, ws=ws), args.dq_steps)
     # algorithmic bytes of the quantization: x once, the difference codes and
-    # block scales, the core codes, scales and bf16 code values
-    q_bytes = M * K * 2 + M * K // 2 + M * K // 16 + C * K * 3 + C * 4
-    flops = 2.0 * M * N * K + 2.0 * C * N * K
+    # block scales, the core codes and scales (and the core's bf16 values when
+    # the core GEMM runs in bf16)
+    q_bytes = M * K * 2 + M * K // 2 + M * K // 16 + C * K * (3 if bf16_core else 1) + C * 4
+    # the linear: the core GEMM (FP8 x FP4 MFMA, or bf16) and the difference
+    # GEMM (FP4 x FP4); its peak is the time-weighted one of the two
+    core_flops, diff_flops = 2.0 * C * N * K, 2.0 * M * N * K
+    flops = core_flops + diff_flops
+    core_peak = PEAK["bf16" if bf16_core else "fp8"]
+    peak = flops / (core_flops / core_peak + diff_flops / PEAK["fp4"])
     ref = x.float() @ w.float().T
     plain = hdq.linear(hdq.PREC_NVFP4, None, W1, xq=hdq.quantize(x, 1, fmt), y_dtype=hdq.DTYPE_F32)
     yd = hdq.dq_linear(a, wq, wdec, y_dtype=hdq.DTYPE_F32, ws=ws)
     nref = float(torch.linalg.vector_norm(ref))
     err = lambda t: round(float(torch.linalg.vector_norm(t - ref)) / nref, 5)
-    out = {"workload": "DeltaQuant cube-delta linear: 13x30x45 video tokens (17550), K 3072 -> N 12288, "
-                       "2x2x2 cubes (3105, ragged), FP8 E4M3 cores, NVFP4-MX differences, bf16 output",
+    ach = flops / (l_ms * 1e-3)
+    out = {"workload": f"DeltaQuant cube-delta linear: 13x30x45 video tokens ({M}), K 3072 -> N 12288, "
+                       f"2x2x2 cubes ({C}, ragged), FP8 E4M3 cores, NVFP4-MX differences, bf16 output",
            "quantize_us": round(q_ms * 1e3, 1),
            "quantize_gbps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
            "quantize_roofline": {"bound": "hbm", "achieved": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
@@ -1063,11 +1071,14 @@ def bench_deltaquant(args, hdq, synth):
                                  "frac": round(q_bytes / (q_ms * 1e-3) / 1e9 / 8000.0, 3),
                                  "traffic": None},
            "linear_us": round(l_ms * 1e3, 1),
-           "linear_tflops": round(flops / (l_ms * 1e-3) / 1e12, 1),
-           "linear_roofline": {"bound": "mfma", "achieved": round(flops / (l_ms * 1e-3) / 1e12, 1),
-                               "peak": 10100.0, "unit": "TFLOP/s",
-                               "frac": round(flops / (l_ms * 1e-3) / 1e12 / 10100.0, 3), "traffic": None},
-           "rel_err_vs_bf16": err(yd), "plain_nvfp4_rel_err_vs_bf16": err(plain)}
+           "linear_tflops": round(ach / 1e12, 1),
+           "linear_roofline": {"bound": "mfma", "achieved": round(ach / 1e12, 1),
+                               "peak": round(peak / 1e12, 1), "unit": "TFLOP/s",
+                               "peak_note": ("time-weighted: core GEMM %s (%.0f TFLOP/s), difference GEMM FP4 "
+                                             "(%.0f TFLOP/s)" % ("bf16" if bf16_core else "FP8 x FP4",
+                                                                 core_peak / 1e12, PEAK["fp4"] / 1e12)),
+                               "frac": round(ach / peak, 3), "traffic": None},
+           "rel_err_vs_bf16": err(yd), "plain_nvfp4mx_rel_err_vs_bf16": err(plain)}
     del ref, plain, yd
     return out
 
