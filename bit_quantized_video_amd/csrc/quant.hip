@@ -322,7 +322,8 @@ hipError_t launch_quant_int_rows(const uint16_t* x, int64_t rows, int64_t cols, 
 // FMT: kNvfp4 (E4M3 scale per 16), kNvfp4Mx (a power of two per aligned
 // pair of 16-blocks), kNvfp4P2 (a power of two per 16-block).
 template <int FMT>
-__device__ __forceinline__ uint32_t nvfp4_chunk(float (&v)[8], float s_t, float six_st, uint32_t* e_out) {
+__device__ __forceinline__ uint32_t nvfp4_chunk(float (&v)[8], float s_t, float six_st, float inv_st,
+                                                uint32_t* e_out) {
   float a = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
@@ -332,15 +333,24 @@ __device__ __forceinline__ uint32_t nvfp4_chunk(float (&v)[8], float s_t, float 
   a = fmaxf(a, xor_lane<1>(a));
   if constexpr (FMT == kNvfp4Mx) a = fmaxf(a, xor_lane<2>(a));
   uint32_t e = 0u;
-  float d = 0.0f;
+  float inv = 0.0f;  // fl32(1 / d), d = the block scale's value times s_t
   if (s_t > 0.0f) {
     const float t = a / six_st;
-    e = FMT == kNvfp4 ? e4m3_encode(t) : e4m3_encode(pow2_ceil_clamped(t));
-    d = e4m3_decode(e) * s_t;
+    if constexpr (FMT == kNvfp4) {
+      e = e4m3_encode(t);
+      const float d = e4m3_decode(e) * s_t;
+      if (d != 0.0f) inv = 1.0f / d;
+    } else {
+      // d = 2^k s_t for the block's power of two 2^k, so fl32(1 / d) =
+      // 2^-k fl32(1 / s_t) exactly (every value stays normal: s_t >= 2^-110
+      // and k in [-9, 8]); 2^-k is 2^k's exponent field mirrored
+      const float p2 = pow2_ceil_clamped(t);
+      e = e4m3_encode(p2);
+      inv = inv_st * __uint_as_float(0x7f000000u - __float_as_uint(p2));
+    }
   }
   *e_out = e;
-  if (d == 0.0f) return 0u;
-  const float inv = 1.0f / d;
+  if (inv == 0.0f) return 0u;
   return e2m1x2_encode(v[0] * inv, v[1] * inv) | (e2m1x2_encode(v[2] * inv, v[3] * inv) << 8) |
          (e2m1x2_encode(v[4] * inv, v[5] * inv) << 16) | (e2m1x2_encode(v[6] * inv, v[7] * inv) << 24);
 }
@@ -365,7 +375,7 @@ __global__ __launch_bounds__(256) void k_quant_nvfp4(
   // 2^8).
   const float s_t = (A >= kTiny) ? A / (FMT == kNvfp4 ? 2688.0f : 1536.0f) : 0.0f;
   if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = s_t;
-  const float six_st = 6.0f * s_t;
+  const float six_st = 6.0f * s_t, inv_st = s_t > 0.0f ? 1.0f / s_t : 0.0f;
   const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
   const uint4* xv = reinterpret_cast<const uint4*>(x);
@@ -387,7 +397,7 @@ __global__ __launch_bounds__(256) void k_quant_nvfp4(
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[i] = v[i] * sc;
       uint32_t e;
-      const uint32_t packed = nvfp4_chunk<FMT>(v, s_t, six_st, &e);
+      const uint32_t packed = nvfp4_chunk<FMT>(v, s_t, six_st, inv_st, &e);
       if (idx < nch) {
         cv[idx] = packed;
         // the lane with the even chunk of the 16-element block writes its scale
@@ -745,7 +755,7 @@ __global__ __launch_bounds__(256) void k_dq_delta(const uint16_t* __restrict__ x
   const float A = __uint_as_float(*damax_bits);
   const float s_t = (A >= kTiny) ? A / (FMT == kNvfp4 ? 2688.0f : 1536.0f) : (A == A ? 0.0f : A);
   if (blockIdx.x == 0 && tid == 0) *tensor_scale = s_t;
-  const float six_st = 6.0f * s_t;
+  const float six_st = 6.0f * s_t, inv_st = s_t > 0.0f ? 1.0f / s_t : 0.0f;
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   const uint2* cc = reinterpret_cast<const uint2*>(ccodes);
   uint32_t* cv = reinterpret_cast<uint32_t*>(codes);
@@ -778,7 +788,7 @@ __global__ __launch_bounds__(256) void k_dq_delta(const uint16_t* __restrict__ x
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = v[i] - e[i] * sc;
         uint32_t eb;
-        const uint32_t packed = nvfp4_chunk<FMT>(v, s_t, six_st, &eb);
+        const uint32_t packed = nvfp4_chunk<FMT>(v, s_t, six_st, inv_st, &eb);
         if (q < kq) {
           cv[xb + q] = packed;
           if ((q & 1) == 0) blk_scale[(xb + q) >> 1] = (uint8_t)eb;
