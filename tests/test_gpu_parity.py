@@ -572,15 +572,14 @@ def test_device_predicated_linear_matches_fixed(case):
     assert torch.equal(y_dyn.view(torch.int16), y_fix.view(torch.int16))
 
 
-@pytest.mark.parametrize("M,N,K", [(300, 384, 512), (1000, 600, 1024), (37, 19, 96), (17776, 3072, 3072)])
+@pytest.mark.parametrize("M,N,K,y_dtype", [(m, n, k, yd) for (m, n, k) in [(300, 384, 512), (1000, 600, 1024), (37, 19, 96)]
+                                             for yd in (hdq.DTYPE_BF16, hdq.DTYPE_F32)]
+                         + [(17776, 3072, 3072, hdq.DTYPE_BF16)])   # full size: bf16 output only
 @pytest.mark.parametrize("fmt", ["nvfp4", "nvfp4_mx", "nvfp4_p2"])
-@pytest.mark.parametrize("y_dtype", [hdq.DTYPE_BF16, hdq.DTYPE_F32])
 def test_linear_dispatch_matches_fixed_precision(M, N, K, fmt, y_dtype):
     """hdq_linear_dispatch runs the decided precision's GEMM (one launch, or
     three gated ones for shapes the single kernel does not take) with the
     same bits as hdq_linear at that precision."""
-    if M == 17776 and y_dtype == hdq.DTYPE_F32:
-        pytest.skip("full size checked with bf16 output")
     say(f"linear dispatch M={M} N={N} K={K} {fmt} y={y_dtype}")
     hb = 32
     x16 = synth.lognormal_tokens(M, K, synth.rng_for(114, M + N))
