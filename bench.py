@@ -1026,7 +1026,7 @@ def bench_deltaquant(args, hdq, synth):
     w = synth.device_gaussian((N, K), 0.02, gen, dev)
     W1 = hdq.LinearWeights(w, 1, fp4_fmt=fmt)    # no rotation: had_block 1
     wq = W1.w_fp4
-    bf16_core = hdq.dq_core_needs_bf16(fmt, C, K)
+    bf16_core = hdq.dq_core_needs_bf16(fmt, C, K, N)
     wdec = hdq.dq_decode_weights(wq) if bf16_core else None
     a = hdq.dq_quantize(x, grid, fmt)
     y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)

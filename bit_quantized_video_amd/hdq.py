@@ -401,11 +401,13 @@ def _dq_grid(grid):
     return DqGridDesc(F, H, W, cf, ch, cw)
 
 
-def dq_core_needs_bf16(fmt, cubes, K):
+def dq_core_needs_bf16(fmt, cubes, K, N=None):
     """Whether hdq_dq_linear's core GEMM runs on the bf16 core values and
     decoded weights: unless the weights' block scales are powers of two (MX
-    or per-16 format), K % 128 == 0 and the core codes fit 32-bit offsets."""
-    return not (fmt in (FMT_NVFP4_MX, FMT_NVFP4_P2) and K % 128 == 0 and cubes * K < 2 ** 31)
+    or per-16 format), K % 128 == 0, and the core codes and (N given) the
+    FP4 weight codes fit 32-bit offsets -- the library's own rule."""
+    fits = cubes * K < 2 ** 31 and (N is None or N * K // 2 < 2 ** 31)
+    return not (fmt in (FMT_NVFP4_MX, FMT_NVFP4_P2) and K % 128 == 0 and fits)
 
 
 class DqActivations:
@@ -451,8 +453,10 @@ def dq_linear_workspace_bytes(grid, K, N, fmt):
 
 
 def dq_linear(a, w_fp4, w_dec=None, y=None, y_dtype=DTYPE_BF16, ws=None, stream=None):
-    """hdq_dq_linear: y = differences x W^T + cube cores x W^T (w_dec and
-    the activations' bf16 core values are needed for plain NVFP4 only)."""
+    """hdq_dq_linear: y = differences x W^T + cube cores x W^T.  w_dec and
+    the activations' bf16 core values are needed only when the core GEMM runs
+    in bf16 (dq_core_needs_bf16 with N: plain NVFP4, K % 128 != 0, or codes
+    past 32-bit offsets); the library returns HDQ_ERR_INVALID without them."""
     M, N = a.delta.rows, w_fp4.rows
     if y is None:
         dt = {DTYPE_F32: torch.float32, DTYPE_BF16: torch.bfloat16}[y_dtype]

@@ -170,7 +170,7 @@ def linear_case(F, H, W, K, N, cube, fmt, rows=None, y_dtype=hdq.DTYPE_BF16, see
     S = dabs @ wabs.T + (core @ wabs.T)[cube_of]
     c = max(4.0, 2.0 * np.sqrt(K / 16.0))
     tol = c * 2.0 ** -24 * S + 4 * 2.0 ** -24 * np.abs(ref64) + 1e-35
-    if not hdq.dq_core_needs_bf16(fmt, core.shape[0], K):
+    if not hdq.dq_core_needs_bf16(fmt, core.shape[0], K, wabs.shape[0]):
         tol = tol + core_fp8_mfma_bound(core, wabs, fmt)[cube_of]
     if y_dtype == hdq.DTYPE_BF16:
         tol = tol + 2.0 ** -8 * 1.01 * np.abs(got)
@@ -195,7 +195,7 @@ def test_dq_linear_matches_oracle(grid, cube, K, N, fmt, y_dtype):
     # float32 output: 1e-5 where the core GEMM accumulates at float32
     # precision (bf16 route); the FP8 x FP4 MFMA's narrower sum (bounded per
     # element above) measures about 1.5e-5 on these inputs, so 1e-4 there
-    fp8 = not hdq.dq_core_needs_bf16(FMTS[fmt], hdq.dq_cubes((*grid, cube)), K)
+    fp8 = not hdq.dq_core_needs_bf16(FMTS[fmt], hdq.dq_cubes((*grid, cube)), K, N)
     assert err <= (1e-3 if y_dtype == hdq.DTYPE_BF16 else 1e-4 if fp8 else 1e-5), err
 
 
