@@ -35,10 +35,6 @@ __device__ __forceinline__ uint32_t e4m3_pow2_to_e8m0(uint32_t b) {
 // its first half zeroed and the second block's: exact, at twice the MFMA
 // work.  Per row and stage the 16 E8M0 bytes are stored as four words:
 // first blocks of lane half 0's and 1's groups, then their second blocks.
-struct Fp4PipeStage {
-  uint4 x[4], w[4];  // codes: 4 x 16-byte chunks per operand per thread
-  uint4 sc;          // the 16 E4M3 bytes of one X or W row (8 MX pairs)
-};
 
 template <int KS>
 __device__ __forceinline__ v16f mfma_fp4(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
@@ -63,7 +59,7 @@ __device__ __forceinline__ void gemm_fp4mx_pipe_body(
   constexpr int SB = XB + WB + (BM + BN) * SCB;       // + E8M0 bytes
   static_assert(2 * SB == fp4_pipe_lds<P2>(), "LDS size");
   constexpr int kOutPitch = BN * 2 + 16;              // bf16 output row staged in LDS
-  static_assert(BM * kOutPitch <= 2 * SB, "output tile must fit the pipeline buffers");
+  static_assert(BM / 2 * kOutPitch <= SB, "half an output tile must fit one pipeline buffer");
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -75,9 +71,13 @@ __device__ __forceinline__ void gemm_fp4mx_pipe_body(
   if (G == 0) return;
   const int ld = K / 2, lds_ = K / 16;
 
-  const int cr = tid >> 3, cc = tid & 7;  // code chunks: 8 threads per row, 64 rows per round
-  const uint32_t cvoff = (uint32_t)(cr * ld + 16 * cc);
-  const int cdst = cr * 128 + 16 * (cc ^ swz128(cr));
+  // Code bytes go straight to LDS by LDS-DMA: instruction p of wave w fills
+  // LDS rows 64 p + 8 w + (lane >> 3), slot lane & 7, with the row's 16-byte
+  // chunk (lane & 7) ^ swz128(row), the swizzled layout the fragment reads
+  // expect.  The swizzle depends on the lane and the wave only, so the four
+  // instructions per operand differ by scalar offsets.
+  const int drow = 8 * wave + (lane >> 3);
+  const uint32_t dvoff = (uint32_t)(drow * ld + 16 * ((lane & 7) ^ swz128(drow)));
   // scales: waves 0-3 take the 256 X rows, waves 4-7 the 256 W rows
   const int sw_ = __builtin_amdgcn_readfirstlane(tid >> 8), srow = tid & 255;
   const uint32_t svoff = (uint32_t)(srow * lds_);
@@ -95,29 +95,29 @@ __device__ __forceinline__ void gemm_fp4mx_pipe_body(
                : make_rsrc(xsc + (int64_t)m0 * lds_, (uint32_t)((int64_t)(M - m0) * lds_));
   };
   open_tile();
-  auto load = [&](Fp4PipeStage& st) {
+  // Issues the next stage's loads: 8 LDS-DMA instructions per wave into
+  // buffer buf, then this thread's 16 scale bytes into a register (sc), the
+  // last of the wave's 9 vector memory operations.
+  uint4 sc;
+  auto issue = [&](int buf) {
+    uint8_t* base = smem + buf * SB + 1024 * wave;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      st.x[p] = buf_load16(xres, cvoff, l_kt * (BK / 2) + p * 64 * ld);
-      st.w[p] = buf_load16(wres, cvoff, l_kt * (BK / 2) + p * 64 * ld);
-    }
-    st.sc = buf_load16(sres, svoff, l_kt * (BK / 16));
+    for (int p = 0; p < 4; ++p) lds_dma16(xres, base + 8192 * p, dvoff, l_kt * (BK / 2) + p * 64 * ld);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) lds_dma16(wres, base + XB + 8192 * p, dvoff, l_kt * (BK / 2) + p * 64 * ld);
+    sc = buf_load16(sres, svoff, l_kt * (BK / 16));
     if (++l_kt == nk) {
       l_kt = 0;
       l_logical += seq.stride;
       if (l_logical < tiles_m * tiles_n) open_tile();
     }
   };
-  auto store = [&](const Fp4PipeStage& st, int buf) {
+  // Writes the staged scale bytes to buffer buf as E8M0 words.
+  auto store_sc = [&](int buf) {
     uint8_t* base = smem + buf * SB;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      *reinterpret_cast<uint4*>(base + cdst + p * 64 * 128) = st.x[p];
-      *reinterpret_cast<uint4*>(base + XB + cdst + p * 64 * 128) = st.w[p];
-    }
     // E8M0 of group g comes from E4M3 byte 2g (P2: and 2g + 1); word h holds
     // g = h, h+2, h+4, h+6
-    const uint32_t d[4] = {st.sc.x, st.sc.y, st.sc.z, st.sc.w};
+    const uint32_t d[4] = {sc.x, sc.y, sc.z, sc.w};
     uint32_t w0 = 0u, w1 = 0u, w2 = 0u, w3 = 0u;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -252,55 +252,66 @@ __device__ __forceinline__ void gemm_fp4mx_pipe_body(
     y[2] = y[2] + (c.z * cs) * stw;
     y[3] = y[3] + (c.w * cs) * stw;
   };
-  auto epilogue = [&](int logical) {
+  auto epilogue = [&](int logical, int buf) {
     int tm, tn;
     grouped_tile(logical, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     if constexpr (ADD) core_rows(m0);
     if constexpr (OUT == kOutBf16) {
-      // Stage the bf16 tile in LDS (both pipeline buffers are free once every
-      // wave is past this stage; the next stage is still in registers), then
-      // write whole 512-byte rows with 16-byte stores.
-      lds_barrier();
-      uint8_t* const lrow = smem + (wm * WM_T * 32 + r32) * kOutPitch + 2 * (wn * WN_T * 32 + 4 * h);
-#pragma unroll
-      for (int i = 0; i < WM_T; ++i) {
-        float4 cv[ADD ? WN_T : 1][4];
-        if constexpr (ADD) core_load(n0, i, cv);
-#pragma unroll
-        for (int j = 0; j < WN_T; ++j)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const v16f& a = acc[j][i];
-            if constexpr (ADD) {
-              float y[4] = {a[4 * g] * scale, a[4 * g + 1] * scale, a[4 * g + 2] * scale, a[4 * g + 3] * scale};
-              core_add(cv[j][g], i, y);
-              *reinterpret_cast<uint2*>(lrow + i * 32 * kOutPitch + 2 * (j * 32 + 8 * g)) =
-                  make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
-            } else {
-              *reinterpret_cast<uint2*>(lrow + i * 32 * kOutPitch + 2 * (j * 32 + 8 * g)) =
-                  make_uint2(pack_bf16x2(a[4 * g] * scale, a[4 * g + 1] * scale),
-                             pack_bf16x2(a[4 * g + 2] * scale, a[4 * g + 3] * scale));
-            }
-          }
-      }
-      lds_barrier();
+      // Stage the bf16 tile in LDS buffer buf, which this stage's compute has
+      // finished with (the other buffer is receiving the next stage), half a
+      // tile at a time: half hh holds fragment rows i = 2 hh, 2 hh + 1 of every
+      // wave, tile rows hh * 64 + 0..63 and 128 + hh * 64 + 0..63, as local rows
+      // 0..127.  Then whole 512-byte rows are written with 16-byte stores.
+      // The barriers wait for LDS accesses only: the next stage's DMA loads
+      // stay in flight.
+      uint8_t* const stage = smem + buf * SB;
       uint16_t* y16 = reinterpret_cast<uint16_t*>(Y);
       const int n = n0 + 8 * (tid & 31);
       const bool vec = n + 8 <= N && (N & 7) == 0;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        lds_only_barrier();
+        uint8_t* const lrow = stage + (wm * 64 + r32) * kOutPitch + 2 * (wn * WN_T * 32 + 4 * h);
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+          const int i = 2 * hh + ii;
+          float4 cv[ADD ? WN_T : 1][4];
+          if constexpr (ADD) core_load(n0, i, cv);
+#pragma unroll
+          for (int j = 0; j < WN_T; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const v16f& a = acc[j][i];
+              if constexpr (ADD) {
+                float y[4] = {a[4 * g] * scale, a[4 * g + 1] * scale, a[4 * g + 2] * scale, a[4 * g + 3] * scale};
+                core_add(cv[j][g], i, y);
+                *reinterpret_cast<uint2*>(lrow + ii * 32 * kOutPitch + 2 * (j * 32 + 8 * g)) =
+                    make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+              } else {
+                *reinterpret_cast<uint2*>(lrow + ii * 32 * kOutPitch + 2 * (j * 32 + 8 * g)) =
+                    make_uint2(pack_bf16x2(a[4 * g] * scale, a[4 * g + 1] * scale),
+                               pack_bf16x2(a[4 * g + 2] * scale, a[4 * g + 3] * scale));
+              }
+            }
+        }
+        lds_only_barrier();
 #pragma unroll 4
-      for (int r = tid >> 5; r < BM; r += 16) {
-        const uint8_t* src = smem + r * kOutPitch + 16 * (tid & 31);
-        if (m0 + r < M) {
-          uint16_t* dst = y16 + (int64_t)(m0 + r) * N + n;
-          if (vec) {
-            store16_nt(dst, src);
-          } else {
-            for (int e = 0; e < 8 && n + e < N; ++e) dst[e] = reinterpret_cast<const uint16_t*>(src)[e];
+        for (int r = tid >> 5; r < BM / 2; r += 16) {
+          const uint8_t* src = stage + r * kOutPitch + 16 * (tid & 31);
+          const int tr = (r >> 6) * 128 + hh * 64 + (r & 63);
+          if (m0 + tr < M) {
+            uint16_t* dst = y16 + (int64_t)(m0 + tr) * N + n;
+            if (vec) {
+              store16_nt(dst, src);
+            } else {
+              for (int e = 0; e < 8 && n + e < N; ++e) dst[e] = reinterpret_cast<const uint16_t*>(src)[e];
+            }
           }
         }
       }
-      lds_barrier();  // the next stage may overwrite the staged tile
+      // The caller's stage barrier orders these LDS reads before the buffer
+      // is refilled.
     } else {
       const bool full_n = n0 + BN <= N && (N & 3) == 0;
 #pragma unroll
@@ -331,35 +342,39 @@ __device__ __forceinline__ void gemm_fp4mx_pipe_body(
   };
 
   int ckt = 0, clogical = seq.first;
-  auto finish_stage = [&]() {
+  auto finish_stage = [&](int buf) {
     if (++ckt == nk) {
-      epilogue(clogical);
+      epilogue(clogical, buf);
       zero_acc();
       ckt = 0;
       clogical += seq.stride;
     }
   };
 
-  Fp4PipeStage ra;
-  load(ra);
-  store(ra, 0);
-  lds_barrier();
+  // Stage g lives in LDS buffer g % 2.  Stage g + 1 is issued at the start
+  // of stage g's compute, into the buffer every wave finished reading before
+  // the last stage barrier; the stage barrier after the compute waits for this
+  // wave's DMA loads and LDS writes (vmcnt and lgkmcnt zero), so after it the
+  // whole stage is in LDS.
+  issue(0);
+  store_sc(0);
+  stage_barrier();
   int g = 0;
   for (; g + 1 < G; g += 2) {
-    load(ra);
+    issue(1);
     compute(0);
-    finish_stage();
-    store(ra, 1);
-    lds_barrier();
-    if (g + 2 < G) load(ra);
+    finish_stage(0);
+    store_sc(1);
+    stage_barrier();
+    if (g + 2 < G) issue(0);
     compute(1);
-    finish_stage();
-    if (g + 2 < G) store(ra, 0);
-    lds_barrier();
+    finish_stage(1);
+    if (g + 2 < G) store_sc(0);
+    stage_barrier();
   }
   if (g < G) {
     compute(0);
-    finish_stage();
+    finish_stage(0);
   }
 }
 

@@ -306,6 +306,26 @@ __device__ __forceinline__ void wait_vmem() {
 // their maximum).
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+// Workgroup barrier after this wave's LDS accesses only (lgkmcnt(0)), for
+// LDS that is not being filled by LDS-DMA: unlike lds_barrier's fence it does
+// not wait for DMA loads in flight to other LDS.  The empty asm statements
+// keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_only_barrier() {
+  wait_lds();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier after all of this wave's vector memory operations
+// (LDS-DMA loads included) and LDS accesses have completed.
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0), expcnt at its maximum
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Bare workgroup barrier for a phase-scheduled loop: the compiler may move
 // no instruction across it (sched_barrier) and no memory access (empty asm
 // with a memory clobber); no fence and no wait.
