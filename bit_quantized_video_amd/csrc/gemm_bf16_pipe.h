@@ -113,6 +113,19 @@ __device__ __forceinline__ void gemm_bf16_pipe_body(
       st.ws = __builtin_amdgcn_raw_buffer_load_b16(wsres, (int)svoff, kt * 4, 0);
     }
   };
+  // LDS-DMA of stage kt (bf16 operands) into buffer buf: instruction p of
+  // wave w fills LDS rows 64 p + 8 w + (lane >> 3), slot lane & 7, with the
+  // row's 16-byte chunk (lane & 7) ^ swz128(row), the layout the fragment
+  // reads expect; the swizzle depends on the lane and the wave only.
+  const int drow = 8 * wave + (lane >> 3);
+  const uint32_t dvoff = (uint32_t)(drow * 2 * K + 16 * ((lane & 7) ^ swz128(drow)));
+  auto issue_dma = [&](int kt, int buf) {
+    uint8_t* base = smem + buf * SB + 1024 * wave;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) lds_dma16(xres, base + 8192 * p, dvoff, kt * 128 + p * 64 * 2 * K);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) lds_dma16(wres, base + XB + 8192 * p, dvoff, kt * 128 + p * 64 * 2 * K);
+  };
   auto store = [&](const Stage& st, int buf) {
     uint8_t* lx = smem + buf * SB;
     uint8_t* lw = lx + XB;
@@ -246,6 +259,26 @@ __device__ __forceinline__ void gemm_bf16_pipe_body(
     grouped_tile(seq.first + t * seq.stride, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     open_tile(m0, n0);
+    if constexpr (SRC == kSrcBf16) {
+      // bf16 operands need no decoding: stage kt + 1 goes straight into LDS
+      // by LDS-DMA while stage kt is computed, and the stage barrier waits
+      // for this wave's DMA loads (vmcnt) and LDS reads.
+      int kt = 0;
+      issue_dma(0, 0);
+      stage_barrier();
+      for (; kt + 1 < nk; kt += 2) {
+        issue_dma(kt + 1, 1);
+        compute(0);
+        stage_barrier();
+        if (kt + 2 < nk) issue_dma(kt + 2, 0);
+        compute(1);
+        stage_barrier();
+      }
+      if (kt < nk) compute(0);
+      epilogue(m0, n0);
+      zero_acc();
+      continue;
+    }
     Stage ra, rb;
     load(ra, 0);
     if (nk > 1) load(rb, 1);
