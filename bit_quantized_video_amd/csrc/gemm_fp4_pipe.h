@@ -99,15 +99,18 @@ __device__ __forceinline__ void gemm_fp4mx_pipe_body(
   // buffer buf, then this thread's 16 scale bytes into a register (sc), the
   // last of the wave's 9 vector memory operations.
   uint4 sc;
+  int l_rev = 0;  // this tile's K stages in descending order (every other tile)
   auto issue = [&](int buf) {
     uint8_t* base = smem + buf * SB + 1024 * wave;
+    const int kt = l_rev ? nk - 1 - l_kt : l_kt;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) lds_dma16(xres, base + 8192 * p, dvoff, l_kt * (BK / 2) + p * 64 * ld);
+    for (int p = 0; p < 4; ++p) lds_dma16(xres, base + 8192 * p, dvoff, kt * (BK / 2) + p * 64 * ld);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) lds_dma16(wres, base + XB + 8192 * p, dvoff, l_kt * (BK / 2) + p * 64 * ld);
-    sc = buf_load16(sres, svoff, l_kt * (BK / 16));
+    for (int p = 0; p < 4; ++p) lds_dma16(wres, base + XB + 8192 * p, dvoff, kt * (BK / 2) + p * 64 * ld);
+    sc = buf_load16(sres, svoff, kt * (BK / 16));
     if (++l_kt == nk) {
       l_kt = 0;
+      l_rev ^= 1;
       l_logical += seq.stride;
       if (l_logical < tiles_m * tiles_n) open_tile();
     }

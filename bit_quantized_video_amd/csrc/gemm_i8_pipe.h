@@ -94,7 +94,12 @@ __device__ __forceinline__ void gemm_i8i4_pipe_body(
   const uint32_t xvoff = (uint32_t)(xrow * K + 16 * ((lane & 7) ^ swz128(xrow)));
   const uint32_t wvoff = (uint32_t)(wrow * ldw + 16 * ((lane & 3) ^ swz64(wrow)));
   __amdgpu_buffer_rsrc_t xres, wres;  // over the current tile's rows
-  auto issue = [&](int kt, int buf) {
+  // Every other tile of a workgroup runs its K stages in descending order,
+  // so it starts on the K slices the tiles before it loaded last, which are
+  // still in this XCD's L2 (int32 sums do not depend on the order).
+  int krev = 0;
+  auto issue = [&](int kt0, int buf) {
+    const int kt = krev ? nk - 1 - kt0 : kt0;
     uint8_t* base = smem + buf * SB + 1024 * wave;
 #pragma unroll
     for (int p = 0; p < C::XI; ++p) lds_dma16(xres, base + 8192 * p, xvoff, kt * BK + p * 64 * K);
@@ -278,6 +283,7 @@ __device__ __forceinline__ void gemm_i8i4_pipe_body(
   // start for group 1, at the end for group 0).
   for (int t = 0; t < seq.count; ++t) {
     const int logical = seq.first + t * seq.stride;
+    krev = t & 1;
     {
       int tm, tn;
       grouped_tile(logical, tiles_m, tiles_n, tm, tn);
