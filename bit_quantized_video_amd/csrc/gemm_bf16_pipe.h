@@ -30,13 +30,14 @@ __device__ __forceinline__ void decode_nvfp4x16(const uint2 codes, uint32_t e, u
 // ---------------------------------------------------------------------------
 // Pipelined kernel for K % 64 == 0: 256 x 256 tile, 8 waves as 2 (tokens) x
 // 4 (features), each 128 x 64 (4 x 2 subtiles of 32 x 32), 64 K per stage,
-// two register sets prefetching the next two stages through buffer loads
-// (rows past M or N read as zero), double-buffered LDS, LDS-only barriers,
-// a persistent tile loop and bf16 output tiles staged in LDS -- the
-// structure of the INT8 kernel.  LDS holds bf16: 128-byte rows per
-// stage (swz128), substep s (16 K) giving lane half h the 16-byte chunk
-// 2s + h.  NVFP4 operands are decoded to exact bf16 when their registers are
-// written to LDS, once per workgroup rather than once per wave.
+// double-buffered LDS, a persistent tile loop and bf16 output tiles staged
+// in LDS -- the structure of the INT8 kernel.  bf16 operands go into LDS by
+// LDS-DMA one stage ahead; NVFP4 operands come through two register sets
+// prefetching the next two stages (buffer loads: rows past M or N read as
+// zero, LDS-only barriers) and are decoded to exact bf16 when the registers
+// are written to LDS, once per workgroup rather than once per wave.  LDS
+// holds bf16: 128-byte rows per stage (swz128), substep s (16 K) giving lane
+// half h the 16-byte chunk 2s + h.
 // LDS: two 64 KB stages, or one staged 256 x 256 bf16 output tile with a
 // padded row pitch, whichever is larger.
 constexpr int kBf16OutPitch = 256 * 2 + 16;

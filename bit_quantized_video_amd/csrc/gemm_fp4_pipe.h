@@ -18,11 +18,11 @@ __device__ __forceinline__ uint32_t e4m3_pow2_to_e8m0(uint32_t b) {
 
 // ---------------------------------------------------------------------------
 // Pipelined kernel for K % 256 == 0: the INT8 kernel's structure (256 x 256
-// tiles, 8 waves as 2 x 4 of 128 x 64, a persistent tile loop, buffer loads
-// prefetching across tile boundaries, double-buffered LDS, LDS-only
-// barriers) with 256 K per stage and one register set: stage g + 1 is
-// loaded while stage g is computed (a second set would not fit beside the
-// unrolled substeps' fragments in 256 VGPRs).  Per stage:
+// tiles, 8 waves as 2 x 4 of 128 x 64, a persistent tile loop, prefetch
+// across tile boundaries, double-buffered LDS) with 256 K per stage: stage
+// g + 1 is loaded while stage g is computed, its code bytes by LDS-DMA into
+// the other buffer and its scale bytes through a register (they are
+// converted to E8M0 on the way into LDS).  Per stage:
 // 128-byte code rows (swz128; substep s of 64 K gives lane half h chunk
 // 2s + h) and, per row, the stage's eight E8M0 bytes (one per 32 K, from the
 // even E4M3 byte of each MX pair) stored as two words, [g0 g2 g4 g6] and
