@@ -147,7 +147,9 @@ def gemm_bytes(M, N, K, prec, fp4):
         a, b = M * K + 4 * M, N * K // 2 + 4 * N
     elif prec == "bf16":
         a, b = 2 * M * K, 2 * N * K
-    else:  # NVFP4: packed E2M1 + one scale byte per 16 elements (the MX kernel reads one per 32)
+    elif fp4 == "nvfp4":  # plain NVFP4: both operands' exact bf16 values
+        a, b = 2 * M * K, 2 * N * K
+    else:  # NVFP4 on the FP4 MFMA: packed E2M1 + one scale byte per 16 elements (MX: one per 32)
         g = 32 if fp4 == "mx" else 16
         a, b = M * K // 2 + M * K // g, N * K // 2 + N * K // g
     return a + b + 2 * M * N
@@ -217,7 +219,9 @@ def build_schedule(args, hdq, synth):
             prev_out = [synth.device_noisy_copy(xs[(t + 1) % 2], float(s_levels[b, li, t]), gen)
                         for t in range(args.timesteps)]
             w = synth.device_gaussian((N, K), 0.02, gen, dev)
-            W = {r: hdq.LinearWeights(w, HB, fp4_fmt=f) for r, f in recipes.items()}
+            # plain NVFP4 also keeps its weights' exact bf16 values: the exact
+            # GEMM then reads both operands decoded (same output bits)
+            W = {r: hdq.LinearWeights(w, HB, fp4_fmt=f, fp4_decoded=(r == "nvfp4")) for r, f in recipes.items()}
             layers.append(dict(name=name, K=K, N=N, x=x, xs=xs, prev_out=prev_out, W=W))
         blocks.append(layers)
         if b % 6 == 5 or b == args.blocks - 1:
@@ -229,7 +233,7 @@ def build_schedule(args, hdq, synth):
     for name, K, N in synth.SCHEDULE_LAYERS:
         shared.append(dict(
             xq8=hdq.QuantizedTensor(hdq.FMT_INT8_ROW, M, K, HB, dev),
-            xq4={r: hdq.QuantizedTensor(f, M, K, HB, dev) for r, f in recipes.items()},
+            xq4={r: hdq.QuantizedTensor(f, M, K, HB, dev, decoded=(r == "nvfp4")) for r, f in recipes.items()},
             y=torch.empty(M, N, dtype=torch.bfloat16, device=dev)))
     ws_sel = torch.empty(hdq.workspace_bytes(hdq.OP_SELECT, M, 12288, M * 12288), dtype=torch.uint8,
                          device=dev)

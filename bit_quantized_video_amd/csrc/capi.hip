@@ -116,8 +116,17 @@ hipError_t enqueue_quantize(const void* x, const hdq_qtensor& q, const float* am
     if (e != hipSuccess) return e;
     amax = slot;
   }
-  return launch_quant_nvfp4(xb, q.rows, q.cols, q.had_block, q.fmt, amax,
-                            static_cast<uint8_t*>(q.codes), q.blk_scale, q.tensor_scale, gate, want, s);
+  hipError_t e = launch_quant_nvfp4(xb, q.rows, q.cols, q.had_block, q.fmt, amax,
+                                   static_cast<uint8_t*>(q.codes), q.blk_scale, q.tensor_scale, gate, want, s);
+  if (e != hipSuccess || q.dec == nullptr) return e;
+  return launch_dq_decode_w(static_cast<const uint8_t*>(q.codes), q.blk_scale, q.rows, q.cols,
+                            static_cast<uint16_t*>(q.dec), s, gate, want);
+}
+
+// The plain-NVFP4 operands' decoded bf16 copies, when both are given and the
+// bf16 body takes the shape (the one-launch kernel's shape rule implies it).
+bool use_decoded(int32_t fmt, const hdq_qtensor& xq, const hdq_qtensor& wq, int64_t M, int64_t N, int64_t K) {
+  return fmt == HDQ_FMT_NVFP4 && xq.dec != nullptr && wq.dec != nullptr && nvfp4_decoded_applies(M, N, K);
 }
 
 }  // namespace
@@ -333,12 +342,13 @@ int hdq_linear_dispatch(const int32_t* decision_dev, const void* x, const hdq_qt
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   const uint16_t* wb = static_cast<const uint16_t*>(w->w_bf16);
+  const bool dec = use_decoded(f, *xq4, w->w_fp4, M, N, K);
   hipError_t e = launch_gemm_dispatch(
       decision_dev, static_cast<const int8_t*>(xq8->codes), xq8->row_scale,
       static_cast<const uint8_t*>(w->w_int4.codes), w->w_int4.row_scale,
-      static_cast<const uint8_t*>(xq4->codes), xq4->blk_scale, xq4->tensor_scale,
-      static_cast<const uint8_t*>(w->w_fp4.codes), w->w_fp4.blk_scale, w->w_fp4.tensor_scale,
-      f, xb, wb, y, y_dtype, M, N, K, s);
+      static_cast<const uint8_t*>(dec ? xq4->dec : xq4->codes), xq4->blk_scale, xq4->tensor_scale,
+      static_cast<const uint8_t*>(dec ? w->w_fp4.dec : w->w_fp4.codes), w->w_fp4.blk_scale,
+      w->w_fp4.tensor_scale, dec ? kNvfp4Decoded : f, xb, wb, y, y_dtype, M, N, K, s);
   if (e == hipSuccess) return HDQ_OK;
   if (e != hipErrorNotSupported) return HDQ_ERR_HIP;
   // shapes the pipelined bodies do not take: the three gated GEMMs
@@ -346,11 +356,17 @@ int hdq_linear_dispatch(const int32_t* decision_dev, const void* x, const hdq_qt
                        static_cast<const uint8_t*>(w->w_int4.codes), w->w_int4.row_scale, y, y_dtype,
                        M, N, K, decision_dev, HDQ_PREC_INT8, s) != hipSuccess)
     return HDQ_ERR_HIP;
-  auto fp4 = fp4_gemm_for(f);
-  if (fp4(static_cast<const uint8_t*>(xq4->codes), xq4->blk_scale, xq4->tensor_scale,
-          static_cast<const uint8_t*>(w->w_fp4.codes), w->w_fp4.blk_scale, w->w_fp4.tensor_scale, y,
-          y_dtype, M, N, K, decision_dev, HDQ_PREC_NVFP4, s) != hipSuccess)
+  if (dec) {
+    if (launch_gemm_nvfp4_decoded(static_cast<const uint16_t*>(xq4->dec), xq4->tensor_scale,
+                                  static_cast<const uint16_t*>(w->w_fp4.dec), w->w_fp4.tensor_scale, y, y_dtype,
+                                  M, N, K, decision_dev, HDQ_PREC_NVFP4, s) != hipSuccess)
+      return HDQ_ERR_HIP;
+  } else if (fp4_gemm_for(f)(static_cast<const uint8_t*>(xq4->codes), xq4->blk_scale, xq4->tensor_scale,
+                             static_cast<const uint8_t*>(w->w_fp4.codes), w->w_fp4.blk_scale,
+                             w->w_fp4.tensor_scale, y, y_dtype, M, N, K, decision_dev, HDQ_PREC_NVFP4,
+                             s) != hipSuccess) {
     return HDQ_ERR_HIP;
+  }
   return hip_status(launch_gemm_bf16(xb, wb, y, y_dtype, M, N, K, decision_dev, HDQ_PREC_BF16, s));
 }
 
@@ -405,13 +421,14 @@ int hdq_linear_dispatch_delta(const int32_t* decision_dev, const void* x, const 
   // the one-launch kernel only (the difference runs on its extra workgroups)
   if (K % 256 != 0 || M * 2 * K >= (1ll << 31) || N * 2 * K >= (1ll << 31)) return HDQ_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool dec = use_decoded(f, *xq4, w->w_fp4, M, N, K);
   return hip_status(launch_gemm_dispatch(
       decision_dev, static_cast<const int8_t*>(xq8->codes), xq8->row_scale,
       static_cast<const uint8_t*>(w->w_int4.codes), w->w_int4.row_scale,
-      static_cast<const uint8_t*>(xq4->codes), xq4->blk_scale, xq4->tensor_scale,
-      static_cast<const uint8_t*>(w->w_fp4.codes), w->w_fp4.blk_scale, w->w_fp4.tensor_scale, f,
-      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w->w_bf16), y, y_dtype, M, N, K, s,
-      &dw));
+      static_cast<const uint8_t*>(dec ? xq4->dec : xq4->codes), xq4->blk_scale, xq4->tensor_scale,
+      static_cast<const uint8_t*>(dec ? w->w_fp4.dec : w->w_fp4.codes), w->w_fp4.blk_scale,
+      w->w_fp4.tensor_scale, dec ? kNvfp4Decoded : f, static_cast<const uint16_t*>(x),
+      static_cast<const uint16_t*>(w->w_bf16), y, y_dtype, M, N, K, s, &dw));
 }
 
 // ---- DeltaQuant ----------------------------------------------------------
@@ -613,6 +630,7 @@ int hdq_linear(int32_t precision, const int32_t* decision_dev, const void* x,
       q.row_scale = reinterpret_cast<float*>(cursor + align_up((size_t)(M * K)));
       q.blk_scale = nullptr;
       q.tensor_scale = nullptr;
+      q.dec = nullptr;
       cursor += qtensor_bytes(M, K, HDQ_FMT_INT8_ROW);
       if ((st = check_quant_shape(M, K, q.had_block, q.fmt)) != HDQ_OK) return st;
       if ((e = enqueue_quantize(x, q, nullptr, nullptr, gate, HDQ_PREC_INT8, s)) != hipSuccess)
@@ -637,6 +655,7 @@ int hdq_linear(int32_t precision, const int32_t* decision_dev, const void* x,
       q.blk_scale = cursor + align_up((size_t)(M * K / 2));
       q.tensor_scale = reinterpret_cast<float*>(q.blk_scale + align_up((size_t)(M * K / 16)));
       q.row_scale = nullptr;
+      q.dec = nullptr;
       cursor += qtensor_bytes(M, K, f);
       uint8_t* pre = nullptr;
       if (x_amax == nullptr) {
@@ -649,8 +668,13 @@ int hdq_linear(int32_t precision, const int32_t* decision_dev, const void* x,
     }
     const uint8_t* xc = static_cast<const uint8_t*>(q.codes);
     const uint8_t* wc = static_cast<const uint8_t*>(w->w_fp4.codes);
-    e = fp4_gemm_for(f)(xc, q.blk_scale, q.tensor_scale, wc, w->w_fp4.blk_scale, w->w_fp4.tensor_scale,
-                        y, y_dtype, M, N, K, gate, HDQ_PREC_NVFP4, s);
+    if (use_decoded(f, q, w->w_fp4, M, N, K))
+      e = launch_gemm_nvfp4_decoded(static_cast<const uint16_t*>(q.dec), q.tensor_scale,
+                                    static_cast<const uint16_t*>(w->w_fp4.dec), w->w_fp4.tensor_scale, y,
+                                    y_dtype, M, N, K, gate, HDQ_PREC_NVFP4, s);
+    else
+      e = fp4_gemm_for(f)(xc, q.blk_scale, q.tensor_scale, wc, w->w_fp4.blk_scale, w->w_fp4.tensor_scale,
+                          y, y_dtype, M, N, K, gate, HDQ_PREC_NVFP4, s);
     if (e != hipSuccess) return HDQ_ERR_HIP;
   }
   if (run_bf16) {

@@ -139,7 +139,7 @@ __global__ __launch_bounds__(256) void k_gemm_bf16mfma(
     __syncthreads();
   }
 
-  const float scale = (SRC == kSrcNvfp4) ? (*xts) * (*wts) : 1.0f;
+  const float scale = (SRC == kSrcNvfp4 || xts != nullptr) ? (*xts) * (*wts) : 1.0f;
   const bool vec = (N & 3) == 0;
 #pragma unroll
   for (int i = 0; i < WM; ++i) {
@@ -227,6 +227,15 @@ hipError_t launch_gemm_nvfp4_bf16(const uint8_t* xc, const uint8_t* xs, const fl
                                   void* y, int out_dtype, int64_t M, int64_t N, int64_t K,
                                   const int32_t* decision, int32_t want, hipStream_t s) {
   return launch_bf16mfma<kSrcNvfp4>(xc, xs, xts, wc, ws, wts, y, out_dtype, M, N, K, decision, want, s);
+}
+
+bool nvfp4_decoded_applies(int64_t M, int64_t N, int64_t K) { return pipe_ok<kSrcBf16>(M, N, K); }
+
+hipError_t launch_gemm_nvfp4_decoded(const uint16_t* xd, const float* xts, const uint16_t* wd,
+                                     const float* wts, void* y, int out_dtype, int64_t M, int64_t N,
+                                     int64_t K, const int32_t* decision, int32_t want, hipStream_t s) {
+  if (!nvfp4_decoded_applies(M, N, K)) return hipErrorNotSupported;
+  return launch_bf16mfma<kSrcBf16>(xd, nullptr, xts, wd, nullptr, wts, y, out_dtype, M, N, K, decision, want, s);
 }
 
 hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* w, void* y, int out_dtype,

@@ -188,7 +188,8 @@ __device__ __forceinline__ void gemm_bf16_pipe_body(
     }
   };
 
-  const float scale = (SRC == kSrcNvfp4) ? (*xts) * (*wts) : 1.0f;
+  // NVFP4 (decoded here or beforehand): the two tensor scales; bf16: none.
+  const float scale = (SRC == kSrcNvfp4 || xts != nullptr) ? (*xts) * (*wts) : 1.0f;
   auto epilogue = [&](int m0, int n0) {
     if constexpr (OUT == kOutBf16) {
       // Stage the bf16 tile in LDS (both pipeline buffers are free once every

@@ -51,6 +51,9 @@ struct DeltaWork {
 };
 
 enum QFmt : int { kInt8Row = 0, kInt4Row = 1, kNvfp4 = 2, kNvfp4Mx = 3, kNvfp4P2 = 4 };
+// The one-launch GEMM's NVFP4 body for plain NVFP4 operands given decoded to
+// bf16 (not a tensor format).
+constexpr int kNvfp4Decoded = 16;
 enum Prec : int { kPrecNvfp4 = 0, kPrecInt8 = 1, kPrecBf16 = 2 };
 enum OutDtype : int { kOutF32 = 0, kOutBf16 = 1, kOutI32 = 2 };
 
@@ -122,6 +125,15 @@ hipError_t launch_gemm_nvfp4_bf16(const uint8_t* xc, const uint8_t* xs, const fl
                                   const uint8_t* wc, const uint8_t* ws, const float* wts,
                                   void* y, int out_dtype, int64_t M, int64_t N, int64_t K,
                                   const int32_t* decision, int32_t want, hipStream_t s);
+// The same product from operands decoded exactly to bf16 beforehand (xd, wd:
+// bf16 [M, K], [N, K]): the bf16 GEMM body with the tensor scales.  Only
+// where the pipelined bf16 body takes the shape (nvfp4_decoded_applies; it
+// then runs the exact NVFP4 kernel's MFMAs in its order): otherwise
+// hipErrorNotSupported.
+bool nvfp4_decoded_applies(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_nvfp4_decoded(const uint16_t* xd, const float* xts, const uint16_t* wd,
+                                     const float* wts, void* y, int out_dtype, int64_t M, int64_t N,
+                                     int64_t K, const int32_t* decision, int32_t want, hipStream_t s);
 // MX-compatible NVFP4 on the block-scaled FP4 MFMA.
 hipError_t launch_gemm_nvfp4_mx(const uint8_t* xc, const uint8_t* xs, const float* xts,
                                 const uint8_t* wc, const uint8_t* ws, const float* wts,
@@ -167,9 +179,10 @@ struct CoreAdd {
 hipError_t launch_dq_quantize(const uint16_t* x, int64_t K, const DqGrid& g, int fmt, uint8_t* ccodes,
                               float* cscale, uint16_t* core_bf16, uint32_t* damax_bits, uint8_t* codes,
                               uint8_t* blk_scale, float* tensor_scale, hipStream_t s);
-// NVFP4 weights [N, K] to bf16 E2M1 x block-scale values.
+// An NVFP4 tensor [N, K] to bf16 E2M1 x block-scale values (exact); with a
+// gate, only when *gate == want.
 hipError_t launch_dq_decode_w(const uint8_t* codes, const uint8_t* blk, int64_t N, int64_t K, uint16_t* out,
-                              hipStream_t s);
+                              hipStream_t s, const int32_t* gate = nullptr, int32_t want = 0);
 // Whether launch_gemm_fp4_core_add takes a shape: the pipelined FP4 body
 // (MX or per-16 power-of-two format, K % 256 == 0, 32-bit operand offsets)
 // with N % 4 == 0.

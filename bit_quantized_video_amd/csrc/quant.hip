@@ -854,7 +854,9 @@ hipError_t launch_dq_quantize(const uint16_t* x, int64_t K, const DqGrid& g, int
 // significant bits), the tensor scale left out: the core GEMM's operand.
 __global__ __launch_bounds__(256) void k_dq_decode_w(const uint8_t* __restrict__ codes,
                                                      const uint8_t* __restrict__ blk, int64_t nch,
-                                                     uint16_t* __restrict__ out) {
+                                                     uint16_t* __restrict__ out,
+                                                     const int32_t* __restrict__ gate, int32_t want) {
+  if (gate != nullptr && *gate != want) return;
   const uint32_t* cv = reinterpret_cast<const uint32_t*>(codes);
   uint4* ov = reinterpret_cast<uint4*>(out);
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nch; i += (int64_t)gridDim.x * 256) {
@@ -871,12 +873,12 @@ __global__ __launch_bounds__(256) void k_dq_decode_w(const uint8_t* __restrict__
 }
 
 hipError_t launch_dq_decode_w(const uint8_t* codes, const uint8_t* blk, int64_t N, int64_t K, uint16_t* out,
-                              hipStream_t s) {
+                              hipStream_t s, const int32_t* gate, int32_t want) {
   const int64_t nch = N * K / 8;
   int64_t blocks = (nch + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(k_dq_decode_w, dim3((unsigned)blocks), dim3(256), 0, s, codes, blk, nch, out);
+  hipLaunchKernelGGL(k_dq_decode_w, dim3((unsigned)blocks), dim3(256), 0, s, codes, blk, nch, out, gate, want);
   return hipGetLastError();
 }
 

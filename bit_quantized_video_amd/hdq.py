@@ -42,7 +42,7 @@ class QTensorDesc(_c.Structure):
     """hdq_qtensor."""
     _fields_ = [("fmt", _c.c_int32), ("had_block", _c.c_int32), ("rows", _c.c_int64),
                 ("cols", _c.c_int64), ("codes", _p), ("row_scale", _p), ("blk_scale", _p),
-                ("tensor_scale", _p)]
+                ("tensor_scale", _p), ("dec", _p)]
 
 
 class DeltaSlice(_c.Structure):
@@ -217,11 +217,13 @@ def _workspace(ws, nbytes, device):
 
 
 class QuantizedTensor:
-    """A quantized tensor: torch buffers plus the hdq_qtensor descriptor."""
+    """A quantized tensor: torch buffers plus the hdq_qtensor descriptor.
+    decoded (NVFP4 formats): also a bf16 [rows, cols] buffer for the codes'
+    exact values, which hdq_quantize fills and the plain-NVFP4 GEMM reads."""
 
-    def __init__(self, fmt, rows, cols, had_block, device):
+    def __init__(self, fmt, rows, cols, had_block, device, decoded=False):
         self.fmt, self.rows, self.cols, self.had_block = fmt, rows, cols, had_block
-        self.row_scale = self.blk_scale = self.tensor_scale = None
+        self.row_scale = self.blk_scale = self.tensor_scale = self.dec = None
         if fmt == FMT_INT8_ROW:
             self.codes = torch.empty(rows, cols, dtype=torch.int8, device=device)
         else:
@@ -231,10 +233,13 @@ class QuantizedTensor:
         else:
             self.blk_scale = torch.empty(rows, cols // 16, dtype=torch.uint8, device=device)
             self.tensor_scale = torch.empty(1, dtype=torch.float32, device=device)
+            if decoded:
+                self.dec = torch.empty(rows, cols, dtype=torch.bfloat16, device=device)
 
     def desc(self):
         return QTensorDesc(self.fmt, self.had_block, self.rows, self.cols, _ptr(self.codes),
-                           _ptr(self.row_scale), _ptr(self.blk_scale), _ptr(self.tensor_scale))
+                           _ptr(self.row_scale), _ptr(self.blk_scale), _ptr(self.tensor_scale),
+                           _ptr(self.dec))
 
 
 def select_precision(prev_in, prev_out, cur_in, had_block=0, delta_thresh=0.1, ratio_thresh=50.0,
@@ -370,12 +375,14 @@ def select_quantize_int8_noalloc(delta_sums, cur_in, had_block, decision, stats,
     return decision, stats, out
 
 
-def quantize(x, had_block, fmt, tensor_amax=None, out=None, ws=None, stream=None, decision=None):
+def quantize(x, had_block, fmt, tensor_amax=None, out=None, ws=None, stream=None, decision=None,
+             decoded=False):
     """hdq_quantize: rotate + quantize a bf16 [rows, cols] tensor (only when
-    the device decision matches the format's precision, if one is given)."""
+    the device decision matches the format's precision, if one is given).
+    decoded: a new output also gets the NVFP4 codes' exact bf16 values."""
     x = _bf16(x, "x")
     rows, cols = x.shape
-    out = QuantizedTensor(fmt, rows, cols, had_block, x.device) if out is None else out
+    out = QuantizedTensor(fmt, rows, cols, had_block, x.device, decoded) if out is None else out
     d = out.desc()
     nbytes = workspace_bytes(OP_QUANTIZE, rows, cols, 0, fmt) if tensor_amax is None else 0
     ws = _workspace(ws, nbytes, x.device)
@@ -472,18 +479,21 @@ def dq_linear(a, w_fp4, w_dec=None, y=None, y_dtype=DTYPE_BF16, ws=None, stream=
 class LinearWeights:
     """A linear layer's weights in every form a precision may need:
     bf16 (unrotated, for the full-precision fallback), INT4 per output
-    channel, and NVFP4 (or its MX-compatible variant)."""
+    channel, and NVFP4 (or its MX-compatible variant).  fp4_decoded: the
+    NVFP4 weights also as their exact bf16 values (N x K x 2 bytes), which
+    the plain-NVFP4 GEMM reads when the activations carry theirs too."""
 
-    def __init__(self, w_bf16, had_block, fp4_fmt=FMT_NVFP4, keep_bf16=True, stream=None):
+    def __init__(self, w_bf16, had_block, fp4_fmt=FMT_NVFP4, keep_bf16=True, stream=None, fp4_decoded=False):
         w_bf16 = _bf16(w_bf16, "w")
         self.N, self.K = w_bf16.shape
         self.had_block = had_block
         self.w_bf16 = w_bf16 if keep_bf16 else None
         self.w_int4 = quantize(w_bf16, had_block, FMT_INT4_ROW, stream=stream)
-        self.w_fp4 = quantize(w_bf16, had_block, fp4_fmt, stream=stream) if fp4_fmt is not None else None
+        self.w_fp4 = (quantize(w_bf16, had_block, fp4_fmt, stream=stream, decoded=fp4_decoded)
+                      if fp4_fmt is not None else None)
 
     def desc(self):
-        empty = QTensorDesc(-1, 0, 0, 0, None, None, None, None)
+        empty = QTensorDesc(-1, 0, 0, 0, None, None, None, None, None)
         return WeightsDesc(self.N, self.K, _ptr(self.w_bf16), self.w_int4.desc(),
                            self.w_fp4.desc() if self.w_fp4 is not None else empty)
 

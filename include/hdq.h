@@ -118,6 +118,13 @@ typedef struct hdq_qtensor {
     float *row_scale;     /* device, INT8/INT4 only (may be NULL otherwise)  */
     uint8_t *blk_scale;   /* device, NVFP4 formats only                      */
     float *tensor_scale;  /* device fp32[1], NVFP4 formats only              */
+    void *dec;            /* NULL, or (NVFP4 formats) device bf16 [rows,
+                           * cols]: each element's E2M1 value times its E4M3
+                           * block scale, without the tensor scale -- exact in
+                           * bf16.  hdq_quantize fills it when given; with
+                           * plain NVFP4 on both operands of a GEMM the exact
+                           * NVFP4 product reads its operands from it.
+                           * Ignored for the INT formats.                    */
 } hdq_qtensor;
 
 /* A linear layer's weights in every form a precision may need.  Members a
@@ -267,7 +274,9 @@ int hdq_select_quantize_int8_noalloc(const double *delta_sums_dev, int64_t delta
  *                 formats; not allowed with INT4_ROW), so one enqueued call
  *                 serves a device-side decision without a host round trip.
  *   out         : host struct with caller-allocated device buffers sized for
- *                 the format; fmt, had_block, rows, cols are written.
+ *                 the format; fmt, had_block, rows, cols are written.  For
+ *                 the NVFP4 formats a non-NULL out->dec also receives the
+ *                 codes' exact bf16 values (gated like the codes).
  * Rows whose max |rotated value| is below 2^-100 get zero codes and a zero
  * scale; an NVFP4 tensor whose amax is below 2^-100 gets s_t = 0 and zero
  * codes and scale bytes.
@@ -303,7 +312,11 @@ int hdq_quantize(const void *x, int64_t rows, int64_t cols, int32_t had_block, i
  *                 N, w_fp4.fmt) (0 when xq is given for INT8).
  * INT8:  acc = sum_k qx*qw (exact int32); y = fl32(fl32(acc * sx[m]) * sw[n]).
  * NVFP4: y = s_tx * s_tw * sum over 16-blocks of E_x E_w sum_k e2m1 e2m1,
- *        float32 accumulation.
+ *        float32 accumulation.  Plain NVFP4 (HDQ_FMT_NVFP4) runs on bf16
+ *        MFMAs: when xq->dec and w->w_fp4.dec are both given the GEMM reads
+ *        those exact bf16 values, otherwise it decodes the codes as it
+ *        stages them -- the same products in the same order, so the same
+ *        output bits.
  * BF16:  y = x w^T with the unrotated bf16 operands, float32 accumulation.
  */
 int hdq_linear(int32_t precision, const int32_t *decision_dev, const void *x,
@@ -321,6 +334,8 @@ int hdq_linear(int32_t precision, const int32_t *decision_dev, const void *x,
  * hdq_linear(P, decision_dev, x or xq, ...) of the decided P, bit for bit.
  * One kernel reads the decision and runs that GEMM (K a multiple of 256 and
  * 2 * K * max(M, N) < 2^31); other shapes enqueue the three gated GEMMs.
+ * Plain NVFP4 with xq4->dec and w->w_fp4.dec given reads the decoded
+ * operands, as hdq_linear does.
  * y_dtype F32 or BF16.  No workspace.
  */
 int hdq_linear_dispatch(const int32_t *decision_dev, const void *x, const hdq_qtensor *xq8,

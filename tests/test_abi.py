@@ -34,6 +34,42 @@ def test_header_declares_the_boundary():
         assert fn in names
 
 
+def test_binding_structs_match_the_header(hdq, tmp_path):
+    """Every struct the binding passes has the header's members, in order, at
+    the offsets a C compiler gives them (gcc on the header itself)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not found")
+    structs = {"hdq_qtensor": hdq.QTensorDesc, "hdq_weights": hdq.WeightsDesc,
+               "hdq_delta_slice": hdq.DeltaSlice, "hdq_dq_grid": hdq.DqGridDesc}
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "hdq.h"', "int main(void) {"]
+    for cname, cls in structs.items():
+        body = re.search(r"typedef struct " + cname + r" \{(.*?)\} " + cname + ";", text, re.S).group(1)
+        members = []
+        for decl in body.split(";"):
+            decl = decl.strip()
+            if decl:
+                head, *rest = decl.split(",")
+                members.append(head.split()[-1].lstrip("*"))
+                members += [r.strip().lstrip("*") for r in rest]
+        assert members == [f[0] for f in cls._fields_], cname
+        lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
+        for m in members:
+            lines.append(f'printf("{cname}.{m} %zu\\n", offsetof({cname}, {m}));')
+    lines.append("return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
+    got = dict(line.split() for line in subprocess.check_output([str(exe)], text=True).splitlines())
+    for cname, cls in structs.items():
+        assert int(got[cname]) == ctypes.sizeof(cls), cname
+        for m, _ in cls._fields_:
+            assert int(got[f"{cname}.{m}"]) == getattr(cls, m).offset, (cname, m)
+
+
 def test_library_exports_every_declared_symbol(hdq):
     lib = ctypes.CDLL(hdq.LIB_PATH)
     for fn in declared_functions():
