@@ -52,6 +52,7 @@ KINDS = OrderedDict([
     ("quant_nvfp4_mx", r"k_quant_nvfp4<3(, \d+)?>"),
     ("quant_nvfp4_p2", r"k_quant_nvfp4<4(, \d+)?>"),
     ("quant_nvfp4", r"k_quant_nvfp4<2(, \d+)?>"),
+    ("decode_nvfp4", r"k_dq_decode_w"),
     ("gemm_int8", r"k_gemm_i8i4(_pipe)?<[\d, ]*1>"),
     ("gemm_nvfp4_mx", r"k_gemm_fp4mx_pipe<1, false>"),
     ("gemm_nvfp4_p2", r"k_gemm_fp4mx_pipe<1, true>"),
@@ -63,7 +64,7 @@ SOURCES = {
     "delta_sums": ["stats.hip"], "select_stats": ["stats.hip"], "select_final": ["stats.hip"],
     "select_final_rows": ["stats.hip"],
     "quant_int8": ["quant.hip"], "quant_nvfp4_mx": ["quant.hip"], "quant_nvfp4": ["quant.hip"],
-    "quant_nvfp4_p2": ["quant.hip"],
+    "quant_nvfp4_p2": ["quant.hip"], "decode_nvfp4": ["quant.hip"],
     "select_quant_int8": ["quant.hip", "stats.hip"],
     "gemm_int8": ["gemm_i8.hip", "gemm_i8_pipe.h", "gemm_dispatch.hip"],
     "gemm_nvfp4_mx": ["gemm_fp4.hip", "gemm_fp4_pipe.h", "gemm_dispatch.hip"],
@@ -75,9 +76,9 @@ SOURCES = {
 # One-launch GEMMs (bf16 output) that run the decided precision: the kind
 # comes from the decision of the layer call (DECISIONS, in call order); the
 # second template argument is the NVFP4 weights' format (2 plain, 3 MX, 4
-# per-16 powers of two).
-DISPATCH = r"k_gemm_dispatch<1, ([234])>"
-FP4_KIND = {"2": "gemm_nvfp4", "3": "gemm_nvfp4_mx", "4": "gemm_nvfp4_p2"}
+# per-16 powers of two; 16 plain from operands decoded to bf16).
+DISPATCH = r"k_gemm_dispatch<1, (2|3|4|16)>"
+FP4_KIND = {"2": "gemm_nvfp4", "3": "gemm_nvfp4_mx", "4": "gemm_nvfp4_p2", "16": "gemm_nvfp4"}
 DECISIONS = None
 
 

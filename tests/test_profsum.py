@@ -62,9 +62,11 @@ def test_one_launch_gemms_take_their_calls_decisions():
         c = P.Classifier()
         mx = "void hdq::k_gemm_dispatch<1, 3>(int const*)"
         plain = "void hdq::k_gemm_dispatch<1, 2>(int const*)"
-        got = [c(mx) for _ in range(5)] + [c(plain) for _ in range(3)]
+        decoded = "void hdq::k_gemm_dispatch<1, 16>(int const*)"   # plain NVFP4 from decoded operands
+        got = [c(mx) for _ in range(5)] + [c(plain) for _ in range(3)] + [c(decoded) for _ in range(2)]
         assert got == ["gemm_int8", "gemm_nvfp4_mx", "gemm_bf16", "gemm_int8", "gemm_int8",
-                       "gemm_int8", "gemm_nvfp4", "gemm_bf16"]
+                       "gemm_int8", "gemm_nvfp4", "gemm_bf16", "gemm_int8", "gemm_nvfp4"]
+        assert P.classify("hdq::k_dq_decode_w(unsigned char const*)") == "decode_nvfp4"
         assert c("void hdq::k_gemm_dispatch<0, 3>(int const*)") is None  # f32 output: not the schedule
     finally:
         P.DECISIONS = None
