@@ -116,11 +116,8 @@ hipError_t enqueue_quantize(const void* x, const hdq_qtensor& q, const float* am
     if (e != hipSuccess) return e;
     amax = slot;
   }
-  hipError_t e = launch_quant_nvfp4(xb, q.rows, q.cols, q.had_block, q.fmt, amax,
-                                   static_cast<uint8_t*>(q.codes), q.blk_scale, q.tensor_scale, gate, want, s);
-  if (e != hipSuccess || q.dec == nullptr) return e;
-  return launch_dq_decode_w(static_cast<const uint8_t*>(q.codes), q.blk_scale, q.rows, q.cols,
-                            static_cast<uint16_t*>(q.dec), s, gate, want);
+  return launch_quant_nvfp4(xb, q.rows, q.cols, q.had_block, q.fmt, amax, static_cast<uint8_t*>(q.codes),
+                            q.blk_scale, q.tensor_scale, gate, want, s, static_cast<uint16_t*>(q.dec));
 }
 
 // The plain-NVFP4 operands' decoded bf16 copies, when both are given and the

@@ -75,11 +75,12 @@ hipError_t launch_quant_int_rows(const uint16_t* x, int64_t rows, int64_t cols, 
                                  void* codes, float* row_scale, const int32_t* decision,
                                  int32_t want, hipStream_t s);
 // NVFP4 / NVFP4_MX: codes uint8 [rows, cols/2], blk_scale uint8 [rows, cols/16],
-// tensor_scale fp32 [1]; amax = device fp32[1] rotated tensor amax.
+// tensor_scale fp32 [1]; amax = device fp32[1] rotated tensor amax; dec:
+// null, or bf16 [rows, cols] for the codes' exact values.
 hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t rows, int64_t cols, int hb, int fmt,
                               const float* amax, uint8_t* codes, uint8_t* blk_scale,
                               float* tensor_scale, const int32_t* decision, int32_t want,
-                              hipStream_t s);
+                              hipStream_t s, uint16_t* dec = nullptr);
 
 // ---- statistics (stats.hip) ----
 constexpr int kStatsMaxBlocks = 1024;
@@ -179,10 +180,9 @@ struct CoreAdd {
 hipError_t launch_dq_quantize(const uint16_t* x, int64_t K, const DqGrid& g, int fmt, uint8_t* ccodes,
                               float* cscale, uint16_t* core_bf16, uint32_t* damax_bits, uint8_t* codes,
                               uint8_t* blk_scale, float* tensor_scale, hipStream_t s);
-// An NVFP4 tensor [N, K] to bf16 E2M1 x block-scale values (exact); with a
-// gate, only when *gate == want.
+// NVFP4 weights [N, K] to bf16 E2M1 x block-scale values.
 hipError_t launch_dq_decode_w(const uint8_t* codes, const uint8_t* blk, int64_t N, int64_t K, uint16_t* out,
-                              hipStream_t s, const int32_t* gate = nullptr, int32_t want = 0);
+                              hipStream_t s);
 // Whether launch_gemm_fp4_core_add takes a shape: the pipelined FP4 body
 // (MX or per-16 power-of-two format, K % 256 == 0, 32-bit operand offsets)
 // with N % 4 == 0.

@@ -355,16 +355,31 @@ __device__ __forceinline__ uint32_t nvfp4_chunk(float (&v)[8], float s_t, float 
          (e2m1x2_encode(v[4] * inv, v[5] * inv) << 16) | (e2m1x2_encode(v[6] * inv, v[7] * inv) << 24);
 }
 
+// Exact bf16 values of one chunk's 8 codes with block-scale byte e: E2M1
+// value x E4M3 value, exact in float32 and in bf16 (at most 6 significant
+// bits), so the top half of the float is the bf16.
+__device__ __forceinline__ uint4 nvfp4_decode_chunk(uint32_t p, uint32_t e) {
+  const float s = e4m3_decode(e);
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t lo = (p >> (8 * j)) & 15u, hi = (p >> (8 * j + 4)) & 15u;
+    o[j] = (__float_as_uint(e2m1_value(lo) * s) >> 16) | ((__float_as_uint(e2m1_value(hi) * s) >> 16) << 16);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 // UNROLL 8-element chunks per lane per iteration, loads issued first; a wave
 // covers UNROLL x 64 consecutive chunks, so every Hadamard block (<= 128)
 // and every 16- or 32-element scale block lies inside aligned lane groups of
 // one wave.  HB > 0: the Hadamard block is HB (the argument is ignored).
-template <int FMT, int HB = 0>
+// DEC: also the codes' exact bf16 values, 16 bytes per chunk, into dec.
+template <int FMT, int HB = 0, bool DEC = false>
 __global__ __launch_bounds__(256) void k_quant_nvfp4(
     const uint16_t* __restrict__ x, int64_t nch, int hb_arg, float c_b,
     const float* __restrict__ amax_ptr, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ blk_scale, float* __restrict__ tensor_scale,
-    const int32_t* __restrict__ decision, int32_t want) {
+    const int32_t* __restrict__ decision, int32_t want, uint16_t* __restrict__ dec) {
   if (decision != nullptr && *decision != want) return;
   const int hb = HB > 0 ? HB : hb_arg;
   constexpr int UNROLL = 2;
@@ -402,15 +417,17 @@ __global__ __launch_bounds__(256) void k_quant_nvfp4(
         cv[idx] = packed;
         // the lane with the even chunk of the 16-element block writes its scale
         if ((idx & 1) == 0) blk_scale[idx >> 1] = (uint8_t)e;
+        if constexpr (DEC) reinterpret_cast<uint4*>(dec)[idx] = nvfp4_decode_chunk(packed, e);
       }
     }
   }
 }
 
-hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t rows, int64_t cols, int hb, int fmt,
-                              const float* amax, uint8_t* codes, uint8_t* blk_scale,
-                              float* tensor_scale, const int32_t* decision, int32_t want,
-                              hipStream_t s) {
+template <bool DEC>
+static hipError_t launch_quant_nvfp4_t(const uint16_t* x, int64_t rows, int64_t cols, int hb, int fmt,
+                                       const float* amax, uint8_t* codes, uint8_t* blk_scale,
+                                       float* tensor_scale, const int32_t* decision, int32_t want,
+                                       uint16_t* dec, hipStream_t s) {
   const int64_t nch = rows * cols / 8;
   const int64_t waves_needed = (nch + 127) / 128;
   // 16 waves per CU x 256 CUs of 4-wave workgroups keeps enough loads in
@@ -420,15 +437,26 @@ hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t rows, int64_t cols, int
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
   const float c_b = hadamard_scale(hb);
-  auto kern = hb == 128 ? (fmt == kNvfp4Mx   ? k_quant_nvfp4<kNvfp4Mx, 128>
-                           : fmt == kNvfp4P2 ? k_quant_nvfp4<kNvfp4P2, 128>
-                                             : k_quant_nvfp4<kNvfp4, 128>)
-                        : (fmt == kNvfp4Mx   ? k_quant_nvfp4<kNvfp4Mx>
-                           : fmt == kNvfp4P2 ? k_quant_nvfp4<kNvfp4P2>
-                                             : k_quant_nvfp4<kNvfp4>);
+  auto kern = hb == 128 ? (fmt == kNvfp4Mx   ? k_quant_nvfp4<kNvfp4Mx, 128, DEC>
+                           : fmt == kNvfp4P2 ? k_quant_nvfp4<kNvfp4P2, 128, DEC>
+                                             : k_quant_nvfp4<kNvfp4, 128, DEC>)
+                        : (fmt == kNvfp4Mx   ? k_quant_nvfp4<kNvfp4Mx, 0, DEC>
+                           : fmt == kNvfp4P2 ? k_quant_nvfp4<kNvfp4P2, 0, DEC>
+                                             : k_quant_nvfp4<kNvfp4, 0, DEC>);
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, s, x, nch, hb, c_b, amax, codes,
-                     blk_scale, tensor_scale, decision, want);
+                     blk_scale, tensor_scale, decision, want, dec);
   return hipGetLastError();
+}
+
+hipError_t launch_quant_nvfp4(const uint16_t* x, int64_t rows, int64_t cols, int hb, int fmt,
+                              const float* amax, uint8_t* codes, uint8_t* blk_scale,
+                              float* tensor_scale, const int32_t* decision, int32_t want,
+                              hipStream_t s, uint16_t* dec) {
+  return dec != nullptr
+             ? launch_quant_nvfp4_t<true>(x, rows, cols, hb, fmt, amax, codes, blk_scale, tensor_scale, decision,
+                                          want, dec, s)
+             : launch_quant_nvfp4_t<false>(x, rows, cols, hb, fmt, amax, codes, blk_scale, tensor_scale, decision,
+                                           want, nullptr, s);
 }
 
 // ------------------------------------------------------------- DeltaQuant
@@ -854,31 +882,21 @@ hipError_t launch_dq_quantize(const uint16_t* x, int64_t K, const DqGrid& g, int
 // significant bits), the tensor scale left out: the core GEMM's operand.
 __global__ __launch_bounds__(256) void k_dq_decode_w(const uint8_t* __restrict__ codes,
                                                      const uint8_t* __restrict__ blk, int64_t nch,
-                                                     uint16_t* __restrict__ out,
-                                                     const int32_t* __restrict__ gate, int32_t want) {
-  if (gate != nullptr && *gate != want) return;
+                                                     uint16_t* __restrict__ out) {
   const uint32_t* cv = reinterpret_cast<const uint32_t*>(codes);
   uint4* ov = reinterpret_cast<uint4*>(out);
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nch; i += (int64_t)gridDim.x * 256) {
-    const uint32_t p = cv[i];
-    const float e = e4m3_decode(blk[i >> 1]);
-    uint32_t o[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t lo = (p >> (8 * j)) & 15u, hi = (p >> (8 * j + 4)) & 15u;
-      o[j] = (__float_as_uint(e2m1_value(lo) * e) >> 16) | ((__float_as_uint(e2m1_value(hi) * e) >> 16) << 16);
-    }
-    ov[i] = make_uint4(o[0], o[1], o[2], o[3]);
+    ov[i] = nvfp4_decode_chunk(cv[i], blk[i >> 1]);
   }
 }
 
 hipError_t launch_dq_decode_w(const uint8_t* codes, const uint8_t* blk, int64_t N, int64_t K, uint16_t* out,
-                              hipStream_t s, const int32_t* gate, int32_t want) {
+                              hipStream_t s) {
   const int64_t nch = N * K / 8;
   int64_t blocks = (nch + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(k_dq_decode_w, dim3((unsigned)blocks), dim3(256), 0, s, codes, blk, nch, out, gate, want);
+  hipLaunchKernelGGL(k_dq_decode_w, dim3((unsigned)blocks), dim3(256), 0, s, codes, blk, nch, out);
   return hipGetLastError();
 }
 
