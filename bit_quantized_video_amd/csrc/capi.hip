@@ -120,10 +120,27 @@ hipError_t enqueue_quantize(const void* x, const hdq_qtensor& q, const float* am
                             q.blk_scale, q.tensor_scale, gate, want, s, static_cast<uint16_t*>(q.dec));
 }
 
-// The plain-NVFP4 operands' decoded bf16 copies, when both are given and the
-// bf16 body takes the shape (the one-launch kernel's shape rule implies it).
-bool use_decoded(int32_t fmt, const hdq_qtensor& xq, const hdq_qtensor& wq, int64_t M, int64_t N, int64_t K) {
-  return fmt == HDQ_FMT_NVFP4 && xq.dec != nullptr && wq.dec != nullptr && nvfp4_decoded_applies(M, N, K);
+// Which decoded bf16 copies the plain-NVFP4 GEMM reads: both operands'
+// (kNvfp4Decoded), the activations' only (kNvfp4XDecoded), or none (0),
+// as given and as the pipelined bf16 body takes the shape (the one-launch
+// kernel's shape rule implies both).
+int decoded_mode(int32_t fmt, const hdq_qtensor& xq, const hdq_qtensor& wq, int64_t M, int64_t N, int64_t K) {
+  if (fmt != HDQ_FMT_NVFP4 || xq.dec == nullptr) return 0;
+  if (wq.dec != nullptr) return nvfp4_decoded_applies(M, N, K) ? kNvfp4Decoded : 0;
+  return nvfp4_xdecoded_applies(M, N, K) ? kNvfp4XDecoded : 0;
+}
+
+// The plain-NVFP4 GEMM from decoded activations (and weights, mode
+// kNvfp4Decoded).
+hipError_t launch_decoded_gemm(int mode, const hdq_qtensor& xq, const hdq_qtensor& wq, void* y, int32_t y_dtype,
+                               int64_t M, int64_t N, int64_t K, const int32_t* gate, hipStream_t s) {
+  if (mode == kNvfp4Decoded)
+    return launch_gemm_nvfp4_decoded(static_cast<const uint16_t*>(xq.dec), xq.tensor_scale,
+                                     static_cast<const uint16_t*>(wq.dec), wq.tensor_scale, y, y_dtype, M, N, K,
+                                     gate, HDQ_PREC_NVFP4, s);
+  return launch_gemm_nvfp4_xdecoded(static_cast<const uint16_t*>(xq.dec), xq.tensor_scale,
+                                    static_cast<const uint8_t*>(wq.codes), wq.blk_scale, wq.tensor_scale, y,
+                                    y_dtype, M, N, K, gate, HDQ_PREC_NVFP4, s);
 }
 
 }  // namespace
@@ -339,13 +356,13 @@ int hdq_linear_dispatch(const int32_t* decision_dev, const void* x, const hdq_qt
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   const uint16_t* wb = static_cast<const uint16_t*>(w->w_bf16);
-  const bool dec = use_decoded(f, *xq4, w->w_fp4, M, N, K);
+  const int dm = decoded_mode(f, *xq4, w->w_fp4, M, N, K);
   hipError_t e = launch_gemm_dispatch(
       decision_dev, static_cast<const int8_t*>(xq8->codes), xq8->row_scale,
       static_cast<const uint8_t*>(w->w_int4.codes), w->w_int4.row_scale,
-      static_cast<const uint8_t*>(dec ? xq4->dec : xq4->codes), xq4->blk_scale, xq4->tensor_scale,
-      static_cast<const uint8_t*>(dec ? w->w_fp4.dec : w->w_fp4.codes), w->w_fp4.blk_scale,
-      w->w_fp4.tensor_scale, dec ? kNvfp4Decoded : f, xb, wb, y, y_dtype, M, N, K, s);
+      static_cast<const uint8_t*>(dm ? xq4->dec : xq4->codes), xq4->blk_scale, xq4->tensor_scale,
+      static_cast<const uint8_t*>(dm == kNvfp4Decoded ? w->w_fp4.dec : w->w_fp4.codes), w->w_fp4.blk_scale,
+      w->w_fp4.tensor_scale, dm ? dm : f, xb, wb, y, y_dtype, M, N, K, s);
   if (e == hipSuccess) return HDQ_OK;
   if (e != hipErrorNotSupported) return HDQ_ERR_HIP;
   // shapes the pipelined bodies do not take: the three gated GEMMs
@@ -353,10 +370,8 @@ int hdq_linear_dispatch(const int32_t* decision_dev, const void* x, const hdq_qt
                        static_cast<const uint8_t*>(w->w_int4.codes), w->w_int4.row_scale, y, y_dtype,
                        M, N, K, decision_dev, HDQ_PREC_INT8, s) != hipSuccess)
     return HDQ_ERR_HIP;
-  if (dec) {
-    if (launch_gemm_nvfp4_decoded(static_cast<const uint16_t*>(xq4->dec), xq4->tensor_scale,
-                                  static_cast<const uint16_t*>(w->w_fp4.dec), w->w_fp4.tensor_scale, y, y_dtype,
-                                  M, N, K, decision_dev, HDQ_PREC_NVFP4, s) != hipSuccess)
+  if (dm) {
+    if (launch_decoded_gemm(dm, *xq4, w->w_fp4, y, y_dtype, M, N, K, decision_dev, s) != hipSuccess)
       return HDQ_ERR_HIP;
   } else if (fp4_gemm_for(f)(static_cast<const uint8_t*>(xq4->codes), xq4->blk_scale, xq4->tensor_scale,
                              static_cast<const uint8_t*>(w->w_fp4.codes), w->w_fp4.blk_scale,
@@ -418,13 +433,13 @@ int hdq_linear_dispatch_delta(const int32_t* decision_dev, const void* x, const 
   // the one-launch kernel only (the difference runs on its extra workgroups)
   if (K % 256 != 0 || M * 2 * K >= (1ll << 31) || N * 2 * K >= (1ll << 31)) return HDQ_ERR_SHAPE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool dec = use_decoded(f, *xq4, w->w_fp4, M, N, K);
+  const int dm = decoded_mode(f, *xq4, w->w_fp4, M, N, K);
   return hip_status(launch_gemm_dispatch(
       decision_dev, static_cast<const int8_t*>(xq8->codes), xq8->row_scale,
       static_cast<const uint8_t*>(w->w_int4.codes), w->w_int4.row_scale,
-      static_cast<const uint8_t*>(dec ? xq4->dec : xq4->codes), xq4->blk_scale, xq4->tensor_scale,
-      static_cast<const uint8_t*>(dec ? w->w_fp4.dec : w->w_fp4.codes), w->w_fp4.blk_scale,
-      w->w_fp4.tensor_scale, dec ? kNvfp4Decoded : f, static_cast<const uint16_t*>(x),
+      static_cast<const uint8_t*>(dm ? xq4->dec : xq4->codes), xq4->blk_scale, xq4->tensor_scale,
+      static_cast<const uint8_t*>(dm == kNvfp4Decoded ? w->w_fp4.dec : w->w_fp4.codes), w->w_fp4.blk_scale,
+      w->w_fp4.tensor_scale, dm ? dm : f, static_cast<const uint16_t*>(x),
       static_cast<const uint16_t*>(w->w_bf16), y, y_dtype, M, N, K, s, &dw));
 }
 
@@ -665,10 +680,8 @@ int hdq_linear(int32_t precision, const int32_t* decision_dev, const void* x,
     }
     const uint8_t* xc = static_cast<const uint8_t*>(q.codes);
     const uint8_t* wc = static_cast<const uint8_t*>(w->w_fp4.codes);
-    if (use_decoded(f, q, w->w_fp4, M, N, K))
-      e = launch_gemm_nvfp4_decoded(static_cast<const uint16_t*>(q.dec), q.tensor_scale,
-                                    static_cast<const uint16_t*>(w->w_fp4.dec), w->w_fp4.tensor_scale, y,
-                                    y_dtype, M, N, K, gate, HDQ_PREC_NVFP4, s);
+    if (const int dm = decoded_mode(f, q, w->w_fp4, M, N, K))
+      e = launch_decoded_gemm(dm, q, w->w_fp4, y, y_dtype, M, N, K, gate, s);
     else
       e = fp4_gemm_for(f)(xc, q.blk_scale, q.tensor_scale, wc, w->w_fp4.blk_scale, w->w_fp4.tensor_scale,
                           y, y_dtype, M, N, K, gate, HDQ_PREC_NVFP4, s);

@@ -230,6 +230,18 @@ hipError_t launch_gemm_nvfp4_bf16(const uint8_t* xc, const uint8_t* xs, const fl
 }
 
 bool nvfp4_decoded_applies(int64_t M, int64_t N, int64_t K) { return pipe_ok<kSrcBf16>(M, N, K); }
+bool nvfp4_xdecoded_applies(int64_t M, int64_t N, int64_t K) {
+  return K % 64 == 0 && M * 2 * K < (1ll << 31) && N * (K / 2) < (1ll << 31);
+}
+
+hipError_t launch_gemm_nvfp4_xdecoded(const uint16_t* xd, const float* xts, const uint8_t* wc,
+                                      const uint8_t* ws, const float* wts, void* y, int out_dtype, int64_t M,
+                                      int64_t N, int64_t K, const int32_t* decision, int32_t want, hipStream_t s) {
+  if (!nvfp4_xdecoded_applies(M, N, K)) return hipErrorNotSupported;
+  if (out_dtype == kOutF32)
+    return launch_bf16_pipe<kSrcNvfp4X, kOutF32>(xd, nullptr, xts, wc, ws, wts, y, M, N, K, decision, want, s);
+  return launch_bf16_pipe<kSrcNvfp4X, kOutBf16>(xd, nullptr, xts, wc, ws, wts, y, M, N, K, decision, want, s);
+}
 
 hipError_t launch_gemm_nvfp4_decoded(const uint16_t* xd, const float* xts, const uint16_t* wd,
                                      const float* wts, void* y, int out_dtype, int64_t M, int64_t N,

@@ -9,7 +9,9 @@
 
 namespace hdq {
 
-enum Src : int { kSrcBf16 = 0, kSrcNvfp4 = 1 };
+// kSrcNvfp4X: X as the exact bf16 values of its NVFP4 codes (decoded
+// beforehand), W as NVFP4 codes decoded here.
+enum Src : int { kSrcBf16 = 0, kSrcNvfp4 = 1, kSrcNvfp4X = 2 };
 
 // 16 NVFP4 elements (8 code bytes) with scale byte e -> 16 bf16, exact.
 // Byte B of `word` (two E2M1 codes) -> bf16 pair of e2m1 * s.
@@ -55,6 +57,11 @@ struct Bf16Stage<kSrcNvfp4> {
   uint4 x, w;         // 32 codes per operand per thread
   uint32_t xs, ws;    // their two E4M3 block scales
 };
+template <>
+struct Bf16Stage<kSrcNvfp4X> {
+  uint4 w;            // 32 W codes per thread
+  uint32_t ws;        // their two E4M3 block scales
+};
 
 template <int SRC, int OUT>
 __device__ __forceinline__ void gemm_bf16_pipe_body(
@@ -92,6 +99,11 @@ __device__ __forceinline__ void gemm_bf16_pipe_body(
       const int64_t ld = 2 * (int64_t)K;
       xres = make_rsrc(reinterpret_cast<const uint8_t*>(X) + m0 * ld, (uint32_t)((M - m0) * ld));
       wres = make_rsrc(reinterpret_cast<const uint8_t*>(W) + n0 * ld, (uint32_t)((N - n0) * ld));
+    } else if constexpr (SRC == kSrcNvfp4X) {
+      const int64_t ldx = 2 * (int64_t)K, ld = K / 2, lds_ = K / 16;
+      xres = make_rsrc(reinterpret_cast<const uint8_t*>(X) + m0 * ldx, (uint32_t)((M - m0) * ldx));
+      wres = make_rsrc(reinterpret_cast<const uint8_t*>(W) + n0 * ld, (uint32_t)((N - n0) * ld));
+      wsres = make_rsrc(wsc + n0 * lds_, (uint32_t)((N - n0) * lds_));
     } else {
       const int64_t ld = K / 2, lds_ = K / 16;
       xres = make_rsrc(reinterpret_cast<const uint8_t*>(X) + m0 * ld, (uint32_t)((M - m0) * ld));
@@ -107,6 +119,9 @@ __device__ __forceinline__ void gemm_bf16_pipe_body(
         st.x[p] = buf_load16(xres, xvoff, kt * 128 + p * 64 * 2 * K);
         st.w[p] = buf_load16(wres, wvoff, kt * 128 + p * 64 * 2 * K);
       }
+    } else if constexpr (SRC == kSrcNvfp4X) {
+      st.w = buf_load16(wres, wvoff, kt * 32);
+      st.ws = __builtin_amdgcn_raw_buffer_load_b16(wsres, (int)svoff, kt * 4, 0);
     } else {
       st.x = buf_load16(xres, xvoff, kt * 32);
       st.w = buf_load16(wres, wvoff, kt * 32);
@@ -124,8 +139,10 @@ __device__ __forceinline__ void gemm_bf16_pipe_body(
     uint8_t* base = smem + buf * SB + 1024 * wave;
 #pragma unroll
     for (int p = 0; p < 4; ++p) lds_dma16(xres, base + 8192 * p, dvoff, kt * 128 + p * 64 * 2 * K);
+    if constexpr (SRC == kSrcBf16) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) lds_dma16(wres, base + XB + 8192 * p, dvoff, kt * 128 + p * 64 * 2 * K);
+      for (int p = 0; p < 4; ++p) lds_dma16(wres, base + XB + 8192 * p, dvoff, kt * 128 + p * 64 * 2 * K);
+    }
   };
   auto store = [&](const Stage& st, int buf) {
     uint8_t* lx = smem + buf * SB;
@@ -136,6 +153,14 @@ __device__ __forceinline__ void gemm_bf16_pipe_body(
         *reinterpret_cast<uint4*>(lx + dst + p * 64 * 128) = st.x[p];
         *reinterpret_cast<uint4*>(lw + dst + p * 64 * 128) = st.w[p];
       }
+    } else if constexpr (SRC == kSrcNvfp4X) {
+      const int r = tid >> 1, c = tid & 1;
+      uint4 d[4];
+      decode_nvfp4x16(make_uint2(st.w.x, st.w.y), st.ws & 0xffu, d[0], d[1]);
+      decode_nvfp4x16(make_uint2(st.w.z, st.w.w), st.ws >> 8, d[2], d[3]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<uint4*>(lw + r * 128 + 16 * ((4 * c + q) ^ swz128(r))) = d[q];
     } else {
       const int r = tid >> 1, c = tid & 1;
       uint4 d[4];
@@ -189,7 +214,7 @@ __device__ __forceinline__ void gemm_bf16_pipe_body(
   };
 
   // NVFP4 (decoded here or beforehand): the two tensor scales; bf16: none.
-  const float scale = (SRC == kSrcNvfp4 || xts != nullptr) ? (*xts) * (*wts) : 1.0f;
+  const float scale = (SRC != kSrcBf16 || xts != nullptr) ? (*xts) * (*wts) : 1.0f;
   auto epilogue = [&](int m0, int n0) {
     if constexpr (OUT == kOutBf16) {
       // Stage the bf16 tile in LDS (both pipeline buffers are free once every
@@ -274,6 +299,36 @@ __device__ __forceinline__ void gemm_bf16_pipe_body(
         stage_barrier();
         if (kt + 2 < nk) issue_dma(kt + 2, 0);
         compute(1);
+        stage_barrier();
+      }
+      if (kt < nk) compute(0);
+      epilogue(m0, n0);
+      zero_acc();
+      continue;
+    }
+    if constexpr (SRC == kSrcNvfp4X) {
+      // X (decoded bf16) by LDS-DMA and W's codes through one register set,
+      // both one stage ahead: stage kt + 1's DMA and W loads are issued
+      // before stage kt is computed, W is decoded into the other buffer
+      // after it, and the stage barrier waits for all of them.
+      Stage ra;
+      int kt = 0;
+      issue_dma(0, 0);
+      load(ra, 0);
+      store(ra, 0);
+      stage_barrier();
+      for (; kt + 1 < nk; kt += 2) {
+        issue_dma(kt + 1, 1);
+        load(ra, kt + 1);
+        compute(0);
+        store(ra, 1);
+        stage_barrier();
+        if (kt + 2 < nk) {
+          issue_dma(kt + 2, 0);
+          load(ra, kt + 2);
+        }
+        compute(1);
+        if (kt + 2 < nk) store(ra, 0);
         stage_barrier();
       }
       if (kt < nk) compute(0);

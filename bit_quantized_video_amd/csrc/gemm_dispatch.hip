@@ -118,7 +118,8 @@ __device__ __forceinline__ void delta_workgroup(const DeltaWork& dw, uint8_t* sm
 
 // FP4: the NVFP4 weights' format (kNvfp4: the exact bf16-MFMA body; kNvfp4Mx,
 // kNvfp4P2: the FP4 MFMA body, one or two passes; kNvfp4Decoded: the bf16
-// body on operands decoded beforehand, xc and wc then pointing at bf16).
+// body on operands decoded beforehand, xc and wc then pointing at bf16;
+// kNvfp4XDecoded: xc points at the activations' bf16 values, W is codes).
 template <int OUT, int FP4>
 __global__ __launch_bounds__(512) void k_gemm_dispatch(
     const int32_t* __restrict__ decision, const int8_t* __restrict__ x8, const float* __restrict__ sx,
@@ -140,6 +141,8 @@ __global__ __launch_bounds__(512) void k_gemm_dispatch(
       gemm_bf16_pipe_body<kSrcNvfp4, OUT>(xc, xsc, xts, wc, wsc, wts, Y, M, N, K, gemm_wgs);
     else if constexpr (FP4 == kNvfp4Decoded)
       gemm_bf16_pipe_body<kSrcBf16, OUT>(xc, nullptr, xts, wc, nullptr, wts, Y, M, N, K, gemm_wgs);
+    else if constexpr (FP4 == kNvfp4XDecoded)
+      gemm_bf16_pipe_body<kSrcNvfp4X, OUT>(xc, nullptr, xts, wc, wsc, wts, Y, M, N, K, gemm_wgs);
     else
       gemm_fp4mx_pipe_body<OUT, FP4 == kNvfp4P2>(xc, xsc, xts, wc, wsc, wts, Y, M, N, K, gemm_wgs);
   } else if (d == kPrecBf16) {
@@ -190,11 +193,13 @@ hipError_t launch_gemm_dispatch(const int32_t* decision, const int8_t* x8, const
     if (fp4_fmt == kNvfp4Mx) HDQ_DISPATCH(kOutBf16, kNvfp4Mx);
     if (fp4_fmt == kNvfp4P2) HDQ_DISPATCH(kOutBf16, kNvfp4P2);
     if (fp4_fmt == kNvfp4Decoded) HDQ_DISPATCH(kOutBf16, kNvfp4Decoded);
+    if (fp4_fmt == kNvfp4XDecoded) HDQ_DISPATCH(kOutBf16, kNvfp4XDecoded);
     HDQ_DISPATCH(kOutBf16, kNvfp4);
   }
   if (fp4_fmt == kNvfp4Mx) HDQ_DISPATCH(kOutF32, kNvfp4Mx);
   if (fp4_fmt == kNvfp4P2) HDQ_DISPATCH(kOutF32, kNvfp4P2);
   if (fp4_fmt == kNvfp4Decoded) HDQ_DISPATCH(kOutF32, kNvfp4Decoded);
+  if (fp4_fmt == kNvfp4XDecoded) HDQ_DISPATCH(kOutF32, kNvfp4XDecoded);
   HDQ_DISPATCH(kOutF32, kNvfp4);
 #undef HDQ_DISPATCH
 }

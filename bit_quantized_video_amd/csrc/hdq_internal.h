@@ -54,6 +54,8 @@ enum QFmt : int { kInt8Row = 0, kInt4Row = 1, kNvfp4 = 2, kNvfp4Mx = 3, kNvfp4P2
 // The one-launch GEMM's NVFP4 body for plain NVFP4 operands given decoded to
 // bf16 (not a tensor format).
 constexpr int kNvfp4Decoded = 16;
+// ... with only the activations decoded (the weights' codes decoded in the GEMM).
+constexpr int kNvfp4XDecoded = 17;
 enum Prec : int { kPrecNvfp4 = 0, kPrecInt8 = 1, kPrecBf16 = 2 };
 enum OutDtype : int { kOutF32 = 0, kOutBf16 = 1, kOutI32 = 2 };
 
@@ -132,6 +134,13 @@ hipError_t launch_gemm_nvfp4_bf16(const uint8_t* xc, const uint8_t* xs, const fl
 // then runs the exact NVFP4 kernel's MFMAs in its order): otherwise
 // hipErrorNotSupported.
 bool nvfp4_decoded_applies(int64_t M, int64_t N, int64_t K);
+// Only the activations decoded beforehand (xd: bf16 [M, K]); the weights'
+// codes are decoded in the GEMM as the exact kernel does.  Pipelined shapes
+// only (nvfp4_xdecoded_applies), else hipErrorNotSupported.
+bool nvfp4_xdecoded_applies(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_nvfp4_xdecoded(const uint16_t* xd, const float* xts, const uint8_t* wc,
+                                      const uint8_t* ws, const float* wts, void* y, int out_dtype, int64_t M,
+                                      int64_t N, int64_t K, const int32_t* decision, int32_t want, hipStream_t s);
 hipError_t launch_gemm_nvfp4_decoded(const uint16_t* xd, const float* xts, const uint16_t* wd,
                                      const float* wts, void* y, int out_dtype, int64_t M, int64_t N,
                                      int64_t K, const int32_t* decision, int32_t want, hipStream_t s);

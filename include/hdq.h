@@ -313,10 +313,10 @@ int hdq_quantize(const void *x, int64_t rows, int64_t cols, int32_t had_block, i
  * INT8:  acc = sum_k qx*qw (exact int32); y = fl32(fl32(acc * sx[m]) * sw[n]).
  * NVFP4: y = s_tx * s_tw * sum over 16-blocks of E_x E_w sum_k e2m1 e2m1,
  *        float32 accumulation.  Plain NVFP4 (HDQ_FMT_NVFP4) runs on bf16
- *        MFMAs: when xq->dec and w->w_fp4.dec are both given the GEMM reads
+ *        MFMAs: when xq->dec (and w->w_fp4.dec) are given the GEMM reads
  *        those exact bf16 values, otherwise it decodes the codes as it
  *        stages them -- the same products in the same order, so the same
- *        output bits.
+ *        output bits.  Both copies given is the fastest form.
  * BF16:  y = x w^T with the unrotated bf16 operands, float32 accumulation.
  */
 int hdq_linear(int32_t precision, const int32_t *decision_dev, const void *x,
@@ -334,7 +334,7 @@ int hdq_linear(int32_t precision, const int32_t *decision_dev, const void *x,
  * hdq_linear(P, decision_dev, x or xq, ...) of the decided P, bit for bit.
  * One kernel reads the decision and runs that GEMM (K a multiple of 256 and
  * 2 * K * max(M, N) < 2^31); other shapes enqueue the three gated GEMMs.
- * Plain NVFP4 with xq4->dec and w->w_fp4.dec given reads the decoded
+ * Plain NVFP4 with xq4->dec (and w->w_fp4.dec) given reads the decoded
  * operands, as hdq_linear does.
  * y_dtype F32 or BF16.  No workspace.
  */

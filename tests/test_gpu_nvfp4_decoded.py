@@ -1,9 +1,9 @@
 """Plain NVFP4 with decoded operands (hdq_qtensor.dec), through the C ABI.
 
-The exact NVFP4 product runs on bf16 MFMAs.  When both operands carry their
+The exact NVFP4 product runs on bf16 MFMAs.  When the operands carry their
 codes' exact bf16 values (E2M1 value x E4M3 block scale, which bf16 holds
-exactly), the GEMM reads those instead of decoding the codes while it
-stages them.  It issues the same MFMAs on the same values in the same order,
+exactly) -- both, or the activations only -- the GEMM reads those instead of
+decoding the codes while it stages them.  It issues the same MFMAs on the same values in the same order,
 so the outputs must equal the codes path bit for bit; the codes path itself
 is checked against the oracle in test_gpu_parity.py.
 
@@ -116,10 +116,12 @@ def test_linear_decoded_operands_same_bits(M, N, K, y_dtype):
     xd, W, Wd, xq, xqd = operands(M, N, K, M + N + K)
     y0 = hdq.linear(hdq.PREC_NVFP4, None, W, xq=xq, y_dtype=y_dtype)
     y1 = hdq.linear(hdq.PREC_NVFP4, None, Wd, xq=xqd, y_dtype=y_dtype)
-    y2 = hdq.linear(hdq.PREC_NVFP4, None, Wd, xq=xq, y_dtype=y_dtype)    # one side only: codes path
+    y2 = hdq.linear(hdq.PREC_NVFP4, None, Wd, xq=xq, y_dtype=y_dtype)    # weights only: codes path
+    y3 = hdq.linear(hdq.PREC_NVFP4, None, W, xq=xqd, y_dtype=y_dtype)    # activations only: W decoded here
     torch.cuda.synchronize()
     assert torch.equal(bits(y1), bits(y0))
     assert torch.equal(bits(y2), bits(y0))
+    assert torch.equal(bits(y3), bits(y0))
 
 
 @pytest.mark.parametrize("M,N,K,y_dtype", [(300, 384, 512, hdq.DTYPE_BF16), (1000, 600, 1024, hdq.DTYPE_F32),
@@ -135,8 +137,10 @@ def test_dispatch_decoded_operands_same_bits(M, N, K, y_dtype):
         d.fill_(prec)
         y0 = hdq.linear_dispatch(d, xd, xq8, xq, W, y_dtype=y_dtype)
         y1 = hdq.linear_dispatch(d, xd, xq8, xqd, Wd, y_dtype=y_dtype)
+        y2 = hdq.linear_dispatch(d, xd, xq8, xqd, W, y_dtype=y_dtype)
         torch.cuda.synchronize()
         assert torch.equal(bits(y1), bits(y0)), prec
+        assert torch.equal(bits(y2), bits(y0)), prec
 
 
 def test_dispatch_delta_decoded_operands_same_bits():
@@ -154,6 +158,11 @@ def test_dispatch_delta_decoded_operands_same_bits():
     y1 = hdq.linear_dispatch_delta(d, xd, xq8, xqd, Wd, [(a, b, 0, nch, parts)], queue)
     torch.cuda.synchronize()
     assert torch.equal(bits(y1), bits(y0))
+    parts2 = torch.zeros_like(parts)
+    y2 = hdq.linear_dispatch_delta(d, xd, xq8, xqd, W, [(a, b, 0, nch, parts2)], queue)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(y2), bits(y0))
+    assert torch.equal(parts2, parts)
     ref = hdq.delta_sums(a, b)
     torch.cuda.synchronize()
     got = parts.sum(dim=0).cpu().numpy()
