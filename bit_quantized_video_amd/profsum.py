@@ -56,7 +56,7 @@ KINDS = OrderedDict([
     ("gemm_int8", r"k_gemm_i8i4(_pipe)?<[\d, ]*1>"),
     ("gemm_nvfp4_mx", r"k_gemm_fp4mx_pipe<1, false>"),
     ("gemm_nvfp4_p2", r"k_gemm_fp4mx_pipe<1, true>"),
-    ("gemm_nvfp4", r"k_gemm_bf16(_pipe|mfma)<1, 1>"),
+    ("gemm_nvfp4", r"k_gemm_bf16(_pipe|mfma)<[12], 1>"),
     ("gemm_bf16", r"k_gemm_bf16(_pipe|mfma)<0, 1>"),
 ])
 # Sources each kind is built from (any change voids a stored traffic figure).
@@ -76,9 +76,10 @@ SOURCES = {
 # One-launch GEMMs (bf16 output) that run the decided precision: the kind
 # comes from the decision of the layer call (DECISIONS, in call order); the
 # second template argument is the NVFP4 weights' format (2 plain, 3 MX, 4
-# per-16 powers of two; 16 plain from operands decoded to bf16).
-DISPATCH = r"k_gemm_dispatch<1, (2|3|4|16)>"
-FP4_KIND = {"2": "gemm_nvfp4", "3": "gemm_nvfp4_mx", "4": "gemm_nvfp4_p2", "16": "gemm_nvfp4"}
+# per-16 powers of two; 16 plain from operands decoded to bf16, 17 from
+# decoded activations only).
+DISPATCH = r"k_gemm_dispatch<1, (2|3|4|16|17)>"
+FP4_KIND = {"2": "gemm_nvfp4", "3": "gemm_nvfp4_mx", "4": "gemm_nvfp4_p2", "16": "gemm_nvfp4", "17": "gemm_nvfp4"}
 DECISIONS = None
 
 
