@@ -135,6 +135,10 @@ __device__ __forceinline__ void gemm_bf16_pipe_body(
   // reads expect; the swizzle depends on the lane and the wave only.
   const int drow = 8 * wave + (lane >> 3);
   const uint32_t dvoff = (uint32_t)(drow * 2 * K + 16 * ((lane & 7) ^ swz128(drow)));
+  // The scheduling barrier keeps the loads where they are issued, ahead of
+  // the stage's compute: left to itself the compiler sinks some of them
+  // (their LDS destination provably differs from what the compute reads)
+  // to just before the stage barrier, which then waits out their latency.
   auto issue_dma = [&](int kt, int buf) {
     uint8_t* base = smem + buf * SB + 1024 * wave;
 #pragma unroll
@@ -143,6 +147,7 @@ __device__ __forceinline__ void gemm_bf16_pipe_body(
 #pragma unroll
       for (int p = 0; p < 4; ++p) lds_dma16(wres, base + XB + 8192 * p, dvoff, kt * 128 + p * 64 * 2 * K);
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
   auto store = [&](const Stage& st, int buf) {
     uint8_t* lx = smem + buf * SB;
