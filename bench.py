@@ -129,11 +129,12 @@ class KernelTimes:
         return out
 
 
-def quant_bytes(M, K, prec):
-    """Algorithmic HBM bytes of one fused rotate+quantize of X [M, K] bf16."""
+def quant_bytes(M, K, prec, decoded=False):
+    """Algorithmic HBM bytes of one fused rotate+quantize of X [M, K] bf16
+    (decoded: the NVFP4 codes' exact bf16 values written as well)."""
     if prec == "int8":
         return 2 * M * K + M * K + 4 * M
-    return 2 * M * K + M * K // 2 + M * K // 16 + 4 + 4
+    return 2 * M * K + M * K // 2 + M * K // 16 + 4 + 4 + (2 * M * K if decoded else 0)
 
 
 def stats_bytes(M, K):
@@ -447,7 +448,7 @@ def schedule_kernel_times(S, args, events_per_step, synth, recipe, side_per_step
                     dt = [ev[i].elapsed_time(ev[i + 1]) if ev[i] is not None and ev[i + 1] is not None
                           else None for i in range(6)]
                     flops = 2.0 * M * N * K
-                    q8, q4 = quant_bytes(M, K, "int8"), quant_bytes(M, K, "nvfp4")
+                    q8, q4 = quant_bytes(M, K, "int8"), quant_bytes(M, K, "nvfp4", recipe == "nvfp4")
                     if dt[0] is None:
                         pass  # GEMM events only
                     elif fused:
@@ -858,12 +859,29 @@ def cpu_model():
     return None
 
 
+_FILL = {}
+
+
+def gpu_filler(ms=5.0):
+    """Queues about `ms` of device copies (256 MiB each): the clocks leave
+    their idle state, and launches enqueued behind it reach the GPU back to
+    back instead of at the host's launch rate."""
+    if "a" not in _FILL:
+        _FILL["a"] = torch.empty(1 << 28, dtype=torch.uint8, device="cuda")
+        _FILL["b"] = torch.empty_like(_FILL["a"])
+    for _ in range(max(1, int(ms / 0.1))):
+        _FILL["b"].copy_(_FILL["a"])
+
+
 def event_time(fn, reps, warm=2):
-    """Average milliseconds of fn() over reps launches (HIP events)."""
+    """Average milliseconds of fn() over reps launches (HIP events), timed
+    behind a few milliseconds of queued copies so that the host enqueues the
+    timed launches while they run."""
     for _ in range(warm):
         fn()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    gpu_filler()
     e0.record()
     for _ in range(reps):
         fn()
@@ -873,7 +891,12 @@ def event_time(fn, reps, warm=2):
 
 
 # the single-layer configurations and the paths each is run on
-CONFIG_PATHS = {1: ("int8", "nvfp4", "nvfp4_mx"), 2: ("int8",), 3: ("nvfp4", "nvfp4_mx"), 4: ("int8",)}
+# (nvfp4: the exact GEMM on both operands' decoded bf16 values, which the
+# quantizer writes beside the codes; nvfp4_staged: the same GEMM decoding the
+# codes while it stages them)
+CONFIG_PATHS = {1: ("int8", "nvfp4", "nvfp4_staged", "nvfp4_mx"), 2: ("int8",),
+                3: ("nvfp4", "nvfp4_staged", "nvfp4_mx"), 4: ("int8",)}
+PATH_FMT = {"int8": "FMT_INT8_ROW", "nvfp4": "FMT_NVFP4", "nvfp4_staged": "FMT_NVFP4", "nvfp4_mx": "FMT_NVFP4_MX"}
 
 
 def bench_configs(args, hdq, synth):
@@ -901,16 +924,18 @@ def bench_configs(args, hdq, synth):
         rows = np.arange(M) if M <= 1024 else np.r_[0:256, M - 112:M]
         recs = {}
         for path in CONFIG_PATHS[cfg]:
-            fmt = {"int8": hdq.FMT_INT8_ROW, "nvfp4": hdq.FMT_NVFP4, "nvfp4_mx": hdq.FMT_NVFP4_MX}[path]
-            W = hdq.LinearWeights(wd, hb, fp4_fmt=None if path == "int8" else fmt, keep_bf16=False)
+            fmt = getattr(hdq, PATH_FMT[path])
+            decoded = path == "nvfp4"
+            W = hdq.LinearWeights(wd, hb, fp4_fmt=None if path == "int8" else fmt, keep_bf16=False,
+                                  fp4_decoded=decoded)
             prec = hdq.PREC_INT8 if path == "int8" else hdq.PREC_NVFP4
-            xq = hdq.QuantizedTensor(fmt, M, K, hb, dev)
+            xq = hdq.QuantizedTensor(fmt, M, K, hb, dev, decoded=decoded)
             amax = None if path == "int8" else hdq.select_precision(None, None, xd, hb)[1][4:5]
             tq = event_time(lambda: hdq.quantize(xd, hb, fmt, tensor_amax=amax, out=xq), args.config_reps)
             tg = event_time(lambda: hdq.linear(prec, None, W, xq=xq, y=y, y_dtype=y_dtype), args.config_reps)
             flops = 2.0 * M * N * K
-            qb = quant_bytes(M, K, "int8" if path == "int8" else "nvfp4")
-            dt = {"int8": "int8", "nvfp4": "bf16", "nvfp4_mx": "fp4"}[path]
+            qb = quant_bytes(M, K, "int8" if path == "int8" else "nvfp4", decoded)
+            dt = {"int8": "int8", "nvfp4": "bf16", "nvfp4_staged": "bf16", "nvfp4_mx": "fp4"}[path]
             rec = {"quant_us": round(tq * 1e3, 1), "quant_gbps": round(qb / (tq * 1e-3) / 1e9, 1),
                    "quant_frac_hbm": round(qb / (tq * 1e-3) / PEAK["hbm"], 4),
                    "gemm_us": round(tg * 1e3, 1), "gemm_dtype": dt,
@@ -922,7 +947,7 @@ def bench_configs(args, hdq, synth):
             got = y.float().cpu().numpy()[rows] if y_dtype == hdq.DTYPE_F32 else \
                 synth.bf16_bits_to_f32(y.view(torch.int16).cpu().numpy().view(np.uint16)[rows])
             xs = np.ascontiguousarray(x16[rows])
-            mx = {"nvfp4": 0, "nvfp4_mx": 1}.get(path, 0)
+            mx = {"nvfp4_mx": 1}.get(path, 0)
             if path == "int8":
                 qw, sw = O.quant_int(w16, hb, 7)
             else:
@@ -1135,10 +1160,12 @@ def bench_single(args, hdq, synth):
     xd = to_dev(x16)
     path = c["paths"][0] if args.fp4 == "nvfp4" else ("nvfp4" if "nvfp4" in c["paths"] else "int8")
     fmt = hdq.FMT_INT8_ROW if path == "int8" else RECIPE_FMT[args.fp4](hdq)
-    W = hdq.LinearWeights(to_dev(w16), hb, fp4_fmt=None if path == "int8" else fmt)
+    # plain NVFP4: the exact GEMM on both operands' decoded bf16 values
+    decoded = path != "int8" and args.fp4 == "nvfp4"
+    W = hdq.LinearWeights(to_dev(w16), hb, fp4_fmt=None if path == "int8" else fmt, fp4_decoded=decoded)
     prec = hdq.PREC_INT8 if path == "int8" else hdq.PREC_NVFP4
     y_dtype = hdq.DTYPE_F32 if c["out"] == "f32" else hdq.DTYPE_BF16
-    xq = hdq.QuantizedTensor(fmt, M, K, hb, dev)
+    xq = hdq.QuantizedTensor(fmt, M, K, hb, dev, decoded=decoded)
     amax = None
     if path != "int8":
         _, st = hdq.select_precision(None, None, xd, hb)
@@ -1161,7 +1188,7 @@ def bench_single(args, hdq, synth):
     tq = np.mean([e[0].elapsed_time(e[1]) for e in evs])
     tg = np.mean([e[1].elapsed_time(e[2]) for e in evs])
     flops = 2.0 * M * N * K
-    qb = quant_bytes(M, K, "int8" if path == "int8" else "nvfp4")
+    qb = quant_bytes(M, K, "int8" if path == "int8" else "nvfp4", decoded)
     dt = "int8" if path == "int8" else ("bf16" if args.fp4 == "nvfp4" else "fp4")
     res = {"metric": METRIC, "value": round(flops / ((tq + tg) * 1e-3) / 1e12, 2), "unit": "TOPS",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
