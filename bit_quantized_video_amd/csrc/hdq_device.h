@@ -153,6 +153,61 @@ __device__ __forceinline__ float fwht8(float (&x)[8], int lane, int hb) {
   }
   return (__builtin_popcount(c) & 1) ? -1.0f : 1.0f;
 }
+
+// Hadamard blocks of 128 with 32 consecutive elements per lane: block q
+// spans lanes 4q .. 4q + 3 in natural order (lane bit 0 = element bit 5,
+// lane bit 1 = element bit 6).  Strides 1..16 run inside the lane, strides
+// 32 and 64 are one v_fmac_f32_dpp per element over quad_perm [1,0,3,2] and
+// [2,3,0,1], with the sign bookkeeping described above: the returned sign is
+// the parity of lane bits 0 and 1.
+#define HDQ_FMAC_DPP8_AT(CTRL, NOP, O)                                                       \
+  asm(NOP                                                                                    \
+      "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"       \
+      "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"       \
+      "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"       \
+      "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"       \
+      "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"       \
+      "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"       \
+      "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"       \
+      "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1"           \
+      : "+v"(x[O + 0]), "+v"(x[O + 1]), "+v"(x[O + 2]), "+v"(x[O + 3]), "+v"(x[O + 4]),       \
+        "+v"(x[O + 5]), "+v"(x[O + 6]), "+v"(x[O + 7])                                        \
+      : "v"(s))
+
+__device__ __forceinline__ float fwht128_w32(float (&x)[32], int lane) {
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if ((i & h) == 0) {
+        const float u = x[i], v = x[i + h];
+        x[i] = u + v;
+        x[i + h] = u - v;
+      }
+    }
+  }
+  // Every block of the first cross-lane stage starts with the two wait
+  // states a DPP read needs after a VALU write (the compiler may place the
+  // last in-lane writes of any register right before it); the second
+  // stage's sources were last written by the first stage's blocks, at
+  // least 24 instructions earlier.
+  {
+    const float s = (lane & 1) ? -1.0f : 1.0f;
+    HDQ_FMAC_DPP8_AT("quad_perm:[1,0,3,2]", "s_nop 1\n\t", 0);
+    HDQ_FMAC_DPP8_AT("quad_perm:[1,0,3,2]", "s_nop 1\n\t", 8);
+    HDQ_FMAC_DPP8_AT("quad_perm:[1,0,3,2]", "s_nop 1\n\t", 16);
+    HDQ_FMAC_DPP8_AT("quad_perm:[1,0,3,2]", "s_nop 1\n\t", 24);
+  }
+  {
+    const float s = (lane & 2) ? -1.0f : 1.0f;
+    HDQ_FMAC_DPP8_AT("quad_perm:[2,3,0,1]", "s_nop 1\n\t", 0);
+    HDQ_FMAC_DPP8_AT("quad_perm:[2,3,0,1]", "", 8);
+    HDQ_FMAC_DPP8_AT("quad_perm:[2,3,0,1]", "", 16);
+    HDQ_FMAC_DPP8_AT("quad_perm:[2,3,0,1]", "", 24);
+  }
+  return (((lane ^ (lane >> 1)) & 1) != 0) ? -1.0f : 1.0f;
+}
+#undef HDQ_FMAC_DPP8_AT
 #undef HDQ_FMAC_DPP8
 
 // ---- FP8 E4M3 block scales (unsigned) -------------------------------------

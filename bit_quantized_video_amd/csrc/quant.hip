@@ -321,19 +321,13 @@ hipError_t launch_quant_int_rows(const uint16_t* x, int64_t rows, int64_t cols, 
 // scaled); returns its 4 code bytes and sets *e to its 16-block's scale byte.
 // FMT: kNvfp4 (E4M3 scale per 16), kNvfp4Mx (a power of two per aligned
 // pair of 16-blocks), kNvfp4P2 (a power of two per 16-block).
+// A block's scale byte (*e_out) and fl32(1 / d), d = the block scale's value
+// times s_t, from the block's max |y| (0 when s_t or d is 0).
 template <int FMT>
-__device__ __forceinline__ uint32_t nvfp4_chunk(float (&v)[8], float s_t, float six_st, float inv_st,
-                                                uint32_t* e_out) {
-  float a = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
-  // the two chunks of a 16-element block sit on lanes l and l ^ 1, the four
-  // of a 32-element group on l ^ {0, 1, 2, 3} (fwht_chunk keeps chunk bits
-  // 0 and 1 on lane bits 0 and 1)
-  a = fmaxf(a, xor_lane<1>(a));
-  if constexpr (FMT == kNvfp4Mx) a = fmaxf(a, xor_lane<2>(a));
+__device__ __forceinline__ float nvfp4_block_inv(float a, float s_t, float six_st, float inv_st,
+                                                 uint32_t* e_out) {
   uint32_t e = 0u;
-  float inv = 0.0f;  // fl32(1 / d), d = the block scale's value times s_t
+  float inv = 0.0f;
   if (s_t > 0.0f) {
     const float t = a / six_st;
     if constexpr (FMT == kNvfp4) {
@@ -350,6 +344,21 @@ __device__ __forceinline__ uint32_t nvfp4_chunk(float (&v)[8], float s_t, float 
     }
   }
   *e_out = e;
+  return inv;
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t nvfp4_chunk(float (&v)[8], float s_t, float six_st, float inv_st,
+                                                uint32_t* e_out) {
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
+  // the two chunks of a 16-element block sit on lanes l and l ^ 1, the four
+  // of a 32-element group on l ^ {0, 1, 2, 3} (fwht_chunk keeps chunk bits
+  // 0 and 1 on lane bits 0 and 1)
+  a = fmaxf(a, xor_lane<1>(a));
+  if constexpr (FMT == kNvfp4Mx) a = fmaxf(a, xor_lane<2>(a));
+  const float inv = nvfp4_block_inv<FMT>(a, s_t, six_st, inv_st, e_out);
   if (inv == 0.0f) return 0u;
   return e2m1x2_encode(v[0] * inv, v[1] * inv) | (e2m1x2_encode(v[2] * inv, v[3] * inv) << 8) |
          (e2m1x2_encode(v[4] * inv, v[5] * inv) << 16) | (e2m1x2_encode(v[6] * inv, v[7] * inv) << 24);
@@ -423,6 +432,88 @@ __global__ __launch_bounds__(256) void k_quant_nvfp4(
   }
 }
 
+// Eight E2M1 codes of y[0..7] * inv in k order, two per byte (the
+// conversion writes the byte its last operand selects).
+__device__ __forceinline__ uint32_t e2m1x8_encode(const float* y, float inv) {
+  uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[0] * inv, y[1] * inv, 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2] * inv, y[3] * inv, 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4] * inv, y[5] * inv, 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6] * inv, y[7] * inv, 1.0f, 3);
+  return w;
+}
+
+// Hadamard block 128: one lane per 32 consecutive elements (fwht128_w32), so
+// a 32-element group's maximum and scale stay inside the lane (one division
+// per 16-element block for every lane that holds it, instead of one per
+// 8-element chunk, and no cross-lane maximum), and a lane writes its 16 code
+// bytes and 2 scale bytes with one store each.  The same arithmetic as
+// k_quant_nvfp4, value for value.
+template <int FMT, bool DEC>
+__global__ __launch_bounds__(256) void k_quant_nvfp4_w32(
+    const uint16_t* __restrict__ x, int64_t ngrp, float c_b, const float* __restrict__ amax_ptr,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ blk_scale, float* __restrict__ tensor_scale,
+    const int32_t* __restrict__ decision, int32_t want, uint16_t* __restrict__ dec) {
+  if (decision != nullptr && *decision != want) return;
+  const int lane = threadIdx.x & 63;
+  const float A = *amax_ptr;
+  const float s_t = (A >= kTiny) ? A / (FMT == kNvfp4 ? 2688.0f : 1536.0f) : 0.0f;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = s_t;
+  const float six_st = 6.0f * s_t, inv_st = s_t > 0.0f ? 1.0f / s_t : 0.0f;
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  // ngrp is a multiple of 4 and the lanes of a wave take consecutive
+  // groups, so the four lanes of a Hadamard block stay active together
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < ngrp; g += stride) {
+    uint4 w[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) w[c] = xv[4 * g + c];
+    float v[32];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      v[8 * c + 0] = bf16_lo(w[c].x);
+      v[8 * c + 1] = bf16_hi(w[c].x);
+      v[8 * c + 2] = bf16_lo(w[c].y);
+      v[8 * c + 3] = bf16_hi(w[c].y);
+      v[8 * c + 4] = bf16_lo(w[c].z);
+      v[8 * c + 5] = bf16_hi(w[c].z);
+      v[8 * c + 6] = bf16_lo(w[c].w);
+      v[8 * c + 7] = bf16_hi(w[c].w);
+    }
+    const float sc = fwht128_w32(v, lane) * c_b;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = v[i] * sc;
+    float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      a0 = fmaxf(a0, fabsf(v[i]));
+      a1 = fmaxf(a1, fabsf(v[16 + i]));
+    }
+    uint32_t e0, e1;
+    float inv0, inv1;
+    if constexpr (FMT == kNvfp4Mx) {
+      inv0 = inv1 = nvfp4_block_inv<FMT>(fmaxf(a0, a1), s_t, six_st, inv_st, &e0);
+      e1 = e0;
+    } else {
+      inv0 = nvfp4_block_inv<FMT>(a0, s_t, six_st, inv_st, &e0);
+      inv1 = nvfp4_block_inv<FMT>(a1, s_t, six_st, inv_st, &e1);
+    }
+    uint32_t p[4];
+    p[0] = inv0 == 0.0f ? 0u : e2m1x8_encode(v + 0, inv0);
+    p[1] = inv0 == 0.0f ? 0u : e2m1x8_encode(v + 8, inv0);
+    p[2] = inv1 == 0.0f ? 0u : e2m1x8_encode(v + 16, inv1);
+    p[3] = inv1 == 0.0f ? 0u : e2m1x8_encode(v + 24, inv1);
+    reinterpret_cast<uint4*>(codes)[g] = make_uint4(p[0], p[1], p[2], p[3]);
+    reinterpret_cast<uint16_t*>(blk_scale)[g] = (uint16_t)(e0 | (e1 << 8));
+    if constexpr (DEC) {
+      uint4* dv = reinterpret_cast<uint4*>(dec) + 4 * g;
+      dv[0] = nvfp4_decode_chunk(p[0], e0);
+      dv[1] = nvfp4_decode_chunk(p[1], e0);
+      dv[2] = nvfp4_decode_chunk(p[2], e1);
+      dv[3] = nvfp4_decode_chunk(p[3], e1);
+    }
+  }
+}
+
 template <bool DEC>
 static hipError_t launch_quant_nvfp4_t(const uint16_t* x, int64_t rows, int64_t cols, int hb, int fmt,
                                        const float* amax, uint8_t* codes, uint8_t* blk_scale,
@@ -437,12 +528,21 @@ static hipError_t launch_quant_nvfp4_t(const uint16_t* x, int64_t rows, int64_t 
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
   const float c_b = hadamard_scale(hb);
-  auto kern = hb == 128 ? (fmt == kNvfp4Mx   ? k_quant_nvfp4<kNvfp4Mx, 128, DEC>
-                           : fmt == kNvfp4P2 ? k_quant_nvfp4<kNvfp4P2, 128, DEC>
-                                             : k_quant_nvfp4<kNvfp4, 128, DEC>)
-                        : (fmt == kNvfp4Mx   ? k_quant_nvfp4<kNvfp4Mx, 0, DEC>
-                           : fmt == kNvfp4P2 ? k_quant_nvfp4<kNvfp4P2, 0, DEC>
-                                             : k_quant_nvfp4<kNvfp4, 0, DEC>);
+  if (hb == 128) {
+    // cols is a multiple of 128, so the 32-element groups come in fours
+    const int64_t ngrp = rows * cols / 32;
+    int64_t wgs = (ngrp + 255) / 256;
+    if (wgs > 4096) wgs = 4096;
+    if (wgs < 1) wgs = 1;
+    auto k32 = fmt == kNvfp4Mx ? k_quant_nvfp4_w32<kNvfp4Mx, DEC>
+                               : fmt == kNvfp4P2 ? k_quant_nvfp4_w32<kNvfp4P2, DEC> : k_quant_nvfp4_w32<kNvfp4, DEC>;
+    hipLaunchKernelGGL(k32, dim3((unsigned)wgs), dim3(256), 0, s, x, ngrp, c_b, amax, codes, blk_scale,
+                       tensor_scale, decision, want, dec);
+    return hipGetLastError();
+  }
+  auto kern = fmt == kNvfp4Mx   ? k_quant_nvfp4<kNvfp4Mx, 0, DEC>
+              : fmt == kNvfp4P2 ? k_quant_nvfp4<kNvfp4P2, 0, DEC>
+                                : k_quant_nvfp4<kNvfp4, 0, DEC>;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, s, x, nch, hb, c_b, amax, codes,
                      blk_scale, tensor_scale, decision, want, dec);
   return hipGetLastError();

@@ -49,9 +49,9 @@ KINDS = OrderedDict([
     ("select_final", r"k_stats_final"),
     ("select_quant_int8", r"k_quant_int_rows<\d+, \d+, false, true(, \d+)?>"),
     ("quant_int8", r"k_quant_int_rows(_long)?<\d+, \d+, false(, false(, \d+)?)?>"),
-    ("quant_nvfp4_mx", r"k_quant_nvfp4<3(, \d+)?(, (true|false))?>"),
-    ("quant_nvfp4_p2", r"k_quant_nvfp4<4(, \d+)?(, (true|false))?>"),
-    ("quant_nvfp4", r"k_quant_nvfp4<2(, \d+)?(, (true|false))?>"),
+    ("quant_nvfp4_mx", r"k_quant_nvfp4(_w32)?<3(, \d+)?(, (true|false))?>"),
+    ("quant_nvfp4_p2", r"k_quant_nvfp4(_w32)?<4(, \d+)?(, (true|false))?>"),
+    ("quant_nvfp4", r"k_quant_nvfp4(_w32)?<2(, \d+)?(, (true|false))?>"),
     ("decode_nvfp4", r"k_dq_decode_w"),
     ("gemm_int8", r"k_gemm_i8i4(_pipe)?<[\d, ]*1>"),
     ("gemm_nvfp4_mx", r"k_gemm_fp4mx_pipe<1, false>"),
