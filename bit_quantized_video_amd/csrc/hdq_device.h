@@ -246,12 +246,6 @@ __device__ __forceinline__ float pow2_ceil_clamped(float t) {
 }
 
 // ---- FP4 E2M1 elements -----------------------------------------------------
-// Value of an E2M1 code (bit 3 the sign; exponent bias 1, one mantissa bit).
-__device__ __forceinline__ float e2m1_value(uint32_t c) {
-  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
-  const float v = e ? __uint_as_float(((e + 126u) << 23) | (m << 22)) : 0.5f * (float)m;
-  return (c & 8u) ? -v : v;
-}
 // Two E2M1 codes (nearest, ties to even, saturating at 6, sign bit = sign of
 // the input) in the low byte: a in bits 3:0, b in bits 7:4.
 __device__ __forceinline__ uint32_t e2m1x2_encode(float a, float b) {

@@ -365,17 +365,18 @@ __device__ __forceinline__ uint32_t nvfp4_chunk(float (&v)[8], float s_t, float 
 }
 
 // Exact bf16 values of one chunk's 8 codes with block-scale byte e: E2M1
-// value x E4M3 value, exact in float32 and in bf16 (at most 6 significant
-// bits), so the top half of the float is the bf16.
+// value (the hardware conversion at scale 1, exact) x E4M3 value, exact in
+// float32 and in bf16 (at most 6 significant bits), so the bf16 rounding
+// returns it unchanged.
+template <int B>
+__device__ __forceinline__ uint32_t nvfp4_decode_pair(uint32_t p, float s) {
+  const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, B);
+  return pack_bf16x2(f[0] * s, f[1] * s);
+}
 __device__ __forceinline__ uint4 nvfp4_decode_chunk(uint32_t p, uint32_t e) {
   const float s = e4m3_decode(e);
-  uint32_t o[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t lo = (p >> (8 * j)) & 15u, hi = (p >> (8 * j + 4)) & 15u;
-    o[j] = (__float_as_uint(e2m1_value(lo) * s) >> 16) | ((__float_as_uint(e2m1_value(hi) * s) >> 16) << 16);
-  }
-  return make_uint4(o[0], o[1], o[2], o[3]);
+  return make_uint4(nvfp4_decode_pair<0>(p, s), nvfp4_decode_pair<1>(p, s), nvfp4_decode_pair<2>(p, s),
+                    nvfp4_decode_pair<3>(p, s));
 }
 
 // UNROLL 8-element chunks per lane per iteration, loads issued first; a wave
@@ -448,11 +449,11 @@ __device__ __forceinline__ uint32_t e2m1x8_encode(const float* y, float inv) {
 // 8-element chunk, and no cross-lane maximum), and a lane writes its 16 code
 // bytes and 2 scale bytes with one store each.  The same arithmetic as
 // k_quant_nvfp4, value for value.
-template <int FMT, bool DEC>
+template <int FMT>
 __global__ __launch_bounds__(256) void k_quant_nvfp4_w32(
     const uint16_t* __restrict__ x, int64_t ngrp, float c_b, const float* __restrict__ amax_ptr,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ blk_scale, float* __restrict__ tensor_scale,
-    const int32_t* __restrict__ decision, int32_t want, uint16_t* __restrict__ dec) {
+    const int32_t* __restrict__ decision, int32_t want) {
   if (decision != nullptr && *decision != want) return;
   const int lane = threadIdx.x & 63;
   const float A = *amax_ptr;
@@ -504,13 +505,6 @@ __global__ __launch_bounds__(256) void k_quant_nvfp4_w32(
     p[3] = inv1 == 0.0f ? 0u : e2m1x8_encode(v + 24, inv1);
     reinterpret_cast<uint4*>(codes)[g] = make_uint4(p[0], p[1], p[2], p[3]);
     reinterpret_cast<uint16_t*>(blk_scale)[g] = (uint16_t)(e0 | (e1 << 8));
-    if constexpr (DEC) {
-      uint4* dv = reinterpret_cast<uint4*>(dec) + 4 * g;
-      dv[0] = nvfp4_decode_chunk(p[0], e0);
-      dv[1] = nvfp4_decode_chunk(p[1], e0);
-      dv[2] = nvfp4_decode_chunk(p[2], e1);
-      dv[3] = nvfp4_decode_chunk(p[3], e1);
-    }
   }
 }
 
@@ -528,21 +522,27 @@ static hipError_t launch_quant_nvfp4_t(const uint16_t* x, int64_t rows, int64_t 
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
   const float c_b = hadamard_scale(hb);
-  if (hb == 128) {
-    // cols is a multiple of 128, so the 32-element groups come in fours
+  if (hb == 128 && !DEC) {
+    // cols is a multiple of 128, so the 32-element groups come in fours.
+    // (With the decoded values, 64 bytes per lane in four 16-byte stores at
+    // a 64-byte lane stride, this layout measured slower at K = 12288 than
+    // the 8-element chunks below, whose stores are contiguous across lanes.)
     const int64_t ngrp = rows * cols / 32;
     int64_t wgs = (ngrp + 255) / 256;
     if (wgs > 4096) wgs = 4096;
     if (wgs < 1) wgs = 1;
-    auto k32 = fmt == kNvfp4Mx ? k_quant_nvfp4_w32<kNvfp4Mx, DEC>
-                               : fmt == kNvfp4P2 ? k_quant_nvfp4_w32<kNvfp4P2, DEC> : k_quant_nvfp4_w32<kNvfp4, DEC>;
+    auto k32 = fmt == kNvfp4Mx ? k_quant_nvfp4_w32<kNvfp4Mx>
+                               : fmt == kNvfp4P2 ? k_quant_nvfp4_w32<kNvfp4P2> : k_quant_nvfp4_w32<kNvfp4>;
     hipLaunchKernelGGL(k32, dim3((unsigned)wgs), dim3(256), 0, s, x, ngrp, c_b, amax, codes, blk_scale,
-                       tensor_scale, decision, want, dec);
+                       tensor_scale, decision, want);
     return hipGetLastError();
   }
-  auto kern = fmt == kNvfp4Mx   ? k_quant_nvfp4<kNvfp4Mx, 0, DEC>
-              : fmt == kNvfp4P2 ? k_quant_nvfp4<kNvfp4P2, 0, DEC>
-                                : k_quant_nvfp4<kNvfp4, 0, DEC>;
+  auto kern = hb == 128 ? (fmt == kNvfp4Mx   ? k_quant_nvfp4<kNvfp4Mx, 128, DEC>
+                           : fmt == kNvfp4P2 ? k_quant_nvfp4<kNvfp4P2, 128, DEC>
+                                             : k_quant_nvfp4<kNvfp4, 128, DEC>)
+                        : (fmt == kNvfp4Mx   ? k_quant_nvfp4<kNvfp4Mx, 0, DEC>
+                           : fmt == kNvfp4P2 ? k_quant_nvfp4<kNvfp4P2, 0, DEC>
+                                             : k_quant_nvfp4<kNvfp4, 0, DEC>);
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, s, x, nch, hb, c_b, amax, codes,
                      blk_scale, tensor_scale, decision, want, dec);
   return hipGetLastError();

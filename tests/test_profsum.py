@@ -70,9 +70,9 @@ def test_one_launch_gemms_take_their_calls_decisions():
         for name, kind in (("void hdq::k_quant_nvfp4<3, 128, false>(unsigned short const*)", "quant_nvfp4_mx"),
                            ("void hdq::k_quant_nvfp4<2, 128, true>(unsigned short const*)", "quant_nvfp4"),
                            ("void hdq::k_quant_nvfp4<4, 0, false>(unsigned short const*)", "quant_nvfp4_p2"),
-                           ("void hdq::k_quant_nvfp4_w32<3, false>(unsigned short const*)", "quant_nvfp4_mx"),
-                           ("void hdq::k_quant_nvfp4_w32<2, true>(unsigned short const*)", "quant_nvfp4"),
-                           ("void hdq::k_quant_nvfp4_w32<4, false>(unsigned short const*)", "quant_nvfp4_p2")):
+                           ("void hdq::k_quant_nvfp4_w32<3>(unsigned short const*)", "quant_nvfp4_mx"),
+                           ("void hdq::k_quant_nvfp4_w32<2>(unsigned short const*)", "quant_nvfp4"),
+                           ("void hdq::k_quant_nvfp4_w32<4>(unsigned short const*)", "quant_nvfp4_p2")):
             assert P.classify(name) == kind, name
         assert c("void hdq::k_gemm_dispatch<0, 3>(int const*)") is None  # f32 output: not the schedule
     finally:
