@@ -170,7 +170,9 @@ def test_quantize_int_zero_and_tiny_rows():
     assert np.array_equal(q.codes.cpu().numpy(), rq)
 
 
-NV_CASES = [(1, 64, 16), (37, 128, 32), (130, 1024, 64), (301, 3072, 128), (5, 12288, 128)]
+# (2800 x 12288 at block 128: more 32-element groups than the grid's threads,
+# so the grid-stride loop runs a second, partial round)
+NV_CASES = [(1, 64, 16), (37, 128, 32), (130, 1024, 64), (301, 3072, 128), (5, 12288, 128), (2800, 12288, 128)]
 
 
 # NVFP4 recipes: the oracle's mx argument for each format
@@ -194,9 +196,11 @@ def test_quantize_nvfp4_bitexact(M, K, hb, fmt, amax_given):
     nvfp4_codes_equal(q.codes.cpu().numpy(), rc, "E2M1 codes")
 
 
-def test_quantize_nvfp4_zero_tensor():
-    x16 = np.zeros((8, 128), np.uint16)
-    q = hdq.quantize(to_dev(x16), 64, hdq.FMT_NVFP4)
+@pytest.mark.parametrize("hb", [64, 128])
+@pytest.mark.parametrize("fmt", list(FP4_FMTS))
+def test_quantize_nvfp4_zero_tensor(hb, fmt):
+    x16 = np.zeros((8, 256), np.uint16)
+    q = hdq.quantize(to_dev(x16), hb, fmt)
     assert q.tensor_scale.item() == 0.0
     assert not q.codes.any().item() and not q.blk_scale.any().item()
 
