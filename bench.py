@@ -1066,6 +1066,7 @@ def bench_deltaquant(args, hdq, synth):
             fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        gpu_filler()
         e0.record()
         for _ in range(n):
             fn()

@@ -863,66 +863,83 @@ __global__ __launch_bounds__(256) void k_dq_core(const uint16_t* __restrict__ x,
 
 __global__ void k_dq_zero(uint32_t* p) { *p = 0u; }
 
-// Each token's difference from the stored core, quantized to NVFP4 with the
-// tensor scale of the largest |difference| (a NaN when that is not finite).
-// A streaming pass, one wave per token row at a time (rows wave, + all
-// waves, ...): lane l takes chunk columns l, l + 64, ... (8 loads of the
-// token and 8 of the cube's E4M3 codes in flight), the stored core decoded
-// per element as code value x scale.  A 16-element block sits on lanes
-// l, l ^ 1 and a 32-element group on l ^ {0..3} (K % 32 == 0); every lane
-// runs the block code (zeros past the row), only the stores are predicated.
+// Each token's difference from the stored core (signed E4M3 code value x the
+// cube's scale), quantized to NVFP4 with the tensor scale of the largest
+// |difference| (a NaN when that is not finite).  A streaming pass with one
+// lane per 32 consecutive elements of a token row (K % 32 == 0), NVFP4 as in
+// k_quant_nvfp4_w32: a 32-element group's maximum and scale stay in the lane,
+// and its 16 code bytes and 2 scale bytes are stored at once.  The groups of
+// all rows are dealt to the grid's threads in order (M * K / 32 < 2^29).
 template <int FMT>
-__global__ __launch_bounds__(256) void k_dq_delta(const uint16_t* __restrict__ x, int K, const DqGrid g, int M,
-                                                  const uint8_t* __restrict__ ccodes,
-                                                  const float* __restrict__ cscale,
-                                                  const uint32_t* __restrict__ damax_bits,
-                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ blk_scale,
-                                                  float* __restrict__ tensor_scale) {
-  constexpr int U = 8;
-  const int tid = threadIdx.x, lane = tid & 63, kq = K >> 3;
+__global__ __launch_bounds__(256) void k_dq_delta_w32(const uint16_t* __restrict__ x, int K, const DqGrid g,
+                                                      int ngrp, const uint8_t* __restrict__ ccodes,
+                                                      const float* __restrict__ cscale,
+                                                      const uint32_t* __restrict__ damax_bits,
+                                                      uint8_t* __restrict__ codes, uint8_t* __restrict__ blk_scale,
+                                                      float* __restrict__ tensor_scale) {
   const float A = __uint_as_float(*damax_bits);
   const float s_t = (A >= kTiny) ? A / (FMT == kNvfp4 ? 2688.0f : 1536.0f) : (A == A ? 0.0f : A);
-  if (blockIdx.x == 0 && tid == 0) *tensor_scale = s_t;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *tensor_scale = s_t;
   const float six_st = 6.0f * s_t, inv_st = s_t > 0.0f ? 1.0f / s_t : 0.0f;
+  const uint32_t gpr = (uint32_t)K >> 5;  // groups per row
   const uint4* xv = reinterpret_cast<const uint4*>(x);
-  const uint2* cc = reinterpret_cast<const uint2*>(ccodes);
-  uint32_t* cv = reinterpret_cast<uint32_t*>(codes);
-  const int nwaves = (int)gridDim.x * 4;
-  for (int row = __builtin_amdgcn_readfirstlane((int)blockIdx.x * 4 + (tid >> 6)); row < M; row += nwaves) {
-    const int cube = dq_cube(row, g);
+  const uint4* cv = reinterpret_cast<const uint4*>(ccodes);
+  const int stride = (int)gridDim.x * (int)blockDim.x;
+  for (int gi = (int)blockIdx.x * (int)blockDim.x + (int)threadIdx.x; gi < ngrp; gi += stride) {
+    const uint32_t row = (uint32_t)gi / gpr, col = (uint32_t)gi - row * gpr;
+    const int cube = dq_cube((int)row, g);
+    uint4 w[4], e16[2];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) w[c] = xv[4 * (int64_t)gi + c];
+    const int64_t cb = ((int64_t)cube * gpr + col) * 2;
+    e16[0] = cv[cb];
+    e16[1] = cv[cb + 1];
     const float sc = cscale[cube];
-    const int64_t xb = (int64_t)row * kq, cb = (int64_t)cube * kq;
-    for (int q0 = 0; q0 < kq; q0 += 64 * U) {
-      uint4 w[U];
-      uint2 e8[U];
+    float v[32], e[32];
 #pragma unroll
-      for (int j = 0; j < U; ++j) {
-        const int q = q0 + 64 * j + lane;
-        const bool ok = q < kq;
-        w[j] = ok ? xv[xb + q] : make_uint4(0u, 0u, 0u, 0u);
-        e8[j] = ok ? cc[cb + q] : make_uint2(0u, 0u);
-      }
-#pragma unroll
-      for (int j = 0; j < U; ++j) {
-        if (q0 + 64 * j >= kq) break;  // uniform
-        const int q = q0 + 64 * j + lane;
-        float v[8];
-        bf16x8_to_f32(w[j], v);
-        // the stored core: signed E4M3 value (the hardware conversion, exact)
-        // times the cube's scale
-        float e[8];
-        e4m3x4_to_f32(e8[j].x, &e[0]);
-        e4m3x4_to_f32(e8[j].y, &e[4]);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = v[i] - e[i] * sc;
-        uint32_t eb;
-        const uint32_t packed = nvfp4_chunk<FMT>(v, s_t, six_st, inv_st, &eb);
-        if (q < kq) {
-          cv[xb + q] = packed;
-          if ((q & 1) == 0) blk_scale[(xb + q) >> 1] = (uint8_t)eb;
-        }
-      }
+    for (int c = 0; c < 4; ++c) {
+      v[8 * c + 0] = bf16_lo(w[c].x);
+      v[8 * c + 1] = bf16_hi(w[c].x);
+      v[8 * c + 2] = bf16_lo(w[c].y);
+      v[8 * c + 3] = bf16_hi(w[c].y);
+      v[8 * c + 4] = bf16_lo(w[c].z);
+      v[8 * c + 5] = bf16_hi(w[c].z);
+      v[8 * c + 6] = bf16_lo(w[c].w);
+      v[8 * c + 7] = bf16_hi(w[c].w);
     }
+    // the stored core: signed E4M3 value (the hardware conversion, exact)
+    // times the cube's scale
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      e4m3x4_to_f32(e16[h].x, &e[16 * h + 0]);
+      e4m3x4_to_f32(e16[h].y, &e[16 * h + 4]);
+      e4m3x4_to_f32(e16[h].z, &e[16 * h + 8]);
+      e4m3x4_to_f32(e16[h].w, &e[16 * h + 12]);
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = v[i] - e[i] * sc;
+    float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      a0 = fmaxf(a0, fabsf(v[i]));
+      a1 = fmaxf(a1, fabsf(v[16 + i]));
+    }
+    uint32_t e0, e1;
+    float inv0, inv1;
+    if constexpr (FMT == kNvfp4Mx) {
+      inv0 = inv1 = nvfp4_block_inv<FMT>(fmaxf(a0, a1), s_t, six_st, inv_st, &e0);
+      e1 = e0;
+    } else {
+      inv0 = nvfp4_block_inv<FMT>(a0, s_t, six_st, inv_st, &e0);
+      inv1 = nvfp4_block_inv<FMT>(a1, s_t, six_st, inv_st, &e1);
+    }
+    uint32_t p[4];
+    p[0] = inv0 == 0.0f ? 0u : e2m1x8_encode(v + 0, inv0);
+    p[1] = inv0 == 0.0f ? 0u : e2m1x8_encode(v + 8, inv0);
+    p[2] = inv1 == 0.0f ? 0u : e2m1x8_encode(v + 16, inv1);
+    p[3] = inv1 == 0.0f ? 0u : e2m1x8_encode(v + 24, inv1);
+    reinterpret_cast<uint4*>(codes)[gi] = make_uint4(p[0], p[1], p[2], p[3]);
+    reinterpret_cast<uint16_t*>(blk_scale)[gi] = (uint16_t)(e0 | (e1 << 8));
   }
 }
 
@@ -968,13 +985,14 @@ hipError_t launch_dq_quantize(const uint16_t* x, int64_t K, const DqGrid& g, int
     hipLaunchKernelGGL(k_dq_core, dim3((unsigned)ncubes), dim3(256), lds, s, x, (int)K, g, ccodes, cscale,
                        core_bf16, damax_bits);
   }
-  auto kdelta = fmt == kNvfp4Mx ? k_dq_delta<kNvfp4Mx> : fmt == kNvfp4P2 ? k_dq_delta<kNvfp4P2> : k_dq_delta<kNvfp4>;
-  const int64_t dslots = fmt == kNvfp4Mx   ? resident_grid<k_dq_delta<kNvfp4Mx>>(256, 0)
-                         : fmt == kNvfp4P2 ? resident_grid<k_dq_delta<kNvfp4P2>>(256, 0)
-                                           : resident_grid<k_dq_delta<kNvfp4>>(256, 0);
-  const int64_t dblocks = (M + 3) / 4;
-  hipLaunchKernelGGL(kdelta, dim3((unsigned)(dblocks < dslots ? dblocks : dslots)), dim3(256), 0, s, x, (int)K, g,
-                     (int)M, ccodes, cscale, damax_bits, codes, blk_scale, tensor_scale);
+  const int ngrp = (int)(M * (K >> 5));
+  int64_t dblocks = (ngrp + 255) / 256;
+  if (dblocks > 4096) dblocks = 4096;
+  auto kdelta = fmt == kNvfp4Mx   ? k_dq_delta_w32<kNvfp4Mx>
+                : fmt == kNvfp4P2 ? k_dq_delta_w32<kNvfp4P2>
+                                  : k_dq_delta_w32<kNvfp4>;
+  hipLaunchKernelGGL(kdelta, dim3((unsigned)dblocks), dim3(256), 0, s, x, (int)K, g, ngrp, ccodes, cscale,
+                     damax_bits, codes, blk_scale, tensor_scale);
   return hipGetLastError();
 }
 
