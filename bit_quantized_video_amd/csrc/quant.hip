@@ -617,41 +617,46 @@ __global__ __launch_bounds__(MAXT) void k_dq_core_reg(const uint16_t* __restrict
                                                      float* __restrict__ scale, uint16_t* __restrict__ core_bf16,
                                                      uint32_t* __restrict__ damax_bits) {
   static_assert(!PIPE || ITER == 1, "the pipelined form holds one column per thread");
-  __shared__ float red[16];
+  // rows, nts and red are double-buffered by cube parity, so one barrier per
+  // cube orders every write after the last read of the same buffer (two
+  // cubes earlier); the largest |difference| and the non-finite flag are
+  // kept per thread over all of the workgroup's cubes and merged once
+  __shared__ float red[2][16];
   __shared__ float redd[16];
-  __shared__ int rows[8];
-  __shared__ int nts;
+  __shared__ int rows[2][8];
+  __shared__ int nts[2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
   const int kq = K >> 3;
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   const int step = PIPE ? (int)gridDim.x : ncubes;
   // a cube's rows into rows[] and its token count into nts
-  auto cube_rows = [&](int cb) {
+  auto cube_rows = [&](int cb, int buf) {
     if (tid < 8 && cb < ncubes) {
       int ntc;
       const int r = dq_rows8(g, cb, tid, &ntc);
-      if (tid < ntc) rows[tid] = r;
-      if (tid == 0) nts = ntc;
+      if (tid < ntc) rows[buf][tid] = r;
+      if (tid == 0) nts[buf] = ntc;
     }
   };
   uint4 wn[ITER][8];
   int ntn = 0;  // the token count of the cube in wn (read with its rows)
-  auto load = [&]() {
-    const int ntc = nts;
+  auto load = [&](int buf) {
+    const int ntc = nts[buf];
     ntn = ntc;
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
       const int q = tid + it * (int)blockDim.x;
 #pragma unroll
       for (int u = 0; u < 8; ++u)
-        wn[it][u] = q < kq && u < ntc ? xv[(int64_t)rows[u] * kq + q] : make_uint4(0u, 0u, 0u, 0u);
+        wn[it][u] = q < kq && u < ntc ? xv[(int64_t)rows[buf][u] * kq + q] : make_uint4(0u, 0u, 0u, 0u);
     }
   };
-  int cube = blockIdx.x;
-  cube_rows(cube);
+  int cube = blockIdx.x, par = 0;
+  cube_rows(cube, 0);
   __syncthreads();
-  load();
-  if (PIPE) __syncthreads();  // rows and nts read by every wave before the next cube's are written
+  load(0);
+  float dmax = 0.0f;
+  bool bad = false;
   do {
     const int nt = ntn;
     uint4 w[ITER][8];
@@ -659,14 +664,13 @@ __global__ __launch_bounds__(MAXT) void k_dq_core_reg(const uint16_t* __restrict
     for (int it = 0; it < ITER; ++it)
 #pragma unroll
       for (int u = 0; u < 8; ++u) w[it][u] = wn[it][u];
-    // the next cube's rows (the current cube's were last read by its loads,
-    // before the previous cube's last barrier); its loads follow the first
-    // barrier below
-    if (PIPE) cube_rows(cube + step);
+    // the next cube's rows into the other buffer (last read by the loads of
+    // the cube before this one, which every wave finished before the
+    // previous cube's barrier); its loads follow the barrier below
+    if (PIPE) cube_rows(cube + step, par ^ 1);
     const float n = (float)nt;
     float c[ITER][8];  // the mean, then the stored core
     float amax = 0.0f;
-    bool bad = false;
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
       float sum[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
@@ -703,14 +707,13 @@ __global__ __launch_bounds__(MAXT) void k_dq_core_reg(const uint16_t* __restrict
       for (int u = 0; u < 8; ++u)
         asm volatile("" : "+v"(w[it][u].x), "+v"(w[it][u].y), "+v"(w[it][u].z), "+v"(w[it][u].w));
     amax = wave_max(amax);
-    if (lane == 0) red[wave] = amax;
+    if (lane == 0) red[par][wave] = amax;
     __syncthreads();  // also publishes the next cube's rows
-    if (PIPE && cube + step < ncubes) load();
+    if (PIPE && cube + step < ncubes) load(par ^ 1);
     amax = 0.0f;
-    for (int i = 0; i < nwaves; ++i) amax = fmaxf(amax, red[i]);
+    for (int i = 0; i < nwaves; ++i) amax = fmaxf(amax, red[par][i]);
     const float sc = amax >= kTiny ? amax / 448.0f : 0.0f;
     if (tid == 0) scale[cube] = sc;
-    float dmax = 0.0f;
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
       const int q = tid + it * (int)blockDim.x;
@@ -748,21 +751,21 @@ __global__ __launch_bounds__(MAXT) void k_dq_core_reg(const uint16_t* __restrict
         }
       }
     }
-    // a NaN difference needs a non-finite token element or stored core, and
-    // so a non-finite mean (flagged above); an overflowing one is infinite and
-    // reaches the maximum
-    bad |= !dq_finite(dmax);
-    dmax = wave_max(dmax);
-    if (lane == 0) redd[wave] = dmax;
-    bad = __syncthreads_or(bad);  // also: every wave has read red and (for its loads) rows
-    if (tid == 0) {
-      float m = 0.0f;
-      for (int i = 0; i < nwaves; ++i) m = fmaxf(m, redd[i]);
-      atomicMax(damax_bits, bad ? kDqNonFinite : __float_as_uint(m));
-    }
-    __syncthreads();  // redd, rows and nts read before the next cube rewrites them
     cube += step;
+    par ^= 1;
   } while (PIPE && cube < ncubes);
+  // a NaN difference needs a non-finite token element or stored core, and
+  // so a non-finite mean (flagged above); an overflowing one is infinite and
+  // reaches the maximum
+  bad |= !dq_finite(dmax);
+  dmax = wave_max(dmax);
+  if (lane == 0) redd[wave] = dmax;
+  bad = __syncthreads_or(bad);
+  if (tid == 0) {
+    float m = 0.0f;
+    for (int i = 0; i < nwaves; ++i) m = fmaxf(m, redd[i]);
+    atomicMax(damax_bits, bad ? kDqNonFinite : __float_as_uint(m));
+  }
 }
 
 // The same for any cube (up to kDqMaxCube tokens) and K: the mean in LDS
