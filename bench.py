@@ -73,6 +73,10 @@ def parse():
     ap.add_argument("--dispatch", choices=["on", "off"], default="on",
                     help="one GEMM launch per layer call for the decided precision (on, default) "
                          "or one gated launch per precision")
+    ap.add_argument("--embed-weight", choices=["capacity", "work"], default="capacity",
+                    help="--delta embed: share the difference chunks among the GEMM launches by the CU "
+                         "time each leaves free (the free CUs over the whole launch plus the workgroups "
+                         "idle in its last tile round; default) or by GEMM work")
     ap.add_argument("--delta-ahead", type=int, default=2,
                     help="with --delta overlap: the difference of call k + D runs beside the GEMMs "
                          "of call k")
@@ -262,13 +266,28 @@ def embed_plan(args, hdq, synth, M, dev):
     its chunks must all have run by the GEMM launch of call k - 1 (call 0's
     runs as a separate pass at the start of the step).  The chunks of calls
     1.. form one queue in call order; launch k takes its share of the queue,
-    proportional to its GEMM's work (so most chunks run beside a GEMM on the
+    proportional to the CU time its GEMM leaves free (--embed-weight
+    capacity) or to its GEMM's work (so most chunks run beside a GEMM on the
     CUs it leaves free), or more when call k + 1's chunks would otherwise
     not be done in time."""
     calls = [(t, b, li) for t in range(args.timesteps) for b in range(args.blocks)
              for li in range(len(synth.SCHEDULE_LAYERS))]
     n = [hdq.delta_chunks(M * synth.SCHEDULE_LAYERS[li][1]) for _, _, li in calls]
     work = [2.0 * M * synth.SCHEDULE_LAYERS[li][1] * synth.SCHEDULE_LAYERS[li][2] for _, _, li in calls]
+    if getattr(args, "embed_weight", "capacity") == "capacity":
+        # CU time a launch leaves to its difference workgroups, in tile times
+        # (a tile's time taken as proportional to K): the CUs the persistent
+        # GEMM leaves free over all of its tile rounds, plus the GEMM
+        # workgroups that have no tile in the last round
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count if torch.cuda.is_available() else 256
+        wgs = (cus & ~7) - (16 if cus >= 128 else 0)
+        def capacity(li):
+            _, K, N = synth.SCHEDULE_LAYERS[li]
+            tiles = -(-M // 256) * -(-N // 256)
+            g = min(tiles, wgs)
+            rounds = -(-tiles // g)
+            return K * ((cus - g) * rounds + (g * rounds - tiles))
+        work = [capacity(li) for _, _, li in calls]
     offs = np.concatenate([[0], np.cumsum(n)]).astype(np.int64)
     parts = torch.full((int(offs[-1]), 2), float("nan"), dtype=torch.float64, device=dev)
     part_of = [parts[offs[k]:offs[k + 1]] for k in range(len(calls))]

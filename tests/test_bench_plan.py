@@ -10,10 +10,12 @@ import bit_quantized_video_amd.hdq as H
 from bit_quantized_video_amd import synth
 
 
+@pytest.mark.parametrize("weight", ["capacity", "work"])
 @pytest.mark.parametrize("blocks,timesteps", [(42, 3), (2, 3), (1, 1)])
-def test_embed_plan_covers_every_chunk_in_time(blocks, timesteps):
+def test_embed_plan_covers_every_chunk_in_time(blocks, timesteps, weight):
     M = synth.M_COGVIDEOX
-    args = argparse.Namespace(timesteps=timesteps, blocks=blocks, dispatch="on", delta="embed")
+    args = argparse.Namespace(timesteps=timesteps, blocks=blocks, dispatch="on", delta="embed",
+                              embed_weight=weight)
     P = bench.embed_plan(args, H, synth, M, "cpu")
     plan = P["embed"]
     calls = [(t, b, li) for t in range(timesteps) for b in range(blocks)
