@@ -13,11 +13,14 @@
 //    weights).  The per-row absmax needs the whole rotated row before the
 //    first code, so one workgroup owns one row and keeps it in registers
 //    (CPT 8-element chunks per thread).
-//  * k_quant_nvfp4: NVFP4 needs only the tensor amax (given) and a 16- or
-//    32-element block max (E4M3 scale per 16, or a power of two per 16 or
-//    per 32), so it is a flat grid-stride kernel with no
-//    workgroup synchronisation; each wave owns 128 consecutive chunks per
-//    iteration (two per lane, loads issued first).
+//  * k_quant_nvfp4_w32 / k_quant_nvfp4: NVFP4 needs only the tensor amax
+//    (given) and a 16- or 32-element block max (E4M3 scale per 16, or a power
+//    of two per 16 or per 32), so they are flat grid-stride kernels with no
+//    workgroup synchronisation.  At Hadamard block 128 a lane holds 32
+//    consecutive elements (a whole 32-element group, so its maximum and scale
+//    stay in the lane); other blocks, and the plain recipe's decoded output,
+//    take 8-element chunks, two per lane (each wave owns 128 consecutive
+//    chunks per iteration, loads issued first).
 #include "hdq_device.h"
 #include "hdq_internal.h"
 
@@ -445,10 +448,10 @@ __device__ __forceinline__ uint32_t e2m1x8_encode(const float* y, float inv) {
 
 // Hadamard block 128: one lane per 32 consecutive elements (fwht128_w32), so
 // a 32-element group's maximum and scale stay inside the lane (one division
-// per 16-element block for every lane that holds it, instead of one per
-// 8-element chunk, and no cross-lane maximum), and a lane writes its 16 code
-// bytes and 2 scale bytes with one store each.  The same arithmetic as
-// k_quant_nvfp4, value for value.
+// per 16-element block -- per 32 with the MX recipe -- where the 8-element
+// layout repeats it for each chunk, and no cross-lane maximum), and a lane
+// writes its 16 code bytes and 2 scale bytes with one store each.  The same
+// arithmetic as k_quant_nvfp4, value for value.
 template <int FMT>
 __global__ __launch_bounds__(256) void k_quant_nvfp4_w32(
     const uint16_t* __restrict__ x, int64_t ngrp, float c_b, const float* __restrict__ amax_ptr,
