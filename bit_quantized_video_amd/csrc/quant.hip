@@ -44,8 +44,9 @@ __device__ __forceinline__ uint32_t low_bytes4(uint32_t a, uint32_t b, uint32_t 
 // max bf16 magnitude bits, ptmax[row] = the row's max |rotated x|, which is
 // the row absmax the quantizer needs anyway), so selection and quantization
 // read x once.  HB > 0: the Hadamard block is HB (the argument is ignored),
-// so the rotation's block-size branches fold away at compile time.
-template <int BLOCK, int CPT, bool INT4, bool STATS = false, int HB = 0>
+// so the rotation's block-size branches fold away at compile time.  FULL:
+// the row is exactly BLOCK x CPT chunks, so no chunk needs a bounds check.
+template <int BLOCK, int CPT, bool INT4, bool STATS = false, int HB = 0, bool FULL = false>
 __global__ __launch_bounds__(BLOCK) void k_quant_int_rows(
     const uint16_t* __restrict__ x, int64_t cols, int hb_arg, float c_b, void* __restrict__ codes,
     float* __restrict__ row_scale, const int32_t* __restrict__ decision, int32_t want,
@@ -69,7 +70,7 @@ __global__ __launch_bounds__(BLOCK) void k_quant_int_rows(
   for (int c = 0; c < CPT; ++c) {
     const int64_t idx = fwht_src((int64_t)c * BLOCK + tid, lane, hb);
     uint4 w = make_uint4(0u, 0u, 0u, 0u);
-    if (idx < nch) w = xr[idx];
+    if (FULL || idx < nch) w = xr[idx];
     bf16x8_to_f32(w, v[c]);
   }
   if constexpr (STATS) {
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(BLOCK) void k_quant_int_rows(
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     const int64_t idx = fwht_src((int64_t)c * BLOCK + tid, lane, hb);
-    if (idx < nch) {
+    if (FULL || idx < nch) {
       uint32_t b[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) b[i] = __float_as_uint(v[c][i] * inv + kMagic);
@@ -189,7 +190,10 @@ template <int BLOCK, int CPT>
 static hipError_t launch_select_q8_t(const uint16_t* x, int64_t rows, int64_t cols, int hb,
                                      void* codes, float* sc, double* psum, uint32_t* pbits,
                                      float* ptmax, hipStream_t s) {
-  if (hb == 128)
+  if (hb == 128 && (cols >> 3) == (int64_t)BLOCK * CPT)
+    hipLaunchKernelGGL((k_quant_int_rows<BLOCK, CPT, false, true, 128, true>), dim3((unsigned)rows), dim3(BLOCK),
+                       0, s, x, cols, hb, hadamard_scale(hb), codes, sc, nullptr, 0, psum, pbits, ptmax);
+  else if (hb == 128)
     hipLaunchKernelGGL((k_quant_int_rows<BLOCK, CPT, false, true, 128>), dim3((unsigned)rows), dim3(BLOCK), 0,
                        s, x, cols, hb, hadamard_scale(hb), codes, sc, nullptr, 0, psum, pbits, ptmax);
   else

@@ -265,9 +265,12 @@ def test_two_part_selection_matches_one_pass(M, K, hb, s):
     assert abs(got[0] / got[1] - ref[0]) <= 2e-6 * ref[0]
 
 
+# (K 3072 and 12288 at block 128 fill a workgroup's chunks exactly, the
+# kernel without bounds checks; K 1920 at block 128 leaves chunks past the row)
 @pytest.mark.parametrize("M,K,hb,s,hist", [(333, 3072, 128, 0.2, True), (64, 1024, 64, 0.05, True),
                                             (9, 12288, 128, 0.1, True), (5, 20480, 128, 0.03, True),
-                                            (17776, 3072, 128, 0.08, True), (100, 512, 32, 0.0, False)])
+                                            (17776, 3072, 128, 0.08, True), (100, 512, 32, 0.0, False),
+                                            (200, 1920, 128, 0.1, True)])
 def test_select_fused_with_int8_quantization(M, K, hb, s, hist):
     """hdq_select_quantize_int8 = hdq_select_precision_sums + INT8 hdq_quantize:
     codes and row scales bit for bit, the decision and delta, max and rotated
