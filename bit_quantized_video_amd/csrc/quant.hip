@@ -177,6 +177,9 @@ static hipError_t launch_int_rows_t(const uint16_t* x, int64_t rows, int64_t col
   if (int4)
     hipLaunchKernelGGL((k_quant_int_rows<BLOCK, CPT, true>), dim3((unsigned)rows), dim3(BLOCK), 0,
                        s, x, cols, hb, c_b, codes, sc, dec, want);
+  else if (hb == 128 && (cols >> 3) == (int64_t)BLOCK * CPT)
+    hipLaunchKernelGGL((k_quant_int_rows<BLOCK, CPT, false, false, 128, true>), dim3((unsigned)rows), dim3(BLOCK),
+                       0, s, x, cols, hb, c_b, codes, sc, dec, want);
   else if (hb == 128)
     hipLaunchKernelGGL((k_quant_int_rows<BLOCK, CPT, false, false, 128>), dim3((unsigned)rows), dim3(BLOCK), 0,
                        s, x, cols, hb, c_b, codes, sc, dec, want);
@@ -505,11 +508,15 @@ __global__ __launch_bounds__(256) void k_quant_nvfp4_w32(
       inv0 = nvfp4_block_inv<FMT>(a0, s_t, six_st, inv_st, &e0);
       inv1 = nvfp4_block_inv<FMT>(a1, s_t, six_st, inv_st, &e1);
     }
+    // encoded unconditionally, then selected (no branch per block): a block
+    // without a scale (inv 0) stores zero codes
     uint32_t p[4];
-    p[0] = inv0 == 0.0f ? 0u : e2m1x8_encode(v + 0, inv0);
-    p[1] = inv0 == 0.0f ? 0u : e2m1x8_encode(v + 8, inv0);
-    p[2] = inv1 == 0.0f ? 0u : e2m1x8_encode(v + 16, inv1);
-    p[3] = inv1 == 0.0f ? 0u : e2m1x8_encode(v + 24, inv1);
+    p[0] = e2m1x8_encode(v + 0, inv0);
+    p[1] = e2m1x8_encode(v + 8, inv0);
+    p[2] = e2m1x8_encode(v + 16, inv1);
+    p[3] = e2m1x8_encode(v + 24, inv1);
+    if (inv0 == 0.0f) p[0] = p[1] = 0u;
+    if (inv1 == 0.0f) p[2] = p[3] = 0u;
     reinterpret_cast<uint4*>(codes)[g] = make_uint4(p[0], p[1], p[2], p[3]);
     reinterpret_cast<uint16_t*>(blk_scale)[g] = (uint16_t)(e0 | (e1 << 8));
   }
@@ -943,11 +950,15 @@ __global__ __launch_bounds__(256) void k_dq_delta_w32(const uint16_t* __restrict
       inv0 = nvfp4_block_inv<FMT>(a0, s_t, six_st, inv_st, &e0);
       inv1 = nvfp4_block_inv<FMT>(a1, s_t, six_st, inv_st, &e1);
     }
+    // encoded unconditionally, then selected (no branch per block): a block
+    // without a scale (inv 0) stores zero codes
     uint32_t p[4];
-    p[0] = inv0 == 0.0f ? 0u : e2m1x8_encode(v + 0, inv0);
-    p[1] = inv0 == 0.0f ? 0u : e2m1x8_encode(v + 8, inv0);
-    p[2] = inv1 == 0.0f ? 0u : e2m1x8_encode(v + 16, inv1);
-    p[3] = inv1 == 0.0f ? 0u : e2m1x8_encode(v + 24, inv1);
+    p[0] = e2m1x8_encode(v + 0, inv0);
+    p[1] = e2m1x8_encode(v + 8, inv0);
+    p[2] = e2m1x8_encode(v + 16, inv1);
+    p[3] = e2m1x8_encode(v + 24, inv1);
+    if (inv0 == 0.0f) p[0] = p[1] = 0u;
+    if (inv1 == 0.0f) p[2] = p[3] = 0u;
     reinterpret_cast<uint4*>(codes)[gi] = make_uint4(p[0], p[1], p[2], p[3]);
     reinterpret_cast<uint16_t*>(blk_scale)[gi] = (uint16_t)(e0 | (e1 << 8));
   }
