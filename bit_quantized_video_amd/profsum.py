@@ -47,8 +47,8 @@ KINDS = OrderedDict([
     ("select_stats", r"k_stats_partial(<[02]>)?"),
     ("select_final_rows", r"k_stats_final_rows"),
     ("select_final", r"k_stats_final"),
-    ("select_quant_int8", r"k_quant_int_rows<\d+, \d+, false, true(, \d+)?>"),
-    ("quant_int8", r"k_quant_int_rows(_long)?<\d+, \d+, false(, false(, \d+)?)?>"),
+    ("select_quant_int8", r"k_quant_int_rows<\d+, \d+, false, true(, \d+)?(, (true|false))?>"),
+    ("quant_int8", r"k_quant_int_rows(_long)?<\d+, \d+, false(, false(, \d+)?(, (true|false))?)?>"),
     ("quant_nvfp4_mx", r"k_quant_nvfp4(_w32)?<3(, \d+)?(, (true|false))?>"),
     ("quant_nvfp4_p2", r"k_quant_nvfp4(_w32)?<4(, \d+)?(, (true|false))?>"),
     ("quant_nvfp4", r"k_quant_nvfp4(_w32)?<2(, \d+)?(, (true|false))?>"),
@@ -109,7 +109,7 @@ class Classifier:
         d = DECISIONS[i % len(DECISIONS)]
         return {1: "gemm_int8", 0: FP4_KIND[fmt], 2: "gemm_bf16"}[d]
 COMMON_SOURCES = ["hdq_device.h", "hdq_internal.h", "../build.py"]
-WEIGHT_PREP = r"k_quant_int_rows(_long)?<\d+, \d+, true(, false(, \d+)?)?>"
+WEIGHT_PREP = r"k_quant_int_rows(_long)?<\d+, \d+, true(, false(, \d+)?(, (true|false))?)?>"
 # A launch that did work: longer than this (trace; gated-off launches take a
 # few microseconds, more when a concurrent stream shares the GPU, and the
 # smallest GEMM that does work takes over 100) / moved more than this (PMC).

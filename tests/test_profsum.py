@@ -21,7 +21,11 @@ def test_classify_kernel_names():
         # with the Hadamard block as a template argument
         "void hdq::k_quant_int_rows<192, 2, false, true, 128>(int)": "select_quant_int8",
         "void hdq::k_quant_int_rows<128, 3, false, false, 128>(int)": "quant_int8",
+        "void hdq::k_quant_int_rows<128, 3, false, false, 128, true>(int)": "quant_int8",
+        "void hdq::k_quant_int_rows<64, 6, false, true, 128, true>(int)": "select_quant_int8",
+        "void hdq::k_quant_int_rows<256, 6, false, true, 128, false>(int)": "select_quant_int8",
         "void hdq::k_quant_int_rows<128, 3, true, false, 0>(int)": None,
+        "void hdq::k_quant_int_rows<128, 3, true, false, 0, false>(int)": None,
         "void hdq::k_quant_nvfp4<3, 128>(int)": "quant_nvfp4_mx",
         "void hdq::k_quant_nvfp4<4, 0>(int)": "quant_nvfp4_p2",
         "void hdq::k_quant_nvfp4<2, 128>(int)": "quant_nvfp4",
@@ -43,6 +47,8 @@ def test_schedule_window_starts_after_weight_prep():
             (4, "void hdq::k_gemm_i8i4_pipe<2, 4, 4, 2, 1>"), (5, "void hdq::k_gemm_i8i4_pipe<2, 4, 4, 2, 0>")]
     assert [r[0] for r in P.schedule_window(rows)] == [3, 4]
     rows[2] = (2, "void hdq::k_quant_int_rows<128, 3, true, false, 0>")
+    assert [r[0] for r in P.schedule_window(rows)] == [3, 4]
+    rows[2] = (2, "void hdq::k_quant_int_rows<128, 3, true, false, 0, false>")  # the full-row argument
     assert [r[0] for r in P.schedule_window(rows)] == [3, 4]
 
 
